@@ -1,0 +1,172 @@
+/*
+ * lamp.h -- C ABI of the LAMP attention forward library for MI355X (gfx950).
+ *
+ * Look-Ahead Mixed-Precision (LAMP) attention, as described in the LAMP
+ * technical summary (gist.science, paper 2601.21623):
+ *   1. baseline K.Q scores y^lo with emulated low-precision accumulation
+ *      PS(mu) ("Experimental results": custom float with mu mantissa bits);
+ *   2. look-ahead selection from the baseline softmax z ("Theoretical
+ *      foundation" item 3): strict rule 2 z_j (1 - z_j) |y_j| > tau, or the
+ *      relaxed relative-threshold rule that drops the normalisation constant
+ *      (one pass, online softmax), or a random control with the strict count;
+ *   3. FP32 recompute of the selected scores only ("Implementation strategy"
+ *      step 3), then softmax, P.V and a row-wise KL(P_FP32 || P_LAMP).
+ *
+ * Conventions shared by every entry point:
+ *   - Tensor pointers are DEVICE pointers owned by the caller; float32,
+ *     contiguous, row-major.  Q, K, V, out: [B, H, S, D] (d fastest).
+ *     Score-shaped buffers: [B, H, S, S] (key fastest).  The library never
+ *     allocates or frees caller memory and never keeps a caller pointer past
+ *     the call.
+ *   - Query row i may attend key j ("valid") iff j <= i when causal = 1,
+ *     always when causal = 0.
+ *   - PS(mu): mu stored fraction bits (precision mu + 1), FP32 exponent range
+ *     with subnormals, round to nearest even after every multiply and every
+ *     add, d ascending from +0.  Operands stay FP32.  mu = 23 is FP32.
+ *   - Scores are scaled once after accumulation, in FP32, by s = the FP32
+ *     value nearest to 1/sqrt(D).
+ *   - Work is enqueued on the given stream (NULL = the default stream);
+ *     outputs are valid once the stream is synchronised.  A non-NULL host
+ *     `stats` makes the call wait for its own work.
+ *   - Errors: every argument check runs before any HIP call.  No C++
+ *     exception crosses this boundary.  The thread-local text of the last
+ *     error is available from lamp_last_error().
+ */
+#ifndef LAMP_H
+#define LAMP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Selection modes. */
+enum {
+    LAMP_STRICT = 0,  /* 2 z_j (1 - z_j) |y^lo_j| > tau over the full row      */
+    LAMP_RELAXED = 1, /* 2 exp(y^lo_j - m_t) |y^lo_j| > tau, m_t = running max
+                         of y^lo over 64-key blocks 0..floor(j/64); one pass   */
+    LAMP_RANDOM = 2   /* per row, as many keys as LAMP_STRICT selects at tau,
+                         the ones with the smallest SplitMix64(seed xor
+                         (((b*H + h)*S + i)*S + j)), ties by lower j           */
+};
+
+/* Return codes. */
+enum {
+    LAMP_OK = 0,
+    LAMP_ERR_INVALID_ARG = -1, /* NULL required pointer, size < 1, mu not in
+                                  [1, 23], tau NaN or negative, causal not 0/1,
+                                  unknown mode, undersized workspace          */
+    LAMP_ERR_UNSUPPORTED = -2, /* D % 4 != 0, D > 256, or sizes that overflow */
+    LAMP_ERR_HIP = -3,         /* a HIP runtime call failed                    */
+    LAMP_ERR_NO_MEMORY = -4    /* the library-managed workspace could not grow */
+};
+
+/* Host-side summary, filled after the call's own work has finished. */
+typedef struct {
+    uint64_t n_rows;        /* B*H*S                                          */
+    uint64_t n_valid;       /* valid (query, key) pairs                       */
+    uint64_t n_selected;    /* scores recomputed in FP32                      */
+    uint64_t n_exact_tiles; /* 64x64 score tiles that left the FP32 fast path
+                               for the exact double-precision PS path (inputs
+                               outside [2^-40, 2^40], non-finite, or mu > 10) */
+    double kl_sum;          /* sum over rows of KL(P_FP32 || P_LAMP)          */
+    double kl_max;          /* max over rows of the same                      */
+    double kl_lowp_sum;     /* sum over rows of KL(P_FP32 || P_lowp), the
+                               all-low-precision baseline                     */
+} lamp_stats;
+
+/* Optional extras for lamp_attention_fwd_ex.  Zero-initialise and set what
+ * you need; every pointer may be NULL. */
+typedef struct {
+    void *stream;             /* hipStream_t to enqueue on; NULL = default    */
+    void *workspace;          /* device scratch of workspace_bytes, or NULL:
+                                 the library keeps a per-device pool          */
+    size_t workspace_bytes;   /* >= lamp_workspace_bytes(...) when given      */
+    uint64_t seed;            /* LAMP_RANDOM seed                             */
+    double *row_kl;           /* device [B,H,S]: KL(P_FP32 || P_LAMP) per row */
+    double *row_kl_lowp;      /* device [B,H,S]: KL(P_FP32 || P_lowp) per row */
+    uint32_t *row_count;      /* device [B,H,S]: selected keys per row        */
+    float *scores_mix;        /* device [B,H,S,S]: y^mix (selected entries
+                                 hold the FP32 recompute, others y^lo); valid
+                                 entries only, others untouched.  Strict and
+                                 random modes, and relaxed when non-NULL      */
+    float *scores_ref;        /* device [B,H,S,S]: uniform FP32 scores y^ref  */
+    void **stage_events;      /* NULL or 2*LAMP_N_STAGES hipEvent_t created by
+                                 the caller; event 2s / 2s+1 are recorded on
+                                 the stream before / after stage s when that
+                                 stage runs (profiling)                       */
+} lamp_params;
+
+/* Stages, for lamp_params.stage_events. */
+enum {
+    LAMP_STAGE_SCAN = 0,      /* operand range scan (fast/exact path choice)  */
+    LAMP_STAGE_SCORES = 1,    /* PS(mu) + FP32 score tiles (strict, random);
+                                 the fused one-pass kernel (relaxed)          */
+    LAMP_STAGE_SELECT = 2,    /* row softmax + selection + compaction         */
+    LAMP_STAGE_RECOMPUTE = 3, /* gather FP32 recompute + scatter              */
+    LAMP_STAGE_FINISH = 4,    /* softmax, probs, P.V, KL (strict, random);
+                                 probs normalise pass (relaxed)               */
+    LAMP_STAGE_STATS = 5,     /* row reductions into lamp_stats               */
+    LAMP_N_STAGES = 6
+};
+
+/*
+ * lamp_attention_fwd -- LAMP attention forward (the whole hot path).
+ *   q, k, v         [B,H,S,D] inputs (required).
+ *   B, H, S, D      sizes, >= 1; D % 4 == 0 and D <= 256.
+ *   causal          0 or 1.
+ *   mu              PS(mu) fraction bits, 1..23.
+ *   tau             selection threshold, >= 0 (+inf selects nothing).
+ *   mode            LAMP_STRICT, LAMP_RELAXED or LAMP_RANDOM.
+ *   out             [B,H,S,D] attention output (required).
+ *   probs           [B,H,S,S] final softmax, or NULL; invalid keys are 0.
+ *   recompute_mask  [B,H,S,ceil(S/32)] uint32 or NULL: bit (j % 32) of word
+ *                   j / 32 is set iff score (i, j) was recomputed; all other
+ *                   bits (invalid keys, padding) are 0.
+ *   stats           host lamp_stats or NULL (non-NULL synchronises).
+ * Uses the default stream and the library-managed workspace.
+ */
+int lamp_attention_fwd(const float *q, const float *k, const float *v,
+                       int B, int H, int S, int D, int causal, int mu, float tau, int mode,
+                       float *out, float *probs, uint32_t *recompute_mask, lamp_stats *stats);
+
+/* Same, with the optional extras of lamp_params (p may be NULL). */
+int lamp_attention_fwd_ex(const float *q, const float *k, const float *v,
+                          int B, int H, int S, int D, int causal, int mu, float tau, int mode,
+                          float *out, float *probs, uint32_t *recompute_mask, lamp_stats *stats,
+                          const lamp_params *p);
+
+/*
+ * lamp_workspace_bytes -- device scratch that lamp_attention_fwd_ex needs for
+ * these sizes and mode when probs / scores_mix / scores_ref are not given by
+ * the caller (an upper bound: it assumes none of them is).  Returns 0 on
+ * invalid sizes.
+ */
+size_t lamp_workspace_bytes(int B, int H, int S, int D, int mode, int want_probs);
+
+/*
+ * lamp_ps_scores -- step 1 alone: the PS(mu) scores y^lo and the uniform FP32
+ * scores y^ref of every valid (i, j), written into [B,H,S,S] buffers (invalid
+ * entries untouched).  Either output may be NULL (not both).  Enqueued on
+ * `stream` (NULL = default); no synchronisation; no workspace beyond a small
+ * library-managed flag array.
+ */
+int lamp_ps_scores(const float *q, const float *k, int B, int H, int S, int D, int causal, int mu,
+                   float *ylo, float *yref, void *stream);
+
+/* Static text for a return code. */
+const char *lamp_strerror(int code);
+
+/* Thread-local detail of this thread's last failing call ("" if none). */
+const char *lamp_last_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int lamp_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LAMP_H */

@@ -1,0 +1,430 @@
+// lamp_api.cpp -- the C ABI declared in include/lamp.h: argument checks,
+// workspace layout, launch sequence, errors.
+//
+// Launch sequence of one call (LAMP summary, "Implementation strategy"):
+//   strict / random:  operand scan -> PS(mu) + FP32 score tiles -> row
+//                     softmax + selection + compaction (random: strict counts,
+//                     then hash selection) -> gather FP32 recompute ->
+//                     softmax + P.V + KL -> [stats]
+//   relaxed:          operand scan -> fused one-pass kernel -> [probs pass]
+//                     -> [stats]
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include <mutex>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "lamp.h"
+#include "lamp_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int set_error(int code, const std::string &msg)
+{
+    g_last_error = msg;
+    return code;
+}
+
+int hip_error(hipError_t e, const char *what)
+{
+    g_last_error = std::string(what) + ": " + hipGetErrorString(e);
+    return LAMP_ERR_HIP;
+}
+
+#define LAMP_HIP_TRY(expr, what)                  \
+    do {                                          \
+        hipError_t e_ = (expr);                   \
+        if (e_ != hipSuccess)                     \
+            return hip_error(e_, what);           \
+    } while (0)
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Library-managed workspace, one per device, grow-only.
+struct Pool {
+    void *ptr = nullptr;
+    size_t bytes = 0;
+};
+std::mutex g_pool_mutex;
+std::vector<Pool> g_pools;
+
+int pool_get(size_t bytes, void **out)
+{
+    int dev = 0;
+    LAMP_HIP_TRY(hipGetDevice(&dev), "hipGetDevice");
+    std::lock_guard<std::mutex> lock(g_pool_mutex);
+    if ((size_t)dev >= g_pools.size())
+        g_pools.resize(dev + 1);
+    Pool &p = g_pools[dev];
+    if (p.bytes < bytes) {
+        if (p.ptr) {
+            // in-flight work may still use the old block
+            LAMP_HIP_TRY(hipDeviceSynchronize(), "hipDeviceSynchronize");
+            LAMP_HIP_TRY(hipFree(p.ptr), "hipFree");
+            p.ptr = nullptr;
+            p.bytes = 0;
+        }
+        void *ptr = nullptr;
+        hipError_t e = hipMalloc(&ptr, bytes);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return set_error(LAMP_ERR_NO_MEMORY,
+                             "hipMalloc of " + std::to_string(bytes) + " bytes failed: " +
+                                 hipGetErrorString(e));
+        }
+        p.ptr = ptr;
+        p.bytes = bytes;
+    }
+    *out = p.ptr;
+    return LAMP_OK;
+}
+
+struct Sizes {
+    uint64_t BH, n_rows, n_valid, n_scores;
+    int tiles, W;
+};
+
+int check_sizes(int B, int H, int S, int D, Sizes *z)
+{
+    if (B < 1 || H < 1 || S < 1 || D < 1)
+        return set_error(LAMP_ERR_INVALID_ARG, "B, H, S and D must be >= 1");
+    if (D % 4 != 0 || D > 256)
+        return set_error(LAMP_ERR_UNSUPPORTED, "D must be a multiple of 4 and at most 256");
+    z->BH = (uint64_t)B * (uint64_t)H;
+    z->n_rows = z->BH * (uint64_t)S;
+    z->tiles = (S + lamp::kTile - 1) / lamp::kTile;
+    z->W = (S + 31) / 32;
+    z->n_scores = z->n_rows * (uint64_t)S;
+    if (z->BH > (1ull << 31) || z->n_rows >= (1ull << 31) ||
+        z->BH * (uint64_t)z->tiles * (uint64_t)z->tiles >= (1ull << 31) ||
+        z->n_scores > (1ull << 40))
+        return set_error(LAMP_ERR_UNSUPPORTED, "problem size overflows the launch geometry");
+    return LAMP_OK;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_args(const float *q, const float *k, const float *v, int causal, int mu, float tau,
+               int mode, const float *out)
+{
+    if (!q || !k || !v || !out)
+        return set_error(LAMP_ERR_INVALID_ARG, "q, k, v and out are required");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return set_error(LAMP_ERR_INVALID_ARG, "q, k, v and out must be 16-byte aligned");
+    if (causal != 0 && causal != 1)
+        return set_error(LAMP_ERR_INVALID_ARG, "causal must be 0 or 1");
+    if (mu < 1 || mu > 23)
+        return set_error(LAMP_ERR_INVALID_ARG, "mu must be in [1, 23]");
+    if (isnan(tau) || tau < 0.0f)
+        return set_error(LAMP_ERR_INVALID_ARG, "tau must be >= 0 and not NaN");
+    if (mode != LAMP_STRICT && mode != LAMP_RELAXED && mode != LAMP_RANDOM)
+        return set_error(LAMP_ERR_INVALID_ARG, "unknown mode");
+    return LAMP_OK;
+}
+
+// Workspace carve-up; offsets of pieces that are not needed stay SIZE_MAX.
+struct Layout {
+    size_t ymix = SIZE_MAX, yref = SIZE_MAX, list = SIZE_MAX, row_count = SIZE_MAX,
+           row_kl = SIZE_MAX, row_kl_lowp = SIZE_MAX, unsafe = SIZE_MAX, dstats = SIZE_MAX,
+           row_m = SIZE_MAX, row_l = SIZE_MAX;
+    size_t total = 0;
+    size_t take(size_t bytes)
+    {
+        size_t off = total;
+        total += align_up(bytes);
+        return off;
+    }
+};
+
+struct Needs {
+    bool ymix, yref, row_count, row_kl, row_kl_lowp;
+};
+
+Layout plan(const Sizes &z, int mode, const Needs &n)
+{
+    Layout L;
+    L.dstats = L.take(sizeof(lamp::DevStats));
+    L.unsafe = L.take(2 * z.BH * (uint64_t)z.tiles);
+    if (n.row_count)
+        L.row_count = L.take(4 * z.n_rows);
+    if (n.row_kl)
+        L.row_kl = L.take(8 * z.n_rows);
+    if (n.row_kl_lowp)
+        L.row_kl_lowp = L.take(8 * z.n_rows);
+    if (mode == LAMP_RELAXED) {
+        if (n.ymix) {   // probs requested: per-row statistics for the probs pass
+            L.row_m = L.take(4 * z.n_rows);
+            L.row_l = L.take(8 * z.n_rows);
+        }
+    } else {
+        if (n.ymix)
+            L.ymix = L.take(4 * z.n_scores);
+        if (n.yref)
+            L.yref = L.take(4 * z.n_scores);
+        L.list = L.take(4 * z.n_valid);
+    }
+    return L;
+}
+
+template <typename T>
+T *at(void *base, size_t off)
+{
+    return off == SIZE_MAX ? nullptr : reinterpret_cast<T *>(static_cast<char *>(base) + off);
+}
+
+struct StageTimer {
+    void **ev;
+    hipStream_t st;
+    hipError_t begin(int s) { return ev ? hipEventRecord((hipEvent_t)ev[2 * s], st) : hipSuccess; }
+    hipError_t end(int s) { return ev ? hipEventRecord((hipEvent_t)ev[2 * s + 1], st) : hipSuccess; }
+};
+
+}  // namespace
+
+extern "C" {
+
+const char *lamp_strerror(int code)
+{
+    switch (code) {
+    case LAMP_OK: return "success";
+    case LAMP_ERR_INVALID_ARG: return "invalid argument";
+    case LAMP_ERR_UNSUPPORTED: return "unsupported problem shape";
+    case LAMP_ERR_HIP: return "HIP runtime error";
+    case LAMP_ERR_NO_MEMORY: return "out of device memory";
+    default: return "unknown error";
+    }
+}
+
+const char *lamp_last_error(void) { return g_last_error.c_str(); }
+
+int lamp_version(void) { return 10000; }
+
+size_t lamp_workspace_bytes(int B, int H, int S, int D, int mode, int want_probs)
+{
+    Sizes z;
+    if (check_sizes(B, H, S, D, &z) != LAMP_OK)
+        return 0;
+    if (mode != LAMP_STRICT && mode != LAMP_RELAXED && mode != LAMP_RANDOM)
+        return 0;
+    z.n_valid = 0;
+    z.n_valid = z.BH * (uint64_t)S * (uint64_t)(S + 1) / 2;   // causal-agnostic bound below
+    z.n_valid = z.n_scores > z.n_valid ? z.n_scores : z.n_valid;
+    Needs n{mode == LAMP_RELAXED ? want_probs != 0 : want_probs == 0, true, true, true, true};
+    return plan(z, mode, n).total;
+}
+
+static int run(const float *q, const float *k, const float *v, int B, int H, int S, int D,
+               int causal, int mu, float tau, int mode, float *out, float *probs,
+               uint32_t *mask, lamp_stats *stats, const lamp_params *pp)
+{
+    g_last_error.clear();
+    int rc = check_args(q, k, v, causal, mu, tau, mode, out);
+    if (rc != LAMP_OK)
+        return rc;
+    Sizes z;
+    rc = check_sizes(B, H, S, D, &z);
+    if (rc != LAMP_OK)
+        return rc;
+    if (mode == LAMP_RELAXED && D > 128)
+        return set_error(LAMP_ERR_UNSUPPORTED, "relaxed mode supports D <= 128");
+    z.n_valid = causal ? z.BH * (uint64_t)S * (uint64_t)(S + 1) / 2 : z.n_scores;
+
+    lamp_params none{};
+    const lamp_params &p = pp ? *pp : none;
+    hipStream_t st = (hipStream_t)p.stream;
+    const bool want_stats = stats != nullptr;
+
+    Needs need;
+    need.row_count = p.row_count == nullptr;
+    need.row_kl = p.row_kl == nullptr && want_stats;
+    need.row_kl_lowp = p.row_kl_lowp == nullptr && want_stats;
+    if (mode == LAMP_RELAXED) {
+        need.ymix = probs != nullptr;
+        need.yref = false;
+    } else {
+        need.ymix = p.scores_mix == nullptr && probs == nullptr;
+        need.yref = p.scores_ref == nullptr;
+    }
+    const Layout L = plan(z, mode, need);
+
+    void *ws = nullptr;
+    if (p.workspace) {
+        if (p.workspace_bytes < L.total)
+            return set_error(LAMP_ERR_INVALID_ARG,
+                             "workspace too small: need " + std::to_string(L.total) + " bytes");
+        if (((uintptr_t)p.workspace & (kAlign - 1)) != 0)
+            return set_error(LAMP_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+        ws = p.workspace;
+    } else {
+        rc = pool_get(L.total, &ws);
+        if (rc != LAMP_OK)
+            return rc;
+    }
+
+    lamp::Problem P;
+    P.q = q;
+    P.k = k;
+    P.v = v;
+    P.BH = (int)z.BH;
+    P.S = S;
+    P.D = D;
+    P.causal = causal;
+    P.mu = mu;
+    P.tau = tau;
+    P.pc = lamp::make_ps_const(mu, D);
+    P.tiles = z.tiles;
+    P.n_rows = z.n_rows;
+    P.head_valid = z.n_valid / z.BH;
+
+    auto *dstats = at<lamp::DevStats>(ws, L.dstats);
+    auto *unsafe = at<uint8_t>(ws, L.unsafe);
+    uint32_t *row_count = p.row_count ? p.row_count : at<uint32_t>(ws, L.row_count);
+    double *row_kl = p.row_kl ? p.row_kl : at<double>(ws, L.row_kl);
+    double *row_kl_lowp = p.row_kl_lowp ? p.row_kl_lowp : at<double>(ws, L.row_kl_lowp);
+    StageTimer tm{p.stage_events, st};
+
+    LAMP_HIP_TRY(lamp::launch_zero(dstats, sizeof(lamp::DevStats), st), "zero stats");
+    LAMP_HIP_TRY(tm.begin(LAMP_STAGE_SCAN), "hipEventRecord");
+    LAMP_HIP_TRY(lamp::launch_operand_scan(P, unsafe, st), "operand scan launch");
+    LAMP_HIP_TRY(tm.end(LAMP_STAGE_SCAN), "hipEventRecord");
+
+    if (mode == LAMP_RELAXED) {
+        float *ymix_raw = p.scores_mix ? p.scores_mix : probs;
+        float *row_m = at<float>(ws, L.row_m);
+        double *row_l = at<double>(ws, L.row_l);
+        LAMP_HIP_TRY(tm.begin(LAMP_STAGE_SCORES), "hipEventRecord");
+        LAMP_HIP_TRY(lamp::launch_relaxed(P, unsafe, out, mask, row_count, row_kl, row_kl_lowp,
+                                          ymix_raw, p.scores_ref, row_m, row_l,
+                                          &dstats->n_exact_tiles, st),
+                     "relaxed kernel launch");
+        LAMP_HIP_TRY(tm.end(LAMP_STAGE_SCORES), "hipEventRecord");
+        if (probs) {
+            LAMP_HIP_TRY(tm.begin(LAMP_STAGE_FINISH), "hipEventRecord");
+            LAMP_HIP_TRY(lamp::launch_normalise(P, ymix_raw, row_m, row_l, probs, st),
+                         "normalise launch");
+            LAMP_HIP_TRY(tm.end(LAMP_STAGE_FINISH), "hipEventRecord");
+        }
+    } else {
+        float *ymix = p.scores_mix ? p.scores_mix : (probs ? probs : at<float>(ws, L.ymix));
+        float *yref = p.scores_ref ? p.scores_ref : at<float>(ws, L.yref);
+        uint32_t *list = at<uint32_t>(ws, L.list);
+        LAMP_HIP_TRY(tm.begin(LAMP_STAGE_SCORES), "hipEventRecord");
+        LAMP_HIP_TRY(lamp::launch_ps_scores(P, unsafe, ymix, yref, &dstats->n_exact_tiles, st),
+                     "score kernel launch");
+        LAMP_HIP_TRY(tm.end(LAMP_STAGE_SCORES), "hipEventRecord");
+        LAMP_HIP_TRY(tm.begin(LAMP_STAGE_SELECT), "hipEventRecord");
+        if (mode == LAMP_STRICT) {
+            LAMP_HIP_TRY(lamp::launch_strict_select(P, ymix, yref, mask, list, row_count,
+                                                    row_kl_lowp, 0, st),
+                         "select kernel launch");
+        } else {
+            LAMP_HIP_TRY(lamp::launch_strict_select(P, ymix, yref, nullptr, nullptr, row_count,
+                                                    row_kl_lowp, 1, st),
+                         "count kernel launch");
+            LAMP_HIP_TRY(lamp::launch_random_select(P, p.seed, mask, list, row_count, st),
+                         "random select launch");
+        }
+        LAMP_HIP_TRY(tm.end(LAMP_STAGE_SELECT), "hipEventRecord");
+        LAMP_HIP_TRY(tm.begin(LAMP_STAGE_RECOMPUTE), "hipEventRecord");
+        LAMP_HIP_TRY(lamp::launch_recompute(P, list, row_count, ymix, st), "recompute launch");
+        LAMP_HIP_TRY(tm.end(LAMP_STAGE_RECOMPUTE), "hipEventRecord");
+        LAMP_HIP_TRY(tm.begin(LAMP_STAGE_FINISH), "hipEventRecord");
+        LAMP_HIP_TRY(lamp::launch_finish(P, ymix, yref, probs, out, row_kl, st), "finish launch");
+        LAMP_HIP_TRY(tm.end(LAMP_STAGE_FINISH), "hipEventRecord");
+    }
+
+    if (want_stats) {
+        LAMP_HIP_TRY(tm.begin(LAMP_STAGE_STATS), "hipEventRecord");
+        LAMP_HIP_TRY(lamp::launch_stats(P, row_kl, row_kl_lowp, row_count, dstats, st),
+                     "stats launch");
+        LAMP_HIP_TRY(tm.end(LAMP_STAGE_STATS), "hipEventRecord");
+        lamp::DevStats ds;
+        LAMP_HIP_TRY(hipMemcpyAsync(&ds, dstats, sizeof(ds), hipMemcpyDeviceToHost, st),
+                     "hipMemcpyAsync stats");
+        LAMP_HIP_TRY(hipStreamSynchronize(st), "hipStreamSynchronize");
+        stats->n_rows = z.n_rows;
+        stats->n_valid = z.n_valid;
+        stats->n_selected = ds.n_selected;
+        stats->n_exact_tiles = ds.n_exact_tiles;
+        stats->kl_sum = ds.kl_sum;
+        stats->kl_max = ds.kl_max;
+        stats->kl_lowp_sum = ds.kl_lowp_sum;
+    }
+    return LAMP_OK;
+}
+
+int lamp_attention_fwd_ex(const float *q, const float *k, const float *v, int B, int H, int S,
+                          int D, int causal, int mu, float tau, int mode, float *out, float *probs,
+                          uint32_t *recompute_mask, lamp_stats *stats, const lamp_params *p)
+{
+    try {
+        return run(q, k, v, B, H, S, D, causal, mu, tau, mode, out, probs, recompute_mask, stats, p);
+    } catch (const std::bad_alloc &) {
+        return set_error(LAMP_ERR_NO_MEMORY, "host allocation failed");
+    } catch (...) {
+        return set_error(LAMP_ERR_HIP, "unexpected exception");
+    }
+}
+
+int lamp_attention_fwd(const float *q, const float *k, const float *v, int B, int H, int S, int D,
+                       int causal, int mu, float tau, int mode, float *out, float *probs,
+                       uint32_t *recompute_mask, lamp_stats *stats)
+{
+    return lamp_attention_fwd_ex(q, k, v, B, H, S, D, causal, mu, tau, mode, out, probs,
+                                 recompute_mask, stats, nullptr);
+}
+
+int lamp_ps_scores(const float *q, const float *k, int B, int H, int S, int D, int causal, int mu,
+                   float *ylo, float *yref, void *stream)
+{
+    try {
+        g_last_error.clear();
+        if (!q || !k)
+            return set_error(LAMP_ERR_INVALID_ARG, "q and k are required");
+        if (!ylo && !yref)
+            return set_error(LAMP_ERR_INVALID_ARG, "at least one of ylo, yref is required");
+        if (!aligned16(q) || !aligned16(k))
+            return set_error(LAMP_ERR_INVALID_ARG, "q and k must be 16-byte aligned");
+        if (causal != 0 && causal != 1)
+            return set_error(LAMP_ERR_INVALID_ARG, "causal must be 0 or 1");
+        if (mu < 1 || mu > 23)
+            return set_error(LAMP_ERR_INVALID_ARG, "mu must be in [1, 23]");
+        Sizes z;
+        int rc = check_sizes(B, H, S, D, &z);
+        if (rc != LAMP_OK)
+            return rc;
+        void *ws = nullptr;
+        rc = pool_get(align_up(2 * z.BH * (uint64_t)z.tiles), &ws);
+        if (rc != LAMP_OK)
+            return rc;
+        lamp::Problem P{};
+        P.q = q;
+        P.k = k;
+        P.BH = (int)z.BH;
+        P.S = S;
+        P.D = D;
+        P.causal = causal;
+        P.mu = mu;
+        P.pc = lamp::make_ps_const(mu, D);
+        P.tiles = z.tiles;
+        P.n_rows = z.n_rows;
+        hipStream_t st = (hipStream_t)stream;
+        LAMP_HIP_TRY(lamp::launch_operand_scan(P, (uint8_t *)ws, st), "operand scan launch");
+        LAMP_HIP_TRY(lamp::launch_ps_scores(P, (uint8_t *)ws, ylo, yref, nullptr, st),
+                     "score kernel launch");
+        return LAMP_OK;
+    } catch (...) {
+        return set_error(LAMP_ERR_HIP, "unexpected exception");
+    }
+}
+
+}  // extern "C"

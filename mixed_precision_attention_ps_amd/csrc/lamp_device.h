@@ -1,0 +1,260 @@
+// lamp_device.h -- device helpers shared by the LAMP kernels: PS(mu)
+// arithmetic, the score micro-tile, wave reductions, the SplitMix64 hash.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "lamp_internal.h"
+
+namespace lamp {
+
+// ---------------------------------------------------------------------------
+// PS(mu) arithmetic.  PS(mu) is the custom float of the LAMP summary's
+// "Experimental results" (mu mantissa bits); here: mu stored fraction bits,
+// FP32 exponent range, round to nearest even after every multiply and add.
+//
+// Fast path (mu <= 10, every nonzero operand magnitude in [2^-40, 2^40]):
+//  * product: p = fl(q k) gives the sign and binade of the exact product (up
+//    to a round-up into the next binade, which rounds identically).  With
+//    C = sign(p) * 2^exponent(p) (p's sign and exponent bits), fma(q *
+//    2^(mu-23), k, C) adds the EXACT scaled product to C -- same sign, so the
+//    magnitude stays in C's binade -- and rounds once at C's ulp, which is
+//    the PS(mu) ulp of the scaled product; C is 2^23 ulps (even), so ties go
+//    to even.  r = fma(...) - C is exact (Sterbenz).  Cost: mul, and, fma, sub.
+//  * sum: s = fl(acc + r) of two PS(mu) values, then RNE of s's bits to mu
+//    fraction bits; double rounding through FP32 is innocuous for
+//    24 >= 2(mu+1)+1, i.e. mu <= 10.  Cost: add, bfe, add3, and.
+//  The accumulator lives in the scaled domain (x 2^(mu-23)); rounding to a
+//  number of significant bits commutes with power-of-two scaling while
+//  values stay normal, which the operand range guarantees.
+// Exact path (any input, any mu): products exact in double, RN_mu in double
+// with FP32 range; double add then RN_mu (53 >= 2*24+2).
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float ps_round_bits(float x, uint32_t sh, uint32_t half_m1,
+                                               uint32_t keep)
+{
+    uint32_t u = __float_as_uint(x);
+    u = (u + ((u >> sh) & 1u) + half_m1) & keep;
+    return __uint_as_float(u);
+}
+
+// One fast-path multiply-accumulate of PS(mu) (scaled domain) and of the
+// sequential FP32 reference, sharing the FP32 product.
+__device__ __forceinline__ void ps_mac_fast(float q, float qs, float k, float &acc_s,
+                                            float &acc_r, uint32_t sh, uint32_t half_m1,
+                                            uint32_t keep)
+{
+    float p = q * k;
+    float C = __uint_as_float(__float_as_uint(p) & 0xff800000u);
+    float t = __builtin_fmaf(qs, k, C);
+    float r = t - C;
+    float s = acc_s + r;
+    acc_s = ps_round_bits(s, sh, half_m1, keep);
+    acc_r = acc_r + p;
+}
+
+// RN_mu of a double with FP32 exponent range (exact path).
+__device__ __forceinline__ double ps_rn64(double x, int mu)
+{
+    if (x == 0.0 || !isfinite(x))
+        return x;
+    int b = ilogb(x);
+    b = b < -126 ? -126 : b;
+    double r = ldexp(rint(ldexp(x, mu - b)), b - mu);
+    if (fabs(r) >= 0x1p128)
+        r = copysign(__builtin_inf(), x);
+    return r;
+}
+
+// ---------------------------------------------------------------------------
+// Score micro-tile.  A work-group owns a 64 x 64 tile (64 query rows, 64
+// keys); thread (ty = tid / 16, tx = tid % 16) owns rows ty*4 + r and keys
+// tx + 16*c (r, c in 0..3).  The head dimension is staged through LDS in
+// 16-wide slices: sQ / sQs hold q and q * 2^(mu-23) as [d][row]; sK holds k as
+// [d][slot] with key j in slot (j % 16) * 4 + j / 16, so that each thread
+// reads its four keys as one 16-byte LDS load.
+// ---------------------------------------------------------------------------
+enum { PATH_FAST = 0, PATH_EXACT = 1, PATH_FP32 = 2 };
+
+struct TileSmem {
+    float q[kDChunk][kTile];
+    float qs[kDChunk][kTile];
+    float k[kDChunk][kTile];
+};
+
+struct TileAcc {
+    float lo[4][4];     // fast path: scaled-domain PS accumulator
+    double lod[4][4];   // exact path: PS accumulator in double
+    float ref[4][4];    // sequential FP32 accumulator
+};
+
+__device__ __forceinline__ int key_slot(int j) { return (j & 15) * 4 + (j >> 4); }
+
+// Global -> register slice loads: thread loads row (tid >> 2), d offset
+// (tid & 3) * 4 of the Q and K blocks.  Rows past S and d past D read 0.
+__device__ __forceinline__ float4 load_slice(const float *base, int row, int nrows, int D, int d)
+{
+    if (row < nrows && d < D)
+        return *reinterpret_cast<const float4 *>(base + (size_t)row * D + d);
+    return make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+template <int PATH>
+__device__ __forceinline__ void stage_slice(TileSmem &sm, float4 qv, float4 kv, int tid,
+                                            float qscale)
+{
+    const int row = tid >> 2, d = (tid & 3) * 4;
+    const float qa[4] = {qv.x, qv.y, qv.z, qv.w};
+    const float ka[4] = {kv.x, kv.y, kv.z, kv.w};
+    const int slot = key_slot(row);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        sm.q[d + e][row] = qa[e];
+        if (PATH == PATH_FAST)
+            sm.qs[d + e][row] = qa[e] * qscale;
+        sm.k[d + e][slot] = ka[e];
+    }
+}
+
+template <int PATH>
+__device__ __forceinline__ void compute_slice(const TileSmem &sm, TileAcc &acc, int tx, int ty,
+                                              const PsConst &pc)
+{
+#pragma unroll
+    for (int dd = 0; dd < kDChunk; ++dd) {
+        const float4 qv = *reinterpret_cast<const float4 *>(&sm.q[dd][ty * 4]);
+        const float4 kv = *reinterpret_cast<const float4 *>(&sm.k[dd][tx * 4]);
+        const float qa[4] = {qv.x, qv.y, qv.z, qv.w};
+        const float ka[4] = {kv.x, kv.y, kv.z, kv.w};
+        if (PATH == PATH_FAST) {
+            const float4 sv = *reinterpret_cast<const float4 *>(&sm.qs[dd][ty * 4]);
+            const float sa[4] = {sv.x, sv.y, sv.z, sv.w};
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    ps_mac_fast(qa[r], sa[r], ka[c], acc.lo[r][c], acc.ref[r][c], pc.sh,
+                                pc.half_m1, pc.keep);
+        } else if (PATH == PATH_EXACT) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    double t = (double)qa[r] * (double)ka[c];
+                    acc.lod[r][c] = ps_rn64(acc.lod[r][c] + ps_rn64(t, pc.mu), pc.mu);
+                    float p = qa[r] * ka[c];
+                    acc.ref[r][c] = acc.ref[r][c] + p;
+                }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    float p = qa[r] * ka[c];
+                    acc.ref[r][c] = acc.ref[r][c] + p;
+                }
+        }
+    }
+}
+
+// Full-D accumulation of one 64x64 tile: rows row0.., keys col0.. of one head.
+template <int PATH>
+__device__ __forceinline__ void score_tile(TileSmem &sm, TileAcc &acc, const float *Qh,
+                                           const float *Kh, int row0, int col0, int S, int D,
+                                           const PsConst &pc)
+{
+    const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            acc.lo[r][c] = 0.0f;
+            acc.lod[r][c] = 0.0;
+            acc.ref[r][c] = 0.0f;
+        }
+    const int lrow = tid >> 2, ld = (tid & 3) * 4;
+    const float *Qb = Qh + (size_t)row0 * D;
+    const float *Kb = Kh + (size_t)col0 * D;
+    const int qrows = S - row0, krows = S - col0;
+    float4 qv = load_slice(Qb, lrow, qrows, D, ld);
+    float4 kv = load_slice(Kb, lrow, krows, D, ld);
+    for (int d0 = 0; d0 < D; d0 += kDChunk) {
+        __syncthreads();
+        stage_slice<PATH>(sm, qv, kv, tid, pc.qscale);
+        __syncthreads();
+        if (d0 + kDChunk < D) {
+            qv = load_slice(Qb, lrow, qrows, D, d0 + kDChunk + ld);
+            kv = load_slice(Kb, lrow, krows, D, d0 + kDChunk + ld);
+        }
+        compute_slice<PATH>(sm, acc, tx, ty, pc);
+    }
+}
+
+// Final scaled scores of the micro-tile.
+template <int PATH>
+__device__ __forceinline__ void tile_scores(const TileAcc &acc, const PsConst &pc, float lo[4][4],
+                                            float ref[4][4])
+{
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            ref[r][c] = acc.ref[r][c] * pc.s;
+            if (PATH == PATH_FAST)
+                lo[r][c] = acc.lo[r][c] * pc.out_scale;
+            else if (PATH == PATH_EXACT)
+                lo[r][c] = (float)acc.lod[r][c] * pc.s;
+            else
+                lo[r][c] = ref[r][c];
+        }
+}
+
+// ---------------------------------------------------------------------------
+// Wave reductions (wave64).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_max(float v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+__device__ __forceinline__ double wave_sum(double v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+__device__ __forceinline__ int wave_sum_int(int v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// Lanes below this one whose bit is set in `mask`.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask)
+{
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// SplitMix64 output for a state (Steele, Lea & Flood, OOPSLA 2014): add the
+// golden gamma, then two xor-shift-multiply mixing rounds and a final
+// xor-shift.
+__device__ __forceinline__ uint64_t splitmix64(uint64_t x)
+{
+    uint64_t z = x + 0x9e3779b97f4a7c15ull;
+    z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
+    z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
+    return z ^ (z >> 31);
+}
+
+}  // namespace lamp

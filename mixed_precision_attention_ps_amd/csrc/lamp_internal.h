@@ -1,0 +1,101 @@
+// lamp_internal.h -- launch-level interface between the C ABI (lamp_api.cpp)
+// and the HIP kernels.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lamp {
+
+constexpr int kTile = 64;        // query rows and keys per score tile
+constexpr int kDChunk = 16;      // head-dimension slice staged in LDS at a time
+constexpr int kThreads = 256;    // threads per work-group (4 wave64)
+
+// Per-launch constants of the PS(mu) arithmetic.
+struct PsConst {
+    int mu;
+    uint32_t sh;        // 23 - mu: fraction bits dropped
+    uint32_t half_m1;   // 2^(sh-1) - 1
+    uint32_t keep;      // mask clearing the dropped bits
+    float qscale;       // 2^(mu-23): scaled operand of the product fma
+    float out_scale;    // s * 2^(23-mu): scale of the scaled-domain accumulator
+    float s;            // FP32 value nearest to 1/sqrt(D)
+};
+
+PsConst make_ps_const(int mu, int D);
+
+struct Problem {
+    const float *q, *k, *v;
+    int BH, S, D, causal, mu;
+    float tau;
+    PsConst pc;
+    int tiles;            // ceil(S / 64)
+    uint64_t n_rows;      // BH * S
+    uint64_t head_valid;  // valid pairs per head
+};
+
+// Operand range scan: unsafe[bh * tiles + t] = 1 when a 64-row block of Q
+// (first BH*tiles entries) or K (next BH*tiles entries) holds a value outside
+// {0} U [2^-40, 2^40] (including inf / nan).
+hipError_t launch_operand_scan(const Problem &p, uint8_t *unsafe, hipStream_t st);
+
+// PS(mu) and FP32 scores of every valid pair into dense [BH, S, S] buffers.
+hipError_t launch_ps_scores(const Problem &p, const uint8_t *unsafe, float *ylo, float *yref,
+                            unsigned long long *exact_tiles, hipStream_t st);
+
+// Strict row softmax + selection.  count_only: write row_count only (random
+// mode); otherwise mask words (if non-null), the per-row compacted index
+// segments in `list` and row_count.  Optional KL(P_ref || P_lowp) per row
+// when yref and row_kl_lowp are non-null (reads y^lo before recompute).
+hipError_t launch_strict_select(const Problem &p, const float *ylo, const float *yref,
+                                uint32_t *mask, uint32_t *list, uint32_t *row_count,
+                                double *row_kl_lowp, int count_only, hipStream_t st);
+
+// Random control: per row, row_count[r] keys with the smallest hashes.
+hipError_t launch_random_select(const Problem &p, uint64_t seed, uint32_t *mask, uint32_t *list,
+                                const uint32_t *row_count, hipStream_t st);
+
+// Gather FP32 recompute of the listed scores, scattered into ymix.
+hipError_t launch_recompute(const Problem &p, const uint32_t *list, const uint32_t *row_count,
+                            float *ymix, hipStream_t st);
+
+// Final softmax (probs may alias ymix), P.V on MFMA, row KL.
+hipError_t launch_finish(const Problem &p, const float *ymix, const float *yref, float *probs,
+                         float *out, double *row_kl, hipStream_t st);
+
+// Relaxed fused one-pass kernel.  ymix_raw: if non-null, y^mix of valid
+// entries is written there (for the probs pass / inspection); row_m / row_l:
+// per-row final max and sum of the online softmax (for the probs pass).
+hipError_t launch_relaxed(const Problem &p, const uint8_t *unsafe, float *out, uint32_t *mask,
+                          uint32_t *row_count, double *row_kl, double *row_kl_lowp,
+                          float *ymix_raw, float *yref_out, float *row_m, double *row_l,
+                          unsigned long long *exact_tiles, hipStream_t st);
+
+// probs[r][j] = exp(ymix[r][j] - row_m[r]) / row_l[r] on valid keys, 0 elsewhere.
+hipError_t launch_normalise(const Problem &p, const float *ymix, const float *row_m,
+                            const double *row_l, float *probs, hipStream_t st);
+
+// Device-side summary.
+struct DevStats {
+    unsigned long long n_selected;
+    unsigned long long n_exact_tiles;
+    double kl_sum, kl_max, kl_lowp_sum;
+};
+
+hipError_t launch_stats(const Problem &p, const double *row_kl, const double *row_kl_lowp,
+                        const uint32_t *row_count, DevStats *ds, hipStream_t st);
+
+// Zero `bytes` (a multiple of 4) with a fill kernel.
+hipError_t launch_zero(void *ptr, size_t bytes, hipStream_t st);
+
+// Start offset of row r's segment in the compacted index list: the number of
+// valid pairs in all earlier rows.
+__host__ __device__ inline uint64_t row_segment(uint64_t r, int S, int causal)
+{
+    uint64_t bh = r / (uint64_t)S, i = r % (uint64_t)S;
+    if (causal)
+        return bh * ((uint64_t)S * (S + 1) / 2) + i * (i + 1) / 2;
+    return r * (uint64_t)S;
+}
+
+}  // namespace lamp

@@ -1,0 +1,179 @@
+// scores.hip -- operand range scan and the PS(mu) / FP32 score tile kernel.
+//
+// Step 1 of LAMP ("Implementation strategy": baseline evaluation at low
+// precision), with the uniform FP32 reference scores of "Experimental
+// results" computed in the same pass from the same FP32 products.
+#include "lamp_device.h"
+
+namespace lamp {
+
+PsConst make_ps_const(int mu, int D)
+{
+    PsConst c;
+    c.mu = mu;
+    c.sh = (uint32_t)(23 - mu);
+    c.half_m1 = c.sh ? (1u << (c.sh - 1)) - 1u : 0u;
+    c.keep = ~((1u << c.sh) - 1u);
+    c.qscale = ldexpf(1.0f, mu - 23);
+    c.s = (float)(1.0 / sqrt((double)D));
+    c.out_scale = ldexpf(c.s, 23 - mu);
+    return c;
+}
+
+// Safe operand: zero, or a finite magnitude in [2^-40, 2^40].
+__device__ __forceinline__ bool operand_safe(float x)
+{
+    uint32_t a = __float_as_uint(x) & 0x7fffffffu;
+    const uint32_t lo = 0x2b800000u;   // 2^-40
+    const uint32_t hi = 0x53800000u;   // 2^40
+    return a == 0u || (a - lo) <= (hi - lo);
+}
+
+// One work-group per 64-row block of Q or K: flag = block holds an unsafe value.
+__global__ __launch_bounds__(kThreads) void operand_scan_kernel(const float *__restrict__ q,
+                                                                const float *__restrict__ k,
+                                                                int BH, int S, int D, int tiles,
+                                                                uint8_t *__restrict__ unsafe)
+{
+    const int blk = blockIdx.x;                  // [0, 2 * BH * tiles)
+    const int which = blk / (BH * tiles);
+    const int rem = blk % (BH * tiles);
+    const int bh = rem / tiles, t = rem % tiles;
+    const float *base = (which == 0 ? q : k) + ((size_t)bh * S + (size_t)t * kTile) * D;
+    const int rows = min(kTile, S - t * kTile);
+    const int n4 = rows * D / 4;
+    bool ok = true;
+    for (int e = threadIdx.x; e < n4; e += kThreads) {
+        float4 v = reinterpret_cast<const float4 *>(base)[e];
+        ok = ok && operand_safe(v.x) && operand_safe(v.y) && operand_safe(v.z) && operand_safe(v.w);
+    }
+    const int all_ok = __syncthreads_and(ok ? 1 : 0);
+    if (threadIdx.x == 0)
+        unsafe[blk] = all_ok ? 0 : 1;
+}
+
+hipError_t launch_operand_scan(const Problem &p, uint8_t *unsafe, hipStream_t st)
+{
+    const int grid = 2 * p.BH * p.tiles;
+    hipLaunchKernelGGL(operand_scan_kernel, dim3(grid), dim3(kThreads), 0, st, p.q, p.k, p.BH,
+                       p.S, p.D, p.tiles, unsafe);
+    return hipGetLastError();
+}
+
+// Tile (ti, tj) of tile index t within a head: the lower triangle (tj <= ti)
+// in row order when causal, the full square otherwise.
+__device__ __forceinline__ void tile_coords(int t, int tiles, int causal, int &ti, int &tj)
+{
+    if (causal) {
+        int a = (int)((sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
+        while ((a + 1) * (a + 2) / 2 <= t) ++a;
+        while (a * (a + 1) / 2 > t) --a;
+        ti = a;
+        tj = t - a * (a + 1) / 2;
+    } else {
+        ti = t / tiles;
+        tj = t % tiles;
+    }
+}
+
+struct ScoreArgs {
+    const float *q, *k;
+    int S, D, causal, tiles, tiles_per_head;
+    PsConst pc;
+    const uint8_t *unsafe_q, *unsafe_k;
+    float *ylo, *yref;
+    unsigned long long *exact_tiles;
+};
+
+template <int PATH>
+__device__ __forceinline__ void score_tile_store(TileSmem &sm, const ScoreArgs &a, int bh, int ti,
+                                                 int tj)
+{
+    const size_t head = (size_t)bh * a.S * a.D;
+    TileAcc acc;
+    score_tile<PATH>(sm, acc, a.q + head, a.k + head, ti * kTile, tj * kTile, a.S, a.D, a.pc);
+    float lo[4][4], ref[4][4];
+    tile_scores<PATH>(acc, a.pc, lo, ref);
+    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int i = ti * kTile + ty * 4 + r;
+        if (i >= a.S)
+            continue;
+        const size_t rowoff = ((size_t)bh * a.S + i) * a.S;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int j = tj * kTile + tx + 16 * c;
+            if (j >= a.S || (a.causal && j > i))
+                continue;
+            if (a.ylo)
+                a.ylo[rowoff + j] = lo[r][c];
+            if (a.yref)
+                a.yref[rowoff + j] = ref[r][c];
+        }
+    }
+}
+
+// Two kernels share the tile grid: the fast kernel takes the tiles whose
+// operands allow the FP32 fast path (and returns on the others); the generic
+// kernel takes every other tile (exact double path, or plain FP32 at mu = 23).
+// Keeping the exact path out of the fast kernel keeps its register budget,
+// and so its occupancy, to what the fast path needs.
+template <bool FAST_KERNEL>
+__global__ __launch_bounds__(kThreads) void ps_scores_kernel(ScoreArgs a)
+{
+    __shared__ TileSmem sm;
+    const int bh = blockIdx.x / a.tiles_per_head;
+    const int t = blockIdx.x % a.tiles_per_head;
+    int ti, tj;
+    tile_coords(t, a.tiles, a.causal, ti, tj);
+    int path;
+    if (a.pc.mu == 23)
+        path = PATH_FP32;
+    else if (a.pc.mu <= 10 && !a.unsafe_q[bh * a.tiles + ti] && !a.unsafe_k[bh * a.tiles + tj])
+        path = PATH_FAST;
+    else
+        path = PATH_EXACT;
+    if (FAST_KERNEL) {
+        if (path == PATH_FAST)
+            score_tile_store<PATH_FAST>(sm, a, bh, ti, tj);
+    } else if (path == PATH_EXACT) {
+        if (threadIdx.x == 0 && a.exact_tiles)
+            atomicAdd(a.exact_tiles, 1ull);
+        score_tile_store<PATH_EXACT>(sm, a, bh, ti, tj);
+    } else if (path == PATH_FP32) {
+        score_tile_store<PATH_FP32>(sm, a, bh, ti, tj);
+    }
+}
+
+hipError_t launch_ps_scores(const Problem &p, const uint8_t *unsafe, float *ylo, float *yref,
+                            unsigned long long *exact_tiles, hipStream_t st)
+{
+    ScoreArgs a;
+    a.q = p.q;
+    a.k = p.k;
+    a.S = p.S;
+    a.D = p.D;
+    a.causal = p.causal;
+    a.tiles = p.tiles;
+    a.tiles_per_head = p.causal ? p.tiles * (p.tiles + 1) / 2 : p.tiles * p.tiles;
+    a.pc = p.pc;
+    a.unsafe_q = unsafe;
+    a.unsafe_k = unsafe + (size_t)p.BH * p.tiles;
+    a.ylo = ylo;
+    a.yref = yref;
+    a.exact_tiles = exact_tiles;
+    const long long grid = (long long)p.BH * a.tiles_per_head;
+    if (grid > 0x7fffffffLL)
+        return hipErrorInvalidValue;
+    if (p.mu <= 10) {
+        hipLaunchKernelGGL(ps_scores_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, st, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    hipLaunchKernelGGL(ps_scores_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace lamp

@@ -1,0 +1,197 @@
+"""Python binding of the LAMP C ABI (include/lamp.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``liblamp.so``.  Tensors are torch CUDA (ROCm) float32 tensors,
+used for their device pointers; work is enqueued on torch's current stream.
+The library must be built (``__graft_entry__.build()``); loading fails loudly
+otherwise -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LAMP_STRICT, LAMP_RELAXED, LAMP_RANDOM = 0, 1, 2
+MODES = {"strict": LAMP_STRICT, "relaxed": LAMP_RELAXED, "random": LAMP_RANDOM}
+LAMP_OK, LAMP_ERR_INVALID_ARG, LAMP_ERR_UNSUPPORTED, LAMP_ERR_HIP, LAMP_ERR_NO_MEMORY = 0, -1, -2, -3, -4
+STAGES = ("scan", "scores", "select", "recompute", "finish", "stats")
+LAMP_N_STAGES = len(STAGES)
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblamp.so")
+
+
+class LampStats(ctypes.Structure):
+    _fields_ = [("n_rows", ctypes.c_uint64), ("n_valid", ctypes.c_uint64),
+                ("n_selected", ctypes.c_uint64), ("n_exact_tiles", ctypes.c_uint64),
+                ("kl_sum", ctypes.c_double), ("kl_max", ctypes.c_double),
+                ("kl_lowp_sum", ctypes.c_double)]
+
+    def as_dict(self):
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+class LampParams(ctypes.Structure):
+    _fields_ = [("stream", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t), ("seed", ctypes.c_uint64),
+                ("row_kl", ctypes.c_void_p), ("row_kl_lowp", ctypes.c_void_p),
+                ("row_count", ctypes.c_void_p), ("scores_mix", ctypes.c_void_p),
+                ("scores_ref", ctypes.c_void_p), ("stage_events", ctypes.c_void_p)]
+
+
+class LampError(RuntimeError):
+    def __init__(self, code: int, detail: str):
+        self.code = code
+        super().__init__(f"LAMP error {code}: {detail}")
+
+
+_lib = None
+
+
+def library():
+    """Load liblamp.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    fwd_args = [P, P, P, I, I, I, I, I, I, F, I, P, P, P, ctypes.POINTER(LampStats)]
+    lib.lamp_attention_fwd.restype = I
+    lib.lamp_attention_fwd.argtypes = fwd_args
+    lib.lamp_attention_fwd_ex.restype = I
+    lib.lamp_attention_fwd_ex.argtypes = fwd_args + [ctypes.POINTER(LampParams)]
+    lib.lamp_workspace_bytes.restype = ctypes.c_size_t
+    lib.lamp_workspace_bytes.argtypes = [I, I, I, I, I, I]
+    lib.lamp_ps_scores.restype = I
+    lib.lamp_ps_scores.argtypes = [P, P, I, I, I, I, I, I, P, P, P]
+    lib.lamp_strerror.restype = ctypes.c_char_p
+    lib.lamp_strerror.argtypes = [I]
+    lib.lamp_last_error.restype = ctypes.c_char_p
+    lib.lamp_last_error.argtypes = []
+    lib.lamp_version.restype = I
+    lib.lamp_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def _check(rc: int):
+    if rc != LAMP_OK:
+        lib = library()
+        detail = (lib.lamp_last_error() or b"").decode() or lib.lamp_strerror(rc).decode()
+        raise LampError(rc, detail)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch tensor")
+    if t.device.type != "cuda" or not t.is_contiguous():
+        raise ValueError("tensors must be contiguous device tensors")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _f32(t, name):
+    if t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32")
+    return _ptr(t)
+
+
+def lamp_workspace_bytes(B, H, S, D, mode, want_probs) -> int:
+    return int(library().lamp_workspace_bytes(B, H, S, D, MODES.get(mode, mode), int(want_probs)))
+
+
+def lamp_ps_scores(q, k, *, causal: bool, mu: int, ylo=None, yref=None):
+    """Step 1 alone: PS(mu) scores and FP32 scores into [B,H,S,S] buffers."""
+    B, H, S, D = q.shape
+    if ylo is None and yref is None:
+        ylo = torch.empty((B, H, S, S), device=q.device, dtype=torch.float32)
+        yref = torch.empty_like(ylo)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(q.device).cuda_stream)
+    _check(library().lamp_ps_scores(_f32(q, "q"), _f32(k, "k"), B, H, S, D, int(causal), int(mu),
+                                    _ptr(ylo), _ptr(yref), stream))
+    return ylo, yref
+
+
+def lamp_attention_fwd(q, k, v, *, causal: bool, mu: int, tau: float, mode="strict", out=None,
+                       probs=None, recompute_mask=None, want_stats: bool = True, seed: int = 0,
+                       row_kl=None, row_kl_lowp=None, row_count=None, scores_mix=None,
+                       scores_ref=None, workspace=None, stage_events=None):
+    """LAMP attention forward through lamp_attention_fwd_ex.
+
+    q, k, v: float32 [B, H, S, D] device tensors.  Optional outputs are written
+    in place when given.  Returns (out, stats_dict_or_None).
+    """
+    B, H, S, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    m = MODES.get(mode, mode)
+    p = LampParams()
+    p.stream = torch.cuda.current_stream(q.device).cuda_stream
+    p.seed = seed & 0xFFFFFFFFFFFFFFFF
+    if workspace is not None:
+        p.workspace = workspace.data_ptr()
+        p.workspace_bytes = workspace.numel() * workspace.element_size()
+    for name, t in (("row_kl", row_kl), ("row_kl_lowp", row_kl_lowp), ("row_count", row_count),
+                    ("scores_mix", scores_mix), ("scores_ref", scores_ref)):
+        if t is not None:
+            setattr(p, name, _ptr(t).value)
+    if stage_events is not None:   # a HipEvents of 2 * LAMP_N_STAGES handles
+        p.stage_events = stage_events.address
+    st = LampStats() if want_stats else None
+    mask_ptr = None
+    if recompute_mask is not None:
+        if recompute_mask.dtype not in (torch.int32, torch.uint32):
+            raise TypeError("recompute_mask must be a 32-bit integer tensor")
+        mask_ptr = _ptr(recompute_mask)
+    _check(library().lamp_attention_fwd_ex(
+        _f32(q, "q"), _f32(k, "k"), _f32(v, "v"), B, H, S, D, int(causal), int(mu),
+        ctypes.c_float(tau), int(m), _f32(out, "out"),
+        None if probs is None else _f32(probs, "probs"), mask_ptr,
+        ctypes.byref(st) if st is not None else None, ctypes.byref(p)))
+    return out, (st.as_dict() if st is not None else None)
+
+
+class HipEvents:
+    """hipEvent_t handles for lamp_params.stage_events, via the HIP runtime.
+
+    torch's Event objects create their handle lazily and only see torch's
+    streams; the library records these on the stream it was given.
+    """
+
+    def __init__(self, n: int):
+        self._hip = ctypes.CDLL("libamdhip64.so")
+        self._hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                  ctypes.c_void_p]
+        self._hip.hipEventQuery.argtypes = [ctypes.c_void_p]
+        self._hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.handles = []
+        for _ in range(n):
+            h = ctypes.c_void_p()
+            if self._hip.hipEventCreate(ctypes.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.handles.append(h)
+        self.array = (ctypes.c_void_p * n)(*[h.value for h in self.handles])
+
+    @property
+    def address(self) -> int:
+        return ctypes.cast(self.array, ctypes.c_void_p).value
+
+    def recorded(self, i: int) -> bool:
+        return self._hip.hipEventQuery(self.handles[i]) == 0
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        t = ctypes.c_float()
+        rc = self._hip.hipEventElapsedTime(ctypes.byref(t), self.handles[a], self.handles[b])
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(t.value)
+
+    def close(self):
+        for h in self.handles:
+            self._hip.hipEventDestroy(h)
+        self.handles = []

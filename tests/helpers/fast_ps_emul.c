@@ -1,12 +1,13 @@
 /* Scalar CPU emulation of the FP32 instruction sequence the HIP kernels use
  * for PS(mu) arithmetic (test code, checked against the oracle):
  *
- *   product  p = fl(q*k); C = 1.5 * 2^exponent(p) (exponent bits of p OR'd
- *            with the top fraction bit); r_s = fma(q_s, k, C) - C, where
- *            q_s = q * 2^(mu-23).  The fma adds the exact scaled product to
- *            C with one rounding at C's ulp, which is the PS(mu) ulp of the
- *            product scaled by 2^(mu-23); C's ulp-count is even, so ties go to
- *            even.  Result: RN_mu(q*k) * 2^(mu-23), exactly.
+ *   product  p = fl(q*k); C = sign(p) * 2^exponent(p) (sign and exponent
+ *            bits of p); r_s = fma(q_s, k, C) - C, where q_s = q * 2^(mu-23).
+ *            The fma adds the exact scaled product to C (same sign, so the
+ *            magnitude stays in C's binade) with one rounding at C's ulp,
+ *            which is the PS(mu) ulp of the product scaled by 2^(mu-23); C is
+ *            2^23 ulps (even), so ties go to even.  Result: RN_mu(q*k) *
+ *            2^(mu-23), exactly.
  *   sum      s = fl(acc_s + r_s), then integer RNE of s's bits to mu fraction
  *            bits (innocuous double rounding for mu <= 10).
  *   score    fl(acc_s * (scale * 2^(23-mu))).
@@ -26,7 +27,7 @@ float emu_prod_scaled(float q, float k, int mu)
 {
     float qs = ldexpf(q, mu - 23);
     float p = q * k;
-    float C = bf((fb(p) & 0x7f800000u) | 0x00400000u);
+    float C = bf(fb(p) & 0xff800000u);
     float t = fmaf(qs, k, C);
     return t - C;
 }

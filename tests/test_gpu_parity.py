@@ -1,0 +1,257 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Every input is seeded and synthetic (mixed_precision_attention_ps_amd.inputs).
+Scores, y^mix, masks and counts must match bit for bit; probabilities,
+outputs and KL within the tolerances stated in tests/parity.py.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+from mixed_precision_attention_ps_amd.configs import WORKLOADS
+from mixed_precision_attention_ps_amd.inputs import make_qkv, make_special
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+STRICT, RELAXED, RANDOM = 0, 1, 2
+MODE_NAME = {STRICT: "strict", RELAXED: "relaxed", RANDOM: "random"}
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    from mixed_precision_attention_ps_amd import lamp
+    lamp.library()
+    return torch.device("cuda:0")
+
+
+def note(msg):
+    print(f"[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def run_gpu(dev, Q, K, V, *, causal, mu, tau, mode, seed=0, want_probs=True, want_mask=True):
+    import torch
+    from mixed_precision_attention_ps_amd import lamp
+    B, H, S, D = Q.shape
+    q, k, v = (torch.from_numpy(x).to(dev) for x in (Q, K, V))
+    W = (S + 31) // 32
+    probs = torch.full((B, H, S, S), -7.0, device=dev) if want_probs else None
+    mask = torch.full((B, H, S, W), -1, dtype=torch.int32, device=dev) if want_mask else None
+    row_kl = torch.zeros((B, H, S), dtype=torch.float64, device=dev)
+    row_kl_lowp = torch.zeros((B, H, S), dtype=torch.float64, device=dev)
+    row_count = torch.zeros((B, H, S), dtype=torch.int32, device=dev)
+    ymix = torch.zeros((B, H, S, S), device=dev)
+    yref = torch.zeros((B, H, S, S), device=dev)
+    note(f"gpu {MODE_NAME[mode]} B={B} H={H} S={S} D={D} causal={causal} mu={mu} tau={tau}")
+    out, st = lamp.lamp_attention_fwd(q, k, v, causal=causal, mu=mu, tau=tau, mode=mode,
+                                      probs=probs, recompute_mask=mask, seed=seed, row_kl=row_kl,
+                                      row_kl_lowp=row_kl_lowp, row_count=row_count,
+                                      scores_mix=ymix, scores_ref=yref)
+    torch.cuda.synchronize()
+    res = {"out": out.cpu().numpy(), "row_kl": row_kl.cpu().numpy(),
+           "row_kl_lowp": row_kl_lowp.cpu().numpy(), "row_count": row_count.cpu().numpy(),
+           "ymix": ymix.cpu().numpy(), "yref": yref.cpu().numpy(), "stats": st}
+    if want_probs:
+        res["probs"] = probs.cpu().numpy()
+    if want_mask:
+        res["mask"] = mask.cpu().numpy().view(np.uint32)
+    return res
+
+
+def run_orc(orc, Q, K, V, *, causal, mu, tau, mode, seed=0, heads=None, rows=None):
+    note(f"oracle {MODE_NAME[mode]} shape={Q.shape} heads={heads} rows={rows}")
+    return orc.lamp_heads(Q, K, V, causal=causal, mu=mu, tau=tau, mode=mode, seed=seed,
+                          heads=heads, rows=rows)
+
+
+def ymix_oracle(r, S):
+    sel = parity.unpack_mask(r["mask"], S)
+    return np.where(sel, r["yref"], r["ylo"])
+
+
+def compare_full(g, r, Q, V, *, causal, tau, heads=None, rows=None, check_probs=True):
+    """Compare GPU results (full [B,H,S,...]) against oracle results on the
+    oracle's heads and rows."""
+    B, H, S, D = Q.shape
+    heads = list(range(B * H)) if heads is None else list(heads)
+    rb, re_ = (0, S) if rows is None else rows
+    sl = slice(rb, re_)
+    valid = parity.valid_mask(S, causal, (rb, re_))[None].repeat(len(heads), 0)
+    gv = lambda name: g[name].reshape((B * H,) + g[name].shape[2:])[heads][:, sl]
+    parity.assert_bits(gv("yref"), r["yref"], valid, "FP32 reference scores")
+    parity.assert_bits(gv("ymix"), ymix_oracle(r, S), valid, "mixed scores")
+    ties = parity.assert_mask(gv("mask"), r["mask"], r["crit"], tau, S)
+    assert (gv("row_count") == r["count"]).all() or ties > 0, "row counts"
+    if check_probs:
+        parity.assert_tol(gv("probs"), r["probs"], np.abs(r["probs"]), "probs")
+    Vf = V.reshape(B * H, S, D)
+    scale = np.stack([parity.out_scale(r["probs"][n].astype(np.float64), Vf[h])
+                      for n, h in enumerate(heads)])
+    parity.assert_tol(gv("out"), r["out"], scale, "out")
+    parity.assert_tol(gv("row_kl"), r["kl"], np.abs(r["kl"]), "row KL")
+    parity.assert_tol(gv("row_kl_lowp"), r["kl_lowp"], np.abs(r["kl_lowp"]), "row KL lowp")
+    return ties
+
+
+# ---------------------------------------------------------------------------
+# Step 1: scores
+# ---------------------------------------------------------------------------
+SCORE_CASES = [
+    (1, 1, 128, 64, False, 4), (1, 2, 200, 64, True, 4), (1, 1, 1, 64, True, 4),
+    (1, 1, 2, 64, False, 4), (1, 1, 63, 64, True, 4), (1, 1, 64, 64, False, 4),
+    (1, 1, 65, 64, True, 4), (1, 1, 127, 64, False, 4), (2, 1, 70, 4, True, 4),
+    (1, 1, 70, 8, False, 4), (1, 1, 70, 20, True, 7), (1, 1, 70, 128, True, 4),
+    (1, 1, 70, 256, False, 10), (1, 1, 96, 64, True, 1), (1, 1, 96, 64, True, 2),
+    (1, 1, 96, 64, True, 7), (1, 1, 96, 64, True, 10), (1, 1, 96, 64, True, 11),
+    (1, 1, 96, 64, True, 16), (1, 1, 96, 64, True, 22), (1, 1, 96, 64, True, 23),
+]
+
+
+@pytest.mark.parametrize("B,H,S,D,causal,mu", SCORE_CASES)
+def test_scores_bitexact(dev, orc, B, H, S, D, causal, mu):
+    import torch
+    from mixed_precision_attention_ps_amd import lamp
+    Q, K, V, _ = make_qkv(B, H, S, D, n_outlier=min(2, D // 4), seed=S * 7 + D + mu)
+    note(f"scores B={B} H={H} S={S} D={D} causal={causal} mu={mu}")
+    q, k = torch.from_numpy(Q).to(dev), torch.from_numpy(K).to(dev)
+    ylo, yref = lamp.lamp_ps_scores(q, k, causal=causal, mu=mu)
+    torch.cuda.synchronize()
+    r = orc.lamp_heads(Q, K, V, causal=causal, mu=mu, tau=np.inf, mode=STRICT,
+                       want=("ylo", "yref"))
+    valid = parity.valid_mask(S, causal)[None].repeat(B * H, 0)
+    parity.assert_bits(ylo.cpu().numpy().reshape(B * H, S, S), r["ylo"], valid, "PS scores")
+    parity.assert_bits(yref.cpu().numpy().reshape(B * H, S, S), r["yref"], valid, "FP32 scores")
+
+
+@pytest.mark.parametrize("kind", ["tiny", "huge", "mixed", "nonfinite"])
+@pytest.mark.parametrize("mu", [4, 10])
+def test_scores_special_values(dev, orc, kind, mu):
+    """Inputs outside the fast path's operand range take the exact path."""
+    import torch
+    from mixed_precision_attention_ps_amd import lamp
+    B, H, S, D = 1, 2, 130, 64
+    Q, K, V = make_special(B, H, S, D, kind=kind, seed=mu)
+    note(f"special scores kind={kind} mu={mu}")
+    q, k = torch.from_numpy(Q).to(dev), torch.from_numpy(K).to(dev)
+    ylo, yref = lamp.lamp_ps_scores(q, k, causal=True, mu=mu)
+    torch.cuda.synchronize()
+    with np.errstate(all="ignore"):
+        r = orc.lamp_heads(Q, K, V, causal=True, mu=mu, tau=np.inf, mode=STRICT,
+                           want=("ylo", "yref"))
+    valid = parity.valid_mask(S, True)[None].repeat(B * H, 0)
+    parity.assert_bits(ylo.cpu().numpy().reshape(B * H, S, S), r["ylo"], valid, "PS scores")
+    parity.assert_bits(yref.cpu().numpy().reshape(B * H, S, S), r["yref"], valid, "FP32 scores")
+
+
+# ---------------------------------------------------------------------------
+# The whole strict / random path
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("tau", [1e-1, 1e-2, 1e-3])
+def test_strict_single_head(dev, orc, tau):
+    w = WORKLOADS["single_head_s128"]
+    Q, K, V, _ = w.qkv()
+    g = run_gpu(dev, Q, K, V, causal=False, mu=4, tau=tau, mode=STRICT)
+    r = run_orc(orc, Q, K, V, causal=False, mu=4, tau=tau, mode=STRICT)
+    ties = compare_full(g, r, Q, V, causal=False, tau=tau)
+    assert ties == 0
+    st = g["stats"]
+    assert st["n_selected"] == r["count"].sum() and st["n_valid"] == 128 * 128
+    assert abs(st["kl_sum"] - r["kl"].sum()) <= 1e-6 * r["kl"].sum() + 1e-7
+
+
+@pytest.fixture(scope="module")
+def gpt2_small():
+    return WORKLOADS["gpt2_small_s1024"].qkv()[:3]
+
+
+@pytest.mark.parametrize("tau", [1e-1, 1e-2, 1e-3, 1e-4])
+def test_strict_gpt2_small(dev, orc, gpt2_small, tau):
+    Q, K, V = gpt2_small
+    g = run_gpu(dev, Q, K, V, causal=True, mu=4, tau=tau, mode=STRICT)
+    r = run_orc(orc, Q, K, V, causal=True, mu=4, tau=tau, mode=STRICT)
+    compare_full(g, r, Q, V, causal=True, tau=tau)
+    assert g["stats"]["n_selected"] == r["count"].sum()
+
+
+def test_random_control_gpt2_small(dev, orc, gpt2_small):
+    Q, K, V = gpt2_small
+    tau = 1e-2
+    g = run_gpu(dev, Q, K, V, causal=True, mu=4, tau=tau, mode=RANDOM, seed=1234)
+    r = run_orc(orc, Q, K, V, causal=True, mu=4, tau=tau, mode=RANDOM, seed=1234)
+    S = Q.shape[2]
+    gm = g["mask"].reshape(-1, S, (S + 31) // 32)
+    assert (gm == r["mask"]).all(), "random-control masks"
+    compare_full(g, r, Q, V, causal=True, tau=np.inf)
+    # the adaptive selection beats the random one at the same per-row counts
+    st = run_gpu(dev, Q, K, V, causal=True, mu=4, tau=tau, mode=STRICT)
+    assert (st["row_count"] == g["row_count"]).all()
+    assert st["row_kl"].mean() <= g["row_kl"].mean() / 2
+
+
+@pytest.mark.parametrize("tau", [0.0, np.inf])
+def test_tau_limits(dev, orc, tau):
+    Q, K, V, _ = make_qkv(1, 2, 160, 64, n_outlier=2, seed=21)
+    g = run_gpu(dev, Q, K, V, causal=True, mu=4, tau=tau, mode=STRICT)
+    r = run_orc(orc, Q, K, V, causal=True, mu=4, tau=tau, mode=STRICT)
+    compare_full(g, r, Q, V, causal=True, tau=tau)
+    if np.isinf(tau):
+        assert g["row_count"].sum() == 0
+        np.testing.assert_array_equal(g["row_kl"], g["row_kl_lowp"])
+
+
+def test_strict_special_inputs(dev, orc):
+    """Zeros, tiny and huge operands in the full path (exact-path tiles)."""
+    Q, K, V = make_special(1, 2, 150, 64, kind="mixed", seed=3)
+    g = run_gpu(dev, Q, K, V, causal=True, mu=4, tau=1e-2, mode=STRICT)
+    r = run_orc(orc, Q, K, V, causal=True, mu=4, tau=1e-2, mode=STRICT)
+    compare_full(g, r, Q, V, causal=True, tau=1e-2)
+    assert g["stats"]["n_exact_tiles"] > 0
+
+
+def test_determinism(dev, gpt2_small):
+    Q, K, V = gpt2_small
+    a = run_gpu(dev, Q, K, V, causal=True, mu=4, tau=1e-2, mode=STRICT)
+    b = run_gpu(dev, Q, K, V, causal=True, mu=4, tau=1e-2, mode=STRICT)
+    for name in ("mask", "ymix", "yref", "row_count", "probs", "out", "row_kl"):
+        assert np.array_equal(a[name].view(np.uint8), b[name].view(np.uint8)), name
+
+
+# ---------------------------------------------------------------------------
+# Relaxed one-pass path
+# ---------------------------------------------------------------------------
+RELAXED_CASES = [
+    (1, 2, 256, 64, True, 4, 1e-2), (1, 1, 200, 64, False, 4, 1e-2),
+    (1, 1, 130, 128, True, 4, 1e-2), (1, 1, 100, 64, True, 23, 1e-3),
+    (1, 1, 100, 64, True, 11, 1e-3), (1, 1, 1, 64, True, 4, 0.0), (1, 1, 70, 8, False, 7, 1e-1),
+]
+
+
+@pytest.mark.parametrize("B,H,S,D,causal,mu,tau", RELAXED_CASES)
+def test_relaxed_small(dev, orc, B, H, S, D, causal, mu, tau):
+    Q, K, V, _ = make_qkv(B, H, S, D, n_outlier=min(2, D // 4), seed=S + D)
+    g = run_gpu(dev, Q, K, V, causal=causal, mu=mu, tau=tau, mode=RELAXED)
+    r = run_orc(orc, Q, K, V, causal=causal, mu=mu, tau=tau, mode=RELAXED)
+    compare_full(g, r, Q, V, causal=causal, tau=tau)
+
+
+def test_relaxed_special_inputs(dev, orc):
+    Q, K, V = make_special(1, 1, 140, 64, kind="mixed", seed=9)
+    g = run_gpu(dev, Q, K, V, causal=True, mu=4, tau=1e-2, mode=RELAXED)
+    r = run_orc(orc, Q, K, V, causal=True, mu=4, tau=1e-2, mode=RELAXED)
+    compare_full(g, r, Q, V, causal=True, tau=1e-2)
+    assert g["stats"]["n_exact_tiles"] > 0
+
+
+def test_relaxed_superset_of_strict(dev, gpt2_small):
+    Q, K, V = gpt2_small
+    st = run_gpu(dev, Q, K, V, causal=True, mu=4, tau=1e-2, mode=STRICT)
+    rl = run_gpu(dev, Q, K, V, causal=True, mu=4, tau=1e-2, mode=RELAXED)
+    S = Q.shape[2]
+    a = parity.unpack_mask(st["mask"], S)
+    b = parity.unpack_mask(rl["mask"], S)
+    assert not (a & ~b).any()
