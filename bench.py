@@ -1,0 +1,222 @@
+#!/usr/bin/env python3
+"""Benchmark: LAMP attention forward on one MI355X.
+
+One step = one lamp_attention_fwd call over the whole hot path (PS(mu) and
+FP32 score tiles, look-ahead selection + compaction, gather FP32 recompute,
+softmax + P.V + row KL), inputs resident in HBM, outputs preallocated, probs,
+recompute mask and row KL written.  Default workload: the GPT-2-XL-shaped
+layer (B=8, H=25, S=1024, D=64, causal, 2 outlier channels x8), strict LAMP,
+mu=4, tau calibrated on the oracle to ~1.6% recompute.
+
+Prints one JSON line with throughput (valid query-key scores per second),
+the dominant kernel's ALU roofline (achieved vs peak lane-operation rate,
+timed live with HIP events around that kernel's stage), and the CPU oracle
+timed on this host on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--mode strict|relaxed|random]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "LAMP attention scores/sec at μ=4 (GPT-2-XL layer) + % VALU/HBM roofline"
+
+# MI355X: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz lane-operation slots per second.
+ALU_PEAK = 256 * 4 * 16 * 2.4e9
+HBM_PEAK = 8.0e12
+
+KERNEL_SOURCES = ["lamp_device.h", "lamp_internal.h", "scores.hip", "select.hip", "finish.hip",
+                  "relaxed.hip"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "mixed_precision_attention_ps_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, workload: str, launches_per_step: int = 1):
+    """HBM bytes per launch from the committed PMC summary, if it was taken on
+    the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        tab = json.load(f)
+    ent = tab.get(f"{kernel}/{workload}")
+    if not ent or ent.get("source_sha") != kernel_source_sha():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(Q, K, V, w, mode_id, mu, tau, heads_n, seed):
+    import numpy as np
+    import oracle
+    oracle.build(force=False)
+    BH = w.B * w.H
+    heads = sorted(set(int(x) for x in np.linspace(0, BH - 1, heads_n)))
+    threads = oracle.max_threads()
+    per_head = w.S * (w.S + 1) // 2 if w.causal else w.S * w.S
+    t0 = time.perf_counter()
+    oracle.lamp_heads(Q, K, V, causal=w.causal, mu=mu, tau=tau, mode=mode_id, heads=heads,
+                      seed=seed, want=("out", "kl", "count", "mask", "probs"))
+    dt = time.perf_counter() - t0
+    n = per_head * len(heads)
+    return {"value": n / dt, "unit": "scores/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(heads)} of {BH} heads (all rows) of {w.name}, same mu/tau/mode; "
+                      f"{n} valid scores in {dt:.2f} s wall, {threads} OpenMP threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gpt2_xl_layer")
+    ap.add_argument("--mode", default="strict", choices=["strict", "relaxed", "random"])
+    ap.add_argument("--mu", type=int, default=4)
+    ap.add_argument("--rate", type=float, default=0.016, help="target recompute rate (tau table)")
+    ap.add_argument("--tau", type=float, default=None, help="explicit tau (overrides --rate)")
+    ap.add_argument("--no-probs", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=24)
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="run a plain copy of this many MiB first (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this LAMP build shards nothing across GPUs "
+              "(each (batch, head) is independent; see DESIGN.md for how it would shard). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from mixed_precision_attention_ps_amd import lamp
+    from mixed_precision_attention_ps_amd.configs import WORKLOADS, tau_for
+
+    w = WORKLOADS[args.workload]
+    mode_id = lamp.MODES[args.mode]
+    tau_mode = "strict" if args.mode == "random" else args.mode
+    tau = args.tau if args.tau is not None else tau_for(w.name, tau_mode, args.mu, args.rate)
+    dev = torch.device("cuda:0")
+    log(f"[bench] {w.name} mode={args.mode} mu={args.mu} tau={tau}")
+
+    Q, K, V, _ = w.qkv()
+    q, k, v = (torch.from_numpy(x).to(dev) for x in (Q, K, V))
+    B, H, S, D = w.B, w.H, w.S, w.D
+    W32 = (S + 31) // 32
+    out = torch.empty_like(q)
+    probs = None if args.no_probs else torch.empty((B, H, S, S), device=dev)
+    mask = torch.empty((B, H, S, W32), dtype=torch.int32, device=dev)
+    row_kl = torch.empty((B, H, S), dtype=torch.float64, device=dev)
+
+    if args.copy_calib_mib:
+        n = args.copy_calib_mib * (1 << 20) // 4
+        a = torch.ones(n, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    def step(events=None):
+        lamp.lamp_attention_fwd(q, k, v, causal=w.causal, mu=args.mu, tau=tau, mode=mode_id,
+                                out=out, probs=probs, recompute_mask=mask, want_stats=False,
+                                row_kl=row_kl, stage_events=events)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev = [lamp.HipEvents(2 * lamp.LAMP_N_STAGES) for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    t_start.record()
+    for s in range(args.steps):
+        step(ev[s])
+    t_stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = t_start.elapsed_time(t_stop)
+
+    stages = {}
+    for si, name in enumerate(lamp.STAGES):
+        if ev[0].recorded(2 * si) and ev[0].recorded(2 * si + 1):
+            try:
+                stages[name] = sum(e.elapsed_ms(2 * si, 2 * si + 1) for e in ev) / args.steps
+            except RuntimeError:
+                pass
+    for e in ev:
+        e.close()
+
+    # untimed: rate and KL of the same call
+    _, st = lamp.lamp_attention_fwd(q, k, v, causal=w.causal, mu=args.mu, tau=tau, mode=mode_id,
+                                    out=out, probs=probs, recompute_mask=mask, want_stats=True)
+    n_valid = st["n_valid"]
+    rate = st["n_selected"] / n_valid
+    ms_per_step = 1e3 * wall / args.steps
+    value = n_valid / (wall / args.steps)
+
+    # dominant kernel: the PS(mu)+FP32 score tiles (strict, random) or the fused
+    # relaxed kernel; algorithmic VALU slots per valid score: 8D (PS(mu) dot:
+    # multiply, add, two 3-instruction roundings per MAC) + D (FP32 reference
+    # dot at two lanes per slot) [+ 20 for the fused softmax/criterion/KL].
+    kname = "relaxed_kernel" if args.mode == "relaxed" else "ps_scores_kernel"
+    w_alg = 9 * D + (20 if args.mode == "relaxed" else 0)
+    t_kernel_ms = stages.get("scores")
+    achieved = w_alg * n_valid / (t_kernel_ms * 1e-3) if t_kernel_ms else None
+    traffic = load_traffic(kname, w.name)
+    roofline = {"bound": "alu", "kernel": kname,
+                "achieved": achieved / 1e12 if achieved else None,
+                "peak": ALU_PEAK / 1e12, "unit": "Tlane-op/s",
+                "frac": achieved / ALU_PEAK if achieved else None,
+                "traffic": traffic, "kernel_ms": t_kernel_ms,
+                "slots_per_score": w_alg}
+    # whole path against the same peak (8D + D + 20 + 2 r D per score) and HBM
+    w_path = 9 * D + 20 + 2 * rate * D
+    hbm_bytes = (0 if args.no_probs else 4) + 1 / 8 + 32 * D / (S + 1)
+    rec = {
+        "metric": METRIC, "value": value, "unit": "scores/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "H": H, "S": S, "D": D, "causal": w.causal,
+                   "mu": args.mu, "mode": args.mode, "tau": tau, "target_rate": args.rate,
+                   "rate": rate, "probs": not args.no_probs, "mask": True, "row_kl": True,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": roofline,
+        "path_alu_frac": w_path * value / ALU_PEAK,
+        "path_hbm_frac": hbm_bytes * value / HBM_PEAK,
+        "gpu_ms_per_step": gpu_ms / args.steps,
+        "stages_ms": stages,
+        "kl_mean": st["kl_sum"] / st["n_rows"],
+        "kl_lowp_mean": st["kl_lowp_sum"] / st["n_rows"],
+        "kl_reduction": (st["kl_lowp_sum"] / st["kl_sum"]) if st["kl_sum"] > 0 else None,
+        "exact_tiles": st["n_exact_tiles"],
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample")
+        rec["cpu_baseline"] = cpu_baseline(Q, K, V, w, mode_id, args.mu, tau, args.cpu_heads, 0)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -102,14 +102,17 @@ typedef struct {
 /* Stages, for lamp_params.stage_events. */
 enum {
     LAMP_STAGE_SCAN = 0,      /* operand range scan (fast/exact path choice)  */
-    LAMP_STAGE_SCORES = 1,    /* PS(mu) + FP32 score tiles (strict, random);
-                                 the fused one-pass kernel (relaxed)          */
+    LAMP_STAGE_SCORES = 1,    /* PS(mu) + FP32 score tiles on the FP32 fast
+                                 path (strict, random); the fused one-pass
+                                 kernel on the fast path (relaxed)            */
     LAMP_STAGE_SELECT = 2,    /* row softmax + selection + compaction         */
     LAMP_STAGE_RECOMPUTE = 3, /* gather FP32 recompute + scatter              */
     LAMP_STAGE_FINISH = 4,    /* softmax, probs, P.V, KL (strict, random);
                                  probs normalise pass (relaxed)               */
     LAMP_STAGE_STATS = 5,     /* row reductions into lamp_stats               */
-    LAMP_N_STAGES = 6
+    LAMP_STAGE_EXACT = 6,     /* score tiles / query blocks outside the FP32
+                                 fast path (exact double path; FP32 at mu=23) */
+    LAMP_N_STAGES = 7
 };
 
 /*

@@ -56,5 +56,22 @@ WORKLOADS = {
     ]
 }
 
-# Filled by oracle/calibrate_tau.py: {(workload, mode, mu, target_rate): tau}.
-TAU_FOR_RATE: dict = {}
+def _load_tau_table() -> dict:
+    import json
+    import os
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "tau_table.json")
+    if not os.path.exists(path):
+        return {}
+    with open(path) as f:
+        return json.load(f)
+
+
+# Written by oracle/calibrate_tau.py: "workload/mode/mu<m>/rate<r>" -> {"tau": ...}.
+TAU_TABLE: dict = _load_tau_table()
+
+
+def tau_for(workload: str, mode: str, mu: int, rate: float) -> float:
+    key = f"{workload}/{mode}/mu{mu}/rate{rate}"
+    if key not in TAU_TABLE:
+        raise KeyError(f"no calibrated tau for {key}; run oracle/calibrate_tau.py")
+    return float(TAU_TABLE[key]["tau"])

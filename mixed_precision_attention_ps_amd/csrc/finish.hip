@@ -1,4 +1,5 @@
-// finish.hip -- final softmax over the mixed scores, P.V on MFMA, row-wise
+// finish.hip -- final softmax over the mixed scores, P.V on MFMA (FP64
+// accumulation), row-wise
 // KL(P_FP32 || P_LAMP), and the row reductions into the summary.
 //
 // "Implementation strategy" step 3 of the LAMP summary ends with "then apply
@@ -10,7 +11,7 @@
 
 namespace lamp {
 
-typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef double doublex4 __attribute__((ext_vector_type(4)));
 
 constexpr int kFinRows = 16;   // query rows per work-group (one MFMA row block)
 constexpr int kFinKeys = 64;   // keys per P.V step
@@ -87,10 +88,12 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(FinishArgs a)
     const double invl = s_invl[prow];
     const int nkeys = a.causal ? min(S, row0 + kFinRows) : S;   // keys this block attends
     const int nb = Dv / 16;                                      // 16-wide column blocks
-    floatx4 acc[4];
+    // P.V accumulates in double on the FP64 MFMA: FP32 accumulation over
+    // hundreds of keys drifts by ~10 ulp of a dominant term, beyond 1e-6.
+    doublex4 acc[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-        acc[q] = floatx4{0.f, 0.f, 0.f, 0.f};
+        acc[q] = doublex4{0.0, 0.0, 0.0, 0.0};
     const size_t vhead = (size_t)bh * S * D;
 
     for (int j0 = 0; j0 < S; j0 += kFinKeys) {
@@ -127,7 +130,8 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(FinishArgs a)
                         const int cb = wave + 4 * q;
                         if (cb * 16 >= h && cb * 16 < h + Dc) {
                             const float bv = sV[(kk * 4 + (lane >> 4)) * Dc + cb * 16 - h + (lane & 15)];
-                            acc[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc[q], 0, 0, 0);
+                            acc[q] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)av, (double)bv,
+                                                                          acc[q], 0, 0, 0);
                         }
                     }
                 }
@@ -149,7 +153,7 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(FinishArgs a)
         for (int v = 0; v < 4; ++v) {
             const int i = row0 + 4 * (lane >> 4) + v;
             if (i < S)
-                a.out[((size_t)bh * S + i) * D + col] = acc[q][v];
+                a.out[((size_t)bh * S + i) * D + col] = (float)acc[q][v];
         }
     }
 }

@@ -301,10 +301,16 @@ static int run(const float *q, const float *k, const float *v, int B, int H, int
         float *ymix_raw = p.scores_mix ? p.scores_mix : probs;
         float *row_m = at<float>(ws, L.row_m);
         double *row_l = at<double>(ws, L.row_l);
+        LAMP_HIP_TRY(tm.begin(LAMP_STAGE_EXACT), "hipEventRecord");
+        LAMP_HIP_TRY(lamp::launch_relaxed(P, unsafe, out, mask, row_count, row_kl, row_kl_lowp,
+                                          ymix_raw, p.scores_ref, row_m, row_l,
+                                          &dstats->n_exact_tiles, false, st),
+                     "relaxed kernel launch");
+        LAMP_HIP_TRY(tm.end(LAMP_STAGE_EXACT), "hipEventRecord");
         LAMP_HIP_TRY(tm.begin(LAMP_STAGE_SCORES), "hipEventRecord");
         LAMP_HIP_TRY(lamp::launch_relaxed(P, unsafe, out, mask, row_count, row_kl, row_kl_lowp,
                                           ymix_raw, p.scores_ref, row_m, row_l,
-                                          &dstats->n_exact_tiles, st),
+                                          &dstats->n_exact_tiles, true, st),
                      "relaxed kernel launch");
         LAMP_HIP_TRY(tm.end(LAMP_STAGE_SCORES), "hipEventRecord");
         if (probs) {
@@ -317,8 +323,12 @@ static int run(const float *q, const float *k, const float *v, int B, int H, int
         float *ymix = p.scores_mix ? p.scores_mix : (probs ? probs : at<float>(ws, L.ymix));
         float *yref = p.scores_ref ? p.scores_ref : at<float>(ws, L.yref);
         uint32_t *list = at<uint32_t>(ws, L.list);
+        LAMP_HIP_TRY(tm.begin(LAMP_STAGE_EXACT), "hipEventRecord");
+        LAMP_HIP_TRY(lamp::launch_ps_scores(P, unsafe, ymix, yref, &dstats->n_exact_tiles, false, st),
+                     "score kernel launch");
+        LAMP_HIP_TRY(tm.end(LAMP_STAGE_EXACT), "hipEventRecord");
         LAMP_HIP_TRY(tm.begin(LAMP_STAGE_SCORES), "hipEventRecord");
-        LAMP_HIP_TRY(lamp::launch_ps_scores(P, unsafe, ymix, yref, &dstats->n_exact_tiles, st),
+        LAMP_HIP_TRY(lamp::launch_ps_scores(P, unsafe, ymix, yref, &dstats->n_exact_tiles, true, st),
                      "score kernel launch");
         LAMP_HIP_TRY(tm.end(LAMP_STAGE_SCORES), "hipEventRecord");
         LAMP_HIP_TRY(tm.begin(LAMP_STAGE_SELECT), "hipEventRecord");
@@ -419,7 +429,9 @@ int lamp_ps_scores(const float *q, const float *k, int B, int H, int S, int D, i
         P.n_rows = z.n_rows;
         hipStream_t st = (hipStream_t)stream;
         LAMP_HIP_TRY(lamp::launch_operand_scan(P, (uint8_t *)ws, st), "operand scan launch");
-        LAMP_HIP_TRY(lamp::launch_ps_scores(P, (uint8_t *)ws, ylo, yref, nullptr, st),
+        LAMP_HIP_TRY(lamp::launch_ps_scores(P, (uint8_t *)ws, ylo, yref, nullptr, false, st),
+                     "score kernel launch");
+        LAMP_HIP_TRY(lamp::launch_ps_scores(P, (uint8_t *)ws, ylo, yref, nullptr, true, st),
                      "score kernel launch");
         return LAMP_OK;
     } catch (...) {

@@ -40,8 +40,10 @@ struct Problem {
 hipError_t launch_operand_scan(const Problem &p, uint8_t *unsafe, hipStream_t st);
 
 // PS(mu) and FP32 scores of every valid pair into dense [BH, S, S] buffers.
+// fast = true: the tiles on the FP32 fast path (launches nothing if mu > 10);
+// fast = false: every other tile.
 hipError_t launch_ps_scores(const Problem &p, const uint8_t *unsafe, float *ylo, float *yref,
-                            unsigned long long *exact_tiles, hipStream_t st);
+                            unsigned long long *exact_tiles, bool fast, hipStream_t st);
 
 // Strict row softmax + selection.  count_only: write row_count only (random
 // mode); otherwise mask words (if non-null), the per-row compacted index
@@ -66,10 +68,12 @@ hipError_t launch_finish(const Problem &p, const float *ymix, const float *yref,
 // Relaxed fused one-pass kernel.  ymix_raw: if non-null, y^mix of valid
 // entries is written there (for the probs pass / inspection); row_m / row_l:
 // per-row final max and sum of the online softmax (for the probs pass).
+// fast = true: query blocks whose every visited tile is on the FP32 fast
+// path; fast = false: the other query blocks.
 hipError_t launch_relaxed(const Problem &p, const uint8_t *unsafe, float *out, uint32_t *mask,
                           uint32_t *row_count, double *row_kl, double *row_kl_lowp,
                           float *ymix_raw, float *yref_out, float *row_m, double *row_l,
-                          unsigned long long *exact_tiles, hipStream_t st);
+                          unsigned long long *exact_tiles, bool fast, hipStream_t st);
 
 // probs[r][j] = exp(ymix[r][j] - row_m[r]) / row_l[r] on valid keys, 0 elsewhere.
 hipError_t launch_normalise(const Problem &p, const float *ymix, const float *row_m,

@@ -21,7 +21,7 @@
 
 namespace lamp {
 
-typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef double doublex4 __attribute__((ext_vector_type(4)));
 
 struct RelaxedArgs {
     const float *q, *k, *v;
@@ -118,10 +118,12 @@ __global__ __launch_bounds__(kThreads) void relaxed_kernel(RelaxedArgs a)
         cnt[r] = 0;
     }
     const int nb = Dv / 16;   // <= NB column blocks of 16
-    floatx4 acc[NB];
+    // P.V accumulators (FP64 MFMA: FP32 accumulation over long rows drifts
+    // beyond the 1e-6 bar)
+    doublex4 acc[NB];
 #pragma unroll
     for (int q = 0; q < NB; ++q)
-        acc[q] = floatx4{0.f, 0.f, 0.f, 0.f};
+        acc[q] = doublex4{0.0, 0.0, 0.0, 0.0};
 
     for (int t = 0; t <= t_end; ++t) {
         const int col0 = t * kTile;
@@ -232,10 +234,9 @@ __global__ __launch_bounds__(kThreads) void relaxed_kernel(RelaxedArgs a)
             m_mix[r] = (i < S) ? mm_new : m_mix[r];
             m_ref[r] = (i < S) ? mr_new : m_ref[r];
             // rescale this row's P.V accumulators (MFMA rows 4*(lane/16)+r)
-            const float af = (float)alpha;
 #pragma unroll
             for (int q = 0; q < NB; ++q)
-                acc[q][r] *= af;
+                acc[q][r] *= alpha;
 
             if (want_lowp) {
                 bl = group16_max(bl);
@@ -283,7 +284,8 @@ __global__ __launch_bounds__(kThreads) void relaxed_kernel(RelaxedArgs a)
                 for (int q = 0; q < NB; ++q) {
                     if (q < nb && q * 16 >= h && q * 16 < h + Dc) {
                         const float bv = sm.v[(kk * 4 + (lane >> 4)) * Dc + q * 16 - h + (lane & 15)];
-                        acc[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc[q], 0, 0, 0);
+                        acc[q] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)av, (double)bv,
+                                                                      acc[q], 0, 0, 0);
                     }
                 }
             }
@@ -323,14 +325,14 @@ __global__ __launch_bounds__(kThreads) void relaxed_kernel(RelaxedArgs a)
                 a.row_l[row] = lm;
         }
         // out rows of this lane's MFMA accumulators are 4*(lane/16)+r = ty*4+r
-        const float inv = (float)(1.0 / lm);
+        const double inv = 1.0 / lm;
 #pragma unroll
         for (int q = 0; q < NB; ++q) {
             if (q >= nb)
                 continue;
             const int col = q * 16 + (lane & 15);
             if (col < D)
-                a.out[row * (uint64_t)D + col] = acc[q][r] * inv;
+                a.out[row * (uint64_t)D + col] = (float)(acc[q][r] * inv);
         }
     }
 }
@@ -338,7 +340,7 @@ __global__ __launch_bounds__(kThreads) void relaxed_kernel(RelaxedArgs a)
 hipError_t launch_relaxed(const Problem &p, const uint8_t *unsafe, float *out, uint32_t *mask,
                           uint32_t *row_count, double *row_kl, double *row_kl_lowp,
                           float *ymix_raw, float *yref_out, float *row_m, double *row_l,
-                          unsigned long long *exact_tiles, hipStream_t st)
+                          unsigned long long *exact_tiles, bool fast, hipStream_t st)
 {
     if (p.D > 128)
         return hipErrorInvalidValue;   // the fused kernel keeps <= 8 MFMA column blocks
@@ -368,14 +370,14 @@ hipError_t launch_relaxed(const Problem &p, const uint8_t *unsafe, float *out, u
     a.row_l = row_l;
     a.exact_tiles = exact_tiles;
     const uint64_t grid = (uint64_t)p.BH * p.tiles;
-    if (p.mu <= 10) {
+    if (fast) {
+        if (p.mu > 10)
+            return hipSuccess;
         if (a.Dv <= 64)
             hipLaunchKernelGGL((relaxed_kernel<4, true>), dim3((unsigned)grid), dim3(kThreads), 0, st, a);
         else
             hipLaunchKernelGGL((relaxed_kernel<8, true>), dim3((unsigned)grid), dim3(kThreads), 0, st, a);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess)
-            return e;
+        return hipGetLastError();
     }
     if (a.Dv <= 64)
         hipLaunchKernelGGL((relaxed_kernel<4, false>), dim3((unsigned)grid), dim3(kThreads), 0, st, a);

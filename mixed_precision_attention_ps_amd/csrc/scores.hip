@@ -147,7 +147,7 @@ __global__ __launch_bounds__(kThreads) void ps_scores_kernel(ScoreArgs a)
 }
 
 hipError_t launch_ps_scores(const Problem &p, const uint8_t *unsafe, float *ylo, float *yref,
-                            unsigned long long *exact_tiles, hipStream_t st)
+                            unsigned long long *exact_tiles, bool fast, hipStream_t st)
 {
     ScoreArgs a;
     a.q = p.q;
@@ -166,13 +166,12 @@ hipError_t launch_ps_scores(const Problem &p, const uint8_t *unsafe, float *ylo,
     const long long grid = (long long)p.BH * a.tiles_per_head;
     if (grid > 0x7fffffffLL)
         return hipErrorInvalidValue;
-    if (p.mu <= 10) {
-        hipLaunchKernelGGL(ps_scores_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, st, a);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess)
-            return e;
+    if (fast) {
+        if (p.mu <= 10)
+            hipLaunchKernelGGL(ps_scores_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, st, a);
+    } else {
+        hipLaunchKernelGGL(ps_scores_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, st, a);
     }
-    hipLaunchKernelGGL(ps_scores_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, st, a);
     return hipGetLastError();
 }
 

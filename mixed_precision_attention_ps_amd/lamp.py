@@ -16,7 +16,7 @@ import torch
 LAMP_STRICT, LAMP_RELAXED, LAMP_RANDOM = 0, 1, 2
 MODES = {"strict": LAMP_STRICT, "relaxed": LAMP_RELAXED, "random": LAMP_RANDOM}
 LAMP_OK, LAMP_ERR_INVALID_ARG, LAMP_ERR_UNSUPPORTED, LAMP_ERR_HIP, LAMP_ERR_NO_MEMORY = 0, -1, -2, -3, -4
-STAGES = ("scan", "scores", "select", "recompute", "finish", "stats")
+STAGES = ("scan", "scores", "select", "recompute", "finish", "stats", "exact")
 LAMP_N_STAGES = len(STAGES)
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblamp.so")

@@ -1,0 +1,82 @@
+"""Find thresholds tau that hit target recompute rates, on the CPU oracle.
+
+Writes mixed_precision_attention_ps_amd/tau_table.json.  Only the oracle and
+the seeded input generator are used.  For each workload and mode the oracle's
+criterion values (strict: 2 z (1 - z) |y^lo|; relaxed: 2 exp(y^lo - m_t)
+|y^lo|) are collected over a sample of heads (and rows), and tau is the FP32
+value at which the fraction of valid scores whose criterion exceeds tau is the
+target rate.  The thresholds are inputs of the benchmark; the rate a run
+actually reaches is measured by that run.
+
+Usage: python oracle/calibrate_tau.py
+"""
+from __future__ import annotations
+
+import json
+import os
+import sys
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+sys.path.insert(0, ROOT)
+
+import oracle  # noqa: E402
+from mixed_precision_attention_ps_amd.configs import WORKLOADS  # noqa: E402
+
+OUT = os.path.join(ROOT, "mixed_precision_attention_ps_amd", "tau_table.json")
+RATES = (0.003, 0.016, 0.076)
+
+
+def tau_for_rate(crit: np.ndarray, rate: float) -> float:
+    c = np.sort(crit)[::-1]
+    k = int(round(rate * c.size))
+    k = min(max(k, 1), c.size - 1)
+    tau = np.float32(0.5 * (c[k - 1] + c[k]))   # between the k-th and (k+1)-th largest
+    return float(tau)
+
+
+def collect(w, mode, mu, heads, row_ranges):
+    Q, K, V, _ = w.qkv()
+    parts = []
+    for rows in row_ranges:
+        r = oracle.lamp_heads(Q, K, V, causal=w.causal, mu=mu, tau=np.inf, mode=mode, heads=heads,
+                              rows=rows, want=("crit",))
+        S = w.S
+        rb, re_ = rows
+        i = np.arange(rb, re_)[:, None]
+        valid = (np.arange(S)[None, :] <= i) if w.causal else np.ones((re_ - rb, S), bool)
+        parts.append(r["crit"][:, valid])
+    return np.concatenate([p.ravel() for p in parts])
+
+
+def main():
+    table = {}
+    w = WORKLOADS["gpt2_xl_layer"]
+    heads = [0, 33, 66, 99, 133, 166, 199]
+    for mode_name, mode in (("strict", oracle.STRICT), ("relaxed", oracle.RELAXED)):
+        for mu in w.mus:
+            crit = collect(w, mode, mu, heads, [(0, w.S)])
+            for rate in RATES:
+                tau = tau_for_rate(crit, rate)
+                table[f"{w.name}/{mode_name}/mu{mu}/rate{rate}"] = {
+                    "tau": tau, "sample_rate": float((crit > np.float32(tau)).mean()),
+                    "sample": f"heads {heads}, all rows"}
+                print(w.name, mode_name, mu, rate, tau, flush=True)
+    w = WORKLOADS["long_context_s16384"]
+    rows = [(0, 64), (4096, 4160), (8192, 8256), (12288, 12352), (16320, 16384)]
+    for mode_name, mode in (("relaxed", oracle.RELAXED), ("strict", oracle.STRICT)):
+        crit = collect(w, mode, 4, [0, 31], rows)
+        tau = tau_for_rate(crit, 0.016)
+        table[f"{w.name}/{mode_name}/mu4/rate0.016"] = {
+            "tau": tau, "sample_rate": float((crit > np.float32(tau)).mean()),
+            "sample": f"heads [0, 31], rows {rows}"}
+        print(w.name, mode_name, tau, flush=True)
+    with open(OUT, "w") as f:
+        json.dump(table, f, indent=1, sort_keys=True)
+    print("wrote", OUT)
+
+
+if __name__ == "__main__":
+    main()

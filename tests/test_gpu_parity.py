@@ -201,7 +201,8 @@ def test_tau_limits(dev, orc, tau):
     compare_full(g, r, Q, V, causal=True, tau=tau)
     if np.isinf(tau):
         assert g["row_count"].sum() == 0
-        np.testing.assert_array_equal(g["row_kl"], g["row_kl_lowp"])
+        # two kernels sum the same terms in different orders
+        np.testing.assert_allclose(g["row_kl"], g["row_kl_lowp"], rtol=1e-10, atol=1e-14)
 
 
 def test_strict_special_inputs(dev, orc):
