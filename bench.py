@@ -29,8 +29,12 @@ sys.path.insert(0, ROOT)
 
 METRIC = "LAMP attention scores/sec at μ=4 (GPT-2-XL layer) + % VALU/HBM roofline"
 
-# MI355X: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz lane-operation slots per second.
-ALU_PEAK = 256 * 4 * 16 * 2.4e9
+# MI355X 32-bit VALU peak in lane-operations per second: the published FP32
+# vector rate, 157.3 TFLOP/s, counts 2 flops per FMA lane-operation, i.e.
+# 256 CUs x 4 SIMDs x 32 lanes x 2.4 GHz = 7.86e13 lane-operations/s.  (The
+# score kernel's measured 9-instruction MAC sequence runs above the 16-lane
+# figure, 3.9e13/s, so 32-bit ALU instructions do issue at this rate.)
+ALU_PEAK = 256 * 4 * 32 * 2.4e9
 HBM_PEAK = 8.0e12
 
 KERNEL_SOURCES = ["lamp_device.h", "lamp_internal.h", "scores.hip", "select.hip", "finish.hip",
@@ -157,13 +161,13 @@ def main():
     wall = time.perf_counter() - t0
     gpu_ms = t_start.elapsed_time(t_stop)
 
+    ran = (["scan", "exact", "scores"] + (["finish"] if probs is not None else [])
+           if args.mode == "relaxed" else
+           ["scan", "exact", "scores", "select", "recompute", "finish"])
     stages = {}
-    for si, name in enumerate(lamp.STAGES):
-        if ev[0].recorded(2 * si) and ev[0].recorded(2 * si + 1):
-            try:
-                stages[name] = sum(e.elapsed_ms(2 * si, 2 * si + 1) for e in ev) / args.steps
-            except RuntimeError:
-                pass
+    for name in ran:
+        si = lamp.STAGES.index(name)
+        stages[name] = sum(e.elapsed_ms(2 * si, 2 * si + 1) for e in ev) / args.steps
     for e in ev:
         e.close()
 

@@ -30,7 +30,9 @@
  *     `stats` makes the call wait for its own work.
  *   - Errors: every argument check runs before any HIP call.  No C++
  *     exception crosses this boundary.  The thread-local text of the last
- *     error is available from lamp_last_error().
+ *     error is available from lamp_last_error().  Launches are checked with
+ *     hipGetLastError, so a call that passes its argument checks first clears
+ *     the calling thread's pending HIP error state.
  */
 #ifndef LAMP_H
 #define LAMP_H

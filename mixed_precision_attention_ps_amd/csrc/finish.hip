@@ -124,7 +124,7 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(FinishArgs a)
                 __syncthreads();
 #pragma unroll 4
                 for (int kk = 0; kk < kFinKeys / 4; ++kk) {
-                    const float av = sP[lane & 15][kk * 4 + (lane >> 4)];
+                    const float av = sP[mfma64_row(lane & 15)][kk * 4 + (lane >> 4)];
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         const int cb = wave + 4 * q;

@@ -228,6 +228,8 @@ static int run(const float *q, const float *k, const float *v, int B, int H, int
 {
     g_last_error.clear();
     int rc = check_args(q, k, v, causal, mu, tau, mode, out);
+    if (rc == LAMP_OK)
+        (void)hipGetLastError();   // launches below are checked with hipGetLastError
     if (rc != LAMP_OK)
         return rc;
     Sizes z;
@@ -428,6 +430,7 @@ int lamp_ps_scores(const float *q, const float *k, int B, int H, int S, int D, i
         P.tiles = z.tiles;
         P.n_rows = z.n_rows;
         hipStream_t st = (hipStream_t)stream;
+        (void)hipGetLastError();
         LAMP_HIP_TRY(lamp::launch_operand_scan(P, (uint8_t *)ws, st), "operand scan launch");
         LAMP_HIP_TRY(lamp::launch_ps_scores(P, (uint8_t *)ws, ylo, yref, nullptr, false, st),
                      "score kernel launch");

@@ -279,7 +279,7 @@ __global__ __launch_bounds__(kThreads) void relaxed_kernel(RelaxedArgs a)
             __syncthreads();
 #pragma unroll 4
             for (int kk = 0; kk < kTile / 4; ++kk) {
-                const float av = sm.u.p[wave * 16 + (lane & 15)][kk * 4 + (lane >> 4)];
+                const float av = sm.u.p[wave * 16 + mfma64_row(lane & 15)][kk * 4 + (lane >> 4)];
 #pragma unroll
                 for (int q = 0; q < NB; ++q) {
                     if (q < nb && q * 16 >= h && q * 16 < h + Dc) {
