@@ -161,6 +161,15 @@ size_t lamp_workspace_bytes(int B, int H, int S, int D, int mode, int want_probs
 int lamp_ps_scores(const float *q, const float *k, int B, int H, int S, int D, int causal, int mu,
                    float *ylo, float *yref, void *stream);
 
+/*
+ * lamp_diag_exp -- diagnostic: evaluates the library's two device exponentials
+ * (the double one used for the selection criterion and the KL sums, the
+ * FP32-accurate one used for probabilities) on n device doubles x, writing
+ * y64[e] and y32[e].  For accuracy tests; enqueued on `stream`.  Returns 0,
+ * -1 on NULL pointers or n < 0, -3 on a launch failure.
+ */
+int lamp_diag_exp(const double *x, double *y64, float *y32, int n, void *stream);
+
 /* Static text for a return code. */
 const char *lamp_strerror(int code);
 

@@ -13,169 +13,235 @@ namespace lamp {
 
 typedef double doublex4 __attribute__((ext_vector_type(4)));
 
-constexpr int kFinRows = 16;   // query rows per work-group (one MFMA row block)
-constexpr int kFinKeys = 64;   // keys per P.V step
+constexpr int kFinRows = 64;   // query rows per work-group (16 per wave)
 
 struct FinishArgs {
-    const float *ymix, *yref, *v;
+    const float *ymix, *v;
+    const RowStats *rs;
     float *probs, *out;
     double *row_kl;
-    int S, D, Dv, causal, blocks_per_head;
+    int S, D, causal, blocks_per_head;
 };
 
+// probs_j = exp(y^mix_j - lse_mix) on the valid keys (0 elsewhere), and
+// out = P.V accumulated in double on the FP64 MFMA (FP32 accumulation over
+// hundreds of keys drifts by ~10 ulp of a dominant term, beyond 1e-6).
+// Each KS-key step: thread (row tid/4, keys KS/4 * (tid%4)..) forms KS/4
+// probabilities; the P and V tiles go to double-buffered LDS (one barrier per
+// step) while the next step's scores and V rows are already being loaded;
+// wave w multiplies rows 16w..16w+15 of P by V.  DV = 16 NB is the padded
+// head dimension (compile-time, so every MFMA and LDS index is static).
+template <int NB, int KS>
 __global__ __launch_bounds__(kThreads) void finish_kernel(FinishArgs a)
 {
-    extern __shared__ float smem[];
-    float(*sP)[kFinKeys] = reinterpret_cast<float(*)[kFinKeys]>(smem);   // [16][64]
-    float *sV = smem + kFinRows * kFinKeys;                                // [64][<=128]
-    __shared__ float s_m[kFinRows];
-    __shared__ double s_invl[kFinRows];
+    constexpr int kFinKeys = KS;          // keys per step
+    constexpr int kFinPP = KS + 4;        // P tile row pitch (2-way LDS reads)
+    constexpr int KPT = KS / 4;           // keys per thread per step
+    constexpr int DV = 16 * NB;
+    constexpr int VP = DV + 16;                  // V tile row pitch (2-way LDS reads)
+    constexpr int NV4 = kFinKeys * DV / 4;             // float4 in a V tile
+    constexpr int V4 = (NV4 + kThreads - 1) / kThreads;   // per thread per step
+    __shared__ float sP[2][kFinRows][kFinPP];
+    __shared__ float sV[2][kFinKeys][VP];
+    __shared__ double s_lse[kFinRows];
 
-    const int S = a.S, D = a.D, Dv = a.Dv;
+    const int S = a.S, D = a.D;
     const int bh = blockIdx.x / a.blocks_per_head;
     const int row0 = (blockIdx.x % a.blocks_per_head) * kFinRows;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-    // Phase 1: per-row statistics of y^mix and y^ref, and the row KL.
-    for (int rr = 0; rr < 4; ++rr) {
-        const int lr = wave * 4 + rr;
+    // lse of each row; rows flagged by the recompute get a pass over the row.
+    for (int rr = 0; rr < kFinRows / 4; ++rr) {
+        const int lr = wave * (kFinRows / 4) + rr;
         const int i = row0 + lr;
-        if (i >= S) {
-            if (lane == 0) {
-                s_m[lr] = 0.0f;
-                s_invl[lr] = 0.0;
+        double lse = 0.0;
+        if (i < S) {
+            const uint64_t r = (uint64_t)bh * S + i;
+            const RowStats st = a.rs[r];
+            lse = st.lse_mix;
+            if (st.full_pass) {
+                const int n = a.causal ? i + 1 : S;
+                const float *ym = a.ymix + r * (uint64_t)S;
+                float mm = -INFINITY;
+                for (int j = lane; j < n; j += 64)
+                    mm = fmaxf(mm, ym[j]);
+                mm = wave_max(mm);
+                double l = 0.0;
+                for (int j = lane; j < n; j += 64)
+                    l += exp64((double)ym[j] - (double)mm);
+                l = wave_sum(l);
+                lse = (double)mm + log(l);
+                if (lane == 0 && a.row_kl)
+                    a.row_kl[r] = st.A / st.L_ref + lse - ((double)st.m_ref + log(st.L_ref));
             }
-            continue;
         }
-        const int n = a.causal ? i + 1 : S;
-        const uint64_t r = (uint64_t)bh * S + i;
-        const float *ym = a.ymix + r * (uint64_t)S;
-        const float *yr = a.yref + r * (uint64_t)S;
-        float mm = -INFINITY, mr = -INFINITY;
-        for (int j = lane; j < n; j += 64) {
-            mm = fmaxf(mm, ym[j]);
-            mr = fmaxf(mr, yr[j]);
-        }
-        mm = wave_max(mm);
-        mr = wave_max(mr);
-        double lm = 0.0, lref = 0.0, aref = 0.0;
-        for (int j = lane; j < n; j += 64) {
-            const float xm = ym[j], xr = yr[j];
-            lm += exp((double)xm - (double)mm);
-            const double er = exp((double)xr - (double)mr);
-            lref += er;
-            aref += er * ((double)xr - (double)xm);
-        }
-        lm = wave_sum(lm);
-        lref = wave_sum(lref);
-        aref = wave_sum(aref);
-        if (lane == 0) {
-            if (a.row_kl)
-                a.row_kl[r] = aref / lref + ((double)mm + log(lm)) - ((double)mr + log(lref));
-            s_m[lr] = mm;
-            s_invl[lr] = 1.0 / lm;
-        }
+        if (lane == 0)
+            s_lse[lr] = lse;
     }
     __syncthreads();
 
-    // Phase 2: probabilities (written if requested) and P.V on MFMA.
-    const int prow = tid >> 4, pk = tid & 15;
+    const int prow = tid >> 2, kseg = (tid & 3) * KPT;
     const int ip = row0 + prow;
-    const int np = ip < S ? (a.causal ? ip + 1 : S) : 0;
-    const uint64_t rp = (uint64_t)bh * S + (ip < S ? ip : 0);
+    const bool prow_ok = ip < S;
+    const int np = prow_ok ? (a.causal ? ip + 1 : S) : 0;
+    const uint64_t rp = (uint64_t)bh * S + (prow_ok ? ip : 0);
     const float *ymp = a.ymix + rp * (uint64_t)S;
-    const float mp = s_m[prow];
-    const double invl = s_invl[prow];
-    const int nkeys = a.causal ? min(S, row0 + kFinRows) : S;   // keys this block attends
-    const int nb = Dv / 16;                                      // 16-wide column blocks
-    // P.V accumulates in double on the FP64 MFMA: FP32 accumulation over
-    // hundreds of keys drifts by ~10 ulp of a dominant term, beyond 1e-6.
-    doublex4 acc[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-        acc[q] = doublex4{0.0, 0.0, 0.0, 0.0};
-    const size_t vhead = (size_t)bh * S * D;
+    float *prp = a.probs ? a.probs + rp * (uint64_t)S : nullptr;
+    const double lse_p = s_lse[prow];
+    const bool vec = (S & 3) == 0;
+    const int nkeys = a.causal ? min(S, row0 + kFinRows) : S;   // keys the block attends
+    const int nsteps = (nkeys + kFinKeys - 1) / kFinKeys;
+    const float *Vh = a.v + (size_t)bh * S * D;
 
-    for (int j0 = 0; j0 < S; j0 += kFinKeys) {
+    auto load_scores = [&](int j0, float (&y)[KPT]) {
+        const int jb = j0 + kseg;
+        if (vec) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int jj = pk + 16 * c;
-            const int j = j0 + jj;
-            float pv = 0.0f;
-            if (j < np)
-                pv = (float)(exp((double)ymp[j] - (double)mp) * invl);
-            if (a.probs && ip < S && j < S)
-                a.probs[rp * (uint64_t)S + j] = pv;
-            sP[prow][jj] = pv;
+            for (int e = 0; e < KPT; e += 4) {
+                float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (jb + e < np)   // a float4 never crosses S (S % 4 == 0)
+                    x = *reinterpret_cast<const float4 *>(ymp + jb + e);
+                y[e] = x.x;
+                y[e + 1] = x.y;
+                y[e + 2] = x.z;
+                y[e + 3] = x.w;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < KPT; ++e)
+                y[e] = (jb + e < np) ? ymp[jb + e] : 0.0f;
         }
-        if (j0 < nkeys) {
-            // V tile in column chunks of at most 128 (LDS: 64 x 128 floats).
-            for (int h = 0; h < Dv; h += 128) {
-                const int Dc = min(128, Dv - h);
-                const int n4 = kFinKeys * Dc / 4;
-                __syncthreads();
-                for (int e = tid; e < n4; e += kThreads) {
-                    const int key = e / (Dc / 4), col = h + (e % (Dc / 4)) * 4;
-                    float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-                    if (j0 + key < S && col < D)
-                        x = *reinterpret_cast<const float4 *>(a.v + vhead + (size_t)(j0 + key) * D + col);
-                    *reinterpret_cast<float4 *>(sV + key * Dc + (col - h)) = x;
-                }
-                __syncthreads();
-#pragma unroll 4
-                for (int kk = 0; kk < kFinKeys / 4; ++kk) {
-                    const float av = sP[mfma64_row(lane & 15)][kk * 4 + (lane >> 4)];
+    };
+    auto load_v = [&](int j0, float4 (&vv)[V4]) {
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int cb = wave + 4 * q;
-                        if (cb * 16 >= h && cb * 16 < h + Dc) {
-                            const float bv = sV[(kk * 4 + (lane >> 4)) * Dc + cb * 16 - h + (lane & 15)];
-                            acc[q] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)av, (double)bv,
-                                                                          acc[q], 0, 0, 0);
-                        }
-                    }
-                }
+        for (int u = 0; u < V4; ++u) {
+            const int e = tid + u * kThreads;
+            const int key = e / (DV / 4), col = (e % (DV / 4)) * 4;
+            float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (e < NV4 && j0 + key < S && col < D)
+                x = *reinterpret_cast<const float4 *>(Vh + (size_t)(j0 + key) * D + col);
+            vv[u] = x;
+        }
+    };
+
+    doublex4 acc[NB];
+#pragma unroll
+    for (int q = 0; q < NB; ++q)
+        acc[q] = doublex4{0.0, 0.0, 0.0, 0.0};
+    float ycur[KPT], ynext[KPT];
+    float4 vcur[V4], vnext[V4];
+    if (nsteps > 0) {
+        load_scores(0, ycur);
+        load_v(0, vcur);
+    }
+    for (int s = 0; s < nsteps; ++s) {
+        const int j0 = s * kFinKeys;
+        const int buf = s & 1;
+        if (s + 1 < nsteps) {
+            load_scores(j0 + kFinKeys, ynext);
+            load_v(j0 + kFinKeys, vnext);
+        }
+        float pv[KPT];
+        const int jb = j0 + kseg;
+#pragma unroll
+        for (int e = 0; e < KPT; ++e)
+            pv[e] = (jb + e < np) ? exp_f32((double)ycur[e] - lse_p) : 0.0f;
+        if (prp && prow_ok) {
+            if (vec) {
+#pragma unroll
+                for (int e = 0; e < KPT; e += 4)
+                    if (jb + e < S)
+                        *reinterpret_cast<float4 *>(prp + jb + e) =
+                            make_float4(pv[e], pv[e + 1], pv[e + 2], pv[e + 3]);
+            } else {
+                for (int e = 0; e < KPT; ++e)
+                    if (jb + e < S)
+                        prp[jb + e] = pv[e];
             }
         }
+#pragma unroll
+        for (int e = 0; e < KPT; e += 4)
+            *reinterpret_cast<float4 *>(&sP[buf][prow][kseg + e]) =
+                make_float4(pv[e], pv[e + 1], pv[e + 2], pv[e + 3]);
+#pragma unroll
+        for (int u = 0; u < V4; ++u) {
+            const int e = tid + u * kThreads;
+            const int key = e / (DV / 4), col = (e % (DV / 4)) * 4;
+            if (e < NV4)
+                *reinterpret_cast<float4 *>(&sV[buf][key][col]) = vcur[u];
+        }
         __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < kFinKeys / 4; ++kk) {
+            const double av = sP[buf][wave * 16 + mfma64_row(lane & 15)][kk * 4 + (lane >> 4)];
+#pragma unroll
+            for (int q = 0; q < NB; ++q) {
+                const double bv = sV[buf][kk * 4 + (lane >> 4)][q * 16 + (lane & 15)];
+                acc[q] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc[q], 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < KPT; ++e)
+            ycur[e] = ynext[e];
+#pragma unroll
+        for (int u = 0; u < V4; ++u)
+            vcur[u] = vnext[u];
     }
 
-    // MFMA 16x16 result layout: lane holds rows 4*(lane/16)+v, column lane%16.
+    // Keys past the causal limit of every row in the block: probabilities 0.
+    if (prp && prow_ok) {
+        for (int j = nsteps * kFinKeys + (tid & 3) * 4; j < S; j += 16) {
+            if (vec)
+                *reinterpret_cast<float4 *>(prp + j) = make_float4(0.f, 0.f, 0.f, 0.f);
+            else
+                for (int e = 0; e < 4 && j + e < S; ++e)
+                    prp[j + e] = 0.0f;
+        }
+    }
+
+    // Lane holds rows 16*wave + 4*(lane/16) + v of column 16q + lane%16.
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int cb = wave + 4 * q;
-        if (cb >= nb)
-            continue;
-        const int col = cb * 16 + (lane & 15);
+    for (int q = 0; q < NB; ++q) {
+        const int col = q * 16 + (lane & 15);
         if (col >= D)
             continue;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-            const int i = row0 + 4 * (lane >> 4) + v;
+            const int i = row0 + wave * 16 + 4 * (lane >> 4) + v;
             if (i < S)
                 a.out[((size_t)bh * S + i) * D + col] = (float)acc[q][v];
         }
     }
 }
 
-hipError_t launch_finish(const Problem &p, const float *ymix, const float *yref, float *probs,
+hipError_t launch_finish(const Problem &p, const float *ymix, const RowStats *rs, float *probs,
                          float *out, double *row_kl, hipStream_t st)
 {
     FinishArgs a;
     a.ymix = ymix;
-    a.yref = yref;
     a.v = p.v;
+    a.rs = rs;
     a.probs = probs;
     a.out = out;
     a.row_kl = row_kl;
     a.S = p.S;
     a.D = p.D;
-    a.Dv = (p.D + 15) / 16 * 16;
     a.causal = p.causal;
     a.blocks_per_head = (p.S + kFinRows - 1) / kFinRows;
-    const size_t shmem = sizeof(float) * (kFinRows * kFinKeys + kFinKeys * min(a.Dv, 128));
-    const uint64_t grid = (uint64_t)p.BH * a.blocks_per_head;
-    hipLaunchKernelGGL(finish_kernel, dim3((unsigned)grid), dim3(kThreads), shmem, st, a);
+    const dim3 grid((unsigned)((uint64_t)p.BH * a.blocks_per_head)), block(kThreads);
+    switch ((p.D + 15) / 16) {
+    case 1: hipLaunchKernelGGL((finish_kernel<1, 32>), grid, block, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((finish_kernel<2, 32>), grid, block, 0, st, a); break;
+    case 3: hipLaunchKernelGGL((finish_kernel<3, 32>), grid, block, 0, st, a); break;
+    case 4: hipLaunchKernelGGL((finish_kernel<4, 32>), grid, block, 0, st, a); break;
+    case 5: hipLaunchKernelGGL((finish_kernel<5, 32>), grid, block, 0, st, a); break;
+    case 6: hipLaunchKernelGGL((finish_kernel<6, 32>), grid, block, 0, st, a); break;
+    case 7: hipLaunchKernelGGL((finish_kernel<7, 32>), grid, block, 0, st, a); break;
+    case 8: hipLaunchKernelGGL((finish_kernel<8, 32>), grid, block, 0, st, a); break;
+    case 9: case 10: case 11: case 12:
+        hipLaunchKernelGGL((finish_kernel<12, 16>), grid, block, 0, st, a); break;
+    default: hipLaunchKernelGGL((finish_kernel<16, 16>), grid, block, 0, st, a); break;
+    }
     return hipGetLastError();
 }
 
@@ -249,3 +315,29 @@ hipError_t launch_zero(void *ptr, size_t bytes, hipStream_t st)
 }
 
 }  // namespace lamp
+
+// ---------------------------------------------------------------------------
+// Diagnostic: the device exponentials on caller data (accuracy tests).
+// ---------------------------------------------------------------------------
+namespace lamp {
+__global__ void exp_probe_kernel(const double *x, double *y64, float *y32, int n)
+{
+    const int e = blockIdx.x * blockDim.x + threadIdx.x;
+    if (e < n) {
+        y64[e] = exp64(x[e]);
+        y32[e] = exp_f32(x[e]);
+    }
+}
+}  // namespace lamp
+
+extern "C" int lamp_diag_exp(const double *x, double *y64, float *y32, int n, void *stream)
+{
+    if (!x || !y64 || !y32 || n < 0)
+        return -1;
+    if (n == 0)
+        return 0;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(lamp::exp_probe_kernel, dim3((n + 255) / 256), dim3(256), 0,
+                       (hipStream_t)stream, x, y64, y32, n);
+    return hipGetLastError() == hipSuccess ? 0 : -3;
+}

@@ -135,7 +135,7 @@ int check_args(const float *q, const float *k, const float *v, int causal, int m
 struct Layout {
     size_t ymix = SIZE_MAX, yref = SIZE_MAX, list = SIZE_MAX, row_count = SIZE_MAX,
            row_kl = SIZE_MAX, row_kl_lowp = SIZE_MAX, unsafe = SIZE_MAX, dstats = SIZE_MAX,
-           row_m = SIZE_MAX, row_l = SIZE_MAX;
+           row_m = SIZE_MAX, row_l = SIZE_MAX, rowstats = SIZE_MAX;
     size_t total = 0;
     size_t take(size_t bytes)
     {
@@ -171,6 +171,7 @@ Layout plan(const Sizes &z, int mode, const Needs &n)
         if (n.yref)
             L.yref = L.take(4 * z.n_scores);
         L.list = L.take(4 * z.n_valid);
+        L.rowstats = L.take(sizeof(lamp::RowStats) * z.n_rows);
     }
     return L;
 }
@@ -334,23 +335,25 @@ static int run(const float *q, const float *k, const float *v, int B, int H, int
                      "score kernel launch");
         LAMP_HIP_TRY(tm.end(LAMP_STAGE_SCORES), "hipEventRecord");
         LAMP_HIP_TRY(tm.begin(LAMP_STAGE_SELECT), "hipEventRecord");
+        auto *rs = at<lamp::RowStats>(ws, L.rowstats);
         if (mode == LAMP_STRICT) {
-            LAMP_HIP_TRY(lamp::launch_strict_select(P, ymix, yref, mask, list, row_count,
-                                                    row_kl_lowp, 0, st),
+            LAMP_HIP_TRY(lamp::launch_strict_select(P, ymix, yref, mask, list, row_count, rs,
+                                                    row_kl, row_kl_lowp, 0, st),
                          "select kernel launch");
         } else {
-            LAMP_HIP_TRY(lamp::launch_strict_select(P, ymix, yref, nullptr, nullptr, row_count,
-                                                    row_kl_lowp, 1, st),
+            LAMP_HIP_TRY(lamp::launch_strict_select(P, ymix, yref, nullptr, nullptr, row_count, rs,
+                                                    row_kl, row_kl_lowp, 1, st),
                          "count kernel launch");
             LAMP_HIP_TRY(lamp::launch_random_select(P, p.seed, mask, list, row_count, st),
                          "random select launch");
         }
         LAMP_HIP_TRY(tm.end(LAMP_STAGE_SELECT), "hipEventRecord");
         LAMP_HIP_TRY(tm.begin(LAMP_STAGE_RECOMPUTE), "hipEventRecord");
-        LAMP_HIP_TRY(lamp::launch_recompute(P, list, row_count, ymix, st), "recompute launch");
+        LAMP_HIP_TRY(lamp::launch_recompute(P, list, row_count, ymix, rs, row_kl, st),
+                     "recompute launch");
         LAMP_HIP_TRY(tm.end(LAMP_STAGE_RECOMPUTE), "hipEventRecord");
         LAMP_HIP_TRY(tm.begin(LAMP_STAGE_FINISH), "hipEventRecord");
-        LAMP_HIP_TRY(lamp::launch_finish(P, ymix, yref, probs, out, row_kl, st), "finish launch");
+        LAMP_HIP_TRY(lamp::launch_finish(P, ymix, rs, probs, out, row_kl, st), "finish launch");
         LAMP_HIP_TRY(tm.end(LAMP_STAGE_FINISH), "hipEventRecord");
     }
 

@@ -6,6 +6,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include "lamp_exp.h"
 #include "lamp_internal.h"
 
 namespace lamp {

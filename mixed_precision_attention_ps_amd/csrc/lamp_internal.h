@@ -45,24 +45,40 @@ hipError_t launch_operand_scan(const Problem &p, uint8_t *unsafe, hipStream_t st
 hipError_t launch_ps_scores(const Problem &p, const uint8_t *unsafe, float *ylo, float *yref,
                             unsigned long long *exact_tiles, bool fast, hipStream_t st);
 
-// Strict row softmax + selection.  count_only: write row_count only (random
-// mode); otherwise mask words (if non-null), the per-row compacted index
-// segments in `list` and row_count.  Optional KL(P_ref || P_lowp) per row
-// when yref and row_kl_lowp are non-null (reads y^lo before recompute).
+// Per-row statistics of the strict / random path (double sums, float maxima).
+struct RowStats {
+    double L_lo;      // sum_j exp(y^lo_j - m_lo)
+    double L_ref;     // sum_j exp(y^ref_j - m_ref)
+    double A;         // sum_j exp(y^ref_j - m_ref) (y^ref_j - y^mix_j); before the
+                      // recompute (y^mix = y^lo) this is the low-precision term
+    double lse_mix;   // log-sum-exp of y^mix over the valid keys
+    float m_lo, m_ref;
+    uint32_t full_pass;   // 1: lse_mix must be recomputed from the whole row
+    uint32_t pad;
+};
+
+// Strict row softmax + selection.  count_only: row statistics and row_count
+// only (random mode); otherwise also mask words (if non-null) and the per-row
+// compacted index segments in `list`.  Writes RowStats with lse_mix = lse(y^lo),
+// row_kl (if non-null) and row_kl_lowp (if non-null) = KL(P_ref || P_lowp);
+// the recompute kernel updates the rows that have selections.
 hipError_t launch_strict_select(const Problem &p, const float *ylo, const float *yref,
                                 uint32_t *mask, uint32_t *list, uint32_t *row_count,
-                                double *row_kl_lowp, int count_only, hipStream_t st);
+                                RowStats *rs, double *row_kl, double *row_kl_lowp,
+                                int count_only, hipStream_t st);
 
 // Random control: per row, row_count[r] keys with the smallest hashes.
 hipError_t launch_random_select(const Problem &p, uint64_t seed, uint32_t *mask, uint32_t *list,
                                 const uint32_t *row_count, hipStream_t st);
 
-// Gather FP32 recompute of the listed scores, scattered into ymix.
+// Gather FP32 recompute of the listed scores, scattered into ymix, with the
+// rows' softmax and KL statistics updated for the changed scores.
 hipError_t launch_recompute(const Problem &p, const uint32_t *list, const uint32_t *row_count,
-                            float *ymix, hipStream_t st);
+                            float *ymix, RowStats *rs, double *row_kl, hipStream_t st);
 
-// Final softmax (probs may alias ymix), P.V on MFMA, row KL.
-hipError_t launch_finish(const Problem &p, const float *ymix, const float *yref, float *probs,
+// Final softmax (probs may alias ymix), P.V on MFMA; rows flagged full_pass
+// get lse_mix (and row_kl) from a pass over the row here.
+hipError_t launch_finish(const Problem &p, const float *ymix, const RowStats *rs, float *probs,
                          float *out, double *row_kl, hipStream_t st);
 
 // Relaxed fused one-pass kernel.  ymix_raw: if non-null, y^mix of valid

@@ -21,11 +21,17 @@ struct SelectArgs {
     uint64_t n_rows;
     double tau;
     uint32_t *mask, *list, *row_count;
-    double *row_kl_lowp;
+    RowStats *rs;
+    double *row_kl, *row_kl_lowp;
     int count_only;
 };
 
-// One wave per row; 4 rows per work-group.
+constexpr int kSelChunk = 16;   // keys per lane held in registers (1024 per wave)
+
+// One wave per row; 4 rows per work-group.  ONE: the whole row fits one
+// register chunk (S <= 1024), so scores and exponentials are read and formed
+// once; otherwise the row is streamed three times.
+template <bool ONE>
 __global__ __launch_bounds__(kThreads) void strict_select_kernel(SelectArgs a)
 {
     const int lane = threadIdx.x & 63;
@@ -36,64 +42,96 @@ __global__ __launch_bounds__(kThreads) void strict_select_kernel(SelectArgs a)
     const int i = (int)(r % (uint64_t)S);
     const int n = a.causal ? i + 1 : S;
     const float *y = a.y + r * (uint64_t)S;
-    const bool want_lowp = a.row_kl_lowp != nullptr && a.yref != nullptr;
-    const float *yr = want_lowp ? a.yref + r * (uint64_t)S : nullptr;
+    const float *yr = a.yref + r * (uint64_t)S;
 
-    // Row maximum (and the reference row's, for KL(P_ref || P_lowp)).
+    float vlo[kSelChunk], vref[kSelChunk];
+    double elo[kSelChunk];
+    // Row maxima of y^lo and y^ref.
     float m = -INFINITY, mr = -INFINITY;
-    for (int j = lane; j < n; j += 64) {
-        m = fmaxf(m, y[j]);
-        if (want_lowp)
+    if (ONE) {
+#pragma unroll
+        for (int t = 0; t < kSelChunk; ++t) {
+            const int j = lane + 64 * t;
+            vlo[t] = j < n ? y[j] : -INFINITY;
+            vref[t] = j < n ? yr[j] : -INFINITY;
+            m = fmaxf(m, vlo[t]);
+            mr = fmaxf(mr, vref[t]);
+        }
+    } else {
+        for (int j = lane; j < n; j += 64) {
+            m = fmaxf(m, y[j]);
             mr = fmaxf(mr, yr[j]);
-    }
-    m = wave_max(m);
-    if (want_lowp)
-        mr = wave_max(mr);
-
-    // A = sum of exp(y - m) below the maximum; cnt = keys at the maximum.
-    double A = 0.0, Lr = 0.0, Br = 0.0;
-    int cnt = 0;
-    for (int j = lane; j < n; j += 64) {
-        const float v = y[j];
-        if (v == m)
-            cnt++;
-        else
-            A += exp((double)v - (double)m);
-        if (want_lowp) {
-            const double er = exp((double)yr[j] - (double)mr);
-            Lr += er;
-            Br += er * ((double)yr[j] - (double)v);
         }
     }
+    m = wave_max(m);
+    mr = wave_max(mr);
+
+    // A: sum of exp(y^lo - m) below the maximum; cnt: keys at the maximum;
+    // Lr, Br: reference sum and sum of e_ref (y^ref - y^lo).
+    double A = 0.0, Lr = 0.0, Br = 0.0;
+    int cnt = 0;
+    auto accumulate = [&](float v, float vr, double &e) {
+        if (v == m) {
+            cnt++;
+            e = 1.0;
+        } else {
+            e = exp64((double)v - (double)m);
+            A += e;
+        }
+        const double er = exp64((double)vr - (double)mr);
+        Lr += er;
+        Br += er * ((double)vr - (double)v);
+    };
+    if (ONE) {
+#pragma unroll
+        for (int t = 0; t < kSelChunk; ++t) {
+            elo[t] = 0.0;
+            if (lane + 64 * t < n)
+                accumulate(vlo[t], vref[t], elo[t]);
+        }
+    } else {
+        double e;
+        for (int j = lane; j < n; j += 64)
+            accumulate(y[j], yr[j], e);
+    }
     A = wave_sum(A);
+    Lr = wave_sum(Lr);
+    Br = wave_sum(Br);
     cnt = wave_sum_int(cnt);
     const double L = A + (double)cnt;
     const double rest_at_max = A + (double)(cnt - 1);
-    if (want_lowp) {
-        Lr = wave_sum(Lr);
-        Br = wave_sum(Br);
-        if (lane == 0)
-            a.row_kl_lowp[r] = Br / Lr + ((double)m + log(L)) - ((double)mr + log(Lr));
+    const double lse_lo = (double)m + log(L);
+    const double lse_ref = (double)mr + log(Lr);
+    const double kl_lowp = Br / Lr + lse_lo - lse_ref;
+    if (lane == 0) {
+        RowStats st;
+        st.L_lo = L;
+        st.L_ref = Lr;
+        st.A = Br;
+        st.lse_mix = lse_lo;
+        st.m_lo = m;
+        st.m_ref = mr;
+        st.full_pass = 0;
+        st.pad = 0;
+        a.rs[r] = st;
+        if (a.row_kl)
+            a.row_kl[r] = kl_lowp;
+        if (a.row_kl_lowp)
+            a.row_kl_lowp[r] = kl_lowp;
     }
 
     // Criterion, mask words and compaction into this row's list segment.
     const uint64_t seg = row_segment(r, S, a.causal);
     uint32_t total = 0;
     const int jend = a.count_only ? n : S;
-    for (int j0 = 0; j0 < jend; j0 += 64) {
-        const int j = j0 + lane;
+    // c = 2 z (1 - z) |y| with z = e / L and 1 - z = rest / L, rest = L - e
+    // (or the sum of the other keys at the maximum): 2 e rest |y| / L^2.
+    const double inv_l2 = 1.0 / (L * L);
+    auto decide = [&](int j0, int j, float v, double e) {
         bool sel = false;
         if (j < n) {
-            const float v = y[j];
-            double e, omz;
-            if (v == m) {
-                e = 1.0;
-                omz = rest_at_max / L;
-            } else {
-                e = exp((double)v - (double)m);
-                omz = (L - e) / L;
-            }
-            const double c = 2.0 * (e / L) * omz * fabs((double)v);
+            const double rest = (v == m) ? rest_at_max : L - e;
+            const double c = 2.0 * e * rest * fabs((double)v) * inv_l2;
             sel = c > a.tau;
         }
         const uint64_t b = __ballot(sel);
@@ -109,6 +147,23 @@ __global__ __launch_bounds__(kThreads) void strict_select_kernel(SelectArgs a)
                 a.list[seg + total + lanes_below(b)] = (uint32_t)j;
         }
         total += (uint32_t)__popcll(b);
+    };
+    if (ONE) {
+#pragma unroll
+        for (int t = 0; t < kSelChunk; ++t)
+            if (64 * t < jend)
+                decide(64 * t, lane + 64 * t, vlo[t], elo[t]);
+    } else {
+        for (int j0 = 0; j0 < jend; j0 += 64) {
+            const int j = j0 + lane;
+            float v = 0.0f;
+            double e = 0.0;
+            if (j < n) {
+                v = y[j];
+                e = (v == m) ? 1.0 : exp64((double)v - (double)m);
+            }
+            decide(j0, j, v, e);
+        }
     }
     if (lane == 0)
         a.row_count[r] = total;
@@ -116,7 +171,8 @@ __global__ __launch_bounds__(kThreads) void strict_select_kernel(SelectArgs a)
 
 hipError_t launch_strict_select(const Problem &p, const float *ylo, const float *yref,
                                 uint32_t *mask, uint32_t *list, uint32_t *row_count,
-                                double *row_kl_lowp, int count_only, hipStream_t st)
+                                RowStats *rs, double *row_kl, double *row_kl_lowp,
+                                int count_only, hipStream_t st)
 {
     SelectArgs a;
     a.y = ylo;
@@ -129,10 +185,15 @@ hipError_t launch_strict_select(const Problem &p, const float *ylo, const float 
     a.mask = mask;
     a.list = list;
     a.row_count = row_count;
+    a.rs = rs;
+    a.row_kl = row_kl;
     a.row_kl_lowp = row_kl_lowp;
     a.count_only = count_only;
     const uint64_t grid = (p.n_rows + 3) / 4;
-    hipLaunchKernelGGL(strict_select_kernel, dim3((unsigned)grid), dim3(kThreads), 0, st, a);
+    if (p.S <= 64 * kSelChunk)
+        hipLaunchKernelGGL(strict_select_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, st, a);
+    else
+        hipLaunchKernelGGL(strict_select_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, st, a);
     return hipGetLastError();
 }
 
@@ -273,47 +334,128 @@ struct RecomputeArgs {
     float s;
     const uint32_t *list, *row_count;
     float *ymix;
+    RowStats *rs;
+    double *row_kl;
 };
+
+// The softmax statistics of y^mix follow from those of y^lo by correcting the
+// changed terms: L_mix = L_lo + sum_sel [exp(y_hi - m_lo) - exp(y_lo - m_lo)]
+// and A = A_lo - sum_sel exp(y_hi - m_ref) (y_hi - y_lo) (a recomputed score
+// equals its FP32 reference, so its KL term vanishes).  When the correction
+// removes most of L_lo (a dominant key moved down) or overflows (a key moved
+// far above m_lo) the row is flagged for a full pass in the finish kernel.
+//
+// One work-group per 64 rows: the rows' list segments are concatenated
+// (block-local prefix of the counts) and every thread takes one listed score
+// per pass; the per-row corrections are then summed in list order by one
+// thread per row, so the result does not depend on scheduling.
+constexpr int kRcRows = 64;
 
 __global__ __launch_bounds__(kThreads) void recompute_kernel(RecomputeArgs a)
 {
-    const int lane = threadIdx.x & 63;
-    const uint64_t r = (uint64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (r >= a.n_rows)
-        return;
-    const int i = (int)(r % (uint64_t)a.S);
-    const uint32_t n = a.causal ? (uint32_t)i + 1u : (uint32_t)a.S;
-    const uint32_t cnt = min(a.row_count[r], n);
-    if (cnt == 0)
-        return;
-    const uint64_t bh = r / (uint64_t)a.S;
-    const float *qi = a.q + r * (uint64_t)a.D;
-    const float *Kh = a.k + bh * (uint64_t)a.S * a.D;
-    const uint64_t seg = row_segment(r, a.S, a.causal);
-    for (uint32_t e = lane; e < cnt; e += 64) {
-        const uint32_t j = a.list[seg + e];
-        if (j >= (uint32_t)a.S)
-            continue;
-        const float4 *kj = reinterpret_cast<const float4 *>(Kh + (size_t)j * a.D);
-        const float4 *q4 = reinterpret_cast<const float4 *>(qi);
-        float acc = 0.0f;
-        for (int d4 = 0; d4 < a.D / 4; ++d4) {
-            const float4 x = q4[d4], y = kj[d4];
-            float p0 = x.x * y.x;
-            acc = acc + p0;
-            float p1 = x.y * y.y;
-            acc = acc + p1;
-            float p2 = x.z * y.z;
-            acc = acc + p2;
-            float p3 = x.w * y.w;
-            acc = acc + p3;
+    __shared__ uint32_t s_off[kRcRows + 1];
+    __shared__ float s_mlo[kRcRows], s_mref[kRcRows];
+    __shared__ double s_dl[kThreads], s_da[kThreads];
+    const int tid = threadIdx.x;
+    const uint64_t r0 = (uint64_t)blockIdx.x * kRcRows;
+    RowStats st{};
+    uint32_t cnt = 0;
+    if (tid < kRcRows) {
+        const uint64_t r = r0 + tid;
+        if (r < a.n_rows) {
+            const int i = (int)(r % (uint64_t)a.S);
+            const uint32_t n = a.causal ? (uint32_t)i + 1u : (uint32_t)a.S;
+            cnt = min(a.row_count[r], n);
+            st = a.rs[r];
         }
-        a.ymix[r * (uint64_t)a.S + j] = acc * a.s;
+        s_off[tid + 1] = cnt;
+        s_mlo[tid] = st.m_lo;
+        s_mref[tid] = st.m_ref;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        s_off[0] = 0;
+        for (int t = 1; t <= kRcRows; ++t)
+            s_off[t] += s_off[t - 1];
+    }
+    __syncthreads();
+    const uint32_t total = s_off[kRcRows];
+    if (total == 0)
+        return;
+    double dL = 0.0, dA = 0.0;
+    for (uint32_t base = 0; base < total; base += kThreads) {
+        const uint32_t e = base + tid;
+        double cl = 0.0, ca = 0.0;
+        if (e < total) {
+            int lo = 0, hi = kRcRows;   // row lr with s_off[lr] <= e < s_off[lr + 1]
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (s_off[mid] <= e)
+                    lo = mid;
+                else
+                    hi = mid;
+            }
+            const int lr = lo;
+            const uint64_t r = r0 + lr;
+            const uint32_t j = a.list[row_segment(r, a.S, a.causal) + (e - s_off[lr])];
+            const uint64_t bh = r / (uint64_t)a.S;
+            if (j < (uint32_t)a.S) {
+                const float4 *q4 = reinterpret_cast<const float4 *>(a.q + r * (uint64_t)a.D);
+                const float4 *k4 = reinterpret_cast<const float4 *>(
+                    a.k + (bh * (uint64_t)a.S + j) * (uint64_t)a.D);
+                float acc = 0.0f;
+                for (int d4 = 0; d4 < a.D / 4; ++d4) {
+                    const float4 x = q4[d4], z = k4[d4];
+                    float p0 = x.x * z.x;
+                    acc = acc + p0;
+                    float p1 = x.y * z.y;
+                    acc = acc + p1;
+                    float p2 = x.z * z.z;
+                    acc = acc + p2;
+                    float p3 = x.w * z.w;
+                    acc = acc + p3;
+                }
+                const float yhi = acc * a.s;
+                float *slot = a.ymix + r * (uint64_t)a.S + j;
+                const float ylo = *slot;
+                *slot = yhi;
+                const double ml = (double)s_mlo[lr], mr = (double)s_mref[lr];
+                cl = exp64((double)yhi - ml) - exp64((double)ylo - ml);
+                ca = exp64((double)yhi - mr) * ((double)yhi - (double)ylo);
+            }
+        }
+        s_dl[tid] = cl;
+        s_da[tid] = ca;
+        __syncthreads();
+        if (tid < kRcRows) {
+            const uint32_t b = max(s_off[tid], base), en = min(s_off[tid + 1], base + kThreads);
+            for (uint32_t x = b; x < en; ++x) {
+                dL += s_dl[x - base];
+                dA += s_da[x - base];
+            }
+        }
+        __syncthreads();
+    }
+    if (tid < kRcRows && cnt > 0) {
+        const uint64_t r = r0 + tid;
+        const double Lmix = st.L_lo + dL;
+        const double Amix = st.A - dA;
+        const double lse_ref = (double)st.m_ref + log(st.L_ref);
+        RowStats o = st;
+        o.A = Amix;
+        if (Lmix >= 0.25 * st.L_lo && isfinite(Lmix)) {
+            o.lse_mix = (double)st.m_lo + log(Lmix);
+            if (a.row_kl)
+                a.row_kl[r] = Amix / st.L_ref + o.lse_mix - lse_ref;
+        } else {
+            o.full_pass = 1;
+        }
+        a.rs[r] = o;
     }
 }
 
 hipError_t launch_recompute(const Problem &p, const uint32_t *list, const uint32_t *row_count,
-                            float *ymix, hipStream_t st)
+                            float *ymix, RowStats *rs, double *row_kl, hipStream_t st)
 {
     RecomputeArgs a;
     a.q = p.q;
@@ -326,7 +468,9 @@ hipError_t launch_recompute(const Problem &p, const uint32_t *list, const uint32
     a.list = list;
     a.row_count = row_count;
     a.ymix = ymix;
-    const uint64_t grid = (p.n_rows + 3) / 4;
+    a.rs = rs;
+    a.row_kl = row_kl;
+    const uint64_t grid = (p.n_rows + kRcRows - 1) / kRcRows;
     hipLaunchKernelGGL(recompute_kernel, dim3((unsigned)grid), dim3(kThreads), 0, st, a);
     return hipGetLastError();
 }

@@ -73,6 +73,8 @@ def library():
     lib.lamp_last_error.argtypes = []
     lib.lamp_version.restype = I
     lib.lamp_version.argtypes = []
+    lib.lamp_diag_exp.restype = I
+    lib.lamp_diag_exp.argtypes = [P, P, P, I, P]
     _lib = lib
     return lib
 
@@ -98,6 +100,17 @@ def _f32(t, name):
     if t.dtype != torch.float32:
         raise TypeError(f"{name} must be float32")
     return _ptr(t)
+
+
+def lamp_diag_exp(x):
+    """The library's double and FP32-accurate exponentials of a float64 tensor."""
+    y64 = torch.empty_like(x)
+    y32 = torch.empty(x.shape, dtype=torch.float32, device=x.device)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(x.device).cuda_stream)
+    rc = library().lamp_diag_exp(_ptr(x), _ptr(y64), _ptr(y32), x.numel(), stream)
+    if rc != 0:
+        raise LampError(rc, "lamp_diag_exp failed")
+    return y64, y32
 
 
 def lamp_workspace_bytes(B, H, S, D, mode, want_probs) -> int:
