@@ -17,6 +17,8 @@
 // bit-identical to its FP32 reference score, which this pass already holds),
 // online softmax of y^mix with P.V on MFMA, and online statistics of y^ref for
 // the row KL(P_FP32 || P_LAMP).
+#include <type_traits>
+
 #include "lamp_device.h"
 
 namespace lamp {
@@ -62,32 +64,55 @@ __device__ __forceinline__ uint32_t group16_sum_u(uint32_t v)
     return v;
 }
 
+// Online state of one query row: maxima of y^lo (m_t), y^mix and y^ref, and
+// the sums relative to them.  Each row is owned by the 16 lanes of one wave
+// that hold it, so its LDS copy needs no barrier.
+struct RowState {
+    float m_t, m_mix, m_ref;
+    uint32_t cnt;
+    double l_mix, l_ref, kl_a, l_lo, kl_b;
+};
+
+template <int DV>
 struct RelaxedSmem {
     union {
-        TileSmem tile;
-        float p[kTile][kTile];   // P tile of the online softmax, [row][key]
+        TileSmem tile;                 // PS(mu) operand staging
+        float p[kTile][kTile + 4];     // P tile of the online softmax, [row][key]
     } u;
-    float v[kTile * 128];        // V tile, [key][col], up to 128 columns at a time
+    float v[kTile][DV + 16];           // V tile, [key][col] (padded rows: 2-way LDS reads)
+    RowState row[kTile];
 };
 
 template <int PATH>
-__device__ __forceinline__ void relaxed_tile_scores(RelaxedSmem &sm, const RelaxedArgs &a,
+__device__ __forceinline__ void relaxed_tile_scores(TileSmem &sm, const RelaxedArgs &a,
                                                     const float *Qh, const float *Kh, int row0,
                                                     int col0, float lo[4][4], float ref[4][4])
 {
     TileAcc acc;
-    score_tile<PATH>(sm.u.tile, acc, Qh, Kh, row0, col0, a.S, a.D, a.pc);
+    score_tile<PATH>(sm, acc, Qh, Kh, row0, col0, a.S, a.D, a.pc);
     tile_scores<PATH>(acc, a.pc, lo, ref);
 }
 
-// FAST_KERNEL: the work-group's query block and every key block it visits
-// allow the FP32 fast path; the other instance takes the remaining query
-// blocks (exact double path per tile where needed, plain FP32 at mu = 23).
-template <int NB, bool FAST_KERNEL>
-__global__ __launch_bounds__(kThreads) void relaxed_kernel(RelaxedArgs a)
+// exp of a difference of row maxima (-inf when a maximum is still unset).
+__device__ __forceinline__ double exp_delta(float from, float to)
 {
-    __shared__ RelaxedSmem sm;
-    const int S = a.S, D = a.D, Dv = a.Dv;
+    return from == -INFINITY ? 0.0 : exp64((double)from - (double)to);
+}
+
+// Per-score exponentials (double): E = exp(y^lo - m_t) serves the criterion
+// and, scaled by exp(m_t - m_mix), the softmax term of an unselected score;
+// e_ref = exp(y^ref - m_ref) serves the reference sums and, scaled by
+// exp(m_ref - m_mix), the softmax term of a selected score (whose y^mix is
+// y^ref).  Two double exps per score; the row factors are per tile.
+template <int NB, bool FAST_KERNEL>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FAST_KERNEL ? 2 : 1)))
+void relaxed_kernel(RelaxedArgs a)
+{
+    constexpr int DV = 16 * NB;
+    constexpr int NV4 = kTile * DV / 4;                   // float4 in a V tile
+    constexpr int V4 = (NV4 + kThreads - 1) / kThreads;   // per thread
+    __shared__ RelaxedSmem<DV> sm;
+    const int S = a.S, D = a.D;
     // heaviest query blocks first (causal work grows with the block index)
     const int qb = a.tiles - 1 - (int)(blockIdx.x / a.BH);
     const int bh = (int)(blockIdx.x % a.BH);
@@ -107,20 +132,15 @@ __global__ __launch_bounds__(kThreads) void relaxed_kernel(RelaxedArgs a)
             return;
     }
 
-    // Row state for rows ty*4 + r (replicated over the 16 lanes of the row).
-    float m_t[4], m_mix[4], m_ref[4], m_lo[4];
-    double l_mix[4], l_ref[4], kl_a[4], l_lo[4], kl_b[4];
-    uint32_t cnt[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        m_t[r] = m_mix[r] = m_ref[r] = m_lo[r] = -INFINITY;
-        l_mix[r] = l_ref[r] = kl_a[r] = l_lo[r] = kl_b[r] = 0.0;
-        cnt[r] = 0;
-    }
-    const int nb = Dv / 16;   // <= NB column blocks of 16
-    // P.V accumulators (FP64 MFMA: FP32 accumulation over long rows drifts
-    // beyond the 1e-6 bar)
-    doublex4 acc[NB];
+    if (tx == 0)
+        for (int r = 0; r < 4; ++r) {
+            RowState z;
+            z.m_t = z.m_mix = z.m_ref = -INFINITY;
+            z.cnt = 0;
+            z.l_mix = z.l_ref = z.kl_a = z.l_lo = z.kl_b = 0.0;
+            sm.row[ty * 4 + r] = z;
+        }
+    doublex4 acc[NB];   // P.V accumulators (FP64 MFMA; FP32 drifts beyond 1e-6)
 #pragma unroll
     for (int q = 0; q < NB; ++q)
         acc[q] = doublex4{0.0, 0.0, 0.0, 0.0};
@@ -133,53 +153,70 @@ __global__ __launch_bounds__(kThreads) void relaxed_kernel(RelaxedArgs a)
                          : (a.pc.mu <= 10 && qsafe && !a.unsafe_k[bh * a.tiles + t]) ? PATH_FAST
                                                                                        : PATH_EXACT;
         if (FAST_KERNEL || path == PATH_FAST) {
-            relaxed_tile_scores<PATH_FAST>(sm, a, Qh, Kh, row0, col0, lo, ref);
+            relaxed_tile_scores<PATH_FAST>(sm.u.tile, a, Qh, Kh, row0, col0, lo, ref);
         } else if (path == PATH_EXACT) {
             if (tid == 0 && a.exact_tiles)
                 atomicAdd(a.exact_tiles, 1ull);
-            relaxed_tile_scores<PATH_EXACT>(sm, a, Qh, Kh, row0, col0, lo, ref);
+            relaxed_tile_scores<PATH_EXACT>(sm.u.tile, a, Qh, Kh, row0, col0, lo, ref);
         } else {
-            relaxed_tile_scores<PATH_FP32>(sm, a, Qh, Kh, row0, col0, lo, ref);
+            relaxed_tile_scores<PATH_FP32>(sm.u.tile, a, Qh, Kh, row0, col0, lo, ref);
+        }
+
+        // V tile loads start now and land during the softmax epilogue.
+        float4 vreg[V4];
+#pragma unroll
+        for (int u = 0; u < V4; ++u) {
+            const int e = tid + u * kThreads;
+            const int key = e / (DV / 4), col = (e % (DV / 4)) * 4;
+            float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (e < NV4 && col0 + key < S && col < D)
+                x = *reinterpret_cast<const float4 *>(Vh + (size_t)(col0 + key) * D + col);
+            vreg[u] = x;
         }
 
         float pmix[4][4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
+        const int gsh = (lane >> 4) * 16;
+        // one query row at a time, with a compile-time row index so that the
+        // score and state arrays stay in registers
+        auto row_step = [&](auto rc) {
+            constexpr int r = decltype(rc)::value;
             const int i = row0 + ty * 4 + r;
             bool valid[4];
-            float bmax = -INFINITY;
+            float bl = -INFINITY;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const int j = col0 + tx + 16 * c;
                 valid[c] = i < S && j < S && (!a.causal || j <= i);
                 if (valid[c])
-                    bmax = fmaxf(bmax, lo[r][c]);
+                    bl = fmaxf(bl, lo[r][c]);
             }
-            bmax = group16_max(bmax);
-            m_t[r] = fmaxf(m_t[r], bmax);
+            bl = group16_max(bl);
+            RowState &rs = sm.row[ty * 4 + r];
+            const float m_t = rs.m_t, m_mix = rs.m_mix, m_ref = rs.m_ref;
+            const float mt_new = fmaxf(m_t, bl);
 
             // selection and y^mix
+            double E[4];
             float mix[4];
             bool sel[4];
+            float bm = -INFINITY, br = -INFINITY;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                sel[c] = false;
-                if (valid[c]) {
-                    const double crit = 2.0 * exp((double)lo[r][c] - (double)m_t[r]) *
-                                        fabs((double)lo[r][c]);
-                    sel[c] = crit > a.tau;
-                }
+                E[c] = valid[c] ? exp64((double)lo[r][c] - (double)mt_new) : 0.0;
+                sel[c] = valid[c] && 2.0 * E[c] * fabs((double)lo[r][c]) > a.tau;
                 mix[c] = sel[c] ? ref[r][c] : lo[r][c];
+                if (valid[c]) {
+                    bm = fmaxf(bm, mix[c]);
+                    br = fmaxf(br, ref[r][c]);
+                }
             }
             // mask bits: ballot per key offset c, 16 bits per row group
-            const int gsh = (lane >> 4) * 16;
             uint32_t bits[4];
 #pragma unroll
             for (int c = 0; c < 4; ++c)
                 bits[c] = (uint32_t)(__ballot(sel[c]) >> gsh) & 0xffffu;
+            const uint32_t w0 = bits[0] | (bits[1] << 16), w1 = bits[2] | (bits[3] << 16);
             if (i < S) {
-                const uint32_t w0 = bits[0] | (bits[1] << 16), w1 = bits[2] | (bits[3] << 16);
-                cnt[r] += tx == 0 ? (uint32_t)(__popc(w0) + __popc(w1)) : 0u;
                 if (a.mask && tx == 0) {
                     const uint64_t mrow = ((uint64_t)bh * S + i) * (uint64_t)a.W;
                     if (2 * t < a.W)
@@ -187,149 +224,136 @@ __global__ __launch_bounds__(kThreads) void relaxed_kernel(RelaxedArgs a)
                     if (2 * t + 1 < a.W)
                         a.mask[mrow + 2 * t + 1] = w1;
                 }
-                const uint64_t yrow = ((uint64_t)bh * S + i) * (uint64_t)S;
+                if (a.ymix_raw || a.yref_out) {
+                    const uint64_t yrow = ((uint64_t)bh * S + i) * (uint64_t)S;
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    if (!valid[c])
-                        continue;
-                    const int j = col0 + tx + 16 * c;
-                    if (a.ymix_raw)
-                        a.ymix_raw[yrow + j] = mix[c];
-                    if (a.yref_out)
-                        a.yref_out[yrow + j] = ref[r][c];
+                    for (int c = 0; c < 4; ++c) {
+                        if (!valid[c])
+                            continue;
+                        const int j = col0 + tx + 16 * c;
+                        if (a.ymix_raw)
+                            a.ymix_raw[yrow + j] = mix[c];
+                        if (a.yref_out)
+                            a.yref_out[yrow + j] = ref[r][c];
+                    }
                 }
             }
 
-            // online softmax of y^mix
-            float bm = -INFINITY, br = -INFINITY, bl = -INFINITY;
-#pragma unroll
-            for (int c = 0; c < 4; ++c)
-                if (valid[c]) {
-                    bm = fmaxf(bm, mix[c]);
-                    br = fmaxf(br, ref[r][c]);
-                    bl = fmaxf(bl, lo[r][c]);
-                }
+            // online softmax of y^mix and reference statistics
             bm = group16_max(bm);
             br = group16_max(br);
-            const float mm_new = fmaxf(m_mix[r], bm);
-            const float mr_new = fmaxf(m_ref[r], br);
-            const double alpha = (m_mix[r] == -INFINITY) ? 0.0 : exp((double)m_mix[r] - (double)mm_new);
-            const double beta = (m_ref[r] == -INFINITY) ? 0.0 : exp((double)m_ref[r] - (double)mr_new);
-            double sl = 0.0, sr = 0.0, sa = 0.0;
+            const float mm_new = fmaxf(m_mix, bm);
+            const float mr_new = fmaxf(m_ref, br);
+            const double alpha = exp_delta(m_mix, mm_new);
+            // row factors; a factor that would overflow (maxima more than
+            // ~700 apart) falls back to a direct exp per score
+            const double f_lo = exp64((double)mt_new - (double)mm_new);
+            const double f_ref = exp64((double)mr_new - (double)mm_new);
+            const bool direct = !(f_lo < 1e300 && f_ref < 1e300);
+            double sl = 0.0, sr = 0.0, sa = 0.0, sll = 0.0, sb = 0.0;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 pmix[r][c] = 0.0f;
                 if (valid[c]) {
-                    const double pe = exp((double)mix[c] - (double)mm_new);
+                    const double er = exp64((double)ref[r][c] - (double)mr_new);
+                    double pe;
+                    if (!direct)
+                        pe = sel[c] ? er * f_ref : E[c] * f_lo;
+                    else
+                        pe = exp64((double)mix[c] - (double)mm_new);
                     pmix[r][c] = (float)pe;
                     sl += pe;
-                    const double er = exp((double)ref[r][c] - (double)mr_new);
                     sr += er;
                     sa += er * ((double)ref[r][c] - (double)mix[c]);
+                    sll += E[c];
+                    sb += er * ((double)ref[r][c] - (double)lo[r][c]);
                 }
             }
-            l_mix[r] = l_mix[r] * alpha + sl;
-            l_ref[r] = l_ref[r] * beta + sr;
-            kl_a[r] = kl_a[r] * beta + sa;
-            m_mix[r] = (i < S) ? mm_new : m_mix[r];
-            m_ref[r] = (i < S) ? mr_new : m_ref[r];
+            sl = group16_sum(sl);
+            sr = group16_sum(sr);
+            sa = group16_sum(sa);
+            if (want_lowp) {
+                sll = group16_sum(sll);
+                sb = group16_sum(sb);
+            }
+            if (i < S && tx == 0) {
+                const double beta = exp_delta(m_ref, mr_new);
+                rs.l_mix = rs.l_mix * alpha + sl;
+                rs.l_ref = rs.l_ref * beta + sr;
+                rs.kl_a = rs.kl_a * beta + sa;
+                if (want_lowp) {
+                    rs.l_lo = rs.l_lo * exp_delta(m_t, mt_new) + sll;
+                    rs.kl_b = rs.kl_b * beta + sb;
+                }
+                rs.m_t = mt_new;
+                rs.m_mix = mm_new;
+                rs.m_ref = mr_new;
+                rs.cnt += (uint32_t)(__popc(w0) + __popc(w1));
+            }
             // rescale this row's P.V accumulators (MFMA rows 4*(lane/16)+r)
 #pragma unroll
             for (int q = 0; q < NB; ++q)
-                acc[q][r] *= alpha;
+                acc[q][r] *= (i < S) ? alpha : 0.0;
+        };
+        row_step(std::integral_constant<int, 0>{});
+        row_step(std::integral_constant<int, 1>{});
+        row_step(std::integral_constant<int, 2>{});
+        row_step(std::integral_constant<int, 3>{});
 
-            if (want_lowp) {
-                bl = group16_max(bl);
-                const float ml_new = fmaxf(m_lo[r], bl);
-                const double gam = (m_lo[r] == -INFINITY) ? 0.0 : exp((double)m_lo[r] - (double)ml_new);
-                const double betal = beta;
-                double sll = 0.0, sb = 0.0;
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    if (valid[c]) {
-                        sll += exp((double)lo[r][c] - (double)ml_new);
-                        sb += exp((double)ref[r][c] - (double)mr_new) *
-                              ((double)ref[r][c] - (double)lo[r][c]);
-                    }
-                l_lo[r] = l_lo[r] * gam + sll;
-                kl_b[r] = kl_b[r] * betal + sb;
-                m_lo[r] = (i < S) ? ml_new : m_lo[r];
-            }
-        }
-
-        // P.V: P tile to LDS (aliases the score staging), V tile to LDS, MFMA.
+        // P.V: P tile (aliases the score staging) and V tile to LDS, MFMA.
         __syncthreads();
 #pragma unroll
         for (int r = 0; r < 4; ++r)
 #pragma unroll
             for (int c = 0; c < 4; ++c)
                 sm.u.p[ty * 4 + r][tx + 16 * c] = pmix[r][c];
-        for (int h = 0; h < Dv; h += 128) {
-            const int Dc = min(128, Dv - h);
-            const int n4 = kTile * Dc / 4;
-            if (h > 0)
-                __syncthreads();
-            for (int e = tid; e < n4; e += kThreads) {
-                const int key = e / (Dc / 4), col = h + (e % (Dc / 4)) * 4;
-                float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (col0 + key < S && col < D)
-                    x = *reinterpret_cast<const float4 *>(Vh + (size_t)(col0 + key) * D + col);
-                *reinterpret_cast<float4 *>(sm.v + key * Dc + (col - h)) = x;
-            }
-            __syncthreads();
-#pragma unroll 4
-            for (int kk = 0; kk < kTile / 4; ++kk) {
-                const float av = sm.u.p[wave * 16 + mfma64_row(lane & 15)][kk * 4 + (lane >> 4)];
 #pragma unroll
-                for (int q = 0; q < NB; ++q) {
-                    if (q < nb && q * 16 >= h && q * 16 < h + Dc) {
-                        const float bv = sm.v[(kk * 4 + (lane >> 4)) * Dc + q * 16 - h + (lane & 15)];
-                        acc[q] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)av, (double)bv,
-                                                                      acc[q], 0, 0, 0);
-                    }
-                }
-            }
+        for (int u = 0; u < V4; ++u) {
+            const int e = tid + u * kThreads;
+            const int key = e / (DV / 4), col = (e % (DV / 4)) * 4;
+            if (e < NV4)
+                *reinterpret_cast<float4 *>(&sm.v[key][col]) = vreg[u];
         }
         __syncthreads();
+#pragma unroll 4
+        for (int kk = 0; kk < kTile / 4; ++kk) {
+            const double av = sm.u.p[wave * 16 + mfma64_row(lane & 15)][kk * 4 + (lane >> 4)];
+#pragma unroll
+            for (int q = 0; q < NB; ++q) {
+                const double bv = sm.v[kk * 4 + (lane >> 4)][q * 16 + (lane & 15)];
+                acc[q] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc[q], 0, 0, 0);
+            }
+        }
     }
 
-    // Finalise rows: combine the 16 lanes' partial sums.
+    // Finalise rows.
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int i = row0 + ty * 4 + r;
-        const double lm = group16_sum(l_mix[r]);
-        const double lr = group16_sum(l_ref[r]);
-        const double ka = group16_sum(kl_a[r]);
-        const uint32_t ct = group16_sum_u(cnt[r]);
-        double ll = 0.0, kb = 0.0;
-        if (want_lowp) {
-            ll = group16_sum(l_lo[r]);
-            kb = group16_sum(kl_b[r]);
-        }
         if (i >= S)
             continue;
+        const RowState rs = sm.row[ty * 4 + r];
         const uint64_t row = (uint64_t)bh * S + i;
         if (a.mask)   // words of key tiles past the causal limit hold no selection
             for (int w = 2 * (t_end + 1) + tx; w < a.W; w += 16)
                 a.mask[row * (uint64_t)a.W + w] = 0u;
         if (tx == 0) {
+            const double lse_ref = (double)rs.m_ref + log(rs.l_ref);
             if (a.row_kl)
-                a.row_kl[row] = ka / lr + ((double)m_mix[r] + log(lm)) - ((double)m_ref[r] + log(lr));
+                a.row_kl[row] = rs.kl_a / rs.l_ref + ((double)rs.m_mix + log(rs.l_mix)) - lse_ref;
             if (want_lowp)
-                a.row_kl_lowp[row] = kb / lr + ((double)m_lo[r] + log(ll)) - ((double)m_ref[r] + log(lr));
+                a.row_kl_lowp[row] = rs.kl_b / rs.l_ref + ((double)rs.m_t + log(rs.l_lo)) - lse_ref;
             if (a.row_count)
-                a.row_count[row] = ct;
+                a.row_count[row] = rs.cnt;
             if (a.row_m)
-                a.row_m[row] = m_mix[r];
+                a.row_m[row] = rs.m_mix;
             if (a.row_l)
-                a.row_l[row] = lm;
+                a.row_l[row] = rs.l_mix;
         }
         // out rows of this lane's MFMA accumulators are 4*(lane/16)+r = ty*4+r
-        const double inv = 1.0 / lm;
+        const double inv = 1.0 / rs.l_mix;
 #pragma unroll
         for (int q = 0; q < NB; ++q) {
-            if (q >= nb)
-                continue;
             const int col = q * 16 + (lane & 15);
             if (col < D)
                 a.out[row * (uint64_t)D + col] = (float)(acc[q][r] * inv);
@@ -370,19 +394,20 @@ hipError_t launch_relaxed(const Problem &p, const uint8_t *unsafe, float *out, u
     a.row_l = row_l;
     a.exact_tiles = exact_tiles;
     const uint64_t grid = (uint64_t)p.BH * p.tiles;
-    if (fast) {
-        if (p.mu > 10)
-            return hipSuccess;
-        if (a.Dv <= 64)
-            hipLaunchKernelGGL((relaxed_kernel<4, true>), dim3((unsigned)grid), dim3(kThreads), 0, st, a);
+    const dim3 g((unsigned)grid), b(kThreads);
+    if (fast && p.mu > 10)
+        return hipSuccess;
+    if (a.Dv <= 64) {
+        if (fast)
+            hipLaunchKernelGGL((relaxed_kernel<4, true>), g, b, 0, st, a);
         else
-            hipLaunchKernelGGL((relaxed_kernel<8, true>), dim3((unsigned)grid), dim3(kThreads), 0, st, a);
-        return hipGetLastError();
+            hipLaunchKernelGGL((relaxed_kernel<4, false>), g, b, 0, st, a);
+    } else {
+        if (fast)
+            hipLaunchKernelGGL((relaxed_kernel<8, true>), g, b, 0, st, a);
+        else
+            hipLaunchKernelGGL((relaxed_kernel<8, false>), g, b, 0, st, a);
     }
-    if (a.Dv <= 64)
-        hipLaunchKernelGGL((relaxed_kernel<4, false>), dim3((unsigned)grid), dim3(kThreads), 0, st, a);
-    else
-        hipLaunchKernelGGL((relaxed_kernel<8, false>), dim3((unsigned)grid), dim3(kThreads), 0, st, a);
     return hipGetLastError();
 }
 
@@ -395,11 +420,11 @@ __global__ __launch_bounds__(kThreads) void normalise_kernel(const float *ymix, 
     const int i = (int)(r % (uint64_t)S);
     const int n = causal ? i + 1 : S;
     const float m = row_m[r];
-    const double inv = 1.0 / row_l[r];
+    const double log_l = log(row_l[r]);
     const float *y = ymix + r * (uint64_t)S;
     float *pr = probs + r * (uint64_t)S;
     for (int j = threadIdx.x; j < S; j += kThreads)
-        pr[j] = j < n ? (float)(exp((double)y[j] - (double)m) * inv) : 0.0f;
+        pr[j] = j < n ? exp_f32((double)y[j] - (double)m - log_l) : 0.0f;
 }
 
 hipError_t launch_normalise(const Problem &p, const float *ymix, const float *row_m,
