@@ -11,7 +11,7 @@
 
 namespace lamp {
 
-typedef double doublex4 __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr int kFinRows = 64;   // query rows per work-group (16 per wave)
 
@@ -24,8 +24,11 @@ struct FinishArgs {
 };
 
 // probs_j = exp(y^mix_j - lse_mix) on the valid keys (0 elsewhere), and
-// out = P.V accumulated in double on the FP64 MFMA (FP32 accumulation over
-// hundreds of keys drifts by ~10 ulp of a dominant term, beyond 1e-6).
+// out = P.V.  P.V runs on the FP32 MFMA (v_mfma_f32_16x16x4f32) into a
+// partial sum that is flushed into a double accumulator every 16 keys: one
+// partial carries at most 4 FP32 roundings (relative 2.4e-7 of its
+// sum_j p_j |v_jd|), so the total stays inside the 1e-6 bar, whereas FP32
+// accumulation over hundreds of keys drifts by ~10 ulp of a dominant term.
 // Each KS-key step: thread (row tid/4, keys KS/4 * (tid%4)..) forms KS/4
 // probabilities; the P and V tiles go to double-buffered LDS (one barrier per
 // step) while the next step's scores and V rows are already being loaded;
@@ -124,10 +127,12 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(FinishArgs a)
         }
     };
 
-    doublex4 acc[NB];
+    double acc[NB][4];
 #pragma unroll
     for (int q = 0; q < NB; ++q)
-        acc[q] = doublex4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            acc[q][v] = 0.0;
     float ycur[KPT], ynext[KPT];
     float4 vcur[V4], vnext[V4];
     if (nsteps > 0) {
@@ -172,13 +177,26 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(FinishArgs a)
         }
         __syncthreads();
 #pragma unroll
-        for (int kk = 0; kk < kFinKeys / 4; ++kk) {
-            const double av = sP[buf][wave * 16 + mfma64_row(lane & 15)][kk * 4 + (lane >> 4)];
+        for (int k16 = 0; k16 < kFinKeys / 16; ++k16) {
+            floatx4 part[NB];
 #pragma unroll
-            for (int q = 0; q < NB; ++q) {
-                const double bv = sV[buf][kk * 4 + (lane >> 4)][q * 16 + (lane & 15)];
-                acc[q] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc[q], 0, 0, 0);
+            for (int q = 0; q < NB; ++q)
+                part[q] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k4 = 0; k4 < 4; ++k4) {
+                const int kk = k16 * 4 + k4;
+                const float av = sP[buf][wave * 16 + (lane & 15)][kk * 4 + (lane >> 4)];
+#pragma unroll
+                for (int q = 0; q < NB; ++q) {
+                    const float bv = sV[buf][kk * 4 + (lane >> 4)][q * 16 + (lane & 15)];
+                    part[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, part[q], 0, 0, 0);
+                }
             }
+#pragma unroll
+            for (int q = 0; q < NB; ++q)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    acc[q][v] += (double)part[q][v];
         }
 #pragma unroll
         for (int e = 0; e < KPT; ++e)

@@ -214,16 +214,6 @@ __device__ __forceinline__ void tile_scores(const TileAcc &acc, const PsConst &p
 }
 
 // ---------------------------------------------------------------------------
-// FP64 MFMA 16x16x4 (v_mfma_f64_16x16x4f64) operand layout: A[i][k] comes from
-// lane i + 16k, B[k][j] from lane j + 16k; the result D[i][j] lands in lane
-// j + 16 (i % 4), register i / 4 (rows interleave by 4, unlike the FP32 16x16x4
-// form whose lane j + 16 (i / 4), register i % 4 holds D[i][j]).  Feeding A's
-// row i from matrix row mfma64_row(i) puts matrix row 4 (lane / 16) + v in
-// register v of each lane, the same rows as the FP32 layout.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ int mfma64_row(int i) { return 4 * (i & 3) + (i >> 2); }
-
-// ---------------------------------------------------------------------------
 // Wave reductions (wave64).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float wave_max(float v)

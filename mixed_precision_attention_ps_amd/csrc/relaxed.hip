@@ -23,7 +23,7 @@
 
 namespace lamp {
 
-typedef double doublex4 __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 struct RelaxedArgs {
     const float *q, *k, *v;
@@ -140,10 +140,15 @@ void relaxed_kernel(RelaxedArgs a)
             z.l_mix = z.l_ref = z.kl_a = z.l_lo = z.kl_b = 0.0;
             sm.row[ty * 4 + r] = z;
         }
-    doublex4 acc[NB];   // P.V accumulators (FP64 MFMA; FP32 drifts beyond 1e-6)
+    // P.V accumulators in double: the FP32 MFMA partial of every 16 keys is
+    // flushed into them (at most 4 FP32 roundings per partial, 2.4e-7 of its
+    // magnitude; FP32 accumulation over a long row drifts beyond 1e-6)
+    double acc[NB][4];
 #pragma unroll
     for (int q = 0; q < NB; ++q)
-        acc[q] = doublex4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            acc[q][v] = 0.0;
 
     for (int t = 0; t <= t_end; ++t) {
         const int col0 = t * kTile;
@@ -315,14 +320,27 @@ void relaxed_kernel(RelaxedArgs a)
                 *reinterpret_cast<float4 *>(&sm.v[key][col]) = vreg[u];
         }
         __syncthreads();
-#pragma unroll 4
-        for (int kk = 0; kk < kTile / 4; ++kk) {
-            const double av = sm.u.p[wave * 16 + mfma64_row(lane & 15)][kk * 4 + (lane >> 4)];
 #pragma unroll
-            for (int q = 0; q < NB; ++q) {
-                const double bv = sm.v[kk * 4 + (lane >> 4)][q * 16 + (lane & 15)];
-                acc[q] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc[q], 0, 0, 0);
+        for (int k16 = 0; k16 < kTile / 16; ++k16) {
+            floatx4 part[NB];
+#pragma unroll
+            for (int q = 0; q < NB; ++q)
+                part[q] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k4 = 0; k4 < 4; ++k4) {
+                const int kk = k16 * 4 + k4;
+                const float av = sm.u.p[wave * 16 + (lane & 15)][kk * 4 + (lane >> 4)];
+#pragma unroll
+                for (int q = 0; q < NB; ++q) {
+                    const float bv = sm.v[kk * 4 + (lane >> 4)][q * 16 + (lane & 15)];
+                    part[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, part[q], 0, 0, 0);
+                }
             }
+#pragma unroll
+            for (int q = 0; q < NB; ++q)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    acc[q][v] += (double)part[q][v];
         }
     }
 
@@ -411,27 +429,45 @@ hipError_t launch_relaxed(const Problem &p, const uint8_t *unsafe, float *out, u
     return hipGetLastError();
 }
 
-// probs of the relaxed path from its raw y^mix and final row statistics.
+// probs of the relaxed path from its raw y^mix and final row statistics:
+// one wave per row, 16-byte loads and stores when rows are 16-byte aligned.
 __global__ __launch_bounds__(kThreads) void normalise_kernel(const float *ymix, const float *row_m,
                                                              const double *row_l, float *probs,
-                                                             int S, int causal)
+                                                             int S, int causal, uint64_t n_rows)
 {
-    const uint64_t r = blockIdx.x;
+    const int lane = threadIdx.x & 63;
+    const uint64_t r = (uint64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= n_rows)
+        return;
     const int i = (int)(r % (uint64_t)S);
     const int n = causal ? i + 1 : S;
-    const float m = row_m[r];
-    const double log_l = log(row_l[r]);
+    const double shift = (double)row_m[r] + log(row_l[r]);
     const float *y = ymix + r * (uint64_t)S;
     float *pr = probs + r * (uint64_t)S;
-    for (int j = threadIdx.x; j < S; j += kThreads)
-        pr[j] = j < n ? exp_f32((double)y[j] - (double)m - log_l) : 0.0f;
+    if ((S & 3) == 0) {
+        for (int j = lane * 4; j < S; j += 256) {
+            float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (j < n)
+                x = *reinterpret_cast<const float4 *>(y + j);
+            float4 o;
+            o.x = j < n ? exp_f32((double)x.x - shift) : 0.0f;
+            o.y = j + 1 < n ? exp_f32((double)x.y - shift) : 0.0f;
+            o.z = j + 2 < n ? exp_f32((double)x.z - shift) : 0.0f;
+            o.w = j + 3 < n ? exp_f32((double)x.w - shift) : 0.0f;
+            *reinterpret_cast<float4 *>(pr + j) = o;
+        }
+    } else {
+        for (int j = lane; j < S; j += 64)
+            pr[j] = j < n ? exp_f32((double)y[j] - shift) : 0.0f;
+    }
 }
 
 hipError_t launch_normalise(const Problem &p, const float *ymix, const float *row_m,
                             const double *row_l, float *probs, hipStream_t st)
 {
-    hipLaunchKernelGGL(normalise_kernel, dim3((unsigned)p.n_rows), dim3(kThreads), 0, st, ymix,
-                       row_m, row_l, probs, p.S, p.causal);
+    const uint64_t grid = (p.n_rows + 3) / 4;
+    hipLaunchKernelGGL(normalise_kernel, dim3((unsigned)grid), dim3(kThreads), 0, st, ymix, row_m,
+                       row_l, probs, p.S, p.causal, p.n_rows);
     return hipGetLastError();
 }
 
