@@ -37,8 +37,8 @@ METRIC = "LAMP attention scores/sec at μ=4 (GPT-2-XL layer) + % VALU/HBM roofli
 ALU_PEAK = 256 * 4 * 32 * 2.4e9
 HBM_PEAK = 8.0e12
 
-KERNEL_SOURCES = ["lamp_device.h", "lamp_internal.h", "scores.hip", "select.hip", "finish.hip",
-                  "relaxed.hip"]
+KERNEL_SOURCES = ["lamp_device.h", "lamp_exp.h", "lamp_internal.h", "scores.hip", "select.hip",
+                  "rows.hip", "finish.hip", "relaxed.hip"]
 
 
 def log(*a):
@@ -161,9 +161,12 @@ def main():
     wall = time.perf_counter() - t0
     gpu_ms = t_start.elapsed_time(t_stop)
 
-    ran = (["scan", "exact", "scores"] + (["finish"] if probs is not None else [])
-           if args.mode == "relaxed" else
-           ["scan", "exact", "scores", "select", "recompute", "finish"])
+    if args.mode == "relaxed":
+        ran = ["scan", "exact", "scores"] + (["finish"] if probs is not None else [])
+    elif args.mode == "strict" and S <= 1024:   # fused row pass: select + recompute in one
+        ran = ["scan", "exact", "scores", "select", "finish"]
+    else:
+        ran = ["scan", "exact", "scores", "select", "recompute", "finish"]
     stages = {}
     for name in ran:
         si = lamp.STAGES.index(name)

@@ -21,6 +21,7 @@ struct FinishArgs {
     float *probs, *out;
     double *row_kl;
     int S, D, causal, blocks_per_head;
+    ExpCoef ek;
 };
 
 // probs_j = exp(y^mix_j - lse_mix) on the valid keys (0 elsewhere), and
@@ -34,7 +35,9 @@ struct FinishArgs {
 // step) while the next step's scores and V rows are already being loaded;
 // wave w multiplies rows 16w..16w+15 of P by V.  DV = 16 NB is the padded
 // head dimension (compile-time, so every MFMA and LDS index is static).
-template <int NB, int KS>
+// PIN: `ymix` already holds the probabilities (P.V only: no lse, no probs
+// write).
+template <int NB, int KS, bool PIN>
 __global__ __launch_bounds__(kThreads) void finish_kernel(FinishArgs a)
 {
     constexpr int kFinKeys = KS;          // keys per step
@@ -54,7 +57,7 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(FinishArgs a)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
     // lse of each row; rows flagged by the recompute get a pass over the row.
-    for (int rr = 0; rr < kFinRows / 4; ++rr) {
+    for (int rr = 0; rr < (PIN ? 0 : kFinRows / 4); ++rr) {
         const int lr = wave * (kFinRows / 4) + rr;
         const int i = row0 + lr;
         double lse = 0.0;
@@ -71,7 +74,7 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(FinishArgs a)
                 mm = wave_max(mm);
                 double l = 0.0;
                 for (int j = lane; j < n; j += 64)
-                    l += exp64((double)ym[j] - (double)mm);
+                    l += exp64((double)ym[j] - (double)mm, a.ek);
                 l = wave_sum(l);
                 lse = (double)mm + log(l);
                 if (lane == 0 && a.row_kl)
@@ -89,8 +92,8 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(FinishArgs a)
     const int np = prow_ok ? (a.causal ? ip + 1 : S) : 0;
     const uint64_t rp = (uint64_t)bh * S + (prow_ok ? ip : 0);
     const float *ymp = a.ymix + rp * (uint64_t)S;
-    float *prp = a.probs ? a.probs + rp * (uint64_t)S : nullptr;
-    const double lse_p = s_lse[prow];
+    float *prp = (!PIN && a.probs) ? a.probs + rp * (uint64_t)S : nullptr;
+    const double lse_p = PIN ? 0.0 : s_lse[prow];
     const bool vec = (S & 3) == 0;
     const int nkeys = a.causal ? min(S, row0 + kFinRows) : S;   // keys the block attends
     const int nsteps = (nkeys + kFinKeys - 1) / kFinKeys;
@@ -150,7 +153,7 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(FinishArgs a)
         const int jb = j0 + kseg;
 #pragma unroll
         for (int e = 0; e < KPT; ++e)
-            pv[e] = (jb + e < np) ? exp_f32((double)ycur[e] - lse_p) : 0.0f;
+            pv[e] = (jb + e < np) ? (PIN ? ycur[e] : exp_f32((double)ycur[e] - lse_p)) : 0.0f;
         if (prp && prow_ok) {
             if (vec) {
 #pragma unroll
@@ -232,6 +235,26 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(FinishArgs a)
     }
 }
 
+template <bool PIN>
+static hipError_t launch_finish_kernel(const FinishArgs &a, const Problem &p, hipStream_t st)
+{
+    const dim3 grid((unsigned)((uint64_t)p.BH * a.blocks_per_head)), block(kThreads);
+    switch ((p.D + 15) / 16) {
+    case 1: hipLaunchKernelGGL((finish_kernel<1, 32, PIN>), grid, block, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((finish_kernel<2, 32, PIN>), grid, block, 0, st, a); break;
+    case 3: hipLaunchKernelGGL((finish_kernel<3, 32, PIN>), grid, block, 0, st, a); break;
+    case 4: hipLaunchKernelGGL((finish_kernel<4, 32, PIN>), grid, block, 0, st, a); break;
+    case 5: hipLaunchKernelGGL((finish_kernel<5, 32, PIN>), grid, block, 0, st, a); break;
+    case 6: hipLaunchKernelGGL((finish_kernel<6, 32, PIN>), grid, block, 0, st, a); break;
+    case 7: hipLaunchKernelGGL((finish_kernel<7, 32, PIN>), grid, block, 0, st, a); break;
+    case 8: hipLaunchKernelGGL((finish_kernel<8, 32, PIN>), grid, block, 0, st, a); break;
+    case 9: case 10: case 11: case 12:
+        hipLaunchKernelGGL((finish_kernel<12, 16, PIN>), grid, block, 0, st, a); break;
+    default: hipLaunchKernelGGL((finish_kernel<16, 16, PIN>), grid, block, 0, st, a); break;
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_finish(const Problem &p, const float *ymix, const RowStats *rs, float *probs,
                          float *out, double *row_kl, hipStream_t st)
 {
@@ -246,21 +269,25 @@ hipError_t launch_finish(const Problem &p, const float *ymix, const RowStats *rs
     a.D = p.D;
     a.causal = p.causal;
     a.blocks_per_head = (p.S + kFinRows - 1) / kFinRows;
-    const dim3 grid((unsigned)((uint64_t)p.BH * a.blocks_per_head)), block(kThreads);
-    switch ((p.D + 15) / 16) {
-    case 1: hipLaunchKernelGGL((finish_kernel<1, 32>), grid, block, 0, st, a); break;
-    case 2: hipLaunchKernelGGL((finish_kernel<2, 32>), grid, block, 0, st, a); break;
-    case 3: hipLaunchKernelGGL((finish_kernel<3, 32>), grid, block, 0, st, a); break;
-    case 4: hipLaunchKernelGGL((finish_kernel<4, 32>), grid, block, 0, st, a); break;
-    case 5: hipLaunchKernelGGL((finish_kernel<5, 32>), grid, block, 0, st, a); break;
-    case 6: hipLaunchKernelGGL((finish_kernel<6, 32>), grid, block, 0, st, a); break;
-    case 7: hipLaunchKernelGGL((finish_kernel<7, 32>), grid, block, 0, st, a); break;
-    case 8: hipLaunchKernelGGL((finish_kernel<8, 32>), grid, block, 0, st, a); break;
-    case 9: case 10: case 11: case 12:
-        hipLaunchKernelGGL((finish_kernel<12, 16>), grid, block, 0, st, a); break;
-    default: hipLaunchKernelGGL((finish_kernel<16, 16>), grid, block, 0, st, a); break;
-    }
-    return hipGetLastError();
+    a.ek = make_exp_coef();
+    return launch_finish_kernel<false>(a, p, st);
+}
+
+hipError_t launch_pv(const Problem &p, const float *probs, float *out, hipStream_t st)
+{
+    FinishArgs a;
+    a.ymix = probs;
+    a.v = p.v;
+    a.rs = nullptr;
+    a.probs = nullptr;
+    a.out = out;
+    a.row_kl = nullptr;
+    a.S = p.S;
+    a.D = p.D;
+    a.causal = p.causal;
+    a.blocks_per_head = (p.S + kFinRows - 1) / kFinRows;
+    a.ek = make_exp_coef();
+    return launch_finish_kernel<true>(a, p, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -338,11 +365,11 @@ hipError_t launch_zero(void *ptr, size_t bytes, hipStream_t st)
 // Diagnostic: the device exponentials on caller data (accuracy tests).
 // ---------------------------------------------------------------------------
 namespace lamp {
-__global__ void exp_probe_kernel(const double *x, double *y64, float *y32, int n)
+__global__ void exp_probe_kernel(const double *x, double *y64, float *y32, int n, ExpCoef ek)
 {
     const int e = blockIdx.x * blockDim.x + threadIdx.x;
     if (e < n) {
-        y64[e] = exp64(x[e]);
+        y64[e] = exp64(x[e], ek);
         y32[e] = exp_f32(x[e]);
     }
 }
@@ -356,6 +383,6 @@ extern "C" int lamp_diag_exp(const double *x, double *y64, float *y32, int n, vo
         return 0;
     (void)hipGetLastError();
     hipLaunchKernelGGL(lamp::exp_probe_kernel, dim3((n + 255) / 256), dim3(256), 0,
-                       (hipStream_t)stream, x, y64, y32, n);
+                       (hipStream_t)stream, x, y64, y32, n, lamp::make_exp_coef());
     return hipGetLastError() == hipSuccess ? 0 : -3;
 }

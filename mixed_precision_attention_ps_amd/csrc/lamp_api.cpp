@@ -2,10 +2,14 @@
 // workspace layout, launch sequence, errors.
 //
 // Launch sequence of one call (LAMP summary, "Implementation strategy"):
-//   strict / random:  operand scan -> PS(mu) + FP32 score tiles -> row
-//                     softmax + selection + compaction (random: strict counts,
-//                     then hash selection) -> gather FP32 recompute ->
-//                     softmax + P.V + KL -> [stats]
+//   strict, S <= 1024: operand scan -> PS(mu) score tiles (+ per-tile FP32
+//                     reference statistics) -> fused row pass (softmax
+//                     statistics, selection, compaction, gather FP32
+//                     recompute, probabilities, KL) -> P.V -> [stats]
+//   strict (longer rows) / random: operand scan -> PS(mu) + FP32 score
+//                     tiles -> row softmax + selection + compaction (random:
+//                     strict counts, then hash selection) -> gather FP32
+//                     recompute -> softmax + P.V + KL -> [stats]
 //   relaxed:          operand scan -> fused one-pass kernel -> [probs pass]
 //                     -> [stats]
 #include <hip/hip_runtime.h>
@@ -135,7 +139,8 @@ int check_args(const float *q, const float *k, const float *v, int causal, int m
 struct Layout {
     size_t ymix = SIZE_MAX, yref = SIZE_MAX, list = SIZE_MAX, row_count = SIZE_MAX,
            row_kl = SIZE_MAX, row_kl_lowp = SIZE_MAX, unsafe = SIZE_MAX, dstats = SIZE_MAX,
-           row_m = SIZE_MAX, row_l = SIZE_MAX, rowstats = SIZE_MAX;
+           row_m = SIZE_MAX, row_l = SIZE_MAX, rowstats = SIZE_MAX, pbuf = SIZE_MAX,
+           part = SIZE_MAX;
     size_t total = 0;
     size_t take(size_t bytes)
     {
@@ -147,7 +152,12 @@ struct Layout {
 
 struct Needs {
     bool ymix, yref, row_count, row_kl, row_kl_lowp;
+    bool fused;   // strict rows of <= 1024 keys: fused row pass
+    bool pbuf;    // fused: probabilities need their own buffer
+    bool part;    // fused: reference statistics per tile (KL wanted)
 };
+
+constexpr int kFusedMaxS = 1024;
 
 Layout plan(const Sizes &z, int mode, const Needs &n)
 {
@@ -165,6 +175,13 @@ Layout plan(const Sizes &z, int mode, const Needs &n)
             L.row_m = L.take(4 * z.n_rows);
             L.row_l = L.take(8 * z.n_rows);
         }
+    } else if (n.fused) {
+        if (n.ymix)
+            L.ymix = L.take(4 * z.n_scores);
+        if (n.pbuf)
+            L.pbuf = L.take(4 * z.n_scores);
+        if (n.part)
+            L.part = L.take(sizeof(lamp::RefPartial) * z.n_rows * (uint64_t)z.tiles);
     } else {
         if (n.ymix)
             L.ymix = L.take(4 * z.n_scores);
@@ -219,8 +236,15 @@ size_t lamp_workspace_bytes(int B, int H, int S, int D, int mode, int want_probs
     z.n_valid = 0;
     z.n_valid = z.BH * (uint64_t)S * (uint64_t)(S + 1) / 2;   // causal-agnostic bound below
     z.n_valid = z.n_scores > z.n_valid ? z.n_scores : z.n_valid;
-    Needs n{mode == LAMP_RELAXED ? want_probs != 0 : want_probs == 0, true, true, true, true};
-    return plan(z, mode, n).total;
+    Needs n{mode == LAMP_RELAXED ? want_probs != 0 : want_probs == 0, true, true, true, true,
+            false, false, false};
+    size_t total = plan(z, mode, n).total;
+    if (mode == LAMP_STRICT && S <= kFusedMaxS) {
+        Needs f{want_probs == 0, false, true, true, true, true, false, true};
+        const size_t tf = plan(z, mode, f).total;
+        total = tf > total ? tf : total;
+    }
+    return total;
 }
 
 static int run(const float *q, const float *k, const float *v, int B, int H, int S, int D,
@@ -246,13 +270,19 @@ static int run(const float *q, const float *k, const float *v, int B, int H, int
     hipStream_t st = (hipStream_t)p.stream;
     const bool want_stats = stats != nullptr;
 
-    Needs need;
+    Needs need{};
     need.row_count = p.row_count == nullptr;
     need.row_kl = p.row_kl == nullptr && want_stats;
     need.row_kl_lowp = p.row_kl_lowp == nullptr && want_stats;
+    need.fused = mode == LAMP_STRICT && S <= kFusedMaxS;
+    const bool want_kl = want_stats || p.row_kl || p.row_kl_lowp;
     if (mode == LAMP_RELAXED) {
         need.ymix = probs != nullptr;
         need.yref = false;
+    } else if (need.fused) {
+        need.ymix = p.scores_mix == nullptr && probs == nullptr;
+        need.pbuf = p.scores_mix != nullptr && probs == nullptr;
+        need.part = want_kl;
     } else {
         need.ymix = p.scores_mix == nullptr && probs == nullptr;
         need.yref = p.scores_ref == nullptr;
@@ -322,16 +352,43 @@ static int run(const float *q, const float *k, const float *v, int B, int H, int
                          "normalise launch");
             LAMP_HIP_TRY(tm.end(LAMP_STAGE_FINISH), "hipEventRecord");
         }
+    } else if (need.fused) {
+        // y^lo lands in its final buffer: scores_mix (y^mix in place), else
+        // probs (probabilities in place), else the workspace
+        float *ybuf = p.scores_mix ? p.scores_mix : (probs ? probs : at<float>(ws, L.ymix));
+        float *pbuf = probs ? probs : (p.scores_mix ? at<float>(ws, L.pbuf) : ybuf);
+        auto *part = at<lamp::RefPartial>(ws, L.part);
+        LAMP_HIP_TRY(tm.begin(LAMP_STAGE_EXACT), "hipEventRecord");
+        LAMP_HIP_TRY(lamp::launch_ps_scores(P, unsafe, ybuf, p.scores_ref, part,
+                                            &dstats->n_exact_tiles, false, st),
+                     "score kernel launch");
+        LAMP_HIP_TRY(tm.end(LAMP_STAGE_EXACT), "hipEventRecord");
+        LAMP_HIP_TRY(tm.begin(LAMP_STAGE_SCORES), "hipEventRecord");
+        LAMP_HIP_TRY(lamp::launch_ps_scores(P, unsafe, ybuf, p.scores_ref, part,
+                                            &dstats->n_exact_tiles, true, st),
+                     "score kernel launch");
+        LAMP_HIP_TRY(tm.end(LAMP_STAGE_SCORES), "hipEventRecord");
+        LAMP_HIP_TRY(tm.begin(LAMP_STAGE_SELECT), "hipEventRecord");
+        LAMP_HIP_TRY(lamp::launch_strict_rows(P, ybuf, part, mask, row_count, pbuf, p.scores_mix,
+                                              part ? row_kl : nullptr,
+                                              part ? row_kl_lowp : nullptr, st),
+                     "row kernel launch");
+        LAMP_HIP_TRY(tm.end(LAMP_STAGE_SELECT), "hipEventRecord");
+        LAMP_HIP_TRY(tm.begin(LAMP_STAGE_FINISH), "hipEventRecord");
+        LAMP_HIP_TRY(lamp::launch_pv(P, pbuf, out, st), "P.V launch");
+        LAMP_HIP_TRY(tm.end(LAMP_STAGE_FINISH), "hipEventRecord");
     } else {
         float *ymix = p.scores_mix ? p.scores_mix : (probs ? probs : at<float>(ws, L.ymix));
         float *yref = p.scores_ref ? p.scores_ref : at<float>(ws, L.yref);
         uint32_t *list = at<uint32_t>(ws, L.list);
         LAMP_HIP_TRY(tm.begin(LAMP_STAGE_EXACT), "hipEventRecord");
-        LAMP_HIP_TRY(lamp::launch_ps_scores(P, unsafe, ymix, yref, &dstats->n_exact_tiles, false, st),
+        LAMP_HIP_TRY(lamp::launch_ps_scores(P, unsafe, ymix, yref, nullptr,
+                                            &dstats->n_exact_tiles, false, st),
                      "score kernel launch");
         LAMP_HIP_TRY(tm.end(LAMP_STAGE_EXACT), "hipEventRecord");
         LAMP_HIP_TRY(tm.begin(LAMP_STAGE_SCORES), "hipEventRecord");
-        LAMP_HIP_TRY(lamp::launch_ps_scores(P, unsafe, ymix, yref, &dstats->n_exact_tiles, true, st),
+        LAMP_HIP_TRY(lamp::launch_ps_scores(P, unsafe, ymix, yref, nullptr,
+                                            &dstats->n_exact_tiles, true, st),
                      "score kernel launch");
         LAMP_HIP_TRY(tm.end(LAMP_STAGE_SCORES), "hipEventRecord");
         LAMP_HIP_TRY(tm.begin(LAMP_STAGE_SELECT), "hipEventRecord");
@@ -435,9 +492,9 @@ int lamp_ps_scores(const float *q, const float *k, int B, int H, int S, int D, i
         hipStream_t st = (hipStream_t)stream;
         (void)hipGetLastError();
         LAMP_HIP_TRY(lamp::launch_operand_scan(P, (uint8_t *)ws, st), "operand scan launch");
-        LAMP_HIP_TRY(lamp::launch_ps_scores(P, (uint8_t *)ws, ylo, yref, nullptr, false, st),
+        LAMP_HIP_TRY(lamp::launch_ps_scores(P, (uint8_t *)ws, ylo, yref, nullptr, nullptr, false, st),
                      "score kernel launch");
-        LAMP_HIP_TRY(lamp::launch_ps_scores(P, (uint8_t *)ws, ylo, yref, nullptr, true, st),
+        LAMP_HIP_TRY(lamp::launch_ps_scores(P, (uint8_t *)ws, ylo, yref, nullptr, nullptr, true, st),
                      "score kernel launch");
         return LAMP_OK;
     } catch (...) {

@@ -215,30 +215,99 @@ __device__ __forceinline__ void tile_scores(const TileAcc &acc, const PsConst &p
 
 // ---------------------------------------------------------------------------
 // Wave reductions (wave64).
+//
+// Within each row of 16 lanes the partners are exchanged through DPP
+// (quad_perm [1,0,3,2] and [2,3,0,1], row_half_mirror, row_mirror): after the
+// four steps every lane of a row holds the row's reduction.  A wave reduction
+// then reads lanes 0, 16, 32 and 48 (readlane) and combines them, so its
+// result is wave-uniform.  No LDS traffic, no waits on it.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float wave_max(float v)
+constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;   // lane i <- lane 7 - i within 8
+constexpr int kDppMirror = 0x140;       // lane i <- lane 15 - i within 16
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1)
-        v = fmaxf(v, __shfl_xor(v, o, 64));
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v)
+{
+    return __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v)));
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp(double v)
+{
+    const uint64_t u = (uint64_t)__double_as_longlong(v);
+    const uint64_t lo = dpp_u32<CTRL>((uint32_t)u);
+    const uint64_t hi = dpp_u32<CTRL>((uint32_t)(u >> 32));
+    return __longlong_as_double((long long)((hi << 32) | lo));
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v)
+{
+    return dpp_u32<CTRL>(v);
+}
+
+template <typename T, typename Op>
+__device__ __forceinline__ T row16_reduce(T v, Op op)
+{
+    v = op(v, dpp<kDppQuadXor1>(v));
+    v = op(v, dpp<kDppQuadXor2>(v));
+    v = op(v, dpp<kDppHalfMirror>(v));
+    v = op(v, dpp<kDppMirror>(v));
     return v;
 }
 
-__device__ __forceinline__ double wave_sum(double v)
+__device__ __forceinline__ float lane_read(float v, int l)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1)
-        v += __shfl_xor(v, o, 64);
-    return v;
+    return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v), l));
 }
 
+__device__ __forceinline__ uint32_t lane_read(uint32_t v, int l)
+{
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
+}
+
+__device__ __forceinline__ double lane_read(double v, int l)
+{
+    const uint64_t u = (uint64_t)__double_as_longlong(v);
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+    return __longlong_as_double((long long)((hi << 32) | lo));
+}
+
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_reduce(T v, Op op)
+{
+    v = row16_reduce(v, op);
+    return op(op(lane_read(v, 0), lane_read(v, 16)), op(lane_read(v, 32), lane_read(v, 48)));
+}
+
+struct OpMax {
+    __device__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+struct OpAdd {
+    template <typename T>
+    __device__ T operator()(T a, T b) const { return a + b; }
+};
+
+__device__ __forceinline__ float wave_max(float v) { return wave_reduce(v, OpMax{}); }
+__device__ __forceinline__ double wave_sum(double v) { return wave_reduce(v, OpAdd{}); }
 __device__ __forceinline__ int wave_sum_int(int v)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1)
-        v += __shfl_xor(v, o, 64);
-    return v;
+    return (int)wave_reduce((uint32_t)v, OpAdd{});
 }
+
+// Max / sum over the 16 lanes that share a row (lane groups of 16).
+__device__ __forceinline__ float group16_max(float v) { return row16_reduce(v, OpMax{}); }
+__device__ __forceinline__ double group16_sum(double v) { return row16_reduce(v, OpAdd{}); }
+__device__ __forceinline__ uint32_t group16_sum_u(uint32_t v) { return row16_reduce(v, OpAdd{}); }
 
 // Lanes below this one whose bit is set in `mask`.
 __device__ __forceinline__ uint32_t lanes_below(uint64_t mask)

@@ -20,7 +20,23 @@
 
 namespace lamp {
 
-__device__ __forceinline__ double exp64(double x)
+// Taylor coefficients 1/12!, 1/11!, ..., 1/2!, 1, 1 (Horner order).  They
+// travel in every kernel's arguments so that they sit in scalar registers
+// and each Horner step is one v_fma_f64 with a scalar operand.
+struct ExpCoef {
+    double c[13];
+};
+
+inline ExpCoef make_exp_coef()
+{
+    const ExpCoef k = {{0x1.1eed8eff8d898p-29, 0x1.ae64567f544e4p-26, 0x1.27e4fb7789f5cp-22,
+                        0x1.71de3a556c734p-19, 0x1.a01a01a01a01ap-16, 0x1.a01a01a01a01ap-13,
+                        0x1.6c16c16c16c17p-10, 0x1.1111111111111p-7, 0x1.5555555555555p-5,
+                        0x1.5555555555555p-3, 0.5, 1.0, 1.0}};
+    return k;
+}
+
+__device__ __forceinline__ double exp64(double x, const ExpCoef &k)
 {
     const double kLog2e = 0x1.71547652b82fep+0;
     const double kLn2Hi = 0x1.62e42ff000000p-1;
@@ -30,23 +46,13 @@ __device__ __forceinline__ double exp64(double x)
     // (NaN passes through)
     if (!(x != x))
         x = fmin(fmax(x, -750.0), 712.0);
-    const double t = x * kLog2e;
-    const double n = rint(t);
+    const double n = rint(x * kLog2e);
     double r = fma(-n, kLn2Hi, x);
     r = fma(-n, kLn2Lo, r);
-    double p = 0x1.1eed8eff8d898p-29;          // 1/12!
-    p = fma(p, r, 0x1.ae64567f544e4p-26);      // 1/11!
-    p = fma(p, r, 0x1.27e4fb7789f5cp-22);      // 1/10!
-    p = fma(p, r, 0x1.71de3a556c734p-19);      // 1/9!
-    p = fma(p, r, 0x1.a01a01a01a01ap-16);      // 1/8!
-    p = fma(p, r, 0x1.a01a01a01a01ap-13);      // 1/7!
-    p = fma(p, r, 0x1.6c16c16c16c17p-10);      // 1/6!
-    p = fma(p, r, 0x1.1111111111111p-7);       // 1/5!
-    p = fma(p, r, 0x1.5555555555555p-5);       // 1/4!
-    p = fma(p, r, 0x1.5555555555555p-3);       // 1/3!
-    p = fma(p, r, 0.5);
-    p = fma(p, r, 1.0);
-    p = fma(p, r, 1.0);
+    double p = k.c[0];
+#pragma unroll
+    for (int i = 1; i < 13; ++i)
+        p = fma(p, r, k.c[i]);
     return ldexp(p, (int)n);
 }
 

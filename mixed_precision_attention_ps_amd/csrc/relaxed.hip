@@ -37,32 +37,8 @@ struct RelaxedArgs {
     float *ymix_raw, *yref_out, *row_m;
     double *row_l;
     unsigned long long *exact_tiles;
+    ExpCoef ek;
 };
-
-// Max / sum over the 16 lanes that share a row (lane groups of 16).
-__device__ __forceinline__ float group16_max(float v)
-{
-#pragma unroll
-    for (int o = 8; o > 0; o >>= 1)
-        v = fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
-}
-
-__device__ __forceinline__ double group16_sum(double v)
-{
-#pragma unroll
-    for (int o = 8; o > 0; o >>= 1)
-        v += __shfl_xor(v, o, 64);
-    return v;
-}
-
-__device__ __forceinline__ uint32_t group16_sum_u(uint32_t v)
-{
-#pragma unroll
-    for (int o = 8; o > 0; o >>= 1)
-        v += __shfl_xor(v, o, 64);
-    return v;
-}
 
 // Online state of one query row: maxima of y^lo (m_t), y^mix and y^ref, and
 // the sums relative to them.  Each row is owned by the 16 lanes of one wave
@@ -94,9 +70,9 @@ __device__ __forceinline__ void relaxed_tile_scores(TileSmem &sm, const RelaxedA
 }
 
 // exp of a difference of row maxima (-inf when a maximum is still unset).
-__device__ __forceinline__ double exp_delta(float from, float to)
+__device__ __forceinline__ double exp_delta(float from, float to, const ExpCoef &k)
 {
-    return from == -INFINITY ? 0.0 : exp64((double)from - (double)to);
+    return from == -INFINITY ? 0.0 : exp64((double)from - (double)to, k);
 }
 
 // Per-score exponentials (double): E = exp(y^lo - m_t) serves the criterion
@@ -207,7 +183,7 @@ void relaxed_kernel(RelaxedArgs a)
             float bm = -INFINITY, br = -INFINITY;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                E[c] = valid[c] ? exp64((double)lo[r][c] - (double)mt_new) : 0.0;
+                E[c] = valid[c] ? exp64((double)lo[r][c] - (double)mt_new, a.ek) : 0.0;
                 sel[c] = valid[c] && 2.0 * E[c] * fabs((double)lo[r][c]) > a.tau;
                 mix[c] = sel[c] ? ref[r][c] : lo[r][c];
                 if (valid[c]) {
@@ -249,23 +225,23 @@ void relaxed_kernel(RelaxedArgs a)
             br = group16_max(br);
             const float mm_new = fmaxf(m_mix, bm);
             const float mr_new = fmaxf(m_ref, br);
-            const double alpha = exp_delta(m_mix, mm_new);
+            const double alpha = exp_delta(m_mix, mm_new, a.ek);
             // row factors; a factor that would overflow (maxima more than
             // ~700 apart) falls back to a direct exp per score
-            const double f_lo = exp64((double)mt_new - (double)mm_new);
-            const double f_ref = exp64((double)mr_new - (double)mm_new);
+            const double f_lo = exp64((double)mt_new - (double)mm_new, a.ek);
+            const double f_ref = exp64((double)mr_new - (double)mm_new, a.ek);
             const bool direct = !(f_lo < 1e300 && f_ref < 1e300);
             double sl = 0.0, sr = 0.0, sa = 0.0, sll = 0.0, sb = 0.0;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 pmix[r][c] = 0.0f;
                 if (valid[c]) {
-                    const double er = exp64((double)ref[r][c] - (double)mr_new);
+                    const double er = exp64((double)ref[r][c] - (double)mr_new, a.ek);
                     double pe;
                     if (!direct)
                         pe = sel[c] ? er * f_ref : E[c] * f_lo;
                     else
-                        pe = exp64((double)mix[c] - (double)mm_new);
+                        pe = exp64((double)mix[c] - (double)mm_new, a.ek);
                     pmix[r][c] = (float)pe;
                     sl += pe;
                     sr += er;
@@ -282,12 +258,12 @@ void relaxed_kernel(RelaxedArgs a)
                 sb = group16_sum(sb);
             }
             if (i < S && tx == 0) {
-                const double beta = exp_delta(m_ref, mr_new);
+                const double beta = exp_delta(m_ref, mr_new, a.ek);
                 rs.l_mix = rs.l_mix * alpha + sl;
                 rs.l_ref = rs.l_ref * beta + sr;
                 rs.kl_a = rs.kl_a * beta + sa;
                 if (want_lowp) {
-                    rs.l_lo = rs.l_lo * exp_delta(m_t, mt_new) + sll;
+                    rs.l_lo = rs.l_lo * exp_delta(m_t, mt_new, a.ek) + sll;
                     rs.kl_b = rs.kl_b * beta + sb;
                 }
                 rs.m_t = mt_new;
@@ -411,6 +387,7 @@ hipError_t launch_relaxed(const Problem &p, const uint8_t *unsafe, float *out, u
     a.row_m = row_m;
     a.row_l = row_l;
     a.exact_tiles = exact_tiles;
+    a.ek = make_exp_coef();
     const uint64_t grid = (uint64_t)p.BH * p.tiles;
     const dim3 g((unsigned)grid), b(kThreads);
     if (fast && p.mu > 10)

@@ -1,0 +1,302 @@
+// rows.hip -- fused strict row pass for rows of at most 1024 keys.
+//
+// LAMP summary, "Implementation strategy": step 2 (look-ahead selection from
+// the baseline output, with the softmax rule of "Theoretical foundation" item
+// 3: recompute y_j iff 2 z_j (1 - z_j) |y_j| > tau) and step 3 (recompute the
+// selected components at FP32, then apply f), for one attention row per wave:
+//   * the row's PS(mu) scores stay in registers (16 per lane);
+//   * its softmax statistics are formed in double (own exp);
+//   * the criterion gives the mask words (ballots) and a compacted list of the
+//     selected keys in LDS (ballot + lane prefix);
+//   * the selected scores are recomputed by a gather FP32 dot (sequential,
+//     multiply then add) and scattered back into the register row;
+//   * the row's log-sum-exp is corrected for the changed terms (or recomputed
+//     over the row when the correction would cancel or overflow);
+//   * probabilities are written as full rows (zeros past the valid keys);
+//   * the row KLs against the FP32 reference use the reference statistics the
+//     score kernel left per 64-key tile.
+#include "lamp_device.h"
+
+namespace lamp {
+
+constexpr int kRowChunk = 16;   // keys per lane: rows of at most 1024 keys
+
+struct RowsArgs {
+    const float *q, *k, *ylo;
+    const RefPartial *part;
+    int S, D, causal, tiles, W;
+    uint64_t n_rows;
+    double tau;
+    float s;
+    uint32_t *mask, *row_count;
+    float *pbuf, *ymix_out;
+    double *row_kl, *row_kl_lowp;
+    ExpCoef ek;
+};
+
+// D4 = D / 4 when the head dimension is a compile-time constant (all loads of
+// a recomputed dot issue back to back), 0 for a runtime D.
+//
+// Register discipline: the loops over a lane's 16 keys are unrolled (the row
+// lives in registers) and guarded only by wave-uniform conditions (the chunk
+// holds valid keys); per-key validity is a select, never a branch, and the
+// per-chunk selection is kept as one bit per lane rather than as 16 wave
+// masks.  Scalar registers then hold no per-chunk state.
+template <int D4>
+__global__ __launch_bounds__(kThreads) void strict_rows_kernel(RowsArgs a)
+{
+    __shared__ uint32_t s_list[4][64 * kRowChunk];   // selected keys, compacted
+    __shared__ float s_yhi[4][64 * kRowChunk];       // recomputed scores, by key
+    __shared__ float4 s_q[4][64];                    // the wave's query row (D <= 256)
+    // the wave index is uniform: readfirstlane tells the compiler so, which
+    // makes the row, its length and every chunk guard scalar
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint64_t r = (uint64_t)blockIdx.x * 4 + wave;
+    if (r >= a.n_rows)
+        return;   // no block barrier below: each wave owns its row
+    const int S = a.S;
+    const int i = (int)(r % (uint64_t)S);
+    const int n = a.causal ? i + 1 : S;
+    const int nch = (n + 63) >> 6;   // chunks of 64 keys holding valid keys
+    const float *y = a.ylo + r * (uint64_t)S;
+
+    // The row and its maximum.  All 16 loads are issued unconditionally, back
+    // to back (a guarded load would wait for its data before the next one);
+    // past the valid keys every lane reads the row's last valid score, one
+    // cache line.
+    float v[kRowChunk];
+#pragma unroll
+    for (int t = 0; t < kRowChunk; ++t)
+        v[t] = y[min(lane + 64 * t, n - 1)];
+    float m = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < kRowChunk; ++t) {
+        v[t] = lane + 64 * t < n ? v[t] : -INFINITY;
+        m = fmaxf(m, v[t]);
+    }
+    m = wave_max(m);
+
+    // e_j = exp(y_j - m); A = sum below the maximum; cnt = keys at it.
+    double e[kRowChunk];
+    double A = 0.0;
+    int cnt = 0;
+#pragma unroll
+    for (int t = 0; t < kRowChunk; ++t) {
+        e[t] = 0.0;
+        if (t < nch) {
+            const bool valid = lane + 64 * t < n;
+            const bool at = valid && v[t] == m;
+            const double x = exp64((double)v[t] - (double)m, a.ek);
+            e[t] = valid ? (at ? 1.0 : x) : 0.0;
+            A += (valid && !at) ? x : 0.0;
+            cnt += at ? 1 : 0;
+        }
+    }
+    A = wave_sum(A);
+    cnt = wave_sum_int(cnt);
+    const double L = A + (double)cnt;
+    const double rest_at_max = A + (double)(cnt - 1);
+    const double inv_l2 = 1.0 / (L * L);
+
+    // Criterion c = 2 z (1 - z) |y| = 2 e rest |y| / L^2, mask, compaction.
+    uint32_t selbits = 0;
+    uint32_t total = 0;
+#pragma unroll
+    for (int t = 0; t < kRowChunk; ++t) {
+        const int j0 = 64 * t;
+        if (j0 < S) {
+            const int j = j0 + lane;
+            bool sel = false;
+            if (t < nch) {
+                const bool valid = j < n;
+                const double rest = (valid && v[t] == m) ? rest_at_max : L - e[t];
+                const double c = 2.0 * e[t] * rest * fabs((double)v[t]) * inv_l2;
+                sel = valid && c > a.tau;
+            }
+            const uint64_t b = __ballot(sel);
+            if (a.mask) {
+                const int w = (j0 >> 5) + lane;
+                if (lane < 2 && w < a.W)
+                    a.mask[r * (uint64_t)a.W + w] = lane ? (uint32_t)(b >> 32) : (uint32_t)b;
+            }
+            if (sel)
+                s_list[wave][total + lanes_below(b)] = (uint32_t)j;
+            selbits |= (sel ? 1u : 0u) << t;
+            total += (uint32_t)__popcll(b);
+        }
+    }
+
+    // Reference statistics from the score kernel's per-tile partials.
+    const bool kl = a.part != nullptr;
+    double Lr = 1.0, Br = 0.0;
+    float mr = 0.0f;
+    if (kl) {
+        const int nt = a.causal ? (i / kTile) + 1 : a.tiles;
+        const RefPartial *pp = a.part + r * (uint64_t)a.tiles;
+        RefPartial mine{0.0, 0.0, -INFINITY, 0.0f};
+        if (lane < nt)
+            mine = pp[lane];
+        mr = wave_max(mine.m);
+        const double f = lane < nt ? exp64((double)mine.m - (double)mr, a.ek) : 0.0;
+        Lr = wave_sum(mine.L * f);
+        Br = wave_sum(mine.B * f);
+    }
+
+    // Gather FP32 recompute of the selected keys (one lane per key); the query
+    // row is read from LDS, each key row in batches of up to 8 x 16 bytes
+    // issued back to back.
+    const uint64_t bh = r / (uint64_t)S;
+    {
+        const float4 *qg = reinterpret_cast<const float4 *>(a.q + r * (uint64_t)a.D);
+        if (lane < a.D / 4)
+            s_q[wave][lane] = qg[lane];
+    }
+    const float4 *q4 = s_q[wave];
+    double dL = 0.0, dA = 0.0;
+    for (uint32_t ei = lane; ei < total; ei += 64) {
+        const uint32_t j = s_list[wave][ei];
+        const float4 *k4 = reinterpret_cast<const float4 *>(a.k + (bh * (uint64_t)S + j) * a.D);
+        float acc = 0.0f;
+        auto mac4 = [&acc](float4 x, float4 z) {
+            float p0 = x.x * z.x;
+            acc = acc + p0;
+            float p1 = x.y * z.y;
+            acc = acc + p1;
+            float p2 = x.z * z.z;
+            acc = acc + p2;
+            float p3 = x.w * z.w;
+            acc = acc + p3;
+        };
+        if constexpr (D4 > 0) {
+            // opaque zero offset: keeps the query-row LDS reads inside the
+            // loop instead of 4*D4 registers hoisted out of it
+            uint32_t qoff = 0;
+            asm volatile("" : "+v"(qoff));
+            constexpr int kB = D4 < 8 ? D4 : 8;   // D4 is a multiple of 4
+#pragma unroll
+            for (int b0 = 0; b0 < D4; b0 += kB) {
+                float4 kr[kB];
+#pragma unroll
+                for (int u = 0; u < kB; ++u)
+                    kr[u] = k4[b0 + u];
+#pragma unroll
+                for (int u = 0; u < kB; ++u)
+                    mac4(q4[qoff + b0 + u], kr[u]);
+            }
+        } else {
+            for (int d4 = 0; d4 < a.D / 4; ++d4)
+                mac4(q4[d4], k4[d4]);
+        }
+        const float yhi = acc * a.s;
+        s_yhi[wave][j] = yhi;
+        const float yl = y[j];
+        dL += exp64((double)yhi - (double)m, a.ek) - exp64((double)yl - (double)m, a.ek);
+        if (kl)
+            dA += exp64((double)yhi - (double)mr, a.ek) * ((double)yhi - (double)yl);
+    }
+    dL = wave_sum(dL);
+    dA = wave_sum(dA);
+    __builtin_amdgcn_wave_barrier();
+
+    // Scatter the recomputed scores into the row: y^mix.
+#pragma unroll
+    for (int t = 0; t < kRowChunk; ++t) {
+        if (t < nch) {
+            const float h = s_yhi[wave][lane + 64 * t];
+            v[t] = ((selbits >> t) & 1u) ? h : v[t];
+        }
+    }
+
+    // Log-sum-exp of y^mix.
+    const double Lmix = L + dL;
+    double lse_mix;
+    if (Lmix >= 0.25 * L && isfinite(Lmix)) {
+        lse_mix = (double)m + log(Lmix);
+    } else {
+        float mm = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < kRowChunk; ++t)
+            mm = fmaxf(mm, v[t]);
+        mm = wave_max(mm);
+        double l = 0.0;
+#pragma unroll
+        for (int t = 0; t < kRowChunk; ++t) {
+            if (t < nch) {
+                const double x = exp64((double)v[t] - (double)mm, a.ek);
+                l += lane + 64 * t < n ? x : 0.0;
+            }
+        }
+        lse_mix = (double)mm + log(wave_sum(l));
+    }
+
+    // Probabilities (full rows) and y^mix.
+    float *pr = a.pbuf + r * (uint64_t)S;
+    float *ym = a.ymix_out ? a.ymix_out + r * (uint64_t)S : nullptr;
+#pragma unroll
+    for (int t = 0; t < kRowChunk; ++t) {
+        const int j = lane + 64 * t;
+        if (64 * t < S) {
+            float pv = 0.0f;
+            if (t < nch) {
+                const float x = exp_f32((double)v[t] - lse_mix);
+                pv = j < n ? x : 0.0f;
+            }
+            if (j < S)
+                pr[j] = pv;
+            if (ym && j < n)
+                ym[j] = v[t];
+        }
+    }
+
+    if (lane == 0) {
+        if (a.row_count)
+            a.row_count[r] = total;
+        if (kl) {
+            const double lse_lo = (double)m + log(L);
+            const double lse_ref = (double)mr + log(Lr);
+            if (a.row_kl_lowp)
+                a.row_kl_lowp[r] = Br / Lr + lse_lo - lse_ref;
+            if (a.row_kl)
+                a.row_kl[r] = (Br - dA) / Lr + lse_mix - lse_ref;
+        }
+    }
+}
+
+hipError_t launch_strict_rows(const Problem &p, const float *ylo, const RefPartial *part,
+                              uint32_t *mask, uint32_t *row_count, float *pbuf, float *ymix_out,
+                              double *row_kl, double *row_kl_lowp, hipStream_t st)
+{
+    if (p.S > 64 * kRowChunk)
+        return hipErrorInvalidValue;
+    RowsArgs a;
+    a.q = p.q;
+    a.k = p.k;
+    a.ylo = ylo;
+    a.part = part;
+    a.S = p.S;
+    a.D = p.D;
+    a.causal = p.causal;
+    a.tiles = p.tiles;
+    a.W = (p.S + 31) / 32;
+    a.n_rows = p.n_rows;
+    a.tau = (double)p.tau;
+    a.s = p.pc.s;
+    a.mask = mask;
+    a.row_count = row_count;
+    a.pbuf = pbuf;
+    a.ymix_out = ymix_out;
+    a.row_kl = row_kl;
+    a.row_kl_lowp = row_kl_lowp;
+    a.ek = make_exp_coef();
+    const uint64_t grid = (p.n_rows + 3) / 4;
+    if (p.D == 64)
+        hipLaunchKernelGGL(strict_rows_kernel<16>, dim3((unsigned)grid), dim3(kThreads), 0, st, a);
+    else if (p.D == 128)
+        hipLaunchKernelGGL(strict_rows_kernel<32>, dim3((unsigned)grid), dim3(kThreads), 0, st, a);
+    else
+        hipLaunchKernelGGL(strict_rows_kernel<0>, dim3((unsigned)grid), dim3(kThreads), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace lamp

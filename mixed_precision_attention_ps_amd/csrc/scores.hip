@@ -82,7 +82,9 @@ struct ScoreArgs {
     PsConst pc;
     const uint8_t *unsafe_q, *unsafe_k;
     float *ylo, *yref;
+    RefPartial *part;
     unsigned long long *exact_tiles;
+    ExpCoef ek;
 };
 
 template <int PATH>
@@ -110,6 +112,41 @@ __device__ __forceinline__ void score_tile_store(TileSmem &sm, const ScoreArgs &
                 a.ylo[rowoff + j] = lo[r][c];
             if (a.yref)
                 a.yref[rowoff + j] = ref[r][c];
+        }
+    }
+    if (a.part) {
+        // this tile's softmax statistics of the reference scores, per row
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = ti * kTile + ty * 4 + r;
+            bool valid[4];
+            float m = -INFINITY;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int j = tj * kTile + tx + 16 * c;
+                valid[c] = i < a.S && j < a.S && (!a.causal || j <= i);
+                if (valid[c])
+                    m = fmaxf(m, ref[r][c]);
+            }
+            m = group16_max(m);
+            double L = 0.0, B = 0.0;
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                if (valid[c]) {
+                    const double e = exp64((double)ref[r][c] - (double)m, a.ek);
+                    L += e;
+                    B += e * ((double)ref[r][c] - (double)lo[r][c]);
+                }
+            L = group16_sum(L);
+            B = group16_sum(B);
+            if (tx == 0 && i < a.S) {
+                RefPartial rp;
+                rp.L = L;
+                rp.B = B;
+                rp.m = m;
+                rp.pad = 0.0f;
+                a.part[((size_t)bh * a.S + i) * a.tiles + tj] = rp;
+            }
         }
     }
 }
@@ -147,7 +184,8 @@ __global__ __launch_bounds__(kThreads) void ps_scores_kernel(ScoreArgs a)
 }
 
 hipError_t launch_ps_scores(const Problem &p, const uint8_t *unsafe, float *ylo, float *yref,
-                            unsigned long long *exact_tiles, bool fast, hipStream_t st)
+                            RefPartial *part, unsigned long long *exact_tiles, bool fast,
+                            hipStream_t st)
 {
     ScoreArgs a;
     a.q = p.q;
@@ -162,7 +200,9 @@ hipError_t launch_ps_scores(const Problem &p, const uint8_t *unsafe, float *ylo,
     a.unsafe_k = unsafe + (size_t)p.BH * p.tiles;
     a.ylo = ylo;
     a.yref = yref;
+    a.part = part;
     a.exact_tiles = exact_tiles;
+    a.ek = make_exp_coef();
     const long long grid = (long long)p.BH * a.tiles_per_head;
     if (grid > 0x7fffffffLL)
         return hipErrorInvalidValue;

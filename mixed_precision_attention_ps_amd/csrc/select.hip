@@ -24,6 +24,7 @@ struct SelectArgs {
     RowStats *rs;
     double *row_kl, *row_kl_lowp;
     int count_only;
+    ExpCoef ek;
 };
 
 constexpr int kSelChunk = 16;   // keys per lane held in registers (1024 per wave)
@@ -75,10 +76,10 @@ __global__ __launch_bounds__(kThreads) void strict_select_kernel(SelectArgs a)
             cnt++;
             e = 1.0;
         } else {
-            e = exp64((double)v - (double)m);
+            e = exp64((double)v - (double)m, a.ek);
             A += e;
         }
-        const double er = exp64((double)vr - (double)mr);
+        const double er = exp64((double)vr - (double)mr, a.ek);
         Lr += er;
         Br += er * ((double)vr - (double)v);
     };
@@ -160,7 +161,7 @@ __global__ __launch_bounds__(kThreads) void strict_select_kernel(SelectArgs a)
             double e = 0.0;
             if (j < n) {
                 v = y[j];
-                e = (v == m) ? 1.0 : exp64((double)v - (double)m);
+                e = (v == m) ? 1.0 : exp64((double)v - (double)m, a.ek);
             }
             decide(j0, j, v, e);
         }
@@ -189,6 +190,7 @@ hipError_t launch_strict_select(const Problem &p, const float *ylo, const float 
     a.row_kl = row_kl;
     a.row_kl_lowp = row_kl_lowp;
     a.count_only = count_only;
+    a.ek = make_exp_coef();
     const uint64_t grid = (p.n_rows + 3) / 4;
     if (p.S <= 64 * kSelChunk)
         hipLaunchKernelGGL(strict_select_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, st, a);
@@ -336,6 +338,7 @@ struct RecomputeArgs {
     float *ymix;
     RowStats *rs;
     double *row_kl;
+    ExpCoef ek;
 };
 
 // The softmax statistics of y^mix follow from those of y^lo by correcting the
@@ -420,8 +423,8 @@ __global__ __launch_bounds__(kThreads) void recompute_kernel(RecomputeArgs a)
                 const float ylo = *slot;
                 *slot = yhi;
                 const double ml = (double)s_mlo[lr], mr = (double)s_mref[lr];
-                cl = exp64((double)yhi - ml) - exp64((double)ylo - ml);
-                ca = exp64((double)yhi - mr) * ((double)yhi - (double)ylo);
+                cl = exp64((double)yhi - ml, a.ek) - exp64((double)ylo - ml, a.ek);
+                ca = exp64((double)yhi - mr, a.ek) * ((double)yhi - (double)ylo);
             }
         }
         s_dl[tid] = cl;
@@ -470,6 +473,7 @@ hipError_t launch_recompute(const Problem &p, const uint32_t *list, const uint32
     a.ymix = ymix;
     a.rs = rs;
     a.row_kl = row_kl;
+    a.ek = make_exp_coef();
     const uint64_t grid = (p.n_rows + kRcRows - 1) / kRcRows;
     hipLaunchKernelGGL(recompute_kernel, dim3((unsigned)grid), dim3(kThreads), 0, st, a);
     return hipGetLastError();

@@ -34,7 +34,8 @@ def note(msg):
     sys.stdout.flush()
 
 
-def run_gpu(dev, Q, K, V, *, causal, mu, tau, mode, seed=0, want_probs=True, want_mask=True):
+def run_gpu(dev, Q, K, V, *, causal, mu, tau, mode, seed=0, want_probs=True, want_mask=True,
+            want_scores=True, want_rows=True, want_stats=True):
     import torch
     from mixed_precision_attention_ps_amd import lamp
     B, H, S, D = Q.shape
@@ -42,20 +43,24 @@ def run_gpu(dev, Q, K, V, *, causal, mu, tau, mode, seed=0, want_probs=True, wan
     W = (S + 31) // 32
     probs = torch.full((B, H, S, S), -7.0, device=dev) if want_probs else None
     mask = torch.full((B, H, S, W), -1, dtype=torch.int32, device=dev) if want_mask else None
-    row_kl = torch.zeros((B, H, S), dtype=torch.float64, device=dev)
-    row_kl_lowp = torch.zeros((B, H, S), dtype=torch.float64, device=dev)
-    row_count = torch.zeros((B, H, S), dtype=torch.int32, device=dev)
-    ymix = torch.zeros((B, H, S, S), device=dev)
-    yref = torch.zeros((B, H, S, S), device=dev)
-    note(f"gpu {MODE_NAME[mode]} B={B} H={H} S={S} D={D} causal={causal} mu={mu} tau={tau}")
+    row_kl = torch.zeros((B, H, S), dtype=torch.float64, device=dev) if want_rows else None
+    row_kl_lowp = torch.zeros((B, H, S), dtype=torch.float64, device=dev) if want_rows else None
+    row_count = torch.zeros((B, H, S), dtype=torch.int32, device=dev) if want_rows else None
+    ymix = torch.zeros((B, H, S, S), device=dev) if want_scores else None
+    yref = torch.zeros((B, H, S, S), device=dev) if want_scores else None
+    note(f"gpu {MODE_NAME[mode]} B={B} H={H} S={S} D={D} causal={causal} mu={mu} tau={tau} "
+         f"probs={want_probs} scores={want_scores} rows={want_rows} stats={want_stats}")
     out, st = lamp.lamp_attention_fwd(q, k, v, causal=causal, mu=mu, tau=tau, mode=mode,
                                       probs=probs, recompute_mask=mask, seed=seed, row_kl=row_kl,
                                       row_kl_lowp=row_kl_lowp, row_count=row_count,
-                                      scores_mix=ymix, scores_ref=yref)
+                                      scores_mix=ymix, scores_ref=yref, want_stats=want_stats)
     torch.cuda.synchronize()
-    res = {"out": out.cpu().numpy(), "row_kl": row_kl.cpu().numpy(),
-           "row_kl_lowp": row_kl_lowp.cpu().numpy(), "row_count": row_count.cpu().numpy(),
-           "ymix": ymix.cpu().numpy(), "yref": yref.cpu().numpy(), "stats": st}
+    res = {"out": out.cpu().numpy(), "stats": st}
+    if want_rows:
+        res.update(row_kl=row_kl.cpu().numpy(), row_kl_lowp=row_kl_lowp.cpu().numpy(),
+                   row_count=row_count.cpu().numpy())
+    if want_scores:
+        res.update(ymix=ymix.cpu().numpy(), yref=yref.cpu().numpy())
     if want_probs:
         res["probs"] = probs.cpu().numpy()
     if want_mask:
@@ -83,19 +88,31 @@ def compare_full(g, r, Q, V, *, causal, tau, heads=None, rows=None, check_probs=
     sl = slice(rb, re_)
     valid = parity.valid_mask(S, causal, (rb, re_))[None].repeat(len(heads), 0)
     gv = lambda name: g[name].reshape((B * H,) + g[name].shape[2:])[heads][:, sl]
-    parity.assert_bits(gv("yref"), r["yref"], valid, "FP32 reference scores")
-    parity.assert_bits(gv("ymix"), ymix_oracle(r, S), valid, "mixed scores")
+    if "yref" in g:
+        parity.assert_bits(gv("yref"), r["yref"], valid, "FP32 reference scores")
+        parity.assert_bits(gv("ymix"), ymix_oracle(r, S), valid, "mixed scores")
     ties = parity.assert_mask(gv("mask"), r["mask"], r["crit"], tau, S)
-    assert (gv("row_count") == r["count"]).all() or ties > 0, "row counts"
-    if check_probs:
+    if "row_count" in g:
+        assert (gv("row_count") == r["count"]).all() or ties > 0, "row counts"
+    if check_probs and "probs" in g:
         parity.assert_tol(gv("probs"), r["probs"], np.abs(r["probs"]), "probs")
     Vf = V.reshape(B * H, S, D)
     scale = np.stack([parity.out_scale(r["probs"][n].astype(np.float64), Vf[h])
                       for n, h in enumerate(heads)])
     parity.assert_tol(gv("out"), r["out"], scale, "out")
-    parity.assert_tol(gv("row_kl"), r["kl"], np.abs(r["kl"]), "row KL")
-    parity.assert_tol(gv("row_kl_lowp"), r["kl_lowp"], np.abs(r["kl_lowp"]), "row KL lowp")
+    if "row_kl" in g:
+        parity.assert_tol(gv("row_kl"), r["kl"], np.abs(r["kl"]), "row KL")
+        parity.assert_tol(gv("row_kl_lowp"), r["kl_lowp"], np.abs(r["kl_lowp"]), "row KL lowp")
+    st = g["stats"]
+    if st is not None and not heads_subset(heads, B * H, rows, S):
+        assert st["n_selected"] == r["count"].sum() or ties > 0
+        assert abs(st["kl_sum"] - r["kl"].sum()) <= 1e-6 * r["kl"].sum() + 1e-7 * r["kl"].size
+        assert abs(st["kl_lowp_sum"] - r["kl_lowp"].sum()) <= 1e-6 * r["kl_lowp"].sum() + 1e-7 * r["kl"].size
     return ties
+
+
+def heads_subset(heads, BH, rows, S):
+    return len(heads) != BH or (rows is not None and tuple(rows) != (0, S))
 
 
 # ---------------------------------------------------------------------------
@@ -279,3 +296,32 @@ def test_device_exponentials_accuracy(dev):
     rel32 = np.abs(y32[f32].astype(np.float64) - ref[f32]) / ref[f32]
     assert rel32.max() < 4e-7, rel32.max()
     assert (y32[x < -110] == 0).all()
+
+
+# Which optional buffers the caller passes decides where the strict path keeps
+# y^lo / y^mix / probabilities (in place or in the workspace): every
+# combination against the oracle.
+@pytest.mark.parametrize("probs,scores,rows,stats", [
+    (True, False, True, False), (False, False, True, False), (True, True, False, True),
+    (False, True, True, True), (False, False, False, True), (True, False, False, False)])
+def test_strict_buffer_configurations(dev, orc, probs, scores, rows, stats):
+    Q, K, V, _ = make_qkv(1, 3, 320, 64, n_outlier=2, seed=77)
+    tau = 1e-2
+    g = run_gpu(dev, Q, K, V, causal=True, mu=4, tau=tau, mode=STRICT, want_probs=probs,
+                want_scores=scores, want_rows=rows, want_stats=stats)
+    r = run_orc(orc, Q, K, V, causal=True, mu=4, tau=tau, mode=STRICT)
+    compare_full(g, r, Q, V, causal=True, tau=tau)
+
+
+@pytest.mark.parametrize("S,causal,mode", [(1100, True, STRICT), (1300, False, STRICT),
+                                           (1025, True, RANDOM), (2048, True, RELAXED)])
+def test_rows_longer_than_1024(dev, orc, S, causal, mode):
+    """Rows past 1024 keys take the streaming (multi-kernel) strict path."""
+    Q, K, V, _ = make_qkv(1, 1, S, 64, n_outlier=2, seed=S)
+    tau = 1e-2
+    rows = (S - 80, S)
+    g = run_gpu(dev, Q, K, V, causal=causal, mu=4, tau=tau, mode=mode, seed=5)
+    r = run_orc(orc, Q, K, V, causal=causal, mu=4, tau=tau, mode=mode, seed=5, rows=rows)
+    compare_full(g, r, Q, V, causal=causal, tau=tau, rows=rows)
+    r0 = run_orc(orc, Q, K, V, causal=causal, mu=4, tau=tau, mode=mode, seed=5, rows=(0, 64))
+    compare_full(g, r0, Q, V, causal=causal, tau=tau, rows=(0, 64))
