@@ -21,7 +21,6 @@ struct FinishArgs {
     float *probs, *out;
     double *row_kl;
     int S, D, causal, blocks_per_head;
-    ExpCoef ek;
 };
 
 // probs_j = exp(y^mix_j - lse_mix) on the valid keys (0 elsewhere), and
@@ -50,6 +49,11 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(FinishArgs a)
     __shared__ float sP[2][kFinRows][kFinPP];
     __shared__ float sV[2][kFinKeys][VP];
     __shared__ double s_lse[kFinRows];
+    __shared__ double s_exp[64];   // 2^(k/64) for exp64
+    if (!PIN) {
+        exp_table_fill(s_exp);
+        __syncthreads();
+    }
 
     const int S = a.S, D = a.D;
     const int bh = blockIdx.x / a.blocks_per_head;
@@ -74,7 +78,7 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(FinishArgs a)
                 mm = wave_max(mm);
                 double l = 0.0;
                 for (int j = lane; j < n; j += 64)
-                    l += exp64((double)ym[j] - (double)mm, a.ek);
+                    l += exp64((double)ym[j] - (double)mm, s_exp);
                 l = wave_sum(l);
                 lse = (double)mm + log(l);
                 if (lane == 0 && a.row_kl)
@@ -269,7 +273,6 @@ hipError_t launch_finish(const Problem &p, const float *ymix, const RowStats *rs
     a.D = p.D;
     a.causal = p.causal;
     a.blocks_per_head = (p.S + kFinRows - 1) / kFinRows;
-    a.ek = make_exp_coef();
     return launch_finish_kernel<false>(a, p, st);
 }
 
@@ -286,7 +289,6 @@ hipError_t launch_pv(const Problem &p, const float *probs, float *out, hipStream
     a.D = p.D;
     a.causal = p.causal;
     a.blocks_per_head = (p.S + kFinRows - 1) / kFinRows;
-    a.ek = make_exp_coef();
     return launch_finish_kernel<true>(a, p, st);
 }
 
@@ -365,11 +367,14 @@ hipError_t launch_zero(void *ptr, size_t bytes, hipStream_t st)
 // Diagnostic: the device exponentials on caller data (accuracy tests).
 // ---------------------------------------------------------------------------
 namespace lamp {
-__global__ void exp_probe_kernel(const double *x, double *y64, float *y32, int n, ExpCoef ek)
+__global__ void exp_probe_kernel(const double *x, double *y64, float *y32, int n)
 {
+    __shared__ double s_exp[64];   // 2^(k/64) for exp64
+    exp_table_fill(s_exp);
+    __syncthreads();
     const int e = blockIdx.x * blockDim.x + threadIdx.x;
     if (e < n) {
-        y64[e] = exp64(x[e], ek);
+        y64[e] = exp64(x[e], s_exp);
         y32[e] = exp_f32(x[e]);
     }
 }
@@ -383,6 +388,6 @@ extern "C" int lamp_diag_exp(const double *x, double *y64, float *y32, int n, vo
         return 0;
     (void)hipGetLastError();
     hipLaunchKernelGGL(lamp::exp_probe_kernel, dim3((n + 255) / 256), dim3(256), 0,
-                       (hipStream_t)stream, x, y64, y32, n, lamp::make_exp_coef());
+                       (hipStream_t)stream, x, y64, y32, n);
     return hipGetLastError() == hipSuccess ? 0 : -3;
 }

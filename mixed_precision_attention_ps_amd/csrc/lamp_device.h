@@ -309,6 +309,30 @@ __device__ __forceinline__ float group16_max(float v) { return row16_reduce(v, O
 __device__ __forceinline__ double group16_sum(double v) { return row16_reduce(v, OpAdd{}); }
 __device__ __forceinline__ uint32_t group16_sum_u(uint32_t v) { return row16_reduce(v, OpAdd{}); }
 
+// ---------------------------------------------------------------------------
+// Buffer (range-checked) access to one row: a buffer resource over `bytes`
+// bytes at a wave-uniform base; lanes whose byte offset falls outside the
+// range read 0 and their stores are dropped.  Offsets are 32-bit, so a row's
+// 16 per-lane chunks share one offset register plus immediate offsets.
+// ---------------------------------------------------------------------------
+constexpr int kBufferRsrcWord3 = 0x00020000;   // gfx9: 32-bit data, raw buffer
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             kBufferRsrcWord3);
+}
+
+__device__ __forceinline__ float buf_load_f32(__amdgpu_buffer_rsrc_t rs, uint32_t byte_off)
+{
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, byte_off, 0, 0));
+}
+
+__device__ __forceinline__ void buf_store_f32(__amdgpu_buffer_rsrc_t rs, uint32_t byte_off, float x)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), rs, byte_off, 0, 0);
+}
+
 // Lanes below this one whose bit is set in `mask`.
 __device__ __forceinline__ uint32_t lanes_below(uint64_t mask)
 {

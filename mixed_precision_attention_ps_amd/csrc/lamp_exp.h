@@ -1,13 +1,20 @@
 // lamp_exp.h -- exponentials for the softmax, criterion and KL sums.
 //
-// exp64: double exp with Cody & Waite range reduction (Cody & Waite,
-// "Software Manual for the Elementary Functions", 1980): n = rint(x / ln 2),
-// r = x - n ln2_hi - n ln2_lo with a two-part ln 2 (ln2_hi has 32 significant
-// bits, so n ln2_hi is exact for |n| < 2^21), then the Taylor polynomial of
-// exp(r) to degree 12 for |r| <= ln2 / 2 (truncation < 1.7e-16 relative), then
-// a power-of-two scale.  About 17 double operations; relative error within a
-// few units of the last place, which keeps the strict criterion's double
-// evaluation far inside the 1e-12 tie band the parity tests allow.
+// exp64: double exp by table-driven range reduction (Tang, "Table-driven
+// implementation of the exponential function in IEEE floating-point
+// arithmetic", ACM TOMS 15(2), 1989, with a 64-entry table):
+//   n = rint(x * 64 / ln 2),  r = x - n (ln2/64)_hi - n (ln2/64)_lo,
+//   |r| <= ln 2 / 128,
+//   exp(x) = 2^(n >> 6) * T[n & 63] * (1 + p(r)),  T[k] = 2^(k/64),
+// p(r) = r + r^2/2 + ... + r^5/120 (Taylor; the first omitted term is below
+// 3.6e-17 relative).  (ln2/64)_hi has 29 significant bits, so n (ln2/64)_hi
+// is exact for |n| < 2^24.  Twelve double operations, one LDS read and a
+// power-of-two scale; relative error within about one unit of the last place,
+// far inside the 1e-12 tie band of the strict and relaxed criteria.
+//
+// The table T lives in LDS: every kernel that calls exp64 declares a
+// 64-double shared array, fills it with exp_table_fill and synchronises its
+// block before the first call.
 //
 // exp_f32: an FP32-accurate exp of a double argument (probabilities): the
 // argument is split in double into n + f, |f| <= 1/2, f is rounded to FP32
@@ -20,40 +27,55 @@
 
 namespace lamp {
 
-// Taylor coefficients 1/12!, 1/11!, ..., 1/2!, 1, 1 (Horner order).  They
-// travel in every kernel's arguments so that they sit in scalar registers
-// and each Horner step is one v_fma_f64 with a scalar operand.
-struct ExpCoef {
-    double c[13];
+// 2^(k/64), k = 0..63, each correctly rounded to double.
+static __constant__ double kExp2Frac64[64] = {
+    0x1.0000000000000p+0, 0x1.02c9a3e778061p+0, 0x1.059b0d3158574p+0, 0x1.0874518759bc8p+0,
+    0x1.0b5586cf9890fp+0, 0x1.0e3ec32d3d1a2p+0, 0x1.11301d0125b51p+0, 0x1.1429aaea92de0p+0,
+    0x1.172b83c7d517bp+0, 0x1.1a35beb6fcb75p+0, 0x1.1d4873168b9aap+0, 0x1.2063b88628cd6p+0,
+    0x1.2387a6e756238p+0, 0x1.26b4565e27cddp+0, 0x1.29e9df51fdee1p+0, 0x1.2d285a6e4030bp+0,
+    0x1.306fe0a31b715p+0, 0x1.33c08b26416ffp+0, 0x1.371a7373aa9cbp+0, 0x1.3a7db34e59ff7p+0,
+    0x1.3dea64c123422p+0, 0x1.4160a21f72e2ap+0, 0x1.44e086061892dp+0, 0x1.486a2b5c13cd0p+0,
+    0x1.4bfdad5362a27p+0, 0x1.4f9b2769d2ca7p+0, 0x1.5342b569d4f82p+0, 0x1.56f4736b527dap+0,
+    0x1.5ab07dd485429p+0, 0x1.5e76f15ad2148p+0, 0x1.6247eb03a5585p+0, 0x1.6623882552225p+0,
+    0x1.6a09e667f3bcdp+0, 0x1.6dfb23c651a2fp+0, 0x1.71f75e8ec5f74p+0, 0x1.75feb564267c9p+0,
+    0x1.7a11473eb0187p+0, 0x1.7e2f336cf4e62p+0, 0x1.82589994cce13p+0, 0x1.868d99b4492edp+0,
+    0x1.8ace5422aa0dbp+0, 0x1.8f1ae99157736p+0, 0x1.93737b0cdc5e5p+0, 0x1.97d829fde4e50p+0,
+    0x1.9c49182a3f090p+0, 0x1.a0c667b5de565p+0, 0x1.a5503b23e255dp+0, 0x1.a9e6b5579fdbfp+0,
+    0x1.ae89f995ad3adp+0, 0x1.b33a2b84f15fbp+0, 0x1.b7f76f2fb5e47p+0, 0x1.bcc1e904bc1d2p+0,
+    0x1.c199bdd85529cp+0, 0x1.c67f12e57d14bp+0, 0x1.cb720dcef9069p+0, 0x1.d072d4a07897cp+0,
+    0x1.d5818dcfba487p+0, 0x1.da9e603db3285p+0, 0x1.dfc97337b9b5fp+0, 0x1.e502ee78b3ff6p+0,
+    0x1.ea4afa2a490dap+0, 0x1.efa1bee615a27p+0, 0x1.f50765b6e4540p+0, 0x1.fa7c1819e90d8p+0,
 };
 
-inline ExpCoef make_exp_coef()
+// Copies the table into a block's LDS array (the caller then synchronises
+// the block).
+__device__ __forceinline__ void exp_table_fill(double *s_tab)
 {
-    const ExpCoef k = {{0x1.1eed8eff8d898p-29, 0x1.ae64567f544e4p-26, 0x1.27e4fb7789f5cp-22,
-                        0x1.71de3a556c734p-19, 0x1.a01a01a01a01ap-16, 0x1.a01a01a01a01ap-13,
-                        0x1.6c16c16c16c17p-10, 0x1.1111111111111p-7, 0x1.5555555555555p-5,
-                        0x1.5555555555555p-3, 0.5, 1.0, 1.0}};
-    return k;
+    for (unsigned k = threadIdx.x; k < 64; k += blockDim.x)
+        s_tab[k] = kExp2Frac64[k];
 }
 
-__device__ __forceinline__ double exp64(double x, const ExpCoef &k)
+__device__ __forceinline__ double exp64(double x, const double *s_tab)
 {
-    const double kLog2e = 0x1.71547652b82fep+0;
-    const double kLn2Hi = 0x1.62e42ff000000p-1;
-    const double kLn2Lo = -0x1.718432a1b0e26p-35;
+    const double k64Log2e = 0x1.71547652b82fep+6;    // 64 / ln 2
+    const double kLn2Hi = 0x1.62e42ff000000p-7;      // (ln 2 / 64), 29 bits
+    const double kLn2Lo = -0x1.718432a1b0e26p-41;    // the rest of ln 2 / 64
     // exp underflows to 0 below -745.2 and overflows above 709.8: clamping the
     // argument keeps the reduction exact and lets the final scale saturate
     // (NaN passes through)
     if (!(x != x))
         x = fmin(fmax(x, -750.0), 712.0);
-    const double n = rint(x * kLog2e);
+    const double n = rint(x * k64Log2e);
     double r = fma(-n, kLn2Hi, x);
     r = fma(-n, kLn2Lo, r);
-    double p = k.c[0];
-#pragma unroll
-    for (int i = 1; i < 13; ++i)
-        p = fma(p, r, k.c[i]);
-    return ldexp(p, (int)n);
+    double q = fma(r, 1.0 / 120.0, 1.0 / 24.0);
+    q = fma(q, r, 1.0 / 6.0);
+    q = fma(q, r, 0.5);
+    q = fma(q, r, 1.0);
+    const double p = q * r;   // exp(r) - 1
+    const int ni = (int)n;
+    const double t = s_tab[ni & 63];
+    return ldexp(fma(t, p, t), ni >> 6);
 }
 
 __device__ __forceinline__ float exp_f32(double x)

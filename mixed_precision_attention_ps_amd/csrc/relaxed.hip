@@ -37,7 +37,6 @@ struct RelaxedArgs {
     float *ymix_raw, *yref_out, *row_m;
     double *row_l;
     unsigned long long *exact_tiles;
-    ExpCoef ek;
 };
 
 // Online state of one query row: maxima of y^lo (m_t), y^mix and y^ref, and
@@ -70,9 +69,9 @@ __device__ __forceinline__ void relaxed_tile_scores(TileSmem &sm, const RelaxedA
 }
 
 // exp of a difference of row maxima (-inf when a maximum is still unset).
-__device__ __forceinline__ double exp_delta(float from, float to, const ExpCoef &k)
+__device__ __forceinline__ double exp_delta(float from, float to, const double *s_exp)
 {
-    return from == -INFINITY ? 0.0 : exp64((double)from - (double)to, k);
+    return from == -INFINITY ? 0.0 : exp64((double)from - (double)to, s_exp);
 }
 
 // Per-score exponentials (double): E = exp(y^lo - m_t) serves the criterion
@@ -88,6 +87,9 @@ void relaxed_kernel(RelaxedArgs a)
     constexpr int NV4 = kTile * DV / 4;                   // float4 in a V tile
     constexpr int V4 = (NV4 + kThreads - 1) / kThreads;   // per thread
     __shared__ RelaxedSmem<DV> sm;
+    __shared__ double s_exp[64];   // 2^(k/64) for exp64
+    exp_table_fill(s_exp);
+    __syncthreads();
     const int S = a.S, D = a.D;
     // heaviest query blocks first (causal work grows with the block index)
     const int qb = a.tiles - 1 - (int)(blockIdx.x / a.BH);
@@ -183,7 +185,7 @@ void relaxed_kernel(RelaxedArgs a)
             float bm = -INFINITY, br = -INFINITY;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                E[c] = valid[c] ? exp64((double)lo[r][c] - (double)mt_new, a.ek) : 0.0;
+                E[c] = valid[c] ? exp64((double)lo[r][c] - (double)mt_new, s_exp) : 0.0;
                 sel[c] = valid[c] && 2.0 * E[c] * fabs((double)lo[r][c]) > a.tau;
                 mix[c] = sel[c] ? ref[r][c] : lo[r][c];
                 if (valid[c]) {
@@ -225,23 +227,23 @@ void relaxed_kernel(RelaxedArgs a)
             br = group16_max(br);
             const float mm_new = fmaxf(m_mix, bm);
             const float mr_new = fmaxf(m_ref, br);
-            const double alpha = exp_delta(m_mix, mm_new, a.ek);
+            const double alpha = exp_delta(m_mix, mm_new, s_exp);
             // row factors; a factor that would overflow (maxima more than
             // ~700 apart) falls back to a direct exp per score
-            const double f_lo = exp64((double)mt_new - (double)mm_new, a.ek);
-            const double f_ref = exp64((double)mr_new - (double)mm_new, a.ek);
+            const double f_lo = exp64((double)mt_new - (double)mm_new, s_exp);
+            const double f_ref = exp64((double)mr_new - (double)mm_new, s_exp);
             const bool direct = !(f_lo < 1e300 && f_ref < 1e300);
             double sl = 0.0, sr = 0.0, sa = 0.0, sll = 0.0, sb = 0.0;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 pmix[r][c] = 0.0f;
                 if (valid[c]) {
-                    const double er = exp64((double)ref[r][c] - (double)mr_new, a.ek);
+                    const double er = exp64((double)ref[r][c] - (double)mr_new, s_exp);
                     double pe;
                     if (!direct)
                         pe = sel[c] ? er * f_ref : E[c] * f_lo;
                     else
-                        pe = exp64((double)mix[c] - (double)mm_new, a.ek);
+                        pe = exp64((double)mix[c] - (double)mm_new, s_exp);
                     pmix[r][c] = (float)pe;
                     sl += pe;
                     sr += er;
@@ -258,12 +260,12 @@ void relaxed_kernel(RelaxedArgs a)
                 sb = group16_sum(sb);
             }
             if (i < S && tx == 0) {
-                const double beta = exp_delta(m_ref, mr_new, a.ek);
+                const double beta = exp_delta(m_ref, mr_new, s_exp);
                 rs.l_mix = rs.l_mix * alpha + sl;
                 rs.l_ref = rs.l_ref * beta + sr;
                 rs.kl_a = rs.kl_a * beta + sa;
                 if (want_lowp) {
-                    rs.l_lo = rs.l_lo * exp_delta(m_t, mt_new, a.ek) + sll;
+                    rs.l_lo = rs.l_lo * exp_delta(m_t, mt_new, s_exp) + sll;
                     rs.kl_b = rs.kl_b * beta + sb;
                 }
                 rs.m_t = mt_new;
@@ -387,7 +389,6 @@ hipError_t launch_relaxed(const Problem &p, const uint8_t *unsafe, float *out, u
     a.row_m = row_m;
     a.row_l = row_l;
     a.exact_tiles = exact_tiles;
-    a.ek = make_exp_coef();
     const uint64_t grid = (uint64_t)p.BH * p.tiles;
     const dim3 g((unsigned)grid), b(kThreads);
     if (fast && p.mu > 10)

@@ -31,7 +31,6 @@ struct RowsArgs {
     uint32_t *mask, *row_count;
     float *pbuf, *ymix_out;
     double *row_kl, *row_kl_lowp;
-    ExpCoef ek;
 };
 
 // D4 = D / 4 when the head dimension is a compile-time constant (all loads of
@@ -41,13 +40,25 @@ struct RowsArgs {
 // lives in registers) and guarded only by wave-uniform conditions (the chunk
 // holds valid keys); per-key validity is a select, never a branch, and the
 // per-chunk selection is kept as one bit per lane rather than as 16 wave
-// masks.  Scalar registers then hold no per-chunk state.
+// masks (a chunk's mask is re-formed by a ballot when needed).  Scalar
+// registers then hold no per-chunk state.
+//
+// Probabilities: p_j = exp(y_j - lse_mix) = e_j / L_mix for every key whose
+// score did not change (e_j = exp(y_j - m) is already in registers), and
+// e_hi / L_mix for a recomputed key (e_hi formed in the recompute loop and
+// kept, rounded to FP32, in LDS).  Only a row that takes the full pass (the
+// correction would cancel or overflow) evaluates exp(y - lse_mix) per key.
 template <int D4>
 __global__ __launch_bounds__(kThreads) void strict_rows_kernel(RowsArgs a)
 {
-    __shared__ uint32_t s_list[4][64 * kRowChunk];   // selected keys, compacted
-    __shared__ float s_yhi[4][64 * kRowChunk];       // recomputed scores, by key
+    // per wave: the selected keys (compacted, in key order); the recompute
+    // loop overwrites each slot with the bits of its recomputed score
+    __shared__ uint32_t s_list[4][64 * kRowChunk];
+    __shared__ float s_ehi[4][64 * kRowChunk];       // exp(y_hi - m), same slots
     __shared__ float4 s_q[4][64];                    // the wave's query row (D <= 256)
+    __shared__ double s_exp[64];                     // 2^(k/64) for exp64
+    exp_table_fill(s_exp);
+    __syncthreads();
     // the wave index is uniform: readfirstlane tells the compiler so, which
     // makes the row, its length and every chunk guard scalar
     const int lane = threadIdx.x & 63;
@@ -60,15 +71,17 @@ __global__ __launch_bounds__(kThreads) void strict_rows_kernel(RowsArgs a)
     const int n = a.causal ? i + 1 : S;
     const int nch = (n + 63) >> 6;   // chunks of 64 keys holding valid keys
     const float *y = a.ylo + r * (uint64_t)S;
+    // the row's valid scores and its probabilities, as buffer ranges: loads
+    // past the valid keys read 0 and stores past the row are dropped, with
+    // no branch (a guarded load would wait for its data before the next one)
+    const __amdgpu_buffer_rsrc_t y_rs = row_rsrc(y, 4u * (uint32_t)n);
+    const __amdgpu_buffer_rsrc_t p_rs = row_rsrc(a.pbuf + r * (uint64_t)S, 4u * (uint32_t)S);
 
-    // The row and its maximum.  All 16 loads are issued unconditionally, back
-    // to back (a guarded load would wait for its data before the next one);
-    // past the valid keys every lane reads the row's last valid score, one
-    // cache line.
+    // The row and its maximum (all 16 loads issued back to back).
     float v[kRowChunk];
 #pragma unroll
     for (int t = 0; t < kRowChunk; ++t)
-        v[t] = y[min(lane + 64 * t, n - 1)];
+        v[t] = buf_load_f32(y_rs, 4u * (uint32_t)(lane + 64 * t));
     float m = -INFINITY;
 #pragma unroll
     for (int t = 0; t < kRowChunk; ++t) {
@@ -87,19 +100,19 @@ __global__ __launch_bounds__(kThreads) void strict_rows_kernel(RowsArgs a)
         if (t < nch) {
             const bool valid = lane + 64 * t < n;
             const bool at = valid && v[t] == m;
-            const double x = exp64((double)v[t] - (double)m, a.ek);
+            const double x = exp64((double)v[t] - (double)m, s_exp);
             e[t] = valid ? (at ? 1.0 : x) : 0.0;
             A += (valid && !at) ? x : 0.0;
-            cnt += at ? 1 : 0;
+            cnt += __popcll(__ballot(at));
         }
     }
     A = wave_sum(A);
-    cnt = wave_sum_int(cnt);
     const double L = A + (double)cnt;
     const double rest_at_max = A + (double)(cnt - 1);
-    const double inv_l2 = 1.0 / (L * L);
 
-    // Criterion c = 2 z (1 - z) |y| = 2 e rest |y| / L^2, mask, compaction.
+    // Criterion 2 z (1 - z) |y| > tau with z = e / L and 1 - z = rest / L,
+    // evaluated as e rest |y| > tau L^2 / 2; mask words and compaction.
+    const double tau_l2 = a.tau * (L * L) * 0.5;
     uint32_t selbits = 0;
     uint32_t total = 0;
 #pragma unroll
@@ -111,8 +124,7 @@ __global__ __launch_bounds__(kThreads) void strict_rows_kernel(RowsArgs a)
             if (t < nch) {
                 const bool valid = j < n;
                 const double rest = (valid && v[t] == m) ? rest_at_max : L - e[t];
-                const double c = 2.0 * e[t] * rest * fabs((double)v[t]) * inv_l2;
-                sel = valid && c > a.tau;
+                sel = valid && e[t] * rest * fabs((double)v[t]) > tau_l2;
             }
             const uint64_t b = __ballot(sel);
             if (a.mask) {
@@ -126,6 +138,14 @@ __global__ __launch_bounds__(kThreads) void strict_rows_kernel(RowsArgs a)
             total += (uint32_t)__popcll(b);
         }
     }
+    // e in FP32 from here on (probabilities only: p = e / L_mix); the empty
+    // asm pins the conversion here, so the doubles die before the recompute
+    float ef[kRowChunk];
+#pragma unroll
+    for (int t = 0; t < kRowChunk; ++t) {
+        ef[t] = (float)e[t];
+        asm volatile("" : "+v"(ef[t]));
+    }
 
     // Reference statistics from the score kernel's per-tile partials.
     const bool kl = a.part != nullptr;
@@ -138,7 +158,7 @@ __global__ __launch_bounds__(kThreads) void strict_rows_kernel(RowsArgs a)
         if (lane < nt)
             mine = pp[lane];
         mr = wave_max(mine.m);
-        const double f = lane < nt ? exp64((double)mine.m - (double)mr, a.ek) : 0.0;
+        const double f = lane < nt ? exp64((double)mine.m - (double)mr, s_exp) : 0.0;
         Lr = wave_sum(mine.L * f);
         Br = wave_sum(mine.B * f);
     }
@@ -157,6 +177,7 @@ __global__ __launch_bounds__(kThreads) void strict_rows_kernel(RowsArgs a)
     for (uint32_t ei = lane; ei < total; ei += 64) {
         const uint32_t j = s_list[wave][ei];
         const float4 *k4 = reinterpret_cast<const float4 *>(a.k + (bh * (uint64_t)S + j) * a.D);
+        const float yl = y[j];
         float acc = 0.0f;
         auto mac4 = [&acc](float4 x, float4 z) {
             float p0 = x.x * z.x;
@@ -189,31 +210,80 @@ __global__ __launch_bounds__(kThreads) void strict_rows_kernel(RowsArgs a)
                 mac4(q4[d4], k4[d4]);
         }
         const float yhi = acc * a.s;
-        s_yhi[wave][j] = yhi;
-        const float yl = y[j];
-        dL += exp64((double)yhi - (double)m, a.ek) - exp64((double)yl - (double)m, a.ek);
+        const double ehi = exp64((double)yhi - (double)m, s_exp);
+        s_list[wave][ei] = __float_as_uint(yhi);
+        s_ehi[wave][ei] = (float)ehi;
+        if (a.ymix_out)   // y^mix is y^lo in place: only recomputed keys change
+            a.ymix_out[r * (uint64_t)S + j] = yhi;
+        dL += ehi - exp64((double)yl - (double)m, s_exp);
         if (kl)
-            dA += exp64((double)yhi - (double)mr, a.ek) * ((double)yhi - (double)yl);
+            dA += exp64((double)yhi - (double)mr, s_exp) * ((double)yhi - (double)yl);
     }
     dL = wave_sum(dL);
     dA = wave_sum(dA);
     __builtin_amdgcn_wave_barrier();
 
-    // Scatter the recomputed scores into the row: y^mix.
+    // Slot in the compacted list of this lane's key in chunk t (meaningful
+    // when the key is selected), given the chunk's selection mask b and the
+    // number of keys selected in the chunks before it.
+    auto slot = [&](uint64_t b, uint32_t before) {
+        return min(before + lanes_below(b), (uint32_t)(64 * kRowChunk - 1));
+    };
+    // y^mix in registers: y^lo read again (the probabilities, which may share
+    // its buffer, are not written yet) and the recomputed scores scattered
+    // over it.
+    auto load_ymix = [&]() {
 #pragma unroll
-    for (int t = 0; t < kRowChunk; ++t) {
-        if (t < nch) {
-            const float h = s_yhi[wave][lane + 64 * t];
-            v[t] = ((selbits >> t) & 1u) ? h : v[t];
+        for (int t = 0; t < kRowChunk; ++t)
+            v[t] = buf_load_f32(y_rs, 4u * (uint32_t)(lane + 64 * t));
+#pragma unroll
+        for (int t = 0; t < kRowChunk; ++t)
+            v[t] = lane + 64 * t < n ? v[t] : -INFINITY;
+        uint32_t before = 0;
+#pragma unroll
+        for (int t = 0; t < kRowChunk; ++t) {
+            if (t < nch) {
+                const bool sel = (selbits >> t) & 1u;
+                const uint64_t b = __ballot(sel);
+                if (b) {
+                    const float h = __uint_as_float(s_list[wave][slot(b, before)]);
+                    v[t] = sel ? h : v[t];
+                    before += (uint32_t)__popcll(b);
+                }
+            }
         }
-    }
+    };
 
-    // Log-sum-exp of y^mix.
     const double Lmix = L + dL;
+    const bool corrected = Lmix >= 0.25 * L && isfinite(Lmix);
     double lse_mix;
-    if (Lmix >= 0.25 * L && isfinite(Lmix)) {
+    if (corrected) {
+        // Log-sum-exp by the correction; p = e / L_mix.
         lse_mix = (double)m + log(Lmix);
+        const double inv = 1.0 / Lmix;
+        uint32_t before = 0;
+#pragma unroll
+        for (int t = 0; t < kRowChunk; ++t) {
+            const int j = lane + 64 * t;
+            if (64 * t < S) {
+                float pv = 0.0f;
+                if (t < nch) {
+                    const bool sel = (selbits >> t) & 1u;
+                    const uint64_t b = __ballot(sel);
+                    float ev = ef[t];
+                    if (b) {
+                        const float eh = s_ehi[wave][slot(b, before)];
+                        ev = sel ? eh : ev;
+                        before += (uint32_t)__popcll(b);
+                    }
+                    pv = j < n ? (float)((double)ev * inv) : 0.0f;
+                }
+                buf_store_f32(p_rs, 4u * (uint32_t)j, pv);
+            }
+        }
     } else {
+        // Full pass over y^mix.
+        load_ymix();
         float mm = -INFINITY;
 #pragma unroll
         for (int t = 0; t < kRowChunk; ++t)
@@ -223,32 +293,24 @@ __global__ __launch_bounds__(kThreads) void strict_rows_kernel(RowsArgs a)
 #pragma unroll
         for (int t = 0; t < kRowChunk; ++t) {
             if (t < nch) {
-                const double x = exp64((double)v[t] - (double)mm, a.ek);
+                const double x = exp64((double)v[t] - (double)mm, s_exp);
                 l += lane + 64 * t < n ? x : 0.0;
             }
         }
         lse_mix = (double)mm + log(wave_sum(l));
-    }
-
-    // Probabilities (full rows) and y^mix.
-    float *pr = a.pbuf + r * (uint64_t)S;
-    float *ym = a.ymix_out ? a.ymix_out + r * (uint64_t)S : nullptr;
 #pragma unroll
-    for (int t = 0; t < kRowChunk; ++t) {
-        const int j = lane + 64 * t;
-        if (64 * t < S) {
-            float pv = 0.0f;
-            if (t < nch) {
-                const float x = exp_f32((double)v[t] - lse_mix);
-                pv = j < n ? x : 0.0f;
+        for (int t = 0; t < kRowChunk; ++t) {
+            const int j = lane + 64 * t;
+            if (64 * t < S) {
+                float pv = 0.0f;
+                if (t < nch) {
+                    const float x = exp_f32((double)v[t] - lse_mix);
+                    pv = j < n ? x : 0.0f;
+                }
+                buf_store_f32(p_rs, 4u * (uint32_t)j, pv);
             }
-            if (j < S)
-                pr[j] = pv;
-            if (ym && j < n)
-                ym[j] = v[t];
         }
     }
-
     if (lane == 0) {
         if (a.row_count)
             a.row_count[r] = total;
@@ -263,11 +325,13 @@ __global__ __launch_bounds__(kThreads) void strict_rows_kernel(RowsArgs a)
     }
 }
 
+// y^mix, when asked for, is formed in place over y^lo (ymix_out == ylo); the
+// probabilities may share y^lo's buffer only when y^mix is not asked for.
 hipError_t launch_strict_rows(const Problem &p, const float *ylo, const RefPartial *part,
                               uint32_t *mask, uint32_t *row_count, float *pbuf, float *ymix_out,
                               double *row_kl, double *row_kl_lowp, hipStream_t st)
 {
-    if (p.S > 64 * kRowChunk)
+    if (p.S > 64 * kRowChunk || (ymix_out && (ymix_out != ylo || pbuf == ylo)))
         return hipErrorInvalidValue;
     RowsArgs a;
     a.q = p.q;
@@ -288,7 +352,6 @@ hipError_t launch_strict_rows(const Problem &p, const float *ylo, const RefParti
     a.ymix_out = ymix_out;
     a.row_kl = row_kl;
     a.row_kl_lowp = row_kl_lowp;
-    a.ek = make_exp_coef();
     const uint64_t grid = (p.n_rows + 3) / 4;
     if (p.D == 64)
         hipLaunchKernelGGL(strict_rows_kernel<16>, dim3((unsigned)grid), dim3(kThreads), 0, st, a);

@@ -84,12 +84,11 @@ struct ScoreArgs {
     float *ylo, *yref;
     RefPartial *part;
     unsigned long long *exact_tiles;
-    ExpCoef ek;
 };
 
 template <int PATH>
-__device__ __forceinline__ void score_tile_store(TileSmem &sm, const ScoreArgs &a, int bh, int ti,
-                                                 int tj)
+__device__ __forceinline__ void score_tile_store(TileSmem &sm, const double *s_exp,
+                                                 const ScoreArgs &a, int bh, int ti, int tj)
 {
     const size_t head = (size_t)bh * a.S * a.D;
     TileAcc acc;
@@ -133,7 +132,7 @@ __device__ __forceinline__ void score_tile_store(TileSmem &sm, const ScoreArgs &
 #pragma unroll
             for (int c = 0; c < 4; ++c)
                 if (valid[c]) {
-                    const double e = exp64((double)ref[r][c] - (double)m, a.ek);
+                    const double e = exp64((double)ref[r][c] - (double)m, s_exp);
                     L += e;
                     B += e * ((double)ref[r][c] - (double)lo[r][c]);
                 }
@@ -160,6 +159,9 @@ template <bool FAST_KERNEL>
 __global__ __launch_bounds__(kThreads) void ps_scores_kernel(ScoreArgs a)
 {
     __shared__ TileSmem sm;
+    __shared__ double s_exp[64];   // 2^(k/64) for exp64
+    exp_table_fill(s_exp);
+    __syncthreads();
     const int bh = blockIdx.x / a.tiles_per_head;
     const int t = blockIdx.x % a.tiles_per_head;
     int ti, tj;
@@ -173,13 +175,13 @@ __global__ __launch_bounds__(kThreads) void ps_scores_kernel(ScoreArgs a)
         path = PATH_EXACT;
     if (FAST_KERNEL) {
         if (path == PATH_FAST)
-            score_tile_store<PATH_FAST>(sm, a, bh, ti, tj);
+            score_tile_store<PATH_FAST>(sm, s_exp, a, bh, ti, tj);
     } else if (path == PATH_EXACT) {
         if (threadIdx.x == 0 && a.exact_tiles)
             atomicAdd(a.exact_tiles, 1ull);
-        score_tile_store<PATH_EXACT>(sm, a, bh, ti, tj);
+        score_tile_store<PATH_EXACT>(sm, s_exp, a, bh, ti, tj);
     } else if (path == PATH_FP32) {
-        score_tile_store<PATH_FP32>(sm, a, bh, ti, tj);
+        score_tile_store<PATH_FP32>(sm, s_exp, a, bh, ti, tj);
     }
 }
 
@@ -202,7 +204,6 @@ hipError_t launch_ps_scores(const Problem &p, const uint8_t *unsafe, float *ylo,
     a.yref = yref;
     a.part = part;
     a.exact_tiles = exact_tiles;
-    a.ek = make_exp_coef();
     const long long grid = (long long)p.BH * a.tiles_per_head;
     if (grid > 0x7fffffffLL)
         return hipErrorInvalidValue;

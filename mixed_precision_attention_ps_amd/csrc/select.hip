@@ -24,7 +24,6 @@ struct SelectArgs {
     RowStats *rs;
     double *row_kl, *row_kl_lowp;
     int count_only;
-    ExpCoef ek;
 };
 
 constexpr int kSelChunk = 16;   // keys per lane held in registers (1024 per wave)
@@ -35,6 +34,9 @@ constexpr int kSelChunk = 16;   // keys per lane held in registers (1024 per wav
 template <bool ONE>
 __global__ __launch_bounds__(kThreads) void strict_select_kernel(SelectArgs a)
 {
+    __shared__ double s_exp[64];   // 2^(k/64) for exp64
+    exp_table_fill(s_exp);
+    __syncthreads();
     const int lane = threadIdx.x & 63;
     const uint64_t r = (uint64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (r >= a.n_rows)
@@ -76,10 +78,10 @@ __global__ __launch_bounds__(kThreads) void strict_select_kernel(SelectArgs a)
             cnt++;
             e = 1.0;
         } else {
-            e = exp64((double)v - (double)m, a.ek);
+            e = exp64((double)v - (double)m, s_exp);
             A += e;
         }
-        const double er = exp64((double)vr - (double)mr, a.ek);
+        const double er = exp64((double)vr - (double)mr, s_exp);
         Lr += er;
         Br += er * ((double)vr - (double)v);
     };
@@ -161,7 +163,7 @@ __global__ __launch_bounds__(kThreads) void strict_select_kernel(SelectArgs a)
             double e = 0.0;
             if (j < n) {
                 v = y[j];
-                e = (v == m) ? 1.0 : exp64((double)v - (double)m, a.ek);
+                e = (v == m) ? 1.0 : exp64((double)v - (double)m, s_exp);
             }
             decide(j0, j, v, e);
         }
@@ -190,7 +192,6 @@ hipError_t launch_strict_select(const Problem &p, const float *ylo, const float 
     a.row_kl = row_kl;
     a.row_kl_lowp = row_kl_lowp;
     a.count_only = count_only;
-    a.ek = make_exp_coef();
     const uint64_t grid = (p.n_rows + 3) / 4;
     if (p.S <= 64 * kSelChunk)
         hipLaunchKernelGGL(strict_select_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, st, a);
@@ -338,7 +339,6 @@ struct RecomputeArgs {
     float *ymix;
     RowStats *rs;
     double *row_kl;
-    ExpCoef ek;
 };
 
 // The softmax statistics of y^mix follow from those of y^lo by correcting the
@@ -359,6 +359,8 @@ __global__ __launch_bounds__(kThreads) void recompute_kernel(RecomputeArgs a)
     __shared__ uint32_t s_off[kRcRows + 1];
     __shared__ float s_mlo[kRcRows], s_mref[kRcRows];
     __shared__ double s_dl[kThreads], s_da[kThreads];
+    __shared__ double s_exp[64];   // 2^(k/64) for exp64 (synchronised below)
+    exp_table_fill(s_exp);
     const int tid = threadIdx.x;
     const uint64_t r0 = (uint64_t)blockIdx.x * kRcRows;
     RowStats st{};
@@ -423,8 +425,8 @@ __global__ __launch_bounds__(kThreads) void recompute_kernel(RecomputeArgs a)
                 const float ylo = *slot;
                 *slot = yhi;
                 const double ml = (double)s_mlo[lr], mr = (double)s_mref[lr];
-                cl = exp64((double)yhi - ml, a.ek) - exp64((double)ylo - ml, a.ek);
-                ca = exp64((double)yhi - mr, a.ek) * ((double)yhi - (double)ylo);
+                cl = exp64((double)yhi - ml, s_exp) - exp64((double)ylo - ml, s_exp);
+                ca = exp64((double)yhi - mr, s_exp) * ((double)yhi - (double)ylo);
             }
         }
         s_dl[tid] = cl;
@@ -473,7 +475,6 @@ hipError_t launch_recompute(const Problem &p, const uint32_t *list, const uint32
     a.ymix = ymix;
     a.rs = rs;
     a.row_kl = row_kl;
-    a.ek = make_exp_coef();
     const uint64_t grid = (p.n_rows + kRcRows - 1) / kRcRows;
     hipLaunchKernelGGL(recompute_kernel, dim3((unsigned)grid), dim3(kThreads), 0, st, a);
     return hipGetLastError();
