@@ -56,8 +56,11 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(FinishArgs a)
     }
 
     const int S = a.S, D = a.D;
-    const int bh = blockIdx.x / a.blocks_per_head;
-    const int row0 = (blockIdx.x % a.blocks_per_head) * kFinRows;
+    // heaviest row blocks first (causal work grows with the block index), so
+    // the light ones fill the tail of the launch
+    const int BH = (int)(gridDim.x / a.blocks_per_head);
+    const int bh = (int)(blockIdx.x % BH);
+    const int row0 = (a.blocks_per_head - 1 - (int)(blockIdx.x / BH)) * kFinRows;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
     // lse of each row; rows flagged by the recompute get a pass over the row.

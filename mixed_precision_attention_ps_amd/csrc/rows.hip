@@ -63,9 +63,12 @@ __global__ __launch_bounds__(kThreads) void strict_rows_kernel(RowsArgs a)
     // makes the row, its length and every chunk guard scalar
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint64_t r = (uint64_t)blockIdx.x * 4 + wave;
-    if (r >= a.n_rows)
+    // rows in descending order: the launch ends on the short rows at the top
+    // of the first head (causal work grows with the row index)
+    const uint64_t rr = (uint64_t)blockIdx.x * 4 + wave;
+    if (rr >= a.n_rows)
         return;   // no block barrier below: each wave owns its row
+    const uint64_t r = a.n_rows - 1 - rr;
     const int S = a.S;
     const int i = (int)(r % (uint64_t)S);
     const int n = a.causal ? i + 1 : S;
