@@ -80,7 +80,7 @@ __device__ __forceinline__ double ps_rn64(double x, int mu)
 // ---------------------------------------------------------------------------
 enum { PATH_FAST = 0, PATH_EXACT = 1, PATH_FP32 = 2 };
 
-struct TileSmem {
+struct alignas(16) TileSmem {
     float q[kDChunk][kTile];
     float qs[kDChunk][kTile];
     float k[kDChunk][kTile];
@@ -94,8 +94,11 @@ struct TileAcc {
 
 __device__ __forceinline__ int key_slot(int j) { return (j & 15) * 4 + (j >> 4); }
 
-// Global -> register slice loads: thread loads row (tid >> 2), d offset
-// (tid & 3) * 4 of the Q and K blocks.  Rows past S and d past D read 0.
+// Global -> register slice loads: with kSliceV4 = kDChunk / 16 float4 per
+// thread, thread tid loads row (tid >> 2), d offsets (tid & 3) * 4 + 16 u of
+// the Q and K blocks.  Rows past S and d past D read 0.
+constexpr int kSliceV4 = kDChunk / 16;
+
 __device__ __forceinline__ float4 load_slice(const float *base, int row, int nrows, int D, int d)
 {
     if (row < nrows && d < D)
@@ -104,19 +107,22 @@ __device__ __forceinline__ float4 load_slice(const float *base, int row, int nro
 }
 
 template <int PATH>
-__device__ __forceinline__ void stage_slice(TileSmem &sm, float4 qv, float4 kv, int tid,
-                                            float qscale)
+__device__ __forceinline__ void stage_slice(TileSmem &sm, const float4 (&qv)[kSliceV4],
+                                            const float4 (&kv)[kSliceV4], int tid, float qscale)
 {
-    const int row = tid >> 2, d = (tid & 3) * 4;
-    const float qa[4] = {qv.x, qv.y, qv.z, qv.w};
-    const float ka[4] = {kv.x, kv.y, kv.z, kv.w};
-    const int slot = key_slot(row);
+    const int row = tid >> 2, slot = key_slot(row);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        sm.q[d + e][row] = qa[e];
-        if (PATH == PATH_FAST)
-            sm.qs[d + e][row] = qa[e] * qscale;
-        sm.k[d + e][slot] = ka[e];
+    for (int u = 0; u < kSliceV4; ++u) {
+        const int d = (tid & 3) * 4 + 16 * u;
+        const float qa[4] = {qv[u].x, qv[u].y, qv[u].z, qv[u].w};
+        const float ka[4] = {kv[u].x, kv[u].y, kv[u].z, kv[u].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            sm.q[d + e][row] = qa[e];
+            if (PATH == PATH_FAST)
+                sm.qs[d + e][row] = qa[e] * qscale;
+            sm.k[d + e][slot] = ka[e];
+        }
     }
 }
 
@@ -180,15 +186,22 @@ __device__ __forceinline__ void score_tile(TileSmem &sm, TileAcc &acc, const flo
     const float *Qb = Qh + (size_t)row0 * D;
     const float *Kb = Kh + (size_t)col0 * D;
     const int qrows = S - row0, krows = S - col0;
-    float4 qv = load_slice(Qb, lrow, qrows, D, ld);
-    float4 kv = load_slice(Kb, lrow, krows, D, ld);
+    float4 qv[kSliceV4], kv[kSliceV4];
+#pragma unroll
+    for (int u = 0; u < kSliceV4; ++u) {
+        qv[u] = load_slice(Qb, lrow, qrows, D, ld + 16 * u);
+        kv[u] = load_slice(Kb, lrow, krows, D, ld + 16 * u);
+    }
     for (int d0 = 0; d0 < D; d0 += kDChunk) {
         __syncthreads();
         stage_slice<PATH>(sm, qv, kv, tid, pc.qscale);
         __syncthreads();
         if (d0 + kDChunk < D) {
-            qv = load_slice(Qb, lrow, qrows, D, d0 + kDChunk + ld);
-            kv = load_slice(Kb, lrow, krows, D, d0 + kDChunk + ld);
+#pragma unroll
+            for (int u = 0; u < kSliceV4; ++u) {
+                qv[u] = load_slice(Qb, lrow, qrows, D, d0 + kDChunk + ld + 16 * u);
+                kv[u] = load_slice(Kb, lrow, krows, D, d0 + kDChunk + ld + 16 * u);
+            }
         }
         compute_slice<PATH>(sm, acc, tx, ty, pc);
     }
@@ -219,39 +232,62 @@ __device__ __forceinline__ void tile_scores(const TileAcc &acc, const PsConst &p
 // Within each row of 16 lanes the partners are exchanged through DPP
 // (quad_perm [1,0,3,2] and [2,3,0,1], row_half_mirror, row_mirror): after the
 // four steps every lane of a row holds the row's reduction.  A wave reduction
-// then reads lanes 0, 16, 32 and 48 (readlane) and combines them, so its
-// result is wave-uniform.  No LDS traffic, no waits on it.
+// then folds the rows with row_bcast:15 (lane 15 of each row into rows 1 and
+// 3) and row_bcast:31 (lane 31 into rows 2 and 3), which leaves the total in
+// lane 63, and reads it with readlane, so the result is wave-uniform.  No
+// LDS traffic, no waits on it.
 // ---------------------------------------------------------------------------
 constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
 constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141;   // lane i <- lane 7 - i within 8
 constexpr int kDppMirror = 0x140;       // lane i <- lane 15 - i within 16
+constexpr int kDppBcast15 = 0x142;      // row r <- lane 15 of row r - 1
+constexpr int kDppBcast31 = 0x143;      // rows 2, 3 <- lane 31
 
+// A DPP move over all rows and banks (every lane has a source).
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t v)
 {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xf, 0xf, false);
 }
 
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v)
+// A DPP move into the rows of ROW_MASK; the other rows keep `old`.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_u32_rows(uint32_t old, uint32_t v)
 {
-    return __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v)));
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROW_MASK, 0xf, false);
 }
 
-template <int CTRL>
-__device__ __forceinline__ double dpp(double v)
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp(float v, float old = 0.0f)
+{
+    if (ROW_MASK == 0xf)
+        return __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v)));
+    return __uint_as_float(dpp_u32_rows<CTRL, ROW_MASK>(__float_as_uint(old), __float_as_uint(v)));
+}
+
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ double dpp(double v, double old = 0.0)
 {
     const uint64_t u = (uint64_t)__double_as_longlong(v);
-    const uint64_t lo = dpp_u32<CTRL>((uint32_t)u);
-    const uint64_t hi = dpp_u32<CTRL>((uint32_t)(u >> 32));
+    const uint64_t o = (uint64_t)__double_as_longlong(old);
+    uint64_t lo, hi;
+    if (ROW_MASK == 0xf) {
+        lo = dpp_u32<CTRL>((uint32_t)u);
+        hi = dpp_u32<CTRL>((uint32_t)(u >> 32));
+    } else {
+        lo = dpp_u32_rows<CTRL, ROW_MASK>((uint32_t)o, (uint32_t)u);
+        hi = dpp_u32_rows<CTRL, ROW_MASK>((uint32_t)(o >> 32), (uint32_t)(u >> 32));
+    }
     return __longlong_as_double((long long)((hi << 32) | lo));
 }
 
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp(uint32_t v)
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ uint32_t dpp(uint32_t v, uint32_t old = 0u)
 {
-    return dpp_u32<CTRL>(v);
+    if (ROW_MASK == 0xf)
+        return dpp_u32<CTRL>(v);
+    return dpp_u32_rows<CTRL, ROW_MASK>(old, v);
 }
 
 template <typename T, typename Op>
@@ -282,11 +318,14 @@ __device__ __forceinline__ double lane_read(double v, int l)
     return __longlong_as_double((long long)((hi << 32) | lo));
 }
 
+// `id` is the identity of `op` (what rows outside a broadcast's mask add).
 template <typename T, typename Op>
-__device__ __forceinline__ T wave_reduce(T v, Op op)
+__device__ __forceinline__ T wave_reduce(T v, Op op, T id)
 {
     v = row16_reduce(v, op);
-    return op(op(lane_read(v, 0), lane_read(v, 16)), op(lane_read(v, 32), lane_read(v, 48)));
+    v = op(v, dpp<kDppBcast15, 0xA>(v, id));
+    v = op(v, dpp<kDppBcast31, 0xC>(v, id));
+    return lane_read(v, 63);
 }
 
 struct OpMax {
@@ -297,11 +336,11 @@ struct OpAdd {
     __device__ T operator()(T a, T b) const { return a + b; }
 };
 
-__device__ __forceinline__ float wave_max(float v) { return wave_reduce(v, OpMax{}); }
-__device__ __forceinline__ double wave_sum(double v) { return wave_reduce(v, OpAdd{}); }
+__device__ __forceinline__ float wave_max(float v) { return wave_reduce(v, OpMax{}, -INFINITY); }
+__device__ __forceinline__ double wave_sum(double v) { return wave_reduce(v, OpAdd{}, 0.0); }
 __device__ __forceinline__ int wave_sum_int(int v)
 {
-    return (int)wave_reduce((uint32_t)v, OpAdd{});
+    return (int)wave_reduce((uint32_t)v, OpAdd{}, 0u);
 }
 
 // Max / sum over the 16 lanes that share a row (lane groups of 16).

@@ -55,16 +55,12 @@ __device__ __forceinline__ void exp_table_fill(double *s_tab)
         s_tab[k] = kExp2Frac64[k];
 }
 
-__device__ __forceinline__ double exp64(double x, const double *s_tab)
+// The reduction, polynomial and scale, for x in [-750, 712].
+__device__ __forceinline__ double exp64_core(double x, const double *s_tab)
 {
     const double k64Log2e = 0x1.71547652b82fep+6;    // 64 / ln 2
     const double kLn2Hi = 0x1.62e42ff000000p-7;      // (ln 2 / 64), 29 bits
     const double kLn2Lo = -0x1.718432a1b0e26p-41;    // the rest of ln 2 / 64
-    // exp underflows to 0 below -745.2 and overflows above 709.8: clamping the
-    // argument keeps the reduction exact and lets the final scale saturate
-    // (NaN passes through)
-    if (!(x != x))
-        x = fmin(fmax(x, -750.0), 712.0);
     const double n = rint(x * k64Log2e);
     double r = fma(-n, kLn2Hi, x);
     r = fma(-n, kLn2Lo, r);
@@ -76,6 +72,23 @@ __device__ __forceinline__ double exp64(double x, const double *s_tab)
     const int ni = (int)n;
     const double t = s_tab[ni & 63];
     return ldexp(fma(t, p, t), ni >> 6);
+}
+
+__device__ __forceinline__ double exp64(double x, const double *s_tab)
+{
+    // exp underflows to 0 below -745.2 and overflows above 709.8: clamping the
+    // argument keeps the reduction exact and lets the final scale saturate
+    // (NaN passes through)
+    if (!(x != x))
+        x = fmin(fmax(x, -750.0), 712.0);
+    return exp64_core(x, s_tab);
+}
+
+// exp of an argument that is <= 0 or -inf (a score minus its row maximum);
+// a NaN argument gives 0, so a caller that must propagate NaN checks for it.
+__device__ __forceinline__ double exp64_nonpos(double x, const double *s_tab)
+{
+    return exp64_core(fmax(x, -750.0), s_tab);
 }
 
 __device__ __forceinline__ float exp_f32(double x)

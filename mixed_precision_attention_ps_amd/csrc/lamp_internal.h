@@ -8,7 +8,7 @@
 namespace lamp {
 
 constexpr int kTile = 64;        // query rows and keys per score tile
-constexpr int kDChunk = 16;      // head-dimension slice staged in LDS at a time
+constexpr int kDChunk = 32;      // head-dimension slice staged in LDS at a time (multiple of 16)
 constexpr int kThreads = 256;    // threads per work-group (4 wave64)
 
 // Per-launch constants of the PS(mu) arithmetic.

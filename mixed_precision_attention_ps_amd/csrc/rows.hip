@@ -93,23 +93,29 @@ __global__ __launch_bounds__(kThreads) void strict_rows_kernel(RowsArgs a)
     }
     m = wave_max(m);
 
-    // e_j = exp(y_j - m); A = sum below the maximum; cnt = keys at it.
+    // e_j = exp(y_j - m); A = sum below the maximum; cnt = keys at it.  The
+    // keys past n hold -inf and give e = 0.  A NaN score gives e = 0 here and
+    // makes the whole row NaN below (through A).
     double e[kRowChunk];
     double A = 0.0;
     int cnt = 0;
+    bool has_nan = false;
 #pragma unroll
     for (int t = 0; t < kRowChunk; ++t) {
         e[t] = 0.0;
         if (t < nch) {
-            const bool valid = lane + 64 * t < n;
-            const bool at = valid && v[t] == m;
-            const double x = exp64((double)v[t] - (double)m, s_exp);
-            e[t] = valid ? (at ? 1.0 : x) : 0.0;
-            A += (valid && !at) ? x : 0.0;
+            const bool at = lane + 64 * t < n && v[t] == m;
+            const double x = exp64_nonpos((double)v[t] - (double)m, s_exp);
+            e[t] = at ? 1.0 : x;
+            A += at ? 0.0 : x;
             cnt += __popcll(__ballot(at));
+            has_nan |= v[t] != v[t];
         }
     }
     A = wave_sum(A);
+    const bool row_nan = __ballot(has_nan) != 0;
+    if (row_nan)
+        A = __builtin_nan("");
     const double L = A + (double)cnt;
     const double rest_at_max = A + (double)(cnt - 1);
 
@@ -161,7 +167,7 @@ __global__ __launch_bounds__(kThreads) void strict_rows_kernel(RowsArgs a)
         if (lane < nt)
             mine = pp[lane];
         mr = wave_max(mine.m);
-        const double f = lane < nt ? exp64((double)mine.m - (double)mr, s_exp) : 0.0;
+        const double f = lane < nt ? exp64_nonpos((double)mine.m - (double)mr, s_exp) : 0.0;
         Lr = wave_sum(mine.L * f);
         Br = wave_sum(mine.B * f);
     }
@@ -218,7 +224,7 @@ __global__ __launch_bounds__(kThreads) void strict_rows_kernel(RowsArgs a)
         s_ehi[wave][ei] = (float)ehi;
         if (a.ymix_out)   // y^mix is y^lo in place: only recomputed keys change
             a.ymix_out[r * (uint64_t)S + j] = yhi;
-        dL += ehi - exp64((double)yl - (double)m, s_exp);
+        dL += ehi - exp64_nonpos((double)yl - (double)m, s_exp);
         if (kl)
             dA += exp64((double)yhi - (double)mr, s_exp) * ((double)yhi - (double)yl);
     }
@@ -259,11 +265,13 @@ __global__ __launch_bounds__(kThreads) void strict_rows_kernel(RowsArgs a)
 
     const double Lmix = L + dL;
     const bool corrected = Lmix >= 0.25 * L && isfinite(Lmix);
-    double lse_mix;
+    // log-sum-exp of y^mix = mix_base + log(mix_l)
+    double mix_base = (double)m, mix_l = Lmix;
+    // 1 / L_mix (lane 0) and 1 / L_ref (lane 1) by one division
+    const double rcp = 1.0 / (lane == 0 ? Lmix : Lr);
     if (corrected) {
-        // Log-sum-exp by the correction; p = e / L_mix.
-        lse_mix = (double)m + log(Lmix);
-        const double inv = 1.0 / Lmix;
+        // p = e / L_mix.
+        const double inv = lane_read(rcp, 0);
         uint32_t before = 0;
 #pragma unroll
         for (int t = 0; t < kRowChunk; ++t) {
@@ -296,11 +304,13 @@ __global__ __launch_bounds__(kThreads) void strict_rows_kernel(RowsArgs a)
 #pragma unroll
         for (int t = 0; t < kRowChunk; ++t) {
             if (t < nch) {
-                const double x = exp64((double)v[t] - (double)mm, s_exp);
+                const double x = exp64_nonpos((double)v[t] - (double)mm, s_exp);
                 l += lane + 64 * t < n ? x : 0.0;
             }
         }
-        lse_mix = (double)mm + log(wave_sum(l));
+        mix_base = (double)mm;
+        mix_l = row_nan ? __builtin_nan("") : wave_sum(l);
+        const double lse_mix = mix_base + log(mix_l);
 #pragma unroll
         for (int t = 0; t < kRowChunk; ++t) {
             const int j = lane + 64 * t;
@@ -314,16 +324,26 @@ __global__ __launch_bounds__(kThreads) void strict_rows_kernel(RowsArgs a)
             }
         }
     }
+    // KL(P_ref || P) = sum p_ref (y_ref - y) + lse(y) - lse(y_ref): the three
+    // logarithms log L_lo, log L_ref, log L_mix in one evaluation (lanes 0-2)
+    double kl_lo = 0.0, kl_mix = 0.0;
+    if (kl) {
+        const double lg = log(lane == 0 ? L : (lane == 1 ? Lr : mix_l));
+        const double lse_lo = (double)m + lane_read(lg, 0);
+        const double lse_ref = (double)mr + lane_read(lg, 1);
+        const double lse_mix = mix_base + lane_read(lg, 2);
+        const double inv_lr = lane_read(rcp, 1);
+        kl_lo = Br * inv_lr + lse_lo - lse_ref;
+        kl_mix = (Br - dA) * inv_lr + lse_mix - lse_ref;
+    }
     if (lane == 0) {
         if (a.row_count)
             a.row_count[r] = total;
         if (kl) {
-            const double lse_lo = (double)m + log(L);
-            const double lse_ref = (double)mr + log(Lr);
             if (a.row_kl_lowp)
-                a.row_kl_lowp[r] = Br / Lr + lse_lo - lse_ref;
+                a.row_kl_lowp[r] = kl_lo;
             if (a.row_kl)
-                a.row_kl[r] = (Br - dA) / Lr + lse_mix - lse_ref;
+                a.row_kl[r] = kl_mix;
         }
     }
 }
