@@ -114,35 +114,54 @@ __device__ __forceinline__ void score_tile_store(TileSmem &sm, const double *s_e
         }
     }
     if (a.part) {
-        // this tile's softmax statistics of the reference scores, per row
+        // this tile's softmax statistics of the reference scores, per row:
+        // every key is evaluated (no divergent branch) and the keys outside
+        // the row are masked out of the sums.  The fast path's scores are
+        // finite (its operands are bounded), so its exponential needs no NaN
+        // handling; the other paths keep NaN in the sums.
+        float m[4];
+        bool valid[4][4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int i = ti * kTile + ty * 4 + r;
-            bool valid[4];
-            float m = -INFINITY;
+            m[r] = -INFINITY;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const int j = tj * kTile + tx + 16 * c;
-                valid[c] = i < a.S && j < a.S && (!a.causal || j <= i);
-                if (valid[c])
-                    m = fmaxf(m, ref[r][c]);
+                valid[r][c] = i < a.S && j < a.S && (!a.causal || j <= i);
+                m[r] = fmaxf(m[r], valid[r][c] ? ref[r][c] : -INFINITY);
             }
-            m = group16_max(m);
-            double L = 0.0, B = 0.0;
+            m[r] = group16_max(m[r]);
+        }
+        double L[4], B[4];
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
-                if (valid[c]) {
-                    const double e = exp64((double)ref[r][c] - (double)m, s_exp);
-                    L += e;
-                    B += e * ((double)ref[r][c] - (double)lo[r][c]);
-                }
-            L = group16_sum(L);
-            B = group16_sum(B);
+        for (int r = 0; r < 4; ++r) {
+            L[r] = 0.0;
+            B[r] = 0.0;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const double x = (double)ref[r][c] - (double)m[r];
+                const double e = PATH == PATH_FAST ? exp64_nonpos(x, s_exp) : exp64(x, s_exp);
+                // y_ref - y_lo in FP32: exact when the two are within a factor
+                // of two (Sterbenz), else within half an ulp of the difference
+                const double dy = (double)(ref[r][c] - lo[r][c]);
+                L[r] += valid[r][c] ? e : 0.0;
+                B[r] = valid[r][c] ? fma(e, dy, B[r]) : B[r];
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            L[r] = group16_sum(L[r]);
+            B[r] = group16_sum(B[r]);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = ti * kTile + ty * 4 + r;
             if (tx == 0 && i < a.S) {
                 RefPartial rp;
-                rp.L = L;
-                rp.B = B;
-                rp.m = m;
+                rp.L = L[r];
+                rp.B = B[r];
+                rp.m = m[r];
                 rp.pad = 0.0f;
                 a.part[((size_t)bh * a.S + i) * a.tiles + tj] = rp;
             }
