@@ -84,6 +84,7 @@ struct ScoreArgs {
     float *ylo, *yref;
     RefPartial *part;
     unsigned long long *exact_tiles;
+    long long n_tiles;   // BH x tiles per head
 };
 
 template <int PATH>
@@ -173,7 +174,9 @@ __device__ __forceinline__ void score_tile_store(TileSmem &sm, const double *s_e
 // operands allow the FP32 fast path (and returns on the others); the generic
 // kernel takes every other tile (exact double path, or plain FP32 at mu = 23).
 // Keeping the exact path out of the fast kernel keeps its register budget,
-// and so its occupancy, to what the fast path needs.
+// and so its occupancy, to what the fast path needs.  The fast kernel has one
+// work-group per tile; the generic one a bounded grid that strides over the
+// tiles (it usually finds none to do, and then costs a few microseconds).
 template <bool FAST_KERNEL>
 __global__ __launch_bounds__(kThreads) void ps_scores_kernel(ScoreArgs a)
 {
@@ -181,28 +184,44 @@ __global__ __launch_bounds__(kThreads) void ps_scores_kernel(ScoreArgs a)
     __shared__ double s_exp[64];   // 2^(k/64) for exp64
     exp_table_fill(s_exp);
     __syncthreads();
-    const int bh = blockIdx.x / a.tiles_per_head;
-    const int t = blockIdx.x % a.tiles_per_head;
-    int ti, tj;
-    tile_coords(t, a.tiles, a.causal, ti, tj);
-    int path;
-    if (a.pc.mu == 23)
-        path = PATH_FP32;
-    else if (a.pc.mu <= 10 && !a.unsafe_q[bh * a.tiles + ti] && !a.unsafe_k[bh * a.tiles + tj])
-        path = PATH_FAST;
-    else
-        path = PATH_EXACT;
-    if (FAST_KERNEL) {
-        if (path == PATH_FAST)
-            score_tile_store<PATH_FAST>(sm, s_exp, a, bh, ti, tj);
-    } else if (path == PATH_EXACT) {
-        if (threadIdx.x == 0 && a.exact_tiles)
-            atomicAdd(a.exact_tiles, 1ull);
-        score_tile_store<PATH_EXACT>(sm, s_exp, a, bh, ti, tj);
-    } else if (path == PATH_FP32) {
-        score_tile_store<PATH_FP32>(sm, s_exp, a, bh, ti, tj);
+    auto tile_path = [&](long long g, int &bh, int &ti, int &tj) {
+        bh = (int)(g / a.tiles_per_head);
+        tile_coords((int)(g % a.tiles_per_head), a.tiles, a.causal, ti, tj);
+        if (a.pc.mu == 23)
+            return (int)PATH_FP32;
+        if (a.pc.mu <= 10 && !a.unsafe_q[bh * a.tiles + ti] && !a.unsafe_k[bh * a.tiles + tj])
+            return (int)PATH_FAST;
+        return (int)PATH_EXACT;
+    };
+    if (!FAST_KERNEL) {
+        // the threads look at this work-group's tiles in parallel; without a
+        // tile for the generic paths the work-group is done
+        bool need = false;
+        for (long long g = blockIdx.x + (long long)threadIdx.x * gridDim.x; g < a.n_tiles;
+             g += (long long)blockDim.x * gridDim.x) {
+            int bh, ti, tj;
+            need |= tile_path(g, bh, ti, tj) != PATH_FAST;
+        }
+        if (!__syncthreads_or(need ? 1 : 0))
+            return;
+    }
+    for (long long g = blockIdx.x; g < a.n_tiles; g += FAST_KERNEL ? a.n_tiles : gridDim.x) {
+        int bh, ti, tj;
+        const int path = tile_path(g, bh, ti, tj);
+        if (FAST_KERNEL) {
+            if (path == PATH_FAST)
+                score_tile_store<PATH_FAST>(sm, s_exp, a, bh, ti, tj);
+        } else if (path == PATH_EXACT) {
+            if (threadIdx.x == 0 && a.exact_tiles)
+                atomicAdd(a.exact_tiles, 1ull);
+            score_tile_store<PATH_EXACT>(sm, s_exp, a, bh, ti, tj);
+        } else if (path == PATH_FP32) {
+            score_tile_store<PATH_FP32>(sm, s_exp, a, bh, ti, tj);
+        }
     }
 }
+
+constexpr long long kGenericGrid = 2048;   // work-groups of the generic kernel
 
 hipError_t launch_ps_scores(const Problem &p, const uint8_t *unsafe, float *ylo, float *yref,
                             RefPartial *part, unsigned long long *exact_tiles, bool fast,
@@ -226,11 +245,15 @@ hipError_t launch_ps_scores(const Problem &p, const uint8_t *unsafe, float *ylo,
     const long long grid = (long long)p.BH * a.tiles_per_head;
     if (grid > 0x7fffffffLL)
         return hipErrorInvalidValue;
+    a.n_tiles = grid;
+    if (grid == 0)
+        return hipSuccess;
     if (fast) {
         if (p.mu <= 10)
             hipLaunchKernelGGL(ps_scores_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, st, a);
     } else {
-        hipLaunchKernelGGL(ps_scores_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, st, a);
+        const long long g = grid < kGenericGrid ? grid : kGenericGrid;
+        hipLaunchKernelGGL(ps_scores_kernel<false>, dim3((unsigned)g), dim3(kThreads), 0, st, a);
     }
     return hipGetLastError();
 }

@@ -205,6 +205,11 @@ hipError_t launch_strict_select(const Problem &p, const float *ylo, const float 
 // (SplitMix64(seed ^ linear index), j).  One work-group per row: an 8-pass
 // radix select over the 64-bit hashes finds the k-th smallest value T; keys
 // with hash < T are selected, and keys equal to T by increasing j until k.
+// HPT > 0: each thread keeps its HPT hashes (keys tid + 256 u) in registers,
+// so they are formed once (rows of at most 256 HPT keys); HPT = 0 forms them
+// again in every pass.  Each pass builds a 256-bin histogram of the current
+// digit with LDS atomics and finds the digit holding the rank by a parallel
+// exclusive scan of the bins (one bin per thread).
 // ---------------------------------------------------------------------------
 struct RandomArgs {
     int S, causal, W;
@@ -213,9 +218,31 @@ struct RandomArgs {
     const uint32_t *row_count;
 };
 
+// Exclusive prefix sum of one value per thread over a 256-thread block.
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, uint32_t *s_wtot)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t inc = x;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(inc, o, 64);
+        if (lane >= o)
+            inc += y;
+    }
+    if (lane == 63)
+        s_wtot[wave] = inc;
+    __syncthreads();
+    uint32_t before = 0;
+    for (int w = 0; w < wave; ++w)
+        before += s_wtot[w];
+    return before + inc - x;
+}
+
+template <int HPT>
 __global__ __launch_bounds__(kThreads) void random_select_kernel(RandomArgs a)
 {
     __shared__ uint32_t hist[256];
+    __shared__ uint32_t s_wtot[4];
     __shared__ uint64_t s_prefix;
     __shared__ uint32_t s_rank;
     __shared__ uint32_t s_eqw[4], s_selw[4];
@@ -227,6 +254,16 @@ __global__ __launch_bounds__(kThreads) void random_select_kernel(RandomArgs a)
     const uint32_t k = a.row_count[r];
     const uint64_t base = r * (uint64_t)S;     // linear index of score (b, h, i, 0)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    auto hash = [&](int j) { return splitmix64(a.seed ^ (base + (uint64_t)j)); };
+
+    uint64_t hc[HPT > 0 ? HPT : 1];
+    if (HPT > 0) {
+#pragma unroll
+        for (int u = 0; u < (HPT > 0 ? HPT : 1); ++u) {
+            const int j = tid + kThreads * u;
+            hc[u] = j < n ? hash(j) : ~0ull;
+        }
+    }
 
     // Radix select of the k-th smallest hash T (8 digits of 8 bits, MSB first);
     // `rank` ends as the number of keys equal to T that are taken.
@@ -236,21 +273,27 @@ __global__ __launch_bounds__(kThreads) void random_select_kernel(RandomArgs a)
         for (int shift = 56; shift >= 0; shift -= 8) {
             hist[tid] = 0;
             __syncthreads();
-            for (int j = tid; j < n; j += kThreads) {
-                const uint64_t h = splitmix64(a.seed ^ (base + (uint64_t)j));
+            auto count = [&](uint64_t h) {
                 if ((h & pmask) == prefix)
                     atomicAdd(&hist[(uint32_t)(h >> shift) & 255u], 1u);
+            };
+            if (HPT > 0) {
+#pragma unroll
+                for (int u = 0; u < (HPT > 0 ? HPT : 1); ++u)
+                    if (tid + kThreads * u < n)
+                        count(hc[u]);
+            } else {
+                for (int j = tid; j < n; j += kThreads)
+                    count(hash(j));
             }
             __syncthreads();
-            if (tid == 0) {
-                uint32_t cum = 0;
-                int d = 0;
-                for (; d < 255; ++d) {
-                    if (cum + hist[d] >= rank)
-                        break;
-                    cum += hist[d];
-                }
-                s_prefix = prefix | ((uint64_t)d << shift);
+            const uint32_t hd = hist[tid];
+            const uint32_t cum = block_excl_scan(hd, s_wtot);
+            // the digit holding the rank: cum < rank <= cum + hist (the last
+            // digit if the rank exceeds the candidates, which the counts
+            // exclude)
+            if ((cum < rank && rank <= cum + hd) || (tid == 255 && rank > cum + hd)) {
+                s_prefix = prefix | ((uint64_t)tid << shift);
                 s_rank = rank - cum;
             }
             __syncthreads();
@@ -267,11 +310,19 @@ __global__ __launch_bounds__(kThreads) void random_select_kernel(RandomArgs a)
     }
     __syncthreads();
     const uint64_t seg = row_segment(r, S, a.causal);
-    for (int j0 = 0; j0 < S; j0 += kThreads) {
+    for (int j0 = 0, u = 0; j0 < S; j0 += kThreads, ++u) {
         const int j = j0 + tid;
         bool lt = false, eq = false;
         if (k > 0 && j < n) {
-            const uint64_t h = splitmix64(a.seed ^ (base + (uint64_t)j));
+            uint64_t h;
+            if (HPT > 0) {
+                h = hc[0];
+#pragma unroll
+                for (int uu = 1; uu < (HPT > 0 ? HPT : 1); ++uu)
+                    h = uu == u ? hc[uu] : h;
+            } else {
+                h = hash(j);
+            }
             lt = h < T;
             eq = h == T;
         }
@@ -285,10 +336,8 @@ __global__ __launch_bounds__(kThreads) void random_select_kernel(RandomArgs a)
         const bool sel = lt || (eq && eq_rank < rank);
         const uint64_t b = __ballot(sel);
         const int w32 = (j0 + wave * 64) >> 5;
-        if (a.mask && lane == 0 && w32 < a.W)
-            a.mask[r * (uint64_t)a.W + w32] = (uint32_t)b;
-        if (a.mask && lane == 1 && w32 + 1 < a.W)
-            a.mask[r * (uint64_t)a.W + w32 + 1] = (uint32_t)(b >> 32);
+        if (a.mask && lane < 2 && w32 + lane < a.W)
+            a.mask[r * (uint64_t)a.W + w32 + lane] = lane ? (uint32_t)(b >> 32) : (uint32_t)b;
         if (lane == 0)
             s_selw[wave] = (uint32_t)__popcll(b);
         __syncthreads();
@@ -320,7 +369,12 @@ hipError_t launch_random_select(const Problem &p, uint64_t seed, uint32_t *mask,
     a.mask = mask;
     a.list = list;
     a.row_count = row_count;
-    hipLaunchKernelGGL(random_select_kernel, dim3((unsigned)p.n_rows), dim3(kThreads), 0, st, a);
+    if (p.S <= 4 * kThreads)
+        hipLaunchKernelGGL(random_select_kernel<4>, dim3((unsigned)p.n_rows), dim3(kThreads), 0, st, a);
+    else if (p.S <= 16 * kThreads)
+        hipLaunchKernelGGL(random_select_kernel<16>, dim3((unsigned)p.n_rows), dim3(kThreads), 0, st, a);
+    else
+        hipLaunchKernelGGL(random_select_kernel<0>, dim3((unsigned)p.n_rows), dim3(kThreads), 0, st, a);
     return hipGetLastError();
 }
 
