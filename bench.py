@@ -199,6 +199,11 @@ def main():
                 "slots_per_score": w_alg}
     # whole path against the same peak (8D + D + 20 + 2 r D per score) and HBM
     w_path = 9 * D + 20 + 2 * rate * D
+    # the same work against the single-pipe 16-lane VALU rate (256 CUs x 4 SIMDs
+    # x 16 lanes x 2.4 GHz = 3.93e13 lane-slots/s), counting the FP32 reference
+    # dot at two lanes per slot as above: the convention of a pure 16-lane
+    # machine, which the measured co-issue of FP32 and integer work exceeds
+    VALU16_PEAK = 256 * 4 * 16 * 2.4e9
     hbm_bytes = (0 if args.no_probs else 4) + 1 / 8 + 32 * D / (S + 1)
     rec = {
         "metric": METRIC, "value": value, "unit": "scores/s", "n_gpus": 1,
@@ -211,6 +216,7 @@ def main():
                    "parallelism": "none (1 GPU)"},
         "roofline": roofline,
         "path_alu_frac": w_path * value / ALU_PEAK,
+        "path_valu16_frac": w_path * value / VALU16_PEAK,
         "path_hbm_frac": hbm_bytes * value / HBM_PEAK,
         "gpu_ms_per_step": gpu_ms / args.steps,
         "stages_ms": stages,

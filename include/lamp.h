@@ -162,6 +162,47 @@ int lamp_ps_scores(const float *q, const float *k, int B, int H, int S, int D, i
                    float *ylo, float *yref, void *stream);
 
 /*
+ * lamp_decode_fwd -- relaxed LAMP at decode shapes: Nq new queries per (batch,
+ * head) against a cache of S keys (LAMP summary, "Experimental results": the
+ * relaxed relative-threshold rule, which needs no look-ahead over the row, so
+ * the keys can be split across the GPU; "Implementation strategy" steps 1-3).
+ * The queries are the last Nq positions of the sequence: with causal = 1,
+ * query t sees keys 0 .. S - Nq + t; with causal = 0 every query sees all S
+ * keys.  Every result equals rows S - Nq .. S - 1 of lamp_attention_fwd in
+ * LAMP_RELAXED mode on the full sequence (same PS(mu) scores, the same
+ * canonical 64-key running maximum for the rule, bit-exact masks).
+ *   q               [B,H,Nq,D] queries (required).
+ *   k, v            [B,H,S,D] key / value cache (required).
+ *   B, H, Nq, S, D  sizes, >= 1; Nq <= 16 and Nq <= S; D % 4 == 0, D <= 256;
+ *                   B*H*Nq <= 65535.
+ *   causal, mu, tau as for lamp_attention_fwd.
+ *   out             [B,H,Nq,D] (required).
+ *   probs           [B,H,Nq,S] or NULL; keys a query does not see are 0.
+ *   recompute_mask  [B,H,Nq,ceil(S/32)] uint32 or NULL, encoded as above.
+ *   stats           host lamp_stats or NULL (non-NULL synchronises); n_rows is
+ *                   B*H*Nq and n_exact_tiles counts 256-key chunks that took
+ *                   the exact double-precision path.
+ *   p               NULL or extras: stream, workspace (see
+ *                   lamp_decode_workspace_bytes), row_kl / row_kl_lowp /
+ *                   row_count per query row ([B,H,Nq]), scores_mix / scores_ref
+ *                   ([B,H,Nq,S]: y^mix and y^ref of the valid keys), and
+ *                   stage_events (LAMP_STAGE_SCORES: score pass;
+ *                   LAMP_STAGE_SELECT: rule, softmax and P.V partials per
+ *                   chunk; LAMP_STAGE_FINISH: combine and probabilities;
+ *                   LAMP_STAGE_STATS).  seed is unused.
+ * Errors and ownership as for lamp_attention_fwd.
+ */
+int lamp_decode_fwd(const float *q, const float *k, const float *v,
+                    int B, int H, int Nq, int S, int D, int causal, int mu, float tau,
+                    float *out, float *probs, uint32_t *recompute_mask, lamp_stats *stats,
+                    const lamp_params *p);
+
+/* Device scratch lamp_decode_fwd needs when none of scores_mix, scores_ref,
+ * row_count, row_kl, row_kl_lowp is given (an upper bound); 0 on invalid
+ * sizes. */
+size_t lamp_decode_workspace_bytes(int B, int H, int Nq, int S, int D);
+
+/*
  * lamp_diag_exp -- diagnostic: evaluates the library's two device exponentials
  * (the double one used for the selection criterion and the KL sums, the
  * FP32-accurate one used for probabilities) on n device doubles x, writing

@@ -53,6 +53,9 @@ WORKLOADS = {
         Workload("relaxed_s4096", 4, 25, 4096, 64, True, 4, 8.0, 1.0, (4,), "relaxed",
                  (1e-1, 1e-2, 1e-3, 1e-4)),
         Workload("long_context_s16384", 1, 32, 16384, 128, True, 1, 16.0, 0.5, (4,), "relaxed"),
+        # decode shapes: the last Nq rows of Q (Nq <= 16) against a 16K-key
+        # cache, GPT-2-XL heads (8 x 25, D = 64, 2 outlier channels x8)
+        Workload("decode_s16384", 8, 25, 16384, 64, True, 2, 8.0, 1.0, (4,), "relaxed"),
     ]
 }
 

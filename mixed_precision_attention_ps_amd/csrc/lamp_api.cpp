@@ -208,6 +208,158 @@ struct StageTimer {
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// Decode shapes (relaxed rule).
+// ---------------------------------------------------------------------------
+namespace {
+
+struct DecodeLayout {
+    size_t ylo = SIZE_MAX, yref = SIZE_MAX, bmax = SIZE_MAX, part = SIZE_MAX, acc = SIZE_MAX,
+           row_lse = SIZE_MAX, row_count = SIZE_MAX, row_kl = SIZE_MAX, row_kl_lowp = SIZE_MAX,
+           dstats = SIZE_MAX;
+    size_t total = 0;
+    size_t take(size_t bytes)
+    {
+        size_t off = total;
+        total += align_up(bytes);
+        return off;
+    }
+};
+
+constexpr int kDecodeMaxQ = 16;
+constexpr int kDecodeChunk = 256;
+
+int check_decode(int B, int H, int Nq, int S, int D)
+{
+    if (B < 1 || H < 1 || Nq < 1 || S < 1 || D < 1)
+        return set_error(LAMP_ERR_INVALID_ARG, "B, H, Nq, S and D must be >= 1");
+    if (Nq > kDecodeMaxQ)
+        return set_error(LAMP_ERR_UNSUPPORTED, "Nq must be at most 16");
+    if (Nq > S)
+        return set_error(LAMP_ERR_INVALID_ARG, "Nq must not exceed S");
+    if (D % 4 != 0 || D > 256)
+        return set_error(LAMP_ERR_UNSUPPORTED, "D must be a multiple of 4 and at most 256");
+    const uint64_t BH = (uint64_t)B * (uint64_t)H;
+    if (BH * (uint64_t)Nq > 65535 || (uint64_t)S > (1ull << 30) ||
+        BH * (uint64_t)Nq * (uint64_t)S > (1ull << 40))
+        return set_error(LAMP_ERR_UNSUPPORTED, "problem size overflows the launch geometry");
+    return LAMP_OK;
+}
+
+DecodeLayout decode_plan(uint64_t BH, int Nq, int S, int D, bool need_ylo, bool need_yref,
+                         bool need_count, bool need_kl, bool need_kl_lowp)
+{
+    DecodeLayout L;
+    const uint64_t rows = BH * (uint64_t)Nq;
+    const uint64_t chunks = (S + kDecodeChunk - 1) / kDecodeChunk;
+    L.dstats = L.take(sizeof(lamp::DevStats));
+    if (need_ylo)
+        L.ylo = L.take(4 * rows * (uint64_t)S);
+    if (need_yref)
+        L.yref = L.take(4 * rows * (uint64_t)S);
+    L.bmax = L.take(4 * rows * (uint64_t)((S + 63) / 64));
+    L.part = L.take(sizeof(lamp::DecPartial) * BH * chunks * (uint64_t)Nq);
+    L.acc = L.take(8 * BH * chunks * (uint64_t)Nq * (uint64_t)D);
+    L.row_lse = L.take(8 * rows);
+    if (need_count)
+        L.row_count = L.take(4 * rows);
+    if (need_kl)
+        L.row_kl = L.take(8 * rows);
+    if (need_kl_lowp)
+        L.row_kl_lowp = L.take(8 * rows);
+    return L;
+}
+
+int run_decode(const float *q, const float *k, const float *v, int B, int H, int Nq, int S, int D,
+               int causal, int mu, float tau, float *out, float *probs, uint32_t *mask,
+               lamp_stats *stats, const lamp_params *pp)
+{
+    g_last_error.clear();
+    int rc = check_args(q, k, v, causal, mu, tau, LAMP_RELAXED, out);
+    if (rc != LAMP_OK)
+        return rc;
+    rc = check_decode(B, H, Nq, S, D);
+    if (rc != LAMP_OK)
+        return rc;
+    (void)hipGetLastError();
+    lamp_params none{};
+    const lamp_params &p = pp ? *pp : none;
+    hipStream_t st = (hipStream_t)p.stream;
+    const bool want_stats = stats != nullptr;
+    const uint64_t BH = (uint64_t)B * (uint64_t)H;
+    const DecodeLayout L =
+        decode_plan(BH, Nq, S, D, p.scores_mix == nullptr, p.scores_ref == nullptr,
+                    p.row_count == nullptr, p.row_kl == nullptr && want_stats,
+                    p.row_kl_lowp == nullptr && want_stats);
+    void *ws = nullptr;
+    if (p.workspace) {
+        if (p.workspace_bytes < L.total)
+            return set_error(LAMP_ERR_INVALID_ARG,
+                             "workspace too small: need " + std::to_string(L.total) + " bytes");
+        if (((uintptr_t)p.workspace & (kAlign - 1)) != 0)
+            return set_error(LAMP_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+        ws = p.workspace;
+    } else {
+        rc = pool_get(L.total, &ws);
+        if (rc != LAMP_OK)
+            return rc;
+    }
+    auto *dstats = at<lamp::DevStats>(ws, L.dstats);
+    lamp::DecodeProblem P;
+    P.q = q;
+    P.k = k;
+    P.v = v;
+    P.BH = (int)BH;
+    P.S = S;
+    P.D = D;
+    P.nq = Nq;
+    P.causal = causal;
+    P.mu = mu;
+    P.tau = tau;
+    lamp::DecodeBuffers b;
+    b.ylo = p.scores_mix ? p.scores_mix : at<float>(ws, L.ylo);
+    b.yref = p.scores_ref ? p.scores_ref : at<float>(ws, L.yref);
+    b.bmax = at<float>(ws, L.bmax);
+    b.mask = mask;
+    b.part = at<lamp::DecPartial>(ws, L.part);
+    b.acc = at<double>(ws, L.acc);
+    b.out = out;
+    b.row_lse = at<double>(ws, L.row_lse);
+    b.row_count = p.row_count ? p.row_count : at<uint32_t>(ws, L.row_count);
+    b.row_kl = p.row_kl ? p.row_kl : at<double>(ws, L.row_kl);
+    b.row_kl_lowp = p.row_kl_lowp ? p.row_kl_lowp : at<double>(ws, L.row_kl_lowp);
+    b.probs = probs;
+    b.exact_chunks = &dstats->n_exact_tiles;
+    LAMP_HIP_TRY(lamp::launch_zero(dstats, sizeof(lamp::DevStats), st), "zero stats");
+    LAMP_HIP_TRY(lamp::launch_decode(P, b, st, p.stage_events), "decode kernels launch");
+    if (want_stats) {
+        lamp::Problem Ps{};
+        Ps.n_rows = BH * (uint64_t)Nq;
+        StageTimer tm{p.stage_events, st};
+        LAMP_HIP_TRY(tm.begin(LAMP_STAGE_STATS), "hipEventRecord");
+        LAMP_HIP_TRY(lamp::launch_stats(Ps, b.row_kl, b.row_kl_lowp, b.row_count, dstats, st),
+                     "stats launch");
+        LAMP_HIP_TRY(tm.end(LAMP_STAGE_STATS), "hipEventRecord");
+        lamp::DevStats ds;
+        LAMP_HIP_TRY(hipMemcpyAsync(&ds, dstats, sizeof(ds), hipMemcpyDeviceToHost, st),
+                     "hipMemcpyAsync stats");
+        LAMP_HIP_TRY(hipStreamSynchronize(st), "hipStreamSynchronize");
+        const uint64_t per_head = causal ? (uint64_t)Nq * (uint64_t)(S - Nq) +
+                                               (uint64_t)Nq * (uint64_t)(Nq + 1) / 2
+                                         : (uint64_t)Nq * (uint64_t)S;
+        stats->n_rows = BH * (uint64_t)Nq;
+        stats->n_valid = BH * per_head;
+        stats->n_selected = ds.n_selected;
+        stats->n_exact_tiles = ds.n_exact_tiles;
+        stats->kl_sum = ds.kl_sum;
+        stats->kl_max = ds.kl_max;
+        stats->kl_lowp_sum = ds.kl_lowp_sum;
+    }
+    return LAMP_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char *lamp_strerror(int code)
@@ -453,6 +605,27 @@ int lamp_attention_fwd(const float *q, const float *k, const float *v, int B, in
 {
     return lamp_attention_fwd_ex(q, k, v, B, H, S, D, causal, mu, tau, mode, out, probs,
                                  recompute_mask, stats, nullptr);
+}
+
+size_t lamp_decode_workspace_bytes(int B, int H, int Nq, int S, int D)
+{
+    if (check_decode(B, H, Nq, S, D) != LAMP_OK)
+        return 0;
+    return decode_plan((uint64_t)B * (uint64_t)H, Nq, S, D, true, true, true, true, true).total;
+}
+
+int lamp_decode_fwd(const float *q, const float *k, const float *v, int B, int H, int Nq, int S,
+                    int D, int causal, int mu, float tau, float *out, float *probs,
+                    uint32_t *recompute_mask, lamp_stats *stats, const lamp_params *p)
+{
+    try {
+        return run_decode(q, k, v, B, H, Nq, S, D, causal, mu, tau, out, probs, recompute_mask,
+                          stats, p);
+    } catch (const std::bad_alloc &) {
+        return set_error(LAMP_ERR_NO_MEMORY, "host allocation failed");
+    } catch (...) {
+        return set_error(LAMP_ERR_HIP, "unexpected exception");
+    }
 }
 
 int lamp_ps_scores(const float *q, const float *k, int B, int H, int S, int D, int causal, int mu,

@@ -117,6 +117,44 @@ hipError_t launch_relaxed(const Problem &p, const uint8_t *unsafe, float *out, u
 hipError_t launch_normalise(const Problem &p, const float *ymix, const float *row_m,
                             const double *row_l, float *probs, hipStream_t st);
 
+// Decode shapes (relaxed rule): nq query rows per head against S keys.
+struct DecodeProblem {
+    const float *q, *k, *v;   // q [BH, nq, D]; k, v [BH, S, D]
+    int BH, S, D, nq, causal, mu;
+    float tau;
+};
+
+// Softmax partial sums of one (head, 256-key chunk, query): maxima of y^mix,
+// y^ref and y^lo over the chunk's valid keys (-inf when it has none), and the
+// sums against them: l_mix = sum exp(y^mix - m_mix), l_ref = sum exp(y^ref -
+// m_ref), a = sum exp(y^ref - m_ref)(y^ref - y^mix), l_lo = sum exp(y^lo -
+// m_lo), b = sum exp(y^ref - m_ref)(y^ref - y^lo); cnt = selected keys.
+struct DecPartial {
+    float m_mix, m_ref, m_lo;
+    uint32_t cnt;
+    double l_mix, l_ref, a, l_lo, b;
+};
+
+struct DecodeBuffers {
+    float *ylo, *yref;          // [BH, nq, S]; ylo ends as y^mix
+    float *bmax;                // [BH, nq, ceil(S/64)]
+    uint32_t *mask;             // [BH, nq, ceil(S/32)] or null
+    DecPartial *part;           // [BH, ceil(S/256), nq]
+    double *acc;                // [BH, ceil(S/256), nq, D]
+    float *out;                 // [BH, nq, D]
+    double *row_lse;            // [BH, nq]
+    double *row_kl, *row_kl_lowp;   // [BH, nq] or null
+    uint32_t *row_count;        // [BH, nq] or null
+    float *probs;               // [BH, nq, S] or null
+    unsigned long long *exact_chunks;
+};
+
+// The four decode kernels in order; stage events (2 per stage, as in the
+// main entry point) are recorded around the score pass, the selection /
+// softmax pass and the combine (+ probabilities) pass when given.
+hipError_t launch_decode(const DecodeProblem &p, const DecodeBuffers &b, hipStream_t st,
+                         void **stage_events);
+
 // Device-side summary.
 struct DevStats {
     unsigned long long n_selected;

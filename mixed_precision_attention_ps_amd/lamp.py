@@ -75,6 +75,11 @@ def library():
     lib.lamp_version.argtypes = []
     lib.lamp_diag_exp.restype = I
     lib.lamp_diag_exp.argtypes = [P, P, P, I, P]
+    lib.lamp_decode_fwd.restype = I
+    lib.lamp_decode_fwd.argtypes = [P, P, P, I, I, I, I, I, I, I, F, P, P, P,
+                                    ctypes.POINTER(LampStats), ctypes.POINTER(LampParams)]
+    lib.lamp_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.lamp_decode_workspace_bytes.argtypes = [I, I, I, I, I]
     _lib = lib
     return lib
 
@@ -163,6 +168,47 @@ def lamp_attention_fwd(q, k, v, *, causal: bool, mu: int, tau: float, mode="stri
     _check(library().lamp_attention_fwd_ex(
         _f32(q, "q"), _f32(k, "k"), _f32(v, "v"), B, H, S, D, int(causal), int(mu),
         ctypes.c_float(tau), int(m), _f32(out, "out"),
+        None if probs is None else _f32(probs, "probs"), mask_ptr,
+        ctypes.byref(st) if st is not None else None, ctypes.byref(p)))
+    return out, (st.as_dict() if st is not None else None)
+
+
+def lamp_decode_fwd(q, k, v, *, causal: bool, mu: int, tau: float, out=None, probs=None,
+                    recompute_mask=None, want_stats: bool = True, row_kl=None, row_kl_lowp=None,
+                    row_count=None, scores_mix=None, scores_ref=None, workspace=None,
+                    stage_events=None):
+    """Relaxed LAMP at decode shapes through lamp_decode_fwd.
+
+    q: float32 [B, H, Nq, D]; k, v: float32 [B, H, S, D] device tensors (the
+    queries are the last Nq positions of the sequence).  Optional outputs are
+    written in place when given.  Returns (out, stats_dict_or_None).
+    """
+    B, H, Nq, D = q.shape
+    S = k.shape[2]
+    if tuple(k.shape) != (B, H, S, D) or tuple(v.shape) != (B, H, S, D):
+        raise ValueError("k and v must be [B, H, S, D] with q's B, H, D")
+    if out is None:
+        out = torch.empty_like(q)
+    p = LampParams()
+    p.stream = torch.cuda.current_stream(q.device).cuda_stream
+    if workspace is not None:
+        p.workspace = workspace.data_ptr()
+        p.workspace_bytes = workspace.numel() * workspace.element_size()
+    for name, t in (("row_kl", row_kl), ("row_kl_lowp", row_kl_lowp), ("row_count", row_count),
+                    ("scores_mix", scores_mix), ("scores_ref", scores_ref)):
+        if t is not None:
+            setattr(p, name, _ptr(t).value)
+    if stage_events is not None:
+        p.stage_events = stage_events.address
+    st = LampStats() if want_stats else None
+    mask_ptr = None
+    if recompute_mask is not None:
+        if recompute_mask.dtype not in (torch.int32, torch.uint32):
+            raise TypeError("recompute_mask must be a 32-bit integer tensor")
+        mask_ptr = _ptr(recompute_mask)
+    _check(library().lamp_decode_fwd(
+        _f32(q, "q"), _f32(k, "k"), _f32(v, "v"), B, H, Nq, S, D, int(causal), int(mu),
+        ctypes.c_float(tau), _f32(out, "out"),
         None if probs is None else _f32(probs, "probs"), mask_ptr,
         ctypes.byref(st) if st is not None else None, ctypes.byref(p)))
     return out, (st.as_dict() if st is not None else None)

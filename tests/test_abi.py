@@ -32,7 +32,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ("lamp_attention_fwd", "lamp_attention_fwd_ex", "lamp_workspace_bytes",
-                 "lamp_ps_scores", "lamp_strerror", "lamp_last_error", "lamp_version"):
+                 "lamp_ps_scores", "lamp_decode_fwd", "lamp_decode_workspace_bytes",
+                 "lamp_strerror", "lamp_last_error", "lamp_version"):
         assert want in names
 
 
@@ -96,6 +97,31 @@ def test_workspace_bytes(lib):
     assert strict_noprobs >= strict + 4 * 8 * 25 * 1024 * 1024
     # relaxed keeps only per-row state
     assert relaxed < 64 * 4 * 25 * 4096
+
+
+def dcall(lib, q=A, k=A, v=A, B=1, H=1, Nq=1, S=8, D=64, causal=1, mu=4, tau=0.1, out=A):
+    return lib.lamp_decode_fwd(q, k, v, B, H, Nq, S, D, causal, mu, ctypes.c_float(tau), out,
+                               None, None, None, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(k=None), -1), (dict(out=None), -1), (dict(v=A + 4), -1),
+    (dict(Nq=0), -1), (dict(S=0), -1), (dict(Nq=9, S=8), -1), (dict(Nq=17, S=64), -2),
+    (dict(D=6), -2), (dict(D=260), -2), (dict(mu=0), -1), (dict(tau=float("nan")), -1),
+    (dict(causal=3), -1), (dict(B=300, H=300), -2),
+])
+def test_decode_arguments_rejected_before_any_device_call(lib, kw, code):
+    rc = dcall(lib, **kw)
+    assert rc == code
+    assert lib.lamp_last_error()
+
+
+def test_decode_workspace_bytes(lib):
+    assert lib.lamp_decode_workspace_bytes(1, 1, 0, 8, 64) == 0
+    assert lib.lamp_decode_workspace_bytes(1, 1, 17, 64, 64) == 0
+    ws = lib.lamp_decode_workspace_bytes(8, 25, 4, 16384, 64)
+    # y^lo and y^ref per score, the P.V partials (one per 256-key chunk)
+    assert ws >= 8 * 8 * 25 * 4 * 16384 + 8 * 8 * 25 * 64 * 4 * 64
 
 
 def test_version_and_strerror(lib):
