@@ -24,6 +24,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -38,7 +40,7 @@ ALU_PEAK = 256 * 4 * 32 * 2.4e9
 HBM_PEAK = 8.0e12
 
 KERNEL_SOURCES = ["lamp_device.h", "lamp_exp.h", "lamp_internal.h", "scores.hip", "select.hip",
-                  "rows.hip", "finish.hip", "relaxed.hip"]
+                  "rows.hip", "finish.hip", "relaxed.hip", "decode.hip"]
 
 
 def log(*a):
@@ -85,6 +87,113 @@ def cpu_baseline(Q, K, V, w, mode_id, mu, tau, heads_n, seed):
                       f"{n} valid scores in {dt:.2f} s wall, {threads} OpenMP threads"}
 
 
+def decode_cpu_baseline(Q, K, V, w, nq, mu, tau, heads_n):
+    import numpy as np
+    import oracle
+    oracle.build(force=False)
+    BH = w.B * w.H
+    heads = sorted(set(int(x) for x in np.linspace(0, BH - 1, heads_n)))
+    threads = oracle.max_threads()
+    S = w.S
+    t0 = time.perf_counter()
+    oracle.lamp_heads(Q, K, V, causal=w.causal, mu=mu, tau=tau, mode=oracle.RELAXED, heads=heads,
+                      rows=(S - nq, S), want=("out", "kl", "count", "mask", "probs"))
+    dt = time.perf_counter() - t0
+    per_head = sum((S - nq + t + 1) if w.causal else S for t in range(nq))
+    n = per_head * len(heads)
+    return {"value": n / dt, "unit": "scores/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(heads)} of {BH} heads, their {nq} decode rows, of {w.name}; "
+                      f"{n} valid scores in {dt:.2f} s wall, {threads} OpenMP threads"}
+
+
+def bench_decode(args, w):
+    """Relaxed LAMP at decode shapes (lamp_decode_fwd): Nq queries per head
+    against the workload's key cache.  HBM-bound at small Nq: the dominant
+    kernel is reported against the HBM peak, with algorithmic bytes = the
+    K (score pass) or V (softmax pass) cache read once plus the score
+    buffers that pass moves."""
+    import torch
+    from mixed_precision_attention_ps_amd import lamp
+    from mixed_precision_attention_ps_amd.configs import tau_for
+    nq = args.nq
+    tau = args.tau if args.tau is not None else tau_for(w.name, "relaxed", args.mu, args.rate)
+    dev = torch.device("cuda:0")
+    log(f"[bench] {w.name} decode nq={nq} mu={args.mu} tau={tau}")
+    Q, K, V, _ = w.qkv()
+    B, H, S, D = w.B, w.H, w.S, w.D
+    q = torch.from_numpy(np.ascontiguousarray(Q[:, :, S - nq:, :])).to(dev)
+    k, v = torch.from_numpy(K).to(dev), torch.from_numpy(V).to(dev)
+    out = torch.empty_like(q)
+    probs = None if args.no_probs else torch.empty((B, H, nq, S), device=dev)
+    mask = torch.empty((B, H, nq, (S + 31) // 32), dtype=torch.int32, device=dev)
+    row_kl = torch.empty((B, H, nq), dtype=torch.float64, device=dev)
+
+    def step(events=None):
+        lamp.lamp_decode_fwd(q, k, v, causal=w.causal, mu=args.mu, tau=tau, out=out, probs=probs,
+                             recompute_mask=mask, row_kl=row_kl, want_stats=False,
+                             stage_events=events)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [lamp.HipEvents(2 * lamp.LAMP_N_STAGES) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s_ in range(args.steps):
+        step(ev[s_])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stages = {}
+    for name in ("scores", "select", "finish"):
+        si = lamp.STAGES.index(name)
+        stages[name] = sum(e.elapsed_ms(2 * si, 2 * si + 1) for e in ev) / args.steps
+    for e in ev:
+        e.close()
+    _, st = lamp.lamp_decode_fwd(q, k, v, causal=w.causal, mu=args.mu, tau=tau, out=out,
+                                 probs=probs, recompute_mask=mask, want_stats=True)
+    n_valid = st["n_valid"]
+    rate = st["n_selected"] / n_valid
+    value = n_valid / (wall / args.steps)
+    BH = B * H
+    cache = BH * S * D * 4                       # K or V, read once
+    chunks = (S + 255) // 256
+    score_bytes = {
+        # K; the queries; y^lo and y^ref written; block maxima
+        "scores": cache + BH * nq * D * 4 + 8 * n_valid + 4 * BH * nq * ((S + 63) // 64),
+        # V; y^lo and y^ref read; y^mix of the selected keys and the mask
+        # written; the chunk partials
+        "select": cache + 8 * n_valid + 4 * rate * n_valid + n_valid / 8
+                  + BH * chunks * nq * (48 + 8 * D),
+    }
+    kstage = max(("scores", "select"), key=lambda n: stages[n])
+    kname = {"scores": "decode_scores_kernel", "select": "decode_softmax_kernel"}[kstage]
+    achieved = score_bytes[kstage] / (stages[kstage] * 1e-3)
+    traffic = load_traffic(kname, f"{w.name}_nq{nq}")
+    rec = {
+        "metric": "LAMP decode scores/sec (relaxed, mu=4) + % HBM roofline", "value": value,
+        "unit": "scores/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": 1e3 * wall / args.steps, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "H": H, "S": S, "D": D, "Nq": nq,
+                   "causal": w.causal, "mu": args.mu, "mode": "relaxed", "tau": tau, "rate": rate,
+                   "probs": probs is not None, "mask": True, "row_kl": True,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "kernel": kname, "achieved": achieved / 1e9,
+                     "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": achieved / HBM_PEAK,
+                     "traffic": traffic, "kernel_ms": stages[kstage],
+                     "bytes_per_launch": score_bytes[kstage]},
+        "path_alu_frac": (9 * D + 40) * value / ALU_PEAK,
+        "stages_ms": stages,
+        "kl_mean": st["kl_sum"] / st["n_rows"],
+        "kl_lowp_mean": st["kl_lowp_sum"] / st["n_rows"],
+        "exact_chunks": st["n_exact_tiles"],
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample")
+        rec["cpu_baseline"] = decode_cpu_baseline(Q, K, V, w, nq, args.mu, tau, 8)
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -100,6 +209,7 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=24)
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="run a plain copy of this many MiB first (counter calibration)")
+    ap.add_argument("--nq", type=int, default=1, help="decode workloads: queries per head")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -116,6 +226,8 @@ def main():
     from mixed_precision_attention_ps_amd.configs import WORKLOADS, tau_for
 
     w = WORKLOADS[args.workload]
+    if w.name.startswith("decode"):
+        return bench_decode(args, w)
     mode_id = lamp.MODES[args.mode]
     tau_mode = "strict" if args.mode == "random" else args.mode
     tau = args.tau if args.tau is not None else tau_for(w.name, tau_mode, args.mu, args.rate)

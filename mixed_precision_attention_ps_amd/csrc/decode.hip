@@ -18,14 +18,14 @@
 //      K).  The FP32 fast path is taken optimistically; a chunk that meets an
 //      operand outside {0} U [2^-40, 2^40] (or any mu > 10) is redone on the
 //      exact double path.
-//   2. decode_softmax_kernel, one work-group per (head, 256-key chunk): for
-//      each query, the running maximum m_t of the relaxed rule (the prefix
-//      maximum of the block maxima up to the key's 64-key block), the rule
-//      2 exp(y^lo - m_t) |y^lo| > tau, the mask words, y^mix, the chunk's
+//   2. decode_softmax_kernel, one wave per (head, 64-key block), without
+//      barriers: for each query, the running maximum m_t of the relaxed rule
+//      (the prefix maximum of the block maxima up to the key's block), the rule
+//      2 exp(y^lo - m_t) |y^lo| > tau, the mask words, y^mix, the block's
 //      softmax partial sums (of y^mix, y^ref and y^lo, each against the
-//      chunk's own maximum) and its P.V partial, with each V row read once for
+//      block's own maximum) and its P.V partial, with each V row read once for
 //      all queries.
-//   3. decode_combine_kernel, one wave per (head, query): the chunk partials
+//   3. decode_combine_kernel, one work-group per (head, query): the block partials
 //      rescaled to the global maxima: out, the row's log-sum-exp, the row KL
 //      (FP32 reference vs LAMP, and vs all-low-precision) and the count.
 //   4. decode_probs_kernel (only when probabilities are asked for).
@@ -37,15 +37,16 @@ constexpr int kDecChunk = 256;   // keys per work-group (one per thread)
 
 struct DecodeArgs {
     const float *q, *k, *v;   // q [BH, nq, D]; k, v [BH, S, D]
-    int S, D, nq, causal, n_chunks, n_blk;
+    int S, D, nq, causal, n_chunks, n_blk, BH;
     double tau;
     PsConst pc;
     float *ylo, *yref;        // [BH, nq, S]
     float *bmax;              // [BH, nq, n_blk]: max of valid y^lo per 64-key block
     uint32_t *mask;           // [BH, nq, W] or null
     int W;
-    DecPartial *part;         // [BH, n_chunks, nq]
-    double *acc;              // [BH, n_chunks, nq, D]
+    uint8_t *unsafe;          // [BH, n_chunks]: chunk left to the exact kernel
+    DecPartial *part;         // [BH, n_blk, nq]
+    float *acc;               // [BH, n_blk, nq, D]
     unsigned long long *exact_chunks;
 };
 
@@ -64,75 +65,181 @@ __device__ __forceinline__ bool dec_safe(float x)
 
 // ---------------------------------------------------------------------------
 // 1. Scores.
+//
+// Fast kernel (mu <= 10): the chunk's K rows are staged through LDS in
+// 32-wide head-dimension slices, loaded with coalesced 16-byte loads (a key's
+// 128-byte slice segment by 8 neighbouring lanes) and stored transposed
+// ([d][key], padded), so that thread = key reads its values conflict-free;
+// the next slice is loaded while the current one is used.  Every loaded
+// value and every query is checked against the fast path's operand range; a
+// chunk that fails is flagged and left to the exact kernel, which strides
+// over the flagged chunks (all chunks when mu > 10) and forms PS(mu) in
+// double from each key's row.
 // ---------------------------------------------------------------------------
+// head-dimension entries of K per LDS pass: 32 (a full 128-byte line per key
+// and load) for few queries, where the pass is bound by the cache stream; 16
+// (half the LDS, more work-groups per CU) for many, where it is bound by ALU
+template <int NQ>
+constexpr int dec_slice() { return NQ <= 4 ? 32 : 16; }
+
+template <int NQ>
+__device__ __forceinline__ void dec_store_scores(const DecodeArgs &a, int bh, int chunk,
+                                                 const float (&lo)[NQ], const float (&ref)[NQ])
+{
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int j = chunk * kDecChunk + tid;
+    const int blk = (chunk * kDecChunk) / 64 + (tid >> 6);
+#pragma unroll
+    for (int t = 0; t < NQ; ++t) {
+        if (t >= a.nq)
+            break;
+        const bool valid = j <= dec_last_key(a, t);
+        const size_t row = (size_t)bh * a.nq + t;
+        if (valid) {
+            a.ylo[row * a.S + j] = lo[t];
+            a.yref[row * a.S + j] = ref[t] * a.pc.s;
+        }
+        const float bm = wave_max(valid ? lo[t] : -INFINITY);
+        if (lane == 0 && blk < a.n_blk)
+            a.bmax[row * a.n_blk + blk] = bm;
+    }
+}
+
+// The queries and the queries times 2^(mu-23) into LDS (s_q[t * D/4 + d4],
+// s_qs likewise), with the operand-range check of every value.
+__device__ __forceinline__ void dec_stage_queries(const DecodeArgs &a, int bh, float4 *s_q,
+                                                  float4 *s_qs, bool &safe)
+{
+    const int D4 = a.D / 4;
+    const float4 *qb = reinterpret_cast<const float4 *>(a.q + (size_t)bh * a.nq * a.D);
+    for (int e = threadIdx.x; e < a.nq * D4; e += kThreads) {
+        const float4 x = qb[e];
+        s_q[e] = x;
+        s_qs[e] = make_float4(x.x * a.pc.qscale, x.y * a.pc.qscale, x.z * a.pc.qscale,
+                              x.w * a.pc.qscale);
+        safe = safe && dec_safe(x.x) && dec_safe(x.y) && dec_safe(x.z) && dec_safe(x.w);
+    }
+}
+
+// Dynamic LDS of the score kernels: the two query arrays, nq * D / 4 float4
+// each.
+extern __shared__ float4 dec_dyn_lds[];
+
 template <int NQ>
 __global__ __launch_bounds__(kThreads) void decode_scores_kernel(DecodeArgs a)
 {
-    __shared__ float4 s_q[NQ][64];    // the queries (D <= 256)
-    __shared__ float4 s_qs[NQ][64];   // the queries times 2^(mu-23)
+    constexpr int kDecSlice = dec_slice<NQ>();
+    __shared__ float s_k[kDecSlice][kDecChunk + 1];   // K slice, [d][key]
     const int chunk = blockIdx.x, bh = blockIdx.y;
     const int tid = threadIdx.x;
-    const int D = a.D, D4 = D / 4, nq = a.nq;
+    const int D = a.D, S = a.S, D4 = D / 4;
+    float4 *s_q = dec_dyn_lds, *s_qs = dec_dyn_lds + a.nq * D4;
     const PsConst pc = a.pc;
     bool safe = true;
-    for (int e = tid; e < nq * D4; e += kThreads) {
-        const int t = e / D4, d4 = e % D4;
-        const float4 x = reinterpret_cast<const float4 *>(a.q + ((size_t)bh * nq + t) * D)[d4];
-        s_q[t][d4] = x;
-        s_qs[t][d4] = make_float4(x.x * pc.qscale, x.y * pc.qscale, x.z * pc.qscale,
-                                  x.w * pc.qscale);
-        safe = safe && dec_safe(x.x) && dec_safe(x.y) && dec_safe(x.z) && dec_safe(x.w);
-    }
-    __syncthreads();
+    dec_stage_queries(a, bh, s_q, s_qs, safe);
 
-    const int j = chunk * kDecChunk + tid;
-    const int jr = j < a.S ? j : a.S - 1;   // rows past S re-read the last row
-    const float4 *k4 = reinterpret_cast<const float4 *>(a.k + ((size_t)bh * a.S + jr) * D);
+    const int key0 = chunk * kDecChunk;
+    constexpr int kV4 = kDecSlice * kDecChunk / 4 / kThreads;   // float4 per thread per slice
+    auto load_slice = [&](int d0, float4 (&r)[kV4]) {
+#pragma unroll
+        for (int u = 0; u < kV4; ++u) {
+            const int f = tid + kThreads * u;
+            const int kk = f / (kDecSlice / 4), d = d0 + 4 * (f % (kDecSlice / 4));
+            const int key = key0 + kk;
+            r[u] = (key < S && d < D)
+                       ? *reinterpret_cast<const float4 *>(a.k + ((size_t)bh * S + key) * D + d)
+                       : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    };
+    float4 kr[kV4];
+    load_slice(0, kr);
     float lo[NQ], ref[NQ];
 #pragma unroll
     for (int t = 0; t < NQ; ++t) {
         lo[t] = 0.0f;
         ref[t] = 0.0f;
     }
-    const bool fast = pc.mu <= 10;
-    if (fast) {
-        // FP32 fast path, 64 head-dimension entries of the key row at a time
-        for (int d0 = 0; d0 < D4; d0 += 16) {
-            float4 kr[16];
+    for (int d0 = 0; d0 < D; d0 += kDecSlice) {
+        __syncthreads();
 #pragma unroll
-            for (int u = 0; u < 16; ++u)
-                kr[u] = d0 + u < D4 ? k4[d0 + u] : make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int u = 0; u < kV4; ++u) {
+            const int f = tid + kThreads * u;
+            const int kk = f / (kDecSlice / 4), dd = 4 * (f % (kDecSlice / 4));
+            s_k[dd][kk] = kr[u].x;
+            s_k[dd + 1][kk] = kr[u].y;
+            s_k[dd + 2][kk] = kr[u].z;
+            s_k[dd + 3][kk] = kr[u].w;
+            safe = safe && dec_safe(kr[u].x) && dec_safe(kr[u].y) && dec_safe(kr[u].z) &&
+                   dec_safe(kr[u].w);
+        }
+        __syncthreads();
+        if (d0 + kDecSlice < D)
+            load_slice(d0 + kDecSlice, kr);
+        const int dn = min(kDecSlice, D - d0);   // a multiple of 4
+        for (int dd = 0; dd < dn; dd += 4) {
+            const float ka[4] = {s_k[dd][tid], s_k[dd + 1][tid], s_k[dd + 2][tid],
+                                 s_k[dd + 3][tid]};
 #pragma unroll
-            for (int u = 0; u < 16; ++u)
-                safe = safe && dec_safe(kr[u].x) && dec_safe(kr[u].y) && dec_safe(kr[u].z) &&
-                       dec_safe(kr[u].w);
+            for (int t = 0; t < NQ; ++t) {
+                if (t < a.nq) {
+                    const int qi = t * D4 + (d0 + dd) / 4;
+                    const float4 qv = s_q[qi], sv = s_qs[qi];
+                    const float qa[4] = {qv.x, qv.y, qv.z, qv.w};
+                    const float sa[4] = {sv.x, sv.y, sv.z, sv.w};
 #pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                if (d0 + u >= D4)
-                    break;
-                const float ka[4] = {kr[u].x, kr[u].y, kr[u].z, kr[u].w};
-#pragma unroll
-                for (int t = 0; t < NQ; ++t) {
-                    if (t < nq) {
-                        const float4 qv = s_q[t][d0 + u], sv = s_qs[t][d0 + u];
-                        const float qa[4] = {qv.x, qv.y, qv.z, qv.w};
-                        const float sa[4] = {sv.x, sv.y, sv.z, sv.w};
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            ps_mac_fast(qa[e], sa[e], ka[e], lo[t], ref[t], pc.sh, pc.half_m1,
-                                        pc.keep);
-                    }
+                    for (int e = 0; e < 4; ++e)
+                        ps_mac_fast(qa[e], sa[e], ka[e], lo[t], ref[t], pc.sh, pc.half_m1,
+                                    pc.keep);
                 }
             }
         }
     }
-    // The exact path (mu > 10, or an operand outside the fast path's range
-    // anywhere in this chunk or the queries): PS(mu) in double.
-    const bool exact = !__syncthreads_and((fast && safe) ? 1 : 0);
-    if (exact) {
+    const bool ok = __syncthreads_and(safe ? 1 : 0);
+    if (tid == 0)
+        a.unsafe[(size_t)bh * a.n_chunks + chunk] = ok ? 0 : 1;
+    if (!ok)
+        return;   // the exact kernel takes this chunk
+#pragma unroll
+    for (int t = 0; t < NQ; ++t)
+        lo[t] = lo[t] * pc.out_scale;
+    dec_store_scores<NQ>(a, bh, chunk, lo, ref);
+}
+
+// Exact path: PS(mu) in double (mu > 10, or a chunk the fast kernel flagged);
+// plain FP32 at mu = 23.  A bounded grid strides over the chunks; each
+// work-group first checks its chunks' flags in parallel and exits when none
+// is its.
+template <int NQ>
+__global__ __launch_bounds__(kThreads) void decode_scores_exact_kernel(DecodeArgs a)
+{
+    const long long total = (long long)a.BH * a.n_chunks;
+    const bool all = a.pc.mu > 10;
+    if (!all) {
+        bool need = false;
+        for (long long g = blockIdx.x + (long long)threadIdx.x * gridDim.x; g < total;
+             g += (long long)blockDim.x * gridDim.x)
+            need |= a.unsafe[g] != 0;
+        if (!__syncthreads_or(need ? 1 : 0))
+            return;
+    }
+    const int tid = threadIdx.x, D = a.D, D4 = D / 4;
+    float4 *s_q = dec_dyn_lds, *s_qs = dec_dyn_lds + a.nq * D4;
+    const PsConst pc = a.pc;
+    for (long long g = blockIdx.x; g < total; g += gridDim.x) {
+        if (!all && !a.unsafe[g])
+            continue;   // uniform over the work-group
+        const int bh = (int)(g / a.n_chunks), chunk = (int)(g % a.n_chunks);
+        bool unused = true;
+        __syncthreads();   // the previous chunk's readers of s_q are done
+        dec_stage_queries(a, bh, s_q, s_qs, unused);
+        __syncthreads();
         if (tid == 0 && a.exact_chunks)
             atomicAdd(a.exact_chunks, 1ull);
+        const int j = chunk * kDecChunk + tid;
+        const int jr = j < a.S ? j : a.S - 1;   // rows past S re-read the last row
+        const float4 *k4 = reinterpret_cast<const float4 *>(a.k + ((size_t)bh * a.S + jr) * D);
         double lod[NQ];
+        float lo[NQ], ref[NQ];
 #pragma unroll
         for (int t = 0; t < NQ; ++t) {
             lod[t] = 0.0;
@@ -143,8 +250,8 @@ __global__ __launch_bounds__(kThreads) void decode_scores_kernel(DecodeArgs a)
             const float ka[4] = {kv.x, kv.y, kv.z, kv.w};
 #pragma unroll
             for (int t = 0; t < NQ; ++t) {
-                if (t < nq) {
-                    const float4 qv = s_q[t][d4];
+                if (t < a.nq) {
+                    const float4 qv = s_q[t * D4 + d4];
                     const float qa[4] = {qv.x, qv.y, qv.z, qv.w};
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
@@ -161,89 +268,46 @@ __global__ __launch_bounds__(kThreads) void decode_scores_kernel(DecodeArgs a)
 #pragma unroll
         for (int t = 0; t < NQ; ++t)
             lo[t] = pc.mu < 23 ? (float)lod[t] * pc.s : ref[t] * pc.s;
-    } else {
-#pragma unroll
-        for (int t = 0; t < NQ; ++t)
-            lo[t] = lo[t] * pc.out_scale;
-    }
-
-    const int lane = tid & 63;
-    const int blk = (chunk * kDecChunk) / 64 + (tid >> 6);
-#pragma unroll
-    for (int t = 0; t < NQ; ++t) {
-        if (t >= nq)
-            break;
-        const bool valid = j <= dec_last_key(a, t);
-        const float yr = ref[t] * pc.s;
-        const size_t row = (size_t)bh * nq + t;
-        if (valid) {
-            a.ylo[row * a.S + j] = lo[t];
-            a.yref[row * a.S + j] = yr;
-        }
-        const float bm = wave_max(valid ? lo[t] : -INFINITY);
-        if (lane == 0 && blk < a.n_blk)
-            a.bmax[row * a.n_blk + blk] = bm;
+        dec_store_scores<NQ>(a, bh, chunk, lo, ref);
     }
 }
 
 // ---------------------------------------------------------------------------
-// 2. Relaxed selection, chunk softmax partials and P.V partial.
+// 2. Relaxed selection, softmax partials and P.V partial per 64-key block.
+//
+// Every wave owns one 64-key block (lane = key) and works alone: no barrier.
+// For each query it forms the rule's running maximum (the prefix maximum of
+// the block maxima), the rule, the mask words and y^mix (in place over y^lo),
+// and the block's partial sums; then the block's P.V partial with lane = head
+// dimension, the block's probabilities broadcast from LDS, each V row read
+// once for all queries (FP32 over 8 keys at a time, flushed into double, the
+// block total stored in FP32: at most 5.4e-7 of sum p|v| in all).
 // ---------------------------------------------------------------------------
 template <int NQ>
 __global__ __launch_bounds__(kThreads) void decode_softmax_kernel(DecodeArgs a)
 {
-    __shared__ float s_p[NQ][kDecChunk];   // exp(y^mix - chunk max), per query
-    __shared__ float s_red[4][8];
-    __shared__ double s_redd[4][8];
-    __shared__ double s_acc[4][64];
-    __shared__ double s_exp[64];   // 2^(k/64) for exp64
+    __shared__ float s_p[4][NQ][64];   // per wave: exp(y^mix - block max), per query
+    __shared__ double s_exp[64];       // 2^(k/64) for exp64
     exp_table_fill(s_exp);
     __syncthreads();
-    const int chunk = blockIdx.x, bh = blockIdx.y;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int bh = blockIdx.y;
+    const int blk = blockIdx.x * 4 + wave;   // this wave's 64-key block
+    if (blk >= a.n_blk)
+        return;   // no barrier below
     const int nq = a.nq, S = a.S, D = a.D;
-    const int j = chunk * kDecChunk + tid;
-    const int blk0 = (chunk * kDecChunk) / 64;
-    const int myblk = blk0 + wave;
-
-    auto block_max = [&](float x) {
-        x = wave_max(x);
-        if (lane == 0)
-            s_red[wave][0] = x;
-        __syncthreads();
-        x = fmaxf(fmaxf(s_red[0][0], s_red[1][0]), fmaxf(s_red[2][0], s_red[3][0]));
-        __syncthreads();
-        return x;
-    };
-    // five double sums at once over the work-group
-    auto block_sum5 = [&](double (&x)[5]) {
-#pragma unroll
-        for (int e = 0; e < 5; ++e) {
-            x[e] = wave_sum(x[e]);
-            if (lane == 0)
-                s_redd[wave][e] = x[e];
-        }
-        __syncthreads();
-#pragma unroll
-        for (int e = 0; e < 5; ++e)
-            x[e] = (s_redd[0][e] + s_redd[1][e]) + (s_redd[2][e] + s_redd[3][e]);
-        __syncthreads();
-    };
+    const int j = blk * 64 + lane;
 
     for (int t = 0; t < nq; ++t) {
         const size_t row = (size_t)bh * nq + t;
         const int last = dec_last_key(a, t);
         const bool valid = j <= last;
         const float *bm = a.bmax + row * a.n_blk;
-        // running maximum of the relaxed rule: prefix maximum of the block
-        // maxima up to this key's block
-        float carry = -INFINITY;
-        for (int b = tid; b < blk0; b += kThreads)
-            carry = fmaxf(carry, bm[b]);
-        carry = block_max(carry);
-        float mt = carry;
-        for (int b = blk0; b <= myblk && b < a.n_blk; ++b)
+        float mt = -INFINITY;
+        for (int b = lane; b <= blk; b += 64)
             mt = fmaxf(mt, bm[b]);
+        mt = wave_max(mt);
 
         float ylo = 0.0f, yref = 0.0f;
         if (valid) {
@@ -255,113 +319,120 @@ __global__ __launch_bounds__(kThreads) void decode_softmax_kernel(DecodeArgs a)
         const float ymix = sel ? yref : ylo;
         const uint64_t b = __ballot(sel);
         if (a.mask) {
-            const int w = (chunk * kDecChunk + wave * 64) / 32 + lane;
+            const int w = blk * 2 + lane;
             if (lane < 2 && w < a.W)
                 a.mask[row * a.W + w] = lane ? (uint32_t)(b >> 32) : (uint32_t)b;
         }
         if (sel)
             a.ylo[row * S + j] = ymix;   // y^lo becomes y^mix in place
-        const float M_mix = block_max(valid ? ymix : -INFINITY);
-        const float M_ref = block_max(valid ? yref : -INFINITY);
-        const float M_lo = block_max(valid ? ylo : -INFINITY);
-        const double em = valid ? exp64((double)ymix - (double)M_mix, s_exp) : 0.0;
-        const double er = valid ? exp64((double)yref - (double)M_ref, s_exp) : 0.0;
-        const double el = valid ? exp64((double)ylo - (double)M_lo, s_exp) : 0.0;
-        s_p[t][tid] = (float)em;
-        double sums[5] = {em, er, er * ((double)yref - (double)ymix), el,
-                          er * ((double)yref - (double)ylo)};
-        block_sum5(sums);
-        if (lane == 0)
-            s_red[wave][1] = __uint_as_float((uint32_t)__popcll(b));
-        __syncthreads();
-        if (tid == 0) {
+        const float M_mix = wave_max(valid ? ymix : -INFINITY);
+        const float M_ref = wave_max(valid ? yref : -INFINITY);
+        const float M_lo = wave_max(valid ? ylo : -INFINITY);
+        const double em = valid ? exp64_nonpos((double)ymix - (double)M_mix, s_exp) : 0.0;
+        const double er = valid ? exp64_nonpos((double)yref - (double)M_ref, s_exp) : 0.0;
+        const double el = valid ? exp64_nonpos((double)ylo - (double)M_lo, s_exp) : 0.0;
+        s_p[wave][t][lane] = (float)em;
+        const double l_mix = wave_sum(em);
+        const double l_ref = wave_sum(er);
+        const double sa = wave_sum(er * ((double)yref - (double)ymix));
+        const double l_lo = wave_sum(el);
+        const double sb = wave_sum(er * ((double)yref - (double)ylo));
+        if (lane == 0) {
             DecPartial pt;
             pt.m_mix = M_mix;
             pt.m_ref = M_ref;
             pt.m_lo = M_lo;
-            pt.cnt = __float_as_uint(s_red[0][1]) + __float_as_uint(s_red[1][1]) +
-                     __float_as_uint(s_red[2][1]) + __float_as_uint(s_red[3][1]);
-            pt.l_mix = sums[0];
-            pt.l_ref = sums[1];
-            pt.a = sums[2];
-            pt.l_lo = sums[3];
-            pt.b = sums[4];
-            a.part[((size_t)bh * a.n_chunks + chunk) * nq + t] = pt;
+            pt.cnt = (uint32_t)__popcll(b);
+            pt.l_mix = l_mix;
+            pt.l_ref = l_ref;
+            pt.a = sa;
+            pt.l_lo = l_lo;
+            pt.b = sb;
+            a.part[((size_t)bh * a.n_blk + blk) * nq + t] = pt;
         }
-        __syncthreads();
     }
+    __builtin_amdgcn_wave_barrier();
 
-    // P.V partial: thread (d = lane (+64 per pass), key group = wave) sums its
-    // 64 keys in FP32 over 8 keys at a time, flushed into double.
-    const int kb = chunk * kDecChunk + wave * 64;
-    const int nk = max(0, min(64, S - kb));
-    const float *Vh = a.v + (size_t)bh * S * D;
+    // P.V partial of this block
+    const int nk = min(64, S - blk * 64);
+    const float *Vb = a.v + ((size_t)bh * S + (size_t)blk * 64) * D;
     for (int d0 = 0; d0 < D; d0 += 64) {
         const int d = d0 + lane;
         double accd[NQ];
 #pragma unroll
         for (int t = 0; t < NQ; ++t)
             accd[t] = 0.0;
-        for (int k0 = 0; k0 < nk; k0 += 8) {
-            float accf[NQ];
+        // 32 V rows in flight per lane, consumed 8 keys per FP32 partial
+        for (int k0 = 0; k0 < nk; k0 += 32) {
+            // rows past the block's keys re-read its last row (their
+            // probabilities are 0) and lanes past D re-read column D - 1
+            // (not stored), so the loads need no guard
+            float vv[32];
 #pragma unroll
-            for (int t = 0; t < NQ; ++t)
-                accf[t] = 0.0f;
-            const int k1 = min(nk, k0 + 8);
-            for (int kk = k0; kk < k1; ++kk) {
-                const float vv = d < D ? Vh[(size_t)(kb + kk) * D + d] : 0.0f;
+            for (int u = 0; u < 32; ++u)
+                vv[u] = Vb[(size_t)min(k0 + u, nk - 1) * D + min(d, D - 1)];
 #pragma unroll
-                for (int t = 0; t < NQ; ++t)
-                    if (t < nq)
-                        accf[t] = __builtin_fmaf(s_p[t][wave * 64 + kk], vv, accf[t]);
+            for (int g = 0; g < 4; ++g) {
+                const int kg = k0 + 8 * g;
+#pragma unroll
+                for (int t = 0; t < NQ; ++t) {
+                    if (t < nq) {
+                        const float4 p0 = *reinterpret_cast<const float4 *>(&s_p[wave][t][kg]);
+                        const float4 p1 =
+                            *reinterpret_cast<const float4 *>(&s_p[wave][t][kg + 4]);
+                        const float pa[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+                        float f = 0.0f;
+#pragma unroll
+                        for (int u = 0; u < 8; ++u)
+                            f = __builtin_fmaf(pa[u], vv[8 * g + u], f);
+                        accd[t] += (double)f;
+                    }
+                }
             }
-#pragma unroll
-            for (int t = 0; t < NQ; ++t)
-                accd[t] += (double)accf[t];
         }
 #pragma unroll
-        for (int t = 0; t < NQ; ++t) {
-            if (t >= nq)
-                break;
-            s_acc[wave][lane] = accd[t];
-            __syncthreads();
-            if (wave == 0 && d < D)
-                a.acc[(((size_t)bh * a.n_chunks + chunk) * nq + t) * D + d] =
-                    (s_acc[0][lane] + s_acc[1][lane]) + (s_acc[2][lane] + s_acc[3][lane]);
-            __syncthreads();
-        }
+        for (int t = 0; t < NQ; ++t)
+            if (t < nq && d < D)
+                a.acc[(((size_t)bh * a.n_blk + blk) * nq + t) * D + d] = (float)accd[t];
     }
 }
 
 // ---------------------------------------------------------------------------
-// 3. Combine the chunk partials: one wave per (head, query).
+// 3. Combine the block partials.
 // ---------------------------------------------------------------------------
 struct CombineArgs {
     const DecPartial *part;
-    const double *acc;
-    int nq, D, n_chunks, n_rows;
+    const float *acc;
+    int nq, D, n_blk, n_rows;
     float *out;
     double *row_lse;   // [BH, nq]: log-sum-exp of y^mix
     double *row_kl, *row_kl_lowp;
     uint32_t *row_count;
 };
 
+constexpr int kCombineSeg = 1024;   // block factors staged in LDS at a time
+
+// One work-group per (head, query) row.  The statistics: every thread takes
+// blocks c = tid (mod 256).  The output: thread (d = lane, part = wave) sums
+// the blocks c = part (mod 4), eight at a time (independent loads in flight).
 __global__ __launch_bounds__(kThreads) void decode_combine_kernel(CombineArgs a)
 {
     __shared__ double s_exp[64];
+    __shared__ float s_m[3][4];
+    __shared__ double s_s[5][4];
+    __shared__ uint32_t s_c[4];
+    __shared__ double s_o[4][64];
+    __shared__ float s_f[kCombineSeg];   // exp(m_mix of block - M) per block
     exp_table_fill(s_exp);
     __syncthreads();
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int r = blockIdx.x * 4 + wave;   // (bh, t) row
-    if (r >= a.n_rows)
-        return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r = blockIdx.x;   // (bh, t) row
     const int bh = r / a.nq, t = r % a.nq;
     auto P = [&](int c) -> const DecPartial & {
-        return a.part[((size_t)bh * a.n_chunks + c) * a.nq + t];
+        return a.part[((size_t)bh * a.n_blk + c) * a.nq + t];
     };
     float Mm = -INFINITY, Mr = -INFINITY, Ml = -INFINITY;
-    for (int c = lane; c < a.n_chunks; c += 64) {
+    for (int c = tid; c < a.n_blk; c += kThreads) {
         Mm = fmaxf(Mm, P(c).m_mix);
         Mr = fmaxf(Mr, P(c).m_ref);
         Ml = fmaxf(Ml, P(c).m_lo);
@@ -369,54 +440,99 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(CombineArgs a)
     Mm = wave_max(Mm);
     Mr = wave_max(Mr);
     Ml = wave_max(Ml);
-    double Lm = 0.0, Lr = 0.0, A = 0.0, Ll = 0.0, B = 0.0;
+    if (lane == 0) {
+        s_m[0][wave] = Mm;
+        s_m[1][wave] = Mr;
+        s_m[2][wave] = Ml;
+    }
+    __syncthreads();
+    Mm = fmaxf(fmaxf(s_m[0][0], s_m[0][1]), fmaxf(s_m[0][2], s_m[0][3]));
+    Mr = fmaxf(fmaxf(s_m[1][0], s_m[1][1]), fmaxf(s_m[1][2], s_m[1][3]));
+    Ml = fmaxf(fmaxf(s_m[2][0], s_m[2][1]), fmaxf(s_m[2][2], s_m[2][3]));
+    double sum[5] = {0.0, 0.0, 0.0, 0.0, 0.0};
     uint32_t cnt = 0;
-    for (int c = lane; c < a.n_chunks; c += 64) {
+    for (int c = tid; c < a.n_blk; c += kThreads) {
         const DecPartial &p = P(c);
         if (p.m_mix == -INFINITY)
-            continue;   // no valid key in this chunk
+            continue;   // no valid key in this block
         const double fm = exp64_nonpos((double)p.m_mix - (double)Mm, s_exp);
         const double fr = exp64_nonpos((double)p.m_ref - (double)Mr, s_exp);
         const double fl = exp64_nonpos((double)p.m_lo - (double)Ml, s_exp);
-        Lm += p.l_mix * fm;
-        Lr += p.l_ref * fr;
-        A += p.a * fr;
-        Ll += p.l_lo * fl;
-        B += p.b * fr;
+        sum[0] += p.l_mix * fm;
+        sum[1] += p.l_ref * fr;
+        sum[2] += p.a * fr;
+        sum[3] += p.l_lo * fl;
+        sum[4] += p.b * fr;
         cnt += p.cnt;
     }
-    Lm = wave_sum(Lm);
-    Lr = wave_sum(Lr);
-    A = wave_sum(A);
-    Ll = wave_sum(Ll);
-    B = wave_sum(B);
-    cnt = (uint32_t)wave_sum_int((int)cnt);
-    // out = sum_c exp(M_c - M) acc_c / L_mix
-    const double inv = 1.0 / Lm;
-    for (int d = lane; d < a.D; d += 64) {
-        double o = 0.0;
-        for (int c = 0; c < a.n_chunks; ++c) {
-            const DecPartial &p = P(c);
-            if (p.m_mix == -INFINITY)
-                continue;
-            const double fm = exp64_nonpos((double)p.m_mix - (double)Mm, s_exp);
-            o += fm * a.acc[(((size_t)bh * a.n_chunks + c) * a.nq + t) * a.D + d];
-        }
-        a.out[(size_t)r * a.D + d] = (float)(o * inv);
+#pragma unroll
+    for (int e = 0; e < 5; ++e) {
+        sum[e] = wave_sum(sum[e]);
+        if (lane == 0)
+            s_s[e][wave] = sum[e];
     }
-    const double lg = log(lane == 0 ? Lm : (lane == 1 ? Lr : Ll));
-    const double lse_mix = (double)Mm + lane_read(lg, 0);
-    const double lse_ref = (double)Mr + lane_read(lg, 1);
-    const double lse_lo = (double)Ml + lane_read(lg, 2);
-    if (lane == 0) {
-        if (a.row_lse)
-            a.row_lse[r] = lse_mix;
-        if (a.row_count)
-            a.row_count[r] = cnt;
-        if (a.row_kl)
-            a.row_kl[r] = A / Lr + lse_mix - lse_ref;
-        if (a.row_kl_lowp)
-            a.row_kl_lowp[r] = B / Lr + lse_lo - lse_ref;
+    cnt = (uint32_t)wave_sum_int((int)cnt);
+    if (lane == 0)
+        s_c[wave] = cnt;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 5; ++e)
+        sum[e] = (s_s[e][0] + s_s[e][1]) + (s_s[e][2] + s_s[e][3]);
+    cnt = s_c[0] + s_c[1] + s_c[2] + s_c[3];
+    const double Lm = sum[0], Lr = sum[1], A = sum[2], Ll = sum[3], B = sum[4];
+
+    // out = sum_c exp(M_c - M) acc_c / L_mix; the block factors go through
+    // LDS in segments of kCombineSeg blocks
+    const double inv = 1.0 / Lm;
+    for (int d0 = 0; d0 < a.D; d0 += 64) {
+        const int d = d0 + lane;
+        double o = 0.0;
+        for (int c0 = 0; c0 < a.n_blk; c0 += kCombineSeg) {
+            const int nc = min(kCombineSeg, a.n_blk - c0);
+            __syncthreads();   // the previous segment's readers are done
+            for (int c = tid; c < nc; c += kThreads) {
+                const float m = P(c0 + c).m_mix;
+                s_f[c] = m == -INFINITY ? 0.0f
+                                        : (float)exp64_nonpos((double)m - (double)Mm, s_exp);
+            }
+            __syncthreads();
+            if (d < a.D) {
+                const float *ac = a.acc + (((size_t)bh * a.n_blk + c0) * a.nq + t) * a.D + d;
+                const size_t stride = (size_t)a.nq * a.D;
+                for (int cb = wave * 8; cb < nc; cb += 32) {
+                    float x[8];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u)
+                        x[u] = cb + u < nc ? ac[(size_t)(cb + u) * stride] : 0.0f;
+#pragma unroll
+                    for (int u = 0; u < 8; ++u)
+                        if (cb + u < nc)
+                            o += (double)s_f[cb + u] * (double)x[u];
+                }
+            }
+        }
+        s_o[wave][lane] = o;
+        __syncthreads();
+        if (wave == 0 && d < a.D)
+            a.out[(size_t)r * a.D + d] =
+                (float)(((s_o[0][lane] + s_o[1][lane]) + (s_o[2][lane] + s_o[3][lane])) * inv);
+        __syncthreads();
+    }
+    if (wave == 0) {
+        const double lg = log(lane == 0 ? Lm : (lane == 1 ? Lr : Ll));
+        const double lse_mix = (double)Mm + lane_read(lg, 0);
+        const double lse_ref = (double)Mr + lane_read(lg, 1);
+        const double lse_lo = (double)Ml + lane_read(lg, 2);
+        if (lane == 0) {
+            if (a.row_lse)
+                a.row_lse[r] = lse_mix;
+            if (a.row_count)
+                a.row_count[r] = cnt;
+            if (a.row_kl)
+                a.row_kl[r] = A / Lr + lse_mix - lse_ref;
+            if (a.row_kl_lowp)
+                a.row_kl_lowp[r] = B / Lr + lse_lo - lse_ref;
+        }
     }
 }
 
@@ -428,13 +544,20 @@ __global__ __launch_bounds__(kThreads) void decode_probs_kernel(const float *ymi
                                                                 float *probs, int S, int nq,
                                                                 int causal)
 {
-    const int r = blockIdx.y;   // (bh, t) row
+    // work-group (x, r): keys 1024 x .. 1024 x + 1023 of row r, 4 per thread
+    const int r = blockIdx.y;
     const int t = r % nq;
     const int last = causal ? S - nq + t : S - 1;
     const double lse = row_lse[r];
-    for (int j = blockIdx.x * kThreads + threadIdx.x; j < S; j += gridDim.x * kThreads)
-        probs[(size_t)r * S + j] =
-            j <= last ? exp_f32((double)ymix[(size_t)r * S + j] - lse) : 0.0f;
+    const float *y = ymix + (size_t)r * S;
+    float *pr = probs + (size_t)r * S;
+    const int j0 = blockIdx.x * 4 * kThreads + threadIdx.x;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int j = j0 + e * kThreads;
+        if (j < S)
+            pr[j] = j <= last ? exp_f32((double)y[j] - lse) : 0.0f;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -464,25 +587,56 @@ hipError_t launch_decode(const DecodeProblem &p, const DecodeBuffers &b, hipStre
     a.part = b.part;
     a.acc = b.acc;
     a.exact_chunks = b.exact_chunks;
+    a.unsafe = b.unsafe;
+    a.BH = p.BH;
     if (a.n_chunks > 65535 * 32 || p.BH > 65535)
         return hipErrorInvalidValue;
     const dim3 grid((unsigned)a.n_chunks, (unsigned)p.BH), block(kThreads);
     hipError_t e;
     if ((e = rec(2 * 1)) != hipSuccess)   // scores stage
         return e;
-#define LAMP_DEC_LAUNCH(K)                                                     \
-    do {                                                                       \
-        if (p.nq <= 1) hipLaunchKernelGGL((K<1>), grid, block, 0, st, a);      \
-        else if (p.nq <= 2) hipLaunchKernelGGL((K<2>), grid, block, 0, st, a); \
-        else if (p.nq <= 4) hipLaunchKernelGGL((K<4>), grid, block, 0, st, a); \
-        else if (p.nq <= 8) hipLaunchKernelGGL((K<8>), grid, block, 0, st, a); \
-        else hipLaunchKernelGGL((K<16>), grid, block, 0, st, a);               \
+    const size_t qlds = 2 * sizeof(float4) * (size_t)p.nq * (p.D / 4);
+#define LAMP_DEC_LAUNCH(K)                                                        \
+    do {                                                                          \
+        if (p.nq <= 1) hipLaunchKernelGGL((K<1>), grid, block, qlds, st, a);      \
+        else if (p.nq <= 2) hipLaunchKernelGGL((K<2>), grid, block, qlds, st, a); \
+        else if (p.nq <= 4) hipLaunchKernelGGL((K<4>), grid, block, qlds, st, a); \
+        else if (p.nq <= 8) hipLaunchKernelGGL((K<8>), grid, block, qlds, st, a); \
+        else hipLaunchKernelGGL((K<16>), grid, block, qlds, st, a);               \
     } while (0)
-    LAMP_DEC_LAUNCH(decode_scores_kernel);
+    if (p.mu <= 10)
+        LAMP_DEC_LAUNCH(decode_scores_kernel);
     if ((e = hipGetLastError()) != hipSuccess || (e = rec(2 * 1 + 1)) != hipSuccess ||
+        (e = rec(2 * 6)) != hipSuccess)   // exact stage
+        return e;
+    {
+        const long long total = (long long)p.BH * a.n_chunks;
+        const dim3 ge((unsigned)(total < 2048 ? total : 2048));
+#define LAMP_DEC_LAUNCH_E(K)                                                    \
+    do {                                                                        \
+        if (p.nq <= 1) hipLaunchKernelGGL((K<1>), ge, block, qlds, st, a);      \
+        else if (p.nq <= 2) hipLaunchKernelGGL((K<2>), ge, block, qlds, st, a); \
+        else if (p.nq <= 4) hipLaunchKernelGGL((K<4>), ge, block, qlds, st, a); \
+        else if (p.nq <= 8) hipLaunchKernelGGL((K<8>), ge, block, qlds, st, a); \
+        else hipLaunchKernelGGL((K<16>), ge, block, qlds, st, a);               \
+    } while (0)
+        LAMP_DEC_LAUNCH_E(decode_scores_exact_kernel);
+#undef LAMP_DEC_LAUNCH_E
+    }
+    if ((e = hipGetLastError()) != hipSuccess || (e = rec(2 * 6 + 1)) != hipSuccess ||
         (e = rec(2 * 2)) != hipSuccess)
         return e;
-    LAMP_DEC_LAUNCH(decode_softmax_kernel);
+    const dim3 grid2((unsigned)((a.n_blk + 3) / 4), (unsigned)p.BH);
+#define LAMP_DEC_LAUNCH2(K)                                                     \
+    do {                                                                        \
+        if (p.nq <= 1) hipLaunchKernelGGL((K<1>), grid2, block, 0, st, a);      \
+        else if (p.nq <= 2) hipLaunchKernelGGL((K<2>), grid2, block, 0, st, a); \
+        else if (p.nq <= 4) hipLaunchKernelGGL((K<4>), grid2, block, 0, st, a); \
+        else if (p.nq <= 8) hipLaunchKernelGGL((K<8>), grid2, block, 0, st, a); \
+        else hipLaunchKernelGGL((K<16>), grid2, block, 0, st, a);               \
+    } while (0)
+    LAMP_DEC_LAUNCH2(decode_softmax_kernel);
+#undef LAMP_DEC_LAUNCH2
 #undef LAMP_DEC_LAUNCH
     if ((e = hipGetLastError()) != hipSuccess || (e = rec(2 * 2 + 1)) != hipSuccess ||
         (e = rec(2 * 4)) != hipSuccess)
@@ -492,21 +646,21 @@ hipError_t launch_decode(const DecodeProblem &p, const DecodeBuffers &b, hipStre
     c.acc = b.acc;
     c.nq = p.nq;
     c.D = p.D;
-    c.n_chunks = a.n_chunks;
+    c.n_blk = a.n_blk;
     c.n_rows = p.BH * p.nq;
     c.out = b.out;
     c.row_lse = b.row_lse;
     c.row_kl = b.row_kl;
     c.row_kl_lowp = b.row_kl_lowp;
     c.row_count = b.row_count;
-    hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)((c.n_rows + 3) / 4)), block, 0, st,
-                       c);
+    hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)c.n_rows), block, 0, st, c);
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
     if (b.probs) {
-        const unsigned gx = (unsigned)min(a.n_chunks, 64);
-        hipLaunchKernelGGL(decode_probs_kernel, dim3(gx, (unsigned)(p.BH * p.nq)), block, 0, st,
-                           b.ylo, b.row_lse, b.probs, p.S, p.nq, p.causal);
+        const dim3 gp((unsigned)((p.S + 4 * kThreads - 1) / (4 * kThreads)),
+                      (unsigned)(p.BH * p.nq));
+        hipLaunchKernelGGL(decode_probs_kernel, gp, block, 0, st, b.ylo, b.row_lse, b.probs, p.S,
+                           p.nq, p.causal);
         if ((e = hipGetLastError()) != hipSuccess)
             return e;
     }

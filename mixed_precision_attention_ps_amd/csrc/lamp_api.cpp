@@ -214,7 +214,8 @@ struct StageTimer {
 namespace {
 
 struct DecodeLayout {
-    size_t ylo = SIZE_MAX, yref = SIZE_MAX, bmax = SIZE_MAX, part = SIZE_MAX, acc = SIZE_MAX,
+    size_t ylo = SIZE_MAX, yref = SIZE_MAX, bmax = SIZE_MAX, unsafe = SIZE_MAX, part = SIZE_MAX,
+           acc = SIZE_MAX,
            row_lse = SIZE_MAX, row_count = SIZE_MAX, row_kl = SIZE_MAX, row_kl_lowp = SIZE_MAX,
            dstats = SIZE_MAX;
     size_t total = 0;
@@ -227,7 +228,6 @@ struct DecodeLayout {
 };
 
 constexpr int kDecodeMaxQ = 16;
-constexpr int kDecodeChunk = 256;
 
 int check_decode(int B, int H, int Nq, int S, int D)
 {
@@ -251,15 +251,16 @@ DecodeLayout decode_plan(uint64_t BH, int Nq, int S, int D, bool need_ylo, bool 
 {
     DecodeLayout L;
     const uint64_t rows = BH * (uint64_t)Nq;
-    const uint64_t chunks = (S + kDecodeChunk - 1) / kDecodeChunk;
     L.dstats = L.take(sizeof(lamp::DevStats));
     if (need_ylo)
         L.ylo = L.take(4 * rows * (uint64_t)S);
     if (need_yref)
         L.yref = L.take(4 * rows * (uint64_t)S);
-    L.bmax = L.take(4 * rows * (uint64_t)((S + 63) / 64));
-    L.part = L.take(sizeof(lamp::DecPartial) * BH * chunks * (uint64_t)Nq);
-    L.acc = L.take(8 * BH * chunks * (uint64_t)Nq * (uint64_t)D);
+    const uint64_t blocks = (S + 63) / 64;
+    L.bmax = L.take(4 * rows * blocks);
+    L.unsafe = L.take(BH * (uint64_t)((S + 255) / 256));
+    L.part = L.take(sizeof(lamp::DecPartial) * rows * blocks);
+    L.acc = L.take(4 * rows * blocks * (uint64_t)D);
     L.row_lse = L.take(8 * rows);
     if (need_count)
         L.row_count = L.take(4 * rows);
@@ -320,9 +321,10 @@ int run_decode(const float *q, const float *k, const float *v, int B, int H, int
     b.ylo = p.scores_mix ? p.scores_mix : at<float>(ws, L.ylo);
     b.yref = p.scores_ref ? p.scores_ref : at<float>(ws, L.yref);
     b.bmax = at<float>(ws, L.bmax);
+    b.unsafe = at<uint8_t>(ws, L.unsafe);
     b.mask = mask;
     b.part = at<lamp::DecPartial>(ws, L.part);
-    b.acc = at<double>(ws, L.acc);
+    b.acc = at<float>(ws, L.acc);
     b.out = out;
     b.row_lse = at<double>(ws, L.row_lse);
     b.row_count = p.row_count ? p.row_count : at<uint32_t>(ws, L.row_count);

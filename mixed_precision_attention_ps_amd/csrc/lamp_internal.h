@@ -124,8 +124,8 @@ struct DecodeProblem {
     float tau;
 };
 
-// Softmax partial sums of one (head, 256-key chunk, query): maxima of y^mix,
-// y^ref and y^lo over the chunk's valid keys (-inf when it has none), and the
+// Softmax partial sums of one (head, 64-key block, query): maxima of y^mix,
+// y^ref and y^lo over the block's valid keys (-inf when it has none), and the
 // sums against them: l_mix = sum exp(y^mix - m_mix), l_ref = sum exp(y^ref -
 // m_ref), a = sum exp(y^ref - m_ref)(y^ref - y^mix), l_lo = sum exp(y^lo -
 // m_lo), b = sum exp(y^ref - m_ref)(y^ref - y^lo); cnt = selected keys.
@@ -138,9 +138,10 @@ struct DecPartial {
 struct DecodeBuffers {
     float *ylo, *yref;          // [BH, nq, S]; ylo ends as y^mix
     float *bmax;                // [BH, nq, ceil(S/64)]
+    uint8_t *unsafe;            // [BH, ceil(S/256)]: chunks for the exact path
     uint32_t *mask;             // [BH, nq, ceil(S/32)] or null
-    DecPartial *part;           // [BH, ceil(S/256), nq]
-    double *acc;                // [BH, ceil(S/256), nq, D]
+    DecPartial *part;           // [BH, ceil(S/64), nq]
+    float *acc;                 // [BH, ceil(S/64), nq, D]: P.V partials
     float *out;                 // [BH, nq, D]
     double *row_lse;            // [BH, nq]
     double *row_kl, *row_kl_lowp;   // [BH, nq] or null
@@ -149,9 +150,10 @@ struct DecodeBuffers {
     unsigned long long *exact_chunks;
 };
 
-// The four decode kernels in order; stage events (2 per stage, as in the
-// main entry point) are recorded around the score pass, the selection /
-// softmax pass and the combine (+ probabilities) pass when given.
+// The decode kernels in order; stage events (2 per stage, as in the main
+// entry point) are recorded around the fast score pass, the exact score pass,
+// the selection / softmax pass and the combine (+ probabilities) pass when
+// given.
 hipError_t launch_decode(const DecodeProblem &p, const DecodeBuffers &b, hipStream_t st,
                          void **stage_events);
 
