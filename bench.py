@@ -87,6 +87,18 @@ def cpu_baseline(Q, K, V, w, mode_id, mu, tau, heads_n, seed):
                       f"{n} valid scores in {dt:.2f} s wall, {threads} OpenMP threads"}
 
 
+def copy_calibration(args, dev):
+    """A plain device copy of known size (the scale of the HBM counters)."""
+    import torch
+    if args.copy_calib_mib:
+        n = args.copy_calib_mib * (1 << 20) // 4
+        a = torch.ones(n, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+
 def decode_cpu_baseline(Q, K, V, w, nq, mu, tau, heads_n):
     import numpy as np
     import oracle
@@ -127,6 +139,7 @@ def bench_decode(args, w):
     probs = None if args.no_probs else torch.empty((B, H, nq, S), device=dev)
     mask = torch.empty((B, H, nq, (S + 31) // 32), dtype=torch.int32, device=dev)
     row_kl = torch.empty((B, H, nq), dtype=torch.float64, device=dev)
+    copy_calibration(args, dev)
 
     def step(events=None):
         lamp.lamp_decode_fwd(q, k, v, causal=w.causal, mu=args.mu, tau=tau, out=out, probs=probs,
@@ -243,13 +256,7 @@ def main():
     mask = torch.empty((B, H, S, W32), dtype=torch.int32, device=dev)
     row_kl = torch.empty((B, H, S), dtype=torch.float64, device=dev)
 
-    if args.copy_calib_mib:
-        n = args.copy_calib_mib * (1 << 20) // 4
-        a = torch.ones(n, device=dev)
-        b = torch.empty_like(a)
-        b.copy_(a)
-        torch.cuda.synchronize()
-        del a, b
+    copy_calibration(args, dev)
 
     def step(events=None):
         lamp.lamp_attention_fwd(q, k, v, causal=w.causal, mu=args.mu, tau=tau, mode=mode_id,
