@@ -28,6 +28,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "lamp_oracle.c")
+_SRC_MLP = os.path.join(_HERE, "lamp_mlp_oracle.c")
 _LIB = os.path.join(_HERE, "liblamp_oracle.so")
 
 STRICT, RELAXED, RANDOM = 0, 1, 2
@@ -40,7 +41,7 @@ def build(force: bool = True) -> str:
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp"
         cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
-               "-std=c11", "-Wall", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"]
+               "-std=c11", "-Wall", "-fPIC", "-shared", "-o", tmp, _SRC, _SRC_MLP, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB)
     return _LIB
@@ -50,7 +51,8 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < max(os.path.getmtime(_SRC),
+                                                                os.path.getmtime(_SRC_MLP)):
         build(force=True)
     lib = ctypes.CDLL(_LIB)
     P = ctypes.c_void_p
@@ -72,6 +74,20 @@ def _load():
     lib.orc_lamp_rows.argtypes = ([P, P, P] + [ctypes.c_int] * 4 + [ctypes.c_float]
                                   + [ctypes.c_int] * 2 + [ctypes.c_uint64] * 2
                                   + [ctypes.c_int] * 3 + [P] * 9)
+    lib.orc_ps_gemm.restype = ctypes.c_int
+    lib.orc_ps_gemm.argtypes = [P, P] + [ctypes.c_int] * 5 + [P, P]
+    lib.orc_gelu.restype = ctypes.c_double
+    lib.orc_gelu.argtypes = [ctypes.c_double]
+    lib.orc_gelu_grad.restype = ctypes.c_double
+    lib.orc_gelu_grad.argtypes = [ctypes.c_double]
+    lib.orc_gelu_criterion.restype = ctypes.c_double
+    lib.orc_gelu_criterion.argtypes = [ctypes.c_float]
+    lib.orc_gelu_lamp.restype = ctypes.c_int
+    lib.orc_gelu_lamp.argtypes = ([P, P, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_int]
+                                  + [P] * 7)
+    lib.orc_ln_lamp.restype = ctypes.c_int
+    lib.orc_ln_lamp.argtypes = ([P, P, ctypes.c_int, ctypes.c_int, P, P, ctypes.c_float,
+                                 ctypes.c_float, ctypes.c_int] + [P] * 7)
     _lib = lib
     return lib
 
@@ -165,3 +181,73 @@ def lamp_heads(Q, K, V, *, causal: bool, mu: int, tau: float, mode: int, heads=N
                                mode=mode, seed=seed, head_lin=hl, row_begin=rb, row_end=re_,
                                block_k=block_k, threads=threads, **kw))
     return {k: np.stack([p[k] for p in parts]) for k in parts[0]}
+
+
+# ---------------------------------------------------------------------------
+# Activation (GELU) and layer-normalisation LAMP after a matrix product
+# (lamp_mlp_oracle.c).
+# ---------------------------------------------------------------------------
+def ps_gemm(X, W, *, mu: int, threads: int = 0):
+    """y = X W^T for X [M, K], W [N, K]: (y_lo PS(mu), y_ref sequential FP32)."""
+    X = np.ascontiguousarray(X, np.float32)
+    W = np.ascontiguousarray(W, np.float32)
+    M, K = X.shape
+    N = W.shape[0]
+    assert W.shape[1] == K
+    ylo = np.empty((M, N), np.float32)
+    yref = np.empty((M, N), np.float32)
+    rc = _load().orc_ps_gemm(_ptr(X), _ptr(W), M, N, K, int(mu), int(threads), _ptr(ylo),
+                             _ptr(yref))
+    if rc != 0:
+        raise ValueError("orc_ps_gemm: bad arguments")
+    return ylo, yref
+
+
+def gelu(y: float) -> float:
+    return _load().orc_gelu(float(y))
+
+
+def gelu_grad(y: float) -> float:
+    return _load().orc_gelu_grad(float(y))
+
+
+def gelu_criterion(y) -> float:
+    return _load().orc_gelu_criterion(float(np.float32(y)))
+
+
+def gelu_lamp(ylo, yref, *, tau: float, threads: int = 0):
+    """GELU LAMP over rows: dict of crit, mask, ymix, out, count, err, err_lowp."""
+    ylo = np.ascontiguousarray(ylo, np.float32)
+    yref = np.ascontiguousarray(yref, np.float32)
+    M, N = ylo.shape
+    W = (N + 31) // 32
+    r = {"crit": np.empty((M, N)), "mask": np.empty((M, W), np.uint32),
+         "ymix": np.empty((M, N), np.float32), "out": np.empty((M, N), np.float32),
+         "count": np.empty(M, np.int32), "err": np.empty(M), "err_lowp": np.empty(M)}
+    rc = _load().orc_gelu_lamp(_ptr(ylo), _ptr(yref), M, N, ctypes.c_float(tau), int(threads),
+                               *(_ptr(r[k]) for k in ("crit", "mask", "ymix", "out", "count",
+                                                      "err", "err_lowp")))
+    if rc != 0:
+        raise ValueError("orc_gelu_lamp: bad arguments")
+    return r
+
+
+def ln_lamp(ylo, yref, gamma, beta, *, eps: float, tau: float, threads: int = 0):
+    """LayerNorm LAMP over rows: dict of mask, ymix, out, count, err, err_lowp,
+    margin."""
+    ylo = np.ascontiguousarray(ylo, np.float32)
+    yref = np.ascontiguousarray(yref, np.float32)
+    gamma = np.ascontiguousarray(gamma, np.float32)
+    beta = np.ascontiguousarray(beta, np.float32)
+    M, N = ylo.shape
+    W = (N + 31) // 32
+    r = {"mask": np.empty((M, W), np.uint32), "ymix": np.empty((M, N), np.float32),
+         "out": np.empty((M, N), np.float32), "count": np.empty(M, np.int32),
+         "err": np.empty(M), "err_lowp": np.empty(M), "margin": np.empty(M)}
+    rc = _load().orc_ln_lamp(_ptr(ylo), _ptr(yref), M, N, _ptr(gamma), _ptr(beta),
+                             ctypes.c_float(eps), ctypes.c_float(tau), int(threads),
+                             *(_ptr(r[k]) for k in ("mask", "ymix", "out", "count", "err",
+                                                    "err_lowp", "margin")))
+    if rc != 0:
+        raise ValueError("orc_ln_lamp: bad arguments")
+    return r
