@@ -239,7 +239,9 @@ int orc_ln_lamp(const float *ylo, const float *yref, int M, int N, const float *
             for (int j = 0; j < N; ++j)
                 v += ((double)lo[j] - m) * ((double)lo[j] - m);
             v /= N;
-            const double T2 = (double)tau * (double)tau * (v + (double)eps) * (double)N;
+            double T2 = (double)tau * (double)tau * (v + (double)eps) * (double)N;
+            if (isnan(T2))   /* tau = +inf with sigma = 0 (or a NaN row): recompute nothing */
+                T2 = INFINITY;
             /* magnitudes sorted descending, ties to the lower index */
             for (int j = 0; j < N; ++j) {
                 keys[j].mag = fabsf(lo[j]);

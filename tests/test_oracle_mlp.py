@@ -219,3 +219,15 @@ def test_ln_lamp_beats_random_selection():
     # the bound the rule minimises weighs components by magnitude; the PS(mu)
     # error of a long dot is not purely relative, so the margin is modest
     assert r["err"].sum() < e_rand
+
+
+def test_ln_infinite_tau_on_a_constant_row_selects_nothing():
+    """tau = +inf recomputes nothing, also where sigma = 0 (eps = 0, a
+    constant row) makes tau^2 sigma^2 n undefined."""
+    y = np.full((2, 16), 0.75, np.float32)
+    g = np.ones(16, np.float32)
+    b = np.zeros(16, np.float32)
+    r = oracle.ln_lamp(y, y, g, b, eps=0.0, tau=np.inf)
+    assert (r["count"] == 0).all()
+    r0 = oracle.ln_lamp(y, y, g, b, eps=0.0, tau=0.0)
+    assert (r0["count"] == 16).all()
