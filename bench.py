@@ -39,17 +39,25 @@ METRIC = "LAMP attention scores/sec at μ=4 (GPT-2-XL layer) + % VALU/HBM roofli
 ALU_PEAK = 256 * 4 * 32 * 2.4e9
 HBM_PEAK = 8.0e12
 
-KERNEL_SOURCES = ["lamp_device.h", "lamp_exp.h", "lamp_internal.h", "scores.hip", "select.hip",
-                  "rows.hip", "finish.hip", "relaxed.hip", "decode.hip"]
+# The sources each measured kernel is built from (its traffic entry is stale
+# once any of them changes).
+_COMMON = ["lamp_device.h", "lamp_exp.h", "lamp_internal.h"]
+KERNEL_SOURCES = {
+    "ps_scores_kernel": _COMMON + ["scores.hip"],
+    "relaxed_kernel": _COMMON + ["relaxed.hip"],
+    "decode_scores_kernel": _COMMON + ["decode.hip"],
+    "decode_softmax_kernel": _COMMON + ["decode.hip"],
+    "ps_gemm_kernel": _COMMON + ["mlp.hip"],
+}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_sha() -> str:
+def kernel_source_sha(kernel: str) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, "mixed_precision_attention_ps_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -64,7 +72,7 @@ def load_traffic(kernel: str, workload: str, launches_per_step: int = 1):
     with open(path) as f:
         tab = json.load(f)
     ent = tab.get(f"{kernel}/{workload}")
-    if not ent or ent.get("source_sha") != kernel_source_sha():
+    if not ent or ent.get("source_sha") != kernel_source_sha(kernel):
         return None
     return ent.get("bytes_per_launch")
 
@@ -207,6 +215,106 @@ def bench_decode(args, w):
     print(json.dumps(rec), flush=True)
 
 
+def mlp_cpu_baseline(X, W, gamma, beta, w, mu, tau, rows_n):
+    import numpy as np
+    import oracle
+    oracle.build(force=False)
+    rows = np.linspace(0, w.M - 1, rows_n).astype(int)
+    threads = oracle.max_threads()
+    t0 = time.perf_counter()
+    ylo, yref = oracle.ps_gemm(X[rows], W, mu=mu)
+    if w.op == "gelu":
+        oracle.gelu_lamp(ylo, yref, tau=tau)
+    else:
+        oracle.ln_lamp(ylo, yref, gamma, beta, eps=w.eps, tau=tau)
+    dt = time.perf_counter() - t0
+    n = rows.size * w.N
+    return {"value": n / dt, "unit": "outputs/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rows.size} of {w.M} rows (all {w.N} columns) of {w.name}, same mu/tau; "
+                      f"{n} outputs in {dt:.2f} s wall, {threads} OpenMP threads"}
+
+
+def bench_mlp(args, w):
+    """LAMP after a PS(mu) matrix product: y = x W^T, then GELU with the
+    activation rule or layer normalisation with the greedy rule.  The
+    dominant kernel is the fast-path product (the same 9-instruction PS(mu)
+    multiply-add as the attention scores, plus the FP32 reference product),
+    reported against the ALU peak with 9 K lane-operations per output."""
+    import torch
+    from mixed_precision_attention_ps_amd import lamp
+    from mixed_precision_attention_ps_amd.configs import tau_for
+    tau = args.tau if args.tau is not None else tau_for(w.name, w.op, args.mu, args.rate)
+    dev = torch.device("cuda:0")
+    log(f"[bench] {w.name} {w.op} M={w.M} N={w.N} K={w.K} mu={args.mu} tau={tau}")
+    X, W, gamma, beta = w.inputs()
+    x, wt, g, b = (torch.from_numpy(a).to(dev) for a in (X, W, gamma, beta))
+    M, N, K = w.M, w.N, w.K
+    out = torch.empty((M, N), device=dev)
+    mask = torch.empty((M, (N + 31) // 32), dtype=torch.int32, device=dev)
+    row_err = torch.empty(M, dtype=torch.float64, device=dev)
+    copy_calibration(args, dev)
+
+    def step(events=None):
+        if w.op == "gelu":
+            lamp.lamp_gelu_fwd(x, wt, mu=args.mu, tau=tau, out=out, recompute_mask=mask,
+                               row_err=row_err, want_stats=False, stage_events=events)
+        else:
+            lamp.lamp_layernorm_fwd(x, wt, g, b, mu=args.mu, eps=w.eps, tau=tau, out=out,
+                                    recompute_mask=mask, row_err=row_err, want_stats=False,
+                                    stage_events=events)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [lamp.HipEvents(2 * lamp.LAMP_N_STAGES) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s_ in range(args.steps):
+        step(ev[s_])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stages = {}
+    for name in ("scan", "exact", "scores", "finish"):
+        si = lamp.STAGES.index(name)
+        stages[name] = sum(e.elapsed_ms(2 * si, 2 * si + 1) for e in ev) / args.steps
+    for e in ev:
+        e.close()
+    if w.op == "gelu":
+        _, st = lamp.lamp_gelu_fwd(x, wt, mu=args.mu, tau=tau, out=out, want_stats=True)
+    else:
+        _, st = lamp.lamp_layernorm_fwd(x, wt, g, b, mu=args.mu, eps=w.eps, tau=tau, out=out,
+                                        want_stats=True)
+    n_out = M * N
+    rate = st["n_selected"] / n_out
+    value = n_out / (wall / args.steps)
+    kname = "ps_gemm_kernel"
+    w_alg = 9 * K
+    t_kernel_ms = stages["scores"]
+    achieved = w_alg * n_out / (t_kernel_ms * 1e-3)
+    rec = {
+        "metric": f"LAMP {w.op} outputs/sec after a PS(mu=4) matrix product + % VALU roofline",
+        "value": value, "unit": "outputs/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": 1e3 * wall / args.steps, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "M": M, "N": N, "K": K, "op": w.op, "mu": args.mu,
+                   "tau": tau, "rate": rate, "mask": True, "row_err": True,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "alu", "kernel": kname, "achieved": achieved / 1e12,
+                     "peak": ALU_PEAK / 1e12, "unit": "Tlane-op/s", "frac": achieved / ALU_PEAK,
+                     "traffic": load_traffic(kname, w.name), "kernel_ms": t_kernel_ms,
+                     "slots_per_output": w_alg},
+        "path_alu_frac": w_alg * value / ALU_PEAK,
+        "stages_ms": stages,
+        "err_mean": st["kl_sum"] / st["n_rows"],
+        "err_lowp_mean": st["kl_lowp_sum"] / st["n_rows"],
+        "exact_tiles": st["n_exact_tiles"],
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample")
+        rec["cpu_baseline"] = mlp_cpu_baseline(X, W, gamma, beta, w, args.mu, tau, 64)
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -236,8 +344,10 @@ def main():
     import torch
 
     from mixed_precision_attention_ps_amd import lamp
-    from mixed_precision_attention_ps_amd.configs import WORKLOADS, tau_for
+    from mixed_precision_attention_ps_amd.configs import MLP_WORKLOADS, WORKLOADS, tau_for
 
+    if args.workload in MLP_WORKLOADS:
+        return bench_mlp(args, MLP_WORKLOADS[args.workload])
     w = WORKLOADS[args.workload]
     if w.name.startswith("decode"):
         return bench_decode(args, w)

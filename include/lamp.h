@@ -203,6 +203,67 @@ int lamp_decode_fwd(const float *q, const float *k, const float *v,
 size_t lamp_decode_workspace_bytes(int B, int H, int Nq, int S, int D);
 
 /*
+ * LAMP after a matrix product y = x W^T accumulated in PS(mu) (LAMP summary,
+ * "Theoretical foundation" item 3: an activation function and layer
+ * normalisation have closed-form sensitivities too; "Implementation strategy"
+ * steps 1-3).  x is [M,K] and W is [N,K], both row-major FP32; y^lo[i][j] is
+ * the PS(mu) dot of row i of x and row j of W in k order (rounded after every
+ * multiply and add), y^ref[i][j] the plain FP32 dot in the same order.
+ *
+ * lamp_gelu_fwd -- GELU (tanh form) on y with the activation rule: y_ij is
+ *   recomputed in FP32 iff |GELU'(y^lo_ij) y^lo_ij| > tau (evaluated in
+ *   double), out = GELU(y^mix) rounded to FP32.
+ *   x, w            inputs (required, 16-byte aligned).
+ *   M, N, K         sizes, >= 1; K % 4 == 0, K <= 2^24.
+ *   mu              PS(mu) fraction bits, 1..23.
+ *   tau             threshold, >= 0 (+inf selects nothing).
+ *   out             [M,N] (required, 16-byte aligned).
+ *   recompute_mask  [M,ceil(N/32)] uint32 or NULL, bit j % 32 of word j / 32
+ *                   set iff y_ij was recomputed (padding bits 0).
+ *   stats           host lamp_stats or NULL (non-NULL synchronises): n_rows M,
+ *                   n_valid M*N, n_selected, n_exact_tiles (64x64 tiles on the
+ *                   exact path), kl_sum / kl_max / kl_lowp_sum hold the row
+ *                   error measures below instead of KL.
+ *   p               NULL or extras: stream, workspace (lamp_mlp_workspace_bytes),
+ *                   row_kl [M] (double): sum_j |out_ij - GELU(y^ref_ij)| in
+ *                   double before the final rounding; row_kl_lowp [M]: the same
+ *                   for the all-PS(mu) output; row_count [M]; scores_mix /
+ *                   scores_ref [M,N]: y^mix and y^ref; stage_events
+ *                   (LAMP_STAGE_SCAN, LAMP_STAGE_SCORES: fast-path tiles with the
+ *                   rule fused, LAMP_STAGE_EXACT, LAMP_STAGE_FINISH: row sums).
+ *
+ * lamp_layernorm_fwd -- layer normalisation of each row of y with the greedy
+ *   rule: with sigma^2 = var(y^lo_i) + eps, the components of largest |y^lo_ij|
+ *   (ties to the lower j) are recomputed until the others have
+ *   sum y_j^2 <= tau^2 sigma^2 N; out = gamma (y^mix - mean) / sqrt(var + eps)
+ *   + beta over y^mix, in double, rounded to FP32.  N <= 8192.
+ *   gamma, beta     [N] (required).  eps >= 0.
+ *   Other arguments as for lamp_gelu_fwd; row_kl / row_kl_lowp hold the l2
+ *   distances ||LN(y^mix) - LN(y^ref)|| and ||LN(y^lo) - LN(y^ref)|| per row.
+ *
+ * Errors and ownership as for lamp_attention_fwd.
+ */
+int lamp_gelu_fwd(const float *x, const float *w, int M, int N, int K, int mu, float tau,
+                  float *out, uint32_t *recompute_mask, lamp_stats *stats, const lamp_params *p);
+
+int lamp_layernorm_fwd(const float *x, const float *w, const float *gamma, const float *beta,
+                       int M, int N, int K, int mu, float eps, float tau, float *out,
+                       uint32_t *recompute_mask, lamp_stats *stats, const lamp_params *p);
+
+/* Device scratch lamp_gelu_fwd (op 1) or lamp_layernorm_fwd (op 2) needs when
+ * none of the optional outputs is given (an upper bound); 0 on invalid
+ * sizes. */
+size_t lamp_mlp_workspace_bytes(int M, int N, int K, int op);
+
+/*
+ * lamp_gemm_scores -- the matrix product alone: y^lo (PS(mu)) and y^ref (FP32)
+ * of x [M,K] and W [N,K] into [M,N] buffers; either may be NULL (not both).
+ * Enqueued on `stream`; no synchronisation.
+ */
+int lamp_gemm_scores(const float *x, const float *w, int M, int N, int K, int mu, float *ylo,
+                     float *yref, void *stream);
+
+/*
  * lamp_diag_exp -- diagnostic: evaluates the library's two device exponentials
  * (the double one used for the selection criterion and the KL sums, the
  * FP32-accurate one used for probabilities) on n device doubles x, writing

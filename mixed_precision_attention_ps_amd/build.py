@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "liblamp.so")
 ARCH = os.environ.get("LAMP_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["scores.hip", "select.hip", "rows.hip", "finish.hip", "relaxed.hip", "decode.hip",
-           "lamp_api.cpp"]
+           "mlp.hip", "lamp_api.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-Wall", "-Wno-unused-function",
           f"--offload-arch={ARCH}",

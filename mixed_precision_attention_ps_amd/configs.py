@@ -1,4 +1,4 @@
-"""The five synthetic LAMP workloads and their thresholds.
+"""The synthetic LAMP workloads and their thresholds.
 
 Shapes, distributions and (mu, mode, tau) sweeps of the workloads the build is
 measured and checked on.  The GPT-2 shapes mirror the models the LAMP
@@ -58,6 +58,40 @@ WORKLOADS = {
         Workload("decode_s16384", 8, 25, 16384, 64, True, 2, 8.0, 1.0, (4,), "relaxed"),
     ]
 }
+
+@dataclass(frozen=True)
+class MlpWorkload:
+    """y = X W^T (X [M, K], W [N, K]) followed by GELU or layer normalisation."""
+    name: str
+    M: int
+    N: int
+    K: int
+    op: str              # "gelu" or "layernorm"
+    w_std: float = 0.02
+    eps: float = 1e-5
+    mus: tuple = (4,)
+    seed: int = 0
+
+    @property
+    def n_valid(self) -> int:
+        return self.M * self.N
+
+    def inputs(self, seed=None):
+        from .inputs import make_mlp
+        return make_mlp(self.M, self.N, self.K, w_std=self.w_std,
+                        seed=self.seed if seed is None else seed)
+
+
+MLP_WORKLOADS = {
+    w.name: w for w in [
+        # GPT-2 XL MLP up-projection of 1024 tokens (d_model 1600 -> 6400)
+        # followed by the activation
+        MlpWorkload("gelu_gpt2_xl_mlp", 1024, 6400, 1600, "gelu"),
+        # GPT-2 XL MLP down-projection (6400 -> 1600) followed by a layer norm
+        MlpWorkload("ln_gpt2_xl", 1024, 1600, 6400, "layernorm"),
+    ]
+}
+
 
 def _load_tau_table() -> dict:
     import json

@@ -362,6 +362,167 @@ int run_decode(const float *q, const float *k, const float *v, int B, int H, int
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// Matrix product + activation / layer normalisation.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int kLnMaxN = 8192;
+
+struct MlpLayout {
+    size_t unsafe = SIZE_MAX, ylo = SIZE_MAX, yref = SIZE_MAX, mask = SIZE_MAX,
+           err_part = SIZE_MAX, errl_part = SIZE_MAX, err = SIZE_MAX, errl = SIZE_MAX,
+           count = SIZE_MAX, dstats = SIZE_MAX;
+    size_t total = 0;
+    size_t take(size_t bytes)
+    {
+        size_t off = total;
+        total += align_up(bytes);
+        return off;
+    }
+};
+
+int check_mlp(int M, int N, int K, int op)
+{
+    if (M < 1 || N < 1 || K < 1)
+        return set_error(LAMP_ERR_INVALID_ARG, "M, N and K must be >= 1");
+    if (K % 4 != 0)
+        return set_error(LAMP_ERR_UNSUPPORTED, "K must be a multiple of 4");
+    if (K > (1 << 24))
+        return set_error(LAMP_ERR_UNSUPPORTED, "K must be <= 2^24");
+    if (op == lamp::MLP_LAYERNORM && N > kLnMaxN)
+        return set_error(LAMP_ERR_UNSUPPORTED, "layer normalisation supports N <= 8192");
+    const uint64_t tm = (M + 63) / 64, tn = (N + 63) / 64;
+    if (tm * tn >= (1ull << 31) || (uint64_t)M * (uint64_t)N > (1ull << 40) ||
+        (uint64_t)M * (uint64_t)K > (1ull << 40) || (uint64_t)N * (uint64_t)K > (1ull << 40))
+        return set_error(LAMP_ERR_UNSUPPORTED, "problem size overflows the launch geometry");
+    return LAMP_OK;
+}
+
+MlpLayout mlp_plan(int M, int N, int op, bool need_ylo, bool need_yref, bool need_mask,
+                   bool need_err, bool need_errl, bool need_count)
+{
+    MlpLayout L;
+    const uint64_t tm = (M + 63) / 64, tn = (N + 63) / 64;
+    L.dstats = L.take(sizeof(lamp::DevStats));
+    L.unsafe = L.take(4 * (tm + tn));
+    if (op == lamp::MLP_LAYERNORM) {
+        if (need_ylo)
+            L.ylo = L.take(4 * (uint64_t)M * N);
+        if (need_yref)
+            L.yref = L.take(4 * (uint64_t)M * N);
+    }
+    if (op == lamp::MLP_GELU) {
+        L.err_part = L.take(8 * (uint64_t)M * tn);
+        L.errl_part = L.take(8 * (uint64_t)M * tn);
+        if (need_mask)
+            L.mask = L.take(4 * (uint64_t)M * ((N + 31) / 32));
+    }
+    if (need_err)
+        L.err = L.take(8 * (uint64_t)M);
+    if (need_errl)
+        L.errl = L.take(8 * (uint64_t)M);
+    if (need_count)
+        L.count = L.take(4 * (uint64_t)M);
+    return L;
+}
+
+int run_mlp(int op, const float *x, const float *w, const float *gamma, const float *beta, int M,
+            int N, int K, int mu, float eps, float tau, float *out, uint32_t *mask,
+            lamp_stats *stats, const lamp_params *pp)
+{
+    g_last_error.clear();
+    if (!x || !w || !out || (op == lamp::MLP_LAYERNORM && (!gamma || !beta)))
+        return set_error(LAMP_ERR_INVALID_ARG, "x, w, out (and gamma, beta) are required");
+    if (!aligned16(x) || !aligned16(w) || !aligned16(out))
+        return set_error(LAMP_ERR_INVALID_ARG, "x, w and out must be 16-byte aligned");
+    if (mu < 1 || mu > 23)
+        return set_error(LAMP_ERR_INVALID_ARG, "mu must be in [1, 23]");
+    if (isnan(tau) || tau < 0.0f)
+        return set_error(LAMP_ERR_INVALID_ARG, "tau must be >= 0 and not NaN");
+    if (op == lamp::MLP_LAYERNORM && (isnan(eps) || eps < 0.0f))
+        return set_error(LAMP_ERR_INVALID_ARG, "eps must be >= 0 and not NaN");
+    int rc = check_mlp(M, N, K, op);
+    if (rc != LAMP_OK)
+        return rc;
+    (void)hipGetLastError();
+    lamp_params none{};
+    const lamp_params &p = pp ? *pp : none;
+    hipStream_t st = (hipStream_t)p.stream;
+    const bool want_stats = stats != nullptr;
+    const MlpLayout L = mlp_plan(M, N, op, true, p.scores_ref == nullptr, mask == nullptr,
+                                 p.row_kl == nullptr, p.row_kl_lowp == nullptr,
+                                 p.row_count == nullptr);
+    void *ws = nullptr;
+    if (p.workspace) {
+        if (p.workspace_bytes < L.total)
+            return set_error(LAMP_ERR_INVALID_ARG,
+                             "workspace too small: need " + std::to_string(L.total) + " bytes");
+        if (((uintptr_t)p.workspace & (kAlign - 1)) != 0)
+            return set_error(LAMP_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+        ws = p.workspace;
+    } else {
+        rc = pool_get(L.total, &ws);
+        if (rc != LAMP_OK)
+            return rc;
+    }
+    auto *dstats = at<lamp::DevStats>(ws, L.dstats);
+    lamp::MlpProblem P;
+    P.x = x;
+    P.w = w;
+    P.gamma = gamma;
+    P.beta = beta;
+    P.M = M;
+    P.N = N;
+    P.K = K;
+    P.mu = mu;
+    P.op = op;
+    P.tau = tau;
+    P.eps = eps;
+    lamp::MlpBuffers b{};
+    b.unsafe = at<uint32_t>(ws, L.unsafe);
+    if (op == lamp::MLP_LAYERNORM) {
+        b.ylo = at<float>(ws, L.ylo);
+        b.yref = p.scores_ref ? p.scores_ref : at<float>(ws, L.yref);
+        b.ymix = p.scores_mix;
+    } else {
+        b.ylo = p.scores_mix;   // y^mix, when asked for
+        b.yref = p.scores_ref;
+    }
+    b.out = out;
+    b.mask = mask ? mask : at<uint32_t>(ws, L.mask);
+    b.err_part = at<double>(ws, L.err_part);
+    b.errl_part = at<double>(ws, L.errl_part);
+    b.err = p.row_kl ? p.row_kl : at<double>(ws, L.err);
+    b.errl = p.row_kl_lowp ? p.row_kl_lowp : at<double>(ws, L.errl);
+    uint32_t *count = p.row_count ? p.row_count : at<uint32_t>(ws, L.count);
+    b.row_count = count;
+    b.exact_tiles = &dstats->n_exact_tiles;
+    LAMP_HIP_TRY(lamp::launch_zero(dstats, sizeof(lamp::DevStats), st), "zero stats");
+    LAMP_HIP_TRY(lamp::launch_mlp(P, b, st, p.stage_events), "matrix product launch");
+    if (op == lamp::MLP_GELU)
+        LAMP_HIP_TRY(lamp::launch_mask_count(b.mask, M, N, count, st), "count launch");
+    if (want_stats) {
+        lamp::Problem Ps{};
+        Ps.n_rows = (uint64_t)M;
+        LAMP_HIP_TRY(lamp::launch_stats(Ps, b.err, b.errl, count, dstats, st), "stats launch");
+        lamp::DevStats ds;
+        LAMP_HIP_TRY(hipMemcpyAsync(&ds, dstats, sizeof(ds), hipMemcpyDeviceToHost, st),
+                     "hipMemcpyAsync stats");
+        LAMP_HIP_TRY(hipStreamSynchronize(st), "hipStreamSynchronize");
+        stats->n_rows = (uint64_t)M;
+        stats->n_valid = (uint64_t)M * (uint64_t)N;
+        stats->n_selected = ds.n_selected;
+        stats->n_exact_tiles = ds.n_exact_tiles;
+        stats->kl_sum = ds.kl_sum;
+        stats->kl_max = ds.kl_max;
+        stats->kl_lowp_sum = ds.kl_lowp_sum;
+    }
+    return LAMP_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char *lamp_strerror(int code)
@@ -625,6 +786,81 @@ int lamp_decode_fwd(const float *q, const float *k, const float *v, int B, int H
                           stats, p);
     } catch (const std::bad_alloc &) {
         return set_error(LAMP_ERR_NO_MEMORY, "host allocation failed");
+    } catch (...) {
+        return set_error(LAMP_ERR_HIP, "unexpected exception");
+    }
+}
+
+int lamp_gelu_fwd(const float *x, const float *w, int M, int N, int K, int mu, float tau,
+                  float *out, uint32_t *recompute_mask, lamp_stats *stats, const lamp_params *p)
+{
+    try {
+        return run_mlp(lamp::MLP_GELU, x, w, nullptr, nullptr, M, N, K, mu, 0.0f, tau, out,
+                       recompute_mask, stats, p);
+    } catch (const std::bad_alloc &) {
+        return set_error(LAMP_ERR_NO_MEMORY, "host allocation failed");
+    } catch (...) {
+        return set_error(LAMP_ERR_HIP, "unexpected exception");
+    }
+}
+
+int lamp_layernorm_fwd(const float *x, const float *w, const float *gamma, const float *beta,
+                       int M, int N, int K, int mu, float eps, float tau, float *out,
+                       uint32_t *recompute_mask, lamp_stats *stats, const lamp_params *p)
+{
+    try {
+        return run_mlp(lamp::MLP_LAYERNORM, x, w, gamma, beta, M, N, K, mu, eps, tau, out,
+                       recompute_mask, stats, p);
+    } catch (const std::bad_alloc &) {
+        return set_error(LAMP_ERR_NO_MEMORY, "host allocation failed");
+    } catch (...) {
+        return set_error(LAMP_ERR_HIP, "unexpected exception");
+    }
+}
+
+size_t lamp_mlp_workspace_bytes(int M, int N, int K, int op)
+{
+    if (op != lamp::MLP_GELU && op != lamp::MLP_LAYERNORM)
+        return 0;
+    if (check_mlp(M, N, K, op) != LAMP_OK)
+        return 0;
+    return mlp_plan(M, N, op, true, true, true, true, true, true).total;
+}
+
+int lamp_gemm_scores(const float *x, const float *w, int M, int N, int K, int mu, float *ylo,
+                     float *yref, void *stream)
+{
+    try {
+        g_last_error.clear();
+        if (!x || !w || (!ylo && !yref))
+            return set_error(LAMP_ERR_INVALID_ARG, "x, w and one of ylo, yref are required");
+        if (!aligned16(x) || !aligned16(w))
+            return set_error(LAMP_ERR_INVALID_ARG, "x and w must be 16-byte aligned");
+        if (mu < 1 || mu > 23)
+            return set_error(LAMP_ERR_INVALID_ARG, "mu must be in [1, 23]");
+        int rc = check_mlp(M, N, K, lamp::MLP_GEMM);
+        if (rc != LAMP_OK)
+            return rc;
+        void *ws = nullptr;
+        const size_t flags = 4 * ((size_t)(M + 63) / 64 + (size_t)(N + 63) / 64);
+        rc = pool_get(align_up(flags), &ws);
+        if (rc != LAMP_OK)
+            return rc;
+        (void)hipGetLastError();
+        lamp::MlpProblem P{};
+        P.x = x;
+        P.w = w;
+        P.M = M;
+        P.N = N;
+        P.K = K;
+        P.mu = mu;
+        P.op = lamp::MLP_GEMM;
+        lamp::MlpBuffers b{};
+        b.unsafe = (uint32_t *)ws;
+        b.ylo = ylo;
+        b.yref = yref;
+        LAMP_HIP_TRY(lamp::launch_mlp(P, b, (hipStream_t)stream, nullptr), "matrix product launch");
+        return LAMP_OK;
     } catch (...) {
         return set_error(LAMP_ERR_HIP, "unexpected exception");
     }

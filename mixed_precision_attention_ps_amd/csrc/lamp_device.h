@@ -167,11 +167,12 @@ __device__ __forceinline__ void compute_slice(const TileSmem &sm, TileAcc &acc, 
     }
 }
 
-// Full-D accumulation of one 64x64 tile: rows row0.., keys col0.. of one head.
+// Full-D accumulation of one 64x64 tile: rows row0.. of Qh (nq rows), keys
+// col0.. of Kh (nk rows); both row-major with D columns.
 template <int PATH>
 __device__ __forceinline__ void score_tile(TileSmem &sm, TileAcc &acc, const float *Qh,
-                                           const float *Kh, int row0, int col0, int S, int D,
-                                           const PsConst &pc)
+                                           const float *Kh, int row0, int col0, int nq, int nk,
+                                           int D, const PsConst &pc)
 {
     const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
 #pragma unroll
@@ -185,7 +186,7 @@ __device__ __forceinline__ void score_tile(TileSmem &sm, TileAcc &acc, const flo
     const int lrow = tid >> 2, ld = (tid & 3) * 4;
     const float *Qb = Qh + (size_t)row0 * D;
     const float *Kb = Kh + (size_t)col0 * D;
-    const int qrows = S - row0, krows = S - col0;
+    const int qrows = nq - row0, krows = nk - col0;
     float4 qv[kSliceV4], kv[kSliceV4];
 #pragma unroll
     for (int u = 0; u < kSliceV4; ++u) {

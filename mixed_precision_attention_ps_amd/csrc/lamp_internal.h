@@ -157,6 +157,38 @@ struct DecodeBuffers {
 hipError_t launch_decode(const DecodeProblem &p, const DecodeBuffers &b, hipStream_t st,
                          void **stage_events);
 
+// Matrix product y = x W^T in PS(mu) followed by an activation (GELU) or a
+// layer normalisation, with the LAMP rule of that closed form.
+enum { MLP_GEMM = 0, MLP_GELU = 1, MLP_LAYERNORM = 2 };
+
+struct MlpProblem {
+    const float *x, *w;           // x [M, K], w [N, K]
+    const float *gamma, *beta;    // [N] (layer normalisation)
+    int M, N, K, mu, op;
+    float tau, eps;
+};
+
+struct MlpBuffers {
+    uint32_t *unsafe;             // [ceil(M/64) + ceil(N/64)] operand range flags
+    float *ylo, *yref;            // [M, N]: y^lo (GELU: y^mix) and y^ref, or null
+    float *ymix;                  // [M, N] or null (layer normalisation)
+    float *out;                   // [M, N]
+    uint32_t *mask;               // [M, ceil(N/32)] or null
+    double *err_part, *errl_part; // [M, ceil(N/64)] (GELU)
+    double *err, *errl;           // [M] or null
+    uint32_t *row_count;          // [M] or null (layer normalisation)
+    unsigned long long *exact_tiles;
+};
+
+// The operand scans, the product (fast tiles and the others), then the GELU
+// row reduction or the layer-normalisation row pass; stage events as in the
+// attention path (scan, exact, scores, finish).
+hipError_t launch_mlp(const MlpProblem &p, const MlpBuffers &b, hipStream_t st,
+                      void **stage_events);
+
+// Per-row popcount of mask words (the GELU counts).
+hipError_t launch_mask_count(const uint32_t *mask, int M, int N, uint32_t *count, hipStream_t st);
+
 // Device-side summary.
 struct DevStats {
     unsigned long long n_selected;

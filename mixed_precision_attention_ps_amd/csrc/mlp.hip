@@ -1,0 +1,569 @@
+// mlp.hip -- LAMP at the pages' two other closed forms, after a matrix
+// product y = x W^T accumulated in PS(mu): an activation function (GELU) and
+// layer normalisation.
+//
+// LAMP summary, "Theoretical foundation" item 3 (an activation function's
+// Jacobian is diagonal, so its sensitive components are read off one by one;
+// for layer normalisation a nearly sparsest selection follows greedily from
+// the input magnitudes sorted) and "Implementation strategy" steps 1-3.  The
+// formulas are readings (the pages give neither):
+//   * GELU, tanh form; recompute y_j iff |GELU'(y_j) y_j| > tau (the l1
+//     change of the output per unit relative change of y_j, as in the softmax
+//     rule), evaluated in double at the low-precision y_j.
+//   * LayerNorm; recompute the largest |y_j| (ties to the lower index) until
+//     the rest has ||y_U||_2 <= tau sigma sqrt(n), sigma^2 = var + eps of the
+//     low-precision row.
+//
+// Kernels:
+//   * gemm_scan_kernel: per 64-row block of x or W, whether every value lies
+//     in the fast path's operand range (many work-groups per block).
+//   * ps_gemm_kernel<FAST, EPI>: one work-group per 64x64 tile of y, the
+//     score-tile machinery of the attention path with x as the query rows and
+//     W as the keys (K = the head dimension), no scale.  EPI_STORE writes
+//     y^lo and y^ref; EPI_GELU applies the GELU rule in the epilogue (the
+//     tile's FP32 reference is the recompute, bit for bit), writes GELU(y^mix),
+//     the mask words, per-(row, tile) l1 error partials and, when asked for,
+//     y^mix and y^ref.
+//   * ln_lamp_kernel: one work-group per row: statistics of y^lo, a bitonic
+//     sort of (magnitude, index) keys in LDS, the suffix sums of squares over
+//     the sorted order, the recompute count k*, then LN(y^mix), the mask, the
+//     count and the l2 errors.
+//   * row_reduce_kernel: the GELU error partials per row.
+#include "lamp_device.h"
+
+namespace lamp {
+
+// ---------------------------------------------------------------------------
+// Operand range scan of one matrix: flags[b] != 0 when 64-row block b holds a
+// value outside {0} U [2^-40, 2^40] (or a non-finite one).  A 64-row block is
+// one contiguous span of 64 K floats; grid.y splits it into kScanSpan-float
+// pieces so that the scan of a long-K operand still fills the GPU.  The flags
+// are cleared before the launch; a work-group that finds an unsafe value
+// sets its block's flag (a rare event: one atomic per such work-group).
+// ---------------------------------------------------------------------------
+constexpr int kScanSpan = 16384;                        // floats per work-group
+constexpr int kScanV4 = kScanSpan / (4 * kThreads);     // float4 loads per thread
+
+__device__ __forceinline__ bool mlp_safe(float x)
+{
+    const uint32_t m = __float_as_uint(x) & 0x7fffffffu;
+    return m == 0u || (m - 0x2b800000u) <= (0x53800000u - 0x2b800000u);
+}
+
+__global__ __launch_bounds__(kThreads) void gemm_scan_kernel(const float *a, int rows, int K,
+                                                             uint32_t *flags)
+{
+    const int b = blockIdx.x;
+    const int r0 = b * kTile, r1 = min(rows, r0 + kTile);
+    const size_t n4 = (size_t)(r1 - r0) * K / 4;   // K % 4 == 0
+    const float4 *p = reinterpret_cast<const float4 *>(a + (size_t)r0 * K);
+    const size_t e0 = (size_t)blockIdx.y * (kScanSpan / 4);
+    bool ok = true;
+#pragma unroll
+    for (int u = 0; u < kScanV4; ++u) {
+        const size_t e = e0 + (size_t)u * kThreads + threadIdx.x;
+        if (e < n4) {
+            const float4 v = p[e];
+            ok = ok && mlp_safe(v.x) && mlp_safe(v.y) && mlp_safe(v.z) && mlp_safe(v.w);
+        }
+    }
+    const int any_bad = __syncthreads_or(ok ? 0 : 1);
+    if (any_bad && threadIdx.x == 0)
+        atomicOr(&flags[b], 1u);
+}
+
+// ---------------------------------------------------------------------------
+// GELU (tanh form) in double through the logistic function, which has no
+// cancellation anywhere: with u = sqrt(2/pi) (y + 0.044715 y^3) and
+// s = 1 / (1 + exp(-2u)) (so that (1 + tanh u) / 2 = s),
+//   GELU(y)  = y s,
+//   GELU'(y) = s + 2 y s (1 - s) u',  u' = sqrt(2/pi) (1 + 3 * 0.044715 y^2).
+// ---------------------------------------------------------------------------
+struct Gelu {
+    double g, dg;
+};
+
+__device__ __forceinline__ Gelu gelu64(double y, const double *s_exp)
+{
+    const double a = 0.7978845608028654, b = 0.044715;
+    const double u = a * (y + b * y * y * y);
+    const double e = exp64(-2.0 * u, s_exp);   // +inf for very negative u
+    const double s = 1.0 / (1.0 + e);          // 0 when e is +inf
+    const double one_minus_s = e < 1e300 ? e * s : 1.0;
+    const double du = a * (1.0 + 3.0 * b * y * y);
+    Gelu r;
+    r.g = y * s;
+    r.dg = s + 2.0 * y * s * one_minus_s * du;
+    return r;
+}
+
+enum { EPI_STORE = 0, EPI_GELU = 1 };
+
+struct GemmArgs {
+    const float *x, *w;          // x [M, K], w [N, K]
+    int M, N, K, tiles_n, W;
+    PsConst pc;                  // s = 1
+    const uint32_t *unsafe_x, *unsafe_w;
+    float *ylo, *yref;           // [M, N] or null
+    float *out;                  // [M, N] (GELU)
+    uint32_t *mask;              // [M, W] or null (GELU)
+    double *err_part, *errl_part;   // [M, tiles_n] (GELU)
+    double tau;
+    unsigned long long *exact_tiles;
+    long long n_tiles;
+};
+
+template <int PATH, int EPI>
+__device__ __forceinline__ void gemm_tile(TileSmem &sm, const double *s_exp, const GemmArgs &a,
+                                          int ti, int tj)
+{
+    TileAcc acc;
+    score_tile<PATH>(sm, acc, a.x, a.w, ti * kTile, tj * kTile, a.M, a.N, a.K, a.pc);
+    float lo[4][4], ref[4][4];
+    tile_scores<PATH>(acc, a.pc, lo, ref);
+    const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4, lane = tid & 63;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int i = ti * kTile + ty * 4 + r;
+        bool valid[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            valid[c] = i < a.M && tj * kTile + tx + 16 * c < a.N;
+        const size_t rowoff = (size_t)(i < a.M ? i : 0) * a.N;
+        if (EPI == EPI_STORE && (a.ylo || a.yref)) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int j = tj * kTile + tx + 16 * c;
+                if (!valid[c])
+                    continue;
+                if (a.ylo)
+                    a.ylo[rowoff + j] = lo[r][c];
+                if (a.yref)
+                    a.yref[rowoff + j] = ref[r][c];
+            }
+        }
+        if (EPI == EPI_GELU) {
+            double el = 0.0, em = 0.0;
+            bool sel[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int j = tj * kTile + tx + 16 * c;
+                const Gelu gl = gelu64((double)lo[r][c], s_exp);
+                sel[c] = valid[c] && fabs(gl.dg * (double)lo[r][c]) > a.tau;
+                const Gelu gr = gelu64((double)ref[r][c], s_exp);
+                const double gm = sel[c] ? gr.g : gl.g;
+                if (valid[c]) {
+                    a.out[rowoff + j] = (float)gm;
+                    if (a.ylo)   // y^mix
+                        a.ylo[rowoff + j] = sel[c] ? ref[r][c] : lo[r][c];
+                    if (a.yref)
+                        a.yref[rowoff + j] = ref[r][c];
+                    em += fabs(gm - gr.g);
+                    el += fabs(gl.g - gr.g);
+                }
+            }
+            // mask words: key tx + 16 c of this row group is bit (tx + 16 c) % 32
+            // of word 2 tj + c / 2; lanes 16 (lane / 16) .. + 15 hold the row
+            const int gsh = lane & 48;
+            uint32_t bits[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                bits[c] = (uint32_t)(__ballot(sel[c]) >> gsh) & 0xffffu;
+            em = group16_sum(em);
+            el = group16_sum(el);
+            if (i < a.M && tx == 0) {
+                if (a.mask) {
+                    const uint32_t w0 = bits[0] | (bits[1] << 16), w1 = bits[2] | (bits[3] << 16);
+                    if (2 * tj < a.W)
+                        a.mask[(size_t)i * a.W + 2 * tj] = w0;
+                    if (2 * tj + 1 < a.W)
+                        a.mask[(size_t)i * a.W + 2 * tj + 1] = w1;
+                }
+                a.err_part[(size_t)i * a.tiles_n + tj] = em;
+                a.errl_part[(size_t)i * a.tiles_n + tj] = el;
+            }
+        }
+    }
+}
+
+// FAST: the tiles whose operands allow the FP32 fast path (one work-group per
+// tile); otherwise a bounded grid striding over the other tiles (exact double
+// path, or plain FP32 at mu = 23), exiting at once when there are none.
+template <bool FAST, int EPI>
+__global__ __launch_bounds__(kThreads) void ps_gemm_kernel(GemmArgs a)
+{
+    __shared__ TileSmem sm;
+    __shared__ double s_exp[64];
+    exp_table_fill(s_exp);
+    __syncthreads();
+    auto path_of = [&](long long g, int &ti, int &tj) {
+        ti = (int)(g / a.tiles_n);
+        tj = (int)(g % a.tiles_n);
+        if (a.pc.mu == 23)
+            return (int)PATH_FP32;
+        if (a.pc.mu <= 10 && !a.unsafe_x[ti] && !a.unsafe_w[tj])
+            return (int)PATH_FAST;
+        return (int)PATH_EXACT;
+    };
+    if (!FAST) {
+        bool need = false;
+        for (long long g = blockIdx.x + (long long)threadIdx.x * gridDim.x; g < a.n_tiles;
+             g += (long long)blockDim.x * gridDim.x) {
+            int ti, tj;
+            need |= path_of(g, ti, tj) != PATH_FAST;
+        }
+        if (!__syncthreads_or(need ? 1 : 0))
+            return;
+    }
+    for (long long g = blockIdx.x; g < a.n_tiles; g += FAST ? a.n_tiles : gridDim.x) {
+        int ti, tj;
+        const int path = path_of(g, ti, tj);
+        if (FAST) {
+            if (path == PATH_FAST)
+                gemm_tile<PATH_FAST, EPI>(sm, s_exp, a, ti, tj);
+        } else if (path == PATH_EXACT) {
+            if (threadIdx.x == 0 && a.exact_tiles)
+                atomicAdd(a.exact_tiles, 1ull);
+            gemm_tile<PATH_EXACT, EPI>(sm, s_exp, a, ti, tj);
+        } else if (path == PATH_FP32) {
+            gemm_tile<PATH_FP32, EPI>(sm, s_exp, a, ti, tj);
+        }
+    }
+}
+
+// Per-row sums of the GELU error partials, in tile order.
+__global__ __launch_bounds__(kThreads) void row_reduce_kernel(const double *ep, const double *elp,
+                                                              int M, int tiles_n, double *err,
+                                                              double *errl)
+{
+    const int i = blockIdx.x * kThreads + threadIdx.x;
+    if (i >= M)
+        return;
+    double e = 0.0, el = 0.0;
+    for (int t = 0; t < tiles_n; ++t) {
+        e += ep[(size_t)i * tiles_n + t];
+        el += elp[(size_t)i * tiles_n + t];
+    }
+    if (err)
+        err[i] = e;
+    if (errl)
+        errl[i] = el;
+}
+
+// ---------------------------------------------------------------------------
+// Layer normalisation LAMP, one work-group per row (N <= kLnMaxN).
+// ---------------------------------------------------------------------------
+constexpr int kLnMaxN = 8192;
+constexpr int kLnPerThread = kLnMaxN / kThreads;   // 32
+
+struct LnArgs {
+    const float *ylo, *yref;     // [M, N]
+    const float *gamma, *beta;   // [N]
+    int M, N, W, P;              // P: N rounded up to a power of two (the sort width)
+    double eps, tau;
+    float *out;                  // [M, N]
+    float *ymix;                 // [M, N] or null
+    uint32_t *mask;              // [M, W] or null
+    uint32_t *row_count;         // [M] or null
+    double *err, *errl;          // [M] or null
+};
+
+// Block sum of a double over the 256 threads (every thread gets the result).
+__device__ __forceinline__ double block_sum_d(double x, double *s_red)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    x = wave_sum(x);
+    __syncthreads();   // s_red may still be read by the previous call
+    if (lane == 0)
+        s_red[wave] = x;
+    __syncthreads();
+    return (s_red[0] + s_red[1]) + (s_red[2] + s_red[3]);
+}
+
+__global__ __launch_bounds__(kThreads) void ln_lamp_kernel(LnArgs a)
+{
+    extern __shared__ uint64_t s_key[];   // P sort keys, then selection flags
+    __shared__ double s_red[4];
+    __shared__ uint32_t s_cnt[4];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int i = blockIdx.x;
+    const int N = a.N;
+    const float *lo = a.ylo + (size_t)i * N, *rf = a.yref + (size_t)i * N;
+
+    // statistics of the low-precision row (the look-ahead estimate of sigma)
+    double s1 = 0.0;
+    for (int j = tid; j < N; j += kThreads)
+        s1 += (double)lo[j];
+    const double m_lo = block_sum_d(s1, s_red) / N;
+    double s2 = 0.0;
+    for (int j = tid; j < N; j += kThreads) {
+        const double d = (double)lo[j] - m_lo;
+        s2 += d * d;
+    }
+    const double v_lo = block_sum_d(s2, s_red) / N;
+    double T2 = a.tau * a.tau * (v_lo + a.eps) * (double)N;
+    if (isnan(T2))   // tau = +inf with sigma = 0 (or a NaN row): recompute nothing
+        T2 = INFINITY;
+
+    // sort keys: descending magnitude, ties to the lower index, as one
+    // ascending 64-bit order: (~|y| bits) << 32 | j; padding keys sort last
+    for (int p = tid; p < a.P; p += kThreads) {
+        uint64_t key = ~0ull;
+        if (p < N) {
+            const uint32_t mag = __float_as_uint(lo[p]) & 0x7fffffffu;
+            key = ((uint64_t)(~mag) << 32) | (uint32_t)p;
+        }
+        s_key[p] = key;
+    }
+    __syncthreads();
+    for (int size = 2; size <= a.P; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int p = tid; p < a.P / 2; p += kThreads) {
+                // element pair (lo_idx, hi_idx) of this compare step
+                const int lo_idx = 2 * p - (p & (stride - 1));
+                const int hi_idx = lo_idx + stride;
+                const bool up = (lo_idx & size) == 0;
+                const uint64_t x = s_key[lo_idx], y = s_key[hi_idx];
+                if ((x > y) == up) {
+                    s_key[lo_idx] = y;
+                    s_key[hi_idx] = x;
+                }
+            }
+            __syncthreads();
+        }
+    }
+
+    // suffix sums of squares over the sorted order: thread tid owns sorted
+    // positions [tid * c, tid * c + c); R_k > T^2 exactly for k < k*, so k*
+    // is the number of positions with R_k > T^2
+    const int c = (N + kThreads - 1) / kThreads;
+    const int q0 = tid * c;
+    double mine = 0.0;
+    float mg[kLnPerThread];
+#pragma unroll
+    for (int u = 0; u < kLnPerThread; ++u) {
+        mg[u] = 0.0f;
+        if (u < c && q0 + u < N) {
+            mg[u] = __uint_as_float(~(uint32_t)(s_key[q0 + u] >> 32));
+            mine += (double)mg[u] * (double)mg[u];
+        }
+    }
+    // exclusive suffix of the thread totals (threads above tid)
+    __shared__ double s_tot[kThreads];
+    s_tot[tid] = mine;
+    __syncthreads();
+    double above = 0.0;
+    for (int t = tid + 1; t < kThreads; ++t)
+        above += s_tot[t];
+    // R_k = above + (my squares from k on), summed upwards from my last
+    // position: every partial sum is of nonnegative terms (no cancellation)
+    uint32_t nbig = 0;   // positions k in my range with R_k > T^2
+    double suf = 0.0;
+#pragma unroll
+    for (int u = kLnPerThread - 1; u >= 0; --u) {
+        if (u < c && q0 + u < N) {
+            suf += (double)mg[u] * (double)mg[u];
+            nbig += above + suf > T2 ? 1u : 0u;
+        }
+    }
+    nbig = (uint32_t)wave_sum_int((int)nbig);
+    __syncthreads();
+    if (lane == 0)
+        s_cnt[wave] = nbig;
+    __syncthreads();
+    const int kstar = (int)(s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3]);
+
+    // selection flags (reuse the key array as a byte map after a barrier)
+    int selj[kLnPerThread];
+#pragma unroll
+    for (int u = 0; u < kLnPerThread; ++u)
+        selj[u] = (u < c && q0 + u < kstar) ? (int)(uint32_t)s_key[q0 + u] : -1;
+    __syncthreads();
+    uint8_t *s_sel = reinterpret_cast<uint8_t *>(s_key);
+    for (int j = tid; j < N; j += kThreads)
+        s_sel[j] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kLnPerThread; ++u)
+        if (selj[u] >= 0)
+            s_sel[selj[u]] = 1;
+    __syncthreads();
+
+    // y^mix and the three layer norms (mix, ref, lo) in double
+    double sm = 0.0, sr = 0.0;
+    for (int j = tid; j < N; j += kThreads) {
+        sm += (double)(s_sel[j] ? rf[j] : lo[j]);
+        sr += (double)rf[j];
+    }
+    const double m_mix = block_sum_d(sm, s_red) / N;
+    const double m_ref = block_sum_d(sr, s_red) / N;
+    double vm = 0.0, vr = 0.0;
+    for (int j = tid; j < N; j += kThreads) {
+        const double dm = (double)(s_sel[j] ? rf[j] : lo[j]) - m_mix;
+        const double dr = (double)rf[j] - m_ref;
+        vm += dm * dm;
+        vr += dr * dr;
+    }
+    const double r_mix = 1.0 / sqrt(block_sum_d(vm, s_red) / N + a.eps);
+    const double r_ref = 1.0 / sqrt(block_sum_d(vr, s_red) / N + a.eps);
+    const double r_lo = 1.0 / sqrt(v_lo + a.eps);
+    double em = 0.0, el = 0.0;
+    for (int j = tid; j < N; j += kThreads) {
+        const bool s = s_sel[j] != 0;
+        const float ym = s ? rf[j] : lo[j];
+        const double g = (double)a.gamma[j], b = (double)a.beta[j];
+        const double o_mix = g * (((double)ym - m_mix) * r_mix) + b;
+        const double o_ref = g * (((double)rf[j] - m_ref) * r_ref) + b;
+        const double o_lo = g * (((double)lo[j] - m_lo) * r_lo) + b;
+        a.out[(size_t)i * N + j] = (float)o_mix;
+        if (a.ymix)
+            a.ymix[(size_t)i * N + j] = ym;
+        em += (o_mix - o_ref) * (o_mix - o_ref);
+        el += (o_lo - o_ref) * (o_lo - o_ref);
+    }
+    em = block_sum_d(em, s_red);
+    el = block_sum_d(el, s_red);
+    if (a.mask) {
+        for (int w = tid; w < a.W; w += kThreads) {
+            uint32_t word = 0;
+            for (int b = 0; b < 32; ++b) {
+                const int j = 32 * w + b;
+                if (j < N && s_sel[j])
+                    word |= 1u << b;
+            }
+            a.mask[(size_t)i * a.W + w] = word;
+        }
+    }
+    if (tid == 0) {
+        if (a.row_count)
+            a.row_count[i] = (uint32_t)kstar;
+        if (a.err)
+            a.err[i] = sqrt(em);
+        if (a.errl)
+            a.errl[i] = sqrt(el);
+    }
+}
+
+// ---------------------------------------------------------------------------
+static PsConst gemm_ps_const(int mu)
+{
+    PsConst c = make_ps_const(mu, 1);   // s = 1/sqrt(1) = 1: no scale
+    return c;
+}
+
+hipError_t launch_mlp(const MlpProblem &p, const MlpBuffers &b, hipStream_t st,
+                      void **stage_events)
+{
+    auto rec = [&](int e) {
+        return stage_events ? hipEventRecord((hipEvent_t)stage_events[e], st) : hipSuccess;
+    };
+    const int tiles_m = (p.M + kTile - 1) / kTile, tiles_n = (p.N + kTile - 1) / kTile;
+    hipError_t e;
+    if ((e = rec(2 * 0)) != hipSuccess)   // scan stage
+        return e;
+    if ((e = launch_zero(b.unsafe, sizeof(uint32_t) * (size_t)(tiles_m + tiles_n), st)) !=
+        hipSuccess)
+        return e;
+    const unsigned spans = (unsigned)(((size_t)kTile * p.K + kScanSpan - 1) / kScanSpan);
+    hipLaunchKernelGGL(gemm_scan_kernel, dim3(tiles_m, spans), dim3(kThreads), 0, st, p.x, p.M,
+                       p.K, b.unsafe);
+    hipLaunchKernelGGL(gemm_scan_kernel, dim3(tiles_n, spans), dim3(kThreads), 0, st, p.w, p.N,
+                       p.K, b.unsafe + tiles_m);
+    if ((e = hipGetLastError()) != hipSuccess || (e = rec(2 * 0 + 1)) != hipSuccess)
+        return e;
+    GemmArgs a;
+    a.x = p.x;
+    a.w = p.w;
+    a.M = p.M;
+    a.N = p.N;
+    a.K = p.K;
+    a.tiles_n = tiles_n;
+    a.W = (p.N + 31) / 32;
+    a.pc = gemm_ps_const(p.mu);
+    a.unsafe_x = b.unsafe;
+    a.unsafe_w = b.unsafe + tiles_m;
+    a.ylo = b.ylo;
+    a.yref = b.yref;
+    a.out = b.out;
+    a.mask = b.mask;
+    a.err_part = b.err_part;
+    a.errl_part = b.errl_part;
+    a.tau = (double)p.tau;
+    a.exact_tiles = b.exact_tiles;
+    a.n_tiles = (long long)tiles_m * tiles_n;
+    if (a.n_tiles > 0x7fffffffLL)
+        return hipErrorInvalidValue;
+    const dim3 block(kThreads);
+    const unsigned gfast = (unsigned)a.n_tiles;
+    const unsigned ggen = (unsigned)(a.n_tiles < 2048 ? a.n_tiles : 2048);
+    const bool gelu = p.op == MLP_GELU;
+    if ((e = rec(2 * 6)) != hipSuccess)   // exact stage
+        return e;
+    if (gelu)
+        hipLaunchKernelGGL((ps_gemm_kernel<false, EPI_GELU>), dim3(ggen), block, 0, st, a);
+    else
+        hipLaunchKernelGGL((ps_gemm_kernel<false, EPI_STORE>), dim3(ggen), block, 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess || (e = rec(2 * 6 + 1)) != hipSuccess ||
+        (e = rec(2 * 1)) != hipSuccess)
+        return e;
+    if (p.mu <= 10) {
+        if (gelu)
+            hipLaunchKernelGGL((ps_gemm_kernel<true, EPI_GELU>), dim3(gfast), block, 0, st, a);
+        else
+            hipLaunchKernelGGL((ps_gemm_kernel<true, EPI_STORE>), dim3(gfast), block, 0, st, a);
+    }
+    if ((e = hipGetLastError()) != hipSuccess || (e = rec(2 * 1 + 1)) != hipSuccess ||
+        (e = rec(2 * 4)) != hipSuccess)
+        return e;
+    if (gelu) {
+        hipLaunchKernelGGL(row_reduce_kernel, dim3((p.M + kThreads - 1) / kThreads), block, 0, st,
+                           b.err_part, b.errl_part, p.M, tiles_n, b.err, b.errl);
+    } else if (p.op == MLP_LAYERNORM) {
+        LnArgs l;
+        l.ylo = b.ylo;
+        l.yref = b.yref;
+        l.gamma = p.gamma;
+        l.beta = p.beta;
+        l.M = p.M;
+        l.N = p.N;
+        l.W = (p.N + 31) / 32;
+        int P = 1;
+        while (P < p.N)
+            P <<= 1;
+        l.P = P;
+        l.eps = (double)p.eps;
+        l.tau = (double)p.tau;
+        l.out = b.out;
+        l.ymix = b.ymix;
+        l.mask = b.mask;
+        l.row_count = b.row_count;
+        l.err = b.err;
+        l.errl = b.errl;
+        hipLaunchKernelGGL(ln_lamp_kernel, dim3(p.M), block, sizeof(uint64_t) * (size_t)P, st, l);
+    }
+    if ((e = hipGetLastError()) != hipSuccess)
+        return e;
+    return rec(2 * 4 + 1);
+}
+
+// Row counts of the GELU rule from its mask words.
+__global__ __launch_bounds__(kThreads) void mask_count_kernel(const uint32_t *mask, int M, int W,
+                                                              uint32_t *count)
+{
+    const int i = blockIdx.x * kThreads + threadIdx.x;
+    if (i >= M)
+        return;
+    uint32_t c = 0;
+    for (int w = 0; w < W; ++w)
+        c += (uint32_t)__popc(mask[(size_t)i * W + w]);
+    count[i] = c;
+}
+
+hipError_t launch_mask_count(const uint32_t *mask, int M, int N, uint32_t *count, hipStream_t st)
+{
+    hipLaunchKernelGGL(mask_count_kernel, dim3((M + kThreads - 1) / kThreads), dim3(kThreads), 0,
+                       st, mask, M, (N + 31) / 32, count);
+    return hipGetLastError();
+}
+
+}  // namespace lamp

@@ -64,7 +64,7 @@ __device__ __forceinline__ void relaxed_tile_scores(TileSmem &sm, const RelaxedA
                                                     int col0, float lo[4][4], float ref[4][4])
 {
     TileAcc acc;
-    score_tile<PATH>(sm, acc, Qh, Kh, row0, col0, a.S, a.D, a.pc);
+    score_tile<PATH>(sm, acc, Qh, Kh, row0, col0, a.S, a.S, a.D, a.pc);
     tile_scores<PATH>(acc, a.pc, lo, ref);
 }
 

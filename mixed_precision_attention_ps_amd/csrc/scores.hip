@@ -93,7 +93,8 @@ __device__ __forceinline__ void score_tile_store(TileSmem &sm, const double *s_e
 {
     const size_t head = (size_t)bh * a.S * a.D;
     TileAcc acc;
-    score_tile<PATH>(sm, acc, a.q + head, a.k + head, ti * kTile, tj * kTile, a.S, a.D, a.pc);
+    score_tile<PATH>(sm, acc, a.q + head, a.k + head, ti * kTile, tj * kTile, a.S, a.S, a.D,
+                     a.pc);
     float lo[4][4], ref[4][4];
     tile_scores<PATH>(acc, a.pc, lo, ref);
     const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;

@@ -12,6 +12,11 @@ power-of-two ``qk_std`` (exact); then ``n_outlier`` channel indices drawn with
 ``rng.choice(D, n_outlier, replace=False)`` and sorted; the same channels of
 Q and K (all batches and heads) are multiplied by ``outlier_factor``.  Scaled
 outlier channels in both Q and K make the softmax rows peaked.
+
+Matrix-product inputs (``make_mlp``): X [M, K] float32 standard normals (the
+normalised activations entering a projection), then W [N, K] standard normals
+times ``w_std`` rounded to float32 (GPT-2's initialisation uses 0.02), then
+gamma = 1 + 0.1 N(0, 1) and beta = 0.1 N(0, 1) of length N.
 """
 from __future__ import annotations
 
@@ -34,6 +39,22 @@ def make_qkv(B: int, H: int, S: int, D: int, *, n_outlier: int = 0,
         Q[..., idx] *= np.float32(outlier_factor)
         K[..., idx] *= np.float32(outlier_factor)
     return Q, K, V, idx
+
+
+def make_mlp(M: int, N: int, K: int, *, w_std: float = 0.02, seed: int = 0):
+    """Return (X, W, gamma, beta) as contiguous float32 arrays."""
+    rng = np.random.default_rng(seed)
+    X = rng.standard_normal((M, K), dtype=np.float32)
+    W = (rng.standard_normal((N, K), dtype=np.float32) * np.float32(w_std)).astype(np.float32)
+    gamma = (1.0 + 0.1 * rng.standard_normal(N)).astype(np.float32)
+    beta = (0.1 * rng.standard_normal(N)).astype(np.float32)
+    return X, W, gamma, beta
+
+
+def make_special_matrix(rows: int, K: int, *, kind: str, seed: int = 0):
+    """One [rows, K] operand outside the normal range, as ``make_special``'s Q."""
+    Q, _, _ = make_special(1, 1, rows, K, kind=kind, seed=seed)
+    return np.ascontiguousarray(Q[0, 0])
 
 
 def make_special(B: int, H: int, S: int, D: int, *, kind: str, seed: int = 0):

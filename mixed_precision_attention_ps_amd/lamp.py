@@ -80,6 +80,16 @@ def library():
                                     ctypes.POINTER(LampStats), ctypes.POINTER(LampParams)]
     lib.lamp_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.lamp_decode_workspace_bytes.argtypes = [I, I, I, I, I]
+    lib.lamp_gelu_fwd.restype = I
+    lib.lamp_gelu_fwd.argtypes = [P, P, I, I, I, I, F, P, P, ctypes.POINTER(LampStats),
+                                  ctypes.POINTER(LampParams)]
+    lib.lamp_layernorm_fwd.restype = I
+    lib.lamp_layernorm_fwd.argtypes = [P, P, P, P, I, I, I, I, F, F, P, P,
+                                       ctypes.POINTER(LampStats), ctypes.POINTER(LampParams)]
+    lib.lamp_mlp_workspace_bytes.restype = ctypes.c_size_t
+    lib.lamp_mlp_workspace_bytes.argtypes = [I, I, I, I]
+    lib.lamp_gemm_scores.restype = I
+    lib.lamp_gemm_scores.argtypes = [P, P, I, I, I, I, P, P, P]
     _lib = lib
     return lib
 
@@ -210,6 +220,97 @@ def lamp_decode_fwd(q, k, v, *, causal: bool, mu: int, tau: float, out=None, pro
         _f32(q, "q"), _f32(k, "k"), _f32(v, "v"), B, H, Nq, S, D, int(causal), int(mu),
         ctypes.c_float(tau), _f32(out, "out"),
         None if probs is None else _f32(probs, "probs"), mask_ptr,
+        ctypes.byref(st) if st is not None else None, ctypes.byref(p)))
+    return out, (st.as_dict() if st is not None else None)
+
+
+MLP_OPS = {"gelu": 1, "layernorm": 2}
+
+
+def _mlp_params(device, workspace, stage_events, **opt):
+    p = LampParams()
+    p.stream = torch.cuda.current_stream(device).cuda_stream
+    if workspace is not None:
+        p.workspace = workspace.data_ptr()
+        p.workspace_bytes = workspace.numel() * workspace.element_size()
+    for name, t in opt.items():
+        if t is not None:
+            setattr(p, name, _ptr(t).value)
+    if stage_events is not None:
+        p.stage_events = stage_events.address
+    return p
+
+
+def _mask_ptr(mask):
+    if mask is None:
+        return None
+    if mask.dtype not in (torch.int32, torch.uint32):
+        raise TypeError("recompute_mask must be a 32-bit integer tensor")
+    return _ptr(mask)
+
+
+def _mlp_shapes(x, w):
+    if x.dim() != 2 or w.dim() != 2 or x.shape[1] != w.shape[1]:
+        raise ValueError("x must be [M, K] and w [N, K]")
+    return x.shape[0], w.shape[0], x.shape[1]
+
+
+def lamp_mlp_workspace_bytes(M, N, K, op) -> int:
+    return int(library().lamp_mlp_workspace_bytes(M, N, K, MLP_OPS.get(op, op)))
+
+
+def lamp_gemm_scores(x, w, *, mu: int, ylo=None, yref=None):
+    """The PS(mu) and FP32 products of x [M, K] and w [N, K] into [M, N]."""
+    M, N, K = _mlp_shapes(x, w)
+    if ylo is None and yref is None:
+        ylo = torch.empty((M, N), device=x.device, dtype=torch.float32)
+        yref = torch.empty_like(ylo)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(x.device).cuda_stream)
+    _check(library().lamp_gemm_scores(_f32(x, "x"), _f32(w, "w"), M, N, K, int(mu), _ptr(ylo),
+                                      _ptr(yref), stream))
+    return ylo, yref
+
+
+def lamp_gelu_fwd(x, w, *, mu: int, tau: float, out=None, recompute_mask=None,
+                  want_stats: bool = True, row_err=None, row_err_lowp=None, row_count=None,
+                  scores_mix=None, scores_ref=None, workspace=None, stage_events=None):
+    """GELU(x w^T) with the activation LAMP rule through lamp_gelu_fwd.
+
+    row_err / row_err_lowp (float64 [M]) receive the l1 distances of the LAMP
+    and all-PS(mu) outputs to the FP32 one.  Returns (out, stats_or_None).
+    """
+    M, N, K = _mlp_shapes(x, w)
+    if out is None:
+        out = torch.empty((M, N), device=x.device, dtype=torch.float32)
+    p = _mlp_params(x.device, workspace, stage_events, row_kl=row_err, row_kl_lowp=row_err_lowp,
+                    row_count=row_count, scores_mix=scores_mix, scores_ref=scores_ref)
+    st = LampStats() if want_stats else None
+    _check(library().lamp_gelu_fwd(
+        _f32(x, "x"), _f32(w, "w"), M, N, K, int(mu), ctypes.c_float(tau), _f32(out, "out"),
+        _mask_ptr(recompute_mask), ctypes.byref(st) if st is not None else None, ctypes.byref(p)))
+    return out, (st.as_dict() if st is not None else None)
+
+
+def lamp_layernorm_fwd(x, w, gamma, beta, *, mu: int, eps: float, tau: float, out=None,
+                       recompute_mask=None, want_stats: bool = True, row_err=None,
+                       row_err_lowp=None, row_count=None, scores_mix=None, scores_ref=None,
+                       workspace=None, stage_events=None):
+    """LayerNorm(x w^T) with the greedy LAMP rule through lamp_layernorm_fwd.
+
+    row_err / row_err_lowp (float64 [M]) receive the l2 distances of the LAMP
+    and all-PS(mu) outputs to the FP32 one.  Returns (out, stats_or_None).
+    """
+    M, N, K = _mlp_shapes(x, w)
+    if tuple(gamma.shape) != (N,) or tuple(beta.shape) != (N,):
+        raise ValueError("gamma and beta must be [N]")
+    if out is None:
+        out = torch.empty((M, N), device=x.device, dtype=torch.float32)
+    p = _mlp_params(x.device, workspace, stage_events, row_kl=row_err, row_kl_lowp=row_err_lowp,
+                    row_count=row_count, scores_mix=scores_mix, scores_ref=scores_ref)
+    st = LampStats() if want_stats else None
+    _check(library().lamp_layernorm_fwd(
+        _f32(x, "x"), _f32(w, "w"), _f32(gamma, "gamma"), _f32(beta, "beta"), M, N, K, int(mu),
+        ctypes.c_float(eps), ctypes.c_float(tau), _f32(out, "out"), _mask_ptr(recompute_mask),
         ctypes.byref(st) if st is not None else None, ctypes.byref(p)))
     return out, (st.as_dict() if st is not None else None)
 

@@ -5,10 +5,14 @@ the seeded input generator are used.  For each workload and mode the oracle's
 criterion values (strict: 2 z (1 - z) |y^lo|; relaxed: 2 exp(y^lo - m_t)
 |y^lo|) are collected over a sample of heads (and rows), and tau is the FP32
 value at which the fraction of valid scores whose criterion exceeds tau is the
-target rate.  The thresholds are inputs of the benchmark; the rate a run
-actually reaches is measured by that run.
+target rate.  After a matrix product the GELU criterion |GELU'(y) y| is
+collected the same way; the layer-normalisation rule has no per-element
+criterion, so its tau is found by bisection on the oracle's row counts.  The
+thresholds are inputs of the benchmark; the rate a run actually reaches is
+measured by that run.
 
-Usage: python oracle/calibrate_tau.py
+Usage: python oracle/calibrate_tau.py [workload ...]   (default: all; named
+workloads are recalibrated and merged into the existing table)
 """
 from __future__ import annotations
 
@@ -23,7 +27,7 @@ ROOT = os.path.dirname(HERE)
 sys.path.insert(0, ROOT)
 
 import oracle  # noqa: E402
-from mixed_precision_attention_ps_amd.configs import WORKLOADS  # noqa: E402
+from mixed_precision_attention_ps_amd.configs import MLP_WORKLOADS, WORKLOADS  # noqa: E402
 
 OUT = os.path.join(ROOT, "mixed_precision_attention_ps_amd", "tau_table.json")
 RATES = (0.003, 0.016, 0.076)
@@ -51,8 +55,54 @@ def collect(w, mode, mu, heads, row_ranges):
     return np.concatenate([p.ravel() for p in parts])
 
 
+MLP_SAMPLE_ROWS = list(range(0, 1024, 32))
+
+
+def calibrate_mlp(table, name):
+    w = MLP_WORKLOADS[name]
+    X, W, gamma, beta = w.inputs()
+    ylo, yref = oracle.ps_gemm(X[MLP_SAMPLE_ROWS], W, mu=4)
+    sample = f"rows {MLP_SAMPLE_ROWS[0]}..{MLP_SAMPLE_ROWS[-1]} step 32, all columns"
+    rate = 0.016
+    if w.op == "gelu":
+        crit = oracle.gelu_lamp(ylo, yref, tau=np.inf)["crit"].ravel()
+        tau = tau_for_rate(crit, rate)
+        got = float((crit > np.float32(tau)).mean())
+    else:
+        # the rate falls as tau grows: bisect over float32 values of tau
+        def frac(t):
+            return oracle.ln_lamp(ylo, yref, gamma, beta, eps=w.eps, tau=t)["count"].sum() / ylo.size
+        lo, hi = 0.0, 4.0
+        for _ in range(60):
+            mid = float(np.float32(0.5 * (lo + hi)))
+            if mid in (lo, hi):
+                break
+            if frac(mid) > rate:
+                lo = mid
+            else:
+                hi = mid
+        tau = hi
+        got = float(frac(tau))
+    table[f"{w.name}/{w.op}/mu4/rate{rate}"] = {"tau": tau, "sample_rate": got, "sample": sample}
+    print(w.name, w.op, tau, got, flush=True)
+
+
 def main():
+    names = sys.argv[1:]
+    if names:
+        with open(OUT) as f:
+            table = json.load(f)
+        for n in names:
+            if n not in MLP_WORKLOADS:
+                raise SystemExit(f"only the matrix-product workloads can be recalibrated alone: {n}")
+            calibrate_mlp(table, n)
+        with open(OUT, "w") as f:
+            json.dump(table, f, indent=1, sort_keys=True)
+        print("wrote", OUT)
+        return
     table = {}
+    for n in MLP_WORKLOADS:
+        calibrate_mlp(table, n)
     w = WORKLOADS["gpt2_xl_layer"]
     heads = [0, 33, 66, 99, 133, 166, 199]
     for mode_name, mode in (("strict", oracle.STRICT), ("relaxed", oracle.RELAXED)):

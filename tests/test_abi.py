@@ -33,6 +33,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ("lamp_attention_fwd", "lamp_attention_fwd_ex", "lamp_workspace_bytes",
                  "lamp_ps_scores", "lamp_decode_fwd", "lamp_decode_workspace_bytes",
+                 "lamp_gelu_fwd", "lamp_layernorm_fwd", "lamp_mlp_workspace_bytes",
+                 "lamp_gemm_scores",
                  "lamp_strerror", "lamp_last_error", "lamp_version"):
         assert want in names
 
@@ -122,6 +124,55 @@ def test_decode_workspace_bytes(lib):
     ws = lib.lamp_decode_workspace_bytes(8, 25, 4, 16384, 64)
     # y^lo and y^ref per score, the P.V partials (one per 256-key chunk)
     assert ws >= 8 * 8 * 25 * 4 * 16384 + 8 * 8 * 25 * 64 * 4 * 64
+
+
+def gcall(lib, x=A, w=A, M=4, N=8, K=64, mu=4, tau=0.1, out=A):
+    return lib.lamp_gelu_fwd(x, w, M, N, K, mu, ctypes.c_float(tau), out, None, None, None)
+
+
+def lcall(lib, x=A, w=A, g=A, b=A, M=4, N=8, K=64, mu=4, eps=1e-5, tau=0.1, out=A):
+    return lib.lamp_layernorm_fwd(x, w, g, b, M, N, K, mu, ctypes.c_float(eps),
+                                  ctypes.c_float(tau), out, None, None, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), -1), (dict(w=None), -1), (dict(out=None), -1), (dict(x=A + 4), -1),
+    (dict(M=0), -1), (dict(N=0), -1), (dict(K=0), -1), (dict(K=6), -2),
+    (dict(mu=0), -1), (dict(mu=24), -1), (dict(tau=float("nan")), -1), (dict(tau=-0.5), -1),
+    (dict(M=1 << 30, N=1 << 30), -2), (dict(M=1, K=1 << 26), -2),
+])
+def test_gelu_arguments_rejected_before_any_device_call(lib, kw, code):
+    assert gcall(lib, **kw) == code
+    assert lib.lamp_last_error()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(g=None), -1), (dict(b=None), -1), (dict(eps=-1.0), -1), (dict(eps=float("nan")), -1),
+    (dict(N=8193), -2), (dict(K=10), -2), (dict(mu=30), -1), (dict(M=0), -1),
+])
+def test_layernorm_arguments_rejected_before_any_device_call(lib, kw, code):
+    assert lcall(lib, **kw) == code
+    assert lib.lamp_last_error()
+
+
+def test_gemm_scores_argument_checks(lib):
+    assert lib.lamp_gemm_scores(A, A, 4, 8, 64, 4, None, None, None) == -1
+    assert lib.lamp_gemm_scores(None, A, 4, 8, 64, 4, A, None, None) == -1
+    assert lib.lamp_gemm_scores(A, A, 4, 8, 62, 4, A, None, None) == -2
+    assert lib.lamp_gemm_scores(A, A, 4, 8, 64, 0, A, None, None) == -1
+
+
+def test_mlp_workspace_bytes(lib):
+    assert lib.lamp_mlp_workspace_bytes(0, 8, 64, 1) == 0
+    assert lib.lamp_mlp_workspace_bytes(4, 8, 64, 0) == 0
+    assert lib.lamp_mlp_workspace_bytes(4, 9000, 64, 2) == 0
+    M, N = 1024, 6400
+    gelu = lib.lamp_mlp_workspace_bytes(M, N, 1600, 1)
+    # per-(row, 64-column tile) error partials, the mask, per-row outputs
+    assert gelu >= 16 * M * (N // 64) + 4 * M * (N // 32) + 20 * M
+    ln = lib.lamp_mlp_workspace_bytes(M, 1600, 6400, 2)
+    # y^lo and y^ref of the whole product
+    assert ln >= 8 * M * 1600
 
 
 def test_version_and_strerror(lib):
