@@ -64,6 +64,8 @@ def _load():
     lib.orc_scale.argtypes = [ctypes.c_int]
     lib.orc_ps_dot.restype = ctypes.c_double
     lib.orc_ps_dot.argtypes = [P, P, ctypes.c_int, ctypes.c_int]
+    lib.orc_ps_dot_blocked.restype = ctypes.c_double
+    lib.orc_ps_dot_blocked.argtypes = [P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int]
     lib.orc_seq32_dot.restype = ctypes.c_float
     lib.orc_seq32_dot.argtypes = [P, P, ctypes.c_int]
     lib.orc_splitmix64.restype = ctypes.c_uint64
@@ -71,11 +73,11 @@ def _load():
     lib.orc_max_threads.restype = ctypes.c_int
     lib.orc_max_threads.argtypes = []
     lib.orc_lamp_rows.restype = ctypes.c_int
-    lib.orc_lamp_rows.argtypes = ([P, P, P] + [ctypes.c_int] * 4 + [ctypes.c_float]
+    lib.orc_lamp_rows.argtypes = ([P, P, P] + [ctypes.c_int] * 5 + [ctypes.c_float]
                                   + [ctypes.c_int] * 2 + [ctypes.c_uint64] * 2
                                   + [ctypes.c_int] * 3 + [P] * 9)
     lib.orc_ps_gemm.restype = ctypes.c_int
-    lib.orc_ps_gemm.argtypes = [P, P] + [ctypes.c_int] * 5 + [P, P]
+    lib.orc_ps_gemm.argtypes = [P, P] + [ctypes.c_int] * 6 + [P, P]
     lib.orc_gelu.restype = ctypes.c_double
     lib.orc_gelu.argtypes = [ctypes.c_double]
     lib.orc_gelu_grad.restype = ctypes.c_double
@@ -116,6 +118,15 @@ def ps_dot(q, k, mu: int) -> float:
     return _load().orc_ps_dot(_ptr(q), _ptr(k), q.size, int(mu))
 
 
+def ps_dot_blocked(q, k, mu: int, block: int) -> float:
+    """PS(mu) dot in the blocked order: runs of `block` products summed from
+    +0, each run's sum added to the running accumulator."""
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    k = np.ascontiguousarray(k, dtype=np.float32)
+    assert q.shape == k.shape and q.ndim == 1
+    return _load().orc_ps_dot_blocked(_ptr(q), _ptr(k), q.size, int(mu), int(block))
+
+
 def seq32_dot(q, k) -> np.float32:
     q = np.ascontiguousarray(q, dtype=np.float32)
     k = np.ascontiguousarray(k, dtype=np.float32)
@@ -133,9 +144,10 @@ def max_threads() -> int:
 
 def lamp_rows(qh, kh, vh, *, causal: bool, mu: int, tau: float, mode: int,
               seed: int = 0, head_lin: int = 0, row_begin: int = 0, row_end=None,
-              block_k: int = 64, threads: int = 0,
+              block_k: int = 64, ps_block: int = 0, threads: int = 0,
               want=("ylo", "yref", "crit", "mask", "probs", "out", "kl", "kl_lowp", "count")):
-    """Rows [row_begin, row_end) of one head.  qh, kh, vh: float32 [S, D]."""
+    """Rows [row_begin, row_end) of one head.  qh, kh, vh: float32 [S, D].
+    ps_block: PS(mu) accumulation order (0 or 1 sequential, else blocked)."""
     lib = _load()
     qh = np.ascontiguousarray(qh, dtype=np.float32)
     kh = np.ascontiguousarray(kh, dtype=np.float32)
@@ -152,7 +164,7 @@ def lamp_rows(qh, kh, vh, *, causal: bool, mu: int, tau: float, mode: int,
               "count": ((n,), np.int32)}
     res = {name: np.zeros(*shapes[name]) for name in want}
     rc = lib.orc_lamp_rows(_ptr(qh), _ptr(kh), _ptr(vh), S, D, int(bool(causal)), int(mu),
-                           ctypes.c_float(np.float32(tau)), int(mode), int(block_k),
+                           int(ps_block), ctypes.c_float(np.float32(tau)), int(mode), int(block_k),
                            ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF),
                            ctypes.c_uint64(head_lin), int(row_begin), int(row_end), int(threads),
                            *[_ptr(res.get(k)) for k in ("ylo", "yref", "crit", "mask", "probs",
@@ -163,7 +175,8 @@ def lamp_rows(qh, kh, vh, *, causal: bool, mu: int, tau: float, mode: int,
 
 
 def lamp_heads(Q, K, V, *, causal: bool, mu: int, tau: float, mode: int, heads=None,
-               rows=None, seed: int = 0, block_k: int = 64, threads: int = 0, want=None):
+               rows=None, seed: int = 0, block_k: int = 64, ps_block: int = 0,
+               threads: int = 0, want=None):
     """Selected heads of a [B, H, S, D] problem.
 
     heads: iterable of linear head indices b*H + h (default: all).
@@ -179,7 +192,7 @@ def lamp_heads(Q, K, V, *, causal: bool, mu: int, tau: float, mode: int, heads=N
     for hl in heads:
         parts.append(lamp_rows(Qf[hl], Kf[hl], Vf[hl], causal=causal, mu=mu, tau=tau,
                                mode=mode, seed=seed, head_lin=hl, row_begin=rb, row_end=re_,
-                               block_k=block_k, threads=threads, **kw))
+                               block_k=block_k, ps_block=ps_block, threads=threads, **kw))
     return {k: np.stack([p[k] for p in parts]) for k in parts[0]}
 
 
@@ -187,8 +200,9 @@ def lamp_heads(Q, K, V, *, causal: bool, mu: int, tau: float, mode: int, heads=N
 # Activation (GELU) and layer-normalisation LAMP after a matrix product
 # (lamp_mlp_oracle.c).
 # ---------------------------------------------------------------------------
-def ps_gemm(X, W, *, mu: int, threads: int = 0):
-    """y = X W^T for X [M, K], W [N, K]: (y_lo PS(mu), y_ref sequential FP32)."""
+def ps_gemm(X, W, *, mu: int, ps_block: int = 0, threads: int = 0):
+    """y = X W^T for X [M, K], W [N, K]: (y_lo PS(mu), y_ref sequential FP32);
+    ps_block as for lamp_rows."""
     X = np.ascontiguousarray(X, np.float32)
     W = np.ascontiguousarray(W, np.float32)
     M, K = X.shape
@@ -196,7 +210,8 @@ def ps_gemm(X, W, *, mu: int, threads: int = 0):
     assert W.shape[1] == K
     ylo = np.empty((M, N), np.float32)
     yref = np.empty((M, N), np.float32)
-    rc = _load().orc_ps_gemm(_ptr(X), _ptr(W), M, N, K, int(mu), int(threads), _ptr(ylo),
+    rc = _load().orc_ps_gemm(_ptr(X), _ptr(W), M, N, K, int(mu), int(ps_block), int(threads),
+                             _ptr(ylo),
                              _ptr(yref))
     if rc != 0:
         raise ValueError("orc_ps_gemm: bad arguments")

@@ -51,16 +51,16 @@
 #include <omp.h>
 #endif
 
-double orc_ps_dot(const float *q, const float *k, int D, int mu);
+double orc_ps_dot_blocked(const float *q, const float *k, int D, int mu, int block);
 float orc_seq32_dot(const float *q, const float *k, int D);
 
 /* ------------------------------------------------------------------------ */
 /* y = x W^T, PS(mu) and FP32 (step 1 and the uniform reference).           */
 /* ------------------------------------------------------------------------ */
-int orc_ps_gemm(const float *x, const float *w, int M, int N, int K, int mu, int nthreads,
-                float *ylo, float *yref)
+int orc_ps_gemm(const float *x, const float *w, int M, int N, int K, int mu, int ps_block,
+                int nthreads, float *ylo, float *yref)
 {
-    if (!x || !w || M < 1 || N < 1 || K < 1 || mu < 1 || mu > 23)
+    if (!x || !w || M < 1 || N < 1 || K < 1 || mu < 1 || mu > 23 || ps_block < 0)
         return -1;
 #ifdef _OPENMP
     if (nthreads > 0)
@@ -73,7 +73,7 @@ int orc_ps_gemm(const float *x, const float *w, int M, int N, int K, int mu, int
         for (int j = 0; j < N; ++j) {
             const float *xi = x + (size_t)i * K, *wj = w + (size_t)j * K;
             if (ylo)
-                ylo[(size_t)i * N + j] = (float)orc_ps_dot(xi, wj, K, mu);
+                ylo[(size_t)i * N + j] = (float)orc_ps_dot_blocked(xi, wj, K, mu, ps_block);
             if (yref)
                 yref[(size_t)i * N + j] = orc_seq32_dot(xi, wj, K);
         }

@@ -87,6 +87,32 @@ double orc_ps_dot(const float *q, const float *k, int D, int mu)
     return acc;
 }
 
+/* Blocked ("packed") accumulation order, the order a native low-precision
+ * dot-product unit would use (LAMP summary, "Significance": the method as a
+ * blueprint for hardware with packed low-precision accumulation; the order
+ * itself is a reading, the pages give none).  Every multiply and add is still
+ * rounded to PS(mu); only the order changes: the products of each run of
+ * `block` consecutive d (the last run may be shorter) are summed from +0 in d
+ * order, and each run's sum is then added to the running accumulator, which
+ * also starts at +0.  block <= 1 (one product per run) and block >= D (one
+ * run) both give the sequential order. */
+double orc_ps_dot_blocked(const float *q, const float *k, int D, int mu, int block)
+{
+    if (block <= 1 || block >= D)
+        return orc_ps_dot(q, k, D, mu);
+    double acc = 0.0;
+    for (int d0 = 0; d0 < D; d0 += block) {
+        const int d1 = d0 + block < D ? d0 + block : D;
+        double part = 0.0;
+        for (int d = d0; d < d1; ++d) {
+            double t = (double)q[d] * (double)k[d];
+            part = orc_rn_mu(part + orc_rn_mu(t, mu), mu);
+        }
+        acc = orc_rn_mu(acc + part, mu);
+    }
+    return acc;
+}
+
 /* Uniform FP32 reference: sequential float loop, multiply then add, no
  * fused multiply-add, d ascending (built with -ffp-contract=off). */
 float orc_seq32_dot(const float *q, const float *k, int D)
@@ -100,9 +126,10 @@ float orc_seq32_dot(const float *q, const float *k, int D)
 }
 
 /* Scaled scores: one FP32 multiply by the FP32 scale after accumulation. */
-static float score_lo(const float *q, const float *k, int D, int mu, float s)
+static float score_lo(const float *q, const float *k, int D, int mu, int ps_block, float s)
 {
-    float a = (float)orc_ps_dot(q, k, D, mu);   /* exact: PS(mu) values are floats */
+    /* exact: PS(mu) values are floats */
+    float a = (float)orc_ps_dot_blocked(q, k, D, mu, ps_block);
     float y = a * s;
     return y;
 }
@@ -239,7 +266,7 @@ typedef struct {
 } row_scratch;
 
 static void lamp_row(const float *Qh, const float *Kh, const float *Vh,
-                     int S, int D, int causal, int mu, float tau, int mode,
+                     int S, int D, int causal, int mu, int ps_block, float tau, int mode,
                      int block_k, uint64_t seed, uint64_t head_lin, int i, float s,
                      row_scratch *w,
                      float *o_ylo, float *o_yref, double *o_crit, uint32_t *o_mask,
@@ -252,7 +279,7 @@ static void lamp_row(const float *Qh, const float *Kh, const float *Vh,
 
     /* Step 1: baseline scores at PS(mu); the uniform FP32 reference beside. */
     for (int j = 0; j < n; ++j) {
-        w->ylo[j] = score_lo(q, Kh + (size_t)j * D, D, mu, s);
+        w->ylo[j] = score_lo(q, Kh + (size_t)j * D, D, mu, ps_block, s);
         w->yref[j] = score_ref(q, Kh + (size_t)j * D, D, s);
     }
 
@@ -333,6 +360,8 @@ static void lamp_row(const float *Qh, const float *Kh, const float *Vh,
  * Rows [row_begin, row_end) of one attention head.
  *   qh, kh, vh : that head's [S, D] float32 blocks.
  *   head_lin   : linear (b*H + h) index, used only by the random control.
+ *   ps_block   : PS(mu) accumulation order: 0 or 1 sequential, else blocked
+ *                with runs of ps_block products (orc_ps_dot_blocked).
  * Every output may be NULL; row r is written at offset (r - row_begin):
  *   ylo, yref, probs : [rows, S] float32 (invalid keys written as 0)
  *   crit             : [rows, S] double, the mode's criterion value
@@ -344,15 +373,15 @@ static void lamp_row(const float *Qh, const float *Kh, const float *Vh,
  * Returns 0, or -1 on bad arguments.
  */
 int orc_lamp_rows(const float *qh, const float *kh, const float *vh,
-                  int S, int D, int causal, int mu, float tau, int mode, int block_k,
-                  uint64_t seed, uint64_t head_lin, int row_begin, int row_end,
+                  int S, int D, int causal, int mu, int ps_block, float tau, int mode,
+                  int block_k, uint64_t seed, uint64_t head_lin, int row_begin, int row_end,
                   int nthreads,
                   float *ylo, float *yref, double *crit, uint32_t *mask,
                   float *probs, float *out, double *kl, double *kl_lowp,
                   int32_t *count)
 {
     if (!qh || !kh || !vh || S < 1 || D < 1 || mu < 1 || mu > 23 ||
-        row_begin < 0 || row_end > S || row_begin > row_end || block_k < 1 ||
+        row_begin < 0 || row_end > S || row_begin > row_end || block_k < 1 || ps_block < 0 ||
         mode < 0 || mode > 2 || !(tau >= 0.0f))
         return -1;
     const float s = orc_scale(D);
@@ -374,7 +403,8 @@ int orc_lamp_rows(const float *qh, const float *kh, const float *vh,
 #pragma omp for schedule(dynamic, 4)
         for (int i = row_begin; i < row_end; ++i) {
             size_t r = (size_t)(i - row_begin);
-            lamp_row(qh, kh, vh, S, D, causal, mu, tau, mode, block_k, seed, head_lin, i, s, &w,
+            lamp_row(qh, kh, vh, S, D, causal, mu, ps_block, tau, mode, block_k, seed, head_lin, i,
+                     s, &w,
                      ylo ? ylo + r * S : NULL, yref ? yref + r * S : NULL,
                      crit ? crit + r * S : NULL, mask ? mask + r * words : NULL,
                      probs ? probs + r * S : NULL, out ? out + r * D : NULL,
