@@ -99,6 +99,18 @@ typedef struct {
                                  the caller; event 2s / 2s+1 are recorded on
                                  the stream before / after stage s when that
                                  stage runs (profiling)                       */
+    int ps_block;             /* PS(mu) accumulation order: 0 or 1 = the
+                                 sequential order (default); a power of two
+                                 b >= 4 (<= 2^24) = the blocked ("packed")
+                                 order of a native low-precision dot unit
+                                 (LAMP summary, "Significance"): the products
+                                 of each run of b consecutive terms are summed
+                                 from +0 in PS(mu), and each run's sum is added
+                                 to the running accumulator with one more
+                                 PS(mu) rounding.  Only y^lo changes; the FP32
+                                 reference and recompute stay sequential.
+                                 Other values: LAMP_ERR_INVALID_ARG (< 0) or
+                                 LAMP_ERR_UNSUPPORTED                         */
 } lamp_params;
 
 /* Stages, for lamp_params.stage_events. */

@@ -125,7 +125,9 @@ __device__ __forceinline__ void dec_stage_queries(const DecodeArgs &a, int bh, f
 // each.
 extern __shared__ float4 dec_dyn_lds[];
 
-template <int NQ>
+// BLOCKED: the blocked PS(mu) accumulation order (a.pc.blk >= 4, a power of
+// two, so runs end only after the last of a group of 4 positions).
+template <int NQ, bool BLOCKED>
 __global__ __launch_bounds__(kThreads) void decode_scores_kernel(DecodeArgs a)
 {
     constexpr int kDecSlice = dec_slice<NQ>();
@@ -153,11 +155,12 @@ __global__ __launch_bounds__(kThreads) void decode_scores_kernel(DecodeArgs a)
     };
     float4 kr[kV4];
     load_slice(0, kr);
-    float lo[NQ], ref[NQ];
+    float lo[NQ], ref[NQ], run[NQ];
 #pragma unroll
     for (int t = 0; t < NQ; ++t) {
         lo[t] = 0.0f;
         ref[t] = 0.0f;
+        run[t] = 0.0f;
     }
     for (int d0 = 0; d0 < D; d0 += kDecSlice) {
         __syncthreads();
@@ -188,12 +191,23 @@ __global__ __launch_bounds__(kThreads) void decode_scores_kernel(DecodeArgs a)
                     const float sa[4] = {sv.x, sv.y, sv.z, sv.w};
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        ps_mac_fast(qa[e], sa[e], ka[e], lo[t], ref[t], pc.sh, pc.half_m1,
-                                    pc.keep);
+                        ps_mac_fast(qa[e], sa[e], ka[e], BLOCKED ? run[t] : lo[t], ref[t], pc.sh,
+                                    pc.half_m1, pc.keep);
+                }
+            }
+            if (BLOCKED && ((d0 + dd + 4) & (pc.blk - 1)) == 0) {   // a run ends here
+#pragma unroll
+                for (int t = 0; t < NQ; ++t) {
+                    lo[t] = ps_round_bits(lo[t] + run[t], pc.sh, pc.half_m1, pc.keep);
+                    run[t] = 0.0f;
                 }
             }
         }
     }
+    if (BLOCKED)   // the last run
+#pragma unroll
+        for (int t = 0; t < NQ; ++t)
+            lo[t] = ps_round_bits(lo[t] + run[t], pc.sh, pc.half_m1, pc.keep);
     const bool ok = __syncthreads_and(safe ? 1 : 0);
     if (tid == 0)
         a.unsafe[(size_t)bh * a.n_chunks + chunk] = ok ? 0 : 1;
@@ -238,12 +252,15 @@ __global__ __launch_bounds__(kThreads) void decode_scores_exact_kernel(DecodeArg
         const int j = chunk * kDecChunk + tid;
         const int jr = j < a.S ? j : a.S - 1;   // rows past S re-read the last row
         const float4 *k4 = reinterpret_cast<const float4 *>(a.k + ((size_t)bh * a.S + jr) * D);
-        double lod[NQ];
-        float lo[NQ], ref[NQ];
+        // blocked order (pc.blk > 0): run sums rund (PS(mu)) / runf (mu = 23)
+        // added into lod / lof where a run ends
+        const bool blocked = pc.blk != 0;
+        double lod[NQ], rund[NQ];
+        float lo[NQ], ref[NQ], lof[NQ], runf[NQ];
 #pragma unroll
         for (int t = 0; t < NQ; ++t) {
-            lod[t] = 0.0;
-            ref[t] = 0.0f;
+            lod[t] = rund[t] = 0.0;
+            ref[t] = lof[t] = runf[t] = 0.0f;
         }
         for (int d4 = 0; d4 < D4; ++d4) {
             const float4 kv = k4[d4];
@@ -257,17 +274,35 @@ __global__ __launch_bounds__(kThreads) void decode_scores_exact_kernel(DecodeArg
                     for (int e = 0; e < 4; ++e) {
                         if (pc.mu < 23) {
                             const double pr = (double)qa[e] * (double)ka[e];
-                            lod[t] = ps_rn64(lod[t] + ps_rn64(pr, pc.mu), pc.mu);
+                            double &acc = blocked ? rund[t] : lod[t];
+                            acc = ps_rn64(acc + ps_rn64(pr, pc.mu), pc.mu);
                         }
                         const float p = qa[e] * ka[e];
+                        if (blocked)
+                            runf[t] = runf[t] + p;
                         ref[t] = ref[t] + p;
                     }
                 }
             }
+            if (blocked && (((d4 + 1) * 4) & (pc.blk - 1)) == 0) {
+#pragma unroll
+                for (int t = 0; t < NQ; ++t) {
+                    lod[t] = ps_rn64(lod[t] + rund[t], pc.mu);
+                    lof[t] = lof[t] + runf[t];
+                    rund[t] = 0.0;
+                    runf[t] = 0.0f;
+                }
+            }
         }
+        if (blocked)   // the last run
+#pragma unroll
+            for (int t = 0; t < NQ; ++t) {
+                lod[t] = ps_rn64(lod[t] + rund[t], pc.mu);
+                lof[t] = lof[t] + runf[t];
+            }
 #pragma unroll
         for (int t = 0; t < NQ; ++t)
-            lo[t] = pc.mu < 23 ? (float)lod[t] * pc.s : ref[t] * pc.s;
+            lo[t] = pc.mu < 23 ? (float)lod[t] * pc.s : (blocked ? lof[t] : ref[t]) * pc.s;
         dec_store_scores<NQ>(a, bh, chunk, lo, ref);
     }
 }
@@ -579,6 +614,7 @@ hipError_t launch_decode(const DecodeProblem &p, const DecodeBuffers &b, hipStre
     a.n_blk = (p.S + 63) / 64;
     a.tau = (double)p.tau;
     a.pc = make_ps_const(p.mu, p.D);
+    set_ps_block(a.pc, p.ps_block, p.D);
     a.ylo = b.ylo;
     a.yref = b.yref;
     a.bmax = b.bmax;
@@ -596,16 +632,20 @@ hipError_t launch_decode(const DecodeProblem &p, const DecodeBuffers &b, hipStre
     if ((e = rec(2 * 1)) != hipSuccess)   // scores stage
         return e;
     const size_t qlds = 2 * sizeof(float4) * (size_t)p.nq * (p.D / 4);
-#define LAMP_DEC_LAUNCH(K)                                                        \
-    do {                                                                          \
-        if (p.nq <= 1) hipLaunchKernelGGL((K<1>), grid, block, qlds, st, a);      \
-        else if (p.nq <= 2) hipLaunchKernelGGL((K<2>), grid, block, qlds, st, a); \
-        else if (p.nq <= 4) hipLaunchKernelGGL((K<4>), grid, block, qlds, st, a); \
-        else if (p.nq <= 8) hipLaunchKernelGGL((K<8>), grid, block, qlds, st, a); \
-        else hipLaunchKernelGGL((K<16>), grid, block, qlds, st, a);               \
+#define LAMP_DEC_LAUNCH(K, BLK)                                                        \
+    do {                                                                               \
+        if (p.nq <= 1) hipLaunchKernelGGL((K<1, BLK>), grid, block, qlds, st, a);      \
+        else if (p.nq <= 2) hipLaunchKernelGGL((K<2, BLK>), grid, block, qlds, st, a); \
+        else if (p.nq <= 4) hipLaunchKernelGGL((K<4, BLK>), grid, block, qlds, st, a); \
+        else if (p.nq <= 8) hipLaunchKernelGGL((K<8, BLK>), grid, block, qlds, st, a); \
+        else hipLaunchKernelGGL((K<16, BLK>), grid, block, qlds, st, a);               \
     } while (0)
-    if (p.mu <= 10)
-        LAMP_DEC_LAUNCH(decode_scores_kernel);
+    if (p.mu <= 10) {
+        if (a.pc.blk != 0)
+            LAMP_DEC_LAUNCH(decode_scores_kernel, true);
+        else
+            LAMP_DEC_LAUNCH(decode_scores_kernel, false);
+    }
     if ((e = hipGetLastError()) != hipSuccess || (e = rec(2 * 1 + 1)) != hipSuccess ||
         (e = rec(2 * 6)) != hipSuccess)   // exact stage
         return e;

@@ -271,6 +271,20 @@ DecodeLayout decode_plan(uint64_t BH, int Nq, int S, int D, bool need_ylo, bool 
     return L;
 }
 
+// The accumulation order of lamp_params.ps_block: 0, 1 or a power of two
+// in [4, 2^24].
+int check_ps_block(int b)
+{
+    if (b < 0)
+        return set_error(LAMP_ERR_INVALID_ARG, "ps_block must be >= 0");
+    if (b <= 1)
+        return LAMP_OK;
+    if (b < 4 || b > (1 << 24) || (b & (b - 1)) != 0)
+        return set_error(LAMP_ERR_UNSUPPORTED,
+                         "ps_block must be 0, 1 or a power of two in [4, 2^24]");
+    return LAMP_OK;
+}
+
 int run_decode(const float *q, const float *k, const float *v, int B, int H, int Nq, int S, int D,
                int causal, int mu, float tau, float *out, float *probs, uint32_t *mask,
                lamp_stats *stats, const lamp_params *pp)
@@ -282,9 +296,12 @@ int run_decode(const float *q, const float *k, const float *v, int B, int H, int
     rc = check_decode(B, H, Nq, S, D);
     if (rc != LAMP_OK)
         return rc;
-    (void)hipGetLastError();
     lamp_params none{};
     const lamp_params &p = pp ? *pp : none;
+    rc = check_ps_block(p.ps_block);
+    if (rc != LAMP_OK)
+        return rc;
+    (void)hipGetLastError();
     hipStream_t st = (hipStream_t)p.stream;
     const bool want_stats = stats != nullptr;
     const uint64_t BH = (uint64_t)B * (uint64_t)H;
@@ -317,6 +334,7 @@ int run_decode(const float *q, const float *k, const float *v, int B, int H, int
     P.causal = causal;
     P.mu = mu;
     P.tau = tau;
+    P.ps_block = p.ps_block;
     lamp::DecodeBuffers b;
     b.ylo = p.scores_mix ? p.scores_mix : at<float>(ws, L.ylo);
     b.yref = p.scores_ref ? p.scores_ref : at<float>(ws, L.yref);
@@ -445,9 +463,12 @@ int run_mlp(int op, const float *x, const float *w, const float *gamma, const fl
     int rc = check_mlp(M, N, K, op);
     if (rc != LAMP_OK)
         return rc;
-    (void)hipGetLastError();
     lamp_params none{};
     const lamp_params &p = pp ? *pp : none;
+    rc = check_ps_block(p.ps_block);
+    if (rc != LAMP_OK)
+        return rc;
+    (void)hipGetLastError();
     hipStream_t st = (hipStream_t)p.stream;
     const bool want_stats = stats != nullptr;
     const MlpLayout L = mlp_plan(M, N, op, true, p.scores_ref == nullptr, mask == nullptr,
@@ -478,6 +499,7 @@ int run_mlp(int op, const float *x, const float *w, const float *gamma, const fl
     P.mu = mu;
     P.op = op;
     P.tau = tau;
+    P.ps_block = p.ps_block;
     P.eps = eps;
     lamp::MlpBuffers b{};
     b.unsafe = at<uint32_t>(ws, L.unsafe);
@@ -568,8 +590,6 @@ static int run(const float *q, const float *k, const float *v, int B, int H, int
 {
     g_last_error.clear();
     int rc = check_args(q, k, v, causal, mu, tau, mode, out);
-    if (rc == LAMP_OK)
-        (void)hipGetLastError();   // launches below are checked with hipGetLastError
     if (rc != LAMP_OK)
         return rc;
     Sizes z;
@@ -582,6 +602,10 @@ static int run(const float *q, const float *k, const float *v, int B, int H, int
 
     lamp_params none{};
     const lamp_params &p = pp ? *pp : none;
+    rc = check_ps_block(p.ps_block);
+    if (rc != LAMP_OK)
+        return rc;
+    (void)hipGetLastError();   // launches below are checked with hipGetLastError
     hipStream_t st = (hipStream_t)p.stream;
     const bool want_stats = stats != nullptr;
 
@@ -629,6 +653,7 @@ static int run(const float *q, const float *k, const float *v, int B, int H, int
     P.mu = mu;
     P.tau = tau;
     P.pc = lamp::make_ps_const(mu, D);
+    lamp::set_ps_block(P.pc, p.ps_block, D);
     P.tiles = z.tiles;
     P.n_rows = z.n_rows;
     P.head_valid = z.n_valid / z.BH;

@@ -87,9 +87,12 @@ struct alignas(16) TileSmem {
 };
 
 struct TileAcc {
-    float lo[4][4];     // fast path: scaled-domain PS accumulator
+    float lo[4][4];     // fast path: scaled-domain PS accumulator (blocked FP32:
+                        // the blocked FP32 sum)
     double lod[4][4];   // exact path: PS accumulator in double
     float ref[4][4];    // sequential FP32 accumulator
+    float blk[4][4];    // blocked order: the current run's sum (fast, FP32)
+    double blkd[4][4];  // blocked order: the current run's sum (exact path)
 };
 
 __device__ __forceinline__ int key_slot(int j) { return (j & 15) * 4 + (j >> 4); }
@@ -126,10 +129,47 @@ __device__ __forceinline__ void stage_slice(TileSmem &sm, const float4 (&qv)[kSl
     }
 }
 
+// compute_slice's run width for a blocked order with runs of blk products
+// (0: sequential).
+__host__ __device__ constexpr int run_width(int blk) { return blk == 0 ? 0 : blk < 32 ? blk : 32; }
+
+// Blocked ("packed") accumulation order: the current run's sum is added to
+// the accumulator (one PS(mu) add) and restarted from +0.
 template <int PATH>
+__device__ __forceinline__ void flush_runs(TileAcc &acc, const PsConst &pc)
+{
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            if (PATH == PATH_FAST) {
+                acc.lo[r][c] = ps_round_bits(acc.lo[r][c] + acc.blk[r][c], pc.sh, pc.half_m1,
+                                             pc.keep);
+                acc.blk[r][c] = 0.0f;
+            } else if (PATH == PATH_EXACT) {
+                acc.lod[r][c] = ps_rn64(acc.lod[r][c] + acc.blkd[r][c], pc.mu);
+                acc.blkd[r][c] = 0.0;
+            } else {
+                acc.lo[r][c] = acc.lo[r][c] + acc.blk[r][c];
+                acc.blk[r][c] = 0.0f;
+            }
+        }
+}
+
+// One 32-wide slice of the head dimension.  Sequential order (P = 0): every
+// product goes into the accumulator.  Blocked order with runs of P = 4, 8 or
+// 16 products: products go into the run sum, which is flushed after every
+// P-th position (compile-time positions, no branch).  P = 32 stands for runs
+// of 32 or more products, whole slices: the caller flushes after a run's
+// last slice.  (A flush that depends on a run-time condition inside or at
+// the end of the unrolled slice makes the compiler hoist all of the slice's
+// LDS reads and spill.)
+template <int PATH, int P>
 __device__ __forceinline__ void compute_slice(const TileSmem &sm, TileAcc &acc, int tx, int ty,
                                               const PsConst &pc)
 {
+    static_assert(P == 0 || P == 4 || P == 8 || P == 16 || P == 32, "run width");
+    constexpr bool BLOCKED = P != 0;
 #pragma unroll
     for (int dd = 0; dd < kDChunk; ++dd) {
         const float4 qv = *reinterpret_cast<const float4 *>(&sm.q[dd][ty * 4]);
@@ -143,15 +183,16 @@ __device__ __forceinline__ void compute_slice(const TileSmem &sm, TileAcc &acc, 
             for (int r = 0; r < 4; ++r)
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
-                    ps_mac_fast(qa[r], sa[r], ka[c], acc.lo[r][c], acc.ref[r][c], pc.sh,
-                                pc.half_m1, pc.keep);
+                    ps_mac_fast(qa[r], sa[r], ka[c], BLOCKED ? acc.blk[r][c] : acc.lo[r][c],
+                                acc.ref[r][c], pc.sh, pc.half_m1, pc.keep);
         } else if (PATH == PATH_EXACT) {
 #pragma unroll
             for (int r = 0; r < 4; ++r)
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     double t = (double)qa[r] * (double)ka[c];
-                    acc.lod[r][c] = ps_rn64(acc.lod[r][c] + ps_rn64(t, pc.mu), pc.mu);
+                    double &a = BLOCKED ? acc.blkd[r][c] : acc.lod[r][c];
+                    a = ps_rn64(a + ps_rn64(t, pc.mu), pc.mu);
                     float p = qa[r] * ka[c];
                     acc.ref[r][c] = acc.ref[r][c] + p;
                 }
@@ -161,19 +202,26 @@ __device__ __forceinline__ void compute_slice(const TileSmem &sm, TileAcc &acc, 
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     float p = qa[r] * ka[c];
+                    if (BLOCKED)
+                        acc.blk[r][c] = acc.blk[r][c] + p;
                     acc.ref[r][c] = acc.ref[r][c] + p;
                 }
         }
+        if (BLOCKED && P < kDChunk && dd % (P ? P : 1) == (P ? P : 1) - 1)
+            flush_runs<PATH>(acc, pc);
     }
 }
 
 // Full-D accumulation of one 64x64 tile: rows row0.. of Qh (nq rows), keys
 // col0.. of Kh (nk rows); both row-major with D columns.
-template <int PATH>
+// P: the run width of the blocked order as compute_slice takes it (0 =
+// sequential; 4, 8, 16; 32 for runs of pc.blk >= 32).
+template <int PATH, int P = 0>
 __device__ __forceinline__ void score_tile(TileSmem &sm, TileAcc &acc, const float *Qh,
                                            const float *Kh, int row0, int col0, int nq, int nk,
                                            int D, const PsConst &pc)
 {
+    constexpr bool BLOCKED = P != 0;
     const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
@@ -182,6 +230,10 @@ __device__ __forceinline__ void score_tile(TileSmem &sm, TileAcc &acc, const flo
             acc.lo[r][c] = 0.0f;
             acc.lod[r][c] = 0.0;
             acc.ref[r][c] = 0.0f;
+            if (BLOCKED) {
+                acc.blk[r][c] = 0.0f;
+                acc.blkd[r][c] = 0.0;
+            }
         }
     const int lrow = tid >> 2, ld = (tid & 3) * 4;
     const float *Qb = Qh + (size_t)row0 * D;
@@ -193,23 +245,34 @@ __device__ __forceinline__ void score_tile(TileSmem &sm, TileAcc &acc, const flo
         qv[u] = load_slice(Qb, lrow, qrows, D, ld + 16 * u);
         kv[u] = load_slice(Kb, lrow, krows, D, ld + 16 * u);
     }
-    for (int d0 = 0; d0 < D; d0 += kDChunk) {
-        __syncthreads();
-        stage_slice<PATH>(sm, qv, kv, tid, pc.qscale);
-        __syncthreads();
-        if (d0 + kDChunk < D) {
+    // runs of >= 32 products (P = 32) cover whole slices: the slice loop
+    // is cut into runs of pc.blk positions with a flush after each; otherwise
+    // one run spans the whole loop
+    const int run = P == kDChunk ? pc.blk : D;
+    for (int r0 = 0; r0 < D; r0 += run) {
+        const int r1 = min(D, r0 + run);
+        for (int d0 = r0; d0 < r1; d0 += kDChunk) {
+            __syncthreads();
+            stage_slice<PATH>(sm, qv, kv, tid, pc.qscale);
+            __syncthreads();
+            if (d0 + kDChunk < D) {
 #pragma unroll
-            for (int u = 0; u < kSliceV4; ++u) {
-                qv[u] = load_slice(Qb, lrow, qrows, D, d0 + kDChunk + ld + 16 * u);
-                kv[u] = load_slice(Kb, lrow, krows, D, d0 + kDChunk + ld + 16 * u);
+                for (int u = 0; u < kSliceV4; ++u) {
+                    qv[u] = load_slice(Qb, lrow, qrows, D, d0 + kDChunk + ld + 16 * u);
+                    kv[u] = load_slice(Kb, lrow, krows, D, d0 + kDChunk + ld + 16 * u);
+                }
             }
+            compute_slice<PATH, P>(sm, acc, tx, ty, pc);
         }
-        compute_slice<PATH>(sm, acc, tx, ty, pc);
+        // the end of a run (P = 32), or of the last run (zero padding past D
+        // leaves run sums unchanged)
+        if (BLOCKED)
+            flush_runs<PATH>(acc, pc);
     }
 }
 
 // Final scaled scores of the micro-tile.
-template <int PATH>
+template <int PATH, int P = 0>
 __device__ __forceinline__ void tile_scores(const TileAcc &acc, const PsConst &pc, float lo[4][4],
                                             float ref[4][4])
 {
@@ -222,6 +285,8 @@ __device__ __forceinline__ void tile_scores(const TileAcc &acc, const PsConst &p
                 lo[r][c] = acc.lo[r][c] * pc.out_scale;
             else if (PATH == PATH_EXACT)
                 lo[r][c] = (float)acc.lod[r][c] * pc.s;
+            else if (P != 0)   // mu = 23 in the blocked order: the blocked FP32 sum
+                lo[r][c] = acc.lo[r][c] * pc.s;
             else
                 lo[r][c] = ref[r][c];
         }

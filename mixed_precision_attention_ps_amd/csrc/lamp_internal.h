@@ -20,9 +20,14 @@ struct PsConst {
     float qscale;       // 2^(mu-23): scaled operand of the product fma
     float out_scale;    // s * 2^(23-mu): scale of the scaled-domain accumulator
     float s;            // FP32 value nearest to 1/sqrt(D)
+    int blk;            // accumulation order: 0 sequential, else runs of blk
+                        // (a power of two, 4 <= blk < dot length) products
 };
 
 PsConst make_ps_const(int mu, int D);
+// Sets the accumulation order: runs of `block` products for a dot of `len`
+// terms; block <= 1 or >= len is the sequential order (blk = 0).
+void set_ps_block(PsConst &c, int block, int len);
 
 struct Problem {
     const float *q, *k, *v;
@@ -122,6 +127,7 @@ struct DecodeProblem {
     const float *q, *k, *v;   // q [BH, nq, D]; k, v [BH, S, D]
     int BH, S, D, nq, causal, mu;
     float tau;
+    int ps_block;             // accumulation order (0 sequential)
 };
 
 // Softmax partial sums of one (head, 64-key block, query): maxima of y^mix,
@@ -166,6 +172,7 @@ struct MlpProblem {
     const float *gamma, *beta;    // [N] (layer normalisation)
     int M, N, K, mu, op;
     float tau, eps;
+    int ps_block;                 // accumulation order (0 sequential)
 };
 
 struct MlpBuffers {

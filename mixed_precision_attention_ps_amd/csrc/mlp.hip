@@ -113,14 +113,14 @@ struct GemmArgs {
     long long n_tiles;
 };
 
-template <int PATH, int EPI>
+template <int PATH, int EPI, int P>
 __device__ __forceinline__ void gemm_tile(TileSmem &sm, const double *s_exp, const GemmArgs &a,
                                           int ti, int tj)
 {
     TileAcc acc;
-    score_tile<PATH>(sm, acc, a.x, a.w, ti * kTile, tj * kTile, a.M, a.N, a.K, a.pc);
+    score_tile<PATH, P>(sm, acc, a.x, a.w, ti * kTile, tj * kTile, a.M, a.N, a.K, a.pc);
     float lo[4][4], ref[4][4];
-    tile_scores<PATH>(acc, a.pc, lo, ref);
+    tile_scores<PATH, P>(acc, a.pc, lo, ref);
     const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4, lane = tid & 63;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -189,7 +189,8 @@ __device__ __forceinline__ void gemm_tile(TileSmem &sm, const double *s_exp, con
 // FAST: the tiles whose operands allow the FP32 fast path (one work-group per
 // tile); otherwise a bounded grid striding over the other tiles (exact double
 // path, or plain FP32 at mu = 23), exiting at once when there are none.
-template <bool FAST, int EPI>
+// P: the run width of the blocked PS(mu) order (run_width(a.pc.blk)).
+template <bool FAST, int EPI, int P>
 __global__ __launch_bounds__(kThreads) void ps_gemm_kernel(GemmArgs a)
 {
     __shared__ TileSmem sm;
@@ -220,13 +221,13 @@ __global__ __launch_bounds__(kThreads) void ps_gemm_kernel(GemmArgs a)
         const int path = path_of(g, ti, tj);
         if (FAST) {
             if (path == PATH_FAST)
-                gemm_tile<PATH_FAST, EPI>(sm, s_exp, a, ti, tj);
+                gemm_tile<PATH_FAST, EPI, P>(sm, s_exp, a, ti, tj);
         } else if (path == PATH_EXACT) {
             if (threadIdx.x == 0 && a.exact_tiles)
                 atomicAdd(a.exact_tiles, 1ull);
-            gemm_tile<PATH_EXACT, EPI>(sm, s_exp, a, ti, tj);
+            gemm_tile<PATH_EXACT, EPI, P>(sm, s_exp, a, ti, tj);
         } else if (path == PATH_FP32) {
-            gemm_tile<PATH_FP32, EPI>(sm, s_exp, a, ti, tj);
+            gemm_tile<PATH_FP32, EPI, P>(sm, s_exp, a, ti, tj);
         }
     }
 }
@@ -445,9 +446,10 @@ __global__ __launch_bounds__(kThreads) void ln_lamp_kernel(LnArgs a)
 }
 
 // ---------------------------------------------------------------------------
-static PsConst gemm_ps_const(int mu)
+static PsConst gemm_ps_const(int mu, int block, int K)
 {
     PsConst c = make_ps_const(mu, 1);   // s = 1/sqrt(1) = 1: no scale
+    set_ps_block(c, block, K);
     return c;
 }
 
@@ -479,7 +481,7 @@ hipError_t launch_mlp(const MlpProblem &p, const MlpBuffers &b, hipStream_t st,
     a.K = p.K;
     a.tiles_n = tiles_n;
     a.W = (p.N + 31) / 32;
-    a.pc = gemm_ps_const(p.mu);
+    a.pc = gemm_ps_const(p.mu, p.ps_block, p.K);
     a.unsafe_x = b.unsafe;
     a.unsafe_w = b.unsafe + tiles_m;
     a.ylo = b.ylo;
@@ -499,19 +501,31 @@ hipError_t launch_mlp(const MlpProblem &p, const MlpBuffers &b, hipStream_t st,
     const bool gelu = p.op == MLP_GELU;
     if ((e = rec(2 * 6)) != hipSuccess)   // exact stage
         return e;
-    if (gelu)
-        hipLaunchKernelGGL((ps_gemm_kernel<false, EPI_GELU>), dim3(ggen), block, 0, st, a);
-    else
-        hipLaunchKernelGGL((ps_gemm_kernel<false, EPI_STORE>), dim3(ggen), block, 0, st, a);
+#define LAMP_GEMM_LAUNCH1(FASTK, EPIK, grid)                                                    \
+    do {                                                                                        \
+        switch (run_width(a.pc.blk)) {                                                          \
+        case 0: hipLaunchKernelGGL((ps_gemm_kernel<FASTK, EPIK, 0>), grid, block, 0, st, a); break;  \
+        case 4: hipLaunchKernelGGL((ps_gemm_kernel<FASTK, EPIK, 4>), grid, block, 0, st, a); break;  \
+        case 8: hipLaunchKernelGGL((ps_gemm_kernel<FASTK, EPIK, 8>), grid, block, 0, st, a); break;  \
+        case 16: hipLaunchKernelGGL((ps_gemm_kernel<FASTK, EPIK, 16>), grid, block, 0, st, a); break; \
+        default: hipLaunchKernelGGL((ps_gemm_kernel<FASTK, EPIK, 32>), grid, block, 0, st, a); break; \
+        }                                                                                       \
+    } while (0)
+#define LAMP_GEMM_LAUNCH(FASTK, grid)                                                           \
+    do {                                                                                        \
+        if (gelu)                                                                               \
+            LAMP_GEMM_LAUNCH1(FASTK, EPI_GELU, grid);                                           \
+        else                                                                                    \
+            LAMP_GEMM_LAUNCH1(FASTK, EPI_STORE, grid);                                          \
+    } while (0)
+    LAMP_GEMM_LAUNCH(false, dim3(ggen));
     if ((e = hipGetLastError()) != hipSuccess || (e = rec(2 * 6 + 1)) != hipSuccess ||
         (e = rec(2 * 1)) != hipSuccess)
         return e;
-    if (p.mu <= 10) {
-        if (gelu)
-            hipLaunchKernelGGL((ps_gemm_kernel<true, EPI_GELU>), dim3(gfast), block, 0, st, a);
-        else
-            hipLaunchKernelGGL((ps_gemm_kernel<true, EPI_STORE>), dim3(gfast), block, 0, st, a);
-    }
+    if (p.mu <= 10)
+        LAMP_GEMM_LAUNCH(true, dim3(gfast));
+#undef LAMP_GEMM_LAUNCH
+#undef LAMP_GEMM_LAUNCH1
     if ((e = hipGetLastError()) != hipSuccess || (e = rec(2 * 1 + 1)) != hipSuccess ||
         (e = rec(2 * 4)) != hipSuccess)
         return e;

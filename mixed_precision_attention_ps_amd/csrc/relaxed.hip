@@ -58,14 +58,14 @@ struct RelaxedSmem {
     RowState row[kTile];
 };
 
-template <int PATH>
+template <int PATH, int P>
 __device__ __forceinline__ void relaxed_tile_scores(TileSmem &sm, const RelaxedArgs &a,
                                                     const float *Qh, const float *Kh, int row0,
                                                     int col0, float lo[4][4], float ref[4][4])
 {
     TileAcc acc;
-    score_tile<PATH>(sm, acc, Qh, Kh, row0, col0, a.S, a.S, a.D, a.pc);
-    tile_scores<PATH>(acc, a.pc, lo, ref);
+    score_tile<PATH, P>(sm, acc, Qh, Kh, row0, col0, a.S, a.S, a.D, a.pc);
+    tile_scores<PATH, P>(acc, a.pc, lo, ref);
 }
 
 // exp of a difference of row maxima (-inf when a maximum is still unset).
@@ -79,7 +79,8 @@ __device__ __forceinline__ double exp_delta(float from, float to, const double *
 // e_ref = exp(y^ref - m_ref) serves the reference sums and, scaled by
 // exp(m_ref - m_mix), the softmax term of a selected score (whose y^mix is
 // y^ref).  Two double exps per score; the row factors are per tile.
-template <int NB, bool FAST_KERNEL>
+// P: the run width of the blocked PS(mu) order (run_width(a.pc.blk)).
+template <int NB, bool FAST_KERNEL, int P>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FAST_KERNEL ? 2 : 1)))
 void relaxed_kernel(RelaxedArgs a)
 {
@@ -136,13 +137,13 @@ void relaxed_kernel(RelaxedArgs a)
                          : (a.pc.mu <= 10 && qsafe && !a.unsafe_k[bh * a.tiles + t]) ? PATH_FAST
                                                                                        : PATH_EXACT;
         if (FAST_KERNEL || path == PATH_FAST) {
-            relaxed_tile_scores<PATH_FAST>(sm.u.tile, a, Qh, Kh, row0, col0, lo, ref);
+            relaxed_tile_scores<PATH_FAST, P>(sm.u.tile, a, Qh, Kh, row0, col0, lo, ref);
         } else if (path == PATH_EXACT) {
             if (tid == 0 && a.exact_tiles)
                 atomicAdd(a.exact_tiles, 1ull);
-            relaxed_tile_scores<PATH_EXACT>(sm.u.tile, a, Qh, Kh, row0, col0, lo, ref);
+            relaxed_tile_scores<PATH_EXACT, P>(sm.u.tile, a, Qh, Kh, row0, col0, lo, ref);
         } else {
-            relaxed_tile_scores<PATH_FP32>(sm.u.tile, a, Qh, Kh, row0, col0, lo, ref);
+            relaxed_tile_scores<PATH_FP32, P>(sm.u.tile, a, Qh, Kh, row0, col0, lo, ref);
         }
 
         // V tile loads start now and land during the softmax epilogue.
@@ -393,17 +394,29 @@ hipError_t launch_relaxed(const Problem &p, const uint8_t *unsafe, float *out, u
     const dim3 g((unsigned)grid), b(kThreads);
     if (fast && p.mu > 10)
         return hipSuccess;
-    if (a.Dv <= 64) {
-        if (fast)
-            hipLaunchKernelGGL((relaxed_kernel<4, true>), g, b, 0, st, a);
-        else
-            hipLaunchKernelGGL((relaxed_kernel<4, false>), g, b, 0, st, a);
-    } else {
-        if (fast)
-            hipLaunchKernelGGL((relaxed_kernel<8, true>), g, b, 0, st, a);
-        else
-            hipLaunchKernelGGL((relaxed_kernel<8, false>), g, b, 0, st, a);
-    }
+#define LAMP_RELAXED_LAUNCH(NB, P)                                                         \
+    do {                                                                                   \
+        if (fast)                                                                          \
+            hipLaunchKernelGGL((relaxed_kernel<NB, true, P>), g, b, 0, st, a);             \
+        else                                                                               \
+            hipLaunchKernelGGL((relaxed_kernel<NB, false, P>), g, b, 0, st, a);            \
+    } while (0)
+#define LAMP_RELAXED_LAUNCH_P(NB)                                                          \
+    do {                                                                                   \
+        switch (run_width(p.pc.blk)) {                                                     \
+        case 0: LAMP_RELAXED_LAUNCH(NB, 0); break;                                         \
+        case 4: LAMP_RELAXED_LAUNCH(NB, 4); break;                                         \
+        case 8: LAMP_RELAXED_LAUNCH(NB, 8); break;                                         \
+        case 16: LAMP_RELAXED_LAUNCH(NB, 16); break;                                       \
+        default: LAMP_RELAXED_LAUNCH(NB, 32); break;                                       \
+        }                                                                                  \
+    } while (0)
+    if (a.Dv <= 64)
+        LAMP_RELAXED_LAUNCH_P(4);
+    else
+        LAMP_RELAXED_LAUNCH_P(8);
+#undef LAMP_RELAXED_LAUNCH_P
+#undef LAMP_RELAXED_LAUNCH
     return hipGetLastError();
 }
 

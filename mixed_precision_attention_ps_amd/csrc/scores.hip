@@ -17,7 +17,13 @@ PsConst make_ps_const(int mu, int D)
     c.qscale = ldexpf(1.0f, mu - 23);
     c.s = (float)(1.0 / sqrt((double)D));
     c.out_scale = ldexpf(c.s, 23 - mu);
+    c.blk = 0;
     return c;
+}
+
+void set_ps_block(PsConst &c, int block, int len)
+{
+    c.blk = (block <= 1 || block >= len) ? 0 : block;
 }
 
 // Safe operand: zero, or a finite magnitude in [2^-40, 2^40].
@@ -87,16 +93,16 @@ struct ScoreArgs {
     long long n_tiles;   // BH x tiles per head
 };
 
-template <int PATH>
+template <int PATH, int P>
 __device__ __forceinline__ void score_tile_store(TileSmem &sm, const double *s_exp,
                                                  const ScoreArgs &a, int bh, int ti, int tj)
 {
     const size_t head = (size_t)bh * a.S * a.D;
     TileAcc acc;
-    score_tile<PATH>(sm, acc, a.q + head, a.k + head, ti * kTile, tj * kTile, a.S, a.S, a.D,
-                     a.pc);
+    score_tile<PATH, P>(sm, acc, a.q + head, a.k + head, ti * kTile, tj * kTile, a.S, a.S, a.D,
+                        a.pc);
     float lo[4][4], ref[4][4];
-    tile_scores<PATH>(acc, a.pc, lo, ref);
+    tile_scores<PATH, P>(acc, a.pc, lo, ref);
     const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -178,7 +184,8 @@ __device__ __forceinline__ void score_tile_store(TileSmem &sm, const double *s_e
 // and so its occupancy, to what the fast path needs.  The fast kernel has one
 // work-group per tile; the generic one a bounded grid that strides over the
 // tiles (it usually finds none to do, and then costs a few microseconds).
-template <bool FAST_KERNEL>
+// P: the run width of the blocked PS(mu) order (run_width(a.pc.blk)).
+template <bool FAST_KERNEL, int P>
 __global__ __launch_bounds__(kThreads) void ps_scores_kernel(ScoreArgs a)
 {
     __shared__ TileSmem sm;
@@ -211,13 +218,13 @@ __global__ __launch_bounds__(kThreads) void ps_scores_kernel(ScoreArgs a)
         const int path = tile_path(g, bh, ti, tj);
         if (FAST_KERNEL) {
             if (path == PATH_FAST)
-                score_tile_store<PATH_FAST>(sm, s_exp, a, bh, ti, tj);
+                score_tile_store<PATH_FAST, P>(sm, s_exp, a, bh, ti, tj);
         } else if (path == PATH_EXACT) {
             if (threadIdx.x == 0 && a.exact_tiles)
                 atomicAdd(a.exact_tiles, 1ull);
-            score_tile_store<PATH_EXACT>(sm, s_exp, a, bh, ti, tj);
+            score_tile_store<PATH_EXACT, P>(sm, s_exp, a, bh, ti, tj);
         } else if (path == PATH_FP32) {
-            score_tile_store<PATH_FP32>(sm, s_exp, a, bh, ti, tj);
+            score_tile_store<PATH_FP32, P>(sm, s_exp, a, bh, ti, tj);
         }
     }
 }
@@ -249,13 +256,24 @@ hipError_t launch_ps_scores(const Problem &p, const uint8_t *unsafe, float *ylo,
     a.n_tiles = grid;
     if (grid == 0)
         return hipSuccess;
+#define LAMP_SCORES_LAUNCH(FASTK, G)                                                           \
+    do {                                                                                       \
+        switch (run_width(p.pc.blk)) {                                                         \
+        case 0: hipLaunchKernelGGL((ps_scores_kernel<FASTK, 0>), G, dim3(kThreads), 0, st, a); break;  \
+        case 4: hipLaunchKernelGGL((ps_scores_kernel<FASTK, 4>), G, dim3(kThreads), 0, st, a); break;  \
+        case 8: hipLaunchKernelGGL((ps_scores_kernel<FASTK, 8>), G, dim3(kThreads), 0, st, a); break;  \
+        case 16: hipLaunchKernelGGL((ps_scores_kernel<FASTK, 16>), G, dim3(kThreads), 0, st, a); break; \
+        default: hipLaunchKernelGGL((ps_scores_kernel<FASTK, 32>), G, dim3(kThreads), 0, st, a); break; \
+        }                                                                                      \
+    } while (0)
     if (fast) {
         if (p.mu <= 10)
-            hipLaunchKernelGGL(ps_scores_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, st, a);
+            LAMP_SCORES_LAUNCH(true, dim3((unsigned)grid));
     } else {
         const long long g = grid < kGenericGrid ? grid : kGenericGrid;
-        hipLaunchKernelGGL(ps_scores_kernel<false>, dim3((unsigned)g), dim3(kThreads), 0, st, a);
+        LAMP_SCORES_LAUNCH(false, dim3((unsigned)g));
     }
+#undef LAMP_SCORES_LAUNCH
     return hipGetLastError();
 }
 

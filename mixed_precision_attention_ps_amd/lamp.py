@@ -37,7 +37,8 @@ class LampParams(ctypes.Structure):
                 ("workspace_bytes", ctypes.c_size_t), ("seed", ctypes.c_uint64),
                 ("row_kl", ctypes.c_void_p), ("row_kl_lowp", ctypes.c_void_p),
                 ("row_count", ctypes.c_void_p), ("scores_mix", ctypes.c_void_p),
-                ("scores_ref", ctypes.c_void_p), ("stage_events", ctypes.c_void_p)]
+                ("scores_ref", ctypes.c_void_p), ("stage_events", ctypes.c_void_p),
+                ("ps_block", ctypes.c_int)]
 
 
 class LampError(RuntimeError):
@@ -147,7 +148,7 @@ def lamp_ps_scores(q, k, *, causal: bool, mu: int, ylo=None, yref=None):
 def lamp_attention_fwd(q, k, v, *, causal: bool, mu: int, tau: float, mode="strict", out=None,
                        probs=None, recompute_mask=None, want_stats: bool = True, seed: int = 0,
                        row_kl=None, row_kl_lowp=None, row_count=None, scores_mix=None,
-                       scores_ref=None, workspace=None, stage_events=None):
+                       scores_ref=None, workspace=None, stage_events=None, ps_block: int = 0):
     """LAMP attention forward through lamp_attention_fwd_ex.
 
     q, k, v: float32 [B, H, S, D] device tensors.  Optional outputs are written
@@ -160,6 +161,7 @@ def lamp_attention_fwd(q, k, v, *, causal: bool, mu: int, tau: float, mode="stri
     p = LampParams()
     p.stream = torch.cuda.current_stream(q.device).cuda_stream
     p.seed = seed & 0xFFFFFFFFFFFFFFFF
+    p.ps_block = int(ps_block)
     if workspace is not None:
         p.workspace = workspace.data_ptr()
         p.workspace_bytes = workspace.numel() * workspace.element_size()
@@ -186,7 +188,7 @@ def lamp_attention_fwd(q, k, v, *, causal: bool, mu: int, tau: float, mode="stri
 def lamp_decode_fwd(q, k, v, *, causal: bool, mu: int, tau: float, out=None, probs=None,
                     recompute_mask=None, want_stats: bool = True, row_kl=None, row_kl_lowp=None,
                     row_count=None, scores_mix=None, scores_ref=None, workspace=None,
-                    stage_events=None):
+                    stage_events=None, ps_block: int = 0):
     """Relaxed LAMP at decode shapes through lamp_decode_fwd.
 
     q: float32 [B, H, Nq, D]; k, v: float32 [B, H, S, D] device tensors (the
@@ -201,6 +203,7 @@ def lamp_decode_fwd(q, k, v, *, causal: bool, mu: int, tau: float, out=None, pro
         out = torch.empty_like(q)
     p = LampParams()
     p.stream = torch.cuda.current_stream(q.device).cuda_stream
+    p.ps_block = int(ps_block)
     if workspace is not None:
         p.workspace = workspace.data_ptr()
         p.workspace_bytes = workspace.numel() * workspace.element_size()
@@ -227,9 +230,10 @@ def lamp_decode_fwd(q, k, v, *, causal: bool, mu: int, tau: float, out=None, pro
 MLP_OPS = {"gelu": 1, "layernorm": 2}
 
 
-def _mlp_params(device, workspace, stage_events, **opt):
+def _mlp_params(device, workspace, stage_events, ps_block=0, **opt):
     p = LampParams()
     p.stream = torch.cuda.current_stream(device).cuda_stream
+    p.ps_block = int(ps_block)
     if workspace is not None:
         p.workspace = workspace.data_ptr()
         p.workspace_bytes = workspace.numel() * workspace.element_size()
@@ -273,7 +277,8 @@ def lamp_gemm_scores(x, w, *, mu: int, ylo=None, yref=None):
 
 def lamp_gelu_fwd(x, w, *, mu: int, tau: float, out=None, recompute_mask=None,
                   want_stats: bool = True, row_err=None, row_err_lowp=None, row_count=None,
-                  scores_mix=None, scores_ref=None, workspace=None, stage_events=None):
+                  scores_mix=None, scores_ref=None, workspace=None, stage_events=None,
+                  ps_block: int = 0):
     """GELU(x w^T) with the activation LAMP rule through lamp_gelu_fwd.
 
     row_err / row_err_lowp (float64 [M]) receive the l1 distances of the LAMP
@@ -282,8 +287,9 @@ def lamp_gelu_fwd(x, w, *, mu: int, tau: float, out=None, recompute_mask=None,
     M, N, K = _mlp_shapes(x, w)
     if out is None:
         out = torch.empty((M, N), device=x.device, dtype=torch.float32)
-    p = _mlp_params(x.device, workspace, stage_events, row_kl=row_err, row_kl_lowp=row_err_lowp,
-                    row_count=row_count, scores_mix=scores_mix, scores_ref=scores_ref)
+    p = _mlp_params(x.device, workspace, stage_events, ps_block, row_kl=row_err,
+                    row_kl_lowp=row_err_lowp, row_count=row_count, scores_mix=scores_mix,
+                    scores_ref=scores_ref)
     st = LampStats() if want_stats else None
     _check(library().lamp_gelu_fwd(
         _f32(x, "x"), _f32(w, "w"), M, N, K, int(mu), ctypes.c_float(tau), _f32(out, "out"),
@@ -294,7 +300,7 @@ def lamp_gelu_fwd(x, w, *, mu: int, tau: float, out=None, recompute_mask=None,
 def lamp_layernorm_fwd(x, w, gamma, beta, *, mu: int, eps: float, tau: float, out=None,
                        recompute_mask=None, want_stats: bool = True, row_err=None,
                        row_err_lowp=None, row_count=None, scores_mix=None, scores_ref=None,
-                       workspace=None, stage_events=None):
+                       workspace=None, stage_events=None, ps_block: int = 0):
     """LayerNorm(x w^T) with the greedy LAMP rule through lamp_layernorm_fwd.
 
     row_err / row_err_lowp (float64 [M]) receive the l2 distances of the LAMP
@@ -305,8 +311,9 @@ def lamp_layernorm_fwd(x, w, gamma, beta, *, mu: int, eps: float, tau: float, ou
         raise ValueError("gamma and beta must be [N]")
     if out is None:
         out = torch.empty((M, N), device=x.device, dtype=torch.float32)
-    p = _mlp_params(x.device, workspace, stage_events, row_kl=row_err, row_kl_lowp=row_err_lowp,
-                    row_count=row_count, scores_mix=scores_mix, scores_ref=scores_ref)
+    p = _mlp_params(x.device, workspace, stage_events, ps_block, row_kl=row_err,
+                    row_kl_lowp=row_err_lowp, row_count=row_count, scores_mix=scores_mix,
+                    scores_ref=scores_ref)
     st = LampStats() if want_stats else None
     _check(library().lamp_layernorm_fwd(
         _f32(x, "x"), _f32(w, "w"), _f32(gamma, "gamma"), _f32(beta, "beta"), M, N, K, int(mu),

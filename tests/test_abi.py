@@ -175,6 +175,22 @@ def test_mlp_workspace_bytes(lib):
     assert ln >= 8 * M * 1600
 
 
+def test_ps_block_checked_before_any_device_call(lib):
+    from mixed_precision_attention_ps_amd import lamp
+    for b, code in ((-1, -1), (2, -2), (3, -2), (6, -2), (12, -2), (1 << 25, -2)):
+        p = lamp.LampParams()
+        p.ps_block = b
+        rc = lib.lamp_attention_fwd_ex(A, A, A, 1, 1, 8, 64, 0, 4, ctypes.c_float(0.1), 0, A,
+                                       None, None, None, ctypes.byref(p))
+        assert rc == code, (b, rc)
+        rc = lib.lamp_decode_fwd(A, A, A, 1, 1, 1, 8, 64, 1, 4, ctypes.c_float(0.1), A, None,
+                                 None, None, ctypes.byref(p))
+        assert rc == code, (b, rc)
+        rc = lib.lamp_gelu_fwd(A, A, 4, 8, 64, 4, ctypes.c_float(0.1), A, None, None,
+                               ctypes.byref(p))
+        assert rc == code, (b, rc)
+
+
 def test_version_and_strerror(lib):
     assert lib.lamp_version() >= 10000
     assert lib.lamp_strerror(0) == b"success"

@@ -35,7 +35,7 @@ def note(msg):
 
 
 def run_gpu(dev, Q, K, V, *, causal, mu, tau, mode, seed=0, want_probs=True, want_mask=True,
-            want_scores=True, want_rows=True, want_stats=True):
+            want_scores=True, want_rows=True, want_stats=True, ps_block=0):
     import torch
     from mixed_precision_attention_ps_amd import lamp
     B, H, S, D = Q.shape
@@ -49,11 +49,13 @@ def run_gpu(dev, Q, K, V, *, causal, mu, tau, mode, seed=0, want_probs=True, wan
     ymix = torch.zeros((B, H, S, S), device=dev) if want_scores else None
     yref = torch.zeros((B, H, S, S), device=dev) if want_scores else None
     note(f"gpu {MODE_NAME[mode]} B={B} H={H} S={S} D={D} causal={causal} mu={mu} tau={tau} "
-         f"probs={want_probs} scores={want_scores} rows={want_rows} stats={want_stats}")
+         f"probs={want_probs} scores={want_scores} rows={want_rows} stats={want_stats} "
+         f"ps_block={ps_block}")
     out, st = lamp.lamp_attention_fwd(q, k, v, causal=causal, mu=mu, tau=tau, mode=mode,
                                       probs=probs, recompute_mask=mask, seed=seed, row_kl=row_kl,
                                       row_kl_lowp=row_kl_lowp, row_count=row_count,
-                                      scores_mix=ymix, scores_ref=yref, want_stats=want_stats)
+                                      scores_mix=ymix, scores_ref=yref, want_stats=want_stats,
+                                      ps_block=ps_block)
     torch.cuda.synchronize()
     res = {"out": out.cpu().numpy(), "stats": st}
     if want_rows:
@@ -68,10 +70,10 @@ def run_gpu(dev, Q, K, V, *, causal, mu, tau, mode, seed=0, want_probs=True, wan
     return res
 
 
-def run_orc(orc, Q, K, V, *, causal, mu, tau, mode, seed=0, heads=None, rows=None):
-    note(f"oracle {MODE_NAME[mode]} shape={Q.shape} heads={heads} rows={rows}")
+def run_orc(orc, Q, K, V, *, causal, mu, tau, mode, seed=0, heads=None, rows=None, ps_block=0):
+    note(f"oracle {MODE_NAME[mode]} shape={Q.shape} heads={heads} rows={rows} ps_block={ps_block}")
     return orc.lamp_heads(Q, K, V, causal=causal, mu=mu, tau=tau, mode=mode, seed=seed,
-                          heads=heads, rows=rows)
+                          heads=heads, rows=rows, ps_block=ps_block)
 
 
 def ymix_oracle(r, S):
