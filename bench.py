@@ -51,6 +51,14 @@ KERNEL_SOURCES = {
 }
 
 
+def run_flush_ops(n: int, block: int) -> int:
+    """Lane-operations the blocked PS(mu) order adds to an n-term dot: one
+    PS(mu) add (add + 3-instruction rounding) per run of `block` products."""
+    if block <= 1 or block >= n:
+        return 0
+    return 4 * ((n + block - 1) // block)
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -77,7 +85,7 @@ def load_traffic(kernel: str, workload: str, launches_per_step: int = 1):
     return ent.get("bytes_per_launch")
 
 
-def cpu_baseline(Q, K, V, w, mode_id, mu, tau, heads_n, seed):
+def cpu_baseline(Q, K, V, w, mode_id, mu, tau, heads_n, seed, ps_block=0):
     import numpy as np
     import oracle
     oracle.build(force=False)
@@ -87,7 +95,7 @@ def cpu_baseline(Q, K, V, w, mode_id, mu, tau, heads_n, seed):
     per_head = w.S * (w.S + 1) // 2 if w.causal else w.S * w.S
     t0 = time.perf_counter()
     oracle.lamp_heads(Q, K, V, causal=w.causal, mu=mu, tau=tau, mode=mode_id, heads=heads,
-                      seed=seed, want=("out", "kl", "count", "mask", "probs"))
+                      seed=seed, ps_block=ps_block, want=("out", "kl", "count", "mask", "probs"))
     dt = time.perf_counter() - t0
     n = per_head * len(heads)
     return {"value": n / dt, "unit": "scores/s", "cores": threads, "kind": "oracle",
@@ -107,7 +115,7 @@ def copy_calibration(args, dev):
         del a, b
 
 
-def decode_cpu_baseline(Q, K, V, w, nq, mu, tau, heads_n):
+def decode_cpu_baseline(Q, K, V, w, nq, mu, tau, heads_n, ps_block=0):
     import numpy as np
     import oracle
     oracle.build(force=False)
@@ -117,7 +125,8 @@ def decode_cpu_baseline(Q, K, V, w, nq, mu, tau, heads_n):
     S = w.S
     t0 = time.perf_counter()
     oracle.lamp_heads(Q, K, V, causal=w.causal, mu=mu, tau=tau, mode=oracle.RELAXED, heads=heads,
-                      rows=(S - nq, S), want=("out", "kl", "count", "mask", "probs"))
+                      rows=(S - nq, S), ps_block=ps_block,
+                      want=("out", "kl", "count", "mask", "probs"))
     dt = time.perf_counter() - t0
     per_head = sum((S - nq + t + 1) if w.causal else S for t in range(nq))
     n = per_head * len(heads)
@@ -152,7 +161,7 @@ def bench_decode(args, w):
     def step(events=None):
         lamp.lamp_decode_fwd(q, k, v, causal=w.causal, mu=args.mu, tau=tau, out=out, probs=probs,
                              recompute_mask=mask, row_kl=row_kl, want_stats=False,
-                             stage_events=events)
+                             stage_events=events, ps_block=args.ps_block)
 
     for _ in range(args.warmup):
         step()
@@ -171,7 +180,8 @@ def bench_decode(args, w):
     for e in ev:
         e.close()
     _, st = lamp.lamp_decode_fwd(q, k, v, causal=w.causal, mu=args.mu, tau=tau, out=out,
-                                 probs=probs, recompute_mask=mask, want_stats=True)
+                                 probs=probs, recompute_mask=mask, want_stats=True,
+                                 ps_block=args.ps_block)
     n_valid = st["n_valid"]
     rate = st["n_selected"] / n_valid
     value = n_valid / (wall / args.steps)
@@ -196,7 +206,8 @@ def bench_decode(args, w):
         "ms_per_step": 1e3 * wall / args.steps, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name, "B": B, "H": H, "S": S, "D": D, "Nq": nq,
-                   "causal": w.causal, "mu": args.mu, "mode": "relaxed", "tau": tau, "rate": rate,
+                   "causal": w.causal, "mu": args.mu, "mode": "relaxed",
+                   "ps_block": args.ps_block, "tau": tau, "rate": rate,
                    "probs": probs is not None, "mask": True, "row_kl": True,
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "kernel": kname, "achieved": achieved / 1e9,
@@ -211,18 +222,18 @@ def bench_decode(args, w):
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")
-        rec["cpu_baseline"] = decode_cpu_baseline(Q, K, V, w, nq, args.mu, tau, 8)
+        rec["cpu_baseline"] = decode_cpu_baseline(Q, K, V, w, nq, args.mu, tau, 8, args.ps_block)
     print(json.dumps(rec), flush=True)
 
 
-def mlp_cpu_baseline(X, W, gamma, beta, w, mu, tau, rows_n):
+def mlp_cpu_baseline(X, W, gamma, beta, w, mu, tau, rows_n, ps_block=0):
     import numpy as np
     import oracle
     oracle.build(force=False)
     rows = np.linspace(0, w.M - 1, rows_n).astype(int)
     threads = oracle.max_threads()
     t0 = time.perf_counter()
-    ylo, yref = oracle.ps_gemm(X[rows], W, mu=mu)
+    ylo, yref = oracle.ps_gemm(X[rows], W, mu=mu, ps_block=ps_block)
     if w.op == "gelu":
         oracle.gelu_lamp(ylo, yref, tau=tau)
     else:
@@ -257,11 +268,12 @@ def bench_mlp(args, w):
     def step(events=None):
         if w.op == "gelu":
             lamp.lamp_gelu_fwd(x, wt, mu=args.mu, tau=tau, out=out, recompute_mask=mask,
-                               row_err=row_err, want_stats=False, stage_events=events)
+                               row_err=row_err, want_stats=False, stage_events=events,
+                               ps_block=args.ps_block)
         else:
             lamp.lamp_layernorm_fwd(x, wt, g, b, mu=args.mu, eps=w.eps, tau=tau, out=out,
                                     recompute_mask=mask, row_err=row_err, want_stats=False,
-                                    stage_events=events)
+                                    stage_events=events, ps_block=args.ps_block)
 
     for _ in range(args.warmup):
         step()
@@ -280,15 +292,16 @@ def bench_mlp(args, w):
     for e in ev:
         e.close()
     if w.op == "gelu":
-        _, st = lamp.lamp_gelu_fwd(x, wt, mu=args.mu, tau=tau, out=out, want_stats=True)
+        _, st = lamp.lamp_gelu_fwd(x, wt, mu=args.mu, tau=tau, out=out, want_stats=True,
+                                   ps_block=args.ps_block)
     else:
         _, st = lamp.lamp_layernorm_fwd(x, wt, g, b, mu=args.mu, eps=w.eps, tau=tau, out=out,
-                                        want_stats=True)
+                                        want_stats=True, ps_block=args.ps_block)
     n_out = M * N
     rate = st["n_selected"] / n_out
     value = n_out / (wall / args.steps)
     kname = "ps_gemm_kernel"
-    w_alg = 9 * K
+    w_alg = 9 * K + run_flush_ops(K, args.ps_block)
     t_kernel_ms = stages["scores"]
     achieved = w_alg * n_out / (t_kernel_ms * 1e-3)
     rec = {
@@ -297,6 +310,7 @@ def bench_mlp(args, w):
         "warmup": args.warmup, "ms_per_step": 1e3 * wall / args.steps, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name, "M": M, "N": N, "K": K, "op": w.op, "mu": args.mu,
+                   "ps_block": args.ps_block,
                    "tau": tau, "rate": rate, "mask": True, "row_err": True,
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "alu", "kernel": kname, "achieved": achieved / 1e12,
@@ -311,7 +325,8 @@ def bench_mlp(args, w):
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")
-        rec["cpu_baseline"] = mlp_cpu_baseline(X, W, gamma, beta, w, args.mu, tau, 64)
+        rec["cpu_baseline"] = mlp_cpu_baseline(X, W, gamma, beta, w, args.mu, tau, 64,
+                                               args.ps_block)
     print(json.dumps(rec), flush=True)
 
 
@@ -331,6 +346,9 @@ def main():
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="run a plain copy of this many MiB first (counter calibration)")
     ap.add_argument("--nq", type=int, default=1, help="decode workloads: queries per head")
+    ap.add_argument("--ps-block", type=int, default=0,
+                    help="PS(mu) accumulation order: 0 sequential, else runs of this many "
+                         "products (blocked order)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -371,7 +389,7 @@ def main():
     def step(events=None):
         lamp.lamp_attention_fwd(q, k, v, causal=w.causal, mu=args.mu, tau=tau, mode=mode_id,
                                 out=out, probs=probs, recompute_mask=mask, want_stats=False,
-                                row_kl=row_kl, stage_events=events)
+                                row_kl=row_kl, stage_events=events, ps_block=args.ps_block)
 
     for _ in range(args.warmup):
         step()
@@ -405,7 +423,8 @@ def main():
 
     # untimed: rate and KL of the same call
     _, st = lamp.lamp_attention_fwd(q, k, v, causal=w.causal, mu=args.mu, tau=tau, mode=mode_id,
-                                    out=out, probs=probs, recompute_mask=mask, want_stats=True)
+                                    out=out, probs=probs, recompute_mask=mask, want_stats=True,
+                                    ps_block=args.ps_block)
     n_valid = st["n_valid"]
     rate = st["n_selected"] / n_valid
     ms_per_step = 1e3 * wall / args.steps
@@ -416,7 +435,7 @@ def main():
     # multiply, add, two 3-instruction roundings per MAC) + D (FP32 reference
     # dot at two lanes per slot) [+ 20 for the fused softmax/criterion/KL].
     kname = "relaxed_kernel" if args.mode == "relaxed" else "ps_scores_kernel"
-    w_alg = 9 * D + (20 if args.mode == "relaxed" else 0)
+    w_alg = 9 * D + (20 if args.mode == "relaxed" else 0) + run_flush_ops(D, args.ps_block)
     t_kernel_ms = stages.get("scores")
     achieved = w_alg * n_valid / (t_kernel_ms * 1e-3) if t_kernel_ms else None
     traffic = load_traffic(kname, w.name)
@@ -427,7 +446,7 @@ def main():
                 "traffic": traffic, "kernel_ms": t_kernel_ms,
                 "slots_per_score": w_alg}
     # whole path against the same peak (8D + D + 20 + 2 r D per score) and HBM
-    w_path = 9 * D + 20 + 2 * rate * D
+    w_path = 9 * D + 20 + 2 * rate * D + run_flush_ops(D, args.ps_block)
     # the same work against the single-pipe 16-lane VALU rate (256 CUs x 4 SIMDs
     # x 16 lanes x 2.4 GHz = 3.93e13 lane-slots/s), counting the FP32 reference
     # dot at two lanes per slot as above: the convention of a pure 16-lane
@@ -440,7 +459,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "H": H, "S": S, "D": D, "causal": w.causal,
-                   "mu": args.mu, "mode": args.mode, "tau": tau, "target_rate": args.rate,
+                   "mu": args.mu, "mode": args.mode, "ps_block": args.ps_block, "tau": tau,
+                   "target_rate": args.rate,
                    "rate": rate, "probs": not args.no_probs, "mask": True, "row_kl": True,
                    "parallelism": "none (1 GPU)"},
         "roofline": roofline,
@@ -456,7 +476,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")
-        rec["cpu_baseline"] = cpu_baseline(Q, K, V, w, mode_id, args.mu, tau, args.cpu_heads, 0)
+        rec["cpu_baseline"] = cpu_baseline(Q, K, V, w, mode_id, args.mu, tau, args.cpu_heads, 0,
+                                           args.ps_block)
     print(json.dumps(rec), flush=True)
 
 

@@ -86,9 +86,9 @@ MLP_WORKLOADS = {
     w.name: w for w in [
         # GPT-2 XL MLP up-projection of 1024 tokens (d_model 1600 -> 6400)
         # followed by the activation
-        MlpWorkload("gelu_gpt2_xl_mlp", 1024, 6400, 1600, "gelu"),
+        MlpWorkload("gelu_gpt2_xl_mlp", 1024, 6400, 1600, "gelu", mus=(4, 7, 10)),
         # GPT-2 XL MLP down-projection (6400 -> 1600) followed by a layer norm
-        MlpWorkload("ln_gpt2_xl", 1024, 1600, 6400, "layernorm"),
+        MlpWorkload("ln_gpt2_xl", 1024, 1600, 6400, "layernorm", mus=(4, 7, 10)),
     ]
 }
 

@@ -60,8 +60,13 @@ MLP_SAMPLE_ROWS = list(range(0, 1024, 32))
 
 def calibrate_mlp(table, name):
     w = MLP_WORKLOADS[name]
+    for mu in w.mus:
+        calibrate_mlp_mu(table, w, mu)
+
+
+def calibrate_mlp_mu(table, w, mu):
     X, W, gamma, beta = w.inputs()
-    ylo, yref = oracle.ps_gemm(X[MLP_SAMPLE_ROWS], W, mu=4)
+    ylo, yref = oracle.ps_gemm(X[MLP_SAMPLE_ROWS], W, mu=mu)
     sample = f"rows {MLP_SAMPLE_ROWS[0]}..{MLP_SAMPLE_ROWS[-1]} step 32, all columns"
     rate = 0.016
     if w.op == "gelu":
@@ -83,8 +88,8 @@ def calibrate_mlp(table, name):
                 hi = mid
         tau = hi
         got = float(frac(tau))
-    table[f"{w.name}/{w.op}/mu4/rate{rate}"] = {"tau": tau, "sample_rate": got, "sample": sample}
-    print(w.name, w.op, tau, got, flush=True)
+    table[f"{w.name}/{w.op}/mu{mu}/rate{rate}"] = {"tau": tau, "sample_rate": got, "sample": sample}
+    print(w.name, w.op, mu, tau, got, flush=True)
 
 
 def main():
