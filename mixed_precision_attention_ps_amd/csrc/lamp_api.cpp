@@ -431,8 +431,9 @@ MlpLayout mlp_plan(int M, int N, int op, bool need_ylo, bool need_yref, bool nee
             L.yref = L.take(4 * (uint64_t)M * N);
     }
     if (op == lamp::MLP_GELU) {
-        L.err_part = L.take(8 * (uint64_t)M * tn);
-        L.errl_part = L.take(8 * (uint64_t)M * tn);
+        const uint64_t nb = (uint64_t)(N + 31) / 32;   // 32-column blocks
+        L.err_part = L.take(8 * (uint64_t)M * nb);
+        L.errl_part = L.take(8 * (uint64_t)M * nb);
         if (need_mask)
             L.mask = L.take(4 * (uint64_t)M * ((N + 31) / 32));
     }

@@ -29,6 +29,8 @@
 //     the sorted order, the recompute count k*, then LN(y^mix), the mask, the
 //     count and the l2 errors.
 //   * row_reduce_kernel: the GELU error partials per row.
+//   * ps_gemm_narrow_kernel: the fast path on 32 x 32 tiles, for products
+//     whose 64 x 64 tiles would load the CUs unevenly.
 #include "lamp_device.h"
 
 namespace lamp {
@@ -107,7 +109,7 @@ struct GemmArgs {
     float *ylo, *yref;           // [M, N] or null
     float *out;                  // [M, N] (GELU)
     uint32_t *mask;              // [M, W] or null (GELU)
-    double *err_part, *errl_part;   // [M, tiles_n] (GELU)
+    double *err_part, *errl_part;   // [M, W]: per (row, 32-column block) (GELU)
     double tau;
     unsigned long long *exact_tiles;
     long long n_tiles;
@@ -143,7 +145,7 @@ __device__ __forceinline__ void gemm_tile(TileSmem &sm, const double *s_exp, con
             }
         }
         if (EPI == EPI_GELU) {
-            double el = 0.0, em = 0.0;
+            double el0 = 0.0, em0 = 0.0, el1 = 0.0, em1 = 0.0;
             bool sel[4];
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
@@ -158,8 +160,11 @@ __device__ __forceinline__ void gemm_tile(TileSmem &sm, const double *s_exp, con
                         a.ylo[rowoff + j] = sel[c] ? ref[r][c] : lo[r][c];
                     if (a.yref)
                         a.yref[rowoff + j] = ref[r][c];
-                    em += fabs(gm - gr.g);
-                    el += fabs(gl.g - gr.g);
+                    const double dm = fabs(gm - gr.g), dl = fabs(gl.g - gr.g);
+                    em0 += c < 2 ? dm : 0.0;
+                    el0 += c < 2 ? dl : 0.0;
+                    em1 += c < 2 ? 0.0 : dm;
+                    el1 += c < 2 ? 0.0 : dl;
                 }
             }
             // mask words: key tx + 16 c of this row group is bit (tx + 16 c) % 32
@@ -169,8 +174,11 @@ __device__ __forceinline__ void gemm_tile(TileSmem &sm, const double *s_exp, con
 #pragma unroll
             for (int c = 0; c < 4; ++c)
                 bits[c] = (uint32_t)(__ballot(sel[c]) >> gsh) & 0xffffu;
-            em = group16_sum(em);
-            el = group16_sum(el);
+            // partials per 32-column block: keys tx, tx + 16 | tx + 32, tx + 48
+            em0 = group16_sum(em0);
+            el0 = group16_sum(el0);
+            em1 = group16_sum(em1);
+            el1 = group16_sum(el1);
             if (i < a.M && tx == 0) {
                 if (a.mask) {
                     const uint32_t w0 = bits[0] | (bits[1] << 16), w1 = bits[2] | (bits[3] << 16);
@@ -179,8 +187,14 @@ __device__ __forceinline__ void gemm_tile(TileSmem &sm, const double *s_exp, con
                     if (2 * tj + 1 < a.W)
                         a.mask[(size_t)i * a.W + 2 * tj + 1] = w1;
                 }
-                a.err_part[(size_t)i * a.tiles_n + tj] = em;
-                a.errl_part[(size_t)i * a.tiles_n + tj] = el;
+                if (2 * tj < a.W) {
+                    a.err_part[(size_t)i * a.W + 2 * tj] = em0;
+                    a.errl_part[(size_t)i * a.W + 2 * tj] = el0;
+                }
+                if (2 * tj + 1 < a.W) {
+                    a.err_part[(size_t)i * a.W + 2 * tj + 1] = em1;
+                    a.errl_part[(size_t)i * a.W + 2 * tj + 1] = el1;
+                }
             }
         }
     }
@@ -232,23 +246,194 @@ __global__ __launch_bounds__(kThreads) void ps_gemm_kernel(GemmArgs a)
     }
 }
 
-// Per-row sums of the GELU error partials, in tile order.
+// ---------------------------------------------------------------------------
+// Narrow fast-path tiles: 32 x 32 outputs per work-group, 2 x 2 per thread.
+//
+// A product with few 64 x 64 tiles (the layer-norm shape: 1024 x 1600, 400
+// tiles, 1600 waves for 1024 SIMDs) leaves the SIMDs that hold two waves to
+// set the time.  A dot cannot be split over K without changing the
+// sequential PS(mu) sums, so the finer grain comes from fewer outputs per
+// thread: four times the waves, each a quarter of the work.  Same PS(mu)
+// multiply-add and the same blocked order as the wide tile; the LDS holds
+// [d][row] and [d][slot] slices of 32 rows, key j in slot (j % 16) * 2 + j / 16
+// so that a thread reads its two keys as one 8-byte load.  Fast path only:
+// a 32 x 32 tile takes the fast path exactly when the 64 x 64 tile holding it
+// does (the operand flags are per 64-row block), and those 64 x 64 tiles are
+// the generic kernel's.
+// ---------------------------------------------------------------------------
+constexpr int kNarrow = 32;
+
+struct alignas(16) NarrowSmem {
+    float q[kDChunk][kNarrow];
+    float qs[kDChunk][kNarrow];
+    float k[kDChunk][kNarrow];
+};
+
+__device__ __forceinline__ int narrow_slot(int j) { return (j & 15) * 2 + (j >> 4); }
+
+template <int P>
+__device__ __forceinline__ void narrow_flush(float (&lo)[2][2], float (&blk)[2][2],
+                                             const PsConst &pc)
+{
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            lo[r][c] = ps_round_bits(lo[r][c] + blk[r][c], pc.sh, pc.half_m1, pc.keep);
+            blk[r][c] = 0.0f;
+        }
+}
+
+template <int EPI, int P>
+__global__ __launch_bounds__(kThreads) void ps_gemm_narrow_kernel(GemmArgs a)
+{
+    __shared__ NarrowSmem sm;
+    __shared__ double s_exp[64];
+    const int tiles_n32 = (a.N + kNarrow - 1) / kNarrow;
+    const int ti = (int)(blockIdx.x / tiles_n32), tj = (int)(blockIdx.x % tiles_n32);
+    if (a.unsafe_x[ti >> 1] || a.unsafe_w[tj >> 1])
+        return;   // the generic kernel's 64 x 64 tile
+    if (EPI == EPI_GELU)
+        exp_table_fill(s_exp);
+    constexpr bool BLOCKED = P != 0;
+    const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4, lane = tid & 63;
+    const int row0 = ti * kNarrow, col0 = tj * kNarrow, K = a.K;
+    const PsConst pc = a.pc;
+    float lo[2][2], ref[2][2], blk[2][2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+            lo[r][c] = ref[r][c] = blk[r][c] = 0.0f;
+    // one float4 of x and of W per thread and slice: row tid / 8, d (tid % 8) * 4
+    const int lrow = tid >> 3, ld = (tid & 7) * 4;
+    const float *xb = a.x + (size_t)row0 * K, *wb = a.w + (size_t)col0 * K;
+    const int xrows = a.M - row0, wrows = a.N - col0;
+    float4 xv = load_slice(xb, lrow, xrows, K, ld);
+    float4 wv = load_slice(wb, lrow, wrows, K, ld);
+    const int run = P == kDChunk ? pc.blk : K;
+    for (int r0 = 0; r0 < K; r0 += run) {
+        const int r1 = min(K, r0 + run);
+        for (int d0 = r0; d0 < r1; d0 += kDChunk) {
+            __syncthreads();
+            {
+                const float xa[4] = {xv.x, xv.y, xv.z, xv.w};
+                const float wa[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    sm.q[ld + e][lrow] = xa[e];
+                    sm.qs[ld + e][lrow] = xa[e] * pc.qscale;
+                    sm.k[ld + e][narrow_slot(lrow)] = wa[e];
+                }
+            }
+            __syncthreads();
+            if (d0 + kDChunk < K) {
+                xv = load_slice(xb, lrow, xrows, K, d0 + kDChunk + ld);
+                wv = load_slice(wb, lrow, wrows, K, d0 + kDChunk + ld);
+            }
+#pragma unroll
+            for (int dd = 0; dd < kDChunk; ++dd) {
+                const float2 qv = *reinterpret_cast<const float2 *>(&sm.q[dd][ty * 2]);
+                const float2 sv = *reinterpret_cast<const float2 *>(&sm.qs[dd][ty * 2]);
+                const float2 kv = *reinterpret_cast<const float2 *>(&sm.k[dd][tx * 2]);
+                const float qa[2] = {qv.x, qv.y}, sa[2] = {sv.x, sv.y}, ka[2] = {kv.x, kv.y};
+#pragma unroll
+                for (int r = 0; r < 2; ++r)
+#pragma unroll
+                    for (int c = 0; c < 2; ++c)
+                        ps_mac_fast(qa[r], sa[r], ka[c], BLOCKED ? blk[r][c] : lo[r][c],
+                                    ref[r][c], pc.sh, pc.half_m1, pc.keep);
+                if (BLOCKED && P < kDChunk && dd % (P ? P : 1) == (P ? P : 1) - 1)
+                    narrow_flush<P>(lo, blk, pc);
+            }
+        }
+        if (BLOCKED)
+            narrow_flush<P>(lo, blk, pc);
+    }
+
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int i = row0 + ty * 2 + r;
+        const size_t rowoff = (size_t)(i < a.M ? i : 0) * a.N;
+        float ylo[2], yref[2];
+        bool valid[2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            ylo[c] = lo[r][c] * pc.out_scale;
+            yref[c] = ref[r][c] * pc.s;
+            valid[c] = i < a.M && col0 + tx + 16 * c < a.N;
+        }
+        if (EPI == EPI_STORE) {
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                if (!valid[c])
+                    continue;
+                const int j = col0 + tx + 16 * c;
+                if (a.ylo)
+                    a.ylo[rowoff + j] = ylo[c];
+                if (a.yref)
+                    a.yref[rowoff + j] = yref[c];
+            }
+        } else {
+            double em = 0.0, el = 0.0;
+            bool sel[2];
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const int j = col0 + tx + 16 * c;
+                const Gelu gl = gelu64((double)ylo[c], s_exp);
+                sel[c] = valid[c] && fabs(gl.dg * (double)ylo[c]) > a.tau;
+                const Gelu gr = gelu64((double)yref[c], s_exp);
+                const double gm = sel[c] ? gr.g : gl.g;
+                if (valid[c]) {
+                    a.out[rowoff + j] = (float)gm;
+                    if (a.ylo)   // y^mix
+                        a.ylo[rowoff + j] = sel[c] ? yref[c] : ylo[c];
+                    if (a.yref)
+                        a.yref[rowoff + j] = yref[c];
+                    em += fabs(gm - gr.g);
+                    el += fabs(gl.g - gr.g);
+                }
+            }
+            // key tx + 16 c is bit tx + 16 c of word tj; lanes 16 (lane / 16)
+            // .. + 15 hold row pair ty
+            const int gsh = lane & 48;
+            const uint32_t b0 = (uint32_t)(__ballot(sel[0]) >> gsh) & 0xffffu;
+            const uint32_t b1 = (uint32_t)(__ballot(sel[1]) >> gsh) & 0xffffu;
+            em = group16_sum(em);
+            el = group16_sum(el);
+            if (i < a.M && tx == 0) {
+                if (a.mask)
+                    a.mask[(size_t)i * a.W + tj] = b0 | (b1 << 16);
+                a.err_part[(size_t)i * a.W + tj] = em;
+                a.errl_part[(size_t)i * a.W + tj] = el;
+            }
+        }
+    }
+}
+
+// Per-row sums of the GELU error partials (one per 32-column block): one wave
+// per row, lane-strided partial sums and a wave reduction.
 __global__ __launch_bounds__(kThreads) void row_reduce_kernel(const double *ep, const double *elp,
-                                                              int M, int tiles_n, double *err,
+                                                              int M, int nb, double *err,
                                                               double *errl)
 {
-    const int i = blockIdx.x * kThreads + threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int i = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (i >= M)
-        return;
+        return;   // no barrier below: each wave owns its row
     double e = 0.0, el = 0.0;
-    for (int t = 0; t < tiles_n; ++t) {
-        e += ep[(size_t)i * tiles_n + t];
-        el += elp[(size_t)i * tiles_n + t];
+    for (int t = lane; t < nb; t += 64) {
+        e += ep[(size_t)i * nb + t];
+        el += elp[(size_t)i * nb + t];
     }
-    if (err)
-        err[i] = e;
-    if (errl)
-        errl[i] = el;
+    e = wave_sum(e);
+    el = wave_sum(el);
+    if (lane == 0) {
+        if (err)
+            err[i] = e;
+        if (errl)
+            errl[i] = el;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -445,6 +630,23 @@ __global__ __launch_bounds__(kThreads) void ln_lamp_kernel(LnArgs a)
     }
 }
 
+// Fraction of the last round of work-groups over the 256 CUs that is full:
+// n work-groups of equal work take ceil(n / 256) rounds.
+static double cu_balance(long long n)
+{
+    const double rounds = (double)((n + 255) / 256);
+    return (double)n / (256.0 * rounds);
+}
+
+// The narrow tiles when they spread the product over the CUs clearly more
+// evenly than the 64 x 64 tiles (measured on MI355X: 640 and 800 tiles, and
+// fewer than 256, gain 13-170 %; tile counts that are multiples of 256 run
+// better wide).
+static bool use_narrow_tiles(long long tiles64, long long tiles32)
+{
+    return cu_balance(tiles32) > cu_balance(tiles64) + 0.05;
+}
+
 // ---------------------------------------------------------------------------
 static PsConst gemm_ps_const(int mu, int block, int K)
 {
@@ -522,16 +724,40 @@ hipError_t launch_mlp(const MlpProblem &p, const MlpBuffers &b, hipStream_t st,
     if ((e = hipGetLastError()) != hipSuccess || (e = rec(2 * 6 + 1)) != hipSuccess ||
         (e = rec(2 * 1)) != hipSuccess)
         return e;
-    if (p.mu <= 10)
-        LAMP_GEMM_LAUNCH(true, dim3(gfast));
+    if (p.mu <= 10) {
+        const long long n32 = (long long)((p.M + kNarrow - 1) / kNarrow) *
+                              ((p.N + kNarrow - 1) / kNarrow);
+        if (use_narrow_tiles(a.n_tiles, n32)) {
+            if (n32 > 0x7fffffffLL)
+                return hipErrorInvalidValue;
+            const dim3 g32((unsigned)n32);
+#define LAMP_NARROW_LAUNCH(EPIK)                                                                  \
+    do {                                                                                          \
+        switch (run_width(a.pc.blk)) {                                                            \
+        case 0: hipLaunchKernelGGL((ps_gemm_narrow_kernel<EPIK, 0>), g32, block, 0, st, a); break;   \
+        case 4: hipLaunchKernelGGL((ps_gemm_narrow_kernel<EPIK, 4>), g32, block, 0, st, a); break;   \
+        case 8: hipLaunchKernelGGL((ps_gemm_narrow_kernel<EPIK, 8>), g32, block, 0, st, a); break;   \
+        case 16: hipLaunchKernelGGL((ps_gemm_narrow_kernel<EPIK, 16>), g32, block, 0, st, a); break; \
+        default: hipLaunchKernelGGL((ps_gemm_narrow_kernel<EPIK, 32>), g32, block, 0, st, a); break; \
+        }                                                                                         \
+    } while (0)
+            if (gelu)
+                LAMP_NARROW_LAUNCH(EPI_GELU);
+            else
+                LAMP_NARROW_LAUNCH(EPI_STORE);
+#undef LAMP_NARROW_LAUNCH
+        } else {
+            LAMP_GEMM_LAUNCH(true, dim3(gfast));
+        }
+    }
 #undef LAMP_GEMM_LAUNCH
 #undef LAMP_GEMM_LAUNCH1
     if ((e = hipGetLastError()) != hipSuccess || (e = rec(2 * 1 + 1)) != hipSuccess ||
         (e = rec(2 * 4)) != hipSuccess)
         return e;
     if (gelu) {
-        hipLaunchKernelGGL(row_reduce_kernel, dim3((p.M + kThreads - 1) / kThreads), block, 0, st,
-                           b.err_part, b.errl_part, p.M, tiles_n, b.err, b.errl);
+        hipLaunchKernelGGL(row_reduce_kernel, dim3((p.M + 3) / 4), block, 0, st, b.err_part,
+                           b.errl_part, p.M, a.W, b.err, b.errl);
     } else if (p.op == MLP_LAYERNORM) {
         LnArgs l;
         l.ylo = b.ylo;

@@ -80,8 +80,11 @@ __device__ __forceinline__ double exp_delta(float from, float to, const double *
 // exp(m_ref - m_mix), the softmax term of a selected score (whose y^mix is
 // y^ref).  Two double exps per score; the row factors are per tile.
 // P: the run width of the blocked PS(mu) order (run_width(a.pc.blk)).
+// Occupancy: at D <= 64 three waves per SIMD (168 registers, a few spilled;
+// 5 % faster than two without spills), at D <= 128 two.
 template <int NB, bool FAST_KERNEL, int P>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FAST_KERNEL ? 2 : 1)))
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(FAST_KERNEL ? (NB == 4 ? 3 : 2) : 1)))
 void relaxed_kernel(RelaxedArgs a)
 {
     constexpr int DV = 16 * NB;

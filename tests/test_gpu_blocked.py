@@ -178,6 +178,11 @@ MLP_CASES = [
     ("gelu", 20, 70, 1600, 4, 0.02, 64),
     ("gelu", 31, 65, 128, 12, 0.1, 16),      # exact double path
     ("gelu", 17, 40, 64, 23, 0.1, 4),        # mu = 23
+    ("gelu", 129, 200, 256, 4, 0.05, 4),     # narrow tiles
+    ("gelu", 129, 200, 100, 4, 0.05, 8),     # narrow tiles, a short last run
+    ("gelu", 70, 300, 256, 4, 0.05, 16),     # narrow tiles
+    ("layernorm", 70, 300, 256, 4, 0.3, 16),
+    ("layernorm", 9, 1600, 6400, 4, 0.3, 64),
     ("layernorm", 9, 1600, 640, 4, 0.2, 32),
     ("layernorm", 20, 70, 96, 10, 0.5, 8),
     ("layernorm", 12, 300, 6400, 4, 0.3, 256),

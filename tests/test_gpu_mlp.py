@@ -164,10 +164,25 @@ def check_ln(g, orc, X, W, gamma, beta, *, mu, eps, tau, rows=None):
 
 
 # ---------------------------------------------------------------------------
+def tile_kind(M, N):
+    """Which fast-path tile the library picks for an M x N product (64 x 64
+    "wide" or 32 x 32 "narrow"): the one that spreads the work-groups more
+    evenly over the 256 CUs (narrow only when clearly better).  Documents the
+    coverage of the cases below."""
+    import math
+
+    def bal(n):
+        return n / (256 * math.ceil(n / 256))
+    t64 = -(-M // 64) * -(-N // 64)
+    t32 = -(-M // 32) * -(-N // 32)
+    return "narrow" if bal(t32) > bal(t64) + 0.05 else "wide"
+
+
 GEMM_CASES = [
     # M, N, K, mu
     (1, 1, 4, 4),
     (70, 130, 256, 4),
+    (130, 300, 100, 4),     # narrow tiles, ragged M, N and K
     (33, 97, 100, 7),       # K not a multiple of the 32-wide chunk
     (64, 64, 1600, 10),
     (65, 66, 68, 12),       # exact double path (mu > 10)
@@ -191,6 +206,8 @@ def test_gemm_scores(dev, orc, M, N, K, mu):
 GELU_CASES = [
     # M, N, K, mu, tau
     (1, 1, 4, 4, 0.1),
+    (70, 300, 100, 4, 0.05),    # narrow tiles, ragged
+    (200, 450, 1600, 7, 0.02),  # narrow tiles
     (70, 130, 256, 4, 0.1),
     (33, 97, 100, 7, 0.05),
     (64, 64, 64, 4, 0.0),
@@ -210,6 +227,39 @@ def test_gelu_small(dev, orc, M, N, K, mu, tau):
         assert g["stats"]["n_exact_tiles"] == 0
 
 
+def test_tile_kinds_covered():
+    kinds = {tile_kind(M, N) for (M, N, *_rest) in GEMM_CASES + GELU_CASES + LN_CASES}
+    assert kinds == {"wide", "narrow"}
+    assert tile_kind(1024, 1600) == "narrow" and tile_kind(1024, 2048) == "wide"
+
+
+@pytest.mark.parametrize("op,M,N,K", [("gemm", 1024, 2048, 64), ("gelu", 1024, 2048, 96),
+                                      ("layernorm", 2048, 1024, 64)])
+def test_wide_tiles_at_size(dev, orc, op, M, N, K):
+    """Products whose 64 x 64 tiles fill the CUs evenly take the wide tiles;
+    sampled rows against the oracle."""
+    import torch
+    from mixed_precision_attention_ps_amd import lamp
+    assert tile_kind(M, N) == "wide"
+    X, W, gamma, beta = make_mlp(M, N, K, w_std=0.1, seed=M + N)
+    rows = [0, 1, 63, 64, 500, M - 1]
+    if op == "gemm":
+        note(f"gemm M={M} N={N} K={K}")
+        x, w = to_dev(dev, X, W)
+        ylo, yref = lamp.lamp_gemm_scores(x, w, mu=4)
+        ol, orf = orc.ps_gemm(X[rows], W, mu=4)
+        full = np.ones((len(rows), N), bool)
+        parity.assert_bits(ylo.cpu().numpy()[rows], ol, full, "PS(mu) products")
+        parity.assert_bits(yref.cpu().numpy()[rows], orf, full, "FP32 products")
+    elif op == "gelu":
+        g = run_gelu(dev, X, W, mu=4, tau=0.1)
+        check_gelu(g, orc, X, W, mu=4, tau=0.1, rows=rows)
+    else:
+        g = run_ln(dev, X, W, gamma, beta, mu=4, eps=1e-5, tau=0.3)
+        _, ties = check_ln(g, orc, X, W, gamma, beta, mu=4, eps=1e-5, tau=0.3, rows=rows)
+        assert ties == 0
+
+
 def test_gelu_tau_infinite(dev, orc):
     X, W, _, _ = make_mlp(40, 100, 128, w_std=0.05, seed=1)
     g = run_gelu(dev, X, W, mu=4, tau=np.inf)
@@ -227,6 +277,28 @@ def test_gelu_special_inputs(dev, orc, kind):
     with np.errstate(all="ignore"):
         check_gelu(g, orc, X, W, mu=4, tau=0.1)
     assert g["stats"]["n_exact_tiles"] > 0
+
+
+@pytest.mark.parametrize("op", ["gelu", "layernorm"])
+def test_mixed_fast_and_exact_blocks(dev, orc, op):
+    """One 64-row block of x and one of W hold values outside the fast path's
+    range: their tiles go to the exact path, every other tile to the (narrow)
+    fast tiles, and the two must agree with the oracle together."""
+    M, N, K = 130, 300, 96
+    assert tile_kind(M, N) == "narrow"
+    X, W, gamma, beta = make_mlp(M, N, K, w_std=0.05, seed=11)
+    X[70, 5] = np.float32(2.0 ** 45)
+    W[200, 3] = np.float32(2.0 ** -60)
+    if op == "gelu":
+        g = run_gelu(dev, X, W, mu=4, tau=0.1)
+        with np.errstate(all="ignore"):
+            check_gelu(g, orc, X, W, mu=4, tau=0.1)
+    else:
+        g = run_ln(dev, X, W, gamma, beta, mu=4, eps=1e-5, tau=0.3)
+        with np.errstate(all="ignore"):
+            check_ln(g, orc, X, W, gamma, beta, mu=4, eps=1e-5, tau=0.3)
+    # x blocks {1} x all W blocks + W block {3} x the other x blocks
+    assert g["stats"]["n_exact_tiles"] == 5 + 2
 
 
 def test_gelu_workspace_and_stream(dev, orc):
