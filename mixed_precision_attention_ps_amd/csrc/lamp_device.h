@@ -214,9 +214,26 @@ __device__ __forceinline__ void compute_slice(const TileSmem &sm, TileAcc &acc, 
 
 // Full-D accumulation of one 64x64 tile: rows row0.. of Qh (nq rows), keys
 // col0.. of Kh (nk rows); both row-major with D columns.
+// Issue priority from a wave's progress through a long dot: the waves that
+// are behind (first quarter of D) get the highest priority.  The arbiter
+// otherwise favours the oldest waves, which then finish first and leave the
+// last stretch of a one-round launch to one or two waves per SIMD, where the
+// FP32 and integer halves of the multiply-add no longer issue side by side.
+// Measured on a 1024 x 1600 x 6400 product: 2.07 -> 1.90 ms.
+__device__ __forceinline__ void progress_priority(int d0, int D)
+{
+    switch ((int)(((long long)d0 * 4) / D)) {
+    case 0: __builtin_amdgcn_s_setprio(3); break;
+    case 1: __builtin_amdgcn_s_setprio(2); break;
+    case 2: __builtin_amdgcn_s_setprio(1); break;
+    default: __builtin_amdgcn_s_setprio(0); break;
+    }
+}
+
 // P: the run width of the blocked order as compute_slice takes it (0 =
-// sequential; 4, 8, 16; 32 for runs of pc.blk >= 32).
-template <int PATH, int P = 0>
+// sequential; 4, 8, 16; 32 for runs of pc.blk >= 32).  PRIO: progress-based
+// issue priority (long dots: the matrix product).
+template <int PATH, int P = 0, bool PRIO = false>
 __device__ __forceinline__ void score_tile(TileSmem &sm, TileAcc &acc, const float *Qh,
                                            const float *Kh, int row0, int col0, int nq, int nk,
                                            int D, const PsConst &pc)
@@ -255,6 +272,8 @@ __device__ __forceinline__ void score_tile(TileSmem &sm, TileAcc &acc, const flo
             __syncthreads();
             stage_slice<PATH>(sm, qv, kv, tid, pc.qscale);
             __syncthreads();
+            if (PRIO)
+                progress_priority(d0, D);
             if (d0 + kDChunk < D) {
 #pragma unroll
                 for (int u = 0; u < kSliceV4; ++u) {

@@ -120,7 +120,7 @@ __device__ __forceinline__ void gemm_tile(TileSmem &sm, const double *s_exp, con
                                           int ti, int tj)
 {
     TileAcc acc;
-    score_tile<PATH, P>(sm, acc, a.x, a.w, ti * kTile, tj * kTile, a.M, a.N, a.K, a.pc);
+    score_tile<PATH, P, true>(sm, acc, a.x, a.w, ti * kTile, tj * kTile, a.M, a.N, a.K, a.pc);
     float lo[4][4], ref[4][4];
     tile_scores<PATH, P>(acc, a.pc, lo, ref);
     const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4, lane = tid & 63;
@@ -327,6 +327,7 @@ __global__ __launch_bounds__(kThreads) void ps_gemm_narrow_kernel(GemmArgs a)
                 }
             }
             __syncthreads();
+            progress_priority(d0, K);
             if (d0 + kDChunk < K) {
                 xv = load_slice(xb, lrow, xrows, K, d0 + kDChunk + ld);
                 wv = load_slice(wb, lrow, wrows, K, d0 + kDChunk + ld);
@@ -638,13 +639,13 @@ static double cu_balance(long long n)
     return (double)n / (256.0 * rounds);
 }
 
-// The narrow tiles when they spread the product over the CUs clearly more
-// evenly than the 64 x 64 tiles (measured on MI355X: 640 and 800 tiles, and
-// fewer than 256, gain 13-170 %; tile counts that are multiples of 256 run
-// better wide).
+// The narrow tiles for products of fewer than 1024 wide tiles that they
+// spread over the CUs clearly more evenly (measured on MI355X with the
+// progress priority: 25-800 tiles gain 8-160 %, except multiples of 256;
+// from 1024 tiles on the wide tiles run 2-9 % faster).
 static bool use_narrow_tiles(long long tiles64, long long tiles32)
 {
-    return cu_balance(tiles32) > cu_balance(tiles64) + 0.05;
+    return tiles64 < 1024 && cu_balance(tiles32) > cu_balance(tiles64) + 0.05;
 }
 
 // ---------------------------------------------------------------------------

@@ -166,16 +166,16 @@ def check_ln(g, orc, X, W, gamma, beta, *, mu, eps, tau, rows=None):
 # ---------------------------------------------------------------------------
 def tile_kind(M, N):
     """Which fast-path tile the library picks for an M x N product (64 x 64
-    "wide" or 32 x 32 "narrow"): the one that spreads the work-groups more
-    evenly over the 256 CUs (narrow only when clearly better).  Documents the
-    coverage of the cases below."""
+    "wide" or 32 x 32 "narrow"): narrow for fewer than 1024 wide tiles when it
+    spreads the work-groups clearly more evenly over the 256 CUs.  Documents
+    the coverage of the cases below."""
     import math
 
     def bal(n):
         return n / (256 * math.ceil(n / 256))
     t64 = -(-M // 64) * -(-N // 64)
     t32 = -(-M // 32) * -(-N // 32)
-    return "narrow" if bal(t32) > bal(t64) + 0.05 else "wide"
+    return "narrow" if t64 < 1024 and bal(t32) > bal(t64) + 0.05 else "wide"
 
 
 GEMM_CASES = [
