@@ -127,14 +127,11 @@ __global__ __launch_bounds__(kThreads) void strict_rows_kernel(RowsArgs a)
 #pragma unroll
     for (int t = 0; t < kRowChunk; ++t) {
         const int j0 = 64 * t;
-        if (j0 < S) {
+        if (t < nch) {   // chunks past the valid keys: zero mask words below
             const int j = j0 + lane;
-            bool sel = false;
-            if (t < nch) {
-                const bool valid = j < n;
-                const double rest = (valid && v[t] == m) ? rest_at_max : L - e[t];
-                sel = valid && e[t] * rest * fabs((double)v[t]) > tau_l2;
-            }
+            const bool valid = j < n;
+            const double rest = (valid && v[t] == m) ? rest_at_max : L - e[t];
+            const bool sel = valid && e[t] * rest * fabs((double)v[t]) > tau_l2;
             const uint64_t b = __ballot(sel);
             if (a.mask) {
                 const int w = (j0 >> 5) + lane;
@@ -147,6 +144,9 @@ __global__ __launch_bounds__(kThreads) void strict_rows_kernel(RowsArgs a)
             total += (uint32_t)__popcll(b);
         }
     }
+    if (a.mask)   // the mask words of the chunks past the valid keys
+        for (int w = 2 * nch + lane; w < a.W; w += 64)
+            a.mask[r * (uint64_t)a.W + w] = 0u;
     // e in FP32 from here on (probabilities only: p = e / L_mix); the empty
     // asm pins the conversion here, so the doubles die before the recompute
     float ef[kRowChunk];
@@ -270,8 +270,9 @@ __global__ __launch_bounds__(kThreads) void strict_rows_kernel(RowsArgs a)
     // 1 / L_mix (lane 0) and 1 / L_ref (lane 1) by one division
     const double rcp = 1.0 / (lane == 0 ? Lmix : Lr);
     if (corrected) {
-        // p = e / L_mix.
-        const double inv = lane_read(rcp, 0);
+        // p = e / L_mix, in FP32: e and 1 / L_mix rounded to FP32 and their
+        // product, at most 3 roundings (1.8e-7 of p)
+        const float inv = (float)lane_read(rcp, 0);
         uint32_t before = 0;
 #pragma unroll
         for (int t = 0; t < kRowChunk; ++t) {
@@ -287,7 +288,7 @@ __global__ __launch_bounds__(kThreads) void strict_rows_kernel(RowsArgs a)
                         ev = sel ? eh : ev;
                         before += (uint32_t)__popcll(b);
                     }
-                    pv = j < n ? (float)((double)ev * inv) : 0.0f;
+                    pv = j < n ? ev * inv : 0.0f;
                 }
                 buf_store_f32(p_rs, 4u * (uint32_t)j, pv);
             }
