@@ -300,6 +300,8 @@ def bench_mlp(args, w):
     n_out = M * N
     rate = st["n_selected"] / n_out
     value = n_out / (wall / args.steps)
+    # the fast-path product kernel (64 x 64 or 32 x 32 tiles, whichever the
+    # library picks for this shape; its traffic entry is keyed the same way)
     kname = "ps_gemm_kernel"
     w_alg = 9 * K + run_flush_ops(K, args.ps_block)
     t_kernel_ms = stages["scores"]
