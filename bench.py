@@ -85,22 +85,33 @@ def load_traffic(kernel: str, workload: str, launches_per_step: int = 1):
     return ent.get("bytes_per_launch")
 
 
-def cpu_baseline(Q, K, V, w, mode_id, mu, tau, heads_n, seed, ps_block=0):
+CPU_TARGET_S = 10.0   # wall time the oracle sample should take
+
+
+def cpu_baseline(Q, K, V, w, mode_id, mu, tau, seed, ps_block=0):
+    """The oracle on whole heads of the workload, spread over the layer, until
+    about CPU_TARGET_S seconds have passed (or every head is done)."""
     import numpy as np
     import oracle
     oracle.build(force=False)
     BH = w.B * w.H
-    heads = sorted(set(int(x) for x in np.linspace(0, BH - 1, heads_n)))
+    order = [int(x) for x in np.random.default_rng(0).permutation(BH)]
     threads = oracle.max_threads()
     per_head = w.S * (w.S + 1) // 2 if w.causal else w.S * w.S
-    t0 = time.perf_counter()
-    oracle.lamp_heads(Q, K, V, causal=w.causal, mu=mu, tau=tau, mode=mode_id, heads=heads,
-                      seed=seed, ps_block=ps_block, want=("out", "kl", "count", "mask", "probs"))
-    dt = time.perf_counter() - t0
-    n = per_head * len(heads)
+    done, dt = 0, 0.0
+    while done < BH and dt < CPU_TARGET_S:
+        heads = order[done:done + 8]
+        t0 = time.perf_counter()
+        oracle.lamp_heads(Q, K, V, causal=w.causal, mu=mu, tau=tau, mode=mode_id, heads=heads,
+                          seed=seed, ps_block=ps_block,
+                          want=("out", "kl", "count", "mask", "probs"))
+        dt += time.perf_counter() - t0
+        done += len(heads)
+    n = per_head * done
     return {"value": n / dt, "unit": "scores/s", "cores": threads, "kind": "oracle",
-            "sample": f"{len(heads)} of {BH} heads (all rows) of {w.name}, same mu/tau/mode; "
-                      f"{n} valid scores in {dt:.2f} s wall, {threads} OpenMP threads"}
+            "sample": f"{done} of {BH} heads (all rows, heads in a seeded random order) of "
+                      f"{w.name}, same mu/tau/mode; {n} valid scores in {dt:.2f} s wall, "
+                      f"{threads} OpenMP threads"}
 
 
 def copy_calibration(args, dev):
@@ -115,23 +126,27 @@ def copy_calibration(args, dev):
         del a, b
 
 
-def decode_cpu_baseline(Q, K, V, w, nq, mu, tau, heads_n, ps_block=0):
+def decode_cpu_baseline(Q, K, V, w, nq, mu, tau, ps_block=0):
     import numpy as np
     import oracle
     oracle.build(force=False)
     BH = w.B * w.H
-    heads = sorted(set(int(x) for x in np.linspace(0, BH - 1, heads_n)))
+    order = [int(x) for x in np.random.default_rng(0).permutation(BH)]
     threads = oracle.max_threads()
     S = w.S
-    t0 = time.perf_counter()
-    oracle.lamp_heads(Q, K, V, causal=w.causal, mu=mu, tau=tau, mode=oracle.RELAXED, heads=heads,
-                      rows=(S - nq, S), ps_block=ps_block,
-                      want=("out", "kl", "count", "mask", "probs"))
-    dt = time.perf_counter() - t0
     per_head = sum((S - nq + t + 1) if w.causal else S for t in range(nq))
-    n = per_head * len(heads)
+    done, dt = 0, 0.0
+    while done < BH and dt < CPU_TARGET_S:
+        heads = order[done:done + 8]
+        t0 = time.perf_counter()
+        oracle.lamp_heads(Q, K, V, causal=w.causal, mu=mu, tau=tau, mode=oracle.RELAXED,
+                          heads=heads, rows=(S - nq, S), ps_block=ps_block,
+                          want=("out", "kl", "count", "mask", "probs"))
+        dt += time.perf_counter() - t0
+        done += len(heads)
+    n = per_head * done
     return {"value": n / dt, "unit": "scores/s", "cores": threads, "kind": "oracle",
-            "sample": f"{len(heads)} of {BH} heads, their {nq} decode rows, of {w.name}; "
+            "sample": f"{done} of {BH} heads, their {nq} decode rows, of {w.name}; "
                       f"{n} valid scores in {dt:.2f} s wall, {threads} OpenMP threads"}
 
 
@@ -222,27 +237,32 @@ def bench_decode(args, w):
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")
-        rec["cpu_baseline"] = decode_cpu_baseline(Q, K, V, w, nq, args.mu, tau, 8, args.ps_block)
+        rec["cpu_baseline"] = decode_cpu_baseline(Q, K, V, w, nq, args.mu, tau, args.ps_block)
     print(json.dumps(rec), flush=True)
 
 
-def mlp_cpu_baseline(X, W, gamma, beta, w, mu, tau, rows_n, ps_block=0):
+def mlp_cpu_baseline(X, W, gamma, beta, w, mu, tau, ps_block=0):
     import numpy as np
     import oracle
     oracle.build(force=False)
-    rows = np.linspace(0, w.M - 1, rows_n).astype(int)
+    order = np.random.default_rng(0).permutation(w.M)
     threads = oracle.max_threads()
-    t0 = time.perf_counter()
-    ylo, yref = oracle.ps_gemm(X[rows], W, mu=mu, ps_block=ps_block)
-    if w.op == "gelu":
-        oracle.gelu_lamp(ylo, yref, tau=tau)
-    else:
-        oracle.ln_lamp(ylo, yref, gamma, beta, eps=w.eps, tau=tau)
-    dt = time.perf_counter() - t0
-    n = rows.size * w.N
+    done, dt = 0, 0.0
+    while done < w.M and dt < CPU_TARGET_S:
+        rows = np.sort(order[done:done + 64])
+        t0 = time.perf_counter()
+        ylo, yref = oracle.ps_gemm(X[rows], W, mu=mu, ps_block=ps_block)
+        if w.op == "gelu":
+            oracle.gelu_lamp(ylo, yref, tau=tau)
+        else:
+            oracle.ln_lamp(ylo, yref, gamma, beta, eps=w.eps, tau=tau)
+        dt += time.perf_counter() - t0
+        done += rows.size
+    n = done * w.N
     return {"value": n / dt, "unit": "outputs/s", "cores": threads, "kind": "oracle",
-            "sample": f"{rows.size} of {w.M} rows (all {w.N} columns) of {w.name}, same mu/tau; "
-                      f"{n} outputs in {dt:.2f} s wall, {threads} OpenMP threads"}
+            "sample": f"{done} of {w.M} rows (all {w.N} columns, rows in a seeded random order) "
+                      f"of {w.name}, same mu/tau; {n} outputs in {dt:.2f} s wall, "
+                      f"{threads} OpenMP threads"}
 
 
 def bench_mlp(args, w):
@@ -327,7 +347,7 @@ def bench_mlp(args, w):
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")
-        rec["cpu_baseline"] = mlp_cpu_baseline(X, W, gamma, beta, w, args.mu, tau, 64,
+        rec["cpu_baseline"] = mlp_cpu_baseline(X, W, gamma, beta, w, args.mu, tau,
                                                args.ps_block)
     print(json.dumps(rec), flush=True)
 
@@ -344,7 +364,6 @@ def main():
     ap.add_argument("--tau", type=float, default=None, help="explicit tau (overrides --rate)")
     ap.add_argument("--no-probs", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=24)
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="run a plain copy of this many MiB first (counter calibration)")
     ap.add_argument("--nq", type=int, default=1, help="decode workloads: queries per head")
@@ -478,8 +497,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")
-        rec["cpu_baseline"] = cpu_baseline(Q, K, V, w, mode_id, args.mu, tau, args.cpu_heads, 0,
-                                           args.ps_block)
+        rec["cpu_baseline"] = cpu_baseline(Q, K, V, w, mode_id, args.mu, tau, 0, args.ps_block)
     print(json.dumps(rec), flush=True)
 
 
