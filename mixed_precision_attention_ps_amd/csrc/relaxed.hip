@@ -149,18 +149,6 @@ void relaxed_kernel(RelaxedArgs a)
             relaxed_tile_scores<PATH_FP32, P>(sm.u.tile, a, Qh, Kh, row0, col0, lo, ref);
         }
 
-        // V tile loads start now and land during the softmax epilogue.
-        float4 vreg[V4];
-#pragma unroll
-        for (int u = 0; u < V4; ++u) {
-            const int e = tid + u * kThreads;
-            const int key = e / (DV / 4), col = (e % (DV / 4)) * 4;
-            float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (e < NV4 && col0 + key < S && col < D)
-                x = *reinterpret_cast<const float4 *>(Vh + (size_t)(col0 + key) * D + col);
-            vreg[u] = x;
-        }
-
         float pmix[4][4];
         const int gsh = (lane >> 4) * 16;
         // one query row at a time, with a compile-time row index so that the
@@ -286,6 +274,19 @@ void relaxed_kernel(RelaxedArgs a)
         row_step(std::integral_constant<int, 1>{});
         row_step(std::integral_constant<int, 2>{});
         row_step(std::integral_constant<int, 3>{});
+
+        // V tile: loaded after the softmax epilogue (its registers would
+        // otherwise stay live across it and spill), just before the P.V stage
+        float4 vreg[V4];
+#pragma unroll
+        for (int u = 0; u < V4; ++u) {
+            const int e = tid + u * kThreads;
+            const int key = e / (DV / 4), col = (e % (DV / 4)) * 4;
+            float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (e < NV4 && col0 + key < S && col < D)
+                x = *reinterpret_cast<const float4 *>(Vh + (size_t)(col0 + key) * D + col);
+            vreg[u] = x;
+        }
 
         // P.V: P tile (aliases the score staging) and V tile to LDS, MFMA.
         __syncthreads();
