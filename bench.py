@@ -374,9 +374,9 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this LAMP build shards nothing across GPUs "
-              "(each (batch, head) is independent; see DESIGN.md for how it would shard). "
-              "Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: every LAMP quantity is per query row, so a layer "
+              "shards over (batch, head) with no exchange and each GPU would run this same "
+              "benchmark on its share; run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
