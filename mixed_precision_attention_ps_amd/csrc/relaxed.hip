@@ -132,6 +132,15 @@ void relaxed_kernel(RelaxedArgs a)
         for (int v = 0; v < 4; ++v)
             acc[q][v] = 0.0;
 
+    // Output rows of this block: a uniform base (scalar registers) and a
+    // 32-bit offset per lane, formed in the loop.  Per-row output addresses
+    // are loop invariants that the compiler hoists out of the key loop; twelve
+    // of them spilled and came back from scratch, each reload a full memory
+    // wait in the epilogue.
+    const uint64_t blk_row = (uint64_t)bh * S + row0;
+    uint32_t *const mask_blk = a.mask ? a.mask + blk_row * (uint64_t)a.W : nullptr;
+    float *const ymix_blk = a.ymix_raw ? a.ymix_raw + blk_row * (uint64_t)S : nullptr;
+    float *const yref_blk = a.yref_out ? a.yref_out + blk_row * (uint64_t)S : nullptr;
     for (int t = 0; t <= t_end; ++t) {
         const int col0 = t * kTile;
         float lo[4][4], ref[4][4];
@@ -192,24 +201,28 @@ void relaxed_kernel(RelaxedArgs a)
                 bits[c] = (uint32_t)(__ballot(sel[c]) >> gsh) & 0xffffu;
             const uint32_t w0 = bits[0] | (bits[1] << 16), w1 = bits[2] | (bits[3] << 16);
             if (i < S) {
-                if (a.mask && tx == 0) {
-                    const uint64_t mrow = ((uint64_t)bh * S + i) * (uint64_t)a.W;
+                // row within the block, opaque to the compiler so that its
+                // offsets are formed here (one multiply) rather than hoisted
+                uint32_t lr = (uint32_t)(ty * 4 + r);
+                asm volatile("" : "+v"(lr));
+                if (mask_blk && tx == 0) {
+                    const uint32_t mo = lr * (uint32_t)a.W;
                     if (2 * t < a.W)
-                        a.mask[mrow + 2 * t] = w0;
+                        mask_blk[mo + 2 * t] = w0;
                     if (2 * t + 1 < a.W)
-                        a.mask[mrow + 2 * t + 1] = w1;
+                        mask_blk[mo + 2 * t + 1] = w1;
                 }
-                if (a.ymix_raw || a.yref_out) {
-                    const uint64_t yrow = ((uint64_t)bh * S + i) * (uint64_t)S;
+                if (ymix_blk || yref_blk) {
+                    const uint32_t yo = lr * (uint32_t)S;
 #pragma unroll
                     for (int c = 0; c < 4; ++c) {
                         if (!valid[c])
                             continue;
-                        const int j = col0 + tx + 16 * c;
-                        if (a.ymix_raw)
-                            a.ymix_raw[yrow + j] = mix[c];
-                        if (a.yref_out)
-                            a.yref_out[yrow + j] = ref[r][c];
+                        const uint32_t j = (uint32_t)(col0 + tx + 16 * c);
+                        if (ymix_blk)
+                            ymix_blk[yo + j] = mix[c];
+                        if (yref_blk)
+                            yref_blk[yo + j] = ref[r][c];
                     }
                 }
             }
