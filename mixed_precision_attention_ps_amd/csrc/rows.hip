@@ -44,17 +44,23 @@ struct RowsArgs {
 // registers then hold no per-chunk state.
 //
 // Probabilities: p_j = exp(y_j - lse_mix) = e_j / L_mix for every key whose
-// score did not change (e_j = exp(y_j - m) is already in registers), and
-// e_hi / L_mix for a recomputed key (e_hi formed in the recompute loop and
-// kept, rounded to FP32, in LDS).  Only a row that takes the full pass (the
-// correction would cancel or overflow) evaluates exp(y - lse_mix) per key.
+// score did not change (e_j = exp(y_j - m), kept in FP32 after the criterion),
+// and e_hi / L_mix for a recomputed key (e_hi = exp(y_hi - m) formed in the
+// recompute loop and kept, rounded to FP32, in the LDS list).  Only a row
+// that takes the full pass (the correction would cancel or overflow)
+// evaluates exp(y - lse_mix) per key; it forms its recomputed scores a second
+// time, since the list then holds e_hi.
+//
+// The kernel is bound by VALU issue (about 1,100 wave instructions per row of
+// 1,024 keys): one double exponential per valid key, none in the probability
+// loop.
 template <int D4>
-__global__ __launch_bounds__(kThreads) void strict_rows_kernel(RowsArgs a)
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5))) void strict_rows_kernel(RowsArgs a)
 {
-    // per wave: the selected keys (compacted, in key order); the recompute
-    // loop overwrites each slot with the bits of its recomputed score
-    __shared__ uint32_t s_list[4][64 * kRowChunk];
-    __shared__ float s_ehi[4][64 * kRowChunk];       // exp(y_hi - m), same slots
+    // per wave: the selected keys (compacted, in key order), and per listed
+    // key e_hi = exp(y_hi - m) in FP32 (full-pass rows: y_hi)
+    __shared__ uint16_t s_key[4][64 * kRowChunk];
+    __shared__ float s_val[4][64 * kRowChunk];
     __shared__ float4 s_q[4][64];                    // the wave's query row (D <= 256)
     __shared__ double s_exp[64];                     // 2^(k/64) for exp64
     exp_table_fill(s_exp);
@@ -120,17 +126,22 @@ __global__ __launch_bounds__(kThreads) void strict_rows_kernel(RowsArgs a)
     const double rest_at_max = A + (double)(cnt - 1);
 
     // Criterion 2 z (1 - z) |y| > tau with z = e / L and 1 - z = rest / L,
-    // evaluated as e rest |y| > tau L^2 / 2; mask words and compaction.
+    // evaluated as e rest |y| > tau L^2 / 2; mask words and compaction.  e in
+    // FP32 is kept for the probabilities (p = e / L_mix).
     const double tau_l2 = a.tau * (L * L) * 0.5;
     uint32_t selbits = 0;
     uint32_t total = 0;
+    float ef[kRowChunk];
 #pragma unroll
     for (int t = 0; t < kRowChunk; ++t) {
         const int j0 = 64 * t;
+        ef[t] = 0.0f;
         if (t < nch) {   // chunks past the valid keys: zero mask words below
             const int j = j0 + lane;
             const bool valid = j < n;
-            const double rest = (valid && v[t] == m) ? rest_at_max : L - e[t];
+            const bool at = valid && v[t] == m;
+            ef[t] = (float)e[t];
+            const double rest = at ? rest_at_max : L - e[t];
             const bool sel = valid && e[t] * rest * fabs((double)v[t]) > tau_l2;
             const uint64_t b = __ballot(sel);
             if (a.mask) {
@@ -139,7 +150,7 @@ __global__ __launch_bounds__(kThreads) void strict_rows_kernel(RowsArgs a)
                     a.mask[r * (uint64_t)a.W + w] = lane ? (uint32_t)(b >> 32) : (uint32_t)b;
             }
             if (sel)
-                s_list[wave][total + lanes_below(b)] = (uint32_t)j;
+                s_key[wave][total + lanes_below(b)] = (uint16_t)j;
             selbits |= (sel ? 1u : 0u) << t;
             total += (uint32_t)__popcll(b);
         }
@@ -147,14 +158,6 @@ __global__ __launch_bounds__(kThreads) void strict_rows_kernel(RowsArgs a)
     if (a.mask)   // the mask words of the chunks past the valid keys
         for (int w = 2 * nch + lane; w < a.W; w += 64)
             a.mask[r * (uint64_t)a.W + w] = 0u;
-    // e in FP32 from here on (probabilities only: p = e / L_mix); the empty
-    // asm pins the conversion here, so the doubles die before the recompute
-    float ef[kRowChunk];
-#pragma unroll
-    for (int t = 0; t < kRowChunk; ++t) {
-        ef[t] = (float)e[t];
-        asm volatile("" : "+v"(ef[t]));
-    }
 
     // Reference statistics from the score kernel's per-tile partials.
     const bool kl = a.part != nullptr;
@@ -182,11 +185,9 @@ __global__ __launch_bounds__(kThreads) void strict_rows_kernel(RowsArgs a)
             s_q[wave][lane] = qg[lane];
     }
     const float4 *q4 = s_q[wave];
-    double dL = 0.0, dA = 0.0;
-    for (uint32_t ei = lane; ei < total; ei += 64) {
-        const uint32_t j = s_list[wave][ei];
+    // y_hi of key j: sequential FP32 dot (multiply, then add, d ascending)
+    auto dot_hi = [&](uint32_t j) {
         const float4 *k4 = reinterpret_cast<const float4 *>(a.k + (bh * (uint64_t)S + j) * a.D);
-        const float yl = y[j];
         float acc = 0.0f;
         auto mac4 = [&acc](float4 x, float4 z) {
             float p0 = x.x * z.x;
@@ -203,7 +204,7 @@ __global__ __launch_bounds__(kThreads) void strict_rows_kernel(RowsArgs a)
             // loop instead of 4*D4 registers hoisted out of it
             uint32_t qoff = 0;
             asm volatile("" : "+v"(qoff));
-            constexpr int kB = D4 < 8 ? D4 : 8;   // D4 is a multiple of 4
+            constexpr int kB = 4;   // D4 is a multiple of 4
 #pragma unroll
             for (int b0 = 0; b0 < D4; b0 += kB) {
                 float4 kr[kB];
@@ -218,10 +219,15 @@ __global__ __launch_bounds__(kThreads) void strict_rows_kernel(RowsArgs a)
             for (int d4 = 0; d4 < a.D / 4; ++d4)
                 mac4(q4[d4], k4[d4]);
         }
-        const float yhi = acc * a.s;
+        return acc * a.s;
+    };
+    double dL = 0.0, dA = 0.0;
+    for (uint32_t ei = lane; ei < total; ei += 64) {
+        const uint32_t j = s_key[wave][ei];
+        const float yl = y[j];
+        const float yhi = dot_hi(j);
         const double ehi = exp64((double)yhi - (double)m, s_exp);
-        s_list[wave][ei] = __float_as_uint(yhi);
-        s_ehi[wave][ei] = (float)ehi;
+        s_val[wave][ei] = (float)ehi;
         if (a.ymix_out)   // y^mix is y^lo in place: only recomputed keys change
             a.ymix_out[r * (uint64_t)S + j] = yhi;
         dL += ehi - exp64_nonpos((double)yl - (double)m, s_exp);
@@ -255,7 +261,7 @@ __global__ __launch_bounds__(kThreads) void strict_rows_kernel(RowsArgs a)
                 const bool sel = (selbits >> t) & 1u;
                 const uint64_t b = __ballot(sel);
                 if (b) {
-                    const float h = __uint_as_float(s_list[wave][slot(b, before)]);
+                    const float h = s_val[wave][slot(b, before)];
                     v[t] = sel ? h : v[t];
                     before += (uint32_t)__popcll(b);
                 }
@@ -284,7 +290,7 @@ __global__ __launch_bounds__(kThreads) void strict_rows_kernel(RowsArgs a)
                     const uint64_t b = __ballot(sel);
                     float ev = ef[t];
                     if (b) {
-                        const float eh = s_ehi[wave][slot(b, before)];
+                        const float eh = s_val[wave][slot(b, before)];
                         ev = sel ? eh : ev;
                         before += (uint32_t)__popcll(b);
                     }
@@ -294,7 +300,10 @@ __global__ __launch_bounds__(kThreads) void strict_rows_kernel(RowsArgs a)
             }
         }
     } else {
-        // Full pass over y^mix.
+        // Full pass over y^mix: the list's scores formed again
+        for (uint32_t ei = lane; ei < total; ei += 64)
+            s_val[wave][ei] = dot_hi(s_key[wave][ei]);
+        __builtin_amdgcn_wave_barrier();
         load_ymix();
         float mm = -INFINITY;
 #pragma unroll
