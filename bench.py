@@ -367,6 +367,9 @@ def main():
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="run a plain copy of this many MiB first (counter calibration)")
     ap.add_argument("--nq", type=int, default=1, help="decode workloads: queries per head")
+    ap.add_argument("--relaxed-path", type=int, default=0, choices=[0, 1, 2],
+                    help="relaxed mode: 0 the library's choice, 1 the fused one-pass kernel, "
+                         "2 score tiles then the row pass (rows of <= 1024 keys)")
     ap.add_argument("--ps-block", type=int, default=0,
                     help="PS(mu) accumulation order: 0 sequential, else runs of this many "
                          "products (blocked order)")
@@ -410,7 +413,8 @@ def main():
     def step(events=None):
         lamp.lamp_attention_fwd(q, k, v, causal=w.causal, mu=args.mu, tau=tau, mode=mode_id,
                                 out=out, probs=probs, recompute_mask=mask, want_stats=False,
-                                row_kl=row_kl, stage_events=events, ps_block=args.ps_block)
+                                row_kl=row_kl, stage_events=events, ps_block=args.ps_block,
+                                relaxed_path=args.relaxed_path)
 
     for _ in range(args.warmup):
         step()
@@ -429,9 +433,13 @@ def main():
     wall = time.perf_counter() - t0
     gpu_ms = t_start.elapsed_time(t_stop)
 
-    if args.mode == "relaxed":
+    # relaxed rows of <= 1024 keys run as score tiles + row pass when probs are
+    # written (library's choice) or when asked for
+    relaxed_rows = args.mode == "relaxed" and S <= 1024 and (
+        args.relaxed_path == 2 or (args.relaxed_path == 0 and probs is not None))
+    if args.mode == "relaxed" and not relaxed_rows:
         ran = ["scan", "exact", "scores"] + (["finish"] if probs is not None else [])
-    elif args.mode == "strict" and S <= 1024:   # fused row pass: select + recompute in one
+    elif S <= 1024 and args.mode in ("strict", "relaxed"):   # fused row pass
         ran = ["scan", "exact", "scores", "select", "finish"]
     else:
         ran = ["scan", "exact", "scores", "select", "recompute", "finish"]
@@ -445,18 +453,20 @@ def main():
     # untimed: rate and KL of the same call
     _, st = lamp.lamp_attention_fwd(q, k, v, causal=w.causal, mu=args.mu, tau=tau, mode=mode_id,
                                     out=out, probs=probs, recompute_mask=mask, want_stats=True,
-                                    ps_block=args.ps_block)
+                                    ps_block=args.ps_block, relaxed_path=args.relaxed_path)
     n_valid = st["n_valid"]
     rate = st["n_selected"] / n_valid
     ms_per_step = 1e3 * wall / args.steps
     value = n_valid / (wall / args.steps)
 
-    # dominant kernel: the PS(mu)+FP32 score tiles (strict, random) or the fused
-    # relaxed kernel; algorithmic VALU slots per valid score: 8D (PS(mu) dot:
-    # multiply, add, two 3-instruction roundings per MAC) + D (FP32 reference
-    # dot at two lanes per slot) [+ 20 for the fused softmax/criterion/KL].
-    kname = "relaxed_kernel" if args.mode == "relaxed" else "ps_scores_kernel"
-    w_alg = 9 * D + (20 if args.mode == "relaxed" else 0) + run_flush_ops(D, args.ps_block)
+    # dominant kernel: the PS(mu)+FP32 score tiles (strict, random, relaxed in
+    # two passes) or the fused relaxed kernel; algorithmic VALU slots per valid
+    # score: 8D (PS(mu) dot: multiply, add, two 3-instruction roundings per
+    # MAC) + D (FP32 reference dot at two lanes per slot) [+ 20 for the fused
+    # softmax/criterion/KL].
+    fused_relaxed = args.mode == "relaxed" and not relaxed_rows
+    kname = "relaxed_kernel" if fused_relaxed else "ps_scores_kernel"
+    w_alg = 9 * D + (20 if fused_relaxed else 0) + run_flush_ops(D, args.ps_block)
     t_kernel_ms = stages.get("scores")
     achieved = w_alg * n_valid / (t_kernel_ms * 1e-3) if t_kernel_ms else None
     traffic = load_traffic(kname, w.name)
@@ -481,6 +491,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "H": H, "S": S, "D": D, "causal": w.causal,
                    "mu": args.mu, "mode": args.mode, "ps_block": args.ps_block, "tau": tau,
+                   "relaxed_impl": ("two-pass" if relaxed_rows else "fused one-pass")
+                   if args.mode == "relaxed" else None,
                    "target_rate": args.rate,
                    "rate": rate, "probs": not args.no_probs, "mask": True, "row_kl": True,
                    "parallelism": "none (1 GPU)"},

@@ -111,6 +111,19 @@ typedef struct {
                                  reference and recompute stay sequential.
                                  Other values: LAMP_ERR_INVALID_ARG (< 0) or
                                  LAMP_ERR_UNSUPPORTED                         */
+    int relaxed_path;         /* LAMP_RELAXED only: which implementation.
+                                 0 = the library's choice: rows of <= 1024
+                                 keys with probs written run in two passes
+                                 (score tiles, then one wave per row: the
+                                 relaxed rule, FP32 recompute, softmax,
+                                 probabilities; then P.V), everything else in
+                                 the fused one-pass kernel (online softmax).
+                                 1 = always the fused one-pass kernel.
+                                 2 = two passes whenever S <= 1024.
+                                 Masks, counts and y^mix are the same either
+                                 way; probabilities, out and KL agree within
+                                 the stated tolerances.  Other values:
+                                 LAMP_ERR_INVALID_ARG                         */
 } lamp_params;
 
 /* Stages, for lamp_params.stage_events. */

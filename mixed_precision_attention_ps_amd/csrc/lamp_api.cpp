@@ -11,7 +11,8 @@
 //                     strict counts, then hash selection) -> gather FP32
 //                     recompute -> softmax + P.V + KL -> [stats]
 //   relaxed:          operand scan -> fused one-pass kernel -> [probs pass]
-//                     -> [stats]
+//                     -> [stats]; rows of <= 1024 keys with probs: the strict
+//                     sequence with the relaxed rule in the row pass
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -152,9 +153,10 @@ struct Layout {
 
 struct Needs {
     bool ymix, yref, row_count, row_kl, row_kl_lowp;
-    bool fused;   // strict rows of <= 1024 keys: fused row pass
+    bool fused;   // rows of <= 1024 keys through the fused row pass (strict;
+                  // relaxed in two passes)
     bool pbuf;    // fused: probabilities need their own buffer
-    bool part;    // fused: reference statistics per tile (KL wanted)
+    bool part;    // fused: per-tile partials (KL wanted; relaxed rule)
 };
 
 constexpr int kFusedMaxS = 1024;
@@ -170,7 +172,7 @@ Layout plan(const Sizes &z, int mode, const Needs &n)
         L.row_kl = L.take(8 * z.n_rows);
     if (n.row_kl_lowp)
         L.row_kl_lowp = L.take(8 * z.n_rows);
-    if (mode == LAMP_RELAXED) {
+    if (mode == LAMP_RELAXED && !n.fused) {
         if (n.ymix) {   // probs requested: per-row statistics for the probs pass
             L.row_m = L.take(4 * z.n_rows);
             L.row_l = L.take(8 * z.n_rows);
@@ -577,7 +579,7 @@ size_t lamp_workspace_bytes(int B, int H, int S, int D, int mode, int want_probs
     Needs n{mode == LAMP_RELAXED ? want_probs != 0 : want_probs == 0, true, true, true, true,
             false, false, false};
     size_t total = plan(z, mode, n).total;
-    if (mode == LAMP_STRICT && S <= kFusedMaxS) {
+    if ((mode == LAMP_STRICT || mode == LAMP_RELAXED) && S <= kFusedMaxS) {
         Needs f{want_probs == 0, false, true, true, true, true, false, true};
         const size_t tf = plan(z, mode, f).total;
         total = tf > total ? tf : total;
@@ -606,6 +608,8 @@ static int run(const float *q, const float *k, const float *v, int B, int H, int
     rc = check_ps_block(p.ps_block);
     if (rc != LAMP_OK)
         return rc;
+    if (p.relaxed_path < 0 || p.relaxed_path > 2)
+        return set_error(LAMP_ERR_INVALID_ARG, "relaxed_path must be 0, 1 or 2");
     (void)hipGetLastError();   // launches below are checked with hipGetLastError
     hipStream_t st = (hipStream_t)p.stream;
     const bool want_stats = stats != nullptr;
@@ -614,15 +618,18 @@ static int run(const float *q, const float *k, const float *v, int B, int H, int
     need.row_count = p.row_count == nullptr;
     need.row_kl = p.row_kl == nullptr && want_stats;
     need.row_kl_lowp = p.row_kl_lowp == nullptr && want_stats;
-    need.fused = mode == LAMP_STRICT && S <= kFusedMaxS;
+    // relaxed rows of <= 1024 keys in two passes (score tiles, row pass)
+    const bool relaxed_rows = mode == LAMP_RELAXED && S <= kFusedMaxS &&
+                              (p.relaxed_path == 2 || (p.relaxed_path == 0 && probs != nullptr));
+    need.fused = (mode == LAMP_STRICT && S <= kFusedMaxS) || relaxed_rows;
     const bool want_kl = want_stats || p.row_kl || p.row_kl_lowp;
-    if (mode == LAMP_RELAXED) {
+    if (mode == LAMP_RELAXED && !need.fused) {
         need.ymix = probs != nullptr;
         need.yref = false;
     } else if (need.fused) {
         need.ymix = p.scores_mix == nullptr && probs == nullptr;
         need.pbuf = p.scores_mix != nullptr && probs == nullptr;
-        need.part = want_kl;
+        need.part = want_kl || relaxed_rows;
     } else {
         need.ymix = p.scores_mix == nullptr && probs == nullptr;
         need.yref = p.scores_ref == nullptr;
@@ -671,7 +678,7 @@ static int run(const float *q, const float *k, const float *v, int B, int H, int
     LAMP_HIP_TRY(lamp::launch_operand_scan(P, unsafe, st), "operand scan launch");
     LAMP_HIP_TRY(tm.end(LAMP_STAGE_SCAN), "hipEventRecord");
 
-    if (mode == LAMP_RELAXED) {
+    if (mode == LAMP_RELAXED && !need.fused) {
         float *ymix_raw = p.scores_mix ? p.scores_mix : probs;
         float *row_m = at<float>(ws, L.row_m);
         double *row_l = at<double>(ws, L.row_l);
@@ -712,7 +719,7 @@ static int run(const float *q, const float *k, const float *v, int B, int H, int
         LAMP_HIP_TRY(tm.begin(LAMP_STAGE_SELECT), "hipEventRecord");
         LAMP_HIP_TRY(lamp::launch_strict_rows(P, ybuf, part, mask, row_count, pbuf, p.scores_mix,
                                               part ? row_kl : nullptr,
-                                              part ? row_kl_lowp : nullptr, st),
+                                              part ? row_kl_lowp : nullptr, relaxed_rows, st),
                      "row kernel launch");
         LAMP_HIP_TRY(tm.end(LAMP_STAGE_SELECT), "hipEventRecord");
         LAMP_HIP_TRY(tm.begin(LAMP_STAGE_FINISH), "hipEventRecord");

@@ -45,11 +45,13 @@ struct Problem {
 hipError_t launch_operand_scan(const Problem &p, uint8_t *unsafe, hipStream_t st);
 
 // Softmax statistics of the FP32 reference scores of one row over one 64-key
-// tile: m = max y^ref, L = sum exp(y^ref - m), B = sum exp(y^ref - m)(y^ref - y^lo).
+// tile: m = max y^ref, L = sum exp(y^ref - m), B = sum exp(y^ref - m)(y^ref - y^lo),
+// and m_lo = max y^lo over the tile's valid keys (the block maximum of the
+// relaxed rule).
 struct RefPartial {
     double L, B;
     float m;
-    float pad;
+    float m_lo;
 };
 
 // PS(mu) and FP32 scores of every valid pair into dense [BH, S, S] buffers
@@ -60,14 +62,16 @@ hipError_t launch_ps_scores(const Problem &p, const uint8_t *unsafe, float *ylo,
                             RefPartial *part, unsigned long long *exact_tiles, bool fast,
                             hipStream_t st);
 
-// Fused strict row pass (S <= 1024): row softmax statistics, the strict
-// criterion, mask words, compaction of the selected keys, their gather FP32
-// recompute, the corrected softmax, probabilities into pbuf (full rows, zeros
-// past the valid keys), y^mix (optional), counts and the row KLs (when part
-// is given).  ylo may alias pbuf or ymix_out (rows are read before written).
+// Fused row pass (S <= 1024): row softmax statistics, the strict criterion
+// (relaxed = false) or the relaxed one (relaxed = true: needs part, for the
+// 64-key block maxima), mask words, compaction of the selected keys, their
+// gather FP32 recompute, the corrected softmax, probabilities into pbuf (full
+// rows, zeros past the valid keys), y^mix (optional), counts and the row KLs
+// (when part is given).  ylo may alias pbuf or ymix_out (rows are read before
+// written).
 hipError_t launch_strict_rows(const Problem &p, const float *ylo, const RefPartial *part,
                               uint32_t *mask, uint32_t *row_count, float *pbuf, float *ymix_out,
-                              double *row_kl, double *row_kl_lowp, hipStream_t st);
+                              double *row_kl, double *row_kl_lowp, bool relaxed, hipStream_t st);
 
 // out = P.V from given probabilities [BH, S, S] (valid keys; P.V on MFMA).
 hipError_t launch_pv(const Problem &p, const float *probs, float *out, hipStream_t st);

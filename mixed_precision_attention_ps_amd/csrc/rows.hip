@@ -1,9 +1,12 @@
-// rows.hip -- fused strict row pass for rows of at most 1024 keys.
+// rows.hip -- fused row pass for rows of at most 1024 keys.
 //
 // LAMP summary, "Implementation strategy": step 2 (look-ahead selection from
 // the baseline output, with the softmax rule of "Theoretical foundation" item
-// 3: recompute y_j iff 2 z_j (1 - z_j) |y_j| > tau) and step 3 (recompute the
-// selected components at FP32, then apply f), for one attention row per wave:
+// 3: recompute y_j iff 2 z_j (1 - z_j) |y_j| > tau; or the relaxed
+// relative-threshold rule of "Experimental results", read as 2 exp(y_j - m_t)
+// |y_j| > tau with m_t the running maximum over the 64-key blocks up to j's)
+// and step 3 (recompute the selected components at FP32, then apply f), for
+// one attention row per wave:
 //   * the row's PS(mu) scores stay in registers (16 per lane);
 //   * its softmax statistics are formed in double (own exp);
 //   * the criterion gives the mask words (ballots) and a compacted list of the
@@ -51,10 +54,17 @@ struct RowsArgs {
 // evaluates exp(y - lse_mix) per key; it forms its recomputed scores a second
 // time, since the list then holds e_hi.
 //
-// The kernel is bound by VALU issue (about 1,100 wave instructions per row of
+// The kernel is bound by VALU issue (about 1,400 wave instructions per row of
 // 1,024 keys): one double exponential per valid key, none in the probability
 // loop.
-template <int D4>
+//
+// RELAXED: the selection uses exp(y_j - m_t) = e_j exp(m - m_t), with the
+// block maxima of y^lo taken from the score tiles' per-tile partials (lane t
+// holds block t's; a prefix maximum across lanes gives m_t); keys where that
+// product would lose precision (e_j below 1e-300, or a row whose factor
+// overflows) take exp(y_j - m_t) directly.  Everything after the selection is
+// the strict pass's.
+template <int D4, bool RELAXED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5))) void strict_rows_kernel(RowsArgs a)
 {
     // per wave: the selected keys (compacted, in key order), and per listed
@@ -86,11 +96,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5))) v
     const __amdgpu_buffer_rsrc_t y_rs = row_rsrc(y, 4u * (uint32_t)n);
     const __amdgpu_buffer_rsrc_t p_rs = row_rsrc(a.pbuf + r * (uint64_t)S, 4u * (uint32_t)S);
 
-    // The row and its maximum (all 16 loads issued back to back).
+    // The row and its maximum (all 16 loads issued back to back).  This
+    // lane's per-tile partial of the score kernel (tile = lane) is read here
+    // by the relaxed pass (its selection needs the block maxima), after the
+    // selection by the strict one.
     float v[kRowChunk];
 #pragma unroll
     for (int t = 0; t < kRowChunk; ++t)
         v[t] = buf_load_f32(y_rs, 4u * (uint32_t)(lane + 64 * t));
+    RefPartial early{0.0, 0.0, -INFINITY, -INFINITY};
+    if constexpr (RELAXED)
+        if (lane < nch)   // nch = the tiles that hold valid keys
+            early = a.part[r * (uint64_t)a.tiles + lane];
     float m = -INFINITY;
 #pragma unroll
     for (int t = 0; t < kRowChunk; ++t) {
@@ -125,9 +142,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5))) v
     const double L = A + (double)cnt;
     const double rest_at_max = A + (double)(cnt - 1);
 
-    // Criterion 2 z (1 - z) |y| > tau with z = e / L and 1 - z = rest / L,
-    // evaluated as e rest |y| > tau L^2 / 2; mask words and compaction.  e in
-    // FP32 is kept for the probabilities (p = e / L_mix).
+    // Relaxed rule: m_t of chunk t (= 64-key block t) on lane t, the prefix
+    // maximum of the block maxima; f_t = exp(m - m_t) >= 1.
+    float mt = -INFINITY;
+    double ft = 1.0;
+    bool direct_row = false;
+    if constexpr (RELAXED) {
+        mt = early.m_lo;
+#pragma unroll
+        for (int off = 1; off < kRowChunk; off <<= 1) {
+            const float o = __shfl_up(mt, off, 64);
+            if (lane >= off)
+                mt = fmaxf(mt, o);
+        }
+        ft = lane < nch ? exp64((double)m - (double)mt, s_exp) : 1.0;
+        direct_row = __ballot(lane < nch && !(ft < 1e300)) != 0;
+    }
+
+    // Strict criterion 2 z (1 - z) |y| > tau with z = e / L and 1 - z =
+    // rest / L, evaluated as e rest |y| > tau L^2 / 2; relaxed criterion
+    // 2 exp(y - m_t) |y| > tau.  Mask words and compaction.  e in FP32 is
+    // kept for the probabilities (p = e / L_mix).
     const double tau_l2 = a.tau * (L * L) * 0.5;
     uint32_t selbits = 0;
     uint32_t total = 0;
@@ -139,10 +174,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5))) v
         if (t < nch) {   // chunks past the valid keys: zero mask words below
             const int j = j0 + lane;
             const bool valid = j < n;
-            const bool at = valid && v[t] == m;
-            ef[t] = (float)e[t];
-            const double rest = at ? rest_at_max : L - e[t];
-            const bool sel = valid && e[t] * rest * fabs((double)v[t]) > tau_l2;
+            bool sel;
+            if constexpr (RELAXED) {
+                ef[t] = (float)e[t];
+                double E = e[t] * lane_read(ft, t);
+                const bool dir = valid && (direct_row || e[t] < 1e-300);
+                if (__ballot(dir) != 0) {
+                    const float mtt = lane_read(mt, t);
+                    if (dir)
+                        E = exp64((double)v[t] - (double)mtt, s_exp);
+                }
+                sel = valid && 2.0 * E * fabs((double)v[t]) > a.tau;
+            } else {
+                const bool at = valid && v[t] == m;
+                ef[t] = (float)e[t];
+                const double rest = at ? rest_at_max : L - e[t];
+                sel = valid && e[t] * rest * fabs((double)v[t]) > tau_l2;
+            }
             const uint64_t b = __ballot(sel);
             if (a.mask) {
                 const int w = (j0 >> 5) + lane;
@@ -165,10 +213,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5))) v
     float mr = 0.0f;
     if (kl) {
         const int nt = a.causal ? (i / kTile) + 1 : a.tiles;
-        const RefPartial *pp = a.part + r * (uint64_t)a.tiles;
         RefPartial mine{0.0, 0.0, -INFINITY, 0.0f};
-        if (lane < nt)
-            mine = pp[lane];
+        if constexpr (RELAXED)
+            mine = early;
+        else if (lane < nt)
+            mine = a.part[r * (uint64_t)a.tiles + lane];
         mr = wave_max(mine.m);
         const double f = lane < nt ? exp64_nonpos((double)mine.m - (double)mr, s_exp) : 0.0;
         Lr = wave_sum(mine.L * f);
@@ -362,9 +411,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5))) v
 // probabilities may share y^lo's buffer only when y^mix is not asked for.
 hipError_t launch_strict_rows(const Problem &p, const float *ylo, const RefPartial *part,
                               uint32_t *mask, uint32_t *row_count, float *pbuf, float *ymix_out,
-                              double *row_kl, double *row_kl_lowp, hipStream_t st)
+                              double *row_kl, double *row_kl_lowp, bool relaxed, hipStream_t st)
 {
-    if (p.S > 64 * kRowChunk || (ymix_out && (ymix_out != ylo || pbuf == ylo)))
+    if (p.S > 64 * kRowChunk || (ymix_out && (ymix_out != ylo || pbuf == ylo)) ||
+        (relaxed && !part))
         return hipErrorInvalidValue;
     RowsArgs a;
     a.q = p.q;
@@ -386,12 +436,23 @@ hipError_t launch_strict_rows(const Problem &p, const float *ylo, const RefParti
     a.row_kl = row_kl;
     a.row_kl_lowp = row_kl_lowp;
     const uint64_t grid = (p.n_rows + 3) / 4;
-    if (p.D == 64)
-        hipLaunchKernelGGL(strict_rows_kernel<16>, dim3((unsigned)grid), dim3(kThreads), 0, st, a);
-    else if (p.D == 128)
-        hipLaunchKernelGGL(strict_rows_kernel<32>, dim3((unsigned)grid), dim3(kThreads), 0, st, a);
+#define LAMP_ROWS_LAUNCH(RLX)                                                                 \
+    do {                                                                                      \
+        if (p.D == 64)                                                                        \
+            hipLaunchKernelGGL((strict_rows_kernel<16, RLX>), dim3((unsigned)grid),           \
+                               dim3(kThreads), 0, st, a);                                     \
+        else if (p.D == 128)                                                                  \
+            hipLaunchKernelGGL((strict_rows_kernel<32, RLX>), dim3((unsigned)grid),           \
+                               dim3(kThreads), 0, st, a);                                     \
+        else                                                                                  \
+            hipLaunchKernelGGL((strict_rows_kernel<0, RLX>), dim3((unsigned)grid),            \
+                               dim3(kThreads), 0, st, a);                                     \
+    } while (0)
+    if (relaxed)
+        LAMP_ROWS_LAUNCH(true);
     else
-        hipLaunchKernelGGL(strict_rows_kernel<0>, dim3((unsigned)grid), dim3(kThreads), 0, st, a);
+        LAMP_ROWS_LAUNCH(false);
+#undef LAMP_ROWS_LAUNCH
     return hipGetLastError();
 }
 

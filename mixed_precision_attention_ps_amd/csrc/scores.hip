@@ -122,24 +122,28 @@ __device__ __forceinline__ void score_tile_store(TileSmem &sm, const double *s_e
         }
     }
     if (a.part) {
-        // this tile's softmax statistics of the reference scores, per row:
+        // this tile's softmax statistics of the reference scores and the
+        // maximum of its PS(mu) scores, per row:
         // every key is evaluated (no divergent branch) and the keys outside
         // the row are masked out of the sums.  The fast path's scores are
         // finite (its operands are bounded), so its exponential needs no NaN
         // handling; the other paths keep NaN in the sums.
-        float m[4];
+        float m[4], mlo[4];
         bool valid[4][4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int i = ti * kTile + ty * 4 + r;
             m[r] = -INFINITY;
+            mlo[r] = -INFINITY;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const int j = tj * kTile + tx + 16 * c;
                 valid[r][c] = i < a.S && j < a.S && (!a.causal || j <= i);
                 m[r] = fmaxf(m[r], valid[r][c] ? ref[r][c] : -INFINITY);
+                mlo[r] = fmaxf(mlo[r], valid[r][c] ? lo[r][c] : -INFINITY);
             }
             m[r] = group16_max(m[r]);
+            mlo[r] = group16_max(mlo[r]);
         }
         double L[4], B[4];
 #pragma unroll
@@ -170,7 +174,7 @@ __device__ __forceinline__ void score_tile_store(TileSmem &sm, const double *s_e
                 rp.L = L[r];
                 rp.B = B[r];
                 rp.m = m[r];
-                rp.pad = 0.0f;
+                rp.m_lo = mlo[r];
                 a.part[((size_t)bh * a.S + i) * a.tiles + tj] = rp;
             }
         }

@@ -38,7 +38,7 @@ class LampParams(ctypes.Structure):
                 ("row_kl", ctypes.c_void_p), ("row_kl_lowp", ctypes.c_void_p),
                 ("row_count", ctypes.c_void_p), ("scores_mix", ctypes.c_void_p),
                 ("scores_ref", ctypes.c_void_p), ("stage_events", ctypes.c_void_p),
-                ("ps_block", ctypes.c_int)]
+                ("ps_block", ctypes.c_int), ("relaxed_path", ctypes.c_int)]
 
 
 class LampError(RuntimeError):
@@ -148,11 +148,14 @@ def lamp_ps_scores(q, k, *, causal: bool, mu: int, ylo=None, yref=None):
 def lamp_attention_fwd(q, k, v, *, causal: bool, mu: int, tau: float, mode="strict", out=None,
                        probs=None, recompute_mask=None, want_stats: bool = True, seed: int = 0,
                        row_kl=None, row_kl_lowp=None, row_count=None, scores_mix=None,
-                       scores_ref=None, workspace=None, stage_events=None, ps_block: int = 0):
+                       scores_ref=None, workspace=None, stage_events=None, ps_block: int = 0,
+                       relaxed_path: int = 0):
     """LAMP attention forward through lamp_attention_fwd_ex.
 
     q, k, v: float32 [B, H, S, D] device tensors.  Optional outputs are written
-    in place when given.  Returns (out, stats_dict_or_None).
+    in place when given.  relaxed_path (relaxed mode): 0 the library's choice,
+    1 the fused one-pass kernel, 2 two passes (score tiles, row pass) for rows
+    of at most 1024 keys.  Returns (out, stats_dict_or_None).
     """
     B, H, S, D = q.shape
     if out is None:
@@ -162,6 +165,7 @@ def lamp_attention_fwd(q, k, v, *, causal: bool, mu: int, tau: float, mode="stri
     p.stream = torch.cuda.current_stream(q.device).cuda_stream
     p.seed = seed & 0xFFFFFFFFFFFFFFFF
     p.ps_block = int(ps_block)
+    p.relaxed_path = int(relaxed_path)
     if workspace is not None:
         p.workspace = workspace.data_ptr()
         p.workspace_bytes = workspace.numel() * workspace.element_size()

@@ -191,6 +191,27 @@ def test_ps_block_checked_before_any_device_call(lib):
         assert rc == code, (b, rc)
 
 
+def test_relaxed_path_checked_before_any_device_call(lib):
+    from mixed_precision_attention_ps_amd import lamp
+    for rp in (-1, 3, 100):
+        p = lamp.LampParams()
+        p.relaxed_path = rp
+        rc = lib.lamp_attention_fwd_ex(A, A, A, 1, 1, 8, 64, 0, 4, ctypes.c_float(0.1), 1, A,
+                                       None, None, None, ctypes.byref(p))
+        assert rc == -1, (rp, rc)
+
+
+def test_workspace_covers_both_relaxed_paths(lib):
+    # rows of <= 1024 keys: the two-pass relaxed path keeps per-tile partials
+    # (24 bytes per row and tile) and, without probs, the score rows
+    B, H, S = 8, 25, 1024
+    rows, tiles = B * H * S, S // 64
+    with_probs = lib.lamp_workspace_bytes(B, H, S, 64, 1, 1)
+    no_probs = lib.lamp_workspace_bytes(B, H, S, 64, 1, 0)
+    assert with_probs >= 24 * rows * tiles
+    assert no_probs >= 4 * rows * S + 24 * rows * tiles
+
+
 def test_version_and_strerror(lib):
     assert lib.lamp_version() >= 10000
     assert lib.lamp_strerror(0) == b"success"

@@ -62,7 +62,7 @@ def inputs(name):
 
 
 def run_case(dev, orc, name, *, mode, mu, tau, heads, row_ranges, want_probs=True,
-             expect_rate=None):
+             expect_rate=None, relaxed_path=0):
     import torch
     from mixed_precision_attention_ps_amd import lamp
     w = WORKLOADS[name]
@@ -70,7 +70,8 @@ def run_case(dev, orc, name, *, mode, mu, tau, heads, row_ranges, want_probs=Tru
     B, H, S, D = Q.shape
     W = (S + 31) // 32
     BH = B * H
-    note(f"full-size {name} {MODE_NAME[mode]} mu={mu} tau={tau} probs={want_probs}")
+    note(f"full-size {name} {MODE_NAME[mode]} mu={mu} tau={tau} probs={want_probs} "
+         f"relaxed_path={relaxed_path}")
     q, k, v = (torch.from_numpy(x).to(dev) for x in (Q, K, V))
     probs = torch.full((B, H, S, S), -7.0, device=dev) if want_probs else None
     mask = torch.full((B, H, S, W), -1, dtype=torch.int32, device=dev)
@@ -80,7 +81,7 @@ def run_case(dev, orc, name, *, mode, mu, tau, heads, row_ranges, want_probs=Tru
     out, st = lamp.lamp_attention_fwd(q, k, v, causal=w.causal, mu=mu, tau=tau, mode=mode,
                                       probs=probs, recompute_mask=mask, row_kl=row_kl,
                                       row_kl_lowp=row_kl_lowp, row_count=row_count,
-                                      want_stats=True)
+                                      want_stats=True, relaxed_path=relaxed_path)
     torch.cuda.synchronize()
     n_valid = w.n_valid
     assert st["n_valid"] == n_valid
@@ -145,10 +146,12 @@ def test_gpt2_xl_strict(dev, orc, mu, rate):
              expect_rate=rate)
 
 
-def test_gpt2_xl_relaxed(dev, orc):
+# relaxed_path 1: the fused one-pass kernel; 2: score tiles, then the row pass
+@pytest.mark.parametrize("path", [1, 2])
+def test_gpt2_xl_relaxed(dev, orc, path):
     tau = tau_for(XL, "relaxed", 4, 0.016)
     run_case(dev, orc, XL, mode=RELAXED, mu=4, tau=tau, heads=XL_HEADS, row_ranges=[(0, 1024)],
-             expect_rate=0.016)
+             expect_rate=0.016, relaxed_path=path)
 
 
 def test_gpt2_xl_random_control(dev, orc):
