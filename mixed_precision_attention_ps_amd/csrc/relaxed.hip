@@ -444,7 +444,8 @@ __global__ __launch_bounds__(kThreads) void normalise_kernel(const float *ymix, 
                                                              int S, int causal, uint64_t n_rows)
 {
     const int lane = threadIdx.x & 63;
-    const uint64_t r = (uint64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    // wave index through readfirstlane: the row's quantities are scalar
+    const uint64_t r = (uint64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (r >= n_rows)
         return;
     const int i = (int)(r % (uint64_t)S);

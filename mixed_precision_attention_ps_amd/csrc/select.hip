@@ -27,10 +27,13 @@ struct SelectArgs {
 };
 
 constexpr int kSelChunk = 16;   // keys per lane held in registers (1024 per wave)
+constexpr int kSelBatch = 8;    // longer rows: 64-key chunks whose loads issue together
 
 // One wave per row; 4 rows per work-group.  ONE: the whole row fits one
 // register chunk (S <= 1024), so scores and exponentials are read and formed
-// once; otherwise the row is streamed three times.
+// once; otherwise the row is streamed three times, kSelBatch chunks of 64
+// keys at a time with all of a batch's loads issued before its arithmetic
+// (range-checked buffer loads: keys past the row read 0 and are skipped).
 template <bool ONE>
 __global__ __launch_bounds__(kThreads) void strict_select_kernel(SelectArgs a)
 {
@@ -38,7 +41,10 @@ __global__ __launch_bounds__(kThreads) void strict_select_kernel(SelectArgs a)
     exp_table_fill(s_exp);
     __syncthreads();
     const int lane = threadIdx.x & 63;
-    const uint64_t r = (uint64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    // the wave index through readfirstlane: the row and every row quantity
+    // (its length, pointers, buffer ranges, loop bounds) are then scalar
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint64_t r = (uint64_t)blockIdx.x * 4 + wave;
     if (r >= a.n_rows)
         return;
     const int S = a.S;
@@ -46,6 +52,8 @@ __global__ __launch_bounds__(kThreads) void strict_select_kernel(SelectArgs a)
     const int n = a.causal ? i + 1 : S;
     const float *y = a.y + r * (uint64_t)S;
     const float *yr = a.yref + r * (uint64_t)S;
+    const __amdgpu_buffer_rsrc_t y_rs = row_rsrc(y, 4u * (uint32_t)n);
+    const __amdgpu_buffer_rsrc_t r_rs = row_rsrc(yr, 4u * (uint32_t)n);
 
     float vlo[kSelChunk], vref[kSelChunk];
     double elo[kSelChunk];
@@ -61,29 +69,45 @@ __global__ __launch_bounds__(kThreads) void strict_select_kernel(SelectArgs a)
             mr = fmaxf(mr, vref[t]);
         }
     } else {
-        for (int j = lane; j < n; j += 64) {
-            m = fmaxf(m, y[j]);
-            mr = fmaxf(mr, yr[j]);
+        for (int j0 = 0; j0 < n; j0 += 64 * kSelBatch) {
+            float vb[kSelBatch], vrb[kSelBatch];
+#pragma unroll
+            for (int u = 0; u < kSelBatch; ++u) {
+                const uint32_t off = 4u * (uint32_t)(j0 + 64 * u + lane);
+                vb[u] = buf_load_f32(y_rs, off);
+                vrb[u] = buf_load_f32(r_rs, off);
+            }
+#pragma unroll
+            for (int u = 0; u < kSelBatch; ++u)
+                if (j0 + 64 * u + lane < n) {
+                    m = fmaxf(m, vb[u]);
+                    mr = fmaxf(mr, vrb[u]);
+                }
         }
     }
     m = wave_max(m);
     mr = wave_max(mr);
 
     // A: sum of exp(y^lo - m) below the maximum; cnt: keys at the maximum;
-    // Lr, Br: reference sum and sum of e_ref (y^ref - y^lo).
+    // Lr, Br: reference sum and sum of e_ref (y^ref - y^lo).  Branch-free,
+    // with the exponential of a non-positive argument; an argument that is
+    // NaN (a NaN score, or inf - inf) makes the sums it feeds NaN, as a NaN
+    // exponential would.
     double A = 0.0, Lr = 0.0, Br = 0.0;
     int cnt = 0;
+    bool nan_lo = false, nan_ref = false;
     auto accumulate = [&](float v, float vr, double &e) {
-        if (v == m) {
-            cnt++;
-            e = 1.0;
-        } else {
-            e = exp64((double)v - (double)m, s_exp);
-            A += e;
-        }
-        const double er = exp64((double)vr - (double)mr, s_exp);
+        const bool at = v == m;
+        const double dl = (double)v - (double)m, dr = (double)vr - (double)mr;
+        const double x = exp64_nonpos(dl, s_exp);
+        e = at ? 1.0 : x;
+        A += at ? 0.0 : x;
+        cnt += at ? 1 : 0;
+        nan_lo |= !at && dl != dl;
+        const double er = exp64_nonpos(dr, s_exp);
         Lr += er;
         Br += er * ((double)vr - (double)v);
+        nan_ref |= dr != dr;
     };
     if (ONE) {
 #pragma unroll
@@ -94,13 +118,30 @@ __global__ __launch_bounds__(kThreads) void strict_select_kernel(SelectArgs a)
         }
     } else {
         double e;
-        for (int j = lane; j < n; j += 64)
-            accumulate(y[j], yr[j], e);
+        for (int j0 = 0; j0 < n; j0 += 64 * kSelBatch) {
+            float vb[kSelBatch], vrb[kSelBatch];
+#pragma unroll
+            for (int u = 0; u < kSelBatch; ++u) {
+                const uint32_t off = 4u * (uint32_t)(j0 + 64 * u + lane);
+                vb[u] = buf_load_f32(y_rs, off);
+                vrb[u] = buf_load_f32(r_rs, off);
+            }
+#pragma unroll
+            for (int u = 0; u < kSelBatch; ++u)
+                if (j0 + 64 * u + lane < n)
+                    accumulate(vb[u], vrb[u], e);
+        }
     }
     A = wave_sum(A);
     Lr = wave_sum(Lr);
     Br = wave_sum(Br);
     cnt = wave_sum_int(cnt);
+    if (__ballot(nan_lo) != 0)
+        A = __builtin_nan("");
+    if (__ballot(nan_ref) != 0) {
+        Lr = __builtin_nan("");
+        Br = __builtin_nan("");
+    }
     const double L = A + (double)cnt;
     const double rest_at_max = A + (double)(cnt - 1);
     const double lse_lo = (double)m + log(L);
@@ -157,15 +198,23 @@ __global__ __launch_bounds__(kThreads) void strict_select_kernel(SelectArgs a)
             if (64 * t < jend)
                 decide(64 * t, lane + 64 * t, vlo[t], elo[t]);
     } else {
-        for (int j0 = 0; j0 < jend; j0 += 64) {
-            const int j = j0 + lane;
-            float v = 0.0f;
-            double e = 0.0;
-            if (j < n) {
-                v = y[j];
-                e = (v == m) ? 1.0 : exp64((double)v - (double)m, s_exp);
+        for (int j0 = 0; j0 < jend; j0 += 64 * kSelBatch) {
+            float vb[kSelBatch];
+#pragma unroll
+            for (int u = 0; u < kSelBatch; ++u)
+                vb[u] = buf_load_f32(y_rs, 4u * (uint32_t)(j0 + 64 * u + lane));
+#pragma unroll
+            for (int u = 0; u < kSelBatch; ++u) {
+                const int jc = j0 + 64 * u;
+                if (jc < jend) {   // wave-uniform: every lane takes part in the ballots
+                    const int j = jc + lane;
+                    double e = 0.0;
+                    if (j < n)   // a NaN row already has NaN statistics (no key selected)
+                        e = (vb[u] == m) ? 1.0
+                                         : exp64_nonpos((double)vb[u] - (double)m, s_exp);
+                    decide(jc, j, vb[u], e);
+                }
             }
-            decide(j0, j, v, e);
         }
     }
     if (lane == 0)
