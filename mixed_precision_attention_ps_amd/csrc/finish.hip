@@ -217,13 +217,22 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(FinishArgs a)
     }
 
     // Keys past the causal limit of every row in the block: probabilities 0.
-    if (prp && prow_ok) {
-        for (int j = nsteps * kFinKeys + (tid & 3) * 4; j < S; j += 16) {
-            if (vec)
-                *reinterpret_cast<float4 *>(prp + j) = make_float4(0.f, 0.f, 0.f, 0.f);
-            else
-                for (int e = 0; e < 4 && j + e < S; ++e)
-                    prp[j + e] = 0.0f;
+    // Wave w clears rows 16w..16w+15, each row's tail in contiguous 1 KB
+    // stores (64 lanes x 16 bytes).
+    if (!PIN && a.probs) {
+        const int z0 = nsteps * kFinKeys;
+        for (int rr = 0; rr < kFinRows / 4; ++rr) {
+            const int iz = row0 + wave * (kFinRows / 4) + rr;
+            if (iz >= S)
+                break;
+            float *pz = a.probs + ((uint64_t)bh * S + iz) * (uint64_t)S;
+            if (vec) {
+                for (int j = z0 + lane * 4; j < S; j += 256)
+                    *reinterpret_cast<float4 *>(pz + j) = make_float4(0.f, 0.f, 0.f, 0.f);
+            } else {
+                for (int j = z0 + lane; j < S; j += 64)
+                    pz[j] = 0.0f;
+            }
         }
     }
 
