@@ -67,6 +67,18 @@ def test_attention_blocked(dev, orc, B, H, S, D, causal, mu, mode, tau, block):
                  check_probs=S <= 400)
 
 
+# the relaxed cases above take the library's choice (two passes for these
+# short rows with probabilities); the fused one-pass kernel's blocked variants:
+@pytest.mark.parametrize("B,H,S,D,causal,mu,mode,tau,block",
+                         [c for c in ATTN_CASES if c[6] == RELAXED])
+def test_attention_blocked_relaxed_fused(dev, orc, B, H, S, D, causal, mu, mode, tau, block):
+    Q, K, V, _ = make_qkv(B, H, S, D, n_outlier=2, seed=S + D + block)
+    g = run_gpu(dev, Q, K, V, causal=causal, mu=mu, tau=tau, mode=mode, seed=3,
+                ps_block=block, relaxed_path=1)
+    r = run_orc(orc, Q, K, V, causal=causal, mu=mu, tau=tau, mode=mode, seed=3, ps_block=block)
+    compare_full(g, r, Q, V, causal=causal, tau=tau)
+
+
 def test_blocked_scores_differ_and_reference_does_not(dev, orc):
     """The order changes y^lo (a mask-free check on the raw scores: tau =
     +inf keeps y^mix = y^lo) and leaves the FP32 reference alone; a run as
