@@ -454,9 +454,13 @@ struct RecomputeArgs {
 // One work-group per 64 rows: the rows' list segments are concatenated
 // (block-local prefix of the counts) and every thread takes one listed score
 // per pass; the per-row corrections are then summed in list order by one
-// thread per row, so the result does not depend on scheduling.
+// thread per row, so the result does not depend on scheduling.  D4 = D / 4
+// when the head dimension is a compile-time constant: the query and key rows
+// are then read in batches of 8 x 16 bytes issued back to back (one memory
+// wait per batch instead of one per 4 products); 0 for a runtime D.
 constexpr int kRcRows = 64;
 
+template <int D4>
 __global__ __launch_bounds__(kThreads) void recompute_kernel(RecomputeArgs a)
 {
     __shared__ uint32_t s_off[kRcRows + 1];
@@ -512,8 +516,7 @@ __global__ __launch_bounds__(kThreads) void recompute_kernel(RecomputeArgs a)
                 const float4 *k4 = reinterpret_cast<const float4 *>(
                     a.k + (bh * (uint64_t)a.S + j) * (uint64_t)a.D);
                 float acc = 0.0f;
-                for (int d4 = 0; d4 < a.D / 4; ++d4) {
-                    const float4 x = q4[d4], z = k4[d4];
+                auto mac4 = [&acc](float4 x, float4 z) {
                     float p0 = x.x * z.x;
                     acc = acc + p0;
                     float p1 = x.y * z.y;
@@ -522,6 +525,24 @@ __global__ __launch_bounds__(kThreads) void recompute_kernel(RecomputeArgs a)
                     acc = acc + p2;
                     float p3 = x.w * z.w;
                     acc = acc + p3;
+                };
+                if constexpr (D4 > 0) {
+                    constexpr int kB = D4 < 8 ? D4 : 8;   // D4 is a multiple of 4
+#pragma unroll
+                    for (int b0 = 0; b0 < D4; b0 += kB) {
+                        float4 qr[kB], kr[kB];
+#pragma unroll
+                        for (int u = 0; u < kB; ++u) {
+                            qr[u] = q4[b0 + u];
+                            kr[u] = k4[b0 + u];
+                        }
+#pragma unroll
+                        for (int u = 0; u < kB; ++u)
+                            mac4(qr[u], kr[u]);
+                    }
+                } else {
+                    for (int d4 = 0; d4 < a.D / 4; ++d4)
+                        mac4(q4[d4], k4[d4]);
                 }
                 const float yhi = acc * a.s;
                 float *slot = a.ymix + r * (uint64_t)a.S + j;
@@ -579,7 +600,12 @@ hipError_t launch_recompute(const Problem &p, const uint32_t *list, const uint32
     a.rs = rs;
     a.row_kl = row_kl;
     const uint64_t grid = (p.n_rows + kRcRows - 1) / kRcRows;
-    hipLaunchKernelGGL(recompute_kernel, dim3((unsigned)grid), dim3(kThreads), 0, st, a);
+    if (p.D == 64)
+        hipLaunchKernelGGL(recompute_kernel<16>, dim3((unsigned)grid), dim3(kThreads), 0, st, a);
+    else if (p.D == 128)
+        hipLaunchKernelGGL(recompute_kernel<32>, dim3((unsigned)grid), dim3(kThreads), 0, st, a);
+    else
+        hipLaunchKernelGGL(recompute_kernel<0>, dim3((unsigned)grid), dim3(kThreads), 0, st, a);
     return hipGetLastError();
 }
 
