@@ -293,7 +293,7 @@ __global__ __launch_bounds__(kThreads) void random_select_kernel(RandomArgs a)
     __shared__ uint32_t hist[256];
     __shared__ uint32_t s_wtot[4];
     __shared__ uint64_t s_prefix;
-    __shared__ uint32_t s_rank;
+    __shared__ uint32_t s_rank, s_hd;
     __shared__ uint32_t s_eqw[4], s_selw[4];
     __shared__ uint32_t s_eq_before, s_sel_before;
     const uint64_t r = blockIdx.x;
@@ -315,9 +315,14 @@ __global__ __launch_bounds__(kThreads) void random_select_kernel(RandomArgs a)
     }
 
     // Radix select of the k-th smallest hash T (8 digits of 8 bits, MSB first);
-    // `rank` ends as the number of keys equal to T that are taken.
+    // `rank` ends as the number of keys equal to T that are taken.  A digit
+    // whose bucket is taken whole (the rank is its last element; with 64-bit
+    // hashes usually after two digits) ends the search: the selection is then
+    // every key whose hash lies at or below the bucket's end, `ub`.
     uint64_t prefix = 0, pmask = 0;
     uint32_t rank = k;
+    bool whole = false;
+    uint64_t ub = 0;
     if (k > 0) {
         for (int shift = 56; shift >= 0; shift -= 8) {
             hist[tid] = 0;
@@ -344,11 +349,17 @@ __global__ __launch_bounds__(kThreads) void random_select_kernel(RandomArgs a)
             if ((cum < rank && rank <= cum + hd) || (tid == 255 && rank > cum + hd)) {
                 s_prefix = prefix | ((uint64_t)tid << shift);
                 s_rank = rank - cum;
+                s_hd = hd;
             }
             __syncthreads();
             prefix = s_prefix;
             rank = s_rank;
             pmask |= 255ull << shift;
+            if (rank == s_hd) {   // uniform: the whole bucket is taken
+                whole = true;
+                ub = prefix | ((1ull << shift) - 1ull);
+                break;
+            }
         }
     }
     const uint64_t T = prefix;
@@ -372,8 +383,8 @@ __global__ __launch_bounds__(kThreads) void random_select_kernel(RandomArgs a)
             } else {
                 h = hash(j);
             }
-            lt = h < T;
-            eq = h == T;
+            lt = whole ? h <= ub : h < T;
+            eq = !whole && h == T;
         }
         const uint64_t tb = __ballot(eq);
         if (lane == 0)
