@@ -12,7 +12,8 @@
 //   * the criterion gives the mask words (ballots) and a compacted list of the
 //     selected keys in LDS (ballot + lane prefix);
 //   * the selected scores are recomputed by a gather FP32 dot (sequential,
-//     multiply then add) and scattered back into the register row;
+//     multiply then add), one lane per listed key; each one's exp(y_hi - m)
+//     goes into its list slot and its y_hi into y^mix (when asked for);
 //   * the row's log-sum-exp is corrected for the changed terms (or recomputed
 //     over the row when the correction would cancel or overflow);
 //   * probabilities are written as full rows (zeros past the valid keys);
