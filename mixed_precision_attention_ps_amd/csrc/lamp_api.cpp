@@ -180,6 +180,8 @@ Layout plan(const Sizes &z, int mode, const Needs &n)
     } else if (n.fused) {
         if (n.ymix)
             L.ymix = L.take(4 * z.n_scores);
+        if (n.yref)
+            L.yref = L.take(4 * z.n_scores);
         if (n.pbuf)
             L.pbuf = L.take(4 * z.n_scores);
         if (n.part)
@@ -580,7 +582,7 @@ size_t lamp_workspace_bytes(int B, int H, int S, int D, int mode, int want_probs
             false, false, false};
     size_t total = plan(z, mode, n).total;
     if ((mode == LAMP_STRICT || mode == LAMP_RELAXED) && S <= kFusedMaxS) {
-        Needs f{want_probs == 0, false, true, true, true, true, false, true};
+        Needs f{want_probs == 0, true, true, true, true, true, false, true};
         const size_t tf = plan(z, mode, f).total;
         total = tf > total ? tf : total;
     }
@@ -630,6 +632,10 @@ static int run(const float *q, const float *k, const float *v, int B, int H, int
         need.ymix = p.scores_mix == nullptr && probs == nullptr;
         need.pbuf = p.scores_mix != nullptr && probs == nullptr;
         need.part = want_kl || relaxed_rows;
+        // the score tiles form y^ref for every pair when they form the
+        // partials: kept, the row pass takes the selected scores' FP32 values
+        // from it instead of forming each dot again
+        need.yref = need.part && p.scores_ref == nullptr;
     } else {
         need.ymix = p.scores_mix == nullptr && probs == nullptr;
         need.yref = p.scores_ref == nullptr;
@@ -705,20 +711,21 @@ static int run(const float *q, const float *k, const float *v, int B, int H, int
         // probs (probabilities in place), else the workspace
         float *ybuf = p.scores_mix ? p.scores_mix : (probs ? probs : at<float>(ws, L.ymix));
         float *pbuf = probs ? probs : (p.scores_mix ? at<float>(ws, L.pbuf) : ybuf);
+        float *yref = p.scores_ref ? p.scores_ref : at<float>(ws, L.yref);
         auto *part = at<lamp::RefPartial>(ws, L.part);
         LAMP_HIP_TRY(tm.begin(LAMP_STAGE_EXACT), "hipEventRecord");
-        LAMP_HIP_TRY(lamp::launch_ps_scores(P, unsafe, ybuf, p.scores_ref, part,
+        LAMP_HIP_TRY(lamp::launch_ps_scores(P, unsafe, ybuf, yref, part,
                                             &dstats->n_exact_tiles, false, st),
                      "score kernel launch");
         LAMP_HIP_TRY(tm.end(LAMP_STAGE_EXACT), "hipEventRecord");
         LAMP_HIP_TRY(tm.begin(LAMP_STAGE_SCORES), "hipEventRecord");
-        LAMP_HIP_TRY(lamp::launch_ps_scores(P, unsafe, ybuf, p.scores_ref, part,
+        LAMP_HIP_TRY(lamp::launch_ps_scores(P, unsafe, ybuf, yref, part,
                                             &dstats->n_exact_tiles, true, st),
                      "score kernel launch");
         LAMP_HIP_TRY(tm.end(LAMP_STAGE_SCORES), "hipEventRecord");
         LAMP_HIP_TRY(tm.begin(LAMP_STAGE_SELECT), "hipEventRecord");
-        LAMP_HIP_TRY(lamp::launch_strict_rows(P, ybuf, part, mask, row_count, pbuf, p.scores_mix,
-                                              part ? row_kl : nullptr,
+        LAMP_HIP_TRY(lamp::launch_strict_rows(P, ybuf, yref, part, mask, row_count, pbuf,
+                                              p.scores_mix, part ? row_kl : nullptr,
                                               part ? row_kl_lowp : nullptr, relaxed_rows, st),
                      "row kernel launch");
         LAMP_HIP_TRY(tm.end(LAMP_STAGE_SELECT), "hipEventRecord");

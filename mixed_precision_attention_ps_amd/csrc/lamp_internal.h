@@ -68,10 +68,13 @@ hipError_t launch_ps_scores(const Problem &p, const uint8_t *unsafe, float *ylo,
 // gather FP32 recompute, the corrected softmax, probabilities into pbuf (full
 // rows, zeros past the valid keys), y^mix (optional), counts and the row KLs
 // (when part is given).  ylo may alias pbuf or ymix_out (rows are read before
-// written).
-hipError_t launch_strict_rows(const Problem &p, const float *ylo, const RefPartial *part,
-                              uint32_t *mask, uint32_t *row_count, float *pbuf, float *ymix_out,
-                              double *row_kl, double *row_kl_lowp, bool relaxed, hipStream_t st);
+// written).  yref: the FP32 reference scores [BH, S, S] when the score tiles
+// kept them (the selected scores' FP32 values are then read from it, bit for
+// bit what the gather FP32 dot gives), or null (the dot is formed).
+hipError_t launch_strict_rows(const Problem &p, const float *ylo, const float *yref,
+                              const RefPartial *part, uint32_t *mask, uint32_t *row_count,
+                              float *pbuf, float *ymix_out, double *row_kl, double *row_kl_lowp,
+                              bool relaxed, hipStream_t st);
 
 // out = P.V from given probabilities [BH, S, S] (valid keys; P.V on MFMA).
 hipError_t launch_pv(const Problem &p, const float *probs, float *out, hipStream_t st);

@@ -26,7 +26,7 @@ namespace lamp {
 constexpr int kRowChunk = 16;   // keys per lane: rows of at most 1024 keys
 
 struct RowsArgs {
-    const float *q, *k, *ylo;
+    const float *q, *k, *ylo, *yref;
     const RefPartial *part;
     int S, D, causal, tiles, W;
     uint64_t n_rows;
@@ -225,11 +225,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5))) v
         Br = wave_sum(mine.B * f);
     }
 
-    // Gather FP32 recompute of the selected keys (one lane per key); the query
-    // row is read from LDS, each key row in batches of up to 8 x 16 bytes
-    // issued back to back.
+    // FP32 recompute of the selected keys (one lane per key): read from the
+    // reference scores when the score tiles kept them (the same sequential
+    // FP32 dot, so the same bits), else a gather dot with the query row read
+    // from LDS and each key row in batches of up to 4 x 16 bytes issued back
+    // to back.
     const uint64_t bh = r / (uint64_t)S;
-    {
+    const float *yr = a.yref ? a.yref + r * (uint64_t)S : nullptr;
+    if (!yr) {
         const float4 *qg = reinterpret_cast<const float4 *>(a.q + r * (uint64_t)a.D);
         if (lane < a.D / 4)
             s_q[wave][lane] = qg[lane];
@@ -275,7 +278,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5))) v
     for (uint32_t ei = lane; ei < total; ei += 64) {
         const uint32_t j = s_key[wave][ei];
         const float yl = y[j];
-        const float yhi = dot_hi(j);
+        const float yhi = yr ? yr[j] : dot_hi(j);
         const double ehi = exp64((double)yhi - (double)m, s_exp);
         s_val[wave][ei] = (float)ehi;
         if (a.ymix_out)   // y^mix is y^lo in place: only recomputed keys change
@@ -352,7 +355,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5))) v
     } else {
         // Full pass over y^mix: the list's scores formed again
         for (uint32_t ei = lane; ei < total; ei += 64)
-            s_val[wave][ei] = dot_hi(s_key[wave][ei]);
+            s_val[wave][ei] = yr ? yr[s_key[wave][ei]] : dot_hi(s_key[wave][ei]);
         __builtin_amdgcn_wave_barrier();
         load_ymix();
         float mm = -INFINITY;
@@ -410,9 +413,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5))) v
 
 // y^mix, when asked for, is formed in place over y^lo (ymix_out == ylo); the
 // probabilities may share y^lo's buffer only when y^mix is not asked for.
-hipError_t launch_strict_rows(const Problem &p, const float *ylo, const RefPartial *part,
-                              uint32_t *mask, uint32_t *row_count, float *pbuf, float *ymix_out,
-                              double *row_kl, double *row_kl_lowp, bool relaxed, hipStream_t st)
+hipError_t launch_strict_rows(const Problem &p, const float *ylo, const float *yref,
+                              const RefPartial *part, uint32_t *mask, uint32_t *row_count,
+                              float *pbuf, float *ymix_out, double *row_kl, double *row_kl_lowp,
+                              bool relaxed, hipStream_t st)
 {
     if (p.S > 64 * kRowChunk || (ymix_out && (ymix_out != ylo || pbuf == ylo)) ||
         (relaxed && !part))
@@ -421,6 +425,7 @@ hipError_t launch_strict_rows(const Problem &p, const float *ylo, const RefParti
     a.q = p.q;
     a.k = p.k;
     a.ylo = ylo;
+    a.yref = yref;
     a.part = part;
     a.S = p.S;
     a.D = p.D;
