@@ -433,13 +433,15 @@ def main():
     wall = time.perf_counter() - t0
     gpu_ms = t_start.elapsed_time(t_stop)
 
-    # relaxed rows of <= 1024 keys run as score tiles + row pass when probs are
-    # written (library's choice) or when asked for
-    relaxed_rows = args.mode == "relaxed" and S <= 1024 and (
-        args.relaxed_path == 2 or (args.relaxed_path == 0 and probs is not None))
+    # relaxed in two passes: asked for, or the library's choice (rows of
+    # <= 1024 keys with probs written; longer rows whenever the dense score
+    # buffers fit, as they do here)
+    relaxed_rows = args.mode == "relaxed" and (args.relaxed_path == 2 or (
+        args.relaxed_path == 0 and (S > 1024 or probs is not None)))
     if args.mode == "relaxed" and not relaxed_rows:
         ran = ["scan", "exact", "scores"] + (["finish"] if probs is not None else [])
-    elif S <= 1024 and args.mode in ("strict", "relaxed"):   # fused row pass
+    elif args.mode == "relaxed" or (S <= 1024 and args.mode == "strict"):
+        # fused row pass, or the streaming relaxed row pass of longer rows
         ran = ["scan", "exact", "scores", "select", "finish"]
     else:
         ran = ["scan", "exact", "scores", "select", "recompute", "finish"]

@@ -116,10 +116,21 @@ typedef struct {
                                  keys with probs written run in two passes
                                  (score tiles, then one wave per row: the
                                  relaxed rule, FP32 recompute, softmax,
-                                 probabilities; then P.V), everything else in
-                                 the fused one-pass kernel (online softmax).
+                                 probabilities; then P.V), other rows of
+                                 <= 1024 keys in the fused one-pass kernel
+                                 (online softmax); longer rows in two passes
+                                 (below) when their dense score buffers fit
+                                 the caller's workspace or the library's
+                                 pool can allocate them, else in the fused
+                                 kernel.
                                  1 = always the fused one-pass kernel.
-                                 2 = two passes whenever S <= 1024.
+                                 2 = always two passes.  Rows longer than
+                                 1024 keys: score tiles keeping y^lo, y^ref
+                                 and per-tile partials, one streaming pass
+                                 per row (relaxed rule, y^mix in place,
+                                 softmax sums, KL), then probabilities and
+                                 P.V; the workspace then holds the dense
+                                 score buffers the caller does not pass.
                                  Masks, counts and y^mix are the same either
                                  way; probabilities, out and KL agree within
                                  the stated tolerances.  Other values:
@@ -175,6 +186,21 @@ int lamp_attention_fwd_ex(const float *q, const float *k, const float *v,
  * invalid sizes.
  */
 size_t lamp_workspace_bytes(int B, int H, int S, int D, int mode, int want_probs);
+
+/*
+ * lamp_workspace_bytes_ex -- the exact device scratch of one
+ * lamp_attention_fwd_ex call: the same sizes, causal flag and mode, whether
+ * probs is given (want_probs) and stats requested (want_stats), and the
+ * call's lamp_params p (may be NULL), whose scores_mix, scores_ref, row_kl,
+ * row_kl_lowp, row_count and relaxed_path decide what the library keeps in
+ * the workspace.  Relaxed rows longer than 1024 keys with relaxed_path 0:
+ * the size of the two-pass form (dense score buffers); a workspace smaller
+ * than that but at least the relaxed_path = 1 size runs the fused one-pass
+ * kernel instead (per-row state only).  Returns 0 on invalid arguments
+ * (lamp_last_error() says which).
+ */
+size_t lamp_workspace_bytes_ex(int B, int H, int S, int D, int causal, int mode, int want_probs,
+                               int want_stats, const lamp_params *p);
 
 /*
  * lamp_ps_scores -- step 1 alone: the PS(mu) scores y^lo and the uniform FP32

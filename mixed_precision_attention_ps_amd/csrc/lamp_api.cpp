@@ -157,6 +157,7 @@ struct Needs {
                   // relaxed in two passes)
     bool pbuf;    // fused: probabilities need their own buffer
     bool part;    // fused: per-tile partials (KL wanted; relaxed rule)
+    bool relaxed_long;   // relaxed in two passes over rows longer than 1024 keys
 };
 
 constexpr int kFusedMaxS = 1024;
@@ -172,7 +173,14 @@ Layout plan(const Sizes &z, int mode, const Needs &n)
         L.row_kl = L.take(8 * z.n_rows);
     if (n.row_kl_lowp)
         L.row_kl_lowp = L.take(8 * z.n_rows);
-    if (mode == LAMP_RELAXED && !n.fused) {
+    if (n.relaxed_long) {
+        if (n.ymix)
+            L.ymix = L.take(4 * z.n_scores);
+        if (n.yref)
+            L.yref = L.take(4 * z.n_scores);
+        L.part = L.take(sizeof(lamp::RefPartial) * z.n_rows * (uint64_t)z.tiles);
+        L.rowstats = L.take(sizeof(lamp::RowStats) * z.n_rows);
+    } else if (mode == LAMP_RELAXED && !n.fused) {
         if (n.ymix) {   // probs requested: per-row statistics for the probs pass
             L.row_m = L.take(4 * z.n_rows);
             L.row_l = L.take(8 * z.n_rows);
@@ -195,6 +203,42 @@ Layout plan(const Sizes &z, int mode, const Needs &n)
         L.rowstats = L.take(sizeof(lamp::RowStats) * z.n_rows);
     }
     return L;
+}
+
+// What a call needs in its workspace, given the optional buffers the caller
+// passes.  relaxed_long: relaxed rows longer than 1024 keys in two passes.
+Needs make_needs(const lamp_params &p, int mode, int S, bool probs, bool want_stats,
+                 bool relaxed_long)
+{
+    Needs need{};
+    need.row_count = p.row_count == nullptr;
+    need.row_kl = p.row_kl == nullptr && want_stats;
+    need.row_kl_lowp = p.row_kl_lowp == nullptr && want_stats;
+    // relaxed rows of <= 1024 keys in two passes (score tiles, row pass)
+    const bool relaxed_rows = mode == LAMP_RELAXED && S <= kFusedMaxS &&
+                              (p.relaxed_path == 2 || (p.relaxed_path == 0 && probs));
+    need.fused = (mode == LAMP_STRICT && S <= kFusedMaxS) || relaxed_rows;
+    need.relaxed_long = relaxed_long;
+    const bool want_kl = want_stats || p.row_kl || p.row_kl_lowp;
+    if (need.relaxed_long) {
+        need.ymix = p.scores_mix == nullptr && !probs;
+        need.yref = p.scores_ref == nullptr;
+    } else if (mode == LAMP_RELAXED && !need.fused) {
+        need.ymix = probs;
+        need.yref = false;
+    } else if (need.fused) {
+        need.ymix = p.scores_mix == nullptr && !probs;
+        need.pbuf = p.scores_mix != nullptr && !probs;
+        need.part = want_kl || relaxed_rows;
+        // the score tiles form y^ref for every pair when they form the
+        // partials: kept, the row pass takes the selected scores' FP32 values
+        // from it instead of forming each dot again
+        need.yref = need.part && p.scores_ref == nullptr;
+    } else {
+        need.ymix = p.scores_mix == nullptr && !probs;
+        need.yref = p.scores_ref == nullptr;
+    }
+    return need;
 }
 
 template <typename T>
@@ -586,7 +630,49 @@ size_t lamp_workspace_bytes(int B, int H, int S, int D, int mode, int want_probs
         const size_t tf = plan(z, mode, f).total;
         total = tf > total ? tf : total;
     }
+    if (mode == LAMP_RELAXED && S > kFusedMaxS) {
+        Needs f{want_probs == 0, true, true, true, true, false, false, false, true};
+        const size_t tf = plan(z, mode, f).total;
+        total = tf > total ? tf : total;
+    }
     return total;
+}
+
+size_t lamp_workspace_bytes_ex(int B, int H, int S, int D, int causal, int mode, int want_probs,
+                               int want_stats, const lamp_params *pp)
+{
+    try {
+        Sizes z;
+        if (check_sizes(B, H, S, D, &z) != LAMP_OK)
+            return 0;
+        if (mode != LAMP_STRICT && mode != LAMP_RELAXED && mode != LAMP_RANDOM) {
+            set_error(LAMP_ERR_INVALID_ARG, "unknown mode");
+            return 0;
+        }
+        if (causal != 0 && causal != 1) {
+            set_error(LAMP_ERR_INVALID_ARG, "causal must be 0 or 1");
+            return 0;
+        }
+        if (mode == LAMP_RELAXED && D > 128) {
+            set_error(LAMP_ERR_UNSUPPORTED, "relaxed mode supports D <= 128");
+            return 0;
+        }
+        lamp_params none{};
+        const lamp_params &p = pp ? *pp : none;
+        if (p.relaxed_path < 0 || p.relaxed_path > 2) {
+            set_error(LAMP_ERR_INVALID_ARG, "relaxed_path must be 0, 1 or 2");
+            return 0;
+        }
+        if (check_ps_block(p.ps_block) != LAMP_OK)
+            return 0;
+        z.n_valid = causal ? z.BH * (uint64_t)S * (uint64_t)(S + 1) / 2 : z.n_scores;
+        const bool relaxed_long = mode == LAMP_RELAXED && S > kFusedMaxS && p.relaxed_path != 1;
+        return plan(z, mode,
+                    make_needs(p, mode, S, want_probs != 0, want_stats != 0, relaxed_long))
+            .total;
+    } catch (...) {
+        return 0;
+    }
 }
 
 static int run(const float *q, const float *k, const float *v, int B, int H, int S, int D,
@@ -616,31 +702,20 @@ static int run(const float *q, const float *k, const float *v, int B, int H, int
     hipStream_t st = (hipStream_t)p.stream;
     const bool want_stats = stats != nullptr;
 
-    Needs need{};
-    need.row_count = p.row_count == nullptr;
-    need.row_kl = p.row_kl == nullptr && want_stats;
-    need.row_kl_lowp = p.row_kl_lowp == nullptr && want_stats;
-    // relaxed rows of <= 1024 keys in two passes (score tiles, row pass)
-    const bool relaxed_rows = mode == LAMP_RELAXED && S <= kFusedMaxS &&
-                              (p.relaxed_path == 2 || (p.relaxed_path == 0 && probs != nullptr));
-    need.fused = (mode == LAMP_STRICT && S <= kFusedMaxS) || relaxed_rows;
-    const bool want_kl = want_stats || p.row_kl || p.row_kl_lowp;
-    if (mode == LAMP_RELAXED && !need.fused) {
-        need.ymix = probs != nullptr;
-        need.yref = false;
-    } else if (need.fused) {
-        need.ymix = p.scores_mix == nullptr && probs == nullptr;
-        need.pbuf = p.scores_mix != nullptr && probs == nullptr;
-        need.part = want_kl || relaxed_rows;
-        // the score tiles form y^ref for every pair when they form the
-        // partials: kept, the row pass takes the selected scores' FP32 values
-        // from it instead of forming each dot again
-        need.yref = need.part && p.scores_ref == nullptr;
-    } else {
-        need.ymix = p.scores_mix == nullptr && probs == nullptr;
-        need.yref = p.scores_ref == nullptr;
-    }
-    const Layout L = plan(z, mode, need);
+    // relaxed rows longer than 1024 keys: two passes when asked for, and by
+    // default when their dense score buffers fit (the caller's workspace, or
+    // what the pool can allocate); the fused one-pass kernel otherwise
+    bool relaxed_long = mode == LAMP_RELAXED && S > kFusedMaxS && p.relaxed_path != 1;
+    Needs need = make_needs(p, mode, S, probs != nullptr, want_stats, relaxed_long);
+    Layout L = plan(z, mode, need);
+    const bool may_fall_back = relaxed_long && p.relaxed_path == 0;
+    auto fall_back = [&]() {
+        relaxed_long = false;
+        need = make_needs(p, mode, S, probs != nullptr, want_stats, false);
+        L = plan(z, mode, need);
+    };
+    if (p.workspace && p.workspace_bytes < L.total && may_fall_back)
+        fall_back();
 
     void *ws = nullptr;
     if (p.workspace) {
@@ -652,6 +727,12 @@ static int run(const float *q, const float *k, const float *v, int B, int H, int
         ws = p.workspace;
     } else {
         rc = pool_get(L.total, &ws);
+        if (rc == LAMP_ERR_NO_MEMORY && may_fall_back) {
+            fall_back();
+            rc = pool_get(L.total, &ws);
+            if (rc == LAMP_OK)
+                g_last_error.clear();
+        }
         if (rc != LAMP_OK)
             return rc;
     }
@@ -684,7 +765,30 @@ static int run(const float *q, const float *k, const float *v, int B, int H, int
     LAMP_HIP_TRY(lamp::launch_operand_scan(P, unsafe, st), "operand scan launch");
     LAMP_HIP_TRY(tm.end(LAMP_STAGE_SCAN), "hipEventRecord");
 
-    if (mode == LAMP_RELAXED && !need.fused) {
+    if (need.relaxed_long) {
+        float *ymix = p.scores_mix ? p.scores_mix : (probs ? probs : at<float>(ws, L.ymix));
+        float *yref = p.scores_ref ? p.scores_ref : at<float>(ws, L.yref);
+        auto *part = at<lamp::RefPartial>(ws, L.part);
+        auto *rs = at<lamp::RowStats>(ws, L.rowstats);
+        LAMP_HIP_TRY(tm.begin(LAMP_STAGE_EXACT), "hipEventRecord");
+        LAMP_HIP_TRY(lamp::launch_ps_scores(P, unsafe, ymix, yref, part,
+                                            &dstats->n_exact_tiles, false, st),
+                     "score kernel launch");
+        LAMP_HIP_TRY(tm.end(LAMP_STAGE_EXACT), "hipEventRecord");
+        LAMP_HIP_TRY(tm.begin(LAMP_STAGE_SCORES), "hipEventRecord");
+        LAMP_HIP_TRY(lamp::launch_ps_scores(P, unsafe, ymix, yref, part,
+                                            &dstats->n_exact_tiles, true, st),
+                     "score kernel launch");
+        LAMP_HIP_TRY(tm.end(LAMP_STAGE_SCORES), "hipEventRecord");
+        LAMP_HIP_TRY(tm.begin(LAMP_STAGE_SELECT), "hipEventRecord");
+        LAMP_HIP_TRY(lamp::launch_relaxed_select(P, ymix, yref, part, mask, row_count, rs,
+                                                 row_kl, row_kl_lowp, st),
+                     "relaxed select launch");
+        LAMP_HIP_TRY(tm.end(LAMP_STAGE_SELECT), "hipEventRecord");
+        LAMP_HIP_TRY(tm.begin(LAMP_STAGE_FINISH), "hipEventRecord");
+        LAMP_HIP_TRY(lamp::launch_finish(P, ymix, rs, probs, out, row_kl, st), "finish launch");
+        LAMP_HIP_TRY(tm.end(LAMP_STAGE_FINISH), "hipEventRecord");
+    } else if (mode == LAMP_RELAXED && !need.fused) {
         float *ymix_raw = p.scores_mix ? p.scores_mix : probs;
         float *row_m = at<float>(ws, L.row_m);
         double *row_l = at<double>(ws, L.row_l);
@@ -726,7 +830,8 @@ static int run(const float *q, const float *k, const float *v, int B, int H, int
         LAMP_HIP_TRY(tm.begin(LAMP_STAGE_SELECT), "hipEventRecord");
         LAMP_HIP_TRY(lamp::launch_strict_rows(P, ybuf, yref, part, mask, row_count, pbuf,
                                               p.scores_mix, part ? row_kl : nullptr,
-                                              part ? row_kl_lowp : nullptr, relaxed_rows, st),
+                                              part ? row_kl_lowp : nullptr,
+                                              mode == LAMP_RELAXED, st),
                      "row kernel launch");
         LAMP_HIP_TRY(tm.end(LAMP_STAGE_SELECT), "hipEventRecord");
         LAMP_HIP_TRY(tm.begin(LAMP_STAGE_FINISH), "hipEventRecord");

@@ -101,6 +101,15 @@ hipError_t launch_strict_select(const Problem &p, const float *ylo, const float 
                                 RowStats *rs, double *row_kl, double *row_kl_lowp,
                                 int count_only, hipStream_t st);
 
+// Relaxed rule over rows of any length after score tiles that kept y^lo (in
+// y, replaced in place by y^mix), y^ref and the per-tile partials: mask words
+// (if non-null), row_count (if non-null), RowStats with lse_mix of y^mix (the
+// finish kernel takes it from there), row_kl and row_kl_lowp (if non-null).
+hipError_t launch_relaxed_select(const Problem &p, float *y, const float *yref,
+                                 const RefPartial *part, uint32_t *mask, uint32_t *row_count,
+                                 RowStats *rs, double *row_kl, double *row_kl_lowp,
+                                 hipStream_t st);
+
 // Random control: per row, row_count[r] keys with the smallest hashes.
 hipError_t launch_random_select(const Problem &p, uint64_t seed, uint32_t *mask, uint32_t *list,
                                 const uint32_t *row_count, hipStream_t st);

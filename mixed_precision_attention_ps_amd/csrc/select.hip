@@ -250,6 +250,236 @@ hipError_t launch_strict_select(const Problem &p, const float *ylo, const float 
 }
 
 // ---------------------------------------------------------------------------
+// Relaxed rule over rows of any length, after score tiles that kept y^lo,
+// y^ref and their per-tile partials (the relaxed relative-threshold variant
+// of "Experimental results", with m_t the running maximum of y^lo over the
+// 64-key blocks up to the key's).  One wave per row and ONE streaming pass:
+// block t of the rule is chunk t of 64 keys and also score tile t, whose
+// partial carries the block's y^lo maximum, so m_t is known when chunk t
+// arrives and each key is decided as the row streams past (one double
+// exponential per key, E = exp(y - m_t)).  A selected key's y^mix is its
+// y^ref, the sequential FP32 score (the recompute, bit for bit), written in
+// place over y^lo.  The softmax sums are taken against shifts known before
+// the pass: exp(y - m_lo) = E exp(m_t - m_lo) for the low-precision sum and
+// exp(y - M) = E exp(m_t - M), M = max(m_lo, m_ref), for the unselected keys
+// of the y^mix sum (one factor per chunk); the selected keys add exp(y^ref -
+// M).  The reference sums come from the partials; a selected key's term
+// p_ref (y^ref - y^lo) leaves the KL sum.
+// ---------------------------------------------------------------------------
+struct RelaxedSelectArgs {
+    float *y;   // y^lo in, y^mix out
+    const float *yref;
+    const RefPartial *part;
+    int S, causal, tiles, W;
+    uint64_t n_rows;
+    double tau;
+    uint32_t *mask, *row_count;
+    RowStats *rs;
+    double *row_kl, *row_kl_lowp;
+};
+
+__global__ __launch_bounds__(kThreads) void relaxed_select_kernel(RelaxedSelectArgs a)
+{
+    __shared__ uint32_t s_qj[4][128];   // per wave: queued selected keys
+    __shared__ float s_qv[4][128];      // and their y^lo
+    __shared__ double s_exp[64];   // 2^(k/64) for exp64
+    exp_table_fill(s_exp);
+    __syncthreads();
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint64_t rr = (uint64_t)blockIdx.x * 4 + wave;
+    if (rr >= a.n_rows)
+        return;   // no block barrier below: each wave owns its row
+    // rows in descending order: long causal rows first, short ones at the end
+    const uint64_t r = a.n_rows - 1 - rr;
+    const int S = a.S;
+    const int i = (int)(r % (uint64_t)S);
+    const int n = a.causal ? i + 1 : S;
+    const int nt = (n + 63) >> 6;   // tiles (= 64-key blocks) holding valid keys
+    float *y = a.y + r * (uint64_t)S;
+    const float *yr = a.yref + r * (uint64_t)S;
+    const RefPartial *pt = a.part + r * (uint64_t)a.tiles;
+    const __amdgpu_buffer_rsrc_t y_rs = row_rsrc(y, 4u * (uint32_t)n);
+
+    // Row maxima of y^lo and y^ref; reference sums rescaled to m_ref.
+    float mlo = -INFINITY, mr = -INFINITY;
+    for (int t = lane; t < nt; t += 64) {
+        mlo = fmaxf(mlo, pt[t].m_lo);
+        mr = fmaxf(mr, pt[t].m);
+    }
+    mlo = wave_max(mlo);
+    mr = wave_max(mr);
+    double Lr = 0.0, Br = 0.0;
+    for (int t = lane; t < nt; t += 64) {
+        const RefPartial p = pt[t];
+        const double f = exp64_nonpos((double)p.m - (double)mr, s_exp);
+        Lr += p.L * f;
+        Br += p.B * f;
+    }
+    Lr = wave_sum(Lr);
+    Br = wave_sum(Br);
+    const double M = (double)fmaxf(mlo, mr);
+
+    // l_lo: sum of exp(y^lo - m_lo); l_un / l_sel: the unselected / selected
+    // keys' part of the sum of exp(y^mix - M); dA: the selected keys' KL terms.
+    // g_lo = exp(m_t - m_lo) and g_mix = exp(m_t - M) change only with m_t.
+    float mt = -INFINITY;
+    double g_lo = 0.0, g_mix = 0.0;
+    double l_lo = 0.0, l_un = 0.0, l_sel = 0.0, dA = 0.0;
+    bool has_nan = false;
+    uint32_t total = 0;
+    // Selected keys wait in this wave's LDS queue (key, y^lo) and are taken
+    // 64 at a time, one per lane: y^ref read, y^mix written, their
+    // exponentials formed, so that work costs one lane per selected key.
+    uint32_t pend = 0;
+    auto take = [&](uint32_t cnt) {   // the first cnt (<= 64) queued keys
+        if ((uint32_t)lane < cnt) {
+            const uint32_t j = s_qj[wave][lane];
+            const float v = s_qv[wave][lane];
+            const float h = yr[j];
+            y[j] = h;
+            l_sel += exp64_nonpos((double)h - M, s_exp);
+            dA += exp64_nonpos((double)h - (double)mr, s_exp) * ((double)h - (double)v);
+        }
+    };
+    for (int j0 = 0; j0 < n; j0 += 64 * kSelBatch) {
+        float vb[kSelBatch], bm[kSelBatch];
+#pragma unroll
+        for (int u = 0; u < kSelBatch; ++u)
+            vb[u] = buf_load_f32(y_rs, 4u * (uint32_t)(j0 + 64 * u + lane));
+#pragma unroll
+        for (int u = 0; u < kSelBatch; ++u) {
+            const int c = (j0 >> 6) + u;
+            bm[u] = c < nt ? pt[c].m_lo : -INFINITY;
+        }
+#pragma unroll
+        for (int u = 0; u < kSelBatch; ++u) {
+            const int jc = j0 + 64 * u;
+            if (jc < n) {   // wave-uniform: every lane takes part in the ballot
+                // the block maximum is uniform: a new running maximum is a
+                // scalar branch (a NaN block maximum never raises it)
+                const float bmu =
+                    __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(bm[u])));
+                if (bmu > mt) {
+                    mt = bmu;
+                    g_lo = exp64_nonpos((double)mt - (double)mlo, s_exp);
+                    g_mix = exp64_nonpos((double)mt - M, s_exp);
+                }
+                const int j = jc + lane;
+                const bool valid = j < n;
+                const float v = vb[u];
+                // y <= m_t for a valid key; a key past the row gives E = 0
+                const double E =
+                    exp64_nonpos(valid ? (double)v - (double)mt : -INFINITY, s_exp);
+                has_nan |= valid && v != v;
+                const bool sel = valid && 2.0 * E * fabs((double)v) > a.tau;
+                l_lo = fma(E, g_lo, l_lo);
+                l_un = sel ? l_un : fma(E, g_mix, l_un);
+                const uint64_t b = __ballot(sel);
+                if (a.mask) {
+                    const int w = (jc >> 5) + lane;
+                    if (lane < 2 && w < a.W)
+                        a.mask[r * (uint64_t)a.W + w] = lane ? (uint32_t)(b >> 32) : (uint32_t)b;
+                }
+                if (b) {
+                    if (sel) {
+                        const uint32_t q = pend + lanes_below(b);
+                        s_qj[wave][q] = (uint32_t)j;
+                        s_qv[wave][q] = v;
+                    }
+                    const uint32_t nb = (uint32_t)__popcll(b);
+                    pend += nb;
+                    total += nb;
+                    if (pend >= 64) {   // take 64, move the rest (< 64) down
+                        __builtin_amdgcn_wave_barrier();
+                        take(64);
+                        const uint32_t rest = pend - 64;
+                        uint32_t qj = 0;
+                        float qv = 0.0f;
+                        if ((uint32_t)lane < rest) {
+                            qj = s_qj[wave][64 + lane];
+                            qv = s_qv[wave][64 + lane];
+                        }
+                        __builtin_amdgcn_wave_barrier();
+                        if ((uint32_t)lane < rest) {
+                            s_qj[wave][lane] = qj;
+                            s_qv[wave][lane] = qv;
+                        }
+                        __builtin_amdgcn_wave_barrier();
+                        pend = rest;
+                    }
+                }
+            }
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+    take(pend);
+    if (a.mask)   // the mask words past the valid keys
+        for (int w = 2 * nt + lane; w < a.W; w += 64)
+            a.mask[r * (uint64_t)a.W + w] = 0u;
+    l_lo = wave_sum(l_lo);
+    l_un = wave_sum(l_un);
+    l_sel = wave_sum(l_sel);
+    dA = wave_sum(dA);
+    if (__ballot(has_nan) != 0) {   // a NaN score makes the row's statistics NaN
+        l_lo = __builtin_nan("");
+        l_un = __builtin_nan("");
+    }
+    const double Lmix = l_un + l_sel;
+    const double lse_ref = (double)mr + log(Lr);
+    const double lse_lo = (double)mlo + log(l_lo);
+    const double lse_mix = M + log(Lmix);
+    // a sum that underflowed (y^mix far below M) is formed again over the row
+    // by the finish kernel
+    const bool full = !(Lmix >= 1e-280);
+    if (lane == 0) {
+        RowStats st;
+        st.L_lo = l_lo;
+        st.L_ref = Lr;
+        st.A = Br - dA;
+        st.lse_mix = lse_mix;
+        st.m_lo = mlo;
+        st.m_ref = mr;
+        st.full_pass = full ? 1u : 0u;
+        st.pad = 0;
+        a.rs[r] = st;
+        if (a.row_count)
+            a.row_count[r] = total;
+        if (a.row_kl && !full)
+            a.row_kl[r] = (Br - dA) / Lr + lse_mix - lse_ref;
+        if (a.row_kl_lowp)
+            a.row_kl_lowp[r] = Br / Lr + lse_lo - lse_ref;
+    }
+}
+
+hipError_t launch_relaxed_select(const Problem &p, float *y, const float *yref,
+                                 const RefPartial *part, uint32_t *mask, uint32_t *row_count,
+                                 RowStats *rs, double *row_kl, double *row_kl_lowp,
+                                 hipStream_t st)
+{
+    if (!y || !yref || !part || !rs)
+        return hipErrorInvalidValue;
+    RelaxedSelectArgs a;
+    a.y = y;
+    a.yref = yref;
+    a.part = part;
+    a.S = p.S;
+    a.causal = p.causal;
+    a.tiles = p.tiles;
+    a.W = (p.S + 31) / 32;
+    a.n_rows = p.n_rows;
+    a.tau = (double)p.tau;
+    a.mask = mask;
+    a.row_count = row_count;
+    a.rs = rs;
+    a.row_kl = row_kl;
+    a.row_kl_lowp = row_kl_lowp;
+    const uint64_t grid = (p.n_rows + 3) / 4;
+    hipLaunchKernelGGL(relaxed_select_kernel, dim3((unsigned)grid), dim3(kThreads), 0, st, a);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Random control: per row, the k = row_count[r] valid keys with the smallest
 // (SplitMix64(seed ^ linear index), j).  One work-group per row: an 8-pass
 // radix select over the 64-bit hashes finds the k-th smallest value T; keys

@@ -66,6 +66,8 @@ def library():
     lib.lamp_attention_fwd_ex.argtypes = fwd_args + [ctypes.POINTER(LampParams)]
     lib.lamp_workspace_bytes.restype = ctypes.c_size_t
     lib.lamp_workspace_bytes.argtypes = [I, I, I, I, I, I]
+    lib.lamp_workspace_bytes_ex.restype = ctypes.c_size_t
+    lib.lamp_workspace_bytes_ex.argtypes = [I, I, I, I, I, I, I, I, ctypes.POINTER(LampParams)]
     lib.lamp_ps_scores.restype = I
     lib.lamp_ps_scores.argtypes = [P, P, I, I, I, I, I, I, P, P, P]
     lib.lamp_strerror.restype = ctypes.c_char_p
@@ -133,6 +135,14 @@ def lamp_workspace_bytes(B, H, S, D, mode, want_probs) -> int:
     return int(library().lamp_workspace_bytes(B, H, S, D, MODES.get(mode, mode), int(want_probs)))
 
 
+def lamp_workspace_bytes_ex(B, H, S, D, causal, mode, want_probs, want_stats,
+                            params: "LampParams | None" = None) -> int:
+    """Exact workspace of one lamp_attention_fwd_ex call with these params."""
+    p = ctypes.byref(params) if params is not None else None
+    return int(library().lamp_workspace_bytes_ex(B, H, S, D, int(causal), MODES.get(mode, mode),
+                                                 int(want_probs), int(want_stats), p))
+
+
 def lamp_ps_scores(q, k, *, causal: bool, mu: int, ylo=None, yref=None):
     """Step 1 alone: PS(mu) scores and FP32 scores into [B,H,S,S] buffers."""
     B, H, S, D = q.shape
@@ -154,8 +164,8 @@ def lamp_attention_fwd(q, k, v, *, causal: bool, mu: int, tau: float, mode="stri
 
     q, k, v: float32 [B, H, S, D] device tensors.  Optional outputs are written
     in place when given.  relaxed_path (relaxed mode): 0 the library's choice,
-    1 the fused one-pass kernel, 2 two passes (score tiles, row pass) for rows
-    of at most 1024 keys.  Returns (out, stats_dict_or_None).
+    1 the fused one-pass kernel, 2 two passes (score tiles, then a row pass).
+    Returns (out, stats_dict_or_None).
     """
     B, H, S, D = q.shape
     if out is None:

@@ -32,6 +32,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ("lamp_attention_fwd", "lamp_attention_fwd_ex", "lamp_workspace_bytes",
+                 "lamp_workspace_bytes_ex",
                  "lamp_ps_scores", "lamp_decode_fwd", "lamp_decode_workspace_bytes",
                  "lamp_gelu_fwd", "lamp_layernorm_fwd", "lamp_mlp_workspace_bytes",
                  "lamp_gemm_scores",
@@ -97,8 +98,9 @@ def test_workspace_bytes(lib):
     # strict keeps the FP32 reference scores and the list: >= 2 * 4 bytes per score
     assert strict >= 8 * 8 * 25 * 1024 * 1024
     assert strict_noprobs >= strict + 4 * 8 * 25 * 1024 * 1024
-    # relaxed keeps only per-row state
-    assert relaxed < 64 * 4 * 25 * 4096
+    # relaxed rows longer than 1024 keys: the bound covers the two-pass form
+    # (y^ref and, without probs, y^lo kept dense)
+    assert relaxed >= 8 * 4 * 25 * 4096 * 4096
 
 
 def dcall(lib, q=A, k=A, v=A, B=1, H=1, Nq=1, S=8, D=64, causal=1, mu=4, tau=0.1, out=A):
@@ -210,6 +212,57 @@ def test_workspace_covers_both_relaxed_paths(lib):
     no_probs = lib.lamp_workspace_bytes(B, H, S, 64, 1, 0)
     assert with_probs >= 24 * rows * tiles
     assert no_probs >= 4 * rows * S + 24 * rows * tiles
+
+
+def test_workspace_covers_relaxed_long_rows_two_pass(lib):
+    # rows longer than 1024 keys in two passes: y^ref, per-tile partials and
+    # per-row statistics, and without probs the score rows too
+    B, H, S = 4, 25, 4096
+    rows, tiles = B * H * S, S // 64
+    with_probs = lib.lamp_workspace_bytes(B, H, S, 64, 1, 1)
+    no_probs = lib.lamp_workspace_bytes(B, H, S, 64, 1, 0)
+    assert with_probs >= 4 * rows * S + 24 * rows * tiles
+    assert no_probs >= 8 * rows * S + 24 * rows * tiles
+
+
+def test_workspace_bytes_ex(lib):
+    from mixed_precision_attention_ps_amd import lamp
+    ex = lamp.lamp_workspace_bytes_ex
+    B, H, S = 4, 25, 4096
+    rows, scores = B * H * S, B * H * S * S
+    # the fused one-pass relaxed kernel keeps per-row state only
+    fused = lamp.LampParams()
+    fused.relaxed_path = 1
+    assert ex(B, H, S, 64, 1, "relaxed", 1, 1, fused) < 64 * rows
+    # the two-pass form (the default for these rows when it fits): y^ref,
+    # partials, row statistics; y^lo too when neither probs nor scores_mix
+    two = ex(B, H, S, 64, 1, "relaxed", 1, 1, None)
+    assert two >= 4 * scores + 24 * rows * (S // 64)
+    assert ex(B, H, S, 64, 1, "relaxed", 0, 1, None) >= two + 4 * scores
+    # every exact size is within the upper bound
+    for mode in ("strict", "relaxed", "random"):
+        for probs in (0, 1):
+            for S_ in (512, 1024, 2048):
+                for causal in (0, 1):
+                    for rp in (0, 1, 2):
+                        p = lamp.LampParams()
+                        p.relaxed_path = rp
+                        e = ex(2, 3, S_, 64, causal, mode, probs, 1, p)
+                        assert 0 < e <= lib.lamp_workspace_bytes(2, 3, S_, 64,
+                                                                 lamp.MODES[mode], probs)
+    # caller-passed buffers leave the workspace
+    p = lamp.LampParams()
+    p.relaxed_path = 2
+    with_ref = ex(B, H, S, 64, 1, "relaxed", 1, 1, p)
+    p.scores_ref = 256
+    assert ex(B, H, S, 64, 1, "relaxed", 1, 1, p) <= with_ref - 4 * scores
+    # invalid arguments give 0
+    assert ex(0, H, S, 64, 1, "relaxed", 1, 1, None) == 0
+    assert ex(B, H, S, 64, 2, "relaxed", 1, 1, None) == 0
+    assert ex(B, H, S, 256, 1, "relaxed", 1, 1, None) == 0
+    bad = lamp.LampParams()
+    bad.relaxed_path = 3
+    assert ex(B, H, S, 64, 1, "relaxed", 1, 1, bad) == 0
 
 
 def test_version_and_strerror(lib):

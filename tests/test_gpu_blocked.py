@@ -79,6 +79,17 @@ def test_attention_blocked_relaxed_fused(dev, orc, B, H, S, D, causal, mu, mode,
     compare_full(g, r, Q, V, causal=causal, tau=tau)
 
 
+def test_attention_blocked_relaxed_long_rows(dev, orc):
+    """Blocked order on rows longer than 1024 keys, relaxed in two passes."""
+    S = 1100
+    Q, K, V, _ = make_qkv(1, 1, S, 64, n_outlier=2, seed=S + 16)
+    g = run_gpu(dev, Q, K, V, causal=True, mu=4, tau=0.05, mode=RELAXED, ps_block=16,
+                want_probs=False, relaxed_path=2)
+    r = run_orc(orc, Q, K, V, causal=True, mu=4, tau=0.05, mode=RELAXED, rows=(S - 40, S),
+                ps_block=16)
+    compare_full(g, r, Q, V, causal=True, tau=0.05, rows=(S - 40, S), check_probs=False)
+
+
 def test_blocked_scores_differ_and_reference_does_not(dev, orc):
     """The order changes y^lo (a mask-free check on the raw scores: tau =
     +inf keeps y^mix = y^lo) and leaves the FP32 reference alone; a run as

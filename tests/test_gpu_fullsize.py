@@ -15,10 +15,12 @@ Workloads (synthetic, seeded; see configs.py):
   * GPT-2-XL layer (8x25x1024x64, causal): strict at mu in {4, 7, 10} and tau
     for ~0.3 %, ~1.6 %, ~7.6 % recompute; relaxed and the random control at
     mu = 4, ~1.6 %;
-  * relaxed S=4096 (4x25x4096x64, causal): relaxed over the tau sweep, strict
-    at one tau on the same inputs;
-  * long context (1x32x16384x128, causal): relaxed at tau for ~1.6 %, and the
-    random control at the strict counts of the same tau.
+  * relaxed S=4096 (4x25x4096x64, causal): relaxed over the tau sweep (fused
+    one-pass kernel; two passes at two taus), strict at one tau on the same
+    inputs;
+  * long context (1x32x16384x128, causal): relaxed at tau for ~1.6 % (both
+    implementations), and the random control at the strict counts of the
+    same tau.
 """
 import gc
 import sys
@@ -164,9 +166,19 @@ R4K = "relaxed_s4096"
 R4K_ROWS = [(0, 64), (2040, 2104), (4032, 4096)]
 
 
+# the fused one-pass kernel (relaxed_path 1) over the tau sweep
 @pytest.mark.parametrize("tau", [1e-1, 1e-2, 1e-3, 1e-4])
 def test_s4096_relaxed(dev, orc, tau):
-    run_case(dev, orc, R4K, mode=RELAXED, mu=4, tau=tau, heads=[0, 99], row_ranges=R4K_ROWS)
+    run_case(dev, orc, R4K, mode=RELAXED, mu=4, tau=tau, heads=[0, 99], row_ranges=R4K_ROWS,
+             relaxed_path=1)
+
+
+# rows longer than 1024 keys in two passes (score tiles with partials, one
+# streaming row pass, softmax and P.V)
+@pytest.mark.parametrize("tau", [1e-2, 1e-4])
+def test_s4096_relaxed_two_pass(dev, orc, tau):
+    run_case(dev, orc, R4K, mode=RELAXED, mu=4, tau=tau, heads=[0, 99], row_ranges=R4K_ROWS,
+             relaxed_path=2)
 
 
 def test_s4096_strict(dev, orc):
@@ -180,7 +192,13 @@ LC_ROWS = [(0, 32), (8190, 8222), (16352, 16384)]
 def test_long_context_relaxed(dev, orc):
     tau = tau_for(LC, "relaxed", 4, 0.016)
     run_case(dev, orc, LC, mode=RELAXED, mu=4, tau=tau, heads=[0, 31], row_ranges=LC_ROWS,
-             expect_rate=0.016)
+             expect_rate=0.016, relaxed_path=1)
+
+
+def test_long_context_relaxed_two_pass(dev, orc):
+    tau = tau_for(LC, "relaxed", 4, 0.016)
+    run_case(dev, orc, LC, mode=RELAXED, mu=4, tau=tau, heads=[0, 31], row_ranges=LC_ROWS,
+             expect_rate=0.016, relaxed_path=2)
 
 
 def test_long_context_random_control(dev, orc):

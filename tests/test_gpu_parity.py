@@ -35,7 +35,8 @@ def note(msg):
 
 
 def run_gpu(dev, Q, K, V, *, causal, mu, tau, mode, seed=0, want_probs=True, want_mask=True,
-            want_scores=True, want_rows=True, want_stats=True, ps_block=0, relaxed_path=0):
+            want_scores=True, want_rows=True, want_stats=True, ps_block=0, relaxed_path=0,
+            workspace=None):
     import torch
     from mixed_precision_attention_ps_amd import lamp
     B, H, S, D = Q.shape
@@ -55,7 +56,8 @@ def run_gpu(dev, Q, K, V, *, causal, mu, tau, mode, seed=0, want_probs=True, wan
                                       probs=probs, recompute_mask=mask, seed=seed, row_kl=row_kl,
                                       row_kl_lowp=row_kl_lowp, row_count=row_count,
                                       scores_mix=ymix, scores_ref=yref, want_stats=want_stats,
-                                      ps_block=ps_block, relaxed_path=relaxed_path)
+                                      ps_block=ps_block, relaxed_path=relaxed_path,
+                                      workspace=workspace)
     torch.cuda.synchronize()
     res = {"out": out.cpu().numpy(), "stats": st}
     if want_rows:
@@ -352,3 +354,95 @@ def test_rows_longer_than_1024(dev, orc, S, causal, mode):
     compare_full(g, r, Q, V, causal=causal, tau=tau, rows=rows)
     r0 = run_orc(orc, Q, K, V, causal=causal, mu=4, tau=tau, mode=mode, seed=5, rows=(0, 64))
     compare_full(g, r0, Q, V, causal=causal, tau=tau, rows=(0, 64))
+
+
+# ---------------------------------------------------------------------------
+# Relaxed rule over rows longer than 1024 keys in two passes (relaxed_path 2:
+# score tiles with partials, one streaming row pass, softmax and P.V)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("S,causal,D,tau", [(1100, True, 64, 1e-2), (1300, False, 64, 1e-3),
+                                            (1025, True, 128, 1e-2), (1090, True, 64, 0.0)])
+def test_relaxed_long_rows_two_pass(dev, orc, S, causal, D, tau):
+    Q, K, V, _ = make_qkv(1, 2, S, D, n_outlier=2, seed=S + D)
+    g = run_gpu(dev, Q, K, V, causal=causal, mu=4, tau=tau, mode=RELAXED, relaxed_path=2)
+    for rows in ((0, 64), (S // 2 - 20, S // 2 + 20), (S - 70, S)):
+        r = run_orc(orc, Q, K, V, causal=causal, mu=4, tau=tau, mode=RELAXED, rows=rows)
+        compare_full(g, r, Q, V, causal=causal, tau=tau, rows=rows)
+
+
+@pytest.mark.parametrize("tau", [0.0, 1e-2])
+def test_relaxed_long_rows_paths_agree(dev, orc, tau):
+    """Fused one-pass kernel and two passes on rows of 1100 keys: the same
+    masks, counts and y^mix bit for bit."""
+    Q, K, V, _ = make_qkv(1, 3, 1100, 64, n_outlier=2, seed=41)
+    a = run_gpu(dev, Q, K, V, causal=True, mu=4, tau=tau, mode=RELAXED, relaxed_path=1)
+    b = run_gpu(dev, Q, K, V, causal=True, mu=4, tau=tau, mode=RELAXED, relaxed_path=2)
+    for name in ("mask", "ymix", "yref", "row_count"):
+        assert np.array_equal(a[name].view(np.uint8), b[name].view(np.uint8)), name
+    r = run_orc(orc, Q, K, V, causal=True, mu=4, tau=tau, mode=RELAXED, heads=[1],
+                rows=(1000, 1100))
+    for g in (a, b):
+        compare_full(g, r, Q, V, causal=True, tau=tau, heads=[1], rows=(1000, 1100))
+
+
+@pytest.mark.parametrize("kind", ["mixed", "tiny"])
+def test_relaxed_long_rows_special_inputs(dev, orc, kind):
+    """Out-of-range operands (exact-path tiles, with their partials) in rows
+    longer than 1024 keys; in "mixed" some rows' maxima lie far above the
+    earlier blocks' maxima."""
+    Q, K, V = make_special(1, 1, 1100, 64, kind=kind, seed=9)
+    g = run_gpu(dev, Q, K, V, causal=True, mu=4, tau=1e-2, mode=RELAXED, relaxed_path=2)
+    for rows in ((0, 64), (1040, 1100)):
+        with np.errstate(all="ignore"):
+            r = run_orc(orc, Q, K, V, causal=True, mu=4, tau=1e-2, mode=RELAXED, rows=rows)
+        compare_full(g, r, Q, V, causal=True, tau=1e-2, rows=rows)
+    assert g["stats"]["n_exact_tiles"] > 0
+
+
+# Where y^lo / y^mix live (probabilities buffer, the caller's score buffer or
+# the workspace) and which optional outputs are written, on the long-row
+# two-pass path.
+@pytest.mark.parametrize("probs,scores,rows,stats", [
+    (True, False, True, False), (False, False, True, False), (True, True, False, True),
+    (False, True, True, True), (False, False, False, True)])
+def test_relaxed_long_rows_buffer_configurations(dev, orc, probs, scores, rows, stats):
+    Q, K, V, _ = make_qkv(1, 1, 1088, 64, n_outlier=2, seed=78)
+    tau = 1e-2
+    g = run_gpu(dev, Q, K, V, causal=True, mu=4, tau=tau, mode=RELAXED, want_probs=probs,
+                want_scores=scores, want_rows=rows, want_stats=stats, relaxed_path=2)
+    r = run_orc(orc, Q, K, V, causal=True, mu=4, tau=tau, mode=RELAXED, rows=(1024, 1088))
+    compare_full(g, r, Q, V, causal=True, tau=tau, rows=(1024, 1088))
+
+
+def test_relaxed_long_rows_default_fits_the_workspace(dev, orc):
+    """relaxed_path 0 on rows longer than 1024 keys: with a caller workspace
+    that holds the fused kernel's per-row state but not the two-pass score
+    buffers, the fused kernel runs; with the two-pass size, two passes run
+    (each run's output equals, bit for bit, that of the implementation named
+    explicitly; the two implementations round the output differently).  All
+    give the oracle's masks and y^mix."""
+    import torch
+    from mixed_precision_attention_ps_amd import lamp
+    B, H, S, D = 1, 2, 1100, 64
+    Q, K, V, _ = make_qkv(B, H, S, D, n_outlier=2, seed=43)
+    tau = 1e-2
+
+    def size(rp):
+        p = lamp.LampParams()
+        p.relaxed_path = rp
+        p.row_kl = p.row_kl_lowp = p.row_count = 256   # passed by the caller (non-NULL)
+        p.scores_mix = p.scores_ref = 256
+        return lamp.lamp_workspace_bytes_ex(B, H, S, D, 1, "relaxed", 1, 1, p)
+
+    small, large = size(1), size(0)
+    assert 0 < small < large
+    fused = run_gpu(dev, Q, K, V, causal=True, mu=4, tau=tau, mode=RELAXED, relaxed_path=1)
+    two = run_gpu(dev, Q, K, V, causal=True, mu=4, tau=tau, mode=RELAXED, relaxed_path=2)
+    assert not np.array_equal(fused["out"], two["out"])
+    r = run_orc(orc, Q, K, V, causal=True, mu=4, tau=tau, mode=RELAXED, rows=(S - 60, S))
+    for nbytes, want in ((small, fused), (large, two)):
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        g = run_gpu(dev, Q, K, V, causal=True, mu=4, tau=tau, mode=RELAXED, workspace=ws)
+        assert np.array_equal(g["out"].view(np.uint32), want["out"].view(np.uint32))
+        compare_full(g, r, Q, V, causal=True, tau=tau, rows=(S - 60, S))
+        del ws
