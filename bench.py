@@ -363,6 +363,8 @@ def main():
     ap.add_argument("--rate", type=float, default=0.016, help="target recompute rate (tau table)")
     ap.add_argument("--tau", type=float, default=None, help="explicit tau (overrides --rate)")
     ap.add_argument("--no-probs", action="store_true")
+    ap.add_argument("--no-kl", action="store_true",
+                    help="attention: no row KL in the timed calls (the serving case)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="run a plain copy of this many MiB first (counter calibration)")
@@ -413,7 +415,8 @@ def main():
     def step(events=None):
         lamp.lamp_attention_fwd(q, k, v, causal=w.causal, mu=args.mu, tau=tau, mode=mode_id,
                                 out=out, probs=probs, recompute_mask=mask, want_stats=False,
-                                row_kl=row_kl, stage_events=events, ps_block=args.ps_block,
+                                row_kl=None if args.no_kl else row_kl, stage_events=events,
+                                ps_block=args.ps_block,
                                 relaxed_path=args.relaxed_path)
 
     for _ in range(args.warmup):
@@ -496,7 +499,8 @@ def main():
                    "relaxed_impl": ("two-pass" if relaxed_rows else "fused one-pass")
                    if args.mode == "relaxed" else None,
                    "target_rate": args.rate,
-                   "rate": rate, "probs": not args.no_probs, "mask": True, "row_kl": True,
+                   "rate": rate, "probs": not args.no_probs, "mask": True,
+                   "row_kl": not args.no_kl,
                    "parallelism": "none (1 GPU)"},
         "roofline": roofline,
         "path_alu_frac": w_path * value / ALU_PEAK,

@@ -752,6 +752,8 @@ static int run(const float *q, const float *k, const float *v, int B, int H, int
     P.tiles = z.tiles;
     P.n_rows = z.n_rows;
     P.head_valid = z.n_valid / z.BH;
+    // the partials' reference sums serve only the row KL
+    P.ref_sums = want_stats || p.row_kl || p.row_kl_lowp;
 
     auto *dstats = at<lamp::DevStats>(ws, L.dstats);
     auto *unsafe = at<uint8_t>(ws, L.unsafe);

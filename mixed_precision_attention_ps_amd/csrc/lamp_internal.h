@@ -37,6 +37,8 @@ struct Problem {
     int tiles;            // ceil(S / 64)
     uint64_t n_rows;      // BH * S
     uint64_t head_valid;  // valid pairs per head
+    bool ref_sums = true; // per-tile partials carry the reference sums L, B
+                          // (false: only the maxima, when no KL is asked for)
 };
 
 // Operand range scan: unsafe[bh * tiles + t] = 1 when a 64-row block of Q

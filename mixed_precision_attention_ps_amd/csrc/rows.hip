@@ -209,7 +209,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5))) v
             a.mask[r * (uint64_t)a.W + w] = 0u;
 
     // Reference statistics from the score kernel's per-tile partials.
-    const bool kl = a.part != nullptr;
+    const bool kl = a.part != nullptr && (a.row_kl || a.row_kl_lowp);
     double Lr = 1.0, Br = 0.0;
     float mr = 0.0f;
     if (kl) {

@@ -89,6 +89,7 @@ struct ScoreArgs {
     const uint8_t *unsafe_q, *unsafe_k;
     float *ylo, *yref;
     RefPartial *part;
+    int ref_sums;        // part: L and B too (else only the maxima; L = B = 0)
     unsigned long long *exact_tiles;
     long long n_tiles;   // BH x tiles per head
 };
@@ -122,8 +123,8 @@ __device__ __forceinline__ void score_tile_store(TileSmem &sm, const double *s_e
         }
     }
     if (a.part) {
-        // this tile's softmax statistics of the reference scores and the
-        // maximum of its PS(mu) scores, per row:
+        // this tile's maxima of its reference and PS(mu) scores and, when a
+        // KL is asked for, the softmax sums of its reference scores, per row:
         // every key is evaluated (no divergent branch) and the keys outside
         // the row are masked out of the sums.  The fast path's scores are
         // finite (its operands are bounded), so its exponential needs no NaN
@@ -150,21 +151,26 @@ __device__ __forceinline__ void score_tile_store(TileSmem &sm, const double *s_e
         for (int r = 0; r < 4; ++r) {
             L[r] = 0.0;
             B[r] = 0.0;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const double x = (double)ref[r][c] - (double)m[r];
-                const double e = PATH == PATH_FAST ? exp64_nonpos(x, s_exp) : exp64(x, s_exp);
-                // y_ref - y_lo in FP32: exact when the two are within a factor
-                // of two (Sterbenz), else within half an ulp of the difference
-                const double dy = (double)(ref[r][c] - lo[r][c]);
-                L[r] += valid[r][c] ? e : 0.0;
-                B[r] = valid[r][c] ? fma(e, dy, B[r]) : B[r];
-            }
         }
+        if (a.ref_sums) {   // uniform over the launch
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            L[r] = group16_sum(L[r]);
-            B[r] = group16_sum(B[r]);
+            for (int r = 0; r < 4; ++r) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const double x = (double)ref[r][c] - (double)m[r];
+                    const double e = PATH == PATH_FAST ? exp64_nonpos(x, s_exp) : exp64(x, s_exp);
+                    // y_ref - y_lo in FP32: exact when the two are within a factor
+                    // of two (Sterbenz), else within half an ulp of the difference
+                    const double dy = (double)(ref[r][c] - lo[r][c]);
+                    L[r] += valid[r][c] ? e : 0.0;
+                    B[r] = valid[r][c] ? fma(e, dy, B[r]) : B[r];
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                L[r] = group16_sum(L[r]);
+                B[r] = group16_sum(B[r]);
+            }
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -253,6 +259,7 @@ hipError_t launch_ps_scores(const Problem &p, const uint8_t *unsafe, float *ylo,
     a.ylo = ylo;
     a.yref = yref;
     a.part = part;
+    a.ref_sums = p.ref_sums ? 1 : 0;
     a.exact_tiles = exact_tiles;
     const long long grid = (long long)p.BH * a.tiles_per_head;
     if (grid > 0x7fffffffLL)

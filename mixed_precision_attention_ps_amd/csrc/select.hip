@@ -301,7 +301,8 @@ __global__ __launch_bounds__(kThreads) void relaxed_select_kernel(RelaxedSelectA
     const RefPartial *pt = a.part + r * (uint64_t)a.tiles;
     const __amdgpu_buffer_rsrc_t y_rs = row_rsrc(y, 4u * (uint32_t)n);
 
-    // Row maxima of y^lo and y^ref; reference sums rescaled to m_ref.
+    // Row maxima of y^lo and y^ref; reference sums rescaled to m_ref (zero,
+    // and unused, when no KL is asked for: the partials then hold no sums).
     float mlo = -INFINITY, mr = -INFINITY;
     for (int t = lane; t < nt; t += 64) {
         mlo = fmaxf(mlo, pt[t].m_lo);

@@ -484,3 +484,20 @@ def test_workspace_bytes_ex_is_exact(dev, mode, S, probs):
         with pytest.raises(lamp.LampError):
             call(buf[:need - 256])
     del buf
+
+
+# Without a KL request the score tiles' partials carry only the maxima (no
+# reference sums); the relaxed two-pass forms must give the same masks,
+# y^mix, probabilities and outputs, bit for bit, as with the KL.
+@pytest.mark.parametrize("S", [320, 1100])
+def test_relaxed_two_pass_without_kl(dev, orc, S):
+    Q, K, V, _ = make_qkv(1, 2, S, 64, n_outlier=2, seed=S + 5)
+    tau = 1e-2
+    with_kl = run_gpu(dev, Q, K, V, causal=True, mu=4, tau=tau, mode=RELAXED, relaxed_path=2)
+    no_kl = run_gpu(dev, Q, K, V, causal=True, mu=4, tau=tau, mode=RELAXED, relaxed_path=2,
+                    want_rows=False, want_stats=False)
+    for name in ("mask", "ymix", "yref", "probs", "out"):
+        assert np.array_equal(with_kl[name].view(np.uint8), no_kl[name].view(np.uint8)), name
+    rows = (S - 64, S)
+    r = run_orc(orc, Q, K, V, causal=True, mu=4, tau=tau, mode=RELAXED, rows=rows)
+    compare_full(no_kl, r, Q, V, causal=True, tau=tau, rows=rows)
