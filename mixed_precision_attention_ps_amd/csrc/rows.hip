@@ -109,11 +109,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5))) v
     if constexpr (RELAXED)
         if (lane < nch)   // nch = the tiles that hold valid keys
             early = a.part[r * (uint64_t)a.tiles + lane];
+    // Key lane + 64 t is valid iff 64 t < n - lane.  Each loop below forms
+    // n - lane from its own opaque copy of n, so the chunk compares are
+    // formed where they are used instead of being kept, 16 mask pairs at a
+    // time, in scalar registers across the loops (which spilled them).
+    auto fresh = [&]() {
+        int x = n;
+        asm volatile("" : "+s"(x));
+        return x - lane;
+    };
     float m = -INFINITY;
+    {
+        const int rem = fresh();
 #pragma unroll
-    for (int t = 0; t < kRowChunk; ++t) {
-        v[t] = lane + 64 * t < n ? v[t] : -INFINITY;
-        m = fmaxf(m, v[t]);
+        for (int t = 0; t < kRowChunk; ++t) {
+            v[t] = 64 * t < rem ? v[t] : -INFINITY;
+            m = fmaxf(m, v[t]);
+        }
     }
     m = wave_max(m);
 
@@ -124,11 +136,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5))) v
     double A = 0.0;
     int cnt = 0;
     bool has_nan = false;
+    const int rem_e = fresh();
 #pragma unroll
     for (int t = 0; t < kRowChunk; ++t) {
         e[t] = 0.0;
         if (t < nch) {
-            const bool at = lane + 64 * t < n && v[t] == m;
+            const bool at = 64 * t < rem_e && v[t] == m;
             const double x = exp64_nonpos((double)v[t] - (double)m, s_exp);
             e[t] = at ? 1.0 : x;
             A += at ? 0.0 : x;
@@ -168,13 +181,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5))) v
     uint32_t selbits = 0;
     uint32_t total = 0;
     float ef[kRowChunk];
+    const int rem_c = fresh();
 #pragma unroll
     for (int t = 0; t < kRowChunk; ++t) {
         const int j0 = 64 * t;
         ef[t] = 0.0f;
         if (t < nch) {   // chunks past the valid keys: zero mask words below
             const int j = j0 + lane;
-            const bool valid = j < n;
+            const bool valid = j0 < rem_c;
             bool sel;
             if constexpr (RELAXED) {
                 ef[t] = (float)e[t];
@@ -333,6 +347,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5))) v
         // product, at most 3 roundings (1.8e-7 of p)
         const float inv = (float)lane_read(rcp, 0);
         uint32_t before = 0;
+        const int rem_p = fresh();
 #pragma unroll
         for (int t = 0; t < kRowChunk; ++t) {
             const int j = lane + 64 * t;
@@ -347,7 +362,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5))) v
                         ev = sel ? eh : ev;
                         before += (uint32_t)__popcll(b);
                     }
-                    pv = j < n ? ev * inv : 0.0f;
+                    pv = 64 * t < rem_p ? ev * inv : 0.0f;
                 }
                 buf_store_f32(p_rs, 4u * (uint32_t)j, pv);
             }
