@@ -868,7 +868,7 @@ static int run(const float *q, const float *k, const float *v, int B, int H, int
         }
         LAMP_HIP_TRY(tm.end(LAMP_STAGE_SELECT), "hipEventRecord");
         LAMP_HIP_TRY(tm.begin(LAMP_STAGE_RECOMPUTE), "hipEventRecord");
-        LAMP_HIP_TRY(lamp::launch_recompute(P, list, row_count, ymix, rs, row_kl, st),
+        LAMP_HIP_TRY(lamp::launch_recompute(P, list, row_count, yref, ymix, rs, row_kl, st),
                      "recompute launch");
         LAMP_HIP_TRY(tm.end(LAMP_STAGE_RECOMPUTE), "hipEventRecord");
         LAMP_HIP_TRY(tm.begin(LAMP_STAGE_FINISH), "hipEventRecord");

@@ -116,10 +116,13 @@ hipError_t launch_relaxed_select(const Problem &p, float *y, const float *yref,
 hipError_t launch_random_select(const Problem &p, uint64_t seed, uint32_t *mask, uint32_t *list,
                                 const uint32_t *row_count, hipStream_t st);
 
-// Gather FP32 recompute of the listed scores, scattered into ymix, with the
-// rows' softmax and KL statistics updated for the changed scores.
+// FP32 recompute of the listed scores, scattered into ymix, with the rows'
+// softmax and KL statistics updated for the changed scores.  yref: the
+// stored FP32 reference scores (the recompute then reads them: the same
+// sequential dot, the same bits), or null (each listed dot is formed).
 hipError_t launch_recompute(const Problem &p, const uint32_t *list, const uint32_t *row_count,
-                            float *ymix, RowStats *rs, double *row_kl, hipStream_t st);
+                            const float *yref, float *ymix, RowStats *rs, double *row_kl,
+                            hipStream_t st);
 
 // Final softmax (probs may alias ymix), P.V on MFMA; rows flagged full_pass
 // get lse_mix (and row_kl) from a pass over the row here.

@@ -670,13 +670,16 @@ hipError_t launch_random_select(const Problem &p, uint64_t seed, uint32_t *mask,
 }
 
 // ---------------------------------------------------------------------------
-// Gather FP32 recompute ("Implementation strategy" step 3): one wave per row;
-// each lane takes one listed key, forms the sequential FP32 dot of q_i and
-// k_j (multiply then add, d ascending, no fused multiply-add), scales it and
-// scatters it over the baseline score.
+// Gather FP32 recompute ("Implementation strategy" step 3): each thread takes
+// one listed key and reads its stored FP32 reference score (the score tiles
+// formed the same sequential dot), or, without stored reference scores, forms
+// the sequential FP32 dot of q_i and k_j (multiply then add, d ascending, no
+// fused multiply-add) and scales it; the result is scattered over the
+// baseline score.
 // ---------------------------------------------------------------------------
 struct RecomputeArgs {
     const float *q, *k;
+    const float *yref;   // stored y^ref, or null: the dot is formed
     int S, D, causal;
     uint64_t n_rows;
     float s;
@@ -753,7 +756,17 @@ __global__ __launch_bounds__(kThreads) void recompute_kernel(RecomputeArgs a)
             const uint64_t r = r0 + lr;
             const uint32_t j = a.list[row_segment(r, a.S, a.causal) + (e - s_off[lr])];
             const uint64_t bh = r / (uint64_t)a.S;
-            if (j < (uint32_t)a.S) {
+            if (j < (uint32_t)a.S && a.yref) {
+                // the stored FP32 reference score: the same sequential dot,
+                // the same bits
+                const float yhi = a.yref[r * (uint64_t)a.S + j];
+                float *slot = a.ymix + r * (uint64_t)a.S + j;
+                const float ylo = *slot;
+                *slot = yhi;
+                const double ml = (double)s_mlo[lr], mr = (double)s_mref[lr];
+                cl = exp64((double)yhi - ml, s_exp) - exp64((double)ylo - ml, s_exp);
+                ca = exp64((double)yhi - mr, s_exp) * ((double)yhi - (double)ylo);
+            } else if (j < (uint32_t)a.S) {
                 const float4 *q4 = reinterpret_cast<const float4 *>(a.q + r * (uint64_t)a.D);
                 const float4 *k4 = reinterpret_cast<const float4 *>(
                     a.k + (bh * (uint64_t)a.S + j) * (uint64_t)a.D);
@@ -826,11 +839,13 @@ __global__ __launch_bounds__(kThreads) void recompute_kernel(RecomputeArgs a)
 }
 
 hipError_t launch_recompute(const Problem &p, const uint32_t *list, const uint32_t *row_count,
-                            float *ymix, RowStats *rs, double *row_kl, hipStream_t st)
+                            const float *yref, float *ymix, RowStats *rs, double *row_kl,
+                            hipStream_t st)
 {
     RecomputeArgs a;
     a.q = p.q;
     a.k = p.k;
+    a.yref = yref;
     a.S = p.S;
     a.D = p.D;
     a.causal = p.causal;
