@@ -118,8 +118,8 @@ hipError_t launch_random_select(const Problem &p, uint64_t seed, uint32_t *mask,
 
 // FP32 recompute of the listed scores, scattered into ymix, with the rows'
 // softmax and KL statistics updated for the changed scores.  yref: the
-// stored FP32 reference scores (the recompute then reads them: the same
-// sequential dot, the same bits), or null (each listed dot is formed).
+// stored FP32 reference scores (required; a listed key's recompute is its
+// y^ref, the same sequential dot).
 hipError_t launch_recompute(const Problem &p, const uint32_t *list, const uint32_t *row_count,
                             const float *yref, float *ymix, RowStats *rs, double *row_kl,
                             hipStream_t st);

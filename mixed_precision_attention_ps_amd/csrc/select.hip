@@ -670,19 +670,15 @@ hipError_t launch_random_select(const Problem &p, uint64_t seed, uint32_t *mask,
 }
 
 // ---------------------------------------------------------------------------
-// Gather FP32 recompute ("Implementation strategy" step 3): each thread takes
-// one listed key and reads its stored FP32 reference score (the score tiles
-// formed the same sequential dot), or, without stored reference scores, forms
-// the sequential FP32 dot of q_i and k_j (multiply then add, d ascending, no
-// fused multiply-add) and scales it; the result is scattered over the
-// baseline score.
+// FP32 recompute ("Implementation strategy" step 3) of the listed keys: the
+// score tiles already formed every score's sequential FP32 dot (multiply then
+// add, d ascending, no fused multiply-add) as y^ref, so each thread takes one
+// listed key and scatters its y^ref over the baseline score.
 // ---------------------------------------------------------------------------
 struct RecomputeArgs {
-    const float *q, *k;
-    const float *yref;   // stored y^ref, or null: the dot is formed
-    int S, D, causal;
+    const float *yref;   // the stored FP32 reference scores
+    int S, causal;
     uint64_t n_rows;
-    float s;
     const uint32_t *list, *row_count;
     float *ymix;
     RowStats *rs;
@@ -699,13 +695,9 @@ struct RecomputeArgs {
 // One work-group per 64 rows: the rows' list segments are concatenated
 // (block-local prefix of the counts) and every thread takes one listed score
 // per pass; the per-row corrections are then summed in list order by one
-// thread per row, so the result does not depend on scheduling.  D4 = D / 4
-// when the head dimension is a compile-time constant: the query and key rows
-// are then read in batches of 8 x 16 bytes issued back to back (one memory
-// wait per batch instead of one per 4 products); 0 for a runtime D.
+// thread per row, so the result does not depend on scheduling.
 constexpr int kRcRows = 64;
 
-template <int D4>
 __global__ __launch_bounds__(kThreads) void recompute_kernel(RecomputeArgs a)
 {
     __shared__ uint32_t s_off[kRcRows + 1];
@@ -755,51 +747,10 @@ __global__ __launch_bounds__(kThreads) void recompute_kernel(RecomputeArgs a)
             const int lr = lo;
             const uint64_t r = r0 + lr;
             const uint32_t j = a.list[row_segment(r, a.S, a.causal) + (e - s_off[lr])];
-            const uint64_t bh = r / (uint64_t)a.S;
-            if (j < (uint32_t)a.S && a.yref) {
-                // the stored FP32 reference score: the same sequential dot,
-                // the same bits
+            if (j < (uint32_t)a.S) {
+                // the stored FP32 reference score: the sequential FP32 dot
+                // the recompute forms, the same bits
                 const float yhi = a.yref[r * (uint64_t)a.S + j];
-                float *slot = a.ymix + r * (uint64_t)a.S + j;
-                const float ylo = *slot;
-                *slot = yhi;
-                const double ml = (double)s_mlo[lr], mr = (double)s_mref[lr];
-                cl = exp64((double)yhi - ml, s_exp) - exp64((double)ylo - ml, s_exp);
-                ca = exp64((double)yhi - mr, s_exp) * ((double)yhi - (double)ylo);
-            } else if (j < (uint32_t)a.S) {
-                const float4 *q4 = reinterpret_cast<const float4 *>(a.q + r * (uint64_t)a.D);
-                const float4 *k4 = reinterpret_cast<const float4 *>(
-                    a.k + (bh * (uint64_t)a.S + j) * (uint64_t)a.D);
-                float acc = 0.0f;
-                auto mac4 = [&acc](float4 x, float4 z) {
-                    float p0 = x.x * z.x;
-                    acc = acc + p0;
-                    float p1 = x.y * z.y;
-                    acc = acc + p1;
-                    float p2 = x.z * z.z;
-                    acc = acc + p2;
-                    float p3 = x.w * z.w;
-                    acc = acc + p3;
-                };
-                if constexpr (D4 > 0) {
-                    constexpr int kB = D4 < 8 ? D4 : 8;   // D4 is a multiple of 4
-#pragma unroll
-                    for (int b0 = 0; b0 < D4; b0 += kB) {
-                        float4 qr[kB], kr[kB];
-#pragma unroll
-                        for (int u = 0; u < kB; ++u) {
-                            qr[u] = q4[b0 + u];
-                            kr[u] = k4[b0 + u];
-                        }
-#pragma unroll
-                        for (int u = 0; u < kB; ++u)
-                            mac4(qr[u], kr[u]);
-                    }
-                } else {
-                    for (int d4 = 0; d4 < a.D / 4; ++d4)
-                        mac4(q4[d4], k4[d4]);
-                }
-                const float yhi = acc * a.s;
                 float *slot = a.ymix + r * (uint64_t)a.S + j;
                 const float ylo = *slot;
                 *slot = yhi;
@@ -842,27 +793,20 @@ hipError_t launch_recompute(const Problem &p, const uint32_t *list, const uint32
                             const float *yref, float *ymix, RowStats *rs, double *row_kl,
                             hipStream_t st)
 {
+    if (!yref)
+        return hipErrorInvalidValue;
     RecomputeArgs a;
-    a.q = p.q;
-    a.k = p.k;
     a.yref = yref;
     a.S = p.S;
-    a.D = p.D;
     a.causal = p.causal;
     a.n_rows = p.n_rows;
-    a.s = p.pc.s;
     a.list = list;
     a.row_count = row_count;
     a.ymix = ymix;
     a.rs = rs;
     a.row_kl = row_kl;
     const uint64_t grid = (p.n_rows + kRcRows - 1) / kRcRows;
-    if (p.D == 64)
-        hipLaunchKernelGGL(recompute_kernel<16>, dim3((unsigned)grid), dim3(kThreads), 0, st, a);
-    else if (p.D == 128)
-        hipLaunchKernelGGL(recompute_kernel<32>, dim3((unsigned)grid), dim3(kThreads), 0, st, a);
-    else
-        hipLaunchKernelGGL(recompute_kernel<0>, dim3((unsigned)grid), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL(recompute_kernel, dim3((unsigned)grid), dim3(kThreads), 0, st, a);
     return hipGetLastError();
 }
 
