@@ -436,14 +436,12 @@ def main():
     wall = time.perf_counter() - t0
     gpu_ms = t_start.elapsed_time(t_stop)
 
-    # relaxed in two passes: asked for, or the library's choice (rows of
-    # <= 1024 keys with probs written; longer rows whenever the dense score
-    # buffers fit, as they do here)
-    relaxed_rows = args.mode == "relaxed" and (args.relaxed_path == 2 or (
-        args.relaxed_path == 0 and (S > 1024 or probs is not None)))
-    if args.mode == "relaxed" and not relaxed_rows:
+    # the implementation the library ran (it reports it; the stage events
+    # that implementation records are the ones read)
+    impl = lamp.last_impl()
+    if impl == "relaxed_fused":
         ran = ["scan", "exact", "scores"] + (["finish"] if probs is not None else [])
-    elif args.mode == "relaxed" or (S <= 1024 and args.mode == "strict"):
+    elif impl in ("strict_rows", "relaxed_rows", "relaxed_stream"):
         # fused row pass, or the streaming relaxed row pass of longer rows
         ran = ["scan", "exact", "scores", "select", "finish"]
     else:
@@ -469,7 +467,7 @@ def main():
     # score: 8D (PS(mu) dot: multiply, add, two 3-instruction roundings per
     # MAC) + D (FP32 reference dot at two lanes per slot) [+ 20 for the fused
     # softmax/criterion/KL].
-    fused_relaxed = args.mode == "relaxed" and not relaxed_rows
+    fused_relaxed = impl == "relaxed_fused"
     kname = "relaxed_kernel" if fused_relaxed else "ps_scores_kernel"
     w_alg = 9 * D + (20 if fused_relaxed else 0) + run_flush_ops(D, args.ps_block)
     t_kernel_ms = stages.get("scores")
@@ -496,8 +494,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "H": H, "S": S, "D": D, "causal": w.causal,
                    "mu": args.mu, "mode": args.mode, "ps_block": args.ps_block, "tau": tau,
-                   "relaxed_impl": ("two-pass" if relaxed_rows else "fused one-pass")
-                   if args.mode == "relaxed" else None,
+                   "impl": impl,
                    "target_rate": args.rate,
                    "rate": rate, "probs": not args.no_probs, "mask": True,
                    "row_kl": not args.no_kl,

@@ -77,14 +77,55 @@ typedef struct {
     double kl_max;          /* max over rows of the same                      */
     double kl_lowp_sum;     /* sum over rows of KL(P_FP32 || P_lowp), the
                                all-low-precision baseline                     */
+    uint64_t n_tie_band;    /* valid keys whose selection criterion c lies
+                               within a relative 2^-16 of tau, |c - tau| <=
+                               2^-16 tau: the near-ties that a single-
+                               precision evaluation of c could not decide and
+                               the library decides in double precision (the
+                               strict rule's ">" of "Theoretical foundation"
+                               item 3; the relaxed rule's and the GELU
+                               rule's likewise).  LAMP_RANDOM: those of the
+                               strict rule that fixes the per-row counts.
+                               Always 0 for the layer norm (no per-key
+                               criterion)                                     */
+    int32_t impl;           /* the implementation that ran (LAMP_IMPL_*)     */
+    int32_t reserved;       /* 0                                              */
 } lamp_stats;
+
+/* Implementations a call can run (lamp_stats.impl, lamp_last_impl()). */
+enum {
+    LAMP_IMPL_NONE = 0,
+    LAMP_IMPL_STRICT_ROWS = 1,     /* strict, rows of <= 1024 keys: score tiles,
+                                      one wave per row (statistics, selection,
+                                      recompute, probabilities), P.V          */
+    LAMP_IMPL_STRICT_STREAM = 2,   /* strict, longer rows: score tiles, row
+                                      selection, list recompute, finish       */
+    LAMP_IMPL_RANDOM = 3,          /* random control: score tiles, strict
+                                      counts, hash selection, recompute,
+                                      finish                                  */
+    LAMP_IMPL_RELAXED_FUSED = 4,   /* relaxed, the fused one-pass kernel (online
+                                      softmax) [+ probabilities pass]         */
+    LAMP_IMPL_RELAXED_ROWS = 5,    /* relaxed, two passes over rows of <= 1024
+                                      keys: score tiles, row pass, P.V        */
+    LAMP_IMPL_RELAXED_STREAM = 6,  /* relaxed, two passes over longer rows:
+                                      score tiles, streaming row pass, finish */
+    LAMP_IMPL_DECODE = 7,          /* lamp_decode_fwd                         */
+    LAMP_IMPL_GELU = 8,            /* lamp_gelu_fwd                           */
+    LAMP_IMPL_LAYERNORM = 9        /* lamp_layernorm_fwd                      */
+};
 
 /* Optional extras for lamp_attention_fwd_ex.  Zero-initialise and set what
  * you need; every pointer may be NULL. */
 typedef struct {
     void *stream;             /* hipStream_t to enqueue on; NULL = default    */
     void *workspace;          /* device scratch of workspace_bytes, or NULL:
-                                 the library keeps a per-device pool          */
+                                 the library keeps a per-device pool, grown
+                                 on demand and shared by every call on that
+                                 device; a call that uses it first makes its
+                                 stream wait for the previous user's work
+                                 (an event), so calls on different streams
+                                 never overlap on the pool.  Pass a
+                                 workspace per stream to let them overlap    */
     size_t workspace_bytes;   /* >= lamp_workspace_bytes(...) when given      */
     uint64_t seed;            /* LAMP_RANDOM seed                             */
     double *row_kl;           /* device [B,H,S]: KL(P_FP32 || P_LAMP) per row */
@@ -135,6 +176,13 @@ typedef struct {
                                  way; probabilities, out and KL agree within
                                  the stated tolerances.  Other values:
                                  LAMP_ERR_INVALID_ARG                         */
+    int block_k;              /* LAMP_RELAXED: the key-block width of the
+                                 relaxed rule's running maximum m_t (part of
+                                 the rule's definition).  0 = 64, the default
+                                 and the only width implemented; any other
+                                 value: LAMP_ERR_UNSUPPORTED (< 0:
+                                 LAMP_ERR_INVALID_ARG).  Ignored by the other
+                                 modes                                        */
 } lamp_params;
 
 /* Stages, for lamp_params.stage_events. */
@@ -322,6 +370,13 @@ int lamp_gemm_scores(const float *x, const float *w, int M, int N, int K, int mu
  * -1 on NULL pointers or n < 0, -3 on a launch failure.
  */
 int lamp_diag_exp(const double *x, double *y64, float *y32, int n, void *stream);
+
+/* The implementation (LAMP_IMPL_*) that the calling thread's last
+ * successful lamp_attention_fwd[_ex], lamp_decode_fwd, lamp_gelu_fwd or
+ * lamp_layernorm_fwd call ran; LAMP_IMPL_NONE before the first one.  The
+ * same value lamp_stats.impl reports, without the synchronisation that
+ * filling lamp_stats costs. */
+int lamp_last_impl(void);
 
 /* Static text for a return code. */
 const char *lamp_strerror(int code);

@@ -48,6 +48,7 @@ struct DecodeArgs {
     DecPartial *part;         // [BH, n_blk, nq]
     float *acc;               // [BH, n_blk, nq, D]
     unsigned long long *exact_chunks;
+    unsigned long long *n_band;
 };
 
 // Keys 0 .. last_key(t) are valid for query t.
@@ -333,6 +334,7 @@ __global__ __launch_bounds__(kThreads) void decode_softmax_kernel(DecodeArgs a)
         return;   // no barrier below
     const int nq = a.nq, S = a.S, D = a.D;
     const int j = blk * 64 + lane;
+    uint32_t ties = 0;   // near ties of the criterion (wave-uniform)
 
     for (int t = 0; t < nq; ++t) {
         const size_t row = (size_t)bh * nq + t;
@@ -350,7 +352,9 @@ __global__ __launch_bounds__(kThreads) void decode_softmax_kernel(DecodeArgs a)
             yref = a.yref[row * S + j];
         }
         const double E = valid ? exp64((double)ylo - (double)mt, s_exp) : 0.0;
-        const bool sel = valid && 2.0 * E * fabs((double)ylo) > a.tau;
+        const double crit = 2.0 * E * fabs((double)ylo);
+        const bool sel = valid && crit > a.tau;
+        ties += (uint32_t)__popcll(__ballot(valid && near_tie(crit, a.tau)));
         const float ymix = sel ? yref : ylo;
         const uint64_t b = __ballot(sel);
         if (a.mask) {
@@ -386,11 +390,15 @@ __global__ __launch_bounds__(kThreads) void decode_softmax_kernel(DecodeArgs a)
             a.part[((size_t)bh * a.n_blk + blk) * nq + t] = pt;
         }
     }
+    add_ties(a.n_band, ties);
     __builtin_amdgcn_wave_barrier();
 
     // P.V partial of this block
     const int nk = min(64, S - blk * 64);
     const float *Vb = a.v + ((size_t)bh * S + (size_t)blk * 64) * D;
+    // a block with keys past some query's limit, or past S (the first
+    // query's limit is the smallest)
+    const bool edge = blk * 64 + 63 > dec_last_key(a, 0);
     for (int d0 = 0; d0 < D; d0 += 64) {
         const int d = d0 + lane;
         double accd[NQ];
@@ -417,9 +425,20 @@ __global__ __launch_bounds__(kThreads) void decode_softmax_kernel(DecodeArgs a)
                             *reinterpret_cast<const float4 *>(&s_p[wave][t][kg + 4]);
                         const float pa[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
                         float f = 0.0f;
+                        if (edge) {
+                            // keys past this query's limit (or past S) carry
+                            // probability 0: their V value is left out, so a
+                            // non-finite one cannot turn 0 * inf into NaN
+                            const int lim = dec_last_key(a, t) - blk * 64;
 #pragma unroll
-                        for (int u = 0; u < 8; ++u)
-                            f = __builtin_fmaf(pa[u], vv[8 * g + u], f);
+                            for (int u = 0; u < 8; ++u)
+                                f = __builtin_fmaf(pa[u], kg + u <= lim ? vv[8 * g + u] : 0.0f,
+                                                   f);
+                        } else {
+#pragma unroll
+                            for (int u = 0; u < 8; ++u)
+                                f = __builtin_fmaf(pa[u], vv[8 * g + u], f);
+                        }
                         accd[t] += (double)f;
                     }
                 }
@@ -613,6 +632,7 @@ hipError_t launch_decode(const DecodeProblem &p, const DecodeBuffers &b, hipStre
     a.n_chunks = (p.S + kDecChunk - 1) / kDecChunk;
     a.n_blk = (p.S + 63) / 64;
     a.tau = (double)p.tau;
+    a.n_band = p.n_band;
     a.pc = make_ps_const(p.mu, p.D);
     set_ps_block(a.pc, p.ps_block, p.D);
     a.ylo = b.ylo;

@@ -50,10 +50,12 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(FinishArgs a)
     __shared__ float sV[2][kFinKeys][VP];
     __shared__ double s_lse[kFinRows];
     __shared__ double s_exp[64];   // 2^(k/64) for exp64
-    if (!PIN) {
+    __shared__ int s_vbad;         // a causal diagonal step met a non-finite V value
+    if (!PIN)
         exp_table_fill(s_exp);
-        __syncthreads();
-    }
+    if (threadIdx.x == 0)
+        s_vbad = 0;
+    __syncthreads();
 
     const int S = a.S, D = a.D;
     // heaviest row blocks first (causal work grows with the block index), so
@@ -178,12 +180,23 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(FinishArgs a)
         for (int e = 0; e < KPT; e += 4)
             *reinterpret_cast<float4 *>(&sP[buf][prow][kseg + e]) =
                 make_float4(pv[e], pv[e + 1], pv[e + 2], pv[e + 3]);
+        // Causal steps that reach the block's own rows hold keys past some
+        // rows' limits, whose probability 0 would turn a non-finite V value
+        // into NaN (0 * inf) in the product: such values are staged as 0 and
+        // added back below for the rows that see their key.
+        const bool diag = a.causal && j0 + kFinKeys > row0;
 #pragma unroll
         for (int u = 0; u < V4; ++u) {
             const int e = tid + u * kThreads;
             const int key = e / (DV / 4), col = (e % (DV / 4)) * 4;
-            if (e < NV4)
-                *reinterpret_cast<float4 *>(&sV[buf][key][col]) = vcur[u];
+            if (e < NV4) {
+                float4 x = vcur[u];
+                if (diag && !(finite4(x))) {
+                    x = finite_or_zero(x);
+                    s_vbad = 1;
+                }
+                *reinterpret_cast<float4 *>(&sV[buf][key][col]) = x;
+            }
         }
         __syncthreads();
 #pragma unroll
@@ -232,6 +245,26 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(FinishArgs a)
             } else {
                 for (int j = z0 + lane; j < S; j += 64)
                     pz[j] = 0.0f;
+            }
+        }
+    }
+
+    // Non-finite V values staged as 0 on the diagonal steps: each one at a
+    // key the row sees adds its infinity or NaN (what any positive
+    // probability times it gives), keys past the row add nothing.
+    if (s_vbad) {
+#pragma unroll
+        for (int q = 0; q < NB; ++q) {
+            const int col = q * 16 + (lane & 15);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int i = row0 + wave * 16 + 4 * (lane >> 4) + v;
+                if (col < D && i < S)
+                    for (int j = row0; j <= i; ++j) {
+                        const float x = Vh[(size_t)j * D + col];
+                        if (!isfinite(x))
+                            acc[q][v] += (double)x;
+                    }
             }
         }
     }

@@ -30,6 +30,7 @@
 namespace {
 
 thread_local std::string g_last_error;
+thread_local int g_last_impl = LAMP_IMPL_NONE;
 
 int set_error(int code, const std::string &msg)
 {
@@ -54,44 +55,76 @@ constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-// Library-managed workspace, one per device, grow-only.
+// Library-managed workspace, one per device, grow-only.  Calls that use it
+// are serialised on the device: a call holds the pool's lock while it
+// enqueues its work, first makes its stream wait for the event the previous
+// user recorded after its last launch, and records that event again after
+// its own (PoolLease's destructor), so work on different streams never runs
+// over the same pool memory at the same time.
 struct Pool {
     void *ptr = nullptr;
     size_t bytes = 0;
+    hipEvent_t done = nullptr;   // recorded after the last user's launches
+    bool pending = false;        // `done` has been recorded at least once
 };
 std::mutex g_pool_mutex;
 std::vector<Pool> g_pools;
 
-int pool_get(size_t bytes, void **out)
-{
-    int dev = 0;
-    LAMP_HIP_TRY(hipGetDevice(&dev), "hipGetDevice");
-    std::lock_guard<std::mutex> lock(g_pool_mutex);
-    if ((size_t)dev >= g_pools.size())
-        g_pools.resize(dev + 1);
-    Pool &p = g_pools[dev];
-    if (p.bytes < bytes) {
-        if (p.ptr) {
-            // in-flight work may still use the old block
-            LAMP_HIP_TRY(hipDeviceSynchronize(), "hipDeviceSynchronize");
-            LAMP_HIP_TRY(hipFree(p.ptr), "hipFree");
-            p.ptr = nullptr;
-            p.bytes = 0;
-        }
-        void *ptr = nullptr;
-        hipError_t e = hipMalloc(&ptr, bytes);
-        if (e != hipSuccess) {
-            (void)hipGetLastError();
-            return set_error(LAMP_ERR_NO_MEMORY,
-                             "hipMalloc of " + std::to_string(bytes) + " bytes failed: " +
-                                 hipGetErrorString(e));
-        }
-        p.ptr = ptr;
-        p.bytes = bytes;
+class PoolLease {
+  public:
+    PoolLease() = default;
+    PoolLease(const PoolLease &) = delete;
+    PoolLease &operator=(const PoolLease &) = delete;
+    ~PoolLease()
+    {
+        if (pool_ && pool_->done && hipEventRecord(pool_->done, st_) == hipSuccess)
+            pool_->pending = true;
     }
-    *out = p.ptr;
-    return LAMP_OK;
-}
+    // The pool of the current device, at least `bytes` large, in *out; the
+    // lock is held until this lease ends.
+    int acquire(size_t bytes, hipStream_t st, void **out)
+    {
+        int dev = 0;
+        LAMP_HIP_TRY(hipGetDevice(&dev), "hipGetDevice");
+        lock_ = std::unique_lock<std::mutex>(g_pool_mutex);
+        if ((size_t)dev >= g_pools.size())
+            g_pools.resize(dev + 1);
+        Pool &p = g_pools[dev];
+        if (!p.done)
+            LAMP_HIP_TRY(hipEventCreateWithFlags(&p.done, hipEventDisableTiming),
+                         "hipEventCreateWithFlags");
+        if (p.bytes < bytes) {
+            if (p.ptr) {
+                // in-flight work may still use the old block
+                LAMP_HIP_TRY(hipDeviceSynchronize(), "hipDeviceSynchronize");
+                LAMP_HIP_TRY(hipFree(p.ptr), "hipFree");
+                p.ptr = nullptr;
+                p.bytes = 0;
+            }
+            void *ptr = nullptr;
+            hipError_t e = hipMalloc(&ptr, bytes);
+            if (e != hipSuccess) {
+                (void)hipGetLastError();
+                return set_error(LAMP_ERR_NO_MEMORY,
+                                 "hipMalloc of " + std::to_string(bytes) + " bytes failed: " +
+                                     hipGetErrorString(e));
+            }
+            p.ptr = ptr;
+            p.bytes = bytes;
+        } else if (p.pending) {
+            LAMP_HIP_TRY(hipStreamWaitEvent(st, p.done, 0), "hipStreamWaitEvent");
+        }
+        pool_ = &p;
+        st_ = st;
+        *out = p.ptr;
+        return LAMP_OK;
+    }
+
+  private:
+    std::unique_lock<std::mutex> lock_;
+    Pool *pool_ = nullptr;
+    hipStream_t st_ = nullptr;
+};
 
 struct Sizes {
     uint64_t BH, n_rows, n_valid, n_scores;
@@ -333,6 +366,32 @@ int check_ps_block(int b)
     return LAMP_OK;
 }
 
+// The relaxed rule's block width (lamp_params.block_k): 0 or 64.
+int check_block_k(int b)
+{
+    if (b < 0)
+        return set_error(LAMP_ERR_INVALID_ARG, "block_k must be >= 0");
+    if (b != 0 && b != 64)
+        return set_error(LAMP_ERR_UNSUPPORTED,
+                         "block_k: only the 64-key block of the relaxed rule is implemented");
+    return LAMP_OK;
+}
+
+void fill_stats(lamp_stats *stats, uint64_t n_rows, uint64_t n_valid, const lamp::DevStats &ds,
+                int impl)
+{
+    stats->n_rows = n_rows;
+    stats->n_valid = n_valid;
+    stats->n_selected = ds.n_selected;
+    stats->n_exact_tiles = ds.n_exact_tiles;
+    stats->kl_sum = ds.kl_sum;
+    stats->kl_max = ds.kl_max;
+    stats->kl_lowp_sum = ds.kl_lowp_sum;
+    stats->n_tie_band = ds.n_tie_band;
+    stats->impl = impl;
+    stats->reserved = 0;
+}
+
 int run_decode(const float *q, const float *k, const float *v, int B, int H, int Nq, int S, int D,
                int causal, int mu, float tau, float *out, float *probs, uint32_t *mask,
                lamp_stats *stats, const lamp_params *pp)
@@ -349,6 +408,9 @@ int run_decode(const float *q, const float *k, const float *v, int B, int H, int
     rc = check_ps_block(p.ps_block);
     if (rc != LAMP_OK)
         return rc;
+    rc = check_block_k(p.block_k);
+    if (rc != LAMP_OK)
+        return rc;
     (void)hipGetLastError();
     hipStream_t st = (hipStream_t)p.stream;
     const bool want_stats = stats != nullptr;
@@ -357,6 +419,7 @@ int run_decode(const float *q, const float *k, const float *v, int B, int H, int
         decode_plan(BH, Nq, S, D, p.scores_mix == nullptr, p.scores_ref == nullptr,
                     p.row_count == nullptr, p.row_kl == nullptr && want_stats,
                     p.row_kl_lowp == nullptr && want_stats);
+    PoolLease lease;
     void *ws = nullptr;
     if (p.workspace) {
         if (p.workspace_bytes < L.total)
@@ -366,7 +429,7 @@ int run_decode(const float *q, const float *k, const float *v, int B, int H, int
             return set_error(LAMP_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
         ws = p.workspace;
     } else {
-        rc = pool_get(L.total, &ws);
+        rc = lease.acquire(L.total, st, &ws);
         if (rc != LAMP_OK)
             return rc;
     }
@@ -383,6 +446,7 @@ int run_decode(const float *q, const float *k, const float *v, int B, int H, int
     P.mu = mu;
     P.tau = tau;
     P.ps_block = p.ps_block;
+    P.n_band = &dstats->n_tie_band;
     lamp::DecodeBuffers b;
     b.ylo = p.scores_mix ? p.scores_mix : at<float>(ws, L.ylo);
     b.yref = p.scores_ref ? p.scores_ref : at<float>(ws, L.yref);
@@ -415,14 +479,9 @@ int run_decode(const float *q, const float *k, const float *v, int B, int H, int
         const uint64_t per_head = causal ? (uint64_t)Nq * (uint64_t)(S - Nq) +
                                                (uint64_t)Nq * (uint64_t)(Nq + 1) / 2
                                          : (uint64_t)Nq * (uint64_t)S;
-        stats->n_rows = BH * (uint64_t)Nq;
-        stats->n_valid = BH * per_head;
-        stats->n_selected = ds.n_selected;
-        stats->n_exact_tiles = ds.n_exact_tiles;
-        stats->kl_sum = ds.kl_sum;
-        stats->kl_max = ds.kl_max;
-        stats->kl_lowp_sum = ds.kl_lowp_sum;
+        fill_stats(stats, BH * (uint64_t)Nq, BH * per_head, ds, LAMP_IMPL_DECODE);
     }
+    g_last_impl = LAMP_IMPL_DECODE;
     return LAMP_OK;
 }
 
@@ -523,6 +582,7 @@ int run_mlp(int op, const float *x, const float *w, const float *gamma, const fl
     const MlpLayout L = mlp_plan(M, N, op, true, p.scores_ref == nullptr, mask == nullptr,
                                  p.row_kl == nullptr, p.row_kl_lowp == nullptr,
                                  p.row_count == nullptr);
+    PoolLease lease;
     void *ws = nullptr;
     if (p.workspace) {
         if (p.workspace_bytes < L.total)
@@ -532,10 +592,11 @@ int run_mlp(int op, const float *x, const float *w, const float *gamma, const fl
             return set_error(LAMP_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
         ws = p.workspace;
     } else {
-        rc = pool_get(L.total, &ws);
+        rc = lease.acquire(L.total, st, &ws);
         if (rc != LAMP_OK)
             return rc;
     }
+    const int impl = op == lamp::MLP_GELU ? LAMP_IMPL_GELU : LAMP_IMPL_LAYERNORM;
     auto *dstats = at<lamp::DevStats>(ws, L.dstats);
     lamp::MlpProblem P;
     P.x = x;
@@ -550,6 +611,7 @@ int run_mlp(int op, const float *x, const float *w, const float *gamma, const fl
     P.tau = tau;
     P.ps_block = p.ps_block;
     P.eps = eps;
+    P.n_band = &dstats->n_tie_band;
     lamp::MlpBuffers b{};
     b.unsafe = at<uint32_t>(ws, L.unsafe);
     if (op == lamp::MLP_LAYERNORM) {
@@ -581,14 +643,9 @@ int run_mlp(int op, const float *x, const float *w, const float *gamma, const fl
         LAMP_HIP_TRY(hipMemcpyAsync(&ds, dstats, sizeof(ds), hipMemcpyDeviceToHost, st),
                      "hipMemcpyAsync stats");
         LAMP_HIP_TRY(hipStreamSynchronize(st), "hipStreamSynchronize");
-        stats->n_rows = (uint64_t)M;
-        stats->n_valid = (uint64_t)M * (uint64_t)N;
-        stats->n_selected = ds.n_selected;
-        stats->n_exact_tiles = ds.n_exact_tiles;
-        stats->kl_sum = ds.kl_sum;
-        stats->kl_max = ds.kl_max;
-        stats->kl_lowp_sum = ds.kl_lowp_sum;
+        fill_stats(stats, (uint64_t)M, (uint64_t)M * (uint64_t)N, ds, impl);
     }
+    g_last_impl = impl;
     return LAMP_OK;
 }
 
@@ -610,7 +667,9 @@ const char *lamp_strerror(int code)
 
 const char *lamp_last_error(void) { return g_last_error.c_str(); }
 
-int lamp_version(void) { return 10000; }
+int lamp_version(void) { return 10100; }
+
+int lamp_last_impl(void) { return g_last_impl; }
 
 size_t lamp_workspace_bytes(int B, int H, int S, int D, int mode, int want_probs)
 {
@@ -665,6 +724,8 @@ size_t lamp_workspace_bytes_ex(int B, int H, int S, int D, int causal, int mode,
         }
         if (check_ps_block(p.ps_block) != LAMP_OK)
             return 0;
+        if (mode == LAMP_RELAXED && check_block_k(p.block_k) != LAMP_OK)
+            return 0;
         z.n_valid = causal ? z.BH * (uint64_t)S * (uint64_t)(S + 1) / 2 : z.n_scores;
         const bool relaxed_long = mode == LAMP_RELAXED && S > kFusedMaxS && p.relaxed_path != 1;
         return plan(z, mode,
@@ -698,7 +759,11 @@ static int run(const float *q, const float *k, const float *v, int B, int H, int
         return rc;
     if (p.relaxed_path < 0 || p.relaxed_path > 2)
         return set_error(LAMP_ERR_INVALID_ARG, "relaxed_path must be 0, 1 or 2");
-    (void)hipGetLastError();   // launches below are checked with hipGetLastError
+    if (mode == LAMP_RELAXED) {
+        rc = check_block_k(p.block_k);
+        if (rc != LAMP_OK)
+            return rc;
+    }
     hipStream_t st = (hipStream_t)p.stream;
     const bool want_stats = stats != nullptr;
 
@@ -716,7 +781,7 @@ static int run(const float *q, const float *k, const float *v, int B, int H, int
     };
     if (p.workspace && p.workspace_bytes < L.total && may_fall_back)
         fall_back();
-
+    PoolLease lease;
     void *ws = nullptr;
     if (p.workspace) {
         if (p.workspace_bytes < L.total)
@@ -726,16 +791,17 @@ static int run(const float *q, const float *k, const float *v, int B, int H, int
             return set_error(LAMP_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
         ws = p.workspace;
     } else {
-        rc = pool_get(L.total, &ws);
+        rc = lease.acquire(L.total, st, &ws);
         if (rc == LAMP_ERR_NO_MEMORY && may_fall_back) {
             fall_back();
-            rc = pool_get(L.total, &ws);
+            rc = lease.acquire(L.total, st, &ws);
             if (rc == LAMP_OK)
                 g_last_error.clear();
         }
         if (rc != LAMP_OK)
             return rc;
     }
+    (void)hipGetLastError();   // launches below are checked with hipGetLastError
 
     lamp::Problem P;
     P.q = q;
@@ -756,12 +822,19 @@ static int run(const float *q, const float *k, const float *v, int B, int H, int
     P.ref_sums = want_stats || p.row_kl || p.row_kl_lowp;
 
     auto *dstats = at<lamp::DevStats>(ws, L.dstats);
+    P.n_band = &dstats->n_tie_band;
     auto *unsafe = at<uint8_t>(ws, L.unsafe);
     uint32_t *row_count = p.row_count ? p.row_count : at<uint32_t>(ws, L.row_count);
     double *row_kl = p.row_kl ? p.row_kl : at<double>(ws, L.row_kl);
     double *row_kl_lowp = p.row_kl_lowp ? p.row_kl_lowp : at<double>(ws, L.row_kl_lowp);
     StageTimer tm{p.stage_events, st};
 
+    const int impl = need.relaxed_long ? LAMP_IMPL_RELAXED_STREAM
+                     : (mode == LAMP_RELAXED && !need.fused) ? LAMP_IMPL_RELAXED_FUSED
+                     : need.fused ? (mode == LAMP_RELAXED ? LAMP_IMPL_RELAXED_ROWS
+                                                          : LAMP_IMPL_STRICT_ROWS)
+                     : mode == LAMP_RANDOM ? LAMP_IMPL_RANDOM
+                                           : LAMP_IMPL_STRICT_STREAM;
     LAMP_HIP_TRY(lamp::launch_zero(dstats, sizeof(lamp::DevStats), st), "zero stats");
     LAMP_HIP_TRY(tm.begin(LAMP_STAGE_SCAN), "hipEventRecord");
     LAMP_HIP_TRY(lamp::launch_operand_scan(P, unsafe, st), "operand scan launch");
@@ -885,14 +958,9 @@ static int run(const float *q, const float *k, const float *v, int B, int H, int
         LAMP_HIP_TRY(hipMemcpyAsync(&ds, dstats, sizeof(ds), hipMemcpyDeviceToHost, st),
                      "hipMemcpyAsync stats");
         LAMP_HIP_TRY(hipStreamSynchronize(st), "hipStreamSynchronize");
-        stats->n_rows = z.n_rows;
-        stats->n_valid = z.n_valid;
-        stats->n_selected = ds.n_selected;
-        stats->n_exact_tiles = ds.n_exact_tiles;
-        stats->kl_sum = ds.kl_sum;
-        stats->kl_max = ds.kl_max;
-        stats->kl_lowp_sum = ds.kl_lowp_sum;
+        fill_stats(stats, z.n_rows, z.n_valid, ds, impl);
     }
+    g_last_impl = impl;
     return LAMP_OK;
 }
 
@@ -990,7 +1058,8 @@ int lamp_gemm_scores(const float *x, const float *w, int M, int N, int K, int mu
             return rc;
         void *ws = nullptr;
         const size_t flags = 4 * ((size_t)(M + 63) / 64 + (size_t)(N + 63) / 64);
-        rc = pool_get(align_up(flags), &ws);
+        PoolLease lease;
+        rc = lease.acquire(align_up(flags), (hipStream_t)stream, &ws);
         if (rc != LAMP_OK)
             return rc;
         (void)hipGetLastError();
@@ -1033,7 +1102,9 @@ int lamp_ps_scores(const float *q, const float *k, int B, int H, int S, int D, i
         if (rc != LAMP_OK)
             return rc;
         void *ws = nullptr;
-        rc = pool_get(align_up(2 * z.BH * (uint64_t)z.tiles), &ws);
+        hipStream_t st = (hipStream_t)stream;
+        PoolLease lease;
+        rc = lease.acquire(align_up(2 * z.BH * (uint64_t)z.tiles), st, &ws);
         if (rc != LAMP_OK)
             return rc;
         lamp::Problem P{};
@@ -1047,7 +1118,6 @@ int lamp_ps_scores(const float *q, const float *k, int B, int H, int S, int D, i
         P.pc = lamp::make_ps_const(mu, D);
         P.tiles = z.tiles;
         P.n_rows = z.n_rows;
-        hipStream_t st = (hipStream_t)stream;
         (void)hipGetLastError();
         LAMP_HIP_TRY(lamp::launch_operand_scan(P, (uint8_t *)ws, st), "operand scan launch");
         LAMP_HIP_TRY(lamp::launch_ps_scores(P, (uint8_t *)ws, ylo, yref, nullptr, nullptr, false, st),

@@ -464,6 +464,36 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask)
                                      __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
+// All four values finite; and the same values with every non-finite one
+// replaced by 0 (V tiles of causal P.V steps, where a key past a row's
+// limit carries probability 0).
+__device__ __forceinline__ bool finite4(float4 x)
+{
+    return isfinite(x.x) && isfinite(x.y) && isfinite(x.z) && isfinite(x.w);
+}
+
+__device__ __forceinline__ float4 finite_or_zero(float4 x)
+{
+    return make_float4(isfinite(x.x) ? x.x : 0.0f, isfinite(x.y) ? x.y : 0.0f,
+                       isfinite(x.z) ? x.z : 0.0f, isfinite(x.w) ? x.w : 0.0f);
+}
+
+// Near tie of a criterion decided as c > t: |c - t| <= 2^-16 t with t
+// finite, the band where a single-precision evaluation of c could not decide
+// (the library decides every key in double precision).
+__device__ __forceinline__ bool near_tie(double c, double t)
+{
+    return fabs(c - t) <= 0x1p-16 * t && t < INFINITY;
+}
+
+// Adds a wave's count of near ties to the call's total: one atomic per wave
+// that has any (wave-uniform count).
+__device__ __forceinline__ void add_ties(unsigned long long *n, uint32_t cnt)
+{
+    if (n && cnt && (threadIdx.x & 63) == 0)
+        atomicAdd(n, (unsigned long long)cnt);
+}
+
 // SplitMix64 output for a state (Steele, Lea & Flood, OOPSLA 2014): add the
 // golden gamma, then two xor-shift-multiply mixing rounds and a final
 // xor-shift.

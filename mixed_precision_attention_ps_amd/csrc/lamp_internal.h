@@ -39,6 +39,7 @@ struct Problem {
     uint64_t head_valid;  // valid pairs per head
     bool ref_sums = true; // per-tile partials carry the reference sums L, B
                           // (false: only the maxima, when no KL is asked for)
+    unsigned long long *n_band = nullptr;   // near-tie count of the criterion
 };
 
 // Operand range scan: unsafe[bh * tiles + t] = 1 when a 64-row block of Q
@@ -149,6 +150,7 @@ struct DecodeProblem {
     int BH, S, D, nq, causal, mu;
     float tau;
     int ps_block;             // accumulation order (0 sequential)
+    unsigned long long *n_band = nullptr;   // near-tie count of the criterion
 };
 
 // Softmax partial sums of one (head, 64-key block, query): maxima of y^mix,
@@ -194,6 +196,7 @@ struct MlpProblem {
     int M, N, K, mu, op;
     float tau, eps;
     int ps_block;                 // accumulation order (0 sequential)
+    unsigned long long *n_band = nullptr;   // near-tie count of the GELU criterion
 };
 
 struct MlpBuffers {
@@ -222,6 +225,7 @@ struct DevStats {
     unsigned long long n_selected;
     unsigned long long n_exact_tiles;
     double kl_sum, kl_max, kl_lowp_sum;
+    unsigned long long n_tie_band;   // criterion values within 2^-16 tau of tau
 };
 
 hipError_t launch_stats(const Problem &p, const double *row_kl, const double *row_kl_lowp,

@@ -113,6 +113,7 @@ struct GemmArgs {
     double tau;
     unsigned long long *exact_tiles;
     long long n_tiles;
+    unsigned long long *n_band;   // near ties of the GELU criterion
 };
 
 template <int PATH, int EPI, int P>
@@ -124,6 +125,7 @@ __device__ __forceinline__ void gemm_tile(TileSmem &sm, const double *s_exp, con
     float lo[4][4], ref[4][4];
     tile_scores<PATH, P>(acc, a.pc, lo, ref);
     const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4, lane = tid & 63;
+    uint32_t ties = 0;   // this thread's near ties of the GELU criterion
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int i = ti * kTile + ty * 4 + r;
@@ -151,7 +153,9 @@ __device__ __forceinline__ void gemm_tile(TileSmem &sm, const double *s_exp, con
             for (int c = 0; c < 4; ++c) {
                 const int j = tj * kTile + tx + 16 * c;
                 const Gelu gl = gelu64((double)lo[r][c], s_exp);
-                sel[c] = valid[c] && fabs(gl.dg * (double)lo[r][c]) > a.tau;
+                const double crit = fabs(gl.dg * (double)lo[r][c]);
+                sel[c] = valid[c] && crit > a.tau;
+                ties += (valid[c] && near_tie(crit, a.tau)) ? 1u : 0u;
                 const Gelu gr = gelu64((double)ref[r][c], s_exp);
                 const double gm = sel[c] ? gr.g : gl.g;
                 if (valid[c]) {
@@ -198,6 +202,8 @@ __device__ __forceinline__ void gemm_tile(TileSmem &sm, const double *s_exp, con
             }
         }
     }
+    if (EPI == EPI_GELU)
+        add_ties(a.n_band, (uint32_t)wave_sum_int((int)ties));
 }
 
 // FAST: the tiles whose operands allow the FP32 fast path (one work-group per
@@ -352,6 +358,7 @@ __global__ __launch_bounds__(kThreads) void ps_gemm_narrow_kernel(GemmArgs a)
             narrow_flush<P>(lo, blk, pc);
     }
 
+    uint32_t ties = 0;   // this thread's near ties of the GELU criterion
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
         const int i = row0 + ty * 2 + r;
@@ -382,7 +389,9 @@ __global__ __launch_bounds__(kThreads) void ps_gemm_narrow_kernel(GemmArgs a)
             for (int c = 0; c < 2; ++c) {
                 const int j = col0 + tx + 16 * c;
                 const Gelu gl = gelu64((double)ylo[c], s_exp);
-                sel[c] = valid[c] && fabs(gl.dg * (double)ylo[c]) > a.tau;
+                const double crit = fabs(gl.dg * (double)ylo[c]);
+                sel[c] = valid[c] && crit > a.tau;
+                ties += (valid[c] && near_tie(crit, a.tau)) ? 1u : 0u;
                 const Gelu gr = gelu64((double)yref[c], s_exp);
                 const double gm = sel[c] ? gr.g : gl.g;
                 if (valid[c]) {
@@ -410,6 +419,8 @@ __global__ __launch_bounds__(kThreads) void ps_gemm_narrow_kernel(GemmArgs a)
             }
         }
     }
+    if (EPI == EPI_GELU)
+        add_ties(a.n_band, (uint32_t)wave_sum_int((int)ties));
 }
 
 // Per-row sums of the GELU error partials (one per 32-column block): one wave
@@ -694,6 +705,7 @@ hipError_t launch_mlp(const MlpProblem &p, const MlpBuffers &b, hipStream_t st,
     a.err_part = b.err_part;
     a.errl_part = b.errl_part;
     a.tau = (double)p.tau;
+    a.n_band = p.n_band;
     a.exact_tiles = b.exact_tiles;
     a.n_tiles = (long long)tiles_m * tiles_n;
     if (a.n_tiles > 0x7fffffffLL)

@@ -37,6 +37,7 @@ struct RelaxedArgs {
     float *ymix_raw, *yref_out, *row_m;
     double *row_l;
     unsigned long long *exact_tiles;
+    unsigned long long *n_band;
 };
 
 // Online state of one query row: maxima of y^lo (m_t), y^mix and y^ref, and
@@ -92,7 +93,10 @@ void relaxed_kernel(RelaxedArgs a)
     constexpr int V4 = (NV4 + kThreads - 1) / kThreads;   // per thread
     __shared__ RelaxedSmem<DV> sm;
     __shared__ double s_exp[64];   // 2^(k/64) for exp64
+    __shared__ int s_vbad;         // the diagonal V tile holds a non-finite value
     exp_table_fill(s_exp);
+    if (threadIdx.x == 0)
+        s_vbad = 0;
     __syncthreads();
     const int S = a.S, D = a.D;
     // heaviest query blocks first (causal work grows with the block index)
@@ -141,6 +145,7 @@ void relaxed_kernel(RelaxedArgs a)
     uint32_t *const mask_blk = a.mask ? a.mask + blk_row * (uint64_t)a.W : nullptr;
     float *const ymix_blk = a.ymix_raw ? a.ymix_raw + blk_row * (uint64_t)S : nullptr;
     float *const yref_blk = a.yref_out ? a.yref_out + blk_row * (uint64_t)S : nullptr;
+    uint32_t ties = 0;   // this thread's near ties of the criterion
     for (int t = 0; t <= t_end; ++t) {
         const int col0 = t * kTile;
         float lo[4][4], ref[4][4];
@@ -187,7 +192,9 @@ void relaxed_kernel(RelaxedArgs a)
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 E[c] = valid[c] ? exp64((double)lo[r][c] - (double)mt_new, s_exp) : 0.0;
-                sel[c] = valid[c] && 2.0 * E[c] * fabs((double)lo[r][c]) > a.tau;
+                const double crit = 2.0 * E[c] * fabs((double)lo[r][c]);
+                sel[c] = valid[c] && crit > a.tau;
+                ties += (valid[c] && near_tie(crit, a.tau)) ? 1u : 0u;
                 mix[c] = sel[c] ? ref[r][c] : lo[r][c];
                 if (valid[c]) {
                     bm = fmaxf(bm, mix[c]);
@@ -308,12 +315,23 @@ void relaxed_kernel(RelaxedArgs a)
 #pragma unroll
             for (int c = 0; c < 4; ++c)
                 sm.u.p[ty * 4 + r][tx + 16 * c] = pmix[r][c];
+        // The causal diagonal tile holds keys past some rows' limits, whose
+        // probability 0 would turn a non-finite V value into NaN (0 * inf) in
+        // the product: such values are staged as 0 and added back at the end
+        // for the rows that see their key.
+        const bool diag = a.causal && t == qb;
 #pragma unroll
         for (int u = 0; u < V4; ++u) {
             const int e = tid + u * kThreads;
             const int key = e / (DV / 4), col = (e % (DV / 4)) * 4;
-            if (e < NV4)
-                *reinterpret_cast<float4 *>(&sm.v[key][col]) = vreg[u];
+            if (e < NV4) {
+                float4 x = vreg[u];
+                if (diag && !finite4(x)) {
+                    x = finite_or_zero(x);
+                    s_vbad = 1;
+                }
+                *reinterpret_cast<float4 *>(&sm.v[key][col]) = x;
+            }
         }
         __syncthreads();
 #pragma unroll
@@ -369,10 +387,22 @@ void relaxed_kernel(RelaxedArgs a)
 #pragma unroll
         for (int q = 0; q < NB; ++q) {
             const int col = q * 16 + (lane & 15);
-            if (col < D)
-                a.out[row * (uint64_t)D + col] = (float)(acc[q][r] * inv);
+            if (col < D) {
+                double o = acc[q][r];
+                // non-finite V values of the diagonal tile, staged as 0: each
+                // one at a key the row sees adds its infinity or NaN (what any
+                // positive probability times it gives)
+                if (s_vbad)
+                    for (int j = row0; j <= i; ++j) {
+                        const float x = Vh[(size_t)j * D + col];
+                        if (!isfinite(x))
+                            o += (double)x;
+                    }
+                a.out[row * (uint64_t)D + col] = (float)(o * inv);
+            }
         }
     }
+    add_ties(a.n_band, (uint32_t)wave_sum_int((int)ties));
 }
 
 hipError_t launch_relaxed(const Problem &p, const uint8_t *unsafe, float *out, uint32_t *mask,
@@ -394,6 +424,7 @@ hipError_t launch_relaxed(const Problem &p, const uint8_t *unsafe, float *out, u
     a.BH = p.BH;
     a.W = (p.S + 31) / 32;
     a.tau = (double)p.tau;
+    a.n_band = p.n_band;
     a.pc = p.pc;
     a.unsafe_q = unsafe;
     a.unsafe_k = unsafe + (size_t)p.BH * p.tiles;

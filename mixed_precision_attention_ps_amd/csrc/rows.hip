@@ -35,6 +35,7 @@ struct RowsArgs {
     uint32_t *mask, *row_count;
     float *pbuf, *ymix_out;
     double *row_kl, *row_kl_lowp;
+    unsigned long long *n_band;
 };
 
 // D4 = D / 4 when the head dimension is a compile-time constant (all loads of
@@ -180,6 +181,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5))) v
     const double tau_l2 = a.tau * (L * L) * 0.5;
     uint32_t selbits = 0;
     uint32_t total = 0;
+    uint32_t ties = 0;
     float ef[kRowChunk];
     const int rem_c = fresh();
 #pragma unroll
@@ -199,12 +201,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5))) v
                     if (dir)
                         E = exp64((double)v[t] - (double)mtt, s_exp);
                 }
-                sel = valid && 2.0 * E * fabs((double)v[t]) > a.tau;
+                const double crit = 2.0 * E * fabs((double)v[t]);
+                sel = valid && crit > a.tau;
+                ties += (uint32_t)__popcll(__ballot(valid && near_tie(crit, a.tau)));
             } else {
                 const bool at = valid && v[t] == m;
                 ef[t] = (float)e[t];
                 const double rest = at ? rest_at_max : L - e[t];
-                sel = valid && e[t] * rest * fabs((double)v[t]) > tau_l2;
+                const double crit = e[t] * rest * fabs((double)v[t]);
+                sel = valid && crit > tau_l2;
+                ties += (uint32_t)__popcll(__ballot(valid && near_tie(crit, tau_l2)));
             }
             const uint64_t b = __ballot(sel);
             if (a.mask) {
@@ -221,6 +227,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5))) v
     if (a.mask)   // the mask words of the chunks past the valid keys
         for (int w = 2 * nch + lane; w < a.W; w += 64)
             a.mask[r * (uint64_t)a.W + w] = 0u;
+    add_ties(a.n_band, ties);
 
     // Reference statistics from the score kernel's per-tile partials.
     const bool kl = a.part != nullptr && (a.row_kl || a.row_kl_lowp);
@@ -456,6 +463,7 @@ hipError_t launch_strict_rows(const Problem &p, const float *ylo, const float *y
     a.ymix_out = ymix_out;
     a.row_kl = row_kl;
     a.row_kl_lowp = row_kl_lowp;
+    a.n_band = p.n_band;
     const uint64_t grid = (p.n_rows + 3) / 4;
 #define LAMP_ROWS_LAUNCH(RLX)                                                                 \
     do {                                                                                      \

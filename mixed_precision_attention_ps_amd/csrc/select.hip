@@ -24,6 +24,7 @@ struct SelectArgs {
     RowStats *rs;
     double *row_kl, *row_kl_lowp;
     int count_only;
+    unsigned long long *n_band;
 };
 
 constexpr int kSelChunk = 16;   // keys per lane held in registers (1024 per wave)
@@ -171,13 +172,16 @@ __global__ __launch_bounds__(kThreads) void strict_select_kernel(SelectArgs a)
     // c = 2 z (1 - z) |y| with z = e / L and 1 - z = rest / L, rest = L - e
     // (or the sum of the other keys at the maximum): 2 e rest |y| / L^2.
     const double inv_l2 = 1.0 / (L * L);
+    uint32_t ties = 0;
     auto decide = [&](int j0, int j, float v, double e) {
-        bool sel = false;
+        bool sel = false, tie = false;
         if (j < n) {
             const double rest = (v == m) ? rest_at_max : L - e;
             const double c = 2.0 * e * rest * fabs((double)v) * inv_l2;
             sel = c > a.tau;
+            tie = near_tie(c, a.tau);
         }
+        ties += (uint32_t)__popcll(__ballot(tie));
         const uint64_t b = __ballot(sel);
         if (!a.count_only) {
             if (a.mask) {
@@ -219,6 +223,7 @@ __global__ __launch_bounds__(kThreads) void strict_select_kernel(SelectArgs a)
     }
     if (lane == 0)
         a.row_count[r] = total;
+    add_ties(a.n_band, ties);
 }
 
 hipError_t launch_strict_select(const Problem &p, const float *ylo, const float *yref,
@@ -234,6 +239,7 @@ hipError_t launch_strict_select(const Problem &p, const float *ylo, const float 
     a.W = (p.S + 31) / 32;
     a.n_rows = p.n_rows;
     a.tau = (double)p.tau;
+    a.n_band = p.n_band;
     a.mask = mask;
     a.list = list;
     a.row_count = row_count;
@@ -276,6 +282,7 @@ struct RelaxedSelectArgs {
     uint32_t *mask, *row_count;
     RowStats *rs;
     double *row_kl, *row_kl_lowp;
+    unsigned long long *n_band;
 };
 
 __global__ __launch_bounds__(kThreads) void relaxed_select_kernel(RelaxedSelectArgs a)
@@ -328,6 +335,7 @@ __global__ __launch_bounds__(kThreads) void relaxed_select_kernel(RelaxedSelectA
     double g_lo = 0.0, g_mix = 0.0;
     double l_lo = 0.0, l_un = 0.0, l_sel = 0.0, dA = 0.0;
     bool has_nan = false;
+    uint32_t ties = 0;
     uint32_t total = 0;
     // Selected keys wait in this wave's LDS queue (key, y^lo) and are taken
     // 64 at a time, one per lane: y^ref read, y^mix written, their
@@ -373,7 +381,9 @@ __global__ __launch_bounds__(kThreads) void relaxed_select_kernel(RelaxedSelectA
                 const double E =
                     exp64_nonpos(valid ? (double)v - (double)mt : -INFINITY, s_exp);
                 has_nan |= valid && v != v;
-                const bool sel = valid && 2.0 * E * fabs((double)v) > a.tau;
+                const double c = 2.0 * E * fabs((double)v);
+                const bool sel = valid && c > a.tau;
+                ties += (uint32_t)__popcll(__ballot(valid && near_tie(c, a.tau)));
                 l_lo = fma(E, g_lo, l_lo);
                 l_un = sel ? l_un : fma(E, g_mix, l_un);
                 const uint64_t b = __ballot(sel);
@@ -451,6 +461,7 @@ __global__ __launch_bounds__(kThreads) void relaxed_select_kernel(RelaxedSelectA
         if (a.row_kl_lowp)
             a.row_kl_lowp[r] = Br / Lr + lse_lo - lse_ref;
     }
+    add_ties(a.n_band, ties);
 }
 
 hipError_t launch_relaxed_select(const Problem &p, float *y, const float *yref,
@@ -470,6 +481,7 @@ hipError_t launch_relaxed_select(const Problem &p, float *y, const float *yref,
     a.W = (p.S + 31) / 32;
     a.n_rows = p.n_rows;
     a.tau = (double)p.tau;
+    a.n_band = p.n_band;
     a.mask = mask;
     a.row_count = row_count;
     a.rs = rs;

@@ -64,6 +64,9 @@ def make_special(B: int, H: int, S: int, D: int, *, kind: str, seed: int = 0):
           "huge"     -- magnitudes spread over [2^40, 2^66] (products overflow)
           "mixed"    -- normal values with a few zeros, tiny and huge entries
           "nonfinite"-- normal values with a few inf / nan entries
+          "nonfinite_v" -- Q, K standard normal; V standard normal with a
+                      few +inf, -inf and nan entries (about 0.1 %, 0.1 % and
+                      0.05 %)
     """
     rng = np.random.default_rng(seed)
     shape = (B, H, S, D)
@@ -89,7 +92,15 @@ def make_special(B: int, H: int, S: int, D: int, *, kind: str, seed: int = 0):
                 X[(u >= 0.02) & (u < 0.021)] = np.inf
                 X[(u >= 0.021) & (u < 0.022)] = -np.inf
                 X[(u >= 0.022) & (u < 0.023)] = np.nan
+    elif kind == "nonfinite_v":
+        Q = rng.standard_normal(shape, dtype=np.float32)
+        K = rng.standard_normal(shape, dtype=np.float32)
     else:
         raise ValueError(kind)
     V = rng.standard_normal(shape, dtype=np.float32)
+    if kind == "nonfinite_v":
+        u = rng.random(shape)
+        V[u < 0.001] = np.inf
+        V[(u >= 0.001) & (u < 0.002)] = -np.inf
+        V[(u >= 0.002) & (u < 0.0025)] = np.nan
     return np.ascontiguousarray(Q), np.ascontiguousarray(K), V

@@ -22,11 +22,16 @@ LAMP_N_STAGES = len(STAGES)
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblamp.so")
 
 
+IMPLS = {0: "none", 1: "strict_rows", 2: "strict_stream", 3: "random", 4: "relaxed_fused",
+         5: "relaxed_rows", 6: "relaxed_stream", 7: "decode", 8: "gelu", 9: "layernorm"}
+
+
 class LampStats(ctypes.Structure):
     _fields_ = [("n_rows", ctypes.c_uint64), ("n_valid", ctypes.c_uint64),
                 ("n_selected", ctypes.c_uint64), ("n_exact_tiles", ctypes.c_uint64),
                 ("kl_sum", ctypes.c_double), ("kl_max", ctypes.c_double),
-                ("kl_lowp_sum", ctypes.c_double)]
+                ("kl_lowp_sum", ctypes.c_double), ("n_tie_band", ctypes.c_uint64),
+                ("impl", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -38,7 +43,8 @@ class LampParams(ctypes.Structure):
                 ("row_kl", ctypes.c_void_p), ("row_kl_lowp", ctypes.c_void_p),
                 ("row_count", ctypes.c_void_p), ("scores_mix", ctypes.c_void_p),
                 ("scores_ref", ctypes.c_void_p), ("stage_events", ctypes.c_void_p),
-                ("ps_block", ctypes.c_int), ("relaxed_path", ctypes.c_int)]
+                ("ps_block", ctypes.c_int), ("relaxed_path", ctypes.c_int),
+                ("block_k", ctypes.c_int)]
 
 
 class LampError(RuntimeError):
@@ -76,6 +82,8 @@ def library():
     lib.lamp_last_error.argtypes = []
     lib.lamp_version.restype = I
     lib.lamp_version.argtypes = []
+    lib.lamp_last_impl.restype = I
+    lib.lamp_last_impl.argtypes = []
     lib.lamp_diag_exp.restype = I
     lib.lamp_diag_exp.argtypes = [P, P, P, I, P]
     lib.lamp_decode_fwd.restype = I
@@ -97,7 +105,7 @@ def library():
     return lib
 
 
-def _check(rc: int):
+def _rc(rc: int):
     if rc != LAMP_OK:
         lib = library()
         detail = (lib.lamp_last_error() or b"").decode() or lib.lamp_strerror(rc).decode()
@@ -118,6 +126,39 @@ def _f32(t, name):
     if t.dtype != torch.float32:
         raise TypeError(f"{name} must be float32")
     return _ptr(t)
+
+
+_INT32 = (torch.int32, torch.uint32)
+
+
+def _check(t, name, shape, dtypes, device):
+    """A tensor the library will read or write: a contiguous tensor of exactly
+    `shape`, one of `dtypes`, on `device` (a wrong size would let the kernels
+    run past its allocation).  None passes."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, not {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} must be {' or '.join(str(d) for d in dtypes)}, not {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, not {tuple(t.shape)}")
+
+
+def _check_workspace(ws, device):
+    if ws is None:
+        return
+    if not isinstance(ws, torch.Tensor) or ws.device != device or not ws.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {device}")
+
+
+def last_impl() -> str:
+    """Name of the implementation the calling thread's last successful call ran."""
+    return IMPLS.get(int(library().lamp_last_impl()), "unknown")
 
 
 def lamp_diag_exp(x):
@@ -146,11 +187,14 @@ def lamp_workspace_bytes_ex(B, H, S, D, causal, mode, want_probs, want_stats,
 def lamp_ps_scores(q, k, *, causal: bool, mu: int, ylo=None, yref=None):
     """Step 1 alone: PS(mu) scores and FP32 scores into [B,H,S,S] buffers."""
     B, H, S, D = q.shape
+    _check(k, "k", (B, H, S, D), (torch.float32,), q.device)
     if ylo is None and yref is None:
         ylo = torch.empty((B, H, S, S), device=q.device, dtype=torch.float32)
         yref = torch.empty_like(ylo)
+    for name, t in (("ylo", ylo), ("yref", yref)):
+        _check(t, name, (B, H, S, S), (torch.float32,), q.device)
     stream = ctypes.c_void_p(torch.cuda.current_stream(q.device).cuda_stream)
-    _check(library().lamp_ps_scores(_f32(q, "q"), _f32(k, "k"), B, H, S, D, int(causal), int(mu),
+    _rc(library().lamp_ps_scores(_f32(q, "q"), _f32(k, "k"), B, H, S, D, int(causal), int(mu),
                                     _ptr(ylo), _ptr(yref), stream))
     return ylo, yref
 
@@ -159,7 +203,7 @@ def lamp_attention_fwd(q, k, v, *, causal: bool, mu: int, tau: float, mode="stri
                        probs=None, recompute_mask=None, want_stats: bool = True, seed: int = 0,
                        row_kl=None, row_kl_lowp=None, row_count=None, scores_mix=None,
                        scores_ref=None, workspace=None, stage_events=None, ps_block: int = 0,
-                       relaxed_path: int = 0):
+                       relaxed_path: int = 0, block_k: int = 0):
     """LAMP attention forward through lamp_attention_fwd_ex.
 
     q, k, v: float32 [B, H, S, D] device tensors.  Optional outputs are written
@@ -167,15 +211,31 @@ def lamp_attention_fwd(q, k, v, *, causal: bool, mu: int, tau: float, mode="stri
     1 the fused one-pass kernel, 2 two passes (score tiles, then a row pass).
     Returns (out, stats_dict_or_None).
     """
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, S, D]")
     B, H, S, D = q.shape
+    dev = q.device
+    W = (S + 31) // 32
     if out is None:
         out = torch.empty_like(q)
+    f32, f64 = (torch.float32,), (torch.float64,)
+    for name, t, shape, dt in (
+            ("k", k, (B, H, S, D), f32), ("v", v, (B, H, S, D), f32),
+            ("out", out, (B, H, S, D), f32), ("probs", probs, (B, H, S, S), f32),
+            ("recompute_mask", recompute_mask, (B, H, S, W), _INT32),
+            ("row_kl", row_kl, (B, H, S), f64), ("row_kl_lowp", row_kl_lowp, (B, H, S), f64),
+            ("row_count", row_count, (B, H, S), _INT32),
+            ("scores_mix", scores_mix, (B, H, S, S), f32),
+            ("scores_ref", scores_ref, (B, H, S, S), f32)):
+        _check(t, name, shape, dt, dev)
+    _check_workspace(workspace, dev)
     m = MODES.get(mode, mode)
     p = LampParams()
     p.stream = torch.cuda.current_stream(q.device).cuda_stream
     p.seed = seed & 0xFFFFFFFFFFFFFFFF
     p.ps_block = int(ps_block)
     p.relaxed_path = int(relaxed_path)
+    p.block_k = int(block_k)
     if workspace is not None:
         p.workspace = workspace.data_ptr()
         p.workspace_bytes = workspace.numel() * workspace.element_size()
@@ -191,7 +251,7 @@ def lamp_attention_fwd(q, k, v, *, causal: bool, mu: int, tau: float, mode="stri
         if recompute_mask.dtype not in (torch.int32, torch.uint32):
             raise TypeError("recompute_mask must be a 32-bit integer tensor")
         mask_ptr = _ptr(recompute_mask)
-    _check(library().lamp_attention_fwd_ex(
+    _rc(library().lamp_attention_fwd_ex(
         _f32(q, "q"), _f32(k, "k"), _f32(v, "v"), B, H, S, D, int(causal), int(mu),
         ctypes.c_float(tau), int(m), _f32(out, "out"),
         None if probs is None else _f32(probs, "probs"), mask_ptr,
@@ -209,12 +269,27 @@ def lamp_decode_fwd(q, k, v, *, causal: bool, mu: int, tau: float, out=None, pro
     queries are the last Nq positions of the sequence).  Optional outputs are
     written in place when given.  Returns (out, stats_dict_or_None).
     """
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B, H, Nq, D] and k [B, H, S, D]")
     B, H, Nq, D = q.shape
     S = k.shape[2]
     if tuple(k.shape) != (B, H, S, D) or tuple(v.shape) != (B, H, S, D):
         raise ValueError("k and v must be [B, H, S, D] with q's B, H, D")
+    dev = q.device
+    W = (S + 31) // 32
     if out is None:
         out = torch.empty_like(q)
+    f32, f64 = (torch.float32,), (torch.float64,)
+    for name, t, shape, dt in (
+            ("k", k, (B, H, S, D), f32), ("v", v, (B, H, S, D), f32),
+            ("out", out, (B, H, Nq, D), f32), ("probs", probs, (B, H, Nq, S), f32),
+            ("recompute_mask", recompute_mask, (B, H, Nq, W), _INT32),
+            ("row_kl", row_kl, (B, H, Nq), f64), ("row_kl_lowp", row_kl_lowp, (B, H, Nq), f64),
+            ("row_count", row_count, (B, H, Nq), _INT32),
+            ("scores_mix", scores_mix, (B, H, Nq, S), f32),
+            ("scores_ref", scores_ref, (B, H, Nq, S), f32)):
+        _check(t, name, shape, dt, dev)
+    _check_workspace(workspace, dev)
     p = LampParams()
     p.stream = torch.cuda.current_stream(q.device).cuda_stream
     p.ps_block = int(ps_block)
@@ -233,7 +308,7 @@ def lamp_decode_fwd(q, k, v, *, causal: bool, mu: int, tau: float, out=None, pro
         if recompute_mask.dtype not in (torch.int32, torch.uint32):
             raise TypeError("recompute_mask must be a 32-bit integer tensor")
         mask_ptr = _ptr(recompute_mask)
-    _check(library().lamp_decode_fwd(
+    _rc(library().lamp_decode_fwd(
         _f32(q, "q"), _f32(k, "k"), _f32(v, "v"), B, H, Nq, S, D, int(causal), int(mu),
         ctypes.c_float(tau), _f32(out, "out"),
         None if probs is None else _f32(probs, "probs"), mask_ptr,
@@ -270,7 +345,22 @@ def _mask_ptr(mask):
 def _mlp_shapes(x, w):
     if x.dim() != 2 or w.dim() != 2 or x.shape[1] != w.shape[1]:
         raise ValueError("x must be [M, K] and w [N, K]")
+    _check(w, "w", tuple(w.shape), (torch.float32,), x.device)
     return x.shape[0], w.shape[0], x.shape[1]
+
+
+def _mlp_checks(x, M, N, out, recompute_mask, row_err, row_err_lowp, row_count, scores_mix,
+                scores_ref, workspace):
+    dev = x.device
+    f32, f64 = (torch.float32,), (torch.float64,)
+    for name, t, shape, dt in (
+            ("out", out, (M, N), f32), ("recompute_mask", recompute_mask, (M, (N + 31) // 32),
+                                        _INT32),
+            ("row_err", row_err, (M,), f64), ("row_err_lowp", row_err_lowp, (M,), f64),
+            ("row_count", row_count, (M,), _INT32), ("scores_mix", scores_mix, (M, N), f32),
+            ("scores_ref", scores_ref, (M, N), f32)):
+        _check(t, name, shape, dt, dev)
+    _check_workspace(workspace, dev)
 
 
 def lamp_mlp_workspace_bytes(M, N, K, op) -> int:
@@ -283,8 +373,10 @@ def lamp_gemm_scores(x, w, *, mu: int, ylo=None, yref=None):
     if ylo is None and yref is None:
         ylo = torch.empty((M, N), device=x.device, dtype=torch.float32)
         yref = torch.empty_like(ylo)
+    for name, t in (("ylo", ylo), ("yref", yref)):
+        _check(t, name, (M, N), (torch.float32,), x.device)
     stream = ctypes.c_void_p(torch.cuda.current_stream(x.device).cuda_stream)
-    _check(library().lamp_gemm_scores(_f32(x, "x"), _f32(w, "w"), M, N, K, int(mu), _ptr(ylo),
+    _rc(library().lamp_gemm_scores(_f32(x, "x"), _f32(w, "w"), M, N, K, int(mu), _ptr(ylo),
                                       _ptr(yref), stream))
     return ylo, yref
 
@@ -301,11 +393,13 @@ def lamp_gelu_fwd(x, w, *, mu: int, tau: float, out=None, recompute_mask=None,
     M, N, K = _mlp_shapes(x, w)
     if out is None:
         out = torch.empty((M, N), device=x.device, dtype=torch.float32)
+    _mlp_checks(x, M, N, out, recompute_mask, row_err, row_err_lowp, row_count, scores_mix,
+                scores_ref, workspace)
     p = _mlp_params(x.device, workspace, stage_events, ps_block, row_kl=row_err,
                     row_kl_lowp=row_err_lowp, row_count=row_count, scores_mix=scores_mix,
                     scores_ref=scores_ref)
     st = LampStats() if want_stats else None
-    _check(library().lamp_gelu_fwd(
+    _rc(library().lamp_gelu_fwd(
         _f32(x, "x"), _f32(w, "w"), M, N, K, int(mu), ctypes.c_float(tau), _f32(out, "out"),
         _mask_ptr(recompute_mask), ctypes.byref(st) if st is not None else None, ctypes.byref(p)))
     return out, (st.as_dict() if st is not None else None)
@@ -323,13 +417,17 @@ def lamp_layernorm_fwd(x, w, gamma, beta, *, mu: int, eps: float, tau: float, ou
     M, N, K = _mlp_shapes(x, w)
     if tuple(gamma.shape) != (N,) or tuple(beta.shape) != (N,):
         raise ValueError("gamma and beta must be [N]")
+    for name, t in (("gamma", gamma), ("beta", beta)):
+        _check(t, name, (N,), (torch.float32,), x.device)
     if out is None:
         out = torch.empty((M, N), device=x.device, dtype=torch.float32)
+    _mlp_checks(x, M, N, out, recompute_mask, row_err, row_err_lowp, row_count, scores_mix,
+                scores_ref, workspace)
     p = _mlp_params(x.device, workspace, stage_events, ps_block, row_kl=row_err,
                     row_kl_lowp=row_err_lowp, row_count=row_count, scores_mix=scores_mix,
                     scores_ref=scores_ref)
     st = LampStats() if want_stats else None
-    _check(library().lamp_layernorm_fwd(
+    _rc(library().lamp_layernorm_fwd(
         _f32(x, "x"), _f32(w, "w"), _f32(gamma, "gamma"), _f32(beta, "beta"), M, N, K, int(mu),
         ctypes.c_float(eps), ctypes.c_float(tau), _f32(out, "out"), _mask_ptr(recompute_mask),
         ctypes.byref(st) if st is not None else None, ctypes.byref(p)))

@@ -83,3 +83,20 @@ def assert_tol(got, want, scale, what, rel=1e-6, abs_=1e-7):
 def out_scale(probs64: np.ndarray, V: np.ndarray) -> np.ndarray:
     """sum_j p_j |v_jd| per (row, d), the natural scale of out."""
     return probs64 @ np.abs(V.astype(np.float64))
+
+
+def assert_out_with_nonfinite(got, want, scale, what="out"):
+    """out where V holds infinities or NaN: every non-finite oracle value is
+    matched exactly (NaN by NaN, an infinity by the same infinity), every
+    finite one within the out tolerance."""
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    nf = ~np.isfinite(want)
+    same = (np.isnan(got) & np.isnan(want)) | (got == want)
+    bad = nf & ~same
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        raise AssertionError(f"{what}: {bad.sum()} non-finite values differ, e.g. "
+                             f"{[(tuple(i), got[tuple(i)], want[tuple(i)]) for i in idx]}")
+    assert nf.any() and (~nf).any(), "the case should hold finite and non-finite outputs"
+    return assert_tol(got[~nf], want[~nf], np.asarray(scale, np.float64)[~nf], what)
