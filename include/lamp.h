@@ -228,6 +228,35 @@ int lamp_attention_fwd_ex(const float *q, const float *k, const float *v,
                           const lamp_params *p);
 
 /*
+ * lamp_attention_fwd_noalloc -- lamp_attention_fwd_ex for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  It allocates nothing (no hipMalloc /
+ * hipFree, no library allocation): its scratch is a fixed device array of
+ * LAMP_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends.  The caller still passes all inputs and outputs.
+ *   Arguments as for lamp_attention_fwd_ex; p->workspace must be NULL
+ *   (LAMP_ERR_INVALID_ARG otherwise).
+ *   A call whose scratch need (lamp_workspace_bytes_ex with the same
+ *   arguments; relaxed rows longer than 1024 keys fall back to the fused
+ *   one-pass kernel first) exceeds LAMP_NOALLOC_SCRATCH_BYTES is refused
+ *   with LAMP_ERR_UNSUPPORTED before any HIP call.  Passing the optional
+ *   buffers (probs, scores_ref, row_count, row_kl) keeps them out of the
+ *   scratch.
+ *   Every call on one GPU shares that GPU's array and leaves its contents
+ *   behind (each call clears what it needs cleared): calls that overlap on
+ *   one GPU -- different streams or host threads without ordering between
+ *   them -- race and give undefined results.  Order them (one stream, or
+ *   events), or use lamp_attention_fwd_ex.
+ *   A non-NULL `stats` still synchronises the stream.
+ */
+#define LAMP_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+int lamp_attention_fwd_noalloc(const float *q, const float *k, const float *v,
+                               int B, int H, int S, int D, int causal, int mu, float tau,
+                               int mode, float *out, float *probs, uint32_t *recompute_mask,
+                               lamp_stats *stats, const lamp_params *p);
+
+/*
  * lamp_workspace_bytes -- device scratch that lamp_attention_fwd_ex needs for
  * these sizes and mode when probs / scores_mix / scores_ref are not given by
  * the caller (an upper bound: it assumes none of them is).  Returns 0 on

@@ -651,6 +651,41 @@ int run_mlp(int op, const float *x, const float *w, const float *gamma, const fl
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free entry point: a fixed device array, one per
+// GPU (the code object's copy on each device), held until the process ends.
+// Host code never uses the array's name as an address: its device address is
+// looked up once per device with hipGetSymbolAddress and kept.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kScratchBytes = LAMP_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices];   // device address of `scratch` per device
+
+int scratch_address(void **out)
+{
+    int dev = 0;
+    LAMP_HIP_TRY(hipGetDevice(&dev), "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices)
+        return set_error(LAMP_ERR_UNSUPPORTED, "device index beyond the scratch table");
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        LAMP_HIP_TRY(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "hipGetSymbolAddress");
+        if (!ptr || ((uintptr_t)ptr & (kAlign - 1)) != 0)
+            return set_error(LAMP_ERR_HIP, "scratch array without a 256-byte aligned address");
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return LAMP_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char *lamp_strerror(int code)
@@ -736,9 +771,14 @@ size_t lamp_workspace_bytes_ex(int B, int H, int S, int D, int causal, int mode,
     }
 }
 
+// Workspace of a call: the caller's (lamp_params.workspace), the library's
+// pool, or -- for lamp_attention_fwd_noalloc -- the fixed scratch array.
+enum class WsSource { kCallerOrPool, kScratch };
+
 static int run(const float *q, const float *k, const float *v, int B, int H, int S, int D,
                int causal, int mu, float tau, int mode, float *out, float *probs,
-               uint32_t *mask, lamp_stats *stats, const lamp_params *pp)
+               uint32_t *mask, lamp_stats *stats, const lamp_params *pp,
+               WsSource src = WsSource::kCallerOrPool)
 {
     g_last_error.clear();
     int rc = check_args(q, k, v, causal, mu, tau, mode, out);
@@ -781,9 +821,29 @@ static int run(const float *q, const float *k, const float *v, int B, int H, int
     };
     if (p.workspace && p.workspace_bytes < L.total && may_fall_back)
         fall_back();
+    if (src == WsSource::kScratch) {
+        if (p.workspace)
+            return set_error(LAMP_ERR_INVALID_ARG,
+                             "lamp_attention_fwd_noalloc takes no workspace (it uses the "
+                             "library's scratch array)");
+        if (L.total > kScratchBytes && may_fall_back)
+            fall_back();
+        if (L.total > kScratchBytes)
+            return set_error(LAMP_ERR_UNSUPPORTED,
+                             "this call needs " + std::to_string(L.total) +
+                                 " bytes of scratch; lamp_attention_fwd_noalloc holds " +
+                                 std::to_string(kScratchBytes) +
+                                 " (pass buffers such as probs / scores_ref / row_count, or "
+                                 "use lamp_attention_fwd_ex)");
+    }
+
     PoolLease lease;
     void *ws = nullptr;
-    if (p.workspace) {
+    if (src == WsSource::kScratch) {
+        rc = scratch_address(&ws);
+        if (rc != LAMP_OK)
+            return rc;
+    } else if (p.workspace) {
         if (p.workspace_bytes < L.total)
             return set_error(LAMP_ERR_INVALID_ARG,
                              "workspace too small: need " + std::to_string(L.total) + " bytes");
@@ -970,6 +1030,21 @@ int lamp_attention_fwd_ex(const float *q, const float *k, const float *v, int B,
 {
     try {
         return run(q, k, v, B, H, S, D, causal, mu, tau, mode, out, probs, recompute_mask, stats, p);
+    } catch (const std::bad_alloc &) {
+        return set_error(LAMP_ERR_NO_MEMORY, "host allocation failed");
+    } catch (...) {
+        return set_error(LAMP_ERR_HIP, "unexpected exception");
+    }
+}
+
+int lamp_attention_fwd_noalloc(const float *q, const float *k, const float *v, int B, int H,
+                               int S, int D, int causal, int mu, float tau, int mode, float *out,
+                               float *probs, uint32_t *recompute_mask, lamp_stats *stats,
+                               const lamp_params *p)
+{
+    try {
+        return run(q, k, v, B, H, S, D, causal, mu, tau, mode, out, probs, recompute_mask, stats,
+                   p, WsSource::kScratch);
     } catch (const std::bad_alloc &) {
         return set_error(LAMP_ERR_NO_MEMORY, "host allocation failed");
     } catch (...) {

@@ -70,6 +70,8 @@ def library():
     lib.lamp_attention_fwd.argtypes = fwd_args
     lib.lamp_attention_fwd_ex.restype = I
     lib.lamp_attention_fwd_ex.argtypes = fwd_args + [ctypes.POINTER(LampParams)]
+    lib.lamp_attention_fwd_noalloc.restype = I
+    lib.lamp_attention_fwd_noalloc.argtypes = fwd_args + [ctypes.POINTER(LampParams)]
     lib.lamp_workspace_bytes.restype = ctypes.c_size_t
     lib.lamp_workspace_bytes.argtypes = [I, I, I, I, I, I]
     lib.lamp_workspace_bytes_ex.restype = ctypes.c_size_t
@@ -203,8 +205,10 @@ def lamp_attention_fwd(q, k, v, *, causal: bool, mu: int, tau: float, mode="stri
                        probs=None, recompute_mask=None, want_stats: bool = True, seed: int = 0,
                        row_kl=None, row_kl_lowp=None, row_count=None, scores_mix=None,
                        scores_ref=None, workspace=None, stage_events=None, ps_block: int = 0,
-                       relaxed_path: int = 0, block_k: int = 0):
-    """LAMP attention forward through lamp_attention_fwd_ex.
+                       relaxed_path: int = 0, block_k: int = 0, noalloc: bool = False):
+    """LAMP attention forward through lamp_attention_fwd_ex (or, with
+    noalloc=True, lamp_attention_fwd_noalloc: no workspace, the library's
+    fixed scratch array).
 
     q, k, v: float32 [B, H, S, D] device tensors.  Optional outputs are written
     in place when given.  relaxed_path (relaxed mode): 0 the library's choice,
@@ -251,7 +255,10 @@ def lamp_attention_fwd(q, k, v, *, causal: bool, mu: int, tau: float, mode="stri
         if recompute_mask.dtype not in (torch.int32, torch.uint32):
             raise TypeError("recompute_mask must be a 32-bit integer tensor")
         mask_ptr = _ptr(recompute_mask)
-    _rc(library().lamp_attention_fwd_ex(
+    if noalloc and workspace is not None:
+        raise ValueError("the allocation-free entry point takes no workspace")
+    fn = library().lamp_attention_fwd_noalloc if noalloc else library().lamp_attention_fwd_ex
+    _rc(fn(
         _f32(q, "q"), _f32(k, "k"), _f32(v, "v"), B, H, S, D, int(causal), int(mu),
         ctypes.c_float(tau), int(m), _f32(out, "out"),
         None if probs is None else _f32(probs, "probs"), mask_ptr,
