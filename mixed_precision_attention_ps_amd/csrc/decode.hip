@@ -354,9 +354,9 @@ __global__ __launch_bounds__(kThreads) void decode_softmax_kernel(DecodeArgs a)
         const double E = valid ? exp64((double)ylo - (double)mt, s_exp) : 0.0;
         const double crit = 2.0 * E * fabs((double)ylo);
         const bool sel = valid && crit > a.tau;
-        ties += (uint32_t)__popcll(__ballot(valid && near_tie(crit, a.tau)));
+        ties += (uint32_t)__popcll(ballot(valid && near_tie(crit, a.tau)));
         const float ymix = sel ? yref : ylo;
-        const uint64_t b = __ballot(sel);
+        const uint64_t b = ballot(sel);
         if (a.mask) {
             const int w = blk * 2 + lane;
             if (lane < 2 && w < a.W)

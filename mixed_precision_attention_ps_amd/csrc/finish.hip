@@ -34,9 +34,7 @@ struct FinishArgs {
 // step) while the next step's scores and V rows are already being loaded;
 // wave w multiplies rows 16w..16w+15 of P by V.  DV = 16 NB is the padded
 // head dimension (compile-time, so every MFMA and LDS index is static).
-// PIN: `ymix` already holds the probabilities (P.V only: no lse, no probs
-// write).
-template <int NB, int KS, bool PIN>
+template <int NB, int KS>
 __global__ __launch_bounds__(kThreads) void finish_kernel(FinishArgs a)
 {
     constexpr int kFinKeys = KS;          // keys per step
@@ -51,8 +49,7 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(FinishArgs a)
     __shared__ double s_lse[kFinRows];
     __shared__ double s_exp[64];   // 2^(k/64) for exp64
     __shared__ int s_vbad;         // a causal diagonal step met a non-finite V value
-    if (!PIN)
-        exp_table_fill(s_exp);
+    exp_table_fill(s_exp);
     if (threadIdx.x == 0)
         s_vbad = 0;
     __syncthreads();
@@ -66,7 +63,7 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(FinishArgs a)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
     // lse of each row; rows flagged by the recompute get a pass over the row.
-    for (int rr = 0; rr < (PIN ? 0 : kFinRows / 4); ++rr) {
+    for (int rr = 0; rr < kFinRows / 4; ++rr) {
         const int lr = wave * (kFinRows / 4) + rr;
         const int i = row0 + lr;
         double lse = 0.0;
@@ -101,8 +98,8 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(FinishArgs a)
     const int np = prow_ok ? (a.causal ? ip + 1 : S) : 0;
     const uint64_t rp = (uint64_t)bh * S + (prow_ok ? ip : 0);
     const float *ymp = a.ymix + rp * (uint64_t)S;
-    float *prp = (!PIN && a.probs) ? a.probs + rp * (uint64_t)S : nullptr;
-    const double lse_p = PIN ? 0.0 : s_lse[prow];
+    float *prp = a.probs ? a.probs + rp * (uint64_t)S : nullptr;
+    const double lse_p = s_lse[prow];
     const bool vec = (S & 3) == 0;
     const int nkeys = a.causal ? min(S, row0 + kFinRows) : S;   // keys the block attends
     const int nsteps = (nkeys + kFinKeys - 1) / kFinKeys;
@@ -162,7 +159,7 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(FinishArgs a)
         const int jb = j0 + kseg;
 #pragma unroll
         for (int e = 0; e < KPT; ++e)
-            pv[e] = (jb + e < np) ? (PIN ? ycur[e] : exp_f32((double)ycur[e] - lse_p)) : 0.0f;
+            pv[e] = (jb + e < np) ? exp_f32((double)ycur[e] - lse_p) : 0.0f;
         if (prp && prow_ok) {
             if (vec) {
 #pragma unroll
@@ -232,7 +229,7 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(FinishArgs a)
     // Keys past the causal limit of every row in the block: probabilities 0.
     // Wave w clears rows 16w..16w+15, each row's tail in contiguous 1 KB
     // stores (64 lanes x 16 bytes).
-    if (!PIN && a.probs) {
+    if (a.probs) {
         const int z0 = nsteps * kFinKeys;
         for (int rr = 0; rr < kFinRows / 4; ++rr) {
             const int iz = row0 + wave * (kFinRows / 4) + rr;
@@ -284,22 +281,21 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(FinishArgs a)
     }
 }
 
-template <bool PIN>
 static hipError_t launch_finish_kernel(const FinishArgs &a, const Problem &p, hipStream_t st)
 {
     const dim3 grid((unsigned)((uint64_t)p.BH * a.blocks_per_head)), block(kThreads);
     switch ((p.D + 15) / 16) {
-    case 1: hipLaunchKernelGGL((finish_kernel<1, 32, PIN>), grid, block, 0, st, a); break;
-    case 2: hipLaunchKernelGGL((finish_kernel<2, 32, PIN>), grid, block, 0, st, a); break;
-    case 3: hipLaunchKernelGGL((finish_kernel<3, 32, PIN>), grid, block, 0, st, a); break;
-    case 4: hipLaunchKernelGGL((finish_kernel<4, 32, PIN>), grid, block, 0, st, a); break;
-    case 5: hipLaunchKernelGGL((finish_kernel<5, 32, PIN>), grid, block, 0, st, a); break;
-    case 6: hipLaunchKernelGGL((finish_kernel<6, 32, PIN>), grid, block, 0, st, a); break;
-    case 7: hipLaunchKernelGGL((finish_kernel<7, 32, PIN>), grid, block, 0, st, a); break;
-    case 8: hipLaunchKernelGGL((finish_kernel<8, 32, PIN>), grid, block, 0, st, a); break;
+    case 1: hipLaunchKernelGGL((finish_kernel<1, 32>), grid, block, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((finish_kernel<2, 32>), grid, block, 0, st, a); break;
+    case 3: hipLaunchKernelGGL((finish_kernel<3, 32>), grid, block, 0, st, a); break;
+    case 4: hipLaunchKernelGGL((finish_kernel<4, 32>), grid, block, 0, st, a); break;
+    case 5: hipLaunchKernelGGL((finish_kernel<5, 32>), grid, block, 0, st, a); break;
+    case 6: hipLaunchKernelGGL((finish_kernel<6, 32>), grid, block, 0, st, a); break;
+    case 7: hipLaunchKernelGGL((finish_kernel<7, 32>), grid, block, 0, st, a); break;
+    case 8: hipLaunchKernelGGL((finish_kernel<8, 32>), grid, block, 0, st, a); break;
     case 9: case 10: case 11: case 12:
-        hipLaunchKernelGGL((finish_kernel<12, 16, PIN>), grid, block, 0, st, a); break;
-    default: hipLaunchKernelGGL((finish_kernel<16, 16, PIN>), grid, block, 0, st, a); break;
+        hipLaunchKernelGGL((finish_kernel<12, 16>), grid, block, 0, st, a); break;
+    default: hipLaunchKernelGGL((finish_kernel<16, 16>), grid, block, 0, st, a); break;
     }
     return hipGetLastError();
 }
@@ -318,24 +314,9 @@ hipError_t launch_finish(const Problem &p, const float *ymix, const RowStats *rs
     a.D = p.D;
     a.causal = p.causal;
     a.blocks_per_head = (p.S + kFinRows - 1) / kFinRows;
-    return launch_finish_kernel<false>(a, p, st);
+    return launch_finish_kernel(a, p, st);
 }
 
-hipError_t launch_pv(const Problem &p, const float *probs, float *out, hipStream_t st)
-{
-    FinishArgs a;
-    a.ymix = probs;
-    a.v = p.v;
-    a.rs = nullptr;
-    a.probs = nullptr;
-    a.out = out;
-    a.row_kl = nullptr;
-    a.S = p.S;
-    a.D = p.D;
-    a.causal = p.causal;
-    a.blocks_per_head = (p.S + kFinRows - 1) / kFinRows;
-    return launch_finish_kernel<true>(a, p, st);
-}
 
 // ---------------------------------------------------------------------------
 // Row reductions into the device summary (one work-group, fixed order).

@@ -174,7 +174,7 @@ struct Layout {
     size_t ymix = SIZE_MAX, yref = SIZE_MAX, list = SIZE_MAX, row_count = SIZE_MAX,
            row_kl = SIZE_MAX, row_kl_lowp = SIZE_MAX, unsafe = SIZE_MAX, dstats = SIZE_MAX,
            row_m = SIZE_MAX, row_l = SIZE_MAX, rowstats = SIZE_MAX, pbuf = SIZE_MAX,
-           part = SIZE_MAX;
+           part = SIZE_MAX, rowkl = SIZE_MAX;
     size_t total = 0;
     size_t take(size_t bytes)
     {
@@ -190,6 +190,7 @@ struct Needs {
                   // relaxed in two passes)
     bool pbuf;    // fused: probabilities need their own buffer
     bool part;    // fused: per-tile partials (KL wanted; relaxed rule)
+    bool rowkl;   // fused: per-row KL records (KL wanted)
     bool relaxed_long;   // relaxed in two passes over rows longer than 1024 keys
 };
 
@@ -227,6 +228,8 @@ Layout plan(const Sizes &z, int mode, const Needs &n)
             L.pbuf = L.take(4 * z.n_scores);
         if (n.part)
             L.part = L.take(sizeof(lamp::RefPartial) * z.n_rows * (uint64_t)z.tiles);
+        if (n.rowkl)
+            L.rowkl = L.take(sizeof(lamp::RowKL) * z.n_rows);
     } else {
         if (n.ymix)
             L.ymix = L.take(4 * z.n_scores);
@@ -263,6 +266,7 @@ Needs make_needs(const lamp_params &p, int mode, int S, bool probs, bool want_st
         need.ymix = p.scores_mix == nullptr && !probs;
         need.pbuf = p.scores_mix != nullptr && !probs;
         need.part = want_kl || relaxed_rows;
+        need.rowkl = want_kl;
         // the score tiles form y^ref for every pair when they form the
         // partials: kept, the row pass takes the selected scores' FP32 values
         // from it instead of forming each dot again
@@ -717,15 +721,15 @@ size_t lamp_workspace_bytes(int B, int H, int S, int D, int mode, int want_probs
     z.n_valid = z.BH * (uint64_t)S * (uint64_t)(S + 1) / 2;   // causal-agnostic bound below
     z.n_valid = z.n_scores > z.n_valid ? z.n_scores : z.n_valid;
     Needs n{mode == LAMP_RELAXED ? want_probs != 0 : want_probs == 0, true, true, true, true,
-            false, false, false};
+            false, false, false, false, false};
     size_t total = plan(z, mode, n).total;
     if ((mode == LAMP_STRICT || mode == LAMP_RELAXED) && S <= kFusedMaxS) {
-        Needs f{want_probs == 0, true, true, true, true, true, false, true};
+        Needs f{want_probs == 0, true, true, true, true, true, false, true, true, false};
         const size_t tf = plan(z, mode, f).total;
         total = tf > total ? tf : total;
     }
     if (mode == LAMP_RELAXED && S > kFusedMaxS) {
-        Needs f{want_probs == 0, true, true, true, true, false, false, false, true};
+        Needs f{want_probs == 0, true, true, true, true, false, false, false, false, true};
         const size_t tf = plan(z, mode, f).total;
         total = tf > total ? tf : total;
     }
@@ -962,16 +966,18 @@ static int run(const float *q, const float *k, const float *v, int B, int H, int
                                             &dstats->n_exact_tiles, true, st),
                      "score kernel launch");
         LAMP_HIP_TRY(tm.end(LAMP_STAGE_SCORES), "hipEventRecord");
+        auto *rowkl = at<lamp::RowKL>(ws, L.rowkl);
         LAMP_HIP_TRY(tm.begin(LAMP_STAGE_SELECT), "hipEventRecord");
-        LAMP_HIP_TRY(lamp::launch_strict_rows(P, ybuf, yref, part, mask, row_count, pbuf,
-                                              p.scores_mix, part ? row_kl : nullptr,
-                                              part ? row_kl_lowp : nullptr,
-                                              mode == LAMP_RELAXED, st),
+        LAMP_HIP_TRY(lamp::launch_rows_pv(P, ybuf, yref, part, mask, row_count, pbuf,
+                                          p.scores_mix, out, rowkl, mode == LAMP_RELAXED, st),
                      "row kernel launch");
         LAMP_HIP_TRY(tm.end(LAMP_STAGE_SELECT), "hipEventRecord");
-        LAMP_HIP_TRY(tm.begin(LAMP_STAGE_FINISH), "hipEventRecord");
-        LAMP_HIP_TRY(lamp::launch_pv(P, pbuf, out, st), "P.V launch");
-        LAMP_HIP_TRY(tm.end(LAMP_STAGE_FINISH), "hipEventRecord");
+        if (rowkl) {
+            LAMP_HIP_TRY(tm.begin(LAMP_STAGE_FINISH), "hipEventRecord");
+            LAMP_HIP_TRY(lamp::launch_row_kl(P, rowkl, part, row_kl, row_kl_lowp, st),
+                         "row KL launch");
+            LAMP_HIP_TRY(tm.end(LAMP_STAGE_FINISH), "hipEventRecord");
+        }
     } else {
         float *ymix = p.scores_mix ? p.scores_mix : (probs ? probs : at<float>(ws, L.ymix));
         float *yref = p.scores_ref ? p.scores_ref : at<float>(ws, L.yref);

@@ -457,6 +457,11 @@ __device__ __forceinline__ void buf_store_f32(__amdgpu_buffer_rsrc_t rs, uint32_
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), rs, byte_off, 0, 0);
 }
 
+// Wave ballot: bit l is set iff `c` holds on (active) lane l.  The compare's
+// own lane mask, with no round trip through a vector register (HIP's
+// __ballot goes through one: a select and a compare per call).
+__device__ __forceinline__ uint64_t ballot(bool c) { return __builtin_amdgcn_ballot_w64(c); }
+
 // Lanes below this one whose bit is set in `mask`.
 __device__ __forceinline__ uint32_t lanes_below(uint64_t mask)
 {

@@ -65,22 +65,36 @@ hipError_t launch_ps_scores(const Problem &p, const uint8_t *unsafe, float *ylo,
                             RefPartial *part, unsigned long long *exact_tiles, bool fast,
                             hipStream_t st);
 
-// Fused row pass (S <= 1024): row softmax statistics, the strict criterion
-// (relaxed = false) or the relaxed one (relaxed = true: needs part, for the
-// 64-key block maxima), mask words, compaction of the selected keys, their
-// gather FP32 recompute, the corrected softmax, probabilities into pbuf (full
-// rows, zeros past the valid keys), y^mix (optional), counts and the row KLs
-// (when part is given).  ylo may alias pbuf or ymix_out (rows are read before
-// written).  yref: the FP32 reference scores [BH, S, S] when the score tiles
-// kept them (the selected scores' FP32 values are then read from it, bit for
-// bit what the gather FP32 dot gives), or null (the dot is formed).
-hipError_t launch_strict_rows(const Problem &p, const float *ylo, const float *yref,
-                              const RefPartial *part, uint32_t *mask, uint32_t *row_count,
-                              float *pbuf, float *ymix_out, double *row_kl, double *row_kl_lowp,
-                              bool relaxed, hipStream_t st);
+// Softmax sums of one row after the fused row pass, for the row KLs: L =
+// sum exp(y^lo - m), the log-sum-exp of y^mix = mix_base + log(mix_l), and
+// dA = sum over the recomputed keys of exp(y^ref - m_ref) (y^ref - y^lo),
+// m_ref the row maximum of y^ref.
+struct RowKL {
+    double L, mix_l, dA;
+    float m, mix_base;
+};
 
-// out = P.V from given probabilities [BH, S, S] (valid keys; P.V on MFMA).
-hipError_t launch_pv(const Problem &p, const float *probs, float *out, hipStream_t st);
+// Fused row pass and P.V (S <= 1024), 16 rows per work-group: row softmax
+// statistics, the strict criterion (relaxed = false) or the relaxed one
+// (relaxed = true: needs part, for the 64-key block maxima), mask words,
+// compaction of the selected keys, their FP32 recompute, the corrected
+// softmax, probabilities into pbuf (full rows, zeros past the valid keys),
+// y^mix (optional), counts, the per-row KL record (rowkl, optional; needs
+// part), then out = P.V.  ylo may alias pbuf or ymix_out (rows are read
+// before written).  yref: the FP32 reference scores [BH, S, S] when the
+// score tiles kept them (the selected scores' FP32 values are then read from
+// it, bit for bit what the gather FP32 dot gives), or null (the dot is
+// formed).
+hipError_t launch_rows_pv(const Problem &p, const float *ylo, const float *yref,
+                          const RefPartial *part, uint32_t *mask, uint32_t *row_count,
+                          float *pbuf, float *ymix_out, float *out, RowKL *rowkl, bool relaxed,
+                          hipStream_t st);
+
+// Row KLs (row_kl: KL(P_ref || P_mix), row_kl_lowp: KL(P_ref || P_lo); either
+// may be null) from the fused row pass's per-row records and the per-tile
+// reference statistics.
+hipError_t launch_row_kl(const Problem &p, const RowKL *rowkl, const RefPartial *part,
+                         double *row_kl, double *row_kl_lowp, hipStream_t st);
 
 // Per-row statistics of the strict / random path (double sums, float maxima).
 struct RowStats {

@@ -177,7 +177,7 @@ __device__ __forceinline__ void gemm_tile(TileSmem &sm, const double *s_exp, con
             uint32_t bits[4];
 #pragma unroll
             for (int c = 0; c < 4; ++c)
-                bits[c] = (uint32_t)(__ballot(sel[c]) >> gsh) & 0xffffu;
+                bits[c] = (uint32_t)(ballot(sel[c]) >> gsh) & 0xffffu;
             // partials per 32-column block: keys tx, tx + 16 | tx + 32, tx + 48
             em0 = group16_sum(em0);
             el0 = group16_sum(el0);
@@ -407,8 +407,8 @@ __global__ __launch_bounds__(kThreads) void ps_gemm_narrow_kernel(GemmArgs a)
             // key tx + 16 c is bit tx + 16 c of word tj; lanes 16 (lane / 16)
             // .. + 15 hold row pair ty
             const int gsh = lane & 48;
-            const uint32_t b0 = (uint32_t)(__ballot(sel[0]) >> gsh) & 0xffffu;
-            const uint32_t b1 = (uint32_t)(__ballot(sel[1]) >> gsh) & 0xffffu;
+            const uint32_t b0 = (uint32_t)(ballot(sel[0]) >> gsh) & 0xffffu;
+            const uint32_t b1 = (uint32_t)(ballot(sel[1]) >> gsh) & 0xffffu;
             em = group16_sum(em);
             el = group16_sum(el);
             if (i < a.M && tx == 0) {

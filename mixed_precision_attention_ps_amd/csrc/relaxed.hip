@@ -205,7 +205,7 @@ void relaxed_kernel(RelaxedArgs a)
             uint32_t bits[4];
 #pragma unroll
             for (int c = 0; c < 4; ++c)
-                bits[c] = (uint32_t)(__ballot(sel[c]) >> gsh) & 0xffffu;
+                bits[c] = (uint32_t)(ballot(sel[c]) >> gsh) & 0xffffu;
             const uint32_t w0 = bits[0] | (bits[1] << 16), w1 = bits[2] | (bits[3] << 16);
             if (i < S) {
                 // row within the block, opaque to the compiler so that its

@@ -137,9 +137,9 @@ __global__ __launch_bounds__(kThreads) void strict_select_kernel(SelectArgs a)
     Lr = wave_sum(Lr);
     Br = wave_sum(Br);
     cnt = wave_sum_int(cnt);
-    if (__ballot(nan_lo) != 0)
+    if (ballot(nan_lo) != 0)
         A = __builtin_nan("");
-    if (__ballot(nan_ref) != 0) {
+    if (ballot(nan_ref) != 0) {
         Lr = __builtin_nan("");
         Br = __builtin_nan("");
     }
@@ -181,8 +181,8 @@ __global__ __launch_bounds__(kThreads) void strict_select_kernel(SelectArgs a)
             sel = c > a.tau;
             tie = near_tie(c, a.tau);
         }
-        ties += (uint32_t)__popcll(__ballot(tie));
-        const uint64_t b = __ballot(sel);
+        ties += (uint32_t)__popcll(ballot(tie));
+        const uint64_t b = ballot(sel);
         if (!a.count_only) {
             if (a.mask) {
                 const int w = j0 >> 5;
@@ -383,10 +383,10 @@ __global__ __launch_bounds__(kThreads) void relaxed_select_kernel(RelaxedSelectA
                 has_nan |= valid && v != v;
                 const double c = 2.0 * E * fabs((double)v);
                 const bool sel = valid && c > a.tau;
-                ties += (uint32_t)__popcll(__ballot(valid && near_tie(c, a.tau)));
+                ties += (uint32_t)__popcll(ballot(valid && near_tie(c, a.tau)));
                 l_lo = fma(E, g_lo, l_lo);
                 l_un = sel ? l_un : fma(E, g_mix, l_un);
-                const uint64_t b = __ballot(sel);
+                const uint64_t b = ballot(sel);
                 if (a.mask) {
                     const int w = (jc >> 5) + lane;
                     if (lane < 2 && w < a.W)
@@ -432,7 +432,7 @@ __global__ __launch_bounds__(kThreads) void relaxed_select_kernel(RelaxedSelectA
     l_un = wave_sum(l_un);
     l_sel = wave_sum(l_sel);
     dA = wave_sum(dA);
-    if (__ballot(has_nan) != 0) {   // a NaN score makes the row's statistics NaN
+    if (ballot(has_nan) != 0) {   // a NaN score makes the row's statistics NaN
         l_lo = __builtin_nan("");
         l_un = __builtin_nan("");
     }
@@ -629,7 +629,7 @@ __global__ __launch_bounds__(kThreads) void random_select_kernel(RandomArgs a)
             lt = whole ? h <= ub : h < T;
             eq = !whole && h == T;
         }
-        const uint64_t tb = __ballot(eq);
+        const uint64_t tb = ballot(eq);
         if (lane == 0)
             s_eqw[wave] = (uint32_t)__popcll(tb);
         __syncthreads();
@@ -637,7 +637,7 @@ __global__ __launch_bounds__(kThreads) void random_select_kernel(RandomArgs a)
         for (int w = 0; w < wave; ++w)
             eq_rank += s_eqw[w];
         const bool sel = lt || (eq && eq_rank < rank);
-        const uint64_t b = __ballot(sel);
+        const uint64_t b = ballot(sel);
         const int w32 = (j0 + wave * 64) >> 5;
         if (a.mask && lane < 2 && w32 + lane < a.W)
             a.mask[r * (uint64_t)a.W + w32 + lane] = lane ? (uint32_t)(b >> 32) : (uint32_t)b;
