@@ -441,8 +441,11 @@ def main():
     impl = lamp.last_impl()
     if impl == "relaxed_fused":
         ran = ["scan", "exact", "scores"] + (["finish"] if probs is not None else [])
-    elif impl in ("strict_rows", "relaxed_rows", "relaxed_stream"):
-        # fused row pass, or the streaming relaxed row pass of longer rows
+    elif impl in ("strict_rows", "relaxed_rows"):
+        # the fused row pass and P.V (with the row KLs)
+        ran = ["scan", "exact", "scores", "select"]
+    elif impl == "relaxed_stream":
+        # the streaming relaxed row pass of longer rows, then P.V
         ran = ["scan", "exact", "scores", "select", "finish"]
     else:
         ran = ["scan", "exact", "scores", "select", "recompute", "finish"]

@@ -174,7 +174,7 @@ struct Layout {
     size_t ymix = SIZE_MAX, yref = SIZE_MAX, list = SIZE_MAX, row_count = SIZE_MAX,
            row_kl = SIZE_MAX, row_kl_lowp = SIZE_MAX, unsafe = SIZE_MAX, dstats = SIZE_MAX,
            row_m = SIZE_MAX, row_l = SIZE_MAX, rowstats = SIZE_MAX, pbuf = SIZE_MAX,
-           part = SIZE_MAX, rowkl = SIZE_MAX;
+           part = SIZE_MAX;
     size_t total = 0;
     size_t take(size_t bytes)
     {
@@ -190,7 +190,7 @@ struct Needs {
                   // relaxed in two passes)
     bool pbuf;    // fused: probabilities need their own buffer
     bool part;    // fused: per-tile partials (KL wanted; relaxed rule)
-    bool rowkl;   // fused: per-row KL records (KL wanted)
+    bool rowkl;   // fused: the row KLs are formed (KL wanted)
     bool relaxed_long;   // relaxed in two passes over rows longer than 1024 keys
 };
 
@@ -228,8 +228,6 @@ Layout plan(const Sizes &z, int mode, const Needs &n)
             L.pbuf = L.take(4 * z.n_scores);
         if (n.part)
             L.part = L.take(sizeof(lamp::RefPartial) * z.n_rows * (uint64_t)z.tiles);
-        if (n.rowkl)
-            L.rowkl = L.take(sizeof(lamp::RowKL) * z.n_rows);
     } else {
         if (n.ymix)
             L.ymix = L.take(4 * z.n_scores);
@@ -966,18 +964,13 @@ static int run(const float *q, const float *k, const float *v, int B, int H, int
                                             &dstats->n_exact_tiles, true, st),
                      "score kernel launch");
         LAMP_HIP_TRY(tm.end(LAMP_STAGE_SCORES), "hipEventRecord");
-        auto *rowkl = at<lamp::RowKL>(ws, L.rowkl);
+        const bool kl = need.rowkl;
         LAMP_HIP_TRY(tm.begin(LAMP_STAGE_SELECT), "hipEventRecord");
         LAMP_HIP_TRY(lamp::launch_rows_pv(P, ybuf, yref, part, mask, row_count, pbuf,
-                                          p.scores_mix, out, rowkl, mode == LAMP_RELAXED, st),
+                                          p.scores_mix, out, kl ? row_kl : nullptr,
+                                          kl ? row_kl_lowp : nullptr, mode == LAMP_RELAXED, st),
                      "row kernel launch");
         LAMP_HIP_TRY(tm.end(LAMP_STAGE_SELECT), "hipEventRecord");
-        if (rowkl) {
-            LAMP_HIP_TRY(tm.begin(LAMP_STAGE_FINISH), "hipEventRecord");
-            LAMP_HIP_TRY(lamp::launch_row_kl(P, rowkl, part, row_kl, row_kl_lowp, st),
-                         "row KL launch");
-            LAMP_HIP_TRY(tm.end(LAMP_STAGE_FINISH), "hipEventRecord");
-        }
     } else {
         float *ymix = p.scores_mix ? p.scores_mix : (probs ? probs : at<float>(ws, L.ymix));
         float *yref = p.scores_ref ? p.scores_ref : at<float>(ws, L.yref);

@@ -79,7 +79,7 @@ struct RowKL {
 // (relaxed = true: needs part, for the 64-key block maxima), mask words,
 // compaction of the selected keys, their FP32 recompute, the corrected
 // softmax, probabilities into pbuf (full rows, zeros past the valid keys),
-// y^mix (optional), counts, the per-row KL record (rowkl, optional; needs
+// y^mix (optional), counts, the row KLs (row_kl / row_kl_lowp, optional; need
 // part), then out = P.V.  ylo may alias pbuf or ymix_out (rows are read
 // before written).  yref: the FP32 reference scores [BH, S, S] when the
 // score tiles kept them (the selected scores' FP32 values are then read from
@@ -87,14 +87,8 @@ struct RowKL {
 // formed).
 hipError_t launch_rows_pv(const Problem &p, const float *ylo, const float *yref,
                           const RefPartial *part, uint32_t *mask, uint32_t *row_count,
-                          float *pbuf, float *ymix_out, float *out, RowKL *rowkl, bool relaxed,
-                          hipStream_t st);
-
-// Row KLs (row_kl: KL(P_ref || P_mix), row_kl_lowp: KL(P_ref || P_lo); either
-// may be null) from the fused row pass's per-row records and the per-tile
-// reference statistics.
-hipError_t launch_row_kl(const Problem &p, const RowKL *rowkl, const RefPartial *part,
-                         double *row_kl, double *row_kl_lowp, hipStream_t st);
+                          float *pbuf, float *ymix_out, float *out, double *row_kl,
+                          double *row_kl_lowp, bool relaxed, hipStream_t st);
 
 // Per-row statistics of the strict / random path (double sums, float maxima).
 struct RowStats {

@@ -21,8 +21,8 @@
 //         recomputed over the row when the correction would cancel or
 //         overflow);
 //       - probabilities are written as full rows (zeros past the valid keys);
-//       - the row's softmax sums go to a per-row record from which
-//         row_kl_kernel forms the KLs (one lane per row);
+//       - the row's softmax sums go to LDS, from which the work-group
+//         forms the 16 rows' KLs (16 lanes per row) once phase A is done;
 //   * phase B, the whole work-group: out = P.V for its 16 rows on the FP32
 //     MFMA, the probabilities read back from the rows phase A just wrote,
 //     the keys split over the four waves.  The MFMA work of one work-group
@@ -44,7 +44,8 @@ struct RowsArgs {
     float s;
     uint32_t *mask, *row_count;
     float *pbuf, *ymix_out, *out;
-    RowKL *rowkl;
+    double *row_kl, *row_kl_lowp;   // null: not asked for
+    int kl;                         // a row KL is asked for (needs part)
     unsigned long long *n_band;
 };
 
@@ -87,7 +88,8 @@ union RowsSmem {
 // is the strict pass's.
 template <int D4, bool RELAXED, int DV, typename Args>
 __device__ __forceinline__ void row_pass(Args &a, RowsSmem<DV> &sm, const double *s_exp,
-                                         int wave, int lane_in, uint64_t r, uint32_t &ties)
+                                         int wave, int lane_in, uint64_t r, uint32_t &ties,
+                                         RowKL *rk_slot)
 {
     // the lane index through an opaque copy: everything derived from it is
     // formed inside the pass, not hoisted out of the caller's row loop and
@@ -117,7 +119,7 @@ __device__ __forceinline__ void row_pass(Args &a, RowsSmem<DV> &sm, const double
     // This lane's per-tile partial of the score kernel (tile = lane; nch =
     // the tiles that hold valid keys): the relaxed rule's block maximum of
     // y^lo, and for the KL the tile maximum of y^ref.
-    const bool kl = a.rowkl != nullptr;
+    const bool kl = a.kl != 0;
     float blk_max = -INFINITY, ref_max = -INFINITY;
     if ((RELAXED || kl) && lane < nch) {
         const RefPartial q = a.part[r * (uint64_t)a.tiles + lane];
@@ -460,7 +462,7 @@ __device__ __forceinline__ void row_pass(Args &a, RowsSmem<DV> &sm, const double
             rk.dA = dA;
             rk.m = m;
             rk.mix_base = (float)mix_base;
-            a.rowkl[r] = rk;
+            *rk_slot = rk;
         }
     }
 }
@@ -617,6 +619,39 @@ __device__ __forceinline__ void group_pv(const RowsArgs &a, RowsSmem<DV> &sm, in
     }
 }
 
+// The group's row KLs from the rows' softmax sums (phase A) and the score
+// tiles' per-tile reference statistics:
+//   KL(P_ref || P_x) = sum_j p_ref_j (y^ref_j - y^x_j) + lse(y^x) - lse(y^ref)
+// with sum_j p_ref_j (y^ref_j - y^lo_j) = B / L_ref from the partials; for
+// y^mix the selected keys' terms leave B (their y^mix is y^ref): dA / L_ref.
+// 16 lanes per row (lane = 64-key tile, rows of at most 1024 keys): a row's
+// partials are one contiguous read, reduced by DPP within the 16 lanes; wave
+// w takes rows 4w .. 4w + 3 of the group.
+__device__ __forceinline__ void group_kl(const RowsArgs &a, const RowKL *s_rk, const double *s_exp,
+                                         int bh, int i0)
+{
+    const int tid = threadIdx.x, t = tid & 15, lr = tid >> 4;
+    const int i = min(i0 + lr, a.S - 1);   // every lane takes part in the DPP sums
+    const uint64_t r = (uint64_t)bh * a.S + i;
+    const int nt = a.causal ? (i / kTile) + 1 : a.tiles;
+    RefPartial q{0.0, 0.0, -INFINITY, 0.0f};
+    if (t < nt)
+        q = a.part[r * (uint64_t)a.tiles + t];
+    const float mr = group16_max(q.m);
+    const double f = t < nt ? exp64_nonpos((double)q.m - (double)mr, s_exp) : 0.0;
+    const double Lr = group16_sum(q.L * f);
+    const double Br = group16_sum(q.B * f);
+    if (t != 0 || i0 + lr >= a.S)
+        return;
+    const RowKL k = s_rk[lr];
+    const double lse_ref = (double)mr + log(Lr);
+    const double inv_lr = 1.0 / Lr;
+    if (a.row_kl_lowp)
+        a.row_kl_lowp[r] = Br * inv_lr + ((double)k.m + log(k.L)) - lse_ref;
+    if (a.row_kl)
+        a.row_kl[r] = (Br - k.dA) * inv_lr + ((double)k.mix_base + log(k.mix_l)) - lse_ref;
+}
+
 // 16 rows per work-group, heaviest (causal) groups first so that the light
 // ones fill the tail of the launch.  Five waves per SIMD at DV = 64 (96
 // VGPRs; 29 KB of LDS per work-group); wider V tiles take more LDS.
@@ -627,6 +662,7 @@ __attribute__((amdgpu_waves_per_eu(DV == 64 ? 5 : (DV == 128 ? 3 : 2)))) void ro
     __shared__ RowsSmem<DV> sm;
     __shared__ double s_exp[64];   // 2^(k/64) for exp64
     __shared__ int s_vbad;         // a diagonal step met a non-finite V value
+    __shared__ RowKL s_rk[kGroupRows];   // the rows' softmax sums for the KLs
     exp_table_fill(s_exp);
     if (threadIdx.x == 0)
         s_vbad = 0;
@@ -651,61 +687,27 @@ __attribute__((amdgpu_waves_per_eu(DV == 64 ? 5 : (DV == 128 ? 3 : 2)))) void ro
         KArgs *ak = kargs;
         asm volatile("" : "+s"(ak));
         if (i < a.S)
-            row_pass<D4, RELAXED, DV>(*ak, sm, s_exp, wave, lane, (uint64_t)bh * a.S + i, ties);
+            row_pass<D4, RELAXED, DV>(*ak, sm, s_exp, wave, lane, (uint64_t)bh * a.S + i, ties,
+                                      &s_rk[wave + 4 * k]);
         __builtin_amdgcn_wave_barrier();
     }
     add_ties(a.n_band, ties);
     __syncthreads();   // the group's probabilities are written; LDS is free
+    if (a.kl)
+        group_kl(a, s_rk, s_exp, bh, i0);
     group_pv<DV>(a, sm, &s_vbad, bh, i0);
-}
-
-// The row KLs from the per-row record of the row pass and the score tiles'
-// per-tile reference statistics:
-//   KL(P_ref || P_x) = sum_j p_ref_j (y^ref_j - y^x_j) + lse(y^x) - lse(y^ref)
-// with sum_j p_ref_j (y^ref_j - y^lo_j) = B / L_ref from the partials; for
-// y^mix the selected keys' terms leave B (their y^mix is y^ref): dA / L_ref.
-// 16 lanes per row (lane = 64-key tile, rows of at most 1024 keys): the
-// row's partials are one contiguous read, reduced by DPP within the 16 lanes.
-__global__ __launch_bounds__(kThreads) void row_kl_kernel(const RowKL *rk, const RefPartial *part,
-                                                          int S, int tiles, int causal,
-                                                          uint64_t n_rows, double *row_kl,
-                                                          double *row_kl_lowp)
-{
-    __shared__ double s_exp[64];   // 2^(k/64) for exp64
-    exp_table_fill(s_exp);
-    __syncthreads();
-    const int t = threadIdx.x & 15;
-    const uint64_t rq = (uint64_t)blockIdx.x * (kThreads / 16) + (threadIdx.x >> 4);
-    const uint64_t r = rq < n_rows ? rq : n_rows - 1;   // every lane takes part in the DPP sums
-    const int i = (int)(r % (uint64_t)S);
-    const int nt = causal ? (i / kTile) + 1 : tiles;
-    RefPartial q{0.0, 0.0, -INFINITY, 0.0f};
-    if (t < nt)
-        q = part[r * (uint64_t)tiles + t];
-    const float mr = group16_max(q.m);
-    const double f = t < nt ? exp64_nonpos((double)q.m - (double)mr, s_exp) : 0.0;
-    const double Lr = group16_sum(q.L * f);
-    const double Br = group16_sum(q.B * f);
-    if (t != 0 || rq >= n_rows)
-        return;
-    const RowKL k = rk[r];
-    const double lse_ref = (double)mr + log(Lr);
-    const double inv_lr = 1.0 / Lr;
-    if (row_kl_lowp)
-        row_kl_lowp[r] = Br * inv_lr + ((double)k.m + log(k.L)) - lse_ref;
-    if (row_kl)
-        row_kl[r] = (Br - k.dA) * inv_lr + ((double)k.mix_base + log(k.mix_l)) - lse_ref;
 }
 
 // y^mix, when asked for, is formed in place over y^lo (ymix_out == ylo); the
 // probabilities may share y^lo's buffer only when y^mix is not asked for.
 hipError_t launch_rows_pv(const Problem &p, const float *ylo, const float *yref,
                           const RefPartial *part, uint32_t *mask, uint32_t *row_count,
-                          float *pbuf, float *ymix_out, float *out, RowKL *rowkl, bool relaxed,
-                          hipStream_t st)
+                          float *pbuf, float *ymix_out, float *out, double *row_kl,
+                          double *row_kl_lowp, bool relaxed, hipStream_t st)
 {
+    const bool kl = row_kl || row_kl_lowp;
     if (p.S > 64 * kRowChunk || (ymix_out && (ymix_out != ylo || pbuf == ylo)) ||
-        (relaxed && !part) || (rowkl && !part) || !pbuf || !out)
+        (relaxed && !part) || (kl && !part) || !pbuf || !out)
         return hipErrorInvalidValue;
     RowsArgs a;
     a.q = p.q;
@@ -728,7 +730,9 @@ hipError_t launch_rows_pv(const Problem &p, const float *ylo, const float *yref,
     a.pbuf = pbuf;
     a.ymix_out = ymix_out;
     a.out = out;
-    a.rowkl = rowkl;
+    a.row_kl = row_kl;
+    a.row_kl_lowp = row_kl_lowp;
+    a.kl = kl ? 1 : 0;
     a.n_band = p.n_band;
     const uint64_t grid = (uint64_t)p.BH * a.groups;
     if (grid > 0x7fffffffULL)
@@ -755,21 +759,6 @@ hipError_t launch_rows_pv(const Problem &p, const float *ylo, const float *yref,
     else
         LAMP_ROWS_LAUNCH(false);
 #undef LAMP_ROWS_LAUNCH
-    return hipGetLastError();
-}
-
-hipError_t launch_row_kl(const Problem &p, const RowKL *rowkl, const RefPartial *part,
-                         double *row_kl, double *row_kl_lowp, hipStream_t st)
-{
-    if (!rowkl || !part)
-        return hipErrorInvalidValue;
-    if (!row_kl && !row_kl_lowp)
-        return hipSuccess;
-    if (p.tiles > 16)
-        return hipErrorInvalidValue;
-    const uint64_t grid = (p.n_rows + kThreads / 16 - 1) / (kThreads / 16);
-    hipLaunchKernelGGL(row_kl_kernel, dim3((unsigned)grid), dim3(kThreads), 0, st, rowkl, part,
-                       p.S, p.tiles, p.causal, p.n_rows, row_kl, row_kl_lowp);
     return hipGetLastError();
 }
 
