@@ -270,8 +270,11 @@ Needs make_needs(const lamp_params &p, int mode, int S, bool probs, bool want_st
         // from it instead of forming each dot again
         need.yref = need.part && p.scores_ref == nullptr;
     } else {
+        // longer strict rows and the random control: y^ref only for the row
+        // KLs (without them the recompute forms each selected key's FP32 dot
+        // from the gathered query and key rows)
         need.ymix = p.scores_mix == nullptr && !probs;
-        need.yref = p.scores_ref == nullptr;
+        need.yref = p.scores_ref == nullptr && want_kl;
     }
     return need;
 }

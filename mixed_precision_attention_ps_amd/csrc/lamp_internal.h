@@ -106,7 +106,8 @@ struct RowStats {
 // only (random mode); otherwise also mask words (if non-null) and the per-row
 // compacted index segments in `list`.  Writes RowStats with lse_mix = lse(y^lo),
 // row_kl (if non-null) and row_kl_lowp (if non-null) = KL(P_ref || P_lowp);
-// the recompute kernel updates the rows that have selections.
+// the recompute kernel updates the rows that have selections.  yref may be
+// null when neither KL is asked for (the reference sums are then skipped).
 hipError_t launch_strict_select(const Problem &p, const float *ylo, const float *yref,
                                 uint32_t *mask, uint32_t *list, uint32_t *row_count,
                                 RowStats *rs, double *row_kl, double *row_kl_lowp,
@@ -127,8 +128,9 @@ hipError_t launch_random_select(const Problem &p, uint64_t seed, uint32_t *mask,
 
 // FP32 recompute of the listed scores, scattered into ymix, with the rows'
 // softmax and KL statistics updated for the changed scores.  yref: the
-// stored FP32 reference scores (required; a listed key's recompute is its
-// y^ref, the same sequential dot).
+// stored FP32 reference scores (a listed key's recompute is its y^ref, the
+// same sequential dot), or null when no row KL is asked for: the dot is then
+// formed from the gathered query and key rows.
 hipError_t launch_recompute(const Problem &p, const uint32_t *list, const uint32_t *row_count,
                             const float *yref, float *ymix, RowStats *rs, double *row_kl,
                             hipStream_t st);

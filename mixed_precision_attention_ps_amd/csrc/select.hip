@@ -52,9 +52,12 @@ __global__ __launch_bounds__(kThreads) void strict_select_kernel(SelectArgs a)
     const int i = (int)(r % (uint64_t)S);
     const int n = a.causal ? i + 1 : S;
     const float *y = a.y + r * (uint64_t)S;
-    const float *yr = a.yref + r * (uint64_t)S;
+    // the reference scores serve only the row KLs: without them (no KL asked
+    // for) their loads read an empty range (0) and their sums are skipped
+    const bool ref = a.yref != nullptr;
+    const float *yr = ref ? a.yref + r * (uint64_t)S : y;
     const __amdgpu_buffer_rsrc_t y_rs = row_rsrc(y, 4u * (uint32_t)n);
-    const __amdgpu_buffer_rsrc_t r_rs = row_rsrc(yr, 4u * (uint32_t)n);
+    const __amdgpu_buffer_rsrc_t r_rs = row_rsrc(yr, ref ? 4u * (uint32_t)n : 0u);
 
     float vlo[kSelChunk], vref[kSelChunk];
     double elo[kSelChunk];
@@ -65,7 +68,7 @@ __global__ __launch_bounds__(kThreads) void strict_select_kernel(SelectArgs a)
         for (int t = 0; t < kSelChunk; ++t) {
             const int j = lane + 64 * t;
             vlo[t] = j < n ? y[j] : -INFINITY;
-            vref[t] = j < n ? yr[j] : -INFINITY;
+            vref[t] = ref && j < n ? yr[j] : -INFINITY;
             m = fmaxf(m, vlo[t]);
             mr = fmaxf(mr, vref[t]);
         }
@@ -105,10 +108,12 @@ __global__ __launch_bounds__(kThreads) void strict_select_kernel(SelectArgs a)
         A += at ? 0.0 : x;
         cnt += at ? 1 : 0;
         nan_lo |= !at && dl != dl;
-        const double er = exp64_nonpos(dr, s_exp);
-        Lr += er;
-        Br += er * ((double)vr - (double)v);
-        nan_ref |= dr != dr;
+        if (ref) {   // wave-uniform
+            const double er = exp64_nonpos(dr, s_exp);
+            Lr += er;
+            Br += er * ((double)vr - (double)v);
+            nan_ref |= dr != dr;
+        }
     };
     if (ONE) {
 #pragma unroll
@@ -688,8 +693,10 @@ hipError_t launch_random_select(const Problem &p, uint64_t seed, uint32_t *mask,
 // listed key and scatters its y^ref over the baseline score.
 // ---------------------------------------------------------------------------
 struct RecomputeArgs {
-    const float *yref;   // the stored FP32 reference scores
-    int S, causal;
+    const float *yref;   // the stored FP32 reference scores, or null (gather dot)
+    const float *q, *k;  // [BH, S, D] (the gather dot)
+    float s;             // the score scale
+    int S, D, causal;
     uint64_t n_rows;
     const uint32_t *list, *row_count;
     float *ymix;
@@ -709,6 +716,39 @@ struct RecomputeArgs {
 // per pass; the per-row corrections are then summed in list order by one
 // thread per row, so the result does not depend on scheduling.
 constexpr int kRcRows = 64;
+
+// y_hi of row r, key j: the sequential FP32 dot (multiply, then add, d
+// ascending) of the query and key rows, scaled.
+__device__ __forceinline__ float gather_dot(const RecomputeArgs &a, uint64_t r, uint32_t j)
+{
+    const uint64_t bh = r / (uint64_t)a.S;
+    const float4 *q4 = reinterpret_cast<const float4 *>(a.q + r * (uint64_t)a.D);
+    const float4 *k4 = reinterpret_cast<const float4 *>(a.k + (bh * (uint64_t)a.S + j) * a.D);
+    float acc = 0.0f;
+    for (int d0 = 0; d0 < a.D / 4; d0 += 4) {
+        float4 qv[4], kv[4];   // four 16-byte loads of each row in flight
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const bool in = d0 + u < a.D / 4;
+            qv[u] = in ? q4[d0 + u] : make_float4(0.f, 0.f, 0.f, 0.f);
+            kv[u] = in ? k4[d0 + u] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (d0 + u < a.D / 4) {
+                float p0 = qv[u].x * kv[u].x;
+                acc = acc + p0;
+                float p1 = qv[u].y * kv[u].y;
+                acc = acc + p1;
+                float p2 = qv[u].z * kv[u].z;
+                acc = acc + p2;
+                float p3 = qv[u].w * kv[u].w;
+                acc = acc + p3;
+            }
+        }
+    }
+    return acc * a.s;
+}
 
 __global__ __launch_bounds__(kThreads) void recompute_kernel(RecomputeArgs a)
 {
@@ -760,15 +800,18 @@ __global__ __launch_bounds__(kThreads) void recompute_kernel(RecomputeArgs a)
             const uint64_t r = r0 + lr;
             const uint32_t j = a.list[row_segment(r, a.S, a.causal) + (e - s_off[lr])];
             if (j < (uint32_t)a.S) {
-                // the stored FP32 reference score: the sequential FP32 dot
-                // the recompute forms, the same bits
-                const float yhi = a.yref[r * (uint64_t)a.S + j];
+                // the stored FP32 reference score (the sequential FP32 dot the
+                // recompute forms, the same bits), or that dot formed here
+                // from the gathered query and key rows
+                const float yhi = a.yref ? a.yref[r * (uint64_t)a.S + j]
+                                         : gather_dot(a, r, j);
                 float *slot = a.ymix + r * (uint64_t)a.S + j;
                 const float ylo = *slot;
                 *slot = yhi;
                 const double ml = (double)s_mlo[lr], mr = (double)s_mref[lr];
                 cl = exp64((double)yhi - ml, s_exp) - exp64((double)ylo - ml, s_exp);
-                ca = exp64((double)yhi - mr, s_exp) * ((double)yhi - (double)ylo);
+                if (a.row_kl)
+                    ca = exp64((double)yhi - mr, s_exp) * ((double)yhi - (double)ylo);
             }
         }
         s_dl[tid] = cl;
@@ -805,11 +848,15 @@ hipError_t launch_recompute(const Problem &p, const uint32_t *list, const uint32
                             const float *yref, float *ymix, RowStats *rs, double *row_kl,
                             hipStream_t st)
 {
-    if (!yref)
+    if (!yref && row_kl)   // the KL's reference statistics come with y^ref
         return hipErrorInvalidValue;
     RecomputeArgs a;
     a.yref = yref;
+    a.q = p.q;
+    a.k = p.k;
+    a.s = p.pc.s;
     a.S = p.S;
+    a.D = p.D;
     a.causal = p.causal;
     a.n_rows = p.n_rows;
     a.list = list;

@@ -103,6 +103,18 @@ def test_workspace_bytes(lib):
     assert relaxed >= 8 * 4 * 25 * 4096 * 4096
 
 
+
+@pytest.mark.parametrize("mode", [0, 2])
+def test_long_rows_without_kl_keep_no_reference_scores(lib, mode):
+    """Strict rows and the random control past 1024 keys without a row KL:
+    the recompute forms each selected score's FP32 dot from the gathered
+    query and key rows, so the workspace holds no dense y^ref (one float per
+    score less than with the KL)."""
+    B, H, S, D = 1, 32, 4096, 64
+    with_kl = lib.lamp_workspace_bytes_ex(B, H, S, D, 1, mode, 1, 1, None)
+    without = lib.lamp_workspace_bytes_ex(B, H, S, D, 1, mode, 1, 0, None)
+    assert 0 < without <= with_kl - 4 * B * H * S * S
+
 def dcall(lib, q=A, k=A, v=A, B=1, H=1, Nq=1, S=8, D=64, causal=1, mu=4, tau=0.1, out=A):
     return lib.lamp_decode_fwd(q, k, v, B, H, Nq, S, D, causal, mu, ctypes.c_float(tau), out,
                                None, None, None, None)
