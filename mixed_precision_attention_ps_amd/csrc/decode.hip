@@ -192,14 +192,14 @@ __global__ __launch_bounds__(kThreads) void decode_scores_kernel(DecodeArgs a)
                     const float sa[4] = {sv.x, sv.y, sv.z, sv.w};
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        ps_mac_fast(qa[e], sa[e], ka[e], BLOCKED ? run[t] : lo[t], ref[t], pc.sh,
-                                    pc.half_m1, pc.keep);
+                        ps_mac_fast(qa[e], sa[e], ka[e], BLOCKED ? run[t] : lo[t], ref[t],
+                                    pc.split);
                 }
             }
             if (BLOCKED && ((d0 + dd + 4) & (pc.blk - 1)) == 0) {   // a run ends here
 #pragma unroll
                 for (int t = 0; t < NQ; ++t) {
-                    lo[t] = ps_round_bits(lo[t] + run[t], pc.sh, pc.half_m1, pc.keep);
+                    lo[t] = ps_round_split(lo[t] + run[t], pc.split);
                     run[t] = 0.0f;
                 }
             }
@@ -208,7 +208,7 @@ __global__ __launch_bounds__(kThreads) void decode_scores_kernel(DecodeArgs a)
     if (BLOCKED)   // the last run
 #pragma unroll
         for (int t = 0; t < NQ; ++t)
-            lo[t] = ps_round_bits(lo[t] + run[t], pc.sh, pc.half_m1, pc.keep);
+            lo[t] = ps_round_split(lo[t] + run[t], pc.split);
     const bool ok = __syncthreads_and(safe ? 1 : 0);
     if (tid == 0)
         a.unsafe[(size_t)bh * a.n_chunks + chunk] = ok ? 0 : 1;

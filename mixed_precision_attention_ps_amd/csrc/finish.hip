@@ -319,54 +319,107 @@ hipError_t launch_finish(const Problem &p, const float *ymix, const RowStats *rs
 
 
 // ---------------------------------------------------------------------------
-// Row reductions into the device summary (one work-group, fixed order).
+// Row reductions into the device summary, in a fixed order: work-group b
+// reduces rows [b c, (b + 1) c) (c = ceil(n_rows / work-groups)) into its
+// partial; the last work-group to finish (a completion count in the zeroed
+// summary) combines the partials in work-group order.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void stats_kernel(const double *row_kl, const double *row_kl_lowp,
-                                                     const uint32_t *row_count, uint64_t n_rows,
-                                                     DevStats *ds)
+constexpr int kStatsThreads = 512;
+
+struct StatsAcc {
+    double sum, max, low;
+    unsigned long long cnt;
+};
+
+__device__ __forceinline__ void stats_combine(StatsAcc &a, const StatsAcc &b)
 {
-    __shared__ double s_sum[1024], s_max[1024], s_low[1024];
-    __shared__ unsigned long long s_cnt[1024];
+    a.sum += b.sum;
+    a.max = fmax(a.max, b.max);
+    a.low += b.low;
+    a.cnt += b.cnt;
+}
+
+// Tree over the work-group's threads (fixed order); thread 0 gets the total.
+__device__ StatsAcc stats_block_reduce(StatsAcc v, StatsAcc *sh)
+{
     const int tid = threadIdx.x;
-    double sum = 0.0, mx = -INFINITY, low = 0.0;
-    unsigned long long cnt = 0;
-    for (uint64_t r = tid; r < n_rows; r += 1024) {
-        if (row_kl) {
-            sum += row_kl[r];
-            mx = fmax(mx, row_kl[r]);
-        }
-        if (row_kl_lowp)
-            low += row_kl_lowp[r];
-        if (row_count)
-            cnt += row_count[r];
-    }
-    s_sum[tid] = sum;
-    s_max[tid] = mx;
-    s_low[tid] = low;
-    s_cnt[tid] = cnt;
+    sh[tid] = v;
     __syncthreads();
-    for (int o = 512; o > 0; o >>= 1) {
+    for (int o = kStatsThreads / 2; o > 0; o >>= 1) {
         if (tid < o) {
-            s_sum[tid] += s_sum[tid + o];
-            s_max[tid] = fmax(s_max[tid], s_max[tid + o]);
-            s_low[tid] += s_low[tid + o];
-            s_cnt[tid] += s_cnt[tid + o];
+            StatsAcc a = sh[tid];
+            stats_combine(a, sh[tid + o]);
+            sh[tid] = a;
         }
         __syncthreads();
     }
+    return sh[0];
+}
+
+__global__ __launch_bounds__(kStatsThreads) void stats_kernel(const double *row_kl,
+                                                              const double *row_kl_lowp,
+                                                              const uint32_t *row_count,
+                                                              uint64_t n_rows, DevStats *ds)
+{
+    __shared__ StatsAcc sh[kStatsThreads];
+    __shared__ int s_last;
+    const int tid = threadIdx.x;
+    const uint64_t per = (n_rows + gridDim.x - 1) / gridDim.x;
+    const uint64_t r0 = per * blockIdx.x;
+    const uint64_t r1 = min(n_rows, r0 + per);
+    StatsAcc v{0.0, -INFINITY, 0.0, 0ull};
+    for (uint64_t r = r0 + tid; r < r1; r += kStatsThreads) {
+        if (row_kl) {
+            const double x = row_kl[r];
+            v.sum += x;
+            v.max = fmax(v.max, x);
+        }
+        if (row_kl_lowp)
+            v.low += row_kl_lowp[r];
+        if (row_count)
+            v.cnt += row_count[r];
+    }
+    const StatsAcc b = stats_block_reduce(v, sh);
     if (tid == 0) {
-        ds->kl_sum = s_sum[0];
-        ds->kl_max = row_kl ? s_max[0] : 0.0;
-        ds->kl_lowp_sum = s_low[0];
-        ds->n_selected = s_cnt[0];
+        StatsPart &pt = ds->part[blockIdx.x];
+        pt.sum = b.sum;
+        pt.max = b.max;
+        pt.low = b.low;
+        pt.cnt = b.cnt;
+        __threadfence();   // the partial is visible before the count says so
+        s_last = atomicAdd(&ds->blocks_done, 1u) == gridDim.x - 1;
+    }
+    __syncthreads();
+    if (!s_last)
+        return;
+    __threadfence();
+    // the other work-groups' partials, read past this CU's cache
+    StatsAcc t{0.0, -INFINITY, 0.0, 0ull};
+    if (tid < (int)gridDim.x) {
+        const volatile StatsPart &pt = ds->part[tid];
+        t.sum = pt.sum;
+        t.max = pt.max;
+        t.low = pt.low;
+        t.cnt = pt.cnt;
+    }
+    const StatsAcc total = stats_block_reduce(t, sh);
+    if (tid == 0) {
+        ds->kl_sum = total.sum;
+        ds->kl_max = row_kl ? total.max : 0.0;
+        ds->kl_lowp_sum = total.low;
+        ds->n_selected = total.cnt;
     }
 }
 
 hipError_t launch_stats(const Problem &p, const double *row_kl, const double *row_kl_lowp,
                         const uint32_t *row_count, DevStats *ds, hipStream_t st)
 {
-    hipLaunchKernelGGL(stats_kernel, dim3(1), dim3(1024), 0, st, row_kl, row_kl_lowp, row_count,
-                       p.n_rows, ds);
+    static_assert(kStatsBlocks <= kStatsThreads, "one partial per thread in the last step");
+    // about 1024 rows per work-group at least
+    const uint64_t want = (p.n_rows + 1023) / 1024;
+    const unsigned grid = (unsigned)(want < 1 ? 1 : (want < kStatsBlocks ? want : kStatsBlocks));
+    hipLaunchKernelGGL(stats_kernel, dim3(grid), dim3(kStatsThreads), 0, st, row_kl, row_kl_lowp,
+                       row_count, p.n_rows, ds);
     return hipGetLastError();
 }
 

@@ -16,6 +16,7 @@
 #include <hip/hip_runtime.h>
 
 #include <math.h>
+#include <stddef.h>
 #include <stdio.h>
 #include <stdlib.h>
 
@@ -265,10 +266,10 @@ Needs make_needs(const lamp_params &p, int mode, int S, bool probs, bool want_st
         need.pbuf = p.scores_mix != nullptr && !probs;
         need.part = want_kl || relaxed_rows;
         need.rowkl = want_kl;
-        // the score tiles form y^ref for every pair when they form the
-        // partials: kept, the row pass takes the selected scores' FP32 values
-        // from it instead of forming each dot again
-        need.yref = need.part && p.scores_ref == nullptr;
+        // no dense y^ref: the score tiles fold every pair's FP32 score into
+        // the partials, and the row pass forms the few selected keys' FP32
+        // scores again by a gather dot (cheaper than storing them all)
+        need.yref = false;
     } else {
         // longer strict rows and the random control: y^ref only for the row
         // KLs (without them the recompute forms each selected key's FP32 dot
@@ -382,6 +383,9 @@ int check_block_k(int b)
     return LAMP_OK;
 }
 
+// the summary fields of DevStats (the work-group partials stay on the device)
+constexpr size_t kStatsHead = offsetof(lamp::DevStats, blocks_done);
+
 void fill_stats(lamp_stats *stats, uint64_t n_rows, uint64_t n_valid, const lamp::DevStats &ds,
                 int impl)
 {
@@ -478,7 +482,7 @@ int run_decode(const float *q, const float *k, const float *v, int B, int H, int
                      "stats launch");
         LAMP_HIP_TRY(tm.end(LAMP_STAGE_STATS), "hipEventRecord");
         lamp::DevStats ds;
-        LAMP_HIP_TRY(hipMemcpyAsync(&ds, dstats, sizeof(ds), hipMemcpyDeviceToHost, st),
+        LAMP_HIP_TRY(hipMemcpyAsync(&ds, dstats, kStatsHead, hipMemcpyDeviceToHost, st),
                      "hipMemcpyAsync stats");
         LAMP_HIP_TRY(hipStreamSynchronize(st), "hipStreamSynchronize");
         const uint64_t per_head = causal ? (uint64_t)Nq * (uint64_t)(S - Nq) +
@@ -645,7 +649,7 @@ int run_mlp(int op, const float *x, const float *w, const float *gamma, const fl
         Ps.n_rows = (uint64_t)M;
         LAMP_HIP_TRY(lamp::launch_stats(Ps, b.err, b.errl, count, dstats, st), "stats launch");
         lamp::DevStats ds;
-        LAMP_HIP_TRY(hipMemcpyAsync(&ds, dstats, sizeof(ds), hipMemcpyDeviceToHost, st),
+        LAMP_HIP_TRY(hipMemcpyAsync(&ds, dstats, kStatsHead, hipMemcpyDeviceToHost, st),
                      "hipMemcpyAsync stats");
         LAMP_HIP_TRY(hipStreamSynchronize(st), "hipStreamSynchronize");
         fill_stats(stats, (uint64_t)M, (uint64_t)M * (uint64_t)N, ds, impl);
@@ -1017,7 +1021,7 @@ static int run(const float *q, const float *k, const float *v, int B, int H, int
                      "stats launch");
         LAMP_HIP_TRY(tm.end(LAMP_STAGE_STATS), "hipEventRecord");
         lamp::DevStats ds;
-        LAMP_HIP_TRY(hipMemcpyAsync(&ds, dstats, sizeof(ds), hipMemcpyDeviceToHost, st),
+        LAMP_HIP_TRY(hipMemcpyAsync(&ds, dstats, kStatsHead, hipMemcpyDeviceToHost, st),
                      "hipMemcpyAsync stats");
         LAMP_HIP_TRY(hipStreamSynchronize(st), "hipStreamSynchronize");
         fill_stats(stats, z.n_rows, z.n_valid, ds, impl);

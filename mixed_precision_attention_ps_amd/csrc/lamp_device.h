@@ -24,9 +24,16 @@ namespace lamp {
 //    magnitude stays in C's binade -- and rounds once at C's ulp, which is
 //    the PS(mu) ulp of the scaled product; C is 2^23 ulps (even), so ties go
 //    to even.  r = fma(...) - C is exact (Sterbenz).  Cost: mul, and, fma, sub.
-//  * sum: s = fl(acc + r) of two PS(mu) values, then RNE of s's bits to mu
-//    fraction bits; double rounding through FP32 is innocuous for
-//    24 >= 2(mu+1)+1, i.e. mu <= 10.  Cost: add, bfe, add3, and.
+//  * sum: s = fl(acc + r) of two PS(mu) values, then RNE of s to mu fraction
+//    bits; double rounding through FP32 is innocuous for 24 >= 2(mu+1)+2,
+//    i.e. mu <= 10.  The RNE is Veltkamp's splitting with the constant
+//    2^(23-mu) + 1: g = fl(C s), hi = fl(g + fl(s - g)) (three FP32 ops with
+//    the short encoding, which issue at twice the rate of the three-operand
+//    integer ones of the bit-level form); for every normal s below 2^100 and
+//    mu = 1..10 it gives the bits of the bit-level RNE (checked exhaustively
+//    over all FP32 inputs by a CPU test).  The fast path's sums are normal
+//    (nonzero magnitudes >= 2^-103 in the scaled domain), below 2^75 and
+//    never -0.  Cost: add, mul, sub, add.
 //  The accumulator lives in the scaled domain (x 2^(mu-23)); rounding to a
 //  number of significant bits commutes with power-of-two scaling while
 //  values stay normal, which the operand range guarantees.
@@ -34,26 +41,25 @@ namespace lamp {
 // with FP32 range; double add then RN_mu (53 >= 2*24+2).
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ float ps_round_bits(float x, uint32_t sh, uint32_t half_m1,
-                                               uint32_t keep)
+// RNE of a fast-path sum to mu fraction bits (split = 2^(23-mu) + 1).
+__device__ __forceinline__ float ps_round_split(float x, float split)
 {
-    uint32_t u = __float_as_uint(x);
-    u = (u + ((u >> sh) & 1u) + half_m1) & keep;
-    return __uint_as_float(u);
+    const float g = split * x;
+    const float d = x - g;
+    return g + d;
 }
 
 // One fast-path multiply-accumulate of PS(mu) (scaled domain) and of the
 // sequential FP32 reference, sharing the FP32 product.
 __device__ __forceinline__ void ps_mac_fast(float q, float qs, float k, float &acc_s,
-                                            float &acc_r, uint32_t sh, uint32_t half_m1,
-                                            uint32_t keep)
+                                            float &acc_r, float split)
 {
     float p = q * k;
     float C = __uint_as_float(__float_as_uint(p) & 0xff800000u);
     float t = __builtin_fmaf(qs, k, C);
     float r = t - C;
     float s = acc_s + r;
-    acc_s = ps_round_bits(s, sh, half_m1, keep);
+    acc_s = ps_round_split(s, split);
     acc_r = acc_r + p;
 }
 
@@ -143,8 +149,7 @@ __device__ __forceinline__ void flush_runs(TileAcc &acc, const PsConst &pc)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             if (PATH == PATH_FAST) {
-                acc.lo[r][c] = ps_round_bits(acc.lo[r][c] + acc.blk[r][c], pc.sh, pc.half_m1,
-                                             pc.keep);
+                acc.lo[r][c] = ps_round_split(acc.lo[r][c] + acc.blk[r][c], pc.split);
                 acc.blk[r][c] = 0.0f;
             } else if (PATH == PATH_EXACT) {
                 acc.lod[r][c] = ps_rn64(acc.lod[r][c] + acc.blkd[r][c], pc.mu);
@@ -184,7 +189,7 @@ __device__ __forceinline__ void compute_slice(const TileSmem &sm, TileAcc &acc, 
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
                     ps_mac_fast(qa[r], sa[r], ka[c], BLOCKED ? acc.blk[r][c] : acc.lo[r][c],
-                                acc.ref[r][c], pc.sh, pc.half_m1, pc.keep);
+                                acc.ref[r][c], pc.split);
         } else if (PATH == PATH_EXACT) {
 #pragma unroll
             for (int r = 0; r < 4; ++r)
@@ -450,6 +455,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void *base, uin
 __device__ __forceinline__ float buf_load_f32(__amdgpu_buffer_rsrc_t rs, uint32_t byte_off)
 {
     return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, byte_off, 0, 0));
+}
+
+// 16 bytes at byte_off (a multiple of 16 here); out of range: zeros
+__device__ __forceinline__ float4 buf_load_f32x4(__amdgpu_buffer_rsrc_t rs, uint32_t byte_off)
+{
+    const auto u = __builtin_amdgcn_raw_buffer_load_b128(rs, byte_off, 0, 0);
+    return make_float4(__uint_as_float(u[0]), __uint_as_float(u[1]), __uint_as_float(u[2]),
+                       __uint_as_float(u[3]));
 }
 
 __device__ __forceinline__ void buf_store_f32(__amdgpu_buffer_rsrc_t rs, uint32_t byte_off, float x)

@@ -15,8 +15,7 @@ constexpr int kThreads = 256;    // threads per work-group (4 wave64)
 struct PsConst {
     int mu;
     uint32_t sh;        // 23 - mu: fraction bits dropped
-    uint32_t half_m1;   // 2^(sh-1) - 1
-    uint32_t keep;      // mask clearing the dropped bits
+    float split;        // 2^sh + 1: Veltkamp splitting constant (rounding of a sum)
     float qscale;       // 2^(mu-23): scaled operand of the product fma
     float out_scale;    // s * 2^(23-mu): scale of the scaled-domain accumulator
     float s;            // FP32 value nearest to 1/sqrt(D)
@@ -231,11 +230,23 @@ hipError_t launch_mlp(const MlpProblem &p, const MlpBuffers &b, hipStream_t st,
 hipError_t launch_mask_count(const uint32_t *mask, int M, int N, uint32_t *count, hipStream_t st);
 
 // Device-side summary.
+// stats_kernel's work-groups: each reduces a fixed slice of the rows
+constexpr int kStatsBlocks = 128;
+
+struct StatsPart {
+    double sum, max, low;
+    unsigned long long cnt;
+};
+
 struct DevStats {
     unsigned long long n_selected;
     unsigned long long n_exact_tiles;
     double kl_sum, kl_max, kl_lowp_sum;
     unsigned long long n_tie_band;   // criterion values within 2^-16 tau of tau
+    // stats_kernel's per-work-group partials and the count of work-groups
+    // that have written theirs (zeroed with the rest of the summary)
+    unsigned int blocks_done, pad;
+    StatsPart part[kStatsBlocks];
 };
 
 hipError_t launch_stats(const Problem &p, const double *row_kl, const double *row_kl_lowp,

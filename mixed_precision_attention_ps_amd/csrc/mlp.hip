@@ -285,7 +285,7 @@ __device__ __forceinline__ void narrow_flush(float (&lo)[2][2], float (&blk)[2][
     for (int r = 0; r < 2; ++r)
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-            lo[r][c] = ps_round_bits(lo[r][c] + blk[r][c], pc.sh, pc.half_m1, pc.keep);
+            lo[r][c] = ps_round_split(lo[r][c] + blk[r][c], pc.split);
             blk[r][c] = 0.0f;
         }
 }
@@ -349,7 +349,7 @@ __global__ __launch_bounds__(kThreads) void ps_gemm_narrow_kernel(GemmArgs a)
 #pragma unroll
                     for (int c = 0; c < 2; ++c)
                         ps_mac_fast(qa[r], sa[r], ka[c], BLOCKED ? blk[r][c] : lo[r][c],
-                                    ref[r][c], pc.sh, pc.half_m1, pc.keep);
+                                    ref[r][c], pc.split);
                 if (BLOCKED && P < kDChunk && dd % (P ? P : 1) == (P ? P : 1) - 1)
                     narrow_flush<P>(lo, blk, pc);
             }

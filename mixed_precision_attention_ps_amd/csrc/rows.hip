@@ -25,8 +25,8 @@
 //         forms the 16 rows' KLs (16 lanes per row) once phase A is done;
 //   * phase B, the whole work-group: out = P.V for its 16 rows on the FP32
 //     MFMA, the probabilities read back from the rows phase A just wrote,
-//     the keys split over the four waves.  The MFMA work of one work-group
-//     overlaps the VALU-bound phase A of the others on the CU.
+//     the keys split over the four waves.  The MFMA work of one
+//     work-group overlaps the VALU-bound phase A of the others on the CU.
 #include "lamp_device.h"
 
 namespace lamp {
@@ -468,17 +468,23 @@ __device__ __forceinline__ void row_pass(Args &a, RowsSmem<DV> &sm, const double
 }
 
 // Phase B: out rows i0 .. i0 + 15 of head bh = P.V over the keys they see,
-// on the FP32 MFMA (v_mfma_f32_16x16x4f32), split over the keys: wave w takes
-// the 16-key steps w, w + 4, ..., with no barrier in the loop, and the four
-// partial tiles are summed through LDS at the end.
+// on the FP32 MFMA (v_mfma_f32_16x16x4f32), split over the keys: wave w
+// takes the 16-key steps w, w + 4, ..., with no barrier in the loop, and the
+// four partial tiles are summed through LDS at the end.
 //
 // Operands straight from memory, in the MFMA's lane layout: lane (g = l / 16,
 // c = l % 16) loads the probabilities of row i0 + c at keys k0 + 4g .. + 3
 // (one float4: MFMA m of the step takes component m, i.e. key k0 + 4g + m)
 // and the V rows k0 + 4g + m at columns CPL c .. CPL c + CPL - 1 (float4
 // loads); MFMA column block cb multiplies by column CPL c + cb, so its output
-// lane (g, c) holds out[i0 + 4g + q][CPL c + cb].  The probabilities are read
-// back from the rows phase A just wrote (L2).
+// lane (g, c) holds out[i0 + 4g + q][CPL c + cb].  The loads are
+// range-checked buffer loads, with no branch or exec mask: the probabilities
+// over the group's rows (rows past S read 0, keys past S are set to 0), V
+// over the head (keys past S read 0; a column past D only feeds an output
+// column that is not stored).  The probabilities are read back from the rows
+// phase A just wrote (L2).  (A second step's loads kept in flight would need
+// 20 more registers than the 96 of five waves per SIMD; the other waves on
+// the SIMD hide the loads' latency instead.)
 //
 // The FP32 partial of every 16 keys (4 MFMAs) is flushed into a double
 // accumulator: one partial carries at most 4 FP32 roundings (2.4e-7 of its
@@ -490,50 +496,22 @@ __device__ __forceinline__ void row_pass(Args &a, RowsSmem<DV> &sm, const double
 // (0 * inf) in the product: such values are taken as 0 and added back at the
 // end for the rows that see their key.
 template <int DV>
-__device__ __forceinline__ void group_pv(const RowsArgs &a, RowsSmem<DV> &sm, int *s_vbad,
-                                         int bh, int i0)
+__device__ __forceinline__ void group_pv(const RowsArgs &a, RowsSmem<DV> &sm, int bh, int i0)
 {
     constexpr int CPL = DV / 16;   // V columns per lane = MFMA column blocks
     constexpr int F4 = CPL / 4;    // float4 per lane per key row
     const int S = a.S, D = a.D;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, c = lane & 15;
     const int nk = a.causal ? min(S, i0 + kGroupRows) : S;   // keys the group sees
     const int nsteps = (nk + 15) / 16;
-    const float *Vh = a.v + (size_t)bh * S * D;
+    const int nrows = min(kGroupRows, S - i0);
+    const __amdgpu_buffer_rsrc_t p_rs =
+        row_rsrc(a.pbuf + ((uint64_t)bh * S + i0) * (uint64_t)S, 4u * (uint32_t)(nrows * S));
+    const __amdgpu_buffer_rsrc_t v_rs = row_rsrc(a.v + (size_t)bh * S * D, 4u * (uint32_t)(S * D));
     const bool vec = (S & 3) == 0;
-    const bool p_on = i0 + c < S;
-    const float *pr = a.pbuf + ((uint64_t)bh * S + (p_on ? i0 + c : 0)) * (uint64_t)S;
-
-    struct Step {
-        float4 p;
-        float4 v[4][F4];
-    };
-    auto load = [&](int k0, Step &st) {
-        const int j = k0 + 4 * g;
-        st.p = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (p_on) {
-            if (vec) {
-                if (j < S)   // S % 4 == 0: a float4 never crosses S
-                    st.p = *reinterpret_cast<const float4 *>(pr + j);
-            } else {
-                st.p.x = j < S ? pr[j] : 0.f;
-                st.p.y = j + 1 < S ? pr[j + 1] : 0.f;
-                st.p.z = j + 2 < S ? pr[j + 2] : 0.f;
-                st.p.w = j + 3 < S ? pr[j + 3] : 0.f;
-            }
-        }
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-            for (int f = 0; f < F4; ++f) {
-                const int col = CPL * c + 4 * f;
-                float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (j + m < S && col < D)   // D % 4 == 0
-                    x = *reinterpret_cast<const float4 *>(Vh + (size_t)(j + m) * D + col);
-                st.v[m][f] = x;
-            }
-    };
+    const uint32_t p_off = 4u * (uint32_t)(c * S);
     auto comp = [](const float4 &x, int e) {
         return e == 0 ? x.x : e == 1 ? x.y : e == 2 ? x.z : x.w;
     };
@@ -544,21 +522,38 @@ __device__ __forceinline__ void group_pv(const RowsArgs &a, RowsSmem<DV> &sm, in
 #pragma unroll
         for (int q = 0; q < 4; ++q)
             acc[cb][q] = 0.0;
-    // (a second step's loads kept in flight would need 20 more registers
-    // than the 96 of five waves per SIMD; the other waves on the SIMD hide
-    // the loads' latency instead)
-    Step cur;
+    bool vbad = false;
     for (int s = wave; s < nsteps; s += 4) {
         const int k0 = 16 * s;
-        load(k0, cur);
+        const int j = k0 + 4 * g;
+        float4 p;
+        if (vec) {   // S % 4 == 0: a float4 lies wholly inside or past the row
+            p = buf_load_f32x4(p_rs, p_off + 4u * (uint32_t)j);
+        } else {
+            p.x = buf_load_f32(p_rs, p_off + 4u * (uint32_t)j);
+            p.y = buf_load_f32(p_rs, p_off + 4u * (uint32_t)(j + 1));
+            p.z = buf_load_f32(p_rs, p_off + 4u * (uint32_t)(j + 2));
+            p.w = buf_load_f32(p_rs, p_off + 4u * (uint32_t)(j + 3));
+        }
+        float4 v[4][F4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int f = 0; f < F4; ++f)
+                v[m][f] = buf_load_f32x4(v_rs, 4u * (uint32_t)((j + m) * D + CPL * c + 4 * f));
+        // keys past S read the next row's probabilities: taken as 0
+        p.x = j < S ? p.x : 0.f;
+        p.y = j + 1 < S ? p.y : 0.f;
+        p.z = j + 2 < S ? p.z : 0.f;
+        p.w = j + 3 < S ? p.w : 0.f;
         if (a.causal && k0 + 16 > i0) {
 #pragma unroll
             for (int m = 0; m < 4; ++m)
 #pragma unroll
                 for (int f = 0; f < F4; ++f)
-                    if (k0 + 4 * g + m >= i0 && !finite4(cur.v[m][f])) {
-                        cur.v[m][f] = finite_or_zero(cur.v[m][f]);
-                        *s_vbad = 1;
+                    if (j + m >= i0 && CPL * c + 4 * f < D && !finite4(v[m][f])) {
+                        v[m][f] = finite_or_zero(v[m][f]);
+                        vbad = true;
                     }
         }
         floatx4 part[CPL];
@@ -567,11 +562,11 @@ __device__ __forceinline__ void group_pv(const RowsArgs &a, RowsSmem<DV> &sm, in
             part[cb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            const float av = comp(cur.p, m);
+            const float av = comp(p, m);
 #pragma unroll
             for (int cb = 0; cb < CPL; ++cb)
-                part[cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                    av, comp(cur.v[m][cb / 4], cb % 4), part[cb], 0, 0, 0);
+                part[cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, comp(v[m][cb / 4], cb % 4),
+                                                                 part[cb], 0, 0, 0);
         }
 #pragma unroll
         for (int cb = 0; cb < CPL; ++cb)
@@ -582,7 +577,10 @@ __device__ __forceinline__ void group_pv(const RowsArgs &a, RowsSmem<DV> &sm, in
 
     // Sum of the four waves' tiles: lane (g, c) of wave w puts its rows
     // 4g + q, columns CPL c + cb into red[w]; then thread t sums the four for
-    // row t / 16, columns CPL (t % 16) ...
+    // row t / 16, columns CPL (t % 16) ...  (The or-reduction is not a fence
+    // for this wave's LDS writes: it comes first, and a plain barrier orders
+    // the tile writes before their reads.)
+    const bool any_bad = __syncthreads_or(vbad ? 1 : 0) != 0;
     float(*red)[kGroupRows][DV + 4] = sm.r.red;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
@@ -593,6 +591,7 @@ __device__ __forceinline__ void group_pv(const RowsArgs &a, RowsSmem<DV> &sm, in
     const int orow = tid >> 4, oc = (tid & 15) * CPL;
     const int i = i0 + orow;
     if (i < S) {
+        const float *Vh = a.v + (size_t)bh * S * D;
         float o[CPL];
 #pragma unroll
         for (int e = 0; e < CPL; ++e) {
@@ -602,7 +601,7 @@ __device__ __forceinline__ void group_pv(const RowsArgs &a, RowsSmem<DV> &sm, in
             // non-finite V values taken as 0 on the diagonal steps: each one
             // at a key the row sees adds its infinity or NaN (what any positive
             // probability times it gives)
-            if (*s_vbad && col < D)
+            if (any_bad && col < D)
                 for (int j = i0; j <= i; ++j) {
                     const float v = Vh[(size_t)j * D + col];
                     if (!isfinite(v))
@@ -661,11 +660,8 @@ __attribute__((amdgpu_waves_per_eu(DV == 64 ? 5 : (DV == 128 ? 3 : 2)))) void ro
 {
     __shared__ RowsSmem<DV> sm;
     __shared__ double s_exp[64];   // 2^(k/64) for exp64
-    __shared__ int s_vbad;         // a diagonal step met a non-finite V value
     __shared__ RowKL s_rk[kGroupRows];   // the rows' softmax sums for the KLs
     exp_table_fill(s_exp);
-    if (threadIdx.x == 0)
-        s_vbad = 0;
     __syncthreads();
     // the wave index is uniform: readfirstlane tells the compiler so, which
     // makes the row, its length and every chunk guard scalar
@@ -695,7 +691,7 @@ __attribute__((amdgpu_waves_per_eu(DV == 64 ? 5 : (DV == 128 ? 3 : 2)))) void ro
     __syncthreads();   // the group's probabilities are written; LDS is free
     if (a.kl)
         group_kl(a, s_rk, s_exp, bh, i0);
-    group_pv<DV>(a, sm, &s_vbad, bh, i0);
+    group_pv<DV>(a, sm, bh, i0);
 }
 
 // y^mix, when asked for, is formed in place over y^lo (ymix_out == ylo); the

@@ -12,8 +12,7 @@ PsConst make_ps_const(int mu, int D)
     PsConst c;
     c.mu = mu;
     c.sh = (uint32_t)(23 - mu);
-    c.half_m1 = c.sh ? (1u << (c.sh - 1)) - 1u : 0u;
-    c.keep = ~((1u << c.sh) - 1u);
+    c.split = (float)((1u << c.sh) + 1u);
     c.qscale = ldexpf(1.0f, mu - 23);
     c.s = (float)(1.0 / sqrt((double)D));
     c.out_scale = ldexpf(c.s, 23 - mu);
@@ -26,16 +25,18 @@ void set_ps_block(PsConst &c, int block, int len)
     c.blk = (block <= 1 || block >= len) ? 0 : block;
 }
 
-// Safe operand: zero, or a finite magnitude in [2^-40, 2^40].
-__device__ __forceinline__ bool operand_safe(float x)
+// Unsafe operand (1): not zero and not a finite magnitude in [2^-40, 2^40].
+__device__ __forceinline__ uint32_t operand_unsafe(float x)
 {
-    uint32_t a = __float_as_uint(x) & 0x7fffffffu;
+    const uint32_t a = __float_as_uint(x) & 0x7fffffffu;
     const uint32_t lo = 0x2b800000u;   // 2^-40
     const uint32_t hi = 0x53800000u;   // 2^40
-    return a == 0u || (a - lo) <= (hi - lo);
+    return (uint32_t)(a != 0u) & (uint32_t)((a - lo) > (hi - lo));
 }
 
-// One work-group per 64-row block of Q or K: flag = block holds an unsafe value.
+// One work-group per 64-row block of Q or K: flag = block holds an unsafe
+// value.  The flags are or-ed without a branch, so a thread's loads are all in
+// flight at once.
 __global__ __launch_bounds__(kThreads) void operand_scan_kernel(const float *__restrict__ q,
                                                                 const float *__restrict__ k,
                                                                 int BH, int S, int D, int tiles,
@@ -45,17 +46,20 @@ __global__ __launch_bounds__(kThreads) void operand_scan_kernel(const float *__r
     const int which = blk / (BH * tiles);
     const int rem = blk % (BH * tiles);
     const int bh = rem / tiles, t = rem % tiles;
-    const float *base = (which == 0 ? q : k) + ((size_t)bh * S + (size_t)t * kTile) * D;
+    const float4 *base = reinterpret_cast<const float4 *>(
+        (which == 0 ? q : k) + ((size_t)bh * S + (size_t)t * kTile) * D);
     const int rows = min(kTile, S - t * kTile);
     const int n4 = rows * D / 4;
-    bool ok = true;
+    uint32_t bad = 0;
+#pragma unroll 4
     for (int e = threadIdx.x; e < n4; e += kThreads) {
-        float4 v = reinterpret_cast<const float4 *>(base)[e];
-        ok = ok && operand_safe(v.x) && operand_safe(v.y) && operand_safe(v.z) && operand_safe(v.w);
+        const float4 v = base[e];
+        bad |= operand_unsafe(v.x) | operand_unsafe(v.y) | operand_unsafe(v.z) |
+               operand_unsafe(v.w);
     }
-    const int all_ok = __syncthreads_and(ok ? 1 : 0);
+    const int any_bad = __syncthreads_or((int)bad);
     if (threadIdx.x == 0)
-        unsafe[blk] = all_ok ? 0 : 1;
+        unsafe[blk] = any_bad ? 1 : 0;
 }
 
 hipError_t launch_operand_scan(const Problem &p, uint8_t *unsafe, hipStream_t st)

@@ -8,8 +8,11 @@
  *            which is the PS(mu) ulp of the product scaled by 2^(mu-23); C is
  *            2^23 ulps (even), so ties go to even.  Result: RN_mu(q*k) *
  *            2^(mu-23), exactly.
- *   sum      s = fl(acc_s + r_s), then integer RNE of s's bits to mu fraction
- *            bits (innocuous double rounding for mu <= 10).
+ *   sum      s = fl(acc_s + r_s), then RNE of s to mu fraction bits by
+ *            Veltkamp's splitting with the constant 2^(23-mu) + 1:
+ *            g = fl(C s), hi = fl(g + fl(s - g)) (innocuous double rounding for
+ *            mu <= 10).  check_split_exhaustive compares that splitting with
+ *            the integer RNE of the bits over every FP32 input.
  *   score    fl(acc_s * (scale * 2^(23-mu))).
  *
  * Valid when every nonzero |q|, |k| lies in [2^-40, 2^40] (products and sums
@@ -32,13 +35,50 @@ float emu_prod_scaled(float q, float k, int mu)
     return t - C;
 }
 
-float emu_round(float s, int mu)
+/* integer RNE of s's bits to mu fraction bits */
+static float emu_round_bits(float s, int mu)
 {
     uint32_t u = fb(s);
     int sh = 23 - mu;
     uint32_t half = 1u << (sh - 1);
     u = (u + ((u >> sh) & 1u) + (half - 1u)) & ~((1u << sh) - 1u);
     return bf(u);
+}
+
+/* the kernels' form: Veltkamp's splitting (three separately rounded FP32 ops) */
+float emu_round(float s, int mu)
+{
+    const float C = (float)((1u << (23 - mu)) + 1u);
+    volatile float g = C * s;
+    volatile float d = s - g;
+    return g + d;
+}
+
+/* Every FP32 pattern with a finite normal value of magnitude below 2^100, and
+ * +0 (the fast path's sums: never -0, nonzero magnitudes far above the
+ * subnormals, below 2^75): the splitting against the integer RNE.  Returns
+ * the number of mismatches; the first one in *first. */
+int64_t check_split_exhaustive(int mu, uint32_t *first)
+{
+    int64_t bad = 0;
+    uint32_t fst = 0;
+#pragma omp parallel for schedule(static) reduction(+ : bad)
+    for (int64_t i = 0; i < (1LL << 32); ++i) {
+        const uint32_t u = (uint32_t)i;
+        const uint32_t e = (u >> 23) & 0xffu;
+        if (e >= 127 + 100 || (e == 0 && u != 0u))
+            continue;
+        const float x = bf(u);
+        if (fb(emu_round(x, mu)) != fb(emu_round_bits(x, mu))) {
+            if (bad == 0) {
+#pragma omp critical
+                fst = u;
+            }
+            bad++;
+        }
+    }
+    *first = fst;
+    return bad;
 }
 
 float emu_ps_score(const float *q, const float *k, int D, int mu, float scale)

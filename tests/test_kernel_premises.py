@@ -2,7 +2,8 @@
 
 The HIP kernels compute PS(mu) products with one FP32 multiply (for the
 exponent), a magic constant and one fused multiply-add, and PS(mu) sums with
-an FP32 add followed by integer round-to-nearest-even of the bits.  A scalar
+an FP32 add followed by round-to-nearest-even to mu fraction bits through
+Veltkamp's splitting (three FP32 operations).  A scalar
 C emulation of exactly that sequence (tests/helpers/fast_ps_emul.c) is
 compared here with the oracle, so a flaw in the premise shows up on the CPU.
 These are host-logic tests; the GPU parity tests compare the kernels
@@ -27,6 +28,8 @@ def emu(orc):
                                    ctypes.c_int, ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64)]
     lib.check_sums_exhaustive.restype = ctypes.c_int64
     lib.check_sums_exhaustive.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.check_split_exhaustive.restype = ctypes.c_int64
+    lib.check_split_exhaustive.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_uint32)]
     lib.check_sums_random.restype = ctypes.c_int64
     lib.check_sums_random.argtypes = [ctypes.c_uint64, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
                                       ctypes.c_int, ctypes.c_void_p]
@@ -46,6 +49,16 @@ def test_magic_product_rounding(emu, orc, mu):
     bad = emu.check_products(11 + mu, 4_000_000, mu, -1, 1, _rn(orc), ctypes.byref(traps))
     assert bad == 0
     assert traps.value > 0 or mu <= 2   # the double-rounding trap was exercised
+
+
+@pytest.mark.parametrize("mu", [1, 4, 10])
+def test_split_rounding_equals_integer_rne_exhaustive(emu, mu):
+    """Veltkamp's splitting rounds to nearest, ties to even, on every FP32
+    input the fast path can produce (normal magnitudes below 2^100, and +0):
+    bit for bit the integer RNE (itself swept against the oracle's RN_mu)."""
+    first = ctypes.c_uint32(0)
+    bad = emu.check_split_exhaustive(mu, ctypes.byref(first))
+    assert bad == 0, (bad, hex(first.value))
 
 
 @pytest.mark.parametrize("mu,emin,emax", [(1, -20, 20), (4, -20, 20), (7, -12, 12)])
