@@ -114,6 +114,11 @@ def cpu_baseline(Q, K, V, w, mode_id, mu, tau, seed, ps_block=0):
                       f"{threads} OpenMP threads"}
 
 
+def tau_for_workload(name: str, mode: str, mu: int, rate: float) -> float:
+    from mixed_precision_attention_ps_amd.configs import tau_for
+    return tau_for(name, mode, mu, rate)
+
+
 def copy_calibration(args, dev):
     """A plain device copy of known size (the scale of the HBM counters)."""
     import torch
@@ -366,6 +371,9 @@ def main():
     ap.add_argument("--no-kl", action="store_true",
                     help="attention: no row KL in the timed calls (the serving case)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-relaxed", action="store_true",
+                    help="strict runs: no relaxed sub-record (the library's choice and the "
+                         "fused kernel on the same layer)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="run a plain copy of this many MiB first (counter calibration)")
     ap.add_argument("--nq", type=int, default=1, help="decode workloads: queries per head")
@@ -384,25 +392,55 @@ def main():
               "benchmark on its share; run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     from mixed_precision_attention_ps_amd import lamp
-    from mixed_precision_attention_ps_amd.configs import MLP_WORKLOADS, WORKLOADS, tau_for
+    from mixed_precision_attention_ps_amd.configs import MLP_WORKLOADS, WORKLOADS
 
     if args.workload in MLP_WORKLOADS:
         return bench_mlp(args, MLP_WORKLOADS[args.workload])
     w = WORKLOADS[args.workload]
     if w.name.startswith("decode"):
         return bench_decode(args, w)
-    mode_id = lamp.MODES[args.mode]
-    tau_mode = "strict" if args.mode == "random" else args.mode
-    tau = args.tau if args.tau is not None else tau_for(w.name, tau_mode, args.mu, args.rate)
     dev = torch.device("cuda:0")
-    log(f"[bench] {w.name} mode={args.mode} mu={args.mu} tau={tau}")
-
     Q, K, V, _ = w.qkv()
     q, k, v = (torch.from_numpy(x).to(dev) for x in (Q, K, V))
+    copy_calibration(args, dev)
+
+    rec = measure_attention(args, w, lamp, torch, q, k, v, args.mode, args.relaxed_path,
+                            args.steps, args.warmup)
+    if args.mode == "strict" and not args.no_relaxed:
+        # the relaxed rule on the same layer and inputs: the implementation
+        # the library picks, and the fused one-pass kernel
+        sub = {}
+        for name, rp in (("library_choice", 0), ("fused_kernel", 1)):
+            r = measure_attention(args, w, lamp, torch, q, k, v, "relaxed", rp, args.steps,
+                                  args.warmup)
+            sub[name] = {key: r[key] for key in ("value", "ms_per_step", "gpu_ms_per_step",
+                                                 "roofline", "path_alu_frac", "stages_ms",
+                                                 "kl_mean", "kl_reduction")}
+            sub[name]["impl"] = r["config"]["impl"]
+            sub[name]["tau"] = r["config"]["tau"]
+            sub[name]["rate"] = r["config"]["rate"]
+            sub[name]["relaxed_path"] = rp
+        rec["relaxed"] = sub
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample")
+        mode_id = lamp.MODES[args.mode]
+        rec["cpu_baseline"] = cpu_baseline(Q, K, V, w, mode_id, args.mu, rec["config"]["tau"], 0,
+                                           args.ps_block)
+    print(json.dumps(rec), flush=True)
+
+
+def measure_attention(args, w, lamp, torch, q, k, v, mode, relaxed_path, steps, warmup):
+    """Times `steps` lamp_attention_fwd calls (after `warmup`) in one mode on
+    the resident inputs; returns the record of that measurement."""
+    mode_id = lamp.MODES[mode]
+    tau_mode = "strict" if mode == "random" else mode
+    tau = args.tau if args.tau is not None else tau_for_workload(w.name, tau_mode, args.mu,
+                                                                 args.rate)
+    dev = q.device
+    log(f"[bench] {w.name} mode={mode} mu={args.mu} tau={tau} relaxed_path={relaxed_path}")
     B, H, S, D = w.B, w.H, w.S, w.D
     W32 = (S + 31) // 32
     out = torch.empty_like(q)
@@ -410,26 +448,23 @@ def main():
     mask = torch.empty((B, H, S, W32), dtype=torch.int32, device=dev)
     row_kl = torch.empty((B, H, S), dtype=torch.float64, device=dev)
 
-    copy_calibration(args, dev)
-
     def step(events=None):
         lamp.lamp_attention_fwd(q, k, v, causal=w.causal, mu=args.mu, tau=tau, mode=mode_id,
                                 out=out, probs=probs, recompute_mask=mask, want_stats=False,
                                 row_kl=None if args.no_kl else row_kl, stage_events=events,
-                                ps_block=args.ps_block,
-                                relaxed_path=args.relaxed_path)
+                                ps_block=args.ps_block, relaxed_path=relaxed_path)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
 
-    ev = [lamp.HipEvents(2 * lamp.LAMP_N_STAGES) for _ in range(args.steps)]
+    ev = [lamp.HipEvents(2 * lamp.LAMP_N_STAGES) for _ in range(steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_stop = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     t_start.record()
-    for s in range(args.steps):
+    for s in range(steps):
         step(ev[s])
     t_stop.record()
     torch.cuda.synchronize()
@@ -452,18 +487,19 @@ def main():
     stages = {}
     for name in ran:
         si = lamp.STAGES.index(name)
-        stages[name] = sum(e.elapsed_ms(2 * si, 2 * si + 1) for e in ev) / args.steps
+        stages[name] = sum(e.elapsed_ms(2 * si, 2 * si + 1) for e in ev) / steps
     for e in ev:
         e.close()
 
     # untimed: rate and KL of the same call
     _, st = lamp.lamp_attention_fwd(q, k, v, causal=w.causal, mu=args.mu, tau=tau, mode=mode_id,
                                     out=out, probs=probs, recompute_mask=mask, want_stats=True,
-                                    ps_block=args.ps_block, relaxed_path=args.relaxed_path)
+                                    ps_block=args.ps_block, relaxed_path=relaxed_path)
+    del out, probs, mask, row_kl
     n_valid = st["n_valid"]
     rate = st["n_selected"] / n_valid
-    ms_per_step = 1e3 * wall / args.steps
-    value = n_valid / (wall / args.steps)
+    ms_per_step = 1e3 * wall / steps
+    value = n_valid / (wall / steps)
 
     # dominant kernel: the PS(mu)+FP32 score tiles (strict, random, relaxed in
     # two passes) or the fused relaxed kernel; algorithmic VALU slots per valid
@@ -490,13 +526,13 @@ def main():
     # machine, which the measured co-issue of FP32 and integer work exceeds
     VALU16_PEAK = 256 * 4 * 16 * 2.4e9
     hbm_bytes = (0 if args.no_probs else 4) + 1 / 8 + 32 * D / (S + 1)
-    rec = {
+    return {
         "metric": METRIC, "value": value, "unit": "scores/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "steps": steps, "warmup": warmup, "ms_per_step": ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "H": H, "S": S, "D": D, "causal": w.causal,
-                   "mu": args.mu, "mode": args.mode, "ps_block": args.ps_block, "tau": tau,
+                   "mu": args.mu, "mode": mode, "ps_block": args.ps_block, "tau": tau,
                    "impl": impl,
                    "target_rate": args.rate,
                    "rate": rate, "probs": not args.no_probs, "mask": True,
@@ -506,17 +542,13 @@ def main():
         "path_alu_frac": w_path * value / ALU_PEAK,
         "path_valu16_frac": w_path * value / VALU16_PEAK,
         "path_hbm_frac": hbm_bytes * value / HBM_PEAK,
-        "gpu_ms_per_step": gpu_ms / args.steps,
+        "gpu_ms_per_step": gpu_ms / steps,
         "stages_ms": stages,
         "kl_mean": st["kl_sum"] / st["n_rows"],
         "kl_lowp_mean": st["kl_lowp_sum"] / st["n_rows"],
         "kl_reduction": (st["kl_lowp_sum"] / st["kl_sum"]) if st["kl_sum"] > 0 else None,
         "exact_tiles": st["n_exact_tiles"],
     }
-    if not args.no_cpu_baseline:
-        log("[bench] timing the CPU oracle on a sample")
-        rec["cpu_baseline"] = cpu_baseline(Q, K, V, w, mode_id, args.mu, tau, 0, args.ps_block)
-    print(json.dumps(rec), flush=True)
 
 
 if __name__ == "__main__":

@@ -266,10 +266,12 @@ Needs make_needs(const lamp_params &p, int mode, int S, bool probs, bool want_st
         need.pbuf = p.scores_mix != nullptr && !probs;
         need.part = want_kl || relaxed_rows;
         need.rowkl = want_kl;
-        // no dense y^ref: the score tiles fold every pair's FP32 score into
-        // the partials, and the row pass forms the few selected keys' FP32
-        // scores again by a gather dot (cheaper than storing them all)
-        need.yref = false;
+        // the score tiles form y^ref for every pair when they form the
+        // partials: kept, the row pass takes the selected scores' FP32 values
+        // from it instead of forming each dot again (a gather dot per
+        // selected key costs the row pass more than the dense store costs the
+        // score tiles)
+        need.yref = need.part && p.scores_ref == nullptr;
     } else {
         // longer strict rows and the random control: y^ref only for the row
         // KLs (without them the recompute forms each selected key's FP32 dot
@@ -890,8 +892,10 @@ static int run(const float *q, const float *k, const float *v, int B, int H, int
     // the partials' reference sums serve only the row KL
     P.ref_sums = want_stats || p.row_kl || p.row_kl_lowp;
 
+    // the device summary's counters are kept (and zeroed) only for a summary
     auto *dstats = at<lamp::DevStats>(ws, L.dstats);
-    P.n_band = &dstats->n_tie_band;
+    unsigned long long *n_exact = want_stats ? &dstats->n_exact_tiles : nullptr;
+    P.n_band = want_stats ? &dstats->n_tie_band : nullptr;
     auto *unsafe = at<uint8_t>(ws, L.unsafe);
     uint32_t *row_count = p.row_count ? p.row_count : at<uint32_t>(ws, L.row_count);
     double *row_kl = p.row_kl ? p.row_kl : at<double>(ws, L.row_kl);
@@ -904,7 +908,8 @@ static int run(const float *q, const float *k, const float *v, int B, int H, int
                                                           : LAMP_IMPL_STRICT_ROWS)
                      : mode == LAMP_RANDOM ? LAMP_IMPL_RANDOM
                                            : LAMP_IMPL_STRICT_STREAM;
-    LAMP_HIP_TRY(lamp::launch_zero(dstats, sizeof(lamp::DevStats), st), "zero stats");
+    if (want_stats)
+        LAMP_HIP_TRY(lamp::launch_zero(dstats, sizeof(lamp::DevStats), st), "zero stats");
     LAMP_HIP_TRY(tm.begin(LAMP_STAGE_SCAN), "hipEventRecord");
     LAMP_HIP_TRY(lamp::launch_operand_scan(P, unsafe, st), "operand scan launch");
     LAMP_HIP_TRY(tm.end(LAMP_STAGE_SCAN), "hipEventRecord");
@@ -916,12 +921,12 @@ static int run(const float *q, const float *k, const float *v, int B, int H, int
         auto *rs = at<lamp::RowStats>(ws, L.rowstats);
         LAMP_HIP_TRY(tm.begin(LAMP_STAGE_EXACT), "hipEventRecord");
         LAMP_HIP_TRY(lamp::launch_ps_scores(P, unsafe, ymix, yref, part,
-                                            &dstats->n_exact_tiles, false, st),
+                                            n_exact, false, st),
                      "score kernel launch");
         LAMP_HIP_TRY(tm.end(LAMP_STAGE_EXACT), "hipEventRecord");
         LAMP_HIP_TRY(tm.begin(LAMP_STAGE_SCORES), "hipEventRecord");
         LAMP_HIP_TRY(lamp::launch_ps_scores(P, unsafe, ymix, yref, part,
-                                            &dstats->n_exact_tiles, true, st),
+                                            n_exact, true, st),
                      "score kernel launch");
         LAMP_HIP_TRY(tm.end(LAMP_STAGE_SCORES), "hipEventRecord");
         LAMP_HIP_TRY(tm.begin(LAMP_STAGE_SELECT), "hipEventRecord");
@@ -939,13 +944,13 @@ static int run(const float *q, const float *k, const float *v, int B, int H, int
         LAMP_HIP_TRY(tm.begin(LAMP_STAGE_EXACT), "hipEventRecord");
         LAMP_HIP_TRY(lamp::launch_relaxed(P, unsafe, out, mask, row_count, row_kl, row_kl_lowp,
                                           ymix_raw, p.scores_ref, row_m, row_l,
-                                          &dstats->n_exact_tiles, false, st),
+                                          n_exact, false, st),
                      "relaxed kernel launch");
         LAMP_HIP_TRY(tm.end(LAMP_STAGE_EXACT), "hipEventRecord");
         LAMP_HIP_TRY(tm.begin(LAMP_STAGE_SCORES), "hipEventRecord");
         LAMP_HIP_TRY(lamp::launch_relaxed(P, unsafe, out, mask, row_count, row_kl, row_kl_lowp,
                                           ymix_raw, p.scores_ref, row_m, row_l,
-                                          &dstats->n_exact_tiles, true, st),
+                                          n_exact, true, st),
                      "relaxed kernel launch");
         LAMP_HIP_TRY(tm.end(LAMP_STAGE_SCORES), "hipEventRecord");
         if (probs) {
@@ -963,12 +968,12 @@ static int run(const float *q, const float *k, const float *v, int B, int H, int
         auto *part = at<lamp::RefPartial>(ws, L.part);
         LAMP_HIP_TRY(tm.begin(LAMP_STAGE_EXACT), "hipEventRecord");
         LAMP_HIP_TRY(lamp::launch_ps_scores(P, unsafe, ybuf, yref, part,
-                                            &dstats->n_exact_tiles, false, st),
+                                            n_exact, false, st),
                      "score kernel launch");
         LAMP_HIP_TRY(tm.end(LAMP_STAGE_EXACT), "hipEventRecord");
         LAMP_HIP_TRY(tm.begin(LAMP_STAGE_SCORES), "hipEventRecord");
         LAMP_HIP_TRY(lamp::launch_ps_scores(P, unsafe, ybuf, yref, part,
-                                            &dstats->n_exact_tiles, true, st),
+                                            n_exact, true, st),
                      "score kernel launch");
         LAMP_HIP_TRY(tm.end(LAMP_STAGE_SCORES), "hipEventRecord");
         const bool kl = need.rowkl;
@@ -984,12 +989,12 @@ static int run(const float *q, const float *k, const float *v, int B, int H, int
         uint32_t *list = at<uint32_t>(ws, L.list);
         LAMP_HIP_TRY(tm.begin(LAMP_STAGE_EXACT), "hipEventRecord");
         LAMP_HIP_TRY(lamp::launch_ps_scores(P, unsafe, ymix, yref, nullptr,
-                                            &dstats->n_exact_tiles, false, st),
+                                            n_exact, false, st),
                      "score kernel launch");
         LAMP_HIP_TRY(tm.end(LAMP_STAGE_EXACT), "hipEventRecord");
         LAMP_HIP_TRY(tm.begin(LAMP_STAGE_SCORES), "hipEventRecord");
         LAMP_HIP_TRY(lamp::launch_ps_scores(P, unsafe, ymix, yref, nullptr,
-                                            &dstats->n_exact_tiles, true, st),
+                                            n_exact, true, st),
                      "score kernel launch");
         LAMP_HIP_TRY(tm.end(LAMP_STAGE_SCORES), "hipEventRecord");
         LAMP_HIP_TRY(tm.begin(LAMP_STAGE_SELECT), "hipEventRecord");

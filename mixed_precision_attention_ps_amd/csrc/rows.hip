@@ -50,13 +50,14 @@ struct RowsArgs {
 };
 
 // LDS: phase A's per-wave selection lists and query rows, then phase B's
-// reduction of the four waves' P.V tiles (DV: V's columns padded to 64 NBW).
-template <int DV>
+// reduction of the four waves' P.V tiles (DV: V's columns padded to 64 NBW;
+// QN: float4 per query row, D / 4 for a compile-time D, else the maximum).
+template <int DV, int QN>
 union RowsSmem {
     struct {
         uint16_t key[4][64 * kRowChunk];   // selected keys, compacted, key order
         float val[4][64 * kRowChunk];      // per listed key exp(y_hi - m) (FP32)
-        float4 q[4][64];                   // the wave's query row (gather dot)
+        float4 q[4][QN];                   // the wave's query row (gather dot)
     } a;
     struct {
         float red[4][kGroupRows][DV + 4];   // the four waves' P.V tiles (FP32)
@@ -86,8 +87,8 @@ union RowsSmem {
 // product would lose precision (e_j below 1e-300, or a row whose factor
 // overflows) take exp(y_j - m_t) directly.  Everything after the selection
 // is the strict pass's.
-template <int D4, bool RELAXED, int DV, typename Args>
-__device__ __forceinline__ void row_pass(Args &a, RowsSmem<DV> &sm, const double *s_exp,
+template <int D4, bool RELAXED, int DV, int QN, typename Args>
+__device__ __forceinline__ void row_pass(Args &a, RowsSmem<DV, QN> &sm, const double *s_exp,
                                          int wave, int lane_in, uint64_t r, uint32_t &ties,
                                          RowKL *rk_slot)
 {
@@ -495,8 +496,8 @@ __device__ __forceinline__ void row_pass(Args &a, RowsSmem<DV> &sm, const double
 // limits, whose probability 0 would turn a non-finite V value into NaN
 // (0 * inf) in the product: such values are taken as 0 and added back at the
 // end for the rows that see their key.
-template <int DV>
-__device__ __forceinline__ void group_pv(const RowsArgs &a, RowsSmem<DV> &sm, int bh, int i0)
+template <int DV, int QN>
+__device__ __forceinline__ void group_pv(const RowsArgs &a, RowsSmem<DV, QN> &sm, int bh, int i0)
 {
     constexpr int CPL = DV / 16;   // V columns per lane = MFMA column blocks
     constexpr int F4 = CPL / 4;    // float4 per lane per key row
@@ -658,7 +659,8 @@ template <int D4, bool RELAXED, int DV>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(DV == 64 ? 5 : (DV == 128 ? 3 : 2)))) void rows_pv_kernel(RowsArgs a)
 {
-    __shared__ RowsSmem<DV> sm;
+    constexpr int QN = D4 > 0 ? D4 : 64;
+    __shared__ RowsSmem<DV, QN> sm;
     __shared__ double s_exp[64];   // 2^(k/64) for exp64
     __shared__ RowKL s_rk[kGroupRows];   // the rows' softmax sums for the KLs
     exp_table_fill(s_exp);
@@ -683,7 +685,7 @@ __attribute__((amdgpu_waves_per_eu(DV == 64 ? 5 : (DV == 128 ? 3 : 2)))) void ro
         KArgs *ak = kargs;
         asm volatile("" : "+s"(ak));
         if (i < a.S)
-            row_pass<D4, RELAXED, DV>(*ak, sm, s_exp, wave, lane, (uint64_t)bh * a.S + i, ties,
+            row_pass<D4, RELAXED, DV, QN>(*ak, sm, s_exp, wave, lane, (uint64_t)bh * a.S + i, ties,
                                       &s_rk[wave + 4 * k]);
         __builtin_amdgcn_wave_barrier();
     }
@@ -691,7 +693,7 @@ __attribute__((amdgpu_waves_per_eu(DV == 64 ? 5 : (DV == 128 ? 3 : 2)))) void ro
     __syncthreads();   // the group's probabilities are written; LDS is free
     if (a.kl)
         group_kl(a, s_rk, s_exp, bh, i0);
-    group_pv<DV>(a, sm, bh, i0);
+    group_pv<DV, QN>(a, sm, bh, i0);
 }
 
 // y^mix, when asked for, is formed in place over y^lo (ymix_out == ylo); the

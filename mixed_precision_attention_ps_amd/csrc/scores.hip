@@ -204,8 +204,6 @@ __global__ __launch_bounds__(kThreads) void ps_scores_kernel(ScoreArgs a)
 {
     __shared__ TileSmem sm;
     __shared__ double s_exp[64];   // 2^(k/64) for exp64
-    exp_table_fill(s_exp);
-    __syncthreads();
     auto tile_path = [&](long long g, int &bh, int &ti, int &tj) {
         bh = (int)(g / a.tiles_per_head);
         tile_coords((int)(g % a.tiles_per_head), a.tiles, a.causal, ti, tj);
@@ -227,6 +225,8 @@ __global__ __launch_bounds__(kThreads) void ps_scores_kernel(ScoreArgs a)
         if (!__syncthreads_or(need ? 1 : 0))
             return;
     }
+    exp_table_fill(s_exp);
+    __syncthreads();
     for (long long g = blockIdx.x; g < a.n_tiles; g += FAST_KERNEL ? a.n_tiles : gridDim.x) {
         int bh, ti, tj;
         const int path = tile_path(g, bh, ti, tj);
@@ -244,6 +244,7 @@ __global__ __launch_bounds__(kThreads) void ps_scores_kernel(ScoreArgs a)
 }
 
 constexpr long long kGenericGrid = 2048;   // work-groups of the generic kernel
+constexpr long long kGenericGridBeside = 512;   // ... when the fast kernel runs too
 
 hipError_t launch_ps_scores(const Problem &p, const uint8_t *unsafe, float *ylo, float *yref,
                             RefPartial *part, unsigned long long *exact_tiles, bool fast,
@@ -285,7 +286,10 @@ hipError_t launch_ps_scores(const Problem &p, const uint8_t *unsafe, float *ylo,
         if (p.mu <= 10)
             LAMP_SCORES_LAUNCH(true, dim3((unsigned)grid));
     } else {
-        const long long g = grid < kGenericGrid ? grid : kGenericGrid;
+        // beside the fast kernel the generic one usually finds no tile: a
+        // smaller grid, whose threads still cover every tile in one look
+        const long long cap = p.mu <= 10 ? kGenericGridBeside : kGenericGrid;
+        const long long g = grid < cap ? grid : cap;
         LAMP_SCORES_LAUNCH(false, dim3((unsigned)g));
     }
 #undef LAMP_SCORES_LAUNCH
