@@ -96,6 +96,7 @@ struct ScoreArgs {
     int ref_sums;        // part: L and B too (else only the maxima; L = B = 0)
     unsigned long long *exact_tiles;
     long long n_tiles;   // BH x tiles per head
+    int BH;
 };
 
 template <int PATH, int P>
@@ -191,6 +192,28 @@ __device__ __forceinline__ void score_tile_store(TileSmem &sm, const double *s_e
     }
 }
 
+#ifndef LAMP_SCORES_XCD
+#define LAMP_SCORES_XCD 1
+#endif
+// Tile index g -> (head, tile of the head).  Work-groups go to the GPU's
+// eight XCDs in turn (g mod 8), each XCD with its own L2: when the heads
+// split evenly over the XCDs, XCD x takes heads x, x + 8, ..., each head's
+// tiles one after another, so that a head's Q and K rows are fetched into
+// one L2 only.  Otherwise heads in order.
+__device__ __forceinline__ void head_tile_of(long long g, int BH, int tiles_per_head, int &bh,
+                                             long long &t)
+{
+    constexpr int kXcd = 8;
+    if (LAMP_SCORES_XCD && BH % kXcd == 0) {
+        const long long l = g / kXcd;
+        bh = (int)(l / tiles_per_head) * kXcd + (int)(g % kXcd);
+        t = l % tiles_per_head;
+    } else {
+        bh = (int)(g / tiles_per_head);
+        t = g % tiles_per_head;
+    }
+}
+
 // Two kernels share the tile grid: the fast kernel takes the tiles whose
 // operands allow the FP32 fast path (and returns on the others); the generic
 // kernel takes every other tile (exact double path, or plain FP32 at mu = 23).
@@ -205,8 +228,9 @@ __global__ __launch_bounds__(kThreads) void ps_scores_kernel(ScoreArgs a)
     __shared__ TileSmem sm;
     __shared__ double s_exp[64];   // 2^(k/64) for exp64
     auto tile_path = [&](long long g, int &bh, int &ti, int &tj) {
-        bh = (int)(g / a.tiles_per_head);
-        tile_coords((int)(g % a.tiles_per_head), a.tiles, a.causal, ti, tj);
+        long long t;
+        head_tile_of(g, a.BH, a.tiles_per_head, bh, t);
+        tile_coords((int)t, a.tiles, a.causal, ti, tj);
         if (a.pc.mu == 23)
             return (int)PATH_FP32;
         if (a.pc.mu <= 10 && !a.unsafe_q[bh * a.tiles + ti] && !a.unsafe_k[bh * a.tiles + tj])
@@ -270,6 +294,7 @@ hipError_t launch_ps_scores(const Problem &p, const uint8_t *unsafe, float *ylo,
     if (grid > 0x7fffffffLL)
         return hipErrorInvalidValue;
     a.n_tiles = grid;
+    a.BH = p.BH;
     if (grid == 0)
         return hipSuccess;
 #define LAMP_SCORES_LAUNCH(FASTK, G)                                                           \
