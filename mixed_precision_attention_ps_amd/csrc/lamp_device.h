@@ -470,6 +470,35 @@ __device__ __forceinline__ void buf_store_f32(__amdgpu_buffer_rsrc_t rs, uint32_
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), rs, byte_off, 0, 0);
 }
 
+// Work-group b of a launch over BH x nblk (head, block) pairs -> head bh and
+// block k, counted from the last block (the heaviest one under a causal
+// mask).  Work-groups go to the GPU's eight XCDs in turn (b mod 8), each XCD
+// with its own L2.  When the heads split evenly over the XCDs in batches of
+// hb, XCD x takes heads x, x + 8, ... in batches of hb and walks a batch's
+// blocks heaviest first with the batch's heads side by side, so that the
+// batch's K or V rows, read by every block of a head, stay in the XCD's L2
+// between its blocks (hb: the largest divisor of an XCD's head count not
+// above hb_max).  Otherwise heaviest blocks first over all heads.
+__device__ __forceinline__ void xcd_head_batches(unsigned b, int BH, int nblk, int hb_max,
+                                                 int &bh, int &k)
+{
+    constexpr int kXcd = 8;
+    int hb = hb_max;
+    while (hb > 1 && (BH / kXcd) % hb != 0)
+        --hb;
+    if (BH % kXcd == 0 && BH >= kXcd) {
+        const int x = (int)(b % kXcd);
+        const int l = (int)(b / kXcd);
+        const int batch = l / (hb * nblk);
+        const int j = l % (hb * nblk);
+        k = nblk - 1 - j / hb;
+        bh = (batch * hb + j % hb) * kXcd + x;
+    } else {
+        bh = (int)(b % (unsigned)BH);
+        k = nblk - 1 - (int)(b / (unsigned)BH);
+    }
+}
+
 // Wave ballot: bit l is set iff `c` holds on (active) lane l.  The compare's
 // own lane mask, with no round trip through a vector register (HIP's
 // __ballot goes through one: a select and a compare per call).

@@ -652,35 +652,6 @@ __device__ __forceinline__ void group_kl(const RowsArgs &a, const RowKL *s_rk, c
         a.row_kl[r] = (Br - k.dA) * inv_lr + ((double)k.mix_base + log(k.mix_l)) - lse_ref;
 }
 
-#ifndef LAMP_ROWS_HB
-#define LAMP_ROWS_HB 5
-#endif
-// Work-group b -> (head, row group).  Work-groups go to the GPU's eight XCDs
-// in turn (b mod 8), each XCD with its own L2; every group reads its head's V
-// rows in P.V.  When the heads split evenly over the XCDs, XCD x takes heads
-// x, x + 8, ... in batches of HB heads, and walks a batch's row groups
-// heaviest first (causal) with the batch's heads side by side: the batch's V
-// stays in the XCD's L2 while its groups run (a whole XCD's heads in turn
-// would cycle more V through L2 than it holds between two groups of one
-// head).  Otherwise: heaviest groups first over all heads.
-__device__ __forceinline__ void group_of_block(const RowsArgs &a, unsigned b, int &bh, int &g)
-{
-    constexpr int kXcd = 8;
-    const int per_xcd = a.BH / kXcd;
-    const int hb = LAMP_ROWS_HB;
-    if (a.BH % kXcd == 0 && per_xcd % hb == 0) {
-        const int x = (int)(b % kXcd);
-        const int l = (int)(b / kXcd);
-        const int batch = l / (hb * a.groups);
-        const int j = l % (hb * a.groups);
-        g = a.groups - 1 - j / hb;
-        bh = (batch * hb + j % hb) * kXcd + x;
-    } else {
-        bh = (int)(b % (unsigned)a.BH);
-        g = a.groups - 1 - (int)(b / (unsigned)a.BH);
-    }
-}
-
 // 16 rows per work-group, heaviest (causal) groups first so that the light
 // ones fill the tail of the launch.  Five waves per SIMD at DV = 64 (96
 // VGPRs; 29 KB of LDS per work-group); wider V tiles take more LDS.
@@ -698,8 +669,11 @@ __attribute__((amdgpu_waves_per_eu(DV == 64 ? 5 : (DV == 128 ? 3 : 2)))) void ro
     // makes the row, its length and every chunk guard scalar
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // batches of five heads per XCD: a batch's V stays in L2 between the
+    // groups of a head (all of an XCD's heads in turn cycle more V through
+    // it than it holds)
     int bh, g;
-    group_of_block(a, blockIdx.x, bh, g);
+    xcd_head_batches(blockIdx.x, a.BH, a.groups, 5, bh, g);
     const int i0 = g * kGroupRows;
     uint32_t ties = 0;
     // The arguments through an opaque pointer to the kernel-argument segment,
