@@ -147,7 +147,11 @@ void relaxed_kernel(RelaxedArgs a)
     uint32_t *const mask_blk = a.mask ? a.mask + blk_row * (uint64_t)a.W : nullptr;
     float *const ymix_blk = a.ymix_raw ? a.ymix_raw + blk_row * (uint64_t)S : nullptr;
     float *const yref_blk = a.yref_out ? a.yref_out + blk_row * (uint64_t)S : nullptr;
-    uint32_t ties = 0;   // this thread's near ties of the criterion
+    // the wave's near ties of the criterion: counted from ballots of the
+    // band test (a scalar count, no vector register kept across the loop)
+    uint32_t ties = 0;
+    const bool count_ties = a.n_band != nullptr && a.tau < INFINITY;
+    const double tie_band = 0x1p-16 * a.tau;
     for (int t = 0; t <= t_end; ++t) {
         const int col0 = t * kTile;
         float lo[4][4], ref[4][4];
@@ -196,7 +200,8 @@ void relaxed_kernel(RelaxedArgs a)
                 E[c] = valid[c] ? exp64((double)lo[r][c] - (double)mt_new, s_exp) : 0.0;
                 const double crit = 2.0 * E[c] * fabs((double)lo[r][c]);
                 sel[c] = valid[c] && crit > a.tau;
-                ties += (valid[c] && near_tie(crit, a.tau)) ? 1u : 0u;
+                if (count_ties)
+                    ties += (uint32_t)__popcll(ballot(valid[c] && fabs(crit - a.tau) <= tie_band));
                 mix[c] = sel[c] ? ref[r][c] : lo[r][c];
                 if (valid[c]) {
                     bm = fmaxf(bm, mix[c]);
@@ -404,7 +409,7 @@ void relaxed_kernel(RelaxedArgs a)
             }
         }
     }
-    add_ties(a.n_band, (uint32_t)wave_sum_int((int)ties));
+    add_ties(a.n_band, ties);
 }
 
 hipError_t launch_relaxed(const Problem &p, const uint8_t *unsafe, float *out, uint32_t *mask,
