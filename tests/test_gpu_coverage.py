@@ -254,3 +254,18 @@ def test_long_rows_gather_recompute(dev, orc, S, causal, D, mode):
         if mode == RANDOM:
             assert (g["mask"].reshape(B * H, S, -1)[:, rows[0]:rows[1]] == r["mask"]).all()
         compare_full(g, r, Q, V, causal=causal, tau=np.inf if mode == RANDOM else tau, rows=rows)
+
+
+# Head orders: with the heads a multiple of 8 the score tiles take one head
+# after another per XCD, and the fused row kernel walks batches of heads per
+# XCD (the largest divisor of an XCD's head count up to 5: 3 at 24 heads, 2 at
+# 16): every (head, row group) must still be computed once, against the oracle
+# on every head.
+@pytest.mark.parametrize("B,H,S,mode", [(3, 8, 320, STRICT), (2, 8, 200, RELAXED),
+                                        (1, 16, 130, STRICT), (1, 40, 96, STRICT)])
+def test_head_orders(dev, orc, B, H, S, mode):
+    Q, K, V, _ = make_qkv(B, H, S, 64, n_outlier=2, seed=B * 100 + H)
+    tau = 1e-2
+    g = run_gpu(dev, Q, K, V, causal=True, mu=4, tau=tau, mode=mode, relaxed_path=2)
+    r = run_orc(orc, Q, K, V, causal=True, mu=4, tau=tau, mode=mode)
+    compare_full(g, r, Q, V, causal=True, tau=tau)
