@@ -16,6 +16,17 @@
 // 64-double shared array, fills it with exp_table_fill and synchronises its
 // block before the first call.
 //
+// exp64_crit / exp64_sum: shorter forms of exp64 for the hot loops, with the
+// same table and range reduction except that ln 2 / 64 is taken as one double
+// (its rounding error, 3.6e-19, times |n| <= 7e4 moves r by at most 2.5e-14)
+// and the Taylor polynomial stops earlier:
+//   exp64_crit, degree 4: remainder below r^5/120 <= 3.9e-14 relative (6.4e-14
+//     with the reduction's error at the ends of the range), for
+//     values that decide a look-ahead criterion (a decision must agree with an
+//     exact evaluation outside a 1e-12 relative band around the threshold);
+//   exp64_sum, degree 3: remainder below r^4/24 <= 3.6e-11 relative, for sums
+//     that only normalise probabilities or enter a KL (1e-7 bars).
+//
 // exp_f32: an FP32-accurate exp of a double argument (probabilities): the
 // argument is split in double into n + f, |f| <= 1/2, f is rounded to FP32
 // (absolute error <= 2^-25) and 2^f is taken by the hardware exp2
@@ -89,6 +100,52 @@ __device__ __forceinline__ double exp64(double x, const double *s_tab)
 __device__ __forceinline__ double exp64_nonpos(double x, const double *s_tab)
 {
     return exp64_core(fmax(x, -750.0), s_tab);
+}
+
+template <int DEG>
+__device__ __forceinline__ double exp64_short_core(double x, const double *s_tab)
+{
+    const double k64Log2e = 0x1.71547652b82fep+6;    // 64 / ln 2
+    const double kLn2_64 = 0x1.62e42fefa39efp-7;     // ln 2 / 64, rounded to double
+    const double n = rint(x * k64Log2e);
+    const double r = fma(-n, kLn2_64, x);
+    double q;
+    if constexpr (DEG >= 4) {
+        q = fma(r, 1.0 / 24.0, 1.0 / 6.0);
+        q = fma(q, r, 0.5);
+    } else {
+        q = fma(r, 1.0 / 6.0, 0.5);
+    }
+    q = fma(q, r, 1.0);
+    const double p = q * r;   // exp(r) - 1
+    const int ni = (int)n;
+    const double t = s_tab[ni & 63];
+    return ldexp(fma(t, p, t), ni >> 6);
+}
+
+// (argument handling as exp64 and exp64_nonpos)
+__device__ __forceinline__ double exp64_crit(double x, const double *s_tab)
+{
+    if (!(x != x))
+        x = fmin(fmax(x, -750.0), 712.0);
+    return exp64_short_core<4>(x, s_tab);
+}
+
+__device__ __forceinline__ double exp64_crit_nonpos(double x, const double *s_tab)
+{
+    return exp64_short_core<4>(fmax(x, -750.0), s_tab);
+}
+
+__device__ __forceinline__ double exp64_sum(double x, const double *s_tab)
+{
+    if (!(x != x))
+        x = fmin(fmax(x, -750.0), 712.0);
+    return exp64_short_core<3>(x, s_tab);
+}
+
+__device__ __forceinline__ double exp64_sum_nonpos(double x, const double *s_tab)
+{
+    return exp64_short_core<3>(fmax(x, -750.0), s_tab);
 }
 
 __device__ __forceinline__ float exp_f32(double x)

@@ -72,14 +72,15 @@ __device__ __forceinline__ void relaxed_tile_scores(TileSmem &sm, const RelaxedA
 // exp of a difference of row maxima (-inf when a maximum is still unset).
 __device__ __forceinline__ double exp_delta(float from, float to, const double *s_exp)
 {
-    return from == -INFINITY ? 0.0 : exp64((double)from - (double)to, s_exp);
+    return from == -INFINITY ? 0.0 : exp64_sum((double)from - (double)to, s_exp);
 }
 
 // Per-score exponentials (double): E = exp(y^lo - m_t) serves the criterion
-// and, scaled by exp(m_t - m_mix), the softmax term of an unselected score;
-// e_ref = exp(y^ref - m_ref) serves the reference sums and, scaled by
-// exp(m_ref - m_mix), the softmax term of a selected score (whose y^mix is
-// y^ref).  Two double exps per score; the row factors are per tile.
+// (exp64_crit) and, scaled by exp(m_t - m_mix), the softmax term of an
+// unselected score; e_ref = exp(y^ref - m_ref) serves the reference sums and,
+// scaled by exp(m_ref - m_mix), the softmax term of a selected score (whose
+// y^mix is y^ref) (exp64_sum, as the row factors).  Two double exps per
+// score; the row factors are per tile.
 // P: the run width of the blocked PS(mu) order (run_width(a.pc.blk)).
 // Occupancy: at D <= 64 three waves per SIMD (168 registers, a few spilled;
 // 5 % faster than two without spills), at D <= 128 two.
@@ -197,7 +198,7 @@ void relaxed_kernel(RelaxedArgs a)
             float bm = -INFINITY, br = -INFINITY;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                E[c] = valid[c] ? exp64((double)lo[r][c] - (double)mt_new, s_exp) : 0.0;
+                E[c] = valid[c] ? exp64_crit((double)lo[r][c] - (double)mt_new, s_exp) : 0.0;
                 const double crit = 2.0 * E[c] * fabs((double)lo[r][c]);
                 sel[c] = valid[c] && crit > a.tau;
                 if (count_ties)
@@ -249,20 +250,20 @@ void relaxed_kernel(RelaxedArgs a)
             const double alpha = exp_delta(m_mix, mm_new, s_exp);
             // row factors; a factor that would overflow (maxima more than
             // ~700 apart) falls back to a direct exp per score
-            const double f_lo = exp64((double)mt_new - (double)mm_new, s_exp);
-            const double f_ref = exp64((double)mr_new - (double)mm_new, s_exp);
+            const double f_lo = exp64_sum((double)mt_new - (double)mm_new, s_exp);
+            const double f_ref = exp64_sum((double)mr_new - (double)mm_new, s_exp);
             const bool direct = !(f_lo < 1e300 && f_ref < 1e300);
             double sl = 0.0, sr = 0.0, sa = 0.0, sll = 0.0, sb = 0.0;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 pmix[r][c] = 0.0f;
                 if (valid[c]) {
-                    const double er = exp64((double)ref[r][c] - (double)mr_new, s_exp);
+                    const double er = exp64_sum((double)ref[r][c] - (double)mr_new, s_exp);
                     double pe;
                     if (!direct)
                         pe = sel[c] ? er * f_ref : E[c] * f_lo;
                     else
-                        pe = exp64((double)mix[c] - (double)mm_new, s_exp);
+                        pe = exp64_sum((double)mix[c] - (double)mm_new, s_exp);
                     pmix[r][c] = (float)pe;
                     sl += pe;
                     sr += er;

@@ -176,7 +176,7 @@ __device__ __forceinline__ void row_pass(Args &a, RowsSmem<DV, QN> &sm, const do
             if (t < nch) {
                 const uint64_t vmask = ballot(64 * t < rem);
                 const bool at = 64 * t < rem && v[t] == m;
-                const double x = exp64_nonpos((double)v[t] - md, s_exp);
+                const double x = exp64_crit_nonpos((double)v[t] - md, s_exp);
                 e[t] = x;
                 A += at ? 0.0 : x;
                 cnt += __popcll(ballot(v[t] == m) & vmask);
@@ -205,7 +205,7 @@ __device__ __forceinline__ void row_pass(Args &a, RowsSmem<DV, QN> &sm, const do
             if (lane >= off)
                 mt = fmaxf(mt, o);
         }
-        ft = lane < nch ? exp64((double)m - (double)mt, s_exp) : 1.0;
+        ft = lane < nch ? exp64_crit((double)m - (double)mt, s_exp) : 1.0;
         direct_row = ballot(lane < nch && !(ft < 1e300)) != 0;
     }
 
@@ -241,7 +241,7 @@ __device__ __forceinline__ void row_pass(Args &a, RowsSmem<DV, QN> &sm, const do
                     if (ballot(dir) != 0) {
                         const float mtt = lane_read(mt, t);
                         if (dir)
-                            E = exp64((double)v[t] - (double)mtt, s_exp);
+                            E = exp64_crit((double)v[t] - (double)mtt, s_exp);
                     }
                     crit = 2.0 * E * fabs((double)v[t]);
                 } else {
@@ -330,13 +330,13 @@ __device__ __forceinline__ void row_pass(Args &a, RowsSmem<DV, QN> &sm, const do
         // y^lo of the key, read before y^mix may overwrite it in place
         const float yl = kl ? y[j] : 0.0f;
         const float yhi = yr ? yr[j] : dot_hi(j);
-        const double ehi = exp64((double)yhi - (double)m, s_exp);
+        const double ehi = exp64_sum((double)yhi - (double)m, s_exp);
         s_val[ei] = (float)ehi;
         if (a.ymix_out)   // y^mix is y^lo in place: only recomputed keys change
             a.ymix_out[r * (uint64_t)S + j] = yhi;
         dL += ehi;
         if (kl)
-            dA += exp64((double)yhi - mr, s_exp) * ((double)yhi - (double)yl);
+            dA += exp64_sum((double)yhi - mr, s_exp) * ((double)yhi - (double)yl);
     }
     dL = wave_sum(dL);
     if (kl)
@@ -638,7 +638,7 @@ __device__ __forceinline__ void group_kl(const RowsArgs &a, const RowKL *s_rk, c
     if (t < nt)
         q = a.part[r * (uint64_t)a.tiles + t];
     const float mr = group16_max(q.m);
-    const double f = t < nt ? exp64_nonpos((double)q.m - (double)mr, s_exp) : 0.0;
+    const double f = t < nt ? exp64_sum_nonpos((double)q.m - (double)mr, s_exp) : 0.0;
     const double Lr = group16_sum(q.L * f);
     const double Br = group16_sum(q.B * f);
     if (t != 0 || i0 + lr >= a.S)

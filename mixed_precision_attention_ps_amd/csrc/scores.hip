@@ -163,7 +163,7 @@ __device__ __forceinline__ void score_tile_store(TileSmem &sm, const double *s_e
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     const double x = (double)ref[r][c] - (double)m[r];
-                    const double e = PATH == PATH_FAST ? exp64_nonpos(x, s_exp) : exp64(x, s_exp);
+                    const double e = PATH == PATH_FAST ? exp64_sum_nonpos(x, s_exp) : exp64_sum(x, s_exp);
                     // y_ref - y_lo in FP32: exact when the two are within a factor
                     // of two (Sterbenz), else within half an ulp of the difference
                     const double dy = (double)(ref[r][c] - lo[r][c]);

@@ -103,13 +103,13 @@ __global__ __launch_bounds__(kThreads) void strict_select_kernel(SelectArgs a)
     auto accumulate = [&](float v, float vr, double &e) {
         const bool at = v == m;
         const double dl = (double)v - (double)m, dr = (double)vr - (double)mr;
-        const double x = exp64_nonpos(dl, s_exp);
+        const double x = exp64_crit_nonpos(dl, s_exp);
         e = at ? 1.0 : x;
         A += at ? 0.0 : x;
         cnt += at ? 1 : 0;
         nan_lo |= !at && dl != dl;
         if (ref) {   // wave-uniform
-            const double er = exp64_nonpos(dr, s_exp);
+            const double er = exp64_sum_nonpos(dr, s_exp);
             Lr += er;
             Br += er * ((double)vr - (double)v);
             nan_ref |= dr != dr;
@@ -220,7 +220,7 @@ __global__ __launch_bounds__(kThreads) void strict_select_kernel(SelectArgs a)
                     double e = 0.0;
                     if (j < n)   // a NaN row already has NaN statistics (no key selected)
                         e = (vb[u] == m) ? 1.0
-                                         : exp64_nonpos((double)vb[u] - (double)m, s_exp);
+                                         : exp64_crit_nonpos((double)vb[u] - (double)m, s_exp);
                     decide(jc, j, vb[u], e);
                 }
             }
@@ -325,7 +325,7 @@ __global__ __launch_bounds__(kThreads) void relaxed_select_kernel(RelaxedSelectA
     double Lr = 0.0, Br = 0.0;
     for (int t = lane; t < nt; t += 64) {
         const RefPartial p = pt[t];
-        const double f = exp64_nonpos((double)p.m - (double)mr, s_exp);
+        const double f = exp64_sum_nonpos((double)p.m - (double)mr, s_exp);
         Lr += p.L * f;
         Br += p.B * f;
     }
@@ -352,8 +352,8 @@ __global__ __launch_bounds__(kThreads) void relaxed_select_kernel(RelaxedSelectA
             const float v = s_qv[wave][lane];
             const float h = yr[j];
             y[j] = h;
-            l_sel += exp64_nonpos((double)h - M, s_exp);
-            dA += exp64_nonpos((double)h - (double)mr, s_exp) * ((double)h - (double)v);
+            l_sel += exp64_sum_nonpos((double)h - M, s_exp);
+            dA += exp64_sum_nonpos((double)h - (double)mr, s_exp) * ((double)h - (double)v);
         }
     };
     for (int j0 = 0; j0 < n; j0 += 64 * kSelBatch) {
@@ -376,15 +376,15 @@ __global__ __launch_bounds__(kThreads) void relaxed_select_kernel(RelaxedSelectA
                     __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(bm[u])));
                 if (bmu > mt) {
                     mt = bmu;
-                    g_lo = exp64_nonpos((double)mt - (double)mlo, s_exp);
-                    g_mix = exp64_nonpos((double)mt - M, s_exp);
+                    g_lo = exp64_sum_nonpos((double)mt - (double)mlo, s_exp);
+                    g_mix = exp64_sum_nonpos((double)mt - M, s_exp);
                 }
                 const int j = jc + lane;
                 const bool valid = j < n;
                 const float v = vb[u];
                 // y <= m_t for a valid key; a key past the row gives E = 0
                 const double E =
-                    exp64_nonpos(valid ? (double)v - (double)mt : -INFINITY, s_exp);
+                    exp64_crit_nonpos(valid ? (double)v - (double)mt : -INFINITY, s_exp);
                 has_nan |= valid && v != v;
                 const double c = 2.0 * E * fabs((double)v);
                 const bool sel = valid && c > a.tau;
@@ -809,9 +809,9 @@ __global__ __launch_bounds__(kThreads) void recompute_kernel(RecomputeArgs a)
                 const float ylo = *slot;
                 *slot = yhi;
                 const double ml = (double)s_mlo[lr], mr = (double)s_mref[lr];
-                cl = exp64((double)yhi - ml, s_exp) - exp64((double)ylo - ml, s_exp);
+                cl = exp64_crit((double)yhi - ml, s_exp) - exp64_crit((double)ylo - ml, s_exp);
                 if (a.row_kl)
-                    ca = exp64((double)yhi - mr, s_exp) * ((double)yhi - (double)ylo);
+                    ca = exp64_sum((double)yhi - mr, s_exp) * ((double)yhi - (double)ylo);
             }
         }
         s_dl[tid] = cl;

@@ -10,6 +10,7 @@ These are host-logic tests; the GPU parity tests compare the kernels
 themselves with the oracle.
 """
 import ctypes
+import math
 
 import numpy as np
 import pytest
@@ -94,3 +95,37 @@ def test_emulated_scores_match_oracle(emu, orc, mu, D, outl):
         got = np.float32(emu.emu_ps_score(qi.ctypes.data, ki.ctypes.data, D, mu, s))
         want = np.float32(np.float32(orc.ps_dot(qi, ki, mu)) * s)
         assert got.view(np.uint32) == want.view(np.uint32), (i, got, want)
+
+
+@pytest.fixture(scope="module")
+def exp_emu():
+    lib = load("exp64_emul")
+    lib.emu_exp64_short.restype = ctypes.c_double
+    lib.emu_exp64_short.argtypes = [ctypes.c_double, ctypes.c_int]
+    lib.max_rel_error.restype = ctypes.c_double
+    lib.max_rel_error.argtypes = [ctypes.c_int, ctypes.c_uint64, ctypes.c_int64, ctypes.c_double,
+                                  ctypes.c_double]
+    return lib
+
+
+@pytest.mark.parametrize("deg,bound", [(4, 6.5e-14), (3, 3.7e-11)])
+def test_short_exp64_error_bounds(exp_emu, deg, bound):
+    """The kernels' shortened double exponentials (Taylor degree 4 for values
+    that decide a criterion, 3 for normalising sums and KLs) stay within the
+    bounds the truncation and the one-double ln 2 / 64 give, over the whole
+    argument range and near 0, where softmax terms concentrate."""
+    worst = 0.0
+    for seed, lo, hi in [(1, -745.0, 0.0), (2, -20.0, 0.0), (3, -0.05, 0.05), (4, 0.0, 709.0)]:
+        worst = max(worst, exp_emu.max_rel_error(deg, seed, 400_000, lo, hi))
+    assert worst <= bound, worst
+    # the truncation is visible: the degree-3 form is not accidentally exact
+    assert deg == 4 or worst > 1e-13
+
+
+@pytest.mark.parametrize("deg", [3, 4])
+def test_short_exp64_special_values(exp_emu, deg):
+    assert exp_emu.emu_exp64_short(0.0, deg) == 1.0   # a key at its row maximum
+    assert exp_emu.emu_exp64_short(float("-inf"), deg) == 0.0
+    assert exp_emu.emu_exp64_short(-800.0, deg) == 0.0
+    assert math.isinf(exp_emu.emu_exp64_short(800.0, deg))
+    assert math.isnan(exp_emu.emu_exp64_short(float("nan"), deg))
