@@ -220,7 +220,8 @@ __device__ __forceinline__ void row_pass(Args &a, RowsSmem<DV, QN> &sm, const do
     const double tau_l2 = a.tau * (L * L) * 0.5;
     const double rhs = RELAXED ? a.tau : tau_l2;
     const double tie_lo = rhs * (1.0 - 0x1p-16), tie_hi = rhs * (1.0 + 0x1p-16);
-    const bool count_ties = rhs < INFINITY;   // (near_tie's finite threshold)
+    // (only when a summary is asked for; near_tie's finite threshold)
+    const bool count_ties = a.n_band != nullptr && rhs < INFINITY;
     uint32_t selbits = 0;
     uint32_t total = 0;
     uint32_t mword = 0;
@@ -254,8 +255,9 @@ __device__ __forceinline__ void row_pass(Args &a, RowsSmem<DV, QN> &sm, const do
                 if (count_ties)
                     ties += (uint32_t)__popcll(ballot(crit > tie_lo) & ~ballot(crit > tie_hi) &
                                                vmask);
-                mword = lane == 2 * t ? (uint32_t)b
-                                      : (lane == 2 * t + 1 ? (uint32_t)(b >> 32) : mword);
+                // (the wave-uniform words written into lanes 2t, 2t + 1)
+                mword = write_lane(mword, (uint32_t)b, 2 * t);
+                mword = write_lane(mword, (uint32_t)(b >> 32), 2 * t + 1);
                 const bool sel = valid && crit > rhs;
                 if (sel)
                     s_key[total + lanes_below(b)] = (uint16_t)(64 * t + lane);

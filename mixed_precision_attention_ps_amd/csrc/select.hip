@@ -186,7 +186,8 @@ __global__ __launch_bounds__(kThreads) void strict_select_kernel(SelectArgs a)
             sel = c > a.tau;
             tie = near_tie(c, a.tau);
         }
-        ties += (uint32_t)__popcll(ballot(tie));
+        if (a.n_band)   // near ties are counted only for a summary
+            ties += (uint32_t)__popcll(ballot(tie));
         const uint64_t b = ballot(sel);
         if (!a.count_only) {
             if (a.mask) {
@@ -388,7 +389,8 @@ __global__ __launch_bounds__(kThreads) void relaxed_select_kernel(RelaxedSelectA
                 has_nan |= valid && v != v;
                 const double c = 2.0 * E * fabs((double)v);
                 const bool sel = valid && c > a.tau;
-                ties += (uint32_t)__popcll(ballot(valid && near_tie(c, a.tau)));
+                if (a.n_band)   // near ties are counted only for a summary
+                    ties += (uint32_t)__popcll(ballot(valid && near_tie(c, a.tau)));
                 l_lo = fma(E, g_lo, l_lo);
                 l_un = sel ? l_un : fma(E, g_mix, l_un);
                 const uint64_t b = ballot(sel);
