@@ -499,16 +499,6 @@ __device__ __forceinline__ void xcd_head_batches(unsigned b, int BH, int nblk, i
     }
 }
 
-// v with lane `lane` (wave-uniform) replaced by the wave-uniform x: one
-// v_writelane_b32 (no load; it writes whatever the exec mask).
-__device__ __forceinline__ uint32_t write_lane(uint32_t v, uint32_t x, int lane)
-{
-    const uint32_t xs = __builtin_amdgcn_readfirstlane(x);
-    const int ls = __builtin_amdgcn_readfirstlane(lane);
-    asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(v) : "s"(xs), "s"(ls));
-    return v;
-}
-
 // Wave ballot: bit l is set iff `c` holds on (active) lane l.  The compare's
 // own lane mask, with no round trip through a vector register (HIP's
 // __ballot goes through one: a select and a compare per call).

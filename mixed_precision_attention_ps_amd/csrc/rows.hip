@@ -255,9 +255,8 @@ __device__ __forceinline__ void row_pass(Args &a, RowsSmem<DV, QN> &sm, const do
                 if (count_ties)
                     ties += (uint32_t)__popcll(ballot(crit > tie_lo) & ~ballot(crit > tie_hi) &
                                                vmask);
-                // (the wave-uniform words written into lanes 2t, 2t + 1)
-                mword = write_lane(mword, (uint32_t)b, 2 * t);
-                mword = write_lane(mword, (uint32_t)(b >> 32), 2 * t + 1);
+                mword = lane == 2 * t ? (uint32_t)b
+                                      : (lane == 2 * t + 1 ? (uint32_t)(b >> 32) : mword);
                 const bool sel = valid && crit > rhs;
                 if (sel)
                     s_key[total + lanes_below(b)] = (uint16_t)(64 * t + lane);
