@@ -32,18 +32,26 @@ struct FinishArgs {
 // Each KS-key step: thread (row tid/4, keys KS/4 * (tid%4)..) forms KS/4
 // probabilities; the P and V tiles go to double-buffered LDS (one barrier per
 // step) while the next step's scores and V rows are already being loaded;
-// wave w multiplies rows 16w..16w+15 of P by V.  DV = 16 NB is the padded
-// head dimension (compile-time, so every MFMA and LDS index is static).
-template <int NB, int KS>
-__global__ __launch_bounds__(kThreads) void finish_kernel(FinishArgs a)
+// wave w multiplies rows 16(w%4)..16(w%4)+15 of P by V.  DV = 16 NB is the
+// padded head dimension (compile-time, so every MFMA and LDS index is
+// static).  WS: the work-group has 4 WS waves, wave w taking the column
+// blocks NB/WS * (w/4) .. of its rows (WS = 2 at D = 128: each wave then
+// holds half the P.V accumulators, and twice the waves fit on a SIMD).
+template <int NB, int KS, int WS>
+__global__ __launch_bounds__(kThreads * WS) void finish_kernel(FinishArgs a)
 {
+    constexpr int NT = kThreads * WS;      // threads per work-group
+    constexpr int NBW = NB / WS;           // MFMA column blocks per wave
+    static_assert(NB % WS == 0, "column split");
     constexpr int kFinKeys = KS;          // keys per step
     constexpr int kFinPP = KS + 4;        // P tile row pitch (2-way LDS reads)
-    constexpr int KPT = KS / 4;           // keys per thread per step
+    constexpr int TPR = NT / kFinRows;    // threads per P row
+    constexpr int KPT = KS / TPR;         // keys per thread per step
+    static_assert(KPT % 4 == 0, "float4 P stores");
     constexpr int DV = 16 * NB;
     constexpr int VP = DV + 16;                  // V tile row pitch (2-way LDS reads)
     constexpr int NV4 = kFinKeys * DV / 4;             // float4 in a V tile
-    constexpr int V4 = (NV4 + kThreads - 1) / kThreads;   // per thread per step
+    constexpr int V4 = (NV4 + NT - 1) / NT;            // per thread per step
     __shared__ float sP[2][kFinRows][kFinPP];
     __shared__ float sV[2][kFinKeys][VP];
     __shared__ double s_lse[kFinRows];
@@ -61,10 +69,13 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(FinishArgs a)
     const int bh = (int)(blockIdx.x % BH);
     const int row0 = (a.blocks_per_head - 1 - (int)(blockIdx.x / BH)) * kFinRows;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // row group and first column block (compile-time 0 for WS = 1)
+    const int rw = WS == 1 ? wave : (wave & 3), cb0 = WS == 1 ? 0 : (wave >> 2) * NBW;
+    constexpr int kRowsPerWave = kFinRows / (4 * WS);
 
     // lse of each row; rows flagged by the recompute get a pass over the row.
-    for (int rr = 0; rr < kFinRows / 4; ++rr) {
-        const int lr = wave * (kFinRows / 4) + rr;
+    for (int rr = 0; rr < kRowsPerWave; ++rr) {
+        const int lr = wave * kRowsPerWave + rr;
         const int i = row0 + lr;
         double lse = 0.0;
         if (i < S) {
@@ -92,7 +103,7 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(FinishArgs a)
     }
     __syncthreads();
 
-    const int prow = tid >> 2, kseg = (tid & 3) * KPT;
+    const int prow = tid / TPR, kseg = (tid % TPR) * KPT;
     const int ip = row0 + prow;
     const bool prow_ok = ip < S;
     const int np = prow_ok ? (a.causal ? ip + 1 : S) : 0;
@@ -127,7 +138,7 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(FinishArgs a)
     auto load_v = [&](int j0, float4 (&vv)[V4]) {
 #pragma unroll
         for (int u = 0; u < V4; ++u) {
-            const int e = tid + u * kThreads;
+            const int e = tid + u * NT;
             const int key = e / (DV / 4), col = (e % (DV / 4)) * 4;
             float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
             if (e < NV4 && j0 + key < S && col < D)
@@ -136,9 +147,9 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(FinishArgs a)
         }
     };
 
-    double acc[NB][4];
+    double acc[NBW][4];
 #pragma unroll
-    for (int q = 0; q < NB; ++q)
+    for (int q = 0; q < NBW; ++q)
 #pragma unroll
         for (int v = 0; v < 4; ++v)
             acc[q][v] = 0.0;
@@ -184,7 +195,7 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(FinishArgs a)
         const bool diag = a.causal && j0 + kFinKeys > row0;
 #pragma unroll
         for (int u = 0; u < V4; ++u) {
-            const int e = tid + u * kThreads;
+            const int e = tid + u * NT;
             const int key = e / (DV / 4), col = (e % (DV / 4)) * 4;
             if (e < NV4) {
                 float4 x = vcur[u];
@@ -198,22 +209,22 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(FinishArgs a)
         __syncthreads();
 #pragma unroll
         for (int k16 = 0; k16 < kFinKeys / 16; ++k16) {
-            floatx4 part[NB];
+            floatx4 part[NBW];
 #pragma unroll
-            for (int q = 0; q < NB; ++q)
+            for (int q = 0; q < NBW; ++q)
                 part[q] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int k4 = 0; k4 < 4; ++k4) {
                 const int kk = k16 * 4 + k4;
-                const float av = sP[buf][wave * 16 + (lane & 15)][kk * 4 + (lane >> 4)];
+                const float av = sP[buf][rw * 16 + (lane & 15)][kk * 4 + (lane >> 4)];
 #pragma unroll
-                for (int q = 0; q < NB; ++q) {
-                    const float bv = sV[buf][kk * 4 + (lane >> 4)][q * 16 + (lane & 15)];
+                for (int q = 0; q < NBW; ++q) {
+                    const float bv = sV[buf][kk * 4 + (lane >> 4)][(cb0 + q) * 16 + (lane & 15)];
                     part[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, part[q], 0, 0, 0);
                 }
             }
 #pragma unroll
-            for (int q = 0; q < NB; ++q)
+            for (int q = 0; q < NBW; ++q)
 #pragma unroll
                 for (int v = 0; v < 4; ++v)
                     acc[q][v] += (double)part[q][v];
@@ -231,8 +242,8 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(FinishArgs a)
     // stores (64 lanes x 16 bytes).
     if (a.probs) {
         const int z0 = nsteps * kFinKeys;
-        for (int rr = 0; rr < kFinRows / 4; ++rr) {
-            const int iz = row0 + wave * (kFinRows / 4) + rr;
+        for (int rr = 0; rr < kRowsPerWave; ++rr) {
+            const int iz = row0 + wave * kRowsPerWave + rr;
             if (iz >= S)
                 break;
             float *pz = a.probs + ((uint64_t)bh * S + iz) * (uint64_t)S;
@@ -251,11 +262,11 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(FinishArgs a)
     // probability times it gives), keys past the row add nothing.
     if (s_vbad) {
 #pragma unroll
-        for (int q = 0; q < NB; ++q) {
-            const int col = q * 16 + (lane & 15);
+        for (int q = 0; q < NBW; ++q) {
+            const int col = (cb0 + q) * 16 + (lane & 15);
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const int i = row0 + wave * 16 + 4 * (lane >> 4) + v;
+                const int i = row0 + rw * 16 + 4 * (lane >> 4) + v;
                 if (col < D && i < S)
                     for (int j = row0; j <= i; ++j) {
                         const float x = Vh[(size_t)j * D + col];
@@ -266,15 +277,16 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(FinishArgs a)
         }
     }
 
-    // Lane holds rows 16*wave + 4*(lane/16) + v of column 16q + lane%16.
+    // Lane holds rows 16 (wave % 4) + 4 (lane / 16) + v of column
+    // 16 (cb0 + q) + lane % 16.
 #pragma unroll
-    for (int q = 0; q < NB; ++q) {
-        const int col = q * 16 + (lane & 15);
+    for (int q = 0; q < NBW; ++q) {
+        const int col = (cb0 + q) * 16 + (lane & 15);
         if (col >= D)
             continue;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-            const int i = row0 + wave * 16 + 4 * (lane >> 4) + v;
+            const int i = row0 + rw * 16 + 4 * (lane >> 4) + v;
             if (i < S)
                 a.out[((size_t)bh * S + i) * D + col] = (float)acc[q][v];
         }
@@ -284,18 +296,19 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(FinishArgs a)
 static hipError_t launch_finish_kernel(const FinishArgs &a, const Problem &p, hipStream_t st)
 {
     const dim3 grid((unsigned)((uint64_t)p.BH * a.blocks_per_head)), block(kThreads);
+    const dim3 block2(2 * kThreads);
     switch ((p.D + 15) / 16) {
-    case 1: hipLaunchKernelGGL((finish_kernel<1, 32>), grid, block, 0, st, a); break;
-    case 2: hipLaunchKernelGGL((finish_kernel<2, 32>), grid, block, 0, st, a); break;
-    case 3: hipLaunchKernelGGL((finish_kernel<3, 32>), grid, block, 0, st, a); break;
-    case 4: hipLaunchKernelGGL((finish_kernel<4, 32>), grid, block, 0, st, a); break;
-    case 5: hipLaunchKernelGGL((finish_kernel<5, 32>), grid, block, 0, st, a); break;
-    case 6: hipLaunchKernelGGL((finish_kernel<6, 32>), grid, block, 0, st, a); break;
-    case 7: hipLaunchKernelGGL((finish_kernel<7, 32>), grid, block, 0, st, a); break;
-    case 8: hipLaunchKernelGGL((finish_kernel<8, 32>), grid, block, 0, st, a); break;
+    case 1: hipLaunchKernelGGL((finish_kernel<1, 32, 1>), grid, block, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((finish_kernel<2, 32, 1>), grid, block, 0, st, a); break;
+    case 3: hipLaunchKernelGGL((finish_kernel<3, 32, 1>), grid, block, 0, st, a); break;
+    case 4: hipLaunchKernelGGL((finish_kernel<4, 32, 1>), grid, block, 0, st, a); break;
+    case 5: hipLaunchKernelGGL((finish_kernel<5, 32, 1>), grid, block, 0, st, a); break;
+    case 6: hipLaunchKernelGGL((finish_kernel<6, 32, 2>), grid, block2, 0, st, a); break;
+    case 7: hipLaunchKernelGGL((finish_kernel<7, 32, 1>), grid, block, 0, st, a); break;
+    case 8: hipLaunchKernelGGL((finish_kernel<8, 32, 2>), grid, block2, 0, st, a); break;
     case 9: case 10: case 11: case 12:
-        hipLaunchKernelGGL((finish_kernel<12, 16>), grid, block, 0, st, a); break;
-    default: hipLaunchKernelGGL((finish_kernel<16, 16>), grid, block, 0, st, a); break;
+        hipLaunchKernelGGL((finish_kernel<12, 16, 1>), grid, block, 0, st, a); break;
+    default: hipLaunchKernelGGL((finish_kernel<16, 16, 1>), grid, block, 0, st, a); break;
     }
     return hipGetLastError();
 }
