@@ -139,7 +139,11 @@ typedef struct {
     void **stage_events;      /* NULL or 2*LAMP_N_STAGES hipEvent_t created by
                                  the caller; event 2s / 2s+1 are recorded on
                                  the stream before / after stage s when that
-                                 stage runs (profiling)                       */
+                                 stage runs (profiling); a NULL entry is not
+                                 recorded.  Each record of an event created
+                                 without hipEventDisableSystemFence writes
+                                 back and invalidates the caches, which slows
+                                 the stage after it                           */
     int ps_block;             /* PS(mu) accumulation order: 0 or 1 = the
                                  sequential order (default); a power of two
                                  b >= 4 (<= 2^24) = the blocked ("packed")

@@ -291,8 +291,12 @@ T *at(void *base, size_t off)
 struct StageTimer {
     void **ev;
     hipStream_t st;
-    hipError_t begin(int s) { return ev ? hipEventRecord((hipEvent_t)ev[2 * s], st) : hipSuccess; }
-    hipError_t end(int s) { return ev ? hipEventRecord((hipEvent_t)ev[2 * s + 1], st) : hipSuccess; }
+    hipError_t begin(int s) { return rec(2 * s); }
+    hipError_t end(int s) { return rec(2 * s + 1); }
+    hipError_t rec(int i)
+    {   // (a NULL entry: that stage is not timed)
+        return ev && ev[i] ? hipEventRecord((hipEvent_t)ev[i], st) : hipSuccess;
+    }
 };
 
 }  // namespace

@@ -445,21 +445,30 @@ class HipEvents:
     """hipEvent_t handles for lamp_params.stage_events, via the HIP runtime.
 
     torch's Event objects create their handle lazily and only see torch's
-    streams; the library records these on the stream it was given.
+    streams; the library records these on the stream it was given.  The
+    events are timing-only (hipEventDisableSystemFence): a default event's
+    record writes back and invalidates the caches, which slows the stage
+    after it.  `only`: the stages to time (None: all); the other entries of
+    the array are NULL and not recorded.
     """
 
-    def __init__(self, n: int):
+    DISABLE_SYSTEM_FENCE = 0x20000000   # hipEventDisableSystemFence
+
+    def __init__(self, n: int, only=None):
         self._hip = ctypes.CDLL("libamdhip64.so")
-        self._hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self._hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p),
+                                                      ctypes.c_uint]
         self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                   ctypes.c_void_p]
         self._hip.hipEventQuery.argtypes = [ctypes.c_void_p]
         self._hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
         self.handles = []
-        for _ in range(n):
+        for i in range(n):
             h = ctypes.c_void_p()
-            if self._hip.hipEventCreate(ctypes.byref(h)) != 0:
-                raise RuntimeError("hipEventCreate failed")
+            if only is None or i // 2 in only:
+                if self._hip.hipEventCreateWithFlags(ctypes.byref(h),
+                                                     self.DISABLE_SYSTEM_FENCE) != 0:
+                    raise RuntimeError("hipEventCreateWithFlags failed")
             self.handles.append(h)
         self.array = (ctypes.c_void_p * n)(*[h.value for h in self.handles])
 
@@ -468,9 +477,11 @@ class HipEvents:
         return ctypes.cast(self.array, ctypes.c_void_p).value
 
     def recorded(self, i: int) -> bool:
-        return self._hip.hipEventQuery(self.handles[i]) == 0
+        return bool(self.handles[i].value) and self._hip.hipEventQuery(self.handles[i]) == 0
 
     def elapsed_ms(self, a: int, b: int) -> float:
+        if not (self.handles[a].value and self.handles[b].value):
+            raise RuntimeError("stage not timed (no event created for it)")
         t = ctypes.c_float()
         rc = self._hip.hipEventElapsedTime(ctypes.byref(t), self.handles[a], self.handles[b])
         if rc != 0:
@@ -479,5 +490,6 @@ class HipEvents:
 
     def close(self):
         for h in self.handles:
-            self._hip.hipEventDestroy(h)
+            if h.value:
+                self._hip.hipEventDestroy(h)
         self.handles = []

@@ -55,6 +55,39 @@ def test_reported_implementation(dev, S, mode, path, probs, want):
 
 
 # ---------------------------------------------------------------------------
+# Stage events: a NULL entry is skipped, the others are recorded
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("only", [None, "scores"])
+def test_stage_events_partial(dev, only):
+    import torch
+    from mixed_precision_attention_ps_amd import lamp
+    B, H, S, D = 1, 2, 256, 64
+    Q, K, V, _ = make_qkv(B, H, S, D, n_outlier=2, seed=7)
+    q, k, v = (torch.from_numpy(x).to(dev) for x in (Q, K, V))
+    out = torch.empty_like(q)
+    probs = torch.empty((B, H, S, S), device=dev)
+    sel = None if only is None else {lamp.STAGES.index(only)}
+    note(f"stage events only={only}")
+    ev = lamp.HipEvents(2 * lamp.LAMP_N_STAGES, only=sel)
+    try:
+        lamp.lamp_attention_fwd(q, k, v, causal=True, mu=4, tau=1e-2, mode="strict", out=out,
+                                probs=probs, want_stats=False, stage_events=ev)
+        torch.cuda.synchronize()
+        assert lamp.last_impl() == "strict_rows"
+        for name in ("scan", "exact", "scores", "select"):   # the stages strict_rows runs
+            si = lamp.STAGES.index(name)
+            timed = sel is None or si in sel
+            assert ev.recorded(2 * si) == timed and ev.recorded(2 * si + 1) == timed, name
+            if timed:
+                assert ev.elapsed_ms(2 * si, 2 * si + 1) >= 0.0
+            else:
+                with pytest.raises(RuntimeError):
+                    ev.elapsed_ms(2 * si, 2 * si + 1)
+    finally:
+        ev.close()
+
+
+# ---------------------------------------------------------------------------
 # Near ties: |c - tau| <= 2^-16 tau, counted over the call
 # ---------------------------------------------------------------------------
 def oracle_ties(r, tau, S, causal):
