@@ -232,6 +232,21 @@ def test_nonfinite_v_causal(dev, orc, S, mode, path):
     parity.assert_tol(g["row_kl"].reshape(B * H, S)[:, sl], r["kl"], np.abs(r["kl"]), "row KL")
 
 
+# Wider heads: the finish kernel at D = 96 and 128 splits the columns over
+# eight waves (each adds the non-finite values of its own column blocks back),
+# and the fused row kernel at D = 128 has its own P.V tile.
+@pytest.mark.parametrize("S,mode,D", [(1100, STRICT, 128), (1100, RANDOM, 96), (200, STRICT, 128)])
+def test_nonfinite_v_causal_wide_heads(dev, orc, S, mode, D):
+    Q, K, V = make_special(1, 2, S, D, kind="nonfinite_v", seed=S + mode + D)
+    tau = 1e-2
+    note(f"nonfinite V S={S} mode={mode} D={D}")
+    g = run_gpu(dev, Q, K, V, causal=True, mu=4, tau=tau, mode=mode, seed=7)
+    rows = None if S <= 256 else (S - 70, S)
+    with np.errstate(all="ignore"):
+        r = run_orc(orc, Q, K, V, causal=True, mu=4, tau=tau, mode=mode, seed=7, rows=rows)
+    check_nonfinite_out(g, r, Q, V, rows=rows)
+
+
 @pytest.mark.parametrize("S,nq", [(200, 4), (256, 1), (130, 16)])
 def test_nonfinite_v_decode(dev, orc, S, nq):
     import torch
