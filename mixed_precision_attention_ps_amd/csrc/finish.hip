@@ -29,14 +29,15 @@ struct FinishArgs {
 // partial carries at most 4 FP32 roundings (relative 2.4e-7 of its
 // sum_j p_j |v_jd|), so the total stays inside the 1e-6 bar, whereas FP32
 // accumulation over hundreds of keys drifts by ~10 ulp of a dominant term.
-// Each KS-key step: thread (row tid/4, keys KS/4 * (tid%4)..) forms KS/4
-// probabilities; the P and V tiles go to double-buffered LDS (one barrier per
+// Each KS-key step: thread (row tid / (4 WS), keys KPT (tid % (4 WS)) ..)
+// forms KPT = KS / (4 WS) probabilities; the P and V tiles go to
+// double-buffered LDS (one barrier per
 // step) while the next step's scores and V rows are already being loaded;
 // wave w multiplies rows 16(w%4)..16(w%4)+15 of P by V.  DV = 16 NB is the
 // padded head dimension (compile-time, so every MFMA and LDS index is
 // static).  WS: the work-group has 4 WS waves, wave w taking the column
-// blocks NB/WS * (w/4) .. of its rows (WS = 2 at D = 128: each wave then
-// holds half the P.V accumulators, and twice the waves fit on a SIMD).
+// blocks NB/WS * (w/4) .. of its rows (WS = 2 at D = 96 and 128: each wave
+// then holds half the P.V accumulators, and twice the waves fit on a SIMD).
 template <int NB, int KS, int WS>
 __global__ __launch_bounds__(kThreads * WS) void finish_kernel(FinishArgs a)
 {
