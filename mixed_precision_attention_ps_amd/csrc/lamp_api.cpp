@@ -1007,6 +1007,12 @@ static int run(const float *q, const float *k, const float *v, int B, int H, int
             LAMP_HIP_TRY(lamp::launch_strict_select(P, ymix, yref, mask, list, row_count, rs,
                                                     row_kl, row_kl_lowp, 0, st),
                          "select kernel launch");
+        } else if (S <= 1024) {
+            // counts and the random selection in one pass (one wave per row)
+            const uint64_t seed = p.seed;
+            LAMP_HIP_TRY(lamp::launch_strict_select(P, ymix, yref, mask, list, row_count, rs,
+                                                    row_kl, row_kl_lowp, 1, st, &seed),
+                         "count + random select launch");
         } else {
             LAMP_HIP_TRY(lamp::launch_strict_select(P, ymix, yref, nullptr, nullptr, row_count, rs,
                                                     row_kl, row_kl_lowp, 1, st),

@@ -107,10 +107,14 @@ struct RowStats {
 // row_kl (if non-null) and row_kl_lowp (if non-null) = KL(P_ref || P_lowp);
 // the recompute kernel updates the rows that have selections.  yref may be
 // null when neither KL is asked for (the reference sums are then skipped).
+// random_seed (count_only, rows of at most 1024 keys): the random control's
+// selection too, in the same pass (the row_count keys with the smallest
+// hashes, as launch_random_select takes them): mask words and list.
 hipError_t launch_strict_select(const Problem &p, const float *ylo, const float *yref,
                                 uint32_t *mask, uint32_t *list, uint32_t *row_count,
                                 RowStats *rs, double *row_kl, double *row_kl_lowp,
-                                int count_only, hipStream_t st);
+                                int count_only, hipStream_t st,
+                                const uint64_t *random_seed = nullptr);
 
 // Relaxed rule over rows of any length after score tiles that kept y^lo (in
 // y, replaced in place by y^mix), y^ref and the per-tile partials: mask words

@@ -25,9 +25,118 @@ struct SelectArgs {
     double *row_kl, *row_kl_lowp;
     int count_only;
     unsigned long long *n_band;
+    int random;       // (count_only, ONE) the random control's selection too
+    uint64_t seed;
 };
 
 constexpr int kSelChunk = 16;   // keys per lane held in registers (1024 per wave)
+
+// Random control inside the count pass, one wave per row of at most 1024
+// keys: the k valid keys with the smallest (SplitMix64(seed ^ linear index),
+// j), the same set as random_select_kernel's.  The hashes stay in registers
+// (key lane + 64 t in h[t]); a radix select over 8-bit digits, MSB first,
+// with a 256-bin histogram per wave in LDS (lane l owns bins 4l .. 4l + 3)
+// finds the k-th smallest hash T, stopping at the first digit whose bucket
+// is taken whole; then keys with hash < T (or at most the bucket's end) are
+// selected, and keys equal to T by increasing j until k.  Mask words for
+// every chunk before S and the list segment in key order.
+__device__ __forceinline__ void random_pick_row(const SelectArgs &a, uint32_t *hist, uint64_t r,
+                                                int n, uint32_t k, int lane)
+{
+    const int S = a.S;
+    const uint64_t base = r * (uint64_t)S;   // linear index of score (b, h, i, 0)
+    uint64_t h[kSelChunk];
+#pragma unroll
+    for (int t = 0; t < kSelChunk; ++t) {
+        const int j = lane + 64 * t;
+        h[t] = j < n ? splitmix64(a.seed ^ (base + (uint64_t)j)) : ~0ull;
+    }
+    uint64_t prefix = 0, pmask = 0, ub = 0;
+    uint32_t rank = k;
+    bool whole = false;
+    if (k > 0) {
+        for (int shift = 56; shift >= 0; shift -= 8) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                hist[4 * lane + q] = 0u;
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int t = 0; t < kSelChunk; ++t)
+                if (64 * t < n && lane + 64 * t < n && (h[t] & pmask) == prefix)
+                    atomicAdd(&hist[(uint32_t)(h[t] >> shift) & 255u], 1u);
+            __builtin_amdgcn_wave_barrier();
+            uint32_t c[4], local = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                c[q] = hist[4 * lane + q];
+                local += c[q];
+            }
+            uint32_t incl = local;   // inclusive prefix over the lanes
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const uint32_t y = __shfl_up(incl, o, 64);
+                if (lane >= o)
+                    incl += y;
+            }
+            // the digit holding the rank: cum < rank <= cum + count (the last
+            // digit if the rank exceeds the candidates, which the counts rule
+            // out)
+            uint32_t cum = incl - local, fdig = 0, fcum = 0, fcnt = 0;
+            bool found = false;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t d = 4u * (uint32_t)lane + (uint32_t)q;
+                if (!found && ((cum < rank && rank <= cum + c[q]) ||
+                               (d == 255u && rank > cum + c[q]))) {
+                    found = true;
+                    fdig = d;
+                    fcum = cum;
+                    fcnt = c[q];
+                }
+                cum += c[q];
+            }
+            const int src = __builtin_ctzll(ballot(found));
+            fdig = (uint32_t)__shfl(fdig, src, 64);
+            fcum = (uint32_t)__shfl(fcum, src, 64);
+            fcnt = (uint32_t)__shfl(fcnt, src, 64);
+            prefix |= (uint64_t)fdig << shift;
+            rank -= fcum;
+            pmask |= 255ull << shift;
+            __builtin_amdgcn_wave_barrier();   // the bins are read before the next clear
+            if (rank == fcnt) {   // uniform: the whole bucket is taken
+                whole = true;
+                ub = prefix | ((1ull << shift) - 1ull);
+                break;
+            }
+        }
+    }
+    const uint64_t T = prefix;
+    const uint64_t seg = row_segment(r, S, a.causal);
+    uint32_t eq_before = 0, total = 0;
+#pragma unroll
+    for (int t = 0; t < kSelChunk; ++t) {
+        if (64 * t < S) {   // wave-uniform
+            const int j = lane + 64 * t;
+            const bool valid = k > 0 && j < n;
+            const bool lt = valid && (whole ? h[t] <= ub : h[t] < T);
+            const bool eq = valid && !whole && h[t] == T;
+            const uint64_t tb = ballot(eq);
+            const bool sel = lt || (eq && eq_before + lanes_below(tb) < rank);
+            eq_before += (uint32_t)__popcll(tb);
+            const uint64_t b = ballot(sel);
+            if (a.mask) {
+                const int w = 2 * t;
+                if (lane == 0 && w < a.W)
+                    a.mask[r * (uint64_t)a.W + w] = (uint32_t)b;
+                if (lane == 1 && w + 1 < a.W)
+                    a.mask[r * (uint64_t)a.W + w + 1] = (uint32_t)(b >> 32);
+            }
+            if (sel && a.list)
+                a.list[seg + total + lanes_below(b)] = (uint32_t)j;
+            total += (uint32_t)__popcll(b);
+        }
+    }
+}
 constexpr int kSelBatch = 8;    // longer rows: 64-key chunks whose loads issue together
 
 // One wave per row; 4 rows per work-group.  ONE: the whole row fits one
@@ -39,6 +148,7 @@ template <bool ONE>
 __global__ __launch_bounds__(kThreads) void strict_select_kernel(SelectArgs a)
 {
     __shared__ double s_exp[64];   // 2^(k/64) for exp64
+    __shared__ uint32_t s_hist[ONE ? 4 : 1][ONE ? 256 : 1];   // per wave (random control)
     exp_table_fill(s_exp);
     __syncthreads();
     const int lane = threadIdx.x & 63;
@@ -230,14 +340,22 @@ __global__ __launch_bounds__(kThreads) void strict_select_kernel(SelectArgs a)
     if (lane == 0)
         a.row_count[r] = total;
     add_ties(a.n_band, ties);
+    if constexpr (ONE) {
+        if (a.random)
+            random_pick_row(a, s_hist[wave], r, n, total, lane);
+    }
 }
 
 hipError_t launch_strict_select(const Problem &p, const float *ylo, const float *yref,
                                 uint32_t *mask, uint32_t *list, uint32_t *row_count,
                                 RowStats *rs, double *row_kl, double *row_kl_lowp,
-                                int count_only, hipStream_t st)
+                                int count_only, hipStream_t st, const uint64_t *random_seed)
 {
+    if (random_seed && (!count_only || p.S > 64 * kSelChunk))
+        return hipErrorInvalidValue;
     SelectArgs a;
+    a.random = random_seed ? 1 : 0;
+    a.seed = random_seed ? *random_seed : 0;
     a.y = ylo;
     a.yref = yref;
     a.S = p.S;
