@@ -351,10 +351,11 @@ __global__ __launch_bounds__(kThreads) void decode_softmax_kernel(DecodeArgs a)
             ylo = a.ylo[row * S + j];
             yref = a.yref[row * S + j];
         }
-        const double E = valid ? exp64((double)ylo - (double)mt, s_exp) : 0.0;
+        const double E = valid ? exp64_crit((double)ylo - (double)mt, s_exp) : 0.0;
         const double crit = 2.0 * E * fabs((double)ylo);
         const bool sel = valid && crit > a.tau;
-        ties += (uint32_t)__popcll(ballot(valid && near_tie(crit, a.tau)));
+        if (a.n_band)   // near ties are counted only for a summary
+            ties += (uint32_t)__popcll(ballot(valid && near_tie(crit, a.tau)));
         const float ymix = sel ? yref : ylo;
         const uint64_t b = ballot(sel);
         if (a.mask) {
@@ -367,9 +368,9 @@ __global__ __launch_bounds__(kThreads) void decode_softmax_kernel(DecodeArgs a)
         const float M_mix = wave_max(valid ? ymix : -INFINITY);
         const float M_ref = wave_max(valid ? yref : -INFINITY);
         const float M_lo = wave_max(valid ? ylo : -INFINITY);
-        const double em = valid ? exp64_nonpos((double)ymix - (double)M_mix, s_exp) : 0.0;
-        const double er = valid ? exp64_nonpos((double)yref - (double)M_ref, s_exp) : 0.0;
-        const double el = valid ? exp64_nonpos((double)ylo - (double)M_lo, s_exp) : 0.0;
+        const double em = valid ? exp64_sum_nonpos((double)ymix - (double)M_mix, s_exp) : 0.0;
+        const double er = valid ? exp64_sum_nonpos((double)yref - (double)M_ref, s_exp) : 0.0;
+        const double el = valid ? exp64_sum_nonpos((double)ylo - (double)M_lo, s_exp) : 0.0;
         s_p[wave][t][lane] = (float)em;
         const double l_mix = wave_sum(em);
         const double l_ref = wave_sum(er);
@@ -509,9 +510,9 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(CombineArgs a)
         const DecPartial &p = P(c);
         if (p.m_mix == -INFINITY)
             continue;   // no valid key in this block
-        const double fm = exp64_nonpos((double)p.m_mix - (double)Mm, s_exp);
-        const double fr = exp64_nonpos((double)p.m_ref - (double)Mr, s_exp);
-        const double fl = exp64_nonpos((double)p.m_lo - (double)Ml, s_exp);
+        const double fm = exp64_sum_nonpos((double)p.m_mix - (double)Mm, s_exp);
+        const double fr = exp64_sum_nonpos((double)p.m_ref - (double)Mr, s_exp);
+        const double fl = exp64_sum_nonpos((double)p.m_lo - (double)Ml, s_exp);
         sum[0] += p.l_mix * fm;
         sum[1] += p.l_ref * fr;
         sum[2] += p.a * fr;
@@ -547,7 +548,7 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(CombineArgs a)
             for (int c = tid; c < nc; c += kThreads) {
                 const float m = P(c0 + c).m_mix;
                 s_f[c] = m == -INFINITY ? 0.0f
-                                        : (float)exp64_nonpos((double)m - (double)Mm, s_exp);
+                                        : (float)exp64_sum_nonpos((double)m - (double)Mm, s_exp);
             }
             __syncthreads();
             if (d < a.D) {

@@ -461,7 +461,7 @@ int run_decode(const float *q, const float *k, const float *v, int B, int H, int
     P.mu = mu;
     P.tau = tau;
     P.ps_block = p.ps_block;
-    P.n_band = &dstats->n_tie_band;
+    P.n_band = want_stats ? &dstats->n_tie_band : nullptr;
     lamp::DecodeBuffers b;
     b.ylo = p.scores_mix ? p.scores_mix : at<float>(ws, L.ylo);
     b.yref = p.scores_ref ? p.scores_ref : at<float>(ws, L.yref);
