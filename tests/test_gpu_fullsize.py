@@ -64,28 +64,29 @@ def inputs(name):
 
 
 def run_case(dev, orc, name, *, mode, mu, tau, heads, row_ranges, want_probs=True,
-             expect_rate=None, relaxed_path=0):
+             expect_rate=None, relaxed_path=0, causal=None):
     import torch
     from mixed_precision_attention_ps_amd import lamp
     w = WORKLOADS[name]
+    causal = w.causal if causal is None else causal
     Q, K, V = inputs(name)
     B, H, S, D = Q.shape
     W = (S + 31) // 32
     BH = B * H
     note(f"full-size {name} {MODE_NAME[mode]} mu={mu} tau={tau} probs={want_probs} "
-         f"relaxed_path={relaxed_path}")
+         f"relaxed_path={relaxed_path} causal={causal}")
     q, k, v = (torch.from_numpy(x).to(dev) for x in (Q, K, V))
     probs = torch.full((B, H, S, S), -7.0, device=dev) if want_probs else None
     mask = torch.full((B, H, S, W), -1, dtype=torch.int32, device=dev)
     row_kl = torch.zeros((B, H, S), dtype=torch.float64, device=dev)
     row_kl_lowp = torch.zeros((B, H, S), dtype=torch.float64, device=dev)
     row_count = torch.zeros((B, H, S), dtype=torch.int32, device=dev)
-    out, st = lamp.lamp_attention_fwd(q, k, v, causal=w.causal, mu=mu, tau=tau, mode=mode,
+    out, st = lamp.lamp_attention_fwd(q, k, v, causal=causal, mu=mu, tau=tau, mode=mode,
                                       probs=probs, recompute_mask=mask, row_kl=row_kl,
                                       row_kl_lowp=row_kl_lowp, row_count=row_count,
                                       want_stats=True, relaxed_path=relaxed_path)
     torch.cuda.synchronize()
-    n_valid = w.n_valid
+    n_valid = w.n_valid if causal == w.causal else BH * S * S
     assert st["n_valid"] == n_valid
     counts = row_count.view(BH, S)
     assert st["n_selected"] == int(counts.sum(dtype=torch.int64).item())
@@ -97,7 +98,7 @@ def run_case(dev, orc, name, *, mode, mu, tau, heads, row_ranges, want_probs=Tru
         ii = torch.arange(0, S, max(1, S // 64), device=dev)
         rs = pv[:, ii, :].double().sum(-1)
         assert torch.allclose(rs, torch.ones_like(rs), rtol=0, atol=1e-5), "probability rows"
-        if w.causal:
+        if causal:
             jj = torch.arange(S, device=dev)
             upper = jj[None, :] > ii[:, None]
             assert (pv[:, ii, :][:, upper] == 0).all(), "masked probabilities"
@@ -116,7 +117,7 @@ def run_case(dev, orc, name, *, mode, mu, tau, heads, row_ranges, want_probs=Tru
         if want_probs:
             g["probs"] = probs.view(BH, S, S)[hs, rb:re_].cpu().numpy()
         note(f"oracle {name} {MODE_NAME[mode]} heads={heads} rows={rows}")
-        r = orc.lamp_heads(Q, K, V, causal=w.causal, mu=mu, tau=tau, mode=mode, heads=heads,
+        r = orc.lamp_heads(Q, K, V, causal=causal, mu=mu, tau=tau, mode=mode, heads=heads,
                            rows=rows)
         ties = parity.assert_mask(g["mask"], r["mask"], r["crit"], tau, S)
         assert (g["count"] == r["count"]).all() or ties > 0, "row counts"
@@ -154,6 +155,15 @@ def test_gpt2_xl_relaxed(dev, orc, path):
     tau = tau_for(XL, "relaxed", 4, 0.016)
     run_case(dev, orc, XL, mode=RELAXED, mu=4, tau=tau, heads=XL_HEADS, row_ranges=[(0, 1024)],
              expect_rate=0.016, relaxed_path=path)
+
+
+# The same layer without the causal mask (every row sees all 1024 keys): the
+# non-causal orders of the score tiles and row groups at full size.
+@pytest.mark.parametrize("mode,path", [(STRICT, 0), (RELAXED, 1), (RELAXED, 2)])
+def test_gpt2_xl_noncausal(dev, orc, mode, path):
+    tau = tau_for(XL, MODE_NAME[mode], 4, 0.016)
+    run_case(dev, orc, XL, mode=mode, mu=4, tau=tau, heads=[0, 199], row_ranges=[(0, 1024)],
+             relaxed_path=path, causal=False)
 
 
 def test_gpt2_xl_random_control(dev, orc):
