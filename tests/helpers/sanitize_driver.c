@@ -35,6 +35,8 @@ int64_t check_products(uint64_t seed, int64_t n, int mu, int emin, int emax, rn_
                        int64_t *traps);
 int64_t check_sums_exhaustive(int mu, int emin, int emax, rn_fn rn);
 int64_t check_sums_random(uint64_t seed, int64_t n, int mu, int emin, int emax, rn_fn rn);
+double emu_exp64_short(double x, int deg);
+double max_rel_error(int deg, uint64_t seed, int64_t n, double lo, double hi);
 
 static uint64_t st = 0x9e3779b97f4a7c15ull;
 static double unif(void)   /* xorshift64*, [0, 1) */
@@ -164,6 +166,15 @@ static int helper_cases(void)
     (void)check_products(5u, 20000, 4, -30, 30, orc_rn_mu, &traps);
     (void)check_sums_exhaustive(4, -3, 3, orc_rn_mu);
     (void)check_sums_random(6u, 20000, 7, -20, 20, orc_rn_mu);
+    /* the shortened exponentials over their range and at the special values
+       (the table index and the scale of a clamped or NaN argument) */
+    for (int deg = 3; deg <= 4; ++deg) {
+        bad |= !(max_rel_error(deg, 11u, 20000, -745.0, 709.0) < 1e-10);
+        const double sp[] = {0.0, -0.0, 1e-300, -1e-300, -745.5, 709.9, 1e300, -1e300,
+                             INFINITY, -INFINITY, NAN};
+        for (unsigned u = 0; u < sizeof sp / sizeof sp[0]; ++u)
+            (void)emu_exp64_short(sp[u], deg);
+    }
     return bad;
 }
 

@@ -19,7 +19,8 @@ def test_oracle_and_helpers_clean_under_asan_ubsan(tmp_path):
             os.path.join(ROOT, "oracle", "lamp_oracle.c"),
             os.path.join(ROOT, "oracle", "lamp_mlp_oracle.c"),
             os.path.join(ROOT, "tests", "helpers", "rn_bits_check.c"),
-            os.path.join(ROOT, "tests", "helpers", "fast_ps_emul.c")]
+            os.path.join(ROOT, "tests", "helpers", "fast_ps_emul.c"),
+            os.path.join(ROOT, "tests", "helpers", "exp64_emul.c")]
     cmd = ["gcc", "-std=c11", "-O1", "-g", "-fno-omit-frame-pointer", "-ffp-contract=off",
            "-fno-fast-math", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
            "-o", str(exe), *srcs, "-lm"]
