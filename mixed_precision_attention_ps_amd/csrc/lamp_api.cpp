@@ -971,20 +971,27 @@ static int run(const float *q, const float *k, const float *v, int B, int H, int
         float *yref = p.scores_ref ? p.scores_ref : at<float>(ws, L.yref);
         auto *part = at<lamp::RefPartial>(ws, L.part);
         LAMP_HIP_TRY(tm.begin(LAMP_STAGE_EXACT), "hipEventRecord");
+        // causal, probabilities asked for: the score tiles write their zeros
+        // above the diagonal tiles (probs never aliases y^ref or the
+        // partials; where it is y^lo's buffer those entries are not scores).
+        // Without probs no zero tail is written at all: P.V reads no key past
+        // a group's diagonal block.
+        float *pzero = P.causal && probs ? pbuf : nullptr;
         LAMP_HIP_TRY(lamp::launch_ps_scores(P, unsafe, ybuf, yref, part,
-                                            n_exact, false, st),
+                                            n_exact, false, st, pzero),
                      "score kernel launch");
         LAMP_HIP_TRY(tm.end(LAMP_STAGE_EXACT), "hipEventRecord");
         LAMP_HIP_TRY(tm.begin(LAMP_STAGE_SCORES), "hipEventRecord");
         LAMP_HIP_TRY(lamp::launch_ps_scores(P, unsafe, ybuf, yref, part,
-                                            n_exact, true, st),
+                                            n_exact, true, st, pzero),
                      "score kernel launch");
         LAMP_HIP_TRY(tm.end(LAMP_STAGE_SCORES), "hipEventRecord");
         const bool kl = need.rowkl;
         LAMP_HIP_TRY(tm.begin(LAMP_STAGE_SELECT), "hipEventRecord");
         LAMP_HIP_TRY(lamp::launch_rows_pv(P, ybuf, yref, part, mask, row_count, pbuf,
                                           p.scores_mix, out, kl ? row_kl : nullptr,
-                                          kl ? row_kl_lowp : nullptr, mode == LAMP_RELAXED, st),
+                                          kl ? row_kl_lowp : nullptr, mode == LAMP_RELAXED, st,
+                                          pzero != nullptr || probs == nullptr),
                      "row kernel launch");
         LAMP_HIP_TRY(tm.end(LAMP_STAGE_SELECT), "hipEventRecord");
     } else {

@@ -59,10 +59,14 @@ struct RefPartial {
 // PS(mu) and FP32 scores of every valid pair into dense [BH, S, S] buffers
 // (either may be null), and optionally the per-row, per-tile RefPartial
 // [BH*S, tiles].  fast = true: the tiles on the FP32 fast path (launches
-// nothing if mu > 10); fast = false: every other tile.
+// nothing if mu > 10); fast = false: every other tile.  pzero (causal only,
+// may be null): a [BH, S, S] buffer whose entries above the causal diagonal
+// tiles (rows of 64-key block a, keys of blocks b > a) are set to 0, each by
+// the work-group of the mirrored tile (b, a): the probabilities' zero tails,
+// written beside the ALU-bound score work instead of by the row pass.
 hipError_t launch_ps_scores(const Problem &p, const uint8_t *unsafe, float *ylo, float *yref,
                             RefPartial *part, unsigned long long *exact_tiles, bool fast,
-                            hipStream_t st);
+                            hipStream_t st, float *pzero = nullptr);
 
 // Softmax sums of one row after the fused row pass, for the row KLs: L =
 // sum exp(y^lo - m), the log-sum-exp of y^mix = mix_base + log(mix_l), and
@@ -77,7 +81,10 @@ struct RowKL {
 // statistics, the strict criterion (relaxed = false) or the relaxed one
 // (relaxed = true: needs part, for the 64-key block maxima), mask words,
 // compaction of the selected keys, their FP32 recompute, the corrected
-// softmax, probabilities into pbuf (full rows, zeros past the valid keys),
+// softmax, probabilities into pbuf (full rows, zeros past the valid keys;
+// tail_done: the zeros past a row's last valid 64-key block are not
+// written, because the score tiles wrote them through pzero or because pbuf
+// is scratch whose tails nothing reads),
 // y^mix (optional), counts, the row KLs (row_kl / row_kl_lowp, optional; need
 // part), then out = P.V.  ylo may alias pbuf or ymix_out (rows are read
 // before written).  yref: the FP32 reference scores [BH, S, S] when the
@@ -87,7 +94,8 @@ struct RowKL {
 hipError_t launch_rows_pv(const Problem &p, const float *ylo, const float *yref,
                           const RefPartial *part, uint32_t *mask, uint32_t *row_count,
                           float *pbuf, float *ymix_out, float *out, double *row_kl,
-                          double *row_kl_lowp, bool relaxed, hipStream_t st);
+                          double *row_kl_lowp, bool relaxed, hipStream_t st,
+                          bool tail_done = false);
 
 // Per-row statistics of the strict / random path (double sums, float maxima).
 struct RowStats {

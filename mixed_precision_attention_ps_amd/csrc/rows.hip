@@ -46,6 +46,7 @@ struct RowsArgs {
     float *pbuf, *ymix_out, *out;
     double *row_kl, *row_kl_lowp;   // null: not asked for
     int kl;                         // a row KL is asked for (needs part)
+    int tail_done;                  // zeros past the valid blocks already written
     unsigned long long *n_band;
 };
 
@@ -354,6 +355,8 @@ __device__ __forceinline__ void row_pass(Args &a, RowsSmem<DV, QN> &sm, const do
     // The row's probabilities past its valid chunks are 0: 16-byte stores
     // over keys 64 nch .. S - 1 (4-byte ones when S is not a multiple of 4)
     auto zero_tail = [&]() {
+        if (a.tail_done)
+            return;
         float *pr = a.pbuf + r * (uint64_t)S;
         if ((S & 3) == 0) {
             for (int j = 64 * nch + 4 * lane; j < S; j += 256)
@@ -705,7 +708,7 @@ __attribute__((amdgpu_waves_per_eu(DV == 64 ? 5 : (DV == 128 ? 3 : 2)))) void ro
 hipError_t launch_rows_pv(const Problem &p, const float *ylo, const float *yref,
                           const RefPartial *part, uint32_t *mask, uint32_t *row_count,
                           float *pbuf, float *ymix_out, float *out, double *row_kl,
-                          double *row_kl_lowp, bool relaxed, hipStream_t st)
+                          double *row_kl_lowp, bool relaxed, hipStream_t st, bool tail_done)
 {
     const bool kl = row_kl || row_kl_lowp;
     if (p.S > 64 * kRowChunk || (ymix_out && (ymix_out != ylo || pbuf == ylo)) ||
@@ -735,6 +738,7 @@ hipError_t launch_rows_pv(const Problem &p, const float *ylo, const float *yref,
     a.row_kl = row_kl;
     a.row_kl_lowp = row_kl_lowp;
     a.kl = kl ? 1 : 0;
+    a.tail_done = tail_done ? 1 : 0;
     a.n_band = p.n_band;
     const uint64_t grid = (uint64_t)p.BH * a.groups;
     if (grid > 0x7fffffffULL)

@@ -92,6 +92,7 @@ struct ScoreArgs {
     PsConst pc;
     const uint8_t *unsafe_q, *unsafe_k;
     float *ylo, *yref;
+    float *pzero;        // causal: zero the mirrored upper tile (may be null)
     RefPartial *part;
     int ref_sums;        // part: L and B too (else only the maxima; L = B = 0)
     unsigned long long *exact_tiles;
@@ -192,6 +193,31 @@ __device__ __forceinline__ void score_tile_store(TileSmem &sm, const double *s_e
     }
 }
 
+// Zeros over rows of 64-row block rb and keys of 64-key block kb (kb > rb,
+// so every key lies past every row: the probabilities there are 0 under the
+// causal mask).  Rows of a block below the last are whole; keys stop at S.
+// 16-byte stores when S is a multiple of 4 (a float4 then lies wholly
+// inside or past the row), else 4-byte ones.
+__device__ __forceinline__ void zero_mirror_tile(float *pz, int S, int bh, int rb, int kb)
+{
+    float *base = pz + ((size_t)bh * S + (size_t)rb * kTile) * S + (size_t)kb * kTile;
+    const int nk = min(kTile, S - kb * kTile);
+    if ((S & 3) == 0) {
+        for (int e = threadIdx.x; e < kTile * (kTile / 4); e += kThreads) {
+            const int r = e / (kTile / 4), c = 4 * (e % (kTile / 4));
+            if (c < nk)
+                *reinterpret_cast<float4 *>(base + (size_t)r * S + c) =
+                    make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    } else {
+        for (int e = threadIdx.x; e < kTile * kTile; e += kThreads) {
+            const int r = e / kTile, c = e % kTile;
+            if (c < nk)
+                base[(size_t)r * S + c] = 0.0f;
+        }
+    }
+}
+
 #ifndef LAMP_SCORES_XCD
 #define LAMP_SCORES_XCD 1
 #endif
@@ -251,9 +277,14 @@ __global__ __launch_bounds__(kThreads) void ps_scores_kernel(ScoreArgs a)
     }
     exp_table_fill(s_exp);
     __syncthreads();
+    // the mirrored zero tiles: every tile's work-group in the fast kernel,
+    // or in the generic one when no fast kernel runs (mu > 10)
+    const bool zero_fill = a.pzero && a.causal && (FAST_KERNEL || a.pc.mu > 10);
     for (long long g = blockIdx.x; g < a.n_tiles; g += FAST_KERNEL ? a.n_tiles : gridDim.x) {
         int bh, ti, tj;
         const int path = tile_path(g, bh, ti, tj);
+        if (zero_fill && tj < ti)
+            zero_mirror_tile(a.pzero, a.S, bh, tj, ti);
         if (FAST_KERNEL) {
             if (path == PATH_FAST)
                 score_tile_store<PATH_FAST, P>(sm, s_exp, a, bh, ti, tj);
@@ -272,7 +303,7 @@ constexpr long long kGenericGridBeside = 512;   // ... when the fast kernel runs
 
 hipError_t launch_ps_scores(const Problem &p, const uint8_t *unsafe, float *ylo, float *yref,
                             RefPartial *part, unsigned long long *exact_tiles, bool fast,
-                            hipStream_t st)
+                            hipStream_t st, float *pzero)
 {
     ScoreArgs a;
     a.q = p.q;
@@ -287,6 +318,7 @@ hipError_t launch_ps_scores(const Problem &p, const uint8_t *unsafe, float *ylo,
     a.unsafe_k = unsafe + (size_t)p.BH * p.tiles;
     a.ylo = ylo;
     a.yref = yref;
+    a.pzero = pzero;
     a.part = part;
     a.ref_sums = p.ref_sums ? 1 : 0;
     a.exact_tiles = exact_tiles;
