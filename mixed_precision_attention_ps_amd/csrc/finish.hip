@@ -21,6 +21,7 @@ struct FinishArgs {
     float *probs, *out;
     double *row_kl;
     int S, D, causal, blocks_per_head;
+    int tail_done;   // the zeros past the block's last key are already written
 };
 
 // probs_j = exp(y^mix_j - lse_mix) on the valid keys (0 elsewhere), and
@@ -241,7 +242,7 @@ __global__ __launch_bounds__(kThreads * WS) void finish_kernel(FinishArgs a)
     // Keys past the causal limit of every row in the block: probabilities 0.
     // Wave w clears rows 16w..16w+15, each row's tail in contiguous 1 KB
     // stores (64 lanes x 16 bytes).
-    if (a.probs) {
+    if (a.probs && !a.tail_done) {
         const int z0 = nsteps * kFinKeys;
         for (int rr = 0; rr < kRowsPerWave; ++rr) {
             const int iz = row0 + wave * kRowsPerWave + rr;
@@ -315,7 +316,7 @@ static hipError_t launch_finish_kernel(const FinishArgs &a, const Problem &p, hi
 }
 
 hipError_t launch_finish(const Problem &p, const float *ymix, const RowStats *rs, float *probs,
-                         float *out, double *row_kl, hipStream_t st)
+                         float *out, double *row_kl, hipStream_t st, bool tail_done)
 {
     FinishArgs a;
     a.ymix = ymix;
@@ -328,6 +329,9 @@ hipError_t launch_finish(const Problem &p, const float *ymix, const RowStats *rs
     a.D = p.D;
     a.causal = p.causal;
     a.blocks_per_head = (p.S + kFinRows - 1) / kFinRows;
+    // (the tail starts at the block's last row + 1 rounded up to a key step,
+    // which is the next 64-key block: the score tiles' mirrored zero tiles)
+    a.tail_done = tail_done && p.causal && kFinRows == kTile ? 1 : 0;
     return launch_finish_kernel(a, p, st);
 }
 

@@ -923,14 +923,17 @@ static int run(const float *q, const float *k, const float *v, int B, int H, int
         float *yref = p.scores_ref ? p.scores_ref : at<float>(ws, L.yref);
         auto *part = at<lamp::RefPartial>(ws, L.part);
         auto *rs = at<lamp::RowStats>(ws, L.rowstats);
+        // causal, probabilities asked for: their zeros above the diagonal
+        // tiles come from the score tiles
+        float *pzero = P.causal && probs ? probs : nullptr;
         LAMP_HIP_TRY(tm.begin(LAMP_STAGE_EXACT), "hipEventRecord");
         LAMP_HIP_TRY(lamp::launch_ps_scores(P, unsafe, ymix, yref, part,
-                                            n_exact, false, st),
+                                            n_exact, false, st, pzero),
                      "score kernel launch");
         LAMP_HIP_TRY(tm.end(LAMP_STAGE_EXACT), "hipEventRecord");
         LAMP_HIP_TRY(tm.begin(LAMP_STAGE_SCORES), "hipEventRecord");
         LAMP_HIP_TRY(lamp::launch_ps_scores(P, unsafe, ymix, yref, part,
-                                            n_exact, true, st),
+                                            n_exact, true, st, pzero),
                      "score kernel launch");
         LAMP_HIP_TRY(tm.end(LAMP_STAGE_SCORES), "hipEventRecord");
         LAMP_HIP_TRY(tm.begin(LAMP_STAGE_SELECT), "hipEventRecord");
@@ -939,27 +942,32 @@ static int run(const float *q, const float *k, const float *v, int B, int H, int
                      "relaxed select launch");
         LAMP_HIP_TRY(tm.end(LAMP_STAGE_SELECT), "hipEventRecord");
         LAMP_HIP_TRY(tm.begin(LAMP_STAGE_FINISH), "hipEventRecord");
-        LAMP_HIP_TRY(lamp::launch_finish(P, ymix, rs, probs, out, row_kl, st), "finish launch");
+        LAMP_HIP_TRY(lamp::launch_finish(P, ymix, rs, probs, out, row_kl, st, pzero != nullptr),
+                     "finish launch");
         LAMP_HIP_TRY(tm.end(LAMP_STAGE_FINISH), "hipEventRecord");
     } else if (mode == LAMP_RELAXED && !need.fused) {
         float *ymix_raw = p.scores_mix ? p.scores_mix : probs;
         float *row_m = at<float>(ws, L.row_m);
         double *row_l = at<double>(ws, L.row_l);
+        // causal, probabilities asked for: each query block's zero tails come
+        // from the fused kernel
+        float *pzero = P.causal && probs ? probs : nullptr;
         LAMP_HIP_TRY(tm.begin(LAMP_STAGE_EXACT), "hipEventRecord");
         LAMP_HIP_TRY(lamp::launch_relaxed(P, unsafe, out, mask, row_count, row_kl, row_kl_lowp,
                                           ymix_raw, p.scores_ref, row_m, row_l,
-                                          n_exact, false, st),
+                                          n_exact, false, st, pzero),
                      "relaxed kernel launch");
         LAMP_HIP_TRY(tm.end(LAMP_STAGE_EXACT), "hipEventRecord");
         LAMP_HIP_TRY(tm.begin(LAMP_STAGE_SCORES), "hipEventRecord");
         LAMP_HIP_TRY(lamp::launch_relaxed(P, unsafe, out, mask, row_count, row_kl, row_kl_lowp,
                                           ymix_raw, p.scores_ref, row_m, row_l,
-                                          n_exact, true, st),
+                                          n_exact, true, st, pzero),
                      "relaxed kernel launch");
         LAMP_HIP_TRY(tm.end(LAMP_STAGE_SCORES), "hipEventRecord");
         if (probs) {
             LAMP_HIP_TRY(tm.begin(LAMP_STAGE_FINISH), "hipEventRecord");
-            LAMP_HIP_TRY(lamp::launch_normalise(P, ymix_raw, row_m, row_l, probs, st),
+            LAMP_HIP_TRY(lamp::launch_normalise(P, ymix_raw, row_m, row_l, probs, st,
+                                                pzero != nullptr),
                          "normalise launch");
             LAMP_HIP_TRY(tm.end(LAMP_STAGE_FINISH), "hipEventRecord");
         }
@@ -998,14 +1006,17 @@ static int run(const float *q, const float *k, const float *v, int B, int H, int
         float *ymix = p.scores_mix ? p.scores_mix : (probs ? probs : at<float>(ws, L.ymix));
         float *yref = p.scores_ref ? p.scores_ref : at<float>(ws, L.yref);
         uint32_t *list = at<uint32_t>(ws, L.list);
+        // causal, probabilities asked for: their zeros above the diagonal
+        // tiles come from the score tiles
+        float *pzero = P.causal && probs ? probs : nullptr;
         LAMP_HIP_TRY(tm.begin(LAMP_STAGE_EXACT), "hipEventRecord");
         LAMP_HIP_TRY(lamp::launch_ps_scores(P, unsafe, ymix, yref, nullptr,
-                                            n_exact, false, st),
+                                            n_exact, false, st, pzero),
                      "score kernel launch");
         LAMP_HIP_TRY(tm.end(LAMP_STAGE_EXACT), "hipEventRecord");
         LAMP_HIP_TRY(tm.begin(LAMP_STAGE_SCORES), "hipEventRecord");
         LAMP_HIP_TRY(lamp::launch_ps_scores(P, unsafe, ymix, yref, nullptr,
-                                            n_exact, true, st),
+                                            n_exact, true, st, pzero),
                      "score kernel launch");
         LAMP_HIP_TRY(tm.end(LAMP_STAGE_SCORES), "hipEventRecord");
         LAMP_HIP_TRY(tm.begin(LAMP_STAGE_SELECT), "hipEventRecord");
@@ -1033,7 +1044,8 @@ static int run(const float *q, const float *k, const float *v, int B, int H, int
                      "recompute launch");
         LAMP_HIP_TRY(tm.end(LAMP_STAGE_RECOMPUTE), "hipEventRecord");
         LAMP_HIP_TRY(tm.begin(LAMP_STAGE_FINISH), "hipEventRecord");
-        LAMP_HIP_TRY(lamp::launch_finish(P, ymix, rs, probs, out, row_kl, st), "finish launch");
+        LAMP_HIP_TRY(lamp::launch_finish(P, ymix, rs, probs, out, row_kl, st, pzero != nullptr),
+                     "finish launch");
         LAMP_HIP_TRY(tm.end(LAMP_STAGE_FINISH), "hipEventRecord");
     }
 

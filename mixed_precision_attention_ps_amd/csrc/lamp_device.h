@@ -438,6 +438,34 @@ __device__ __forceinline__ float group16_max(float v) { return row16_reduce(v, O
 __device__ __forceinline__ double group16_sum(double v) { return row16_reduce(v, OpAdd{}); }
 __device__ __forceinline__ uint32_t group16_sum_u(uint32_t v) { return row16_reduce(v, OpAdd{}); }
 
+// Zeros over rows row0 .. row0 + nrows - 1, keys k0 .. k1 - 1 of head bh of a
+// [BH, S, S] buffer, by the whole work-group (nt threads).  Under a causal
+// mask these are probabilities past every row's last key when k0 is past the
+// last row: the zero tails of the rows, written by a kernel whose own work
+// is ALU-bound instead of by the memory-bound one after it.  16-byte stores
+// when S and k0 are multiples of 4 (a float4 then lies wholly inside or past
+// the range), else 4-byte ones.
+__device__ __forceinline__ void zero_block(float *pz, int S, int bh, int row0, int nrows, int k0,
+                                           int k1, int nt)
+{
+    float *base = pz + ((size_t)bh * S + (size_t)row0) * S;
+    const int w = k1 - k0;
+    if (w <= 0 || nrows <= 0)
+        return;
+    if ((S & 3) == 0 && (k0 & 3) == 0) {
+        const int w4 = (w + 3) / 4;
+        for (int e = threadIdx.x; e < nrows * w4; e += nt) {
+            const int r = e / w4, c = k0 + 4 * (e % w4);
+            *reinterpret_cast<float4 *>(base + (size_t)r * S + c) = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    } else {
+        for (int e = threadIdx.x; e < nrows * w; e += nt) {
+            const int r = e / w, c = k0 + e % w;
+            base[(size_t)r * S + c] = 0.0f;
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Buffer (range-checked) access to one row: a buffer resource over `bytes`
 // bytes at a wave-uniform base; lanes whose byte offset falls outside the

@@ -148,22 +148,30 @@ hipError_t launch_recompute(const Problem &p, const uint32_t *list, const uint32
 
 // Final softmax (probs may alias ymix), P.V on MFMA; rows flagged full_pass
 // get lse_mix (and row_kl) from a pass over the row here.
+// tail_done (causal): the zeros past each row block's last key (the next
+// 64-key block on) are already in probs, from the score tiles' pzero.
 hipError_t launch_finish(const Problem &p, const float *ymix, const RowStats *rs, float *probs,
-                         float *out, double *row_kl, hipStream_t st);
+                         float *out, double *row_kl, hipStream_t st, bool tail_done = false);
 
 // Relaxed fused one-pass kernel.  ymix_raw: if non-null, y^mix of valid
 // entries is written there (for the probs pass / inspection); row_m / row_l:
 // per-row final max and sum of the online softmax (for the probs pass).
 // fast = true: query blocks whose every visited tile is on the FP32 fast
-// path; fast = false: the other query blocks.
+// path; fast = false: the other query blocks.  pzero (causal, may be null):
+// each query block's work-group also writes the zeros of its rows past its
+// own 64-key block into this [BH, S, S] buffer (the probabilities).
 hipError_t launch_relaxed(const Problem &p, const uint8_t *unsafe, float *out, uint32_t *mask,
                           uint32_t *row_count, double *row_kl, double *row_kl_lowp,
                           float *ymix_raw, float *yref_out, float *row_m, double *row_l,
-                          unsigned long long *exact_tiles, bool fast, hipStream_t st);
+                          unsigned long long *exact_tiles, bool fast, hipStream_t st,
+                          float *pzero = nullptr);
 
-// probs[r][j] = exp(ymix[r][j] - row_m[r]) / row_l[r] on valid keys, 0 elsewhere.
+// probs[r][j] = exp(ymix[r][j] - row_m[r]) / row_l[r] on valid keys, 0 elsewhere
+// (tail_done, causal: 0 only up to the end of the row's 64-key block; the
+// rest was written by the fused kernel through pzero).
 hipError_t launch_normalise(const Problem &p, const float *ymix, const float *row_m,
-                            const double *row_l, float *probs, hipStream_t st);
+                            const double *row_l, float *probs, hipStream_t st,
+                            bool tail_done = false);
 
 // Decode shapes (relaxed rule): nq query rows per head against S keys.
 struct DecodeProblem {

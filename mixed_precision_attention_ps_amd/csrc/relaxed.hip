@@ -35,6 +35,7 @@ struct RelaxedArgs {
     uint32_t *mask, *row_count;
     double *row_kl, *row_kl_lowp;
     float *ymix_raw, *yref_out, *row_m;
+    float *pzero;   // causal: the block's probability zero tails (may be null)
     double *row_l;
     unsigned long long *exact_tiles;
     unsigned long long *n_band;
@@ -120,6 +121,11 @@ void relaxed_kernel(RelaxedArgs a)
         if (all_fast != FAST_KERNEL)
             return;
     }
+    // the zero tails of this block's probability rows (keys of the blocks
+    // past it), written here, beside the ALU-bound tile work, rather than
+    // by the memory-bound probabilities pass
+    if (a.pzero && a.causal)
+        zero_block(a.pzero, S, bh, row0, min(kTile, S - row0), row0 + kTile, S, kThreads);
 
     if (tx == 0)
         for (int r = 0; r < 4; ++r) {
@@ -416,7 +422,8 @@ void relaxed_kernel(RelaxedArgs a)
 hipError_t launch_relaxed(const Problem &p, const uint8_t *unsafe, float *out, uint32_t *mask,
                           uint32_t *row_count, double *row_kl, double *row_kl_lowp,
                           float *ymix_raw, float *yref_out, float *row_m, double *row_l,
-                          unsigned long long *exact_tiles, bool fast, hipStream_t st)
+                          unsigned long long *exact_tiles, bool fast, hipStream_t st,
+                          float *pzero)
 {
     if (p.D > 128)
         return hipErrorInvalidValue;   // the fused kernel keeps <= 8 MFMA column blocks
@@ -445,6 +452,7 @@ hipError_t launch_relaxed(const Problem &p, const uint8_t *unsafe, float *out, u
     a.yref_out = yref_out;
     a.row_m = row_m;
     a.row_l = row_l;
+    a.pzero = pzero;
     a.exact_tiles = exact_tiles;
     const uint64_t grid = (uint64_t)p.BH * p.tiles;
     const dim3 g((unsigned)grid), b(kThreads);
@@ -480,7 +488,8 @@ hipError_t launch_relaxed(const Problem &p, const uint8_t *unsafe, float *out, u
 // one wave per row, 16-byte loads and stores when rows are 16-byte aligned.
 __global__ __launch_bounds__(kThreads) void normalise_kernel(const float *ymix, const float *row_m,
                                                              const double *row_l, float *probs,
-                                                             int S, int causal, uint64_t n_rows)
+                                                             int S, int causal, uint64_t n_rows,
+                                                             int tail_done)
 {
     const int lane = threadIdx.x & 63;
     // wave index through readfirstlane: the row's quantities are scalar
@@ -489,11 +498,13 @@ __global__ __launch_bounds__(kThreads) void normalise_kernel(const float *ymix, 
         return;
     const int i = (int)(r % (uint64_t)S);
     const int n = causal ? i + 1 : S;
+    // tail_done: the keys past the row's 64-key block hold zeros already
+    const int jend = tail_done && causal ? min(S, (i / kTile + 1) * kTile) : S;
     const double shift = (double)row_m[r] + log(row_l[r]);
     const float *y = ymix + r * (uint64_t)S;
     float *pr = probs + r * (uint64_t)S;
     if ((S & 3) == 0) {
-        for (int j = lane * 4; j < S; j += 256) {
+        for (int j = lane * 4; j < jend; j += 256) {
             float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
             if (j < n)
                 x = *reinterpret_cast<const float4 *>(y + j);
@@ -505,17 +516,17 @@ __global__ __launch_bounds__(kThreads) void normalise_kernel(const float *ymix, 
             *reinterpret_cast<float4 *>(pr + j) = o;
         }
     } else {
-        for (int j = lane; j < S; j += 64)
+        for (int j = lane; j < jend; j += 64)
             pr[j] = j < n ? exp_f32((double)y[j] - shift) : 0.0f;
     }
 }
 
 hipError_t launch_normalise(const Problem &p, const float *ymix, const float *row_m,
-                            const double *row_l, float *probs, hipStream_t st)
+                            const double *row_l, float *probs, hipStream_t st, bool tail_done)
 {
     const uint64_t grid = (p.n_rows + 3) / 4;
     hipLaunchKernelGGL(normalise_kernel, dim3((unsigned)grid), dim3(kThreads), 0, st, ymix, row_m,
-                       row_l, probs, p.S, p.causal, p.n_rows);
+                       row_l, probs, p.S, p.causal, p.n_rows, tail_done ? 1 : 0);
     return hipGetLastError();
 }
 

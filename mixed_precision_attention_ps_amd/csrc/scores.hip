@@ -193,31 +193,6 @@ __device__ __forceinline__ void score_tile_store(TileSmem &sm, const double *s_e
     }
 }
 
-// Zeros over rows of 64-row block rb and keys of 64-key block kb (kb > rb,
-// so every key lies past every row: the probabilities there are 0 under the
-// causal mask).  Rows of a block below the last are whole; keys stop at S.
-// 16-byte stores when S is a multiple of 4 (a float4 then lies wholly
-// inside or past the row), else 4-byte ones.
-__device__ __forceinline__ void zero_mirror_tile(float *pz, int S, int bh, int rb, int kb)
-{
-    float *base = pz + ((size_t)bh * S + (size_t)rb * kTile) * S + (size_t)kb * kTile;
-    const int nk = min(kTile, S - kb * kTile);
-    if ((S & 3) == 0) {
-        for (int e = threadIdx.x; e < kTile * (kTile / 4); e += kThreads) {
-            const int r = e / (kTile / 4), c = 4 * (e % (kTile / 4));
-            if (c < nk)
-                *reinterpret_cast<float4 *>(base + (size_t)r * S + c) =
-                    make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-    } else {
-        for (int e = threadIdx.x; e < kTile * kTile; e += kThreads) {
-            const int r = e / kTile, c = e % kTile;
-            if (c < nk)
-                base[(size_t)r * S + c] = 0.0f;
-        }
-    }
-}
-
 #ifndef LAMP_SCORES_XCD
 #define LAMP_SCORES_XCD 1
 #endif
@@ -283,8 +258,9 @@ __global__ __launch_bounds__(kThreads) void ps_scores_kernel(ScoreArgs a)
     for (long long g = blockIdx.x; g < a.n_tiles; g += FAST_KERNEL ? a.n_tiles : gridDim.x) {
         int bh, ti, tj;
         const int path = tile_path(g, bh, ti, tj);
-        if (zero_fill && tj < ti)
-            zero_mirror_tile(a.pzero, a.S, bh, tj, ti);
+        if (zero_fill && tj < ti)   // rows of block tj (whole), keys of block ti
+            zero_block(a.pzero, a.S, bh, tj * kTile, kTile, ti * kTile,
+                       min(a.S, (ti + 1) * kTile), kThreads);
         if (FAST_KERNEL) {
             if (path == PATH_FAST)
                 score_tile_store<PATH_FAST, P>(sm, s_exp, a, bh, ti, tj);
