@@ -140,14 +140,15 @@ __device__ __forceinline__ void stage_slice(TileSmem &sm, const float4 (&qv)[kSl
 __host__ __device__ constexpr int run_width(int blk) { return blk == 0 ? 0 : blk < 32 ? blk : 32; }
 
 // Blocked ("packed") accumulation order: the current run's sum is added to
-// the accumulator (one PS(mu) add) and restarted from +0.
-template <int PATH>
+// the accumulator (one PS(mu) add) and restarted from +0.  NC: the key
+// groups c < NC the thread accumulates (see compute_slice).
+template <int PATH, int NC = 4>
 __device__ __forceinline__ void flush_runs(TileAcc &acc, const PsConst &pc)
 {
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
+        for (int c = 0; c < NC; ++c) {
             if (PATH == PATH_FAST) {
                 acc.lo[r][c] = ps_round_split(acc.lo[r][c] + acc.blk[r][c], pc.split);
                 acc.blk[r][c] = 0.0f;
@@ -168,12 +169,15 @@ __device__ __forceinline__ void flush_runs(TileAcc &acc, const PsConst &pc)
 // of 32 or more products, whole slices: the caller flushes after a run's
 // last slice.  (A flush that depends on a run-time condition inside or at
 // the end of the unrolled slice makes the compiler hoist all of the slice's
-// LDS reads and spill.)
-template <int PATH, int P>
+// LDS reads and spill.)  NC: only the keys tx + 16 c with c < NC are
+// accumulated (a causal diagonal tile's rows 16 w .. 16 w + 15 see no key
+// past 16 w + 15: wave w needs c <= w); the others stay +0.
+template <int PATH, int P, int NC = 4>
 __device__ __forceinline__ void compute_slice(const TileSmem &sm, TileAcc &acc, int tx, int ty,
                                               const PsConst &pc)
 {
     static_assert(P == 0 || P == 4 || P == 8 || P == 16 || P == 32, "run width");
+    static_assert(NC >= 1 && NC <= 4, "key groups");
     constexpr bool BLOCKED = P != 0;
 #pragma unroll
     for (int dd = 0; dd < kDChunk; ++dd) {
@@ -187,14 +191,14 @@ __device__ __forceinline__ void compute_slice(const TileSmem &sm, TileAcc &acc, 
 #pragma unroll
             for (int r = 0; r < 4; ++r)
 #pragma unroll
-                for (int c = 0; c < 4; ++c)
+                for (int c = 0; c < NC; ++c)
                     ps_mac_fast(qa[r], sa[r], ka[c], BLOCKED ? acc.blk[r][c] : acc.lo[r][c],
                                 acc.ref[r][c], pc.split);
         } else if (PATH == PATH_EXACT) {
 #pragma unroll
             for (int r = 0; r < 4; ++r)
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
+                for (int c = 0; c < NC; ++c) {
                     double t = (double)qa[r] * (double)ka[c];
                     double &a = BLOCKED ? acc.blkd[r][c] : acc.lod[r][c];
                     a = ps_rn64(a + ps_rn64(t, pc.mu), pc.mu);
@@ -205,7 +209,7 @@ __device__ __forceinline__ void compute_slice(const TileSmem &sm, TileAcc &acc, 
 #pragma unroll
             for (int r = 0; r < 4; ++r)
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
+                for (int c = 0; c < NC; ++c) {
                     float p = qa[r] * ka[c];
                     if (BLOCKED)
                         acc.blk[r][c] = acc.blk[r][c] + p;
@@ -213,7 +217,7 @@ __device__ __forceinline__ void compute_slice(const TileSmem &sm, TileAcc &acc, 
                 }
         }
         if (BLOCKED && P < kDChunk && dd % (P ? P : 1) == (P ? P : 1) - 1)
-            flush_runs<PATH>(acc, pc);
+            flush_runs<PATH, NC>(acc, pc);
     }
 }
 
@@ -237,8 +241,9 @@ __device__ __forceinline__ void progress_priority(int d0, int D)
 
 // P: the run width of the blocked order as compute_slice takes it (0 =
 // sequential; 4, 8, 16; 32 for runs of pc.blk >= 32).  PRIO: progress-based
-// issue priority (long dots: the matrix product).
-template <int PATH, int P = 0, bool PRIO = false>
+// issue priority (long dots: the matrix product).  NC: key groups per thread
+// (compute_slice).
+template <int PATH, int P = 0, bool PRIO = false, int NC = 4>
 __device__ __forceinline__ void score_tile(TileSmem &sm, TileAcc &acc, const float *Qh,
                                            const float *Kh, int row0, int col0, int nq, int nk,
                                            int D, const PsConst &pc)
@@ -286,12 +291,12 @@ __device__ __forceinline__ void score_tile(TileSmem &sm, TileAcc &acc, const flo
                     kv[u] = load_slice(Kb, lrow, krows, D, d0 + kDChunk + ld + 16 * u);
                 }
             }
-            compute_slice<PATH, P>(sm, acc, tx, ty, pc);
+            compute_slice<PATH, P, NC>(sm, acc, tx, ty, pc);
         }
         // the end of a run (P = 32), or of the last run (zero padding past D
         // leaves run sums unchanged)
         if (BLOCKED)
-            flush_runs<PATH>(acc, pc);
+            flush_runs<PATH, NC>(acc, pc);
     }
 }
 

@@ -71,10 +71,18 @@ hipError_t launch_operand_scan(const Problem &p, uint8_t *unsafe, hipStream_t st
 }
 
 // Tile (ti, tj) of tile index t within a head: the lower triangle (tj <= ti)
-// in row order when causal, the full square otherwise.
+// in row order when causal (causal == 2: the strict lower triangle, tj < ti,
+// the diagonal tiles being a launch of their own), the full square otherwise.
 __device__ __forceinline__ void tile_coords(int t, int tiles, int causal, int &ti, int &tj)
 {
-    if (causal) {
+    if (causal == 2) {
+        // row a >= 1 holds tiles a (a - 1) / 2 .. a (a + 1) / 2 - 1
+        int a = (int)((sqrtf(8.0f * (float)t + 1.0f) + 1.0f) * 0.5f);
+        while (a * (a - 1) / 2 > t) --a;
+        while ((a + 1) * a / 2 <= t) ++a;
+        ti = a;
+        tj = t - a * (a - 1) / 2;
+    } else if (causal) {
         int a = (int)((sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
         while ((a + 1) * (a + 2) / 2 <= t) ++a;
         while (a * (a + 1) / 2 > t) --a;
@@ -98,16 +106,18 @@ struct ScoreArgs {
     unsigned long long *exact_tiles;
     long long n_tiles;   // BH x tiles per head
     int BH;
+    int tile_set;        // causal: 2 = off-diagonal tiles only (the fast kernel
+                         // when the diagonal kernel runs), else 1
 };
 
-template <int PATH, int P>
+template <int PATH, int P, int NC = 4>
 __device__ __forceinline__ void score_tile_store(TileSmem &sm, const double *s_exp,
                                                  const ScoreArgs &a, int bh, int ti, int tj)
 {
     const size_t head = (size_t)bh * a.S * a.D;
     TileAcc acc;
-    score_tile<PATH, P>(sm, acc, a.q + head, a.k + head, ti * kTile, tj * kTile, a.S, a.S, a.D,
-                        a.pc);
+    score_tile<PATH, P, false, NC>(sm, acc, a.q + head, a.k + head, ti * kTile, tj * kTile, a.S,
+                                   a.S, a.D, a.pc);
     float lo[4][4], ref[4][4];
     tile_scores<PATH, P>(acc, a.pc, lo, ref);
     const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
@@ -231,7 +241,7 @@ __global__ __launch_bounds__(kThreads) void ps_scores_kernel(ScoreArgs a)
     auto tile_path = [&](long long g, int &bh, int &ti, int &tj) {
         long long t;
         head_tile_of(g, a.BH, a.tiles_per_head, bh, t);
-        tile_coords((int)t, a.tiles, a.causal, ti, tj);
+        tile_coords((int)t, a.tiles, a.causal ? (FAST_KERNEL ? a.tile_set : 1) : 0, ti, tj);
         if (a.pc.mu == 23)
             return (int)PATH_FP32;
         if (a.pc.mu <= 10 && !a.unsafe_q[bh * a.tiles + ti] && !a.unsafe_k[bh * a.tiles + tj])
@@ -274,6 +284,35 @@ __global__ __launch_bounds__(kThreads) void ps_scores_kernel(ScoreArgs a)
     }
 }
 
+// Causal diagonal tiles on the fast path, one work-group each.  Wave w holds
+// the tile's rows 16 w .. 16 w + 15, which see keys up to 16 w + 15 only:
+// it multiplies the key groups c <= w (keys tx + 16 c) and leaves the rest,
+// all above the diagonal, at +0 (masked in the epilogue).  The waves take
+// their own copy of the tile loop (wave-uniform); every copy passes the same
+// barriers of the shared operand staging.  The other paths' diagonal tiles
+// stay with the generic kernel.
+template <int P>
+__global__ __launch_bounds__(kThreads) void ps_scores_diag_kernel(ScoreArgs a)
+{
+    __shared__ TileSmem sm;
+    __shared__ double s_exp[64];
+    const long long g = blockIdx.x;
+    int bh;
+    long long t;
+    head_tile_of(g, a.BH, a.tiles, bh, t);
+    const int ti = (int)t;
+    if (a.pc.mu > 10 || a.unsafe_q[bh * a.tiles + ti] || a.unsafe_k[bh * a.tiles + ti])
+        return;
+    exp_table_fill(s_exp);
+    __syncthreads();
+    switch (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) {
+    case 0: score_tile_store<PATH_FAST, P, 1>(sm, s_exp, a, bh, ti, ti); break;
+    case 1: score_tile_store<PATH_FAST, P, 2>(sm, s_exp, a, bh, ti, ti); break;
+    case 2: score_tile_store<PATH_FAST, P, 3>(sm, s_exp, a, bh, ti, ti); break;
+    default: score_tile_store<PATH_FAST, P, 4>(sm, s_exp, a, bh, ti, ti); break;
+    }
+}
+
 constexpr long long kGenericGrid = 2048;   // work-groups of the generic kernel
 constexpr long long kGenericGridBeside = 512;   // ... when the fast kernel runs too
 
@@ -303,6 +342,7 @@ hipError_t launch_ps_scores(const Problem &p, const uint8_t *unsafe, float *ylo,
         return hipErrorInvalidValue;
     a.n_tiles = grid;
     a.BH = p.BH;
+    a.tile_set = 1;
     if (grid == 0)
         return hipSuccess;
 #define LAMP_SCORES_LAUNCH(FASTK, G)                                                           \
@@ -316,8 +356,27 @@ hipError_t launch_ps_scores(const Problem &p, const uint8_t *unsafe, float *ylo,
         }                                                                                      \
     } while (0)
     if (fast) {
-        if (p.mu <= 10)
+        if (p.mu <= 10 && p.causal && p.tiles > 1) {
+            // the off-diagonal tiles, then the diagonal ones in their own launch
+            ScoreArgs o = a;
+            o.tile_set = 2;
+            o.tiles_per_head = p.tiles * (p.tiles - 1) / 2;
+            o.n_tiles = (long long)p.BH * o.tiles_per_head;
+            {
+                ScoreArgs &a = o;   // the launch macro's argument
+                LAMP_SCORES_LAUNCH(true, dim3((unsigned)o.n_tiles));
+            }
+            const dim3 gd((unsigned)((long long)p.BH * p.tiles));
+            switch (run_width(p.pc.blk)) {
+            case 0: hipLaunchKernelGGL((ps_scores_diag_kernel<0>), gd, dim3(kThreads), 0, st, a); break;
+            case 4: hipLaunchKernelGGL((ps_scores_diag_kernel<4>), gd, dim3(kThreads), 0, st, a); break;
+            case 8: hipLaunchKernelGGL((ps_scores_diag_kernel<8>), gd, dim3(kThreads), 0, st, a); break;
+            case 16: hipLaunchKernelGGL((ps_scores_diag_kernel<16>), gd, dim3(kThreads), 0, st, a); break;
+            default: hipLaunchKernelGGL((ps_scores_diag_kernel<32>), gd, dim3(kThreads), 0, st, a); break;
+            }
+        } else if (p.mu <= 10) {
             LAMP_SCORES_LAUNCH(true, dim3((unsigned)grid));
+        }
     } else {
         // beside the fast kernel the generic one usually finds no tile: a
         // smaller grid, whose threads still cover every tile in one look
