@@ -107,8 +107,11 @@ struct ScoreArgs {
     long long n_tiles;   // BH x tiles per head
     int BH;
     int tile_set;        // causal: 2 = off-diagonal tiles only (the fast kernel
-                         // when the diagonal kernel runs), else 1
+                         // when the diagonal tiles run apart), else 1
+    long long diag_from; // fast kernel, >= 0: work-groups from here on take the
+                         // diagonal tiles (diag_tile), after the others
 };
+
 
 template <int PATH, int P, int NC = 4>
 __device__ __forceinline__ void score_tile_store(TileSmem &sm, const double *s_exp,
@@ -225,6 +228,33 @@ __device__ __forceinline__ void head_tile_of(long long g, int BH, int tiles_per_
     }
 }
 
+// Causal diagonal tiles on the fast path, one work-group each.  Wave w holds
+// the tile's rows 16 w .. 16 w + 15, which see keys up to 16 w + 15 only:
+// it multiplies the key groups c <= w (keys tx + 16 c) and leaves the rest,
+// all above the diagonal, at +0 (masked in the epilogue).  The waves take
+// their own copy of the tile loop (wave-uniform); every copy passes the same
+// barriers of the shared operand staging.  The other paths' diagonal tiles
+// stay with the generic kernel.
+// Diagonal tile g (head-major over the heads' tiles, the score kernel's XCD
+// order) when it is on the fast path; s_exp filled and synchronised.
+template <int P>
+__device__ __forceinline__ void diag_tile(TileSmem &sm, const double *s_exp, const ScoreArgs &a,
+                                          long long g)
+{
+    int bh;
+    long long t;
+    head_tile_of(g, a.BH, a.tiles, bh, t);
+    const int ti = (int)t;
+    if (a.pc.mu > 10 || a.unsafe_q[bh * a.tiles + ti] || a.unsafe_k[bh * a.tiles + ti])
+        return;
+    switch (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) {
+    case 0: score_tile_store<PATH_FAST, P, 1>(sm, s_exp, a, bh, ti, ti); break;
+    case 1: score_tile_store<PATH_FAST, P, 2>(sm, s_exp, a, bh, ti, ti); break;
+    case 2: score_tile_store<PATH_FAST, P, 3>(sm, s_exp, a, bh, ti, ti); break;
+    default: score_tile_store<PATH_FAST, P, 4>(sm, s_exp, a, bh, ti, ti); break;
+    }
+}
+
 // Two kernels share the tile grid: the fast kernel takes the tiles whose
 // operands allow the FP32 fast path (and returns on the others); the generic
 // kernel takes every other tile (exact double path, or plain FP32 at mu = 23).
@@ -262,6 +292,14 @@ __global__ __launch_bounds__(kThreads) void ps_scores_kernel(ScoreArgs a)
     }
     exp_table_fill(s_exp);
     __syncthreads();
+    // sequential order: the diagonal tiles are the grid's last work-groups
+    // (they fill the tail of the launch)
+    if constexpr (FAST_KERNEL && P == 0) {
+        if (a.diag_from >= 0 && (long long)blockIdx.x >= a.diag_from) {
+            diag_tile<P>(sm, s_exp, a, (long long)blockIdx.x - a.diag_from);
+            return;
+        }
+    }
     // the mirrored zero tiles: every tile's work-group in the fast kernel,
     // or in the generic one when no fast kernel runs (mu > 10)
     const bool zero_fill = a.pzero && a.causal && (FAST_KERNEL || a.pc.mu > 10);
@@ -284,33 +322,14 @@ __global__ __launch_bounds__(kThreads) void ps_scores_kernel(ScoreArgs a)
     }
 }
 
-// Causal diagonal tiles on the fast path, one work-group each.  Wave w holds
-// the tile's rows 16 w .. 16 w + 15, which see keys up to 16 w + 15 only:
-// it multiplies the key groups c <= w (keys tx + 16 c) and leaves the rest,
-// all above the diagonal, at +0 (masked in the epilogue).  The waves take
-// their own copy of the tile loop (wave-uniform); every copy passes the same
-// barriers of the shared operand staging.  The other paths' diagonal tiles
-// stay with the generic kernel.
 template <int P>
 __global__ __launch_bounds__(kThreads) void ps_scores_diag_kernel(ScoreArgs a)
 {
     __shared__ TileSmem sm;
     __shared__ double s_exp[64];
-    const long long g = blockIdx.x;
-    int bh;
-    long long t;
-    head_tile_of(g, a.BH, a.tiles, bh, t);
-    const int ti = (int)t;
-    if (a.pc.mu > 10 || a.unsafe_q[bh * a.tiles + ti] || a.unsafe_k[bh * a.tiles + ti])
-        return;
     exp_table_fill(s_exp);
     __syncthreads();
-    switch (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) {
-    case 0: score_tile_store<PATH_FAST, P, 1>(sm, s_exp, a, bh, ti, ti); break;
-    case 1: score_tile_store<PATH_FAST, P, 2>(sm, s_exp, a, bh, ti, ti); break;
-    case 2: score_tile_store<PATH_FAST, P, 3>(sm, s_exp, a, bh, ti, ti); break;
-    default: score_tile_store<PATH_FAST, P, 4>(sm, s_exp, a, bh, ti, ti); break;
-    }
+    diag_tile<P>(sm, s_exp, a, blockIdx.x);
 }
 
 constexpr long long kGenericGrid = 2048;   // work-groups of the generic kernel
@@ -343,6 +362,7 @@ hipError_t launch_ps_scores(const Problem &p, const uint8_t *unsafe, float *ylo,
     a.n_tiles = grid;
     a.BH = p.BH;
     a.tile_set = 1;
+    a.diag_from = -1;
     if (grid == 0)
         return hipSuccess;
 #define LAMP_SCORES_LAUNCH(FASTK, G)                                                           \
@@ -362,13 +382,22 @@ hipError_t launch_ps_scores(const Problem &p, const uint8_t *unsafe, float *ylo,
             o.tile_set = 2;
             o.tiles_per_head = p.tiles * (p.tiles - 1) / 2;
             o.n_tiles = (long long)p.BH * o.tiles_per_head;
+            const long long nd = (long long)p.BH * p.tiles;
+            if (run_width(p.pc.blk) == 0) {
+                // one launch: the diagonal tiles after the others
+                o.diag_from = o.n_tiles;
+                if (o.n_tiles + nd > 0x7fffffffLL)
+                    return hipErrorInvalidValue;
+                hipLaunchKernelGGL((ps_scores_kernel<true, 0>), dim3((unsigned)(o.n_tiles + nd)),
+                                   dim3(kThreads), 0, st, o);
+                return hipGetLastError();
+            }
             {
                 ScoreArgs &a = o;   // the launch macro's argument
                 LAMP_SCORES_LAUNCH(true, dim3((unsigned)o.n_tiles));
             }
-            const dim3 gd((unsigned)((long long)p.BH * p.tiles));
+            const dim3 gd((unsigned)nd);
             switch (run_width(p.pc.blk)) {
-            case 0: hipLaunchKernelGGL((ps_scores_diag_kernel<0>), gd, dim3(kThreads), 0, st, a); break;
             case 4: hipLaunchKernelGGL((ps_scores_diag_kernel<4>), gd, dim3(kThreads), 0, st, a); break;
             case 8: hipLaunchKernelGGL((ps_scores_diag_kernel<8>), gd, dim3(kThreads), 0, st, a); break;
             case 16: hipLaunchKernelGGL((ps_scores_diag_kernel<16>), gd, dim3(kThreads), 0, st, a); break;
