@@ -893,8 +893,10 @@ static int run(const float *q, const float *k, const float *v, int B, int H, int
     P.tiles = z.tiles;
     P.n_rows = z.n_rows;
     P.head_valid = z.n_valid / z.BH;
-    // the partials' reference sums serve only the row KL
+    // the partials' reference sums serve only the row KL, their y^lo block
+    // maxima only the relaxed rule
     P.ref_sums = want_stats || p.row_kl || p.row_kl_lowp;
+    P.lo_max = mode == LAMP_RELAXED;
 
     // the device summary's counters are kept (and zeroed) only for a summary
     auto *dstats = at<lamp::DevStats>(ws, L.dstats);

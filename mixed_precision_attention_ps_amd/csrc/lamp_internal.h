@@ -36,6 +36,8 @@ struct Problem {
     int tiles;            // ceil(S / 64)
     uint64_t n_rows;      // BH * S
     uint64_t head_valid;  // valid pairs per head
+    bool lo_max = true;   // per-tile partials carry m_lo (the relaxed rule's block
+                          // maxima; else -inf)
     bool ref_sums = true; // per-tile partials carry the reference sums L, B
                           // (false: only the maxima, when no KL is asked for)
     unsigned long long *n_band = nullptr;   // near-tie count of the criterion

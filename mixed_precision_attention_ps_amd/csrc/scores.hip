@@ -103,6 +103,7 @@ struct ScoreArgs {
     float *pzero;        // causal: zero the mirrored upper tile (may be null)
     RefPartial *part;
     int ref_sums;        // part: L and B too (else only the maxima; L = B = 0)
+    int lo_max;          // part: m_lo too (else -inf)
     unsigned long long *exact_tiles;
     long long n_tiles;   // BH x tiles per head
     int BH;
@@ -160,10 +161,17 @@ __device__ __forceinline__ void score_tile_store(TileSmem &sm, const double *s_e
                 const int j = tj * kTile + tx + 16 * c;
                 valid[r][c] = i < a.S && j < a.S && (!a.causal || j <= i);
                 m[r] = fmaxf(m[r], valid[r][c] ? ref[r][c] : -INFINITY);
-                mlo[r] = fmaxf(mlo[r], valid[r][c] ? lo[r][c] : -INFINITY);
             }
             m[r] = group16_max(m[r]);
-            mlo[r] = group16_max(mlo[r]);
+        }
+        if (a.lo_max) {   // uniform over the launch
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    mlo[r] = fmaxf(mlo[r], valid[r][c] ? lo[r][c] : -INFINITY);
+                mlo[r] = group16_max(mlo[r]);
+            }
         }
         double L[4], B[4];
 #pragma unroll
@@ -355,6 +363,7 @@ hipError_t launch_ps_scores(const Problem &p, const uint8_t *unsafe, float *ylo,
     a.pzero = pzero;
     a.part = part;
     a.ref_sums = p.ref_sums ? 1 : 0;
+    a.lo_max = p.lo_max ? 1 : 0;
     a.exact_tiles = exact_tiles;
     const long long grid = (long long)p.BH * a.tiles_per_head;
     if (grid > 0x7fffffffLL)
