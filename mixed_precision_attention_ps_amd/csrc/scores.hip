@@ -72,7 +72,8 @@ hipError_t launch_operand_scan(const Problem &p, uint8_t *unsafe, hipStream_t st
 
 // Tile (ti, tj) of tile index t within a head: the lower triangle (tj <= ti)
 // in row order when causal (causal == 2: the strict lower triangle, tj < ti,
-// the diagonal tiles being a launch of their own), the full square otherwise.
+// the diagonal tiles being the launch's last work-groups), the full square
+// otherwise.
 __device__ __forceinline__ void tile_coords(int t, int tiles, int causal, int &ti, int &tj)
 {
     if (causal == 2) {
@@ -107,8 +108,8 @@ struct ScoreArgs {
     unsigned long long *exact_tiles;
     long long n_tiles;   // BH x tiles per head
     int BH;
-    int tile_set;        // causal: 2 = off-diagonal tiles only (the fast kernel
-                         // when the diagonal tiles run apart), else 1
+    int tile_set;        // causal: 2 = off-diagonal tiles in the tile loop (the
+                         // diagonal ones from diag_from on), else 1
     long long diag_from; // fast kernel, >= 0: work-groups from here on take the
                          // diagonal tiles (diag_tile), after the others
 };
@@ -236,15 +237,17 @@ __device__ __forceinline__ void head_tile_of(long long g, int BH, int tiles_per_
     }
 }
 
-// Causal diagonal tiles on the fast path, one work-group each.  Wave w holds
-// the tile's rows 16 w .. 16 w + 15, which see keys up to 16 w + 15 only:
-// it multiplies the key groups c <= w (keys tx + 16 c) and leaves the rest,
-// all above the diagonal, at +0 (masked in the epilogue).  The waves take
-// their own copy of the tile loop (wave-uniform); every copy passes the same
-// barriers of the shared operand staging.  The other paths' diagonal tiles
-// stay with the generic kernel.
-// Diagonal tile g (head-major over the heads' tiles, the score kernel's XCD
-// order) when it is on the fast path; s_exp filled and synchronised.
+// Causal diagonal tile g (head-major over the heads' tiles, the score
+// kernel's XCD order) when it is on the fast path, by one work-group (s_exp
+// filled and synchronised).  Wave w holds the tile's rows 16 w .. 16 w + 15,
+// which see keys up to 16 w + 15 only: it multiplies the key groups c <= w
+// (keys tx + 16 c) and leaves the rest, all above the diagonal, at +0
+// (masked in the epilogue).  The waves take their own copy of the tile loop
+// (wave-uniform); every copy passes the same barriers of the shared operand
+// staging.  The other paths' diagonal tiles stay with the generic kernel.
+// Sequential order only: with the blocked orders' run sums the copies need
+// 109 registers (four waves per SIMD), and their diagonal tiles stay in the
+// plain tile loop.
 template <int P>
 __device__ __forceinline__ void diag_tile(TileSmem &sm, const double *s_exp, const ScoreArgs &a,
                                           long long g)
@@ -330,15 +333,6 @@ __global__ __launch_bounds__(kThreads) void ps_scores_kernel(ScoreArgs a)
     }
 }
 
-template <int P>
-__global__ __launch_bounds__(kThreads) void ps_scores_diag_kernel(ScoreArgs a)
-{
-    __shared__ TileSmem sm;
-    __shared__ double s_exp[64];
-    exp_table_fill(s_exp);
-    __syncthreads();
-    diag_tile<P>(sm, s_exp, a, blockIdx.x);
-}
 
 constexpr long long kGenericGrid = 2048;   // work-groups of the generic kernel
 constexpr long long kGenericGridBeside = 512;   // ... when the fast kernel runs too
@@ -385,33 +379,18 @@ hipError_t launch_ps_scores(const Problem &p, const uint8_t *unsafe, float *ylo,
         }                                                                                      \
     } while (0)
     if (fast) {
-        if (p.mu <= 10 && p.causal && p.tiles > 1) {
-            // the off-diagonal tiles, then the diagonal ones in their own launch
+        if (p.mu <= 10 && p.causal && p.tiles > 1 && run_width(p.pc.blk) == 0) {
+            // one launch: the off-diagonal tiles, then the diagonal ones
             ScoreArgs o = a;
             o.tile_set = 2;
             o.tiles_per_head = p.tiles * (p.tiles - 1) / 2;
             o.n_tiles = (long long)p.BH * o.tiles_per_head;
+            o.diag_from = o.n_tiles;
             const long long nd = (long long)p.BH * p.tiles;
-            if (run_width(p.pc.blk) == 0) {
-                // one launch: the diagonal tiles after the others
-                o.diag_from = o.n_tiles;
-                if (o.n_tiles + nd > 0x7fffffffLL)
-                    return hipErrorInvalidValue;
-                hipLaunchKernelGGL((ps_scores_kernel<true, 0>), dim3((unsigned)(o.n_tiles + nd)),
-                                   dim3(kThreads), 0, st, o);
-                return hipGetLastError();
-            }
-            {
-                ScoreArgs &a = o;   // the launch macro's argument
-                LAMP_SCORES_LAUNCH(true, dim3((unsigned)o.n_tiles));
-            }
-            const dim3 gd((unsigned)nd);
-            switch (run_width(p.pc.blk)) {
-            case 4: hipLaunchKernelGGL((ps_scores_diag_kernel<4>), gd, dim3(kThreads), 0, st, a); break;
-            case 8: hipLaunchKernelGGL((ps_scores_diag_kernel<8>), gd, dim3(kThreads), 0, st, a); break;
-            case 16: hipLaunchKernelGGL((ps_scores_diag_kernel<16>), gd, dim3(kThreads), 0, st, a); break;
-            default: hipLaunchKernelGGL((ps_scores_diag_kernel<32>), gd, dim3(kThreads), 0, st, a); break;
-            }
+            if (o.n_tiles + nd > 0x7fffffffLL)
+                return hipErrorInvalidValue;
+            hipLaunchKernelGGL((ps_scores_kernel<true, 0>), dim3((unsigned)(o.n_tiles + nd)),
+                               dim3(kThreads), 0, st, o);
         } else if (p.mu <= 10) {
             LAMP_SCORES_LAUNCH(true, dim3((unsigned)grid));
         }
