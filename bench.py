@@ -120,7 +120,9 @@ def tau_for_workload(name: str, mode: str, mu: int, rate: float) -> float:
 
 
 def copy_calibration(args, dev):
-    """A plain device copy of known size (the scale of the HBM counters)."""
+    """A plain device copy of known size (the scale of the HBM counters), and
+    a read-only reduction over the same bytes (a cross-check of the read
+    scale)."""
     import torch
     if args.copy_calib_mib:
         n = args.copy_calib_mib * (1 << 20) // 4
@@ -128,7 +130,10 @@ def copy_calibration(args, dev):
         b = torch.empty_like(a)
         b.copy_(a)
         torch.cuda.synchronize()
-        del a, b
+        del a
+        s = torch.amax(b)
+        torch.cuda.synchronize()
+        del b, s
 
 
 def decode_cpu_baseline(Q, K, V, w, nq, mu, tau, ps_block=0):
