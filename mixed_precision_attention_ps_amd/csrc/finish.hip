@@ -168,6 +168,11 @@ __global__ __launch_bounds__(kThreads * WS) void finish_kernel(FinishArgs a)
             load_scores(j0 + kFinKeys, ynext);
             load_v(j0 + kFinKeys, vnext);
         }
+        // issue priority: the step's probabilities and staging (exponentials,
+        // stores: what the barrier waits on) at 2, its MFMA steps at 0, so
+        // that a work-group's barrier is reached sooner on a SIMD shared with
+        // others' MFMA work (S = 4096 layer: 1.88 -> 1.82 ms)
+        __builtin_amdgcn_s_setprio(2);
         float pv[KPT];
         const int jb = j0 + kseg;
 #pragma unroll
@@ -209,6 +214,7 @@ __global__ __launch_bounds__(kThreads * WS) void finish_kernel(FinishArgs a)
             }
         }
         __syncthreads();
+        __builtin_amdgcn_s_setprio(0);
 #pragma unroll
         for (int k16 = 0; k16 < kFinKeys / 16; ++k16) {
             floatx4 part[NBW];
