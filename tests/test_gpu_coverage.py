@@ -56,7 +56,7 @@ def xl_inputs():
     return WORKLOADS[XL].qkv()[:3]
 
 
-def xl_call(dev, Q, K, V, *, tau, kl, scores, stats):
+def xl_call(dev, Q, K, V, *, tau, kl, scores, stats, mode=STRICT):
     import torch
     from mixed_precision_attention_ps_amd import lamp
     B, H, S, D = Q.shape
@@ -71,8 +71,8 @@ def xl_call(dev, Q, K, V, *, tau, kl, scores, stats):
     if scores:
         t["scores_mix"] = torch.zeros((B, H, S, S), device=dev)
         t["scores_ref"] = torch.zeros((B, H, S, S), device=dev)
-    note(f"full tensor {XL} strict tau={tau} kl={kl} scores={scores} stats={stats}")
-    out, st = lamp.lamp_attention_fwd(q, k, v, causal=True, mu=4, tau=tau, mode=STRICT,
+    note(f"full tensor {XL} mode={mode} tau={tau} kl={kl} scores={scores} stats={stats}")
+    out, st = lamp.lamp_attention_fwd(q, k, v, causal=True, mu=4, tau=tau, mode=mode,
                                       probs=t["probs"], recompute_mask=t["mask"],
                                       row_kl=t.get("row_kl"), row_kl_lowp=t.get("row_kl_lowp"),
                                       row_count=t.get("row_count"),
@@ -83,7 +83,7 @@ def xl_call(dev, Q, K, V, *, tau, kl, scores, stats):
     return t, st
 
 
-def compare_chunked(orc, t, st, Q, K, V, tau, *, kl, scores):
+def compare_chunked(orc, t, st, Q, K, V, tau, *, kl, scores, mode=STRICT):
     """Every head against the oracle, HEAD_CHUNK heads at a time."""
     B, H, S, D = Q.shape
     BH = B * H
@@ -96,7 +96,7 @@ def compare_chunked(orc, t, st, Q, K, V, tau, *, kl, scores):
         want = ["crit", "mask", "probs", "out", "kl", "kl_lowp", "count"]
         if scores:
             want += ["ylo", "yref"]
-        r = orc.lamp_heads(Q, K, V, causal=True, mu=4, tau=tau, mode=STRICT, heads=heads,
+        r = orc.lamp_heads(Q, K, V, causal=True, mu=4, tau=tau, mode=mode, heads=heads,
                            want=tuple(want))
         g = lambda name, shape: t[name].view(BH, *shape)[sl].cpu().numpy()
         ties += parity.assert_mask(g("mask", (S, (S + 31) // 32)).view(np.uint32), r["mask"],
@@ -148,6 +148,18 @@ def test_xl_full_tensor_serving_gather(dev, orc, xl_inputs):
     tau = tau_for(XL, "strict", 4, 0.016)
     t, st = xl_call(dev, Q, K, V, tau=tau, kl=False, scores=False, stats=False)
     compare_chunked(orc, t, None, Q, K, V, tau, kl=False, scores=False)
+
+
+def test_xl_full_tensor_relaxed_bench_configuration(dev, orc, xl_inputs):
+    """The relaxed rule in the bench's configuration (the library's choice:
+    score tiles, then the relaxed row pass with P.V; probabilities, mask, row
+    KLs and statistics), every head and row against the oracle."""
+    from mixed_precision_attention_ps_amd import lamp
+    Q, K, V = xl_inputs
+    tau = tau_for(XL, "relaxed", 4, 0.016)
+    t, st = xl_call(dev, Q, K, V, tau=tau, kl=True, scores=False, stats=True, mode=RELAXED)
+    assert lamp.IMPLS[st["impl"]] == "relaxed_rows"
+    compare_chunked(orc, t, st, Q, K, V, tau, kl=True, scores=False, mode=RELAXED)
 
 
 R4K = "relaxed_s4096"
